@@ -1,0 +1,160 @@
+"""FP8 (OCP E4M3) dynamically quantized linear layers for AMD MI355X (gfx950).
+
+Python binding of libdq.so. Each function here has the name of the C entry point it calls and
+only marshals arguments: it checks tensor devices, dtypes and shapes, allocates outputs with
+torch (device memory only) when the caller passes none, and calls the library on the current
+stream. Every step of the computation runs in the HIP kernels of libdq; there is no fallback.
+
+    q, scale   = dq_quantize_fp8(x)                # x: bf16 [M, K] on the GPU
+    qw, w_scale = dq_quantize_weight_fp8(w)        # w: bf16 [N, K], once per weight
+    out = dq_linear_fp8(q, scale, qw, w_scale, bias, "gelu_tanh")
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdq.so")
+
+DQ_OK, DQ_ERR_NULL, DQ_ERR_SHAPE, DQ_ERR_ALIGN, DQ_ERR_ALIAS, DQ_ERR_EPILOGUE, DQ_ERR_HIP = range(7)
+EPILOGUES = {"bias": 0, "gelu_tanh": 1, "gated_residual": 2}
+
+
+class DQError(RuntimeError):
+    """A nonzero status from libdq."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.hip_error = lib().dq_last_hip_error() if status == DQ_ERR_HIP else 0
+        msg = lib().dq_status_string(status).decode()
+        extra = f" (hipError {self.hip_error})" if self.hip_error else ""
+        super().__init__(f"{where}: status {status}: {msg}{extra}")
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libdq.so. Raises if it was not built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python fp8_dynamic_quant_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.dq_quantize_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.dq_quantize_fp8.restype = i32
+        L.dq_quantize_weight_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.dq_quantize_weight_fp8.restype = i32
+        L.dq_linear_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp]
+        L.dq_linear_fp8.restype = i32
+        L.dq_status_string.argtypes = [i32]
+        L.dq_status_string.restype = ctypes.c_char_p
+        L.dq_last_hip_error.argtypes = []
+        L.dq_last_hip_error.restype = i32
+        L.dq_abi_version.argtypes = []
+        L.dq_abi_version.restype = i32
+        _LIB = L
+    return _LIB
+
+
+lib()  # fail at import when the library is missing
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check(status, where):
+    if status != DQ_OK:
+        raise DQError(status, where)
+
+
+def _quantize(fn, where, x, q, scale, stream):
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError(f"{where}: input must be a 2-D tensor")
+    if x.device.type != "cuda":
+        raise ValueError(f"{where}: input must be on a GPU")
+    R, K = x.shape
+    dev = x.device
+    _need(x, "input", torch.bfloat16, (R, K), dev)
+    q = torch.empty((R, K), dtype=torch.uint8, device=dev) if q is None else q
+    scale = torch.empty((R,), dtype=torch.float32, device=dev) if scale is None else scale
+    _need(q, "codes", torch.uint8, (R, K), dev)
+    _need(scale, "scale", torch.float32, (R,), dev)
+    with torch.cuda.device(dev):
+        _check(fn(_ptr(x), R, K, _ptr(q), _ptr(scale), _stream(stream, dev)), where)
+    return q, scale
+
+
+def dq_quantize_fp8(x, q=None, scale=None, stream=None):
+    """Per-token FP8 quantization: x bf16 [M, K] -> (codes uint8 [M, K], scale float32 [M])."""
+    return _quantize(lib().dq_quantize_fp8, "dq_quantize_fp8", x, q, scale, stream)
+
+
+def dq_quantize_weight_fp8(w, qw=None, w_scale=None, stream=None):
+    """Per-output-channel FP8 quantization: w bf16 [N, K] -> (codes [N, K], scale [N])."""
+    return _quantize(lib().dq_quantize_weight_fp8, "dq_quantize_weight_fp8", w, qw, w_scale, stream)
+
+
+def dq_linear_fp8(q, scale, qw, w_scale, bias=None, epilogue="bias", gate=None, residual=None,
+                  out=None, stream=None):
+    """W8A8 GEMM + fused epilogue -> bf16 [M, N].
+
+    epilogue: "bias" | "gelu_tanh" | "gated_residual" (needs gate [N] and residual [M, N];
+    out may be residual itself for an in-place update).
+    """
+    if epilogue not in EPILOGUES:
+        raise ValueError(f"unknown epilogue {epilogue!r}")
+    if not isinstance(q, torch.Tensor) or q.dim() != 2 or not isinstance(qw, torch.Tensor) \
+            or qw.dim() != 2:
+        raise ValueError("dq_linear_fp8: q and qw must be 2-D tensors")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("dq_linear_fp8: tensors must be on a GPU")
+    M, K = q.shape
+    N = qw.shape[0]
+    _need(q, "q", torch.uint8, (M, K), dev)
+    _need(scale, "scale", torch.float32, (M,), dev)
+    _need(qw, "qw", torch.uint8, (N, K), dev)
+    _need(w_scale, "w_scale", torch.float32, (N,), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, (N,), dev)
+    if epilogue == "gated_residual":
+        if gate is None or residual is None:
+            raise ValueError("gated_residual needs gate and residual")
+        _need(gate, "gate", torch.bfloat16, (N,), dev)
+        _need(residual, "residual", torch.bfloat16, (M, N), dev)
+    else:
+        gate = residual = None
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
+    _need(out, "out", torch.bfloat16, (M, N), dev)
+    with torch.cuda.device(dev):
+        _check(lib().dq_linear_fp8(_ptr(q), _ptr(scale), M, K, _ptr(qw), _ptr(w_scale), N,
+                                   _ptr(bias), EPILOGUES[epilogue], _ptr(gate), _ptr(residual),
+                                   _ptr(out), _stream(stream, dev)), "dq_linear_fp8")
+    return out
+
+
+__all__ = ["dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8", "DQError", "EPILOGUES",
+           "lib", "LIB_PATH"]

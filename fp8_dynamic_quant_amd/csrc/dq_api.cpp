@@ -1,0 +1,122 @@
+// C ABI of libdq: argument checks on the host, then asynchronous launches on the caller's stream.
+// Every check runs before any HIP call, so a rejected call enqueues nothing and needs no GPU.
+#include "../../include/dq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "dq_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxElems = int64_t(1) << 47;
+constexpr int64_t kMaxLinearK = int64_t(1) << 24;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a + na) and [b, b + nb) overlap (byte ranges, empty ranges never overlap).
+bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  if (na == 0 || nb == 0 || a == nullptr || b == nullptr) return false;
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return DQ_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return DQ_ERR_HIP;
+}
+
+int check_quantize(const void* x, int64_t R, int64_t K, const void* q, const float* scale) {
+  if (R < 0 || R > kMaxDim || K < 8 || K > kMaxDim || (K % 8) != 0) return DQ_ERR_SHAPE;
+  if (R > 0 && K > kMaxElems / R) return DQ_ERR_SHAPE;
+  if (R == 0) return DQ_OK;
+  if (!x || !q || !scale) return DQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scale)) return DQ_ERR_ALIGN;
+  const uint64_t n = static_cast<uint64_t>(R) * static_cast<uint64_t>(K);
+  if (overlap(q, n, x, 2 * n) || overlap(scale, 4 * static_cast<uint64_t>(R), x, 2 * n) ||
+      overlap(scale, 4 * static_cast<uint64_t>(R), q, n))
+    return DQ_ERR_ALIAS;
+  return DQ_OK;
+}
+
+int quantize_rows(const void* x, int64_t R, int64_t K, void* q, float* scale, void* stream) {
+  const int st = check_quantize(x, R, K, q, scale);
+  if (st != DQ_OK || R == 0) return st;
+  return hip_status(dq::launch_quantize_rows(static_cast<const uint16_t*>(x), R, K,
+                                             static_cast<uint8_t*>(q), scale,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int dq_quantize_fp8(const void* x, int64_t M, int64_t K, void* q, float* scale, void* stream) {
+  return quantize_rows(x, M, K, q, scale, stream);
+}
+
+int dq_quantize_weight_fp8(const void* w, int64_t N, int64_t K, void* qw, float* w_scale,
+                           void* stream) {
+  return quantize_rows(w, N, K, qw, w_scale, stream);
+}
+
+int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const void* qw,
+                  const float* w_scale, int64_t N, const void* bias, int epilogue,
+                  const void* gate, const void* residual, void* out, void* stream) {
+  // K < 2^24 keeps a 256-row tile of an operand inside one 32-bit buffer range
+  if (M < 0 || M > kMaxDim || K < 128 || K >= kMaxLinearK || (K % 128) != 0 || N < 64 ||
+      N > kMaxDim || (N % 64) != 0)
+    return DQ_ERR_SHAPE;
+  if ((M > 0 && K > kMaxElems / M) || K > kMaxElems / N || (M > 0 && N > kMaxElems / M))
+    return DQ_ERR_SHAPE;
+  if (epilogue != DQ_EPI_BIAS && epilogue != DQ_EPI_GELU_TANH &&
+      epilogue != DQ_EPI_GATED_RESIDUAL)
+    return DQ_ERR_EPILOGUE;
+  const bool gated = epilogue == DQ_EPI_GATED_RESIDUAL;
+  if (gated && (!gate || !residual)) return DQ_ERR_EPILOGUE;
+  if (M == 0) return DQ_OK;
+  if (!q || !scale || !qw || !w_scale || !out) return DQ_ERR_NULL;
+  if (!aligned16(q) || !aligned16(scale) || !aligned16(qw) || !aligned16(w_scale) ||
+      !aligned16(out) || (bias && !aligned16(bias)) || (gated && !aligned16(gate)) ||
+      (gated && !aligned16(residual)))
+    return DQ_ERR_ALIGN;
+  const uint64_t m = static_cast<uint64_t>(M), k = static_cast<uint64_t>(K),
+                 n = static_cast<uint64_t>(N);
+  const uint64_t out_bytes = 2 * m * n;
+  if (overlap(out, out_bytes, q, m * k) || overlap(out, out_bytes, scale, 4 * m) ||
+      overlap(out, out_bytes, qw, n * k) || overlap(out, out_bytes, w_scale, 4 * n) ||
+      overlap(out, out_bytes, bias, bias ? 2 * n : 0) ||
+      (gated && overlap(out, out_bytes, gate, 2 * n)))
+    return DQ_ERR_ALIAS;
+  if (gated && residual != out && overlap(out, out_bytes, residual, out_bytes)) return DQ_ERR_ALIAS;
+  return hip_status(dq::launch_linear(
+      static_cast<const uint8_t*>(q), scale, M, K, static_cast<const uint8_t*>(qw), w_scale, N,
+      static_cast<const uint16_t*>(bias), epilogue,
+      gated ? static_cast<const uint16_t*>(gate) : nullptr,
+      gated ? static_cast<const uint16_t*>(residual) : nullptr, static_cast<uint16_t*>(out),
+      static_cast<hipStream_t>(stream)));
+}
+
+const char* dq_status_string(int status) {
+  switch (status) {
+    case DQ_OK: return "ok";
+    case DQ_ERR_NULL: return "a required pointer is NULL";
+    case DQ_ERR_SHAPE: return "a size is out of range or breaks a multiple-of rule";
+    case DQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case DQ_ERR_ALIAS: return "an output overlaps an input";
+    case DQ_ERR_EPILOGUE: return "unknown epilogue, or gate/residual missing for the gated one";
+    case DQ_ERR_HIP: return "a HIP runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+int dq_last_hip_error(void) { return g_last_hip_error; }
+
+int dq_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,188 @@
+// Per-row dynamic FP8 (OCP E4M3) quantization for gfx950.
+//
+// One wavefront owns one row. Each lane loads its share of the row as 16-byte chunks (8 bf16)
+// straight into registers, so the row is read from HBM exactly once:
+//   1. amax: |bf16| compares like its 15 magnitude bits read as an unsigned integer (finite
+//      inputs), so the running max is a packed 16-bit integer max; then a wavefront butterfly.
+//   2. scale = amax / 448 (IEEE division, correctly rounded).
+//   3. code = E4M3(x / scale): an IEEE division per element, then the hardware conversion
+//      v_cvt_pk_fp8_f32, which rounds to nearest-even into OCP E4M3. That conversion does not
+//      saturate (inputs above 464 become NaN), but x / scale <= 448 (1 + 2^-23) whenever the
+//      scale is a normal fp32, which rounds to 448. Rows with a subnormal scale clamp the
+//      quotient to +-448 first.
+//   4. An all-zero row stores scale 0 and copies each sign bit into its code.
+// Codes leave as 8-byte stores (one per 16-byte input chunk), consecutive lanes on consecutive
+// addresses. The scheme follows the dynamic FP8 quantization of weights and activations on the
+// page "Solucion de WaveSpeed para Acelerar la Generacion de Imagenes FLUX.1-dev", section
+// "Cuantizacion Dinamica FP8", with one scale per row.
+#include "dq_internal.h"
+
+namespace dq {
+namespace {
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kE4M3Max = 448.0f;
+constexpr float kFltMinNormal = 1.17549435082228750797e-38f;
+
+__device__ __forceinline__ uint32_t absmax_pk(uint32_t acc, uint32_t w) {
+  u16x2 a = __builtin_bit_cast(u16x2, acc);
+  u16x2 b = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+}
+
+__device__ __forceinline__ uint32_t absmax4(uint32_t acc, uint4 v) {
+  acc = absmax_pk(acc, v.x);
+  acc = absmax_pk(acc, v.y);
+  acc = absmax_pk(acc, v.z);
+  return absmax_pk(acc, v.w);
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t m) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)m, off, 64);
+    m = m > o ? m : o;
+  }
+  return m;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two dwords of bf16 (4 values) -> four E4M3 codes in one dword.
+template <bool kClamp>
+__device__ __forceinline__ uint32_t encode4(uint32_t w0, uint32_t w1, float s) {
+  float a = bf16_lo(w0) / s;
+  float b = bf16_hi(w0) / s;
+  float c = bf16_lo(w1) / s;
+  float d = bf16_hi(w1) / s;
+  if (kClamp) {
+    a = fminf(fmaxf(a, -kE4M3Max), kE4M3Max);
+    b = fminf(fmaxf(b, -kE4M3Max), kE4M3Max);
+    c = fminf(fmaxf(c, -kE4M3Max), kE4M3Max);
+    d = fminf(fmaxf(d, -kE4M3Max), kE4M3Max);
+  }
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return (uint32_t)r;
+}
+
+// Codes of an all-zero row: the sign bit of each bf16 moved to bit 7 of its byte.
+__device__ __forceinline__ uint32_t signs4(uint32_t w0, uint32_t w1) {
+  return ((w0 >> 8) & 0x80u) | ((w0 >> 16) & 0x8000u) | ((w1 << 8) & 0x800000u) |
+         (w1 & 0x80000000u);
+}
+
+template <bool kClamp>
+__device__ __forceinline__ uint2 encode8(uint4 v, float s) {
+  return make_uint2(encode4<kClamp>(v.x, v.y, s), encode4<kClamp>(v.z, v.w, s));
+}
+
+__device__ __forceinline__ uint2 signs8(uint4 v) {
+  return make_uint2(signs4(v.x, v.y), signs4(v.z, v.w));
+}
+
+// Register-resident version: lane l holds chunks l, l+64, ..., l+64*(NCH-1) of its row.
+template <int NCH>
+__global__ void __launch_bounds__(256) quant_rows_reg(const uint16_t* __restrict__ x, int R, int K,
+                                                      uint8_t* __restrict__ q,
+                                                      float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= R) return;
+  const int C = K >> 3;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)row * (size_t)K);
+  uint2* qr = reinterpret_cast<uint2*>(q + (size_t)row * (size_t)K);
+
+  uint4 v[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    v[i] = (c < C) ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) mx = absmax4(mx, v[i]);
+  uint32_t m = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
+  m = __builtin_amdgcn_readfirstlane(wave_max(m));
+
+  const float amax = __uint_as_float(m << 16);
+  const float s = amax / kE4M3Max;
+  if (lane == 0) scale[row] = s;
+
+  if (m == 0) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < C) qr[c] = signs8(v[i]);
+    }
+  } else if (s < kFltMinNormal) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < C) qr[c] = encode8<true>(v[i], s);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < C) qr[c] = encode8<false>(v[i], s);
+    }
+  }
+}
+
+// Any K: two passes over the row (the second pass usually hits in L2).
+__global__ void __launch_bounds__(256) quant_rows_loop(const uint16_t* __restrict__ x, int R, int K,
+                                                       uint8_t* __restrict__ q,
+                                                       float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= R) return;
+  const int C = K >> 3;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)row * (size_t)K);
+  uint2* qr = reinterpret_cast<uint2*>(q + (size_t)row * (size_t)K);
+  uint32_t mx = 0;
+  for (int c = lane; c < C; c += 64) mx = absmax4(mx, xr[c]);
+  uint32_t m = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
+  m = __builtin_amdgcn_readfirstlane(wave_max(m));
+  const float amax = __uint_as_float(m << 16);
+  const float s = amax / kE4M3Max;
+  if (lane == 0) scale[row] = s;
+  if (m == 0) {
+    for (int c = lane; c < C; c += 64) qr[c] = signs8(xr[c]);
+  } else if (s < kFltMinNormal) {
+    for (int c = lane; c < C; c += 64) qr[c] = encode8<true>(xr[c], s);
+  } else {
+    for (int c = lane; c < C; c += 64) qr[c] = encode8<false>(xr[c], s);
+  }
+}
+
+template <int NCH>
+hipError_t launch_reg(const uint16_t* x, int R, int K, uint8_t* q, float* scale, hipStream_t st) {
+  hipLaunchKernelGGL(quant_rows_reg<NCH>, dim3((R + 3) / 4), dim3(256), 0, st, x, R, K, q, scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows(const uint16_t* x, int64_t R, int64_t K, uint8_t* q, float* scale,
+                                hipStream_t stream) {
+  if (R == 0) return hipSuccess;
+  const int r = (int)R, k = (int)K;
+  const int64_t nch = (K / 8 + 63) / 64;  // 16-byte chunks per lane
+  if (nch <= 1) return launch_reg<1>(x, r, k, q, scale, stream);
+  if (nch <= 2) return launch_reg<2>(x, r, k, q, scale, stream);
+  if (nch <= 3) return launch_reg<3>(x, r, k, q, scale, stream);
+  if (nch <= 4) return launch_reg<4>(x, r, k, q, scale, stream);
+  if (nch <= 6) return launch_reg<6>(x, r, k, q, scale, stream);
+  if (nch <= 8) return launch_reg<8>(x, r, k, q, scale, stream);
+  if (nch <= 12) return launch_reg<12>(x, r, k, q, scale, stream);
+  if (nch <= 16) return launch_reg<16>(x, r, k, q, scale, stream);
+  if (nch <= 24) return launch_reg<24>(x, r, k, q, scale, stream);
+  if (nch <= 30) return launch_reg<30>(x, r, k, q, scale, stream);
+  hipLaunchKernelGGL(quant_rows_loop, dim3((r + 3) / 4), dim3(256), 0, stream, x, r, k, q, scale);
+  return hipGetLastError();
+}
+
+}  // namespace dq

@@ -1,0 +1,131 @@
+/*
+ * dq.h -- C ABI of libdq: FP8 (OCP E4M3) dynamically quantized linear layers for AMD MI355X
+ * (gfx950).
+ *
+ * The operation is the dynamically quantized linear layer of a FLUX-style diffusion
+ * transformer:
+ *   - weights and activations are brought to FP8 at run time so that the 8-bit matrix units do
+ *     the GEMM (page "Solucion de WaveSpeed para Acelerar la Generacion de Imagenes
+ *     FLUX.1-dev", section "Cuantizacion Dinamica FP8");
+ *   - the model keeps bf16 tensors around an FP8 compute core (page "WaveSpeedAI X DataCrunch:
+ *     Inferencia de Imagenes FLUX en Tiempo Real en B200", section "Marco de Inferencia
+ *     Propietario": mixed BF16/FP8 precision);
+ *   - the GEMM carries its epilogue fused (page "Accelerarea generarii de imagini cu FLUX 3
+ *     Image Klein pe GPU-urile Blackwell NVIDIA", the paragraph after "Tabelul 1" on GEMMs with
+ *     fused epilogues);
+ *   - no host round trips and memory planned ahead of time (page "WaveSpeedAI X DataCrunch",
+ *     section "Marco de Inferencia Propietario"): every call is asynchronous on the caller's
+ *     stream, and the library allocates nothing.
+ *
+ * Readings taken where the pages are silent: one scale per row (token of x, output channel of
+ * W); OCP E4M3 (largest finite 448); scale = amax / 448 and each code = E4M3(x / scale), both
+ * divisions correctly rounded in fp32, rounding to nearest with ties to the even code and
+ * saturation at +-448; an all-zero row gets scale 0 and signed-zero codes.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, owned by the caller, row-major and contiguous,
+ *     16-byte aligned. bf16 tensors are passed as raw 16-bit storage, FP8 tensors as raw bytes.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued on it and the call
+ *     returns without waiting; nothing is allocated, freed or synchronized.
+ *   - Arguments are checked on the host before anything is enqueued. On a failed check the call
+ *     returns a nonzero DQ_ERR_* code and enqueues nothing. A failed kernel launch returns
+ *     DQ_ERR_HIP and the HIP error code can be read with dq_last_hip_error(). Faults inside a
+ *     kernel surface at the caller's next synchronization, as for any HIP kernel.
+ *   - Calls are thread-safe; the library keeps no per-call state.
+ *   - M = 0 is valid and enqueues nothing.
+ */
+#ifndef DQ_H
+#define DQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum {
+  DQ_OK = 0,
+  DQ_ERR_NULL = 1,      /* a required pointer is NULL */
+  DQ_ERR_SHAPE = 2,     /* a size is negative, too large, or breaks a multiple-of rule */
+  DQ_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
+  DQ_ERR_ALIAS = 4,     /* an output overlaps an input (other than out == residual) */
+  DQ_ERR_EPILOGUE = 5,  /* unknown epilogue, or gate/residual missing for the gated one */
+  DQ_ERR_HIP = 6        /* a HIP runtime call failed; see dq_last_hip_error() */
+};
+
+/* Epilogues of dq_linear_fp8 (v = acc * scale[m] * w_scale[n] + bias[n]). */
+enum {
+  DQ_EPI_BIAS = 0,           /* out = bf16(v) */
+  DQ_EPI_GELU_TANH = 1,      /* out = bf16(0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))) */
+  DQ_EPI_GATED_RESIDUAL = 2  /* out = bf16(residual[m,n] + gate[n] * v) */
+};
+
+/*
+ * dq_quantize_fp8 -- per-token dynamic FP8 quantization of activations.
+ * Follows "Cuantizacion Dinamica FP8" (page "Solucion de WaveSpeed para Acelerar la Generacion
+ * de Imagenes FLUX.1-dev"): scales are recomputed from the live tensor on every call.
+ *
+ *   x      bf16 [M, K]   input activations (read only)
+ *   q      uint8 [M, K]  output E4M3 codes
+ *   scale  float [M]     output per-row scale: scale[m] = fl32(max_k |x[m,k]| / 448)
+ *   q[m,k] = E4M3_RNE_SAT(fl32(x[m,k] / scale[m])); a zero row gives scale 0 and codes 0x00/0x80
+ *   (the sign bit of each x).
+ * Requirements: 0 <= M < 2^31, 8 <= K < 2^31, K % 8 == 0, M*K < 2^47, x/q/scale 16-byte
+ * aligned, q and scale not overlapping x or each other. Inputs must be finite (NaN/Inf inputs
+ * give unspecified codes).
+ */
+int dq_quantize_fp8(const void* x, int64_t M, int64_t K, void* q, float* scale, void* stream);
+
+/*
+ * dq_quantize_weight_fp8 -- per-output-channel FP8 quantization of a weight W [N, K]
+ * (row n = output channel n). The same arithmetic as dq_quantize_fp8, applied once when a
+ * weight is loaded; the result (qw, w_scale) is what dq_linear_fp8 consumes.
+ *
+ *   w        bf16 [N, K]   weight (read only)
+ *   qw       uint8 [N, K]  output E4M3 codes
+ *   w_scale  float [N]     output per-channel scale
+ * Requirements as dq_quantize_fp8 with M replaced by N.
+ */
+int dq_quantize_weight_fp8(const void* w, int64_t N, int64_t K, void* qw, float* w_scale,
+                           void* stream);
+
+/*
+ * dq_linear_fp8 -- W8A8 GEMM with the dequant / bias / activation epilogue fused.
+ * The GEMM with a fused epilogue follows the page "Accelerarea generarii de imagini cu FLUX 3
+ * Image Klein pe GPU-urile Blackwell NVIDIA" (paragraph after "Tabelul 1").
+ *
+ *   q         uint8 [M, K]   activation codes (from dq_quantize_fp8)
+ *   scale     float [M]      activation scales
+ *   qw        uint8 [N, K]   weight codes (from dq_quantize_weight_fp8), K-contiguous
+ *   w_scale   float [N]      weight scales
+ *   bias      bf16 [N]       or NULL (= zero bias)
+ *   epilogue  DQ_EPI_*
+ *   gate      bf16 [N]       required iff epilogue == DQ_EPI_GATED_RESIDUAL, else ignored
+ *   residual  bf16 [M, N]    required iff epilogue == DQ_EPI_GATED_RESIDUAL, else ignored;
+ *                            may be the same pointer as out (in-place residual update)
+ *   out       bf16 [M, N]    output
+ *   acc[m,n] = sum_k dec(q[m,k]) * dec(qw[n,k]) accumulated by the FP8 matrix units into fp32;
+ *   v = acc * scale[m] * w_scale[n] + bias[n], then the epilogue, rounded once to bf16 (nearest
+ *   even).
+ * Requirements: 0 <= M < 2^31, 128 <= K < 2^24 with K % 128 == 0, 64 <= N < 2^31 with
+ * N % 64 == 0, all pointers 16-byte aligned, out overlapping no input except out == residual.
+ */
+int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const void* qw,
+                  const float* w_scale, int64_t N, const void* bias, int epilogue,
+                  const void* gate, const void* residual, void* out, void* stream);
+
+/* Static English text for a status code (never NULL). */
+const char* dq_status_string(int status);
+
+/* The hipError_t behind the most recent DQ_ERR_HIP returned on the calling thread (0 if none). */
+int dq_last_hip_error(void);
+
+/* ABI version of this header (currently 1). */
+int dq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DQ_H */

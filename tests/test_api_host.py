@@ -1,0 +1,146 @@
+"""The C-ABI library on the host: it loads, exports every declared entry point, and rejects bad
+arguments before touching the GPU (so these run without one). Fake device addresses are never
+dereferenced: every call here fails its host-side checks, or has M = 0 and enqueues nothing.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dq.h")
+LIB = os.path.join(ROOT, "fp8_dynamic_quant_amd", "libdq.so")
+
+OK, NULL, SHAPE, ALIGN, ALIAS, EPI, HIP = range(7)
+BIAS, GELU, GATED = 0, 1, 2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libdq.so is not built (python fp8_dynamic_quant_amd/build.py)")
+    L = ctypes.CDLL(LIB)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    L.dq_quantize_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.dq_quantize_weight_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.dq_linear_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp]
+    L.dq_status_string.restype = ctypes.c_char_p
+    L.dq_status_string.argtypes = [i32]
+    return L
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(dq_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = _declared()
+    for n in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
+              "dq_status_string", "dq_last_hip_error", "dq_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.dq_abi_version() == 1
+    for st in range(7):
+        s = lib.dq_status_string(st)
+        assert s and len(s) > 1
+    assert lib.dq_status_string(12345) == b"unknown status"
+    assert lib.dq_last_hip_error() == 0
+
+
+X, Q, S = 0x10000000, 0x20000000, 0x30000000          # fake, 16-byte aligned, far apart
+
+
+@pytest.mark.parametrize("fn", ["dq_quantize_fp8", "dq_quantize_weight_fp8"])
+def test_quantize_argument_checks(lib, fn):
+    f = getattr(lib, fn)
+    assert f(X, 0, 64, Q, S, None) == OK                    # empty: nothing to do
+    assert f(None, 4, 64, Q, S, None) == NULL
+    assert f(X, 4, 64, None, S, None) == NULL
+    assert f(X, 4, 64, Q, None, None) == NULL
+    assert f(X, -1, 64, Q, S, None) == SHAPE
+    assert f(X, 4, 0, Q, S, None) == SHAPE
+    assert f(X, 4, 12, Q, S, None) == SHAPE                 # K % 8
+    assert f(X, 4, 4, Q, S, None) == SHAPE                  # K < 8
+    assert f(X, 1 << 31, 64, Q, S, None) == SHAPE           # M too large
+    assert f(X + 2, 4, 64, Q, S, None) == ALIGN
+    assert f(X, 4, 64, Q + 8, S, None) == ALIGN
+    assert f(X, 4, 64, Q, S + 4, None) == ALIGN
+    assert f(X, 4, 64, X + 64, S, None) == ALIAS            # codes inside x
+    assert f(X, 4, 64, Q, X, None) == ALIAS                 # scales inside x
+    assert f(X, 4, 64, Q, Q + 128, None) == ALIAS           # scales inside codes
+
+
+def test_quantize_adjacent_buffers_are_not_aliases(lib):
+    # x occupies [X, X + 2*4*64); codes right after it do not overlap
+    # (the call is rejected for another reason so that nothing is launched)
+    assert lib.dq_quantize_fp8(X, 4, 64, X + 2 * 4 * 64, None, None) == NULL
+
+
+Aq, As, Wq, Ws, Bi, Ga, Re, Ou = (0x1000000 * i for i in range(1, 9))
+
+
+def lin(lib, M=64, K=256, N=128, q=Aq, sa=As, qw=Wq, sw=Ws, bias=Bi, epi=BIAS, gate=Ga,
+        res=Re, out=Ou):
+    return lib.dq_linear_fp8(q, sa, M, K, qw, sw, N, bias, epi, gate, res, out, None)
+
+
+def test_linear_argument_checks(lib):
+    assert lin(lib, M=0) == OK
+    assert lin(lib, M=0, epi=7) == EPI                       # epilogue is checked even when empty
+    assert lin(lib, K=192) == SHAPE                          # K % 128
+    assert lin(lib, K=0) == SHAPE
+    assert lin(lib, K=1 << 24) == SHAPE                      # one tile must fit a 32-bit range
+    assert lin(lib, N=96) == SHAPE                           # N % 64
+    assert lin(lib, N=0) == SHAPE
+    assert lin(lib, M=-3) == SHAPE
+    assert lin(lib, epi=3) == EPI
+    assert lin(lib, epi=-1) == EPI
+    assert lin(lib, epi=GATED, gate=None) == EPI
+    assert lin(lib, epi=GATED, res=None) == EPI
+    assert lin(lib, q=None) == NULL
+    assert lin(lib, sa=None) == NULL
+    assert lin(lib, qw=None) == NULL
+    assert lin(lib, sw=None) == NULL
+    assert lin(lib, out=None) == NULL
+    assert lin(lib, q=Aq + 1) == ALIGN
+    assert lin(lib, bias=Bi + 2) == ALIGN
+    assert lin(lib, epi=GATED, gate=Ga + 2) == ALIGN
+    assert lin(lib, epi=GATED, res=Re + 2) == ALIGN
+    assert lin(lib, out=Ou + 8) == ALIGN
+    assert lin(lib, out=Aq) == ALIAS                         # out over the codes
+    assert lin(lib, out=Ws) == ALIAS
+    assert lin(lib, out=Bi) == ALIAS
+    assert lin(lib, epi=GATED, out=Ga) == ALIAS
+    assert lin(lib, epi=GATED, out=Re + 64) == ALIAS         # partial overlap with residual
+
+
+def test_last_hip_error_untouched_by_argument_errors(lib):
+    assert lin(lib, K=100) == SHAPE
+    assert lib.dq_last_hip_error() == 0
+
+
+def test_python_binding_names_match_the_c_entry_points():
+    import fp8_dynamic_quant_amd as dq
+    for name in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8"):
+        assert callable(getattr(dq, name))
+    assert dq.lib().dq_abi_version() == 1
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    import fp8_dynamic_quant_amd as dq
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        dq.dq_quantize_fp8(x)
+    with pytest.raises(ValueError):
+        dq.dq_linear_fp8(torch.zeros(4, 128, dtype=torch.uint8), torch.zeros(4),
+                         torch.zeros(64, 128, dtype=torch.uint8), torch.zeros(64))
