@@ -1,0 +1,339 @@
+"""Benchmark of the FP8 dynamic-quant linear path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the hot path over one batch: per-token FP8 quantization of the bf16
+activations (dq_quantize_fp8) followed by the FP8 GEMM with its fused epilogue (dq_linear_fp8).
+Weights are quantized once, off the timed path. Inputs are seeded synthetic tensors of the
+workload's shapes, resident in HBM before timing starts; several buffer sets rotate so that the
+256 MB last-level cache does not hold a step's inputs.
+
+Prints one JSON line: whole-step throughput (TFLOP/s), the GEMM kernel against the FP8 matrix
+peak, the quantize kernel against HBM bandwidth, the linears of a full FLUX-dev denoising step
+(ms), and the CPU oracle timed on the host as a baseline.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 matrix peak
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E bandwidth
+METRIC = "FP8-DQ linear TFLOP/s & % FP8 MFMA peak; quantizer GB/s; DiT-step linears ms"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = {
+    "gemm": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "gemm_fp8.hip"),
+    "quantize": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "quantize.hip"),
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(kind, workload_name):
+    """HBM bytes per launch measured with rocprofv3 counters, if the kernel source is unchanged."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+        rec = data[workload_name][kind]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kind]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------------------------
+# GPU side
+# ---------------------------------------------------------------------------------------------
+
+def to_dev_bf16(torch, u16, dev):
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def bench_linear(shape, seed, steps, warmup, n_sets):
+    """Time `steps` steps of quantize + linear. Returns a dict of timings."""
+    import torch
+    import fp8_dynamic_quant_amd as dq
+    from workloads import make_linear_inputs
+
+    dev = torch.device("cuda:0")
+    inp = make_linear_inputs(shape, seed)
+    M, K, N = shape.M, shape.K, shape.N
+    gated = shape.epilogue == "gated_residual"
+    sets = []
+    for _ in range(n_sets):
+        x = to_dev_bf16(torch, inp.x, dev)
+        w = to_dev_bf16(torch, inp.w, dev)
+        qw, sw = dq.dq_quantize_weight_fp8(w)
+        del w
+        st = {
+            "x": x, "qw": qw, "sw": sw,
+            "q": torch.empty((M, K), dtype=torch.uint8, device=dev),
+            "sa": torch.empty((M,), dtype=torch.float32, device=dev),
+            "bias": to_dev_bf16(torch, inp.bias, dev),
+            "out": torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+            "gate": to_dev_bf16(torch, inp.gate, dev) if gated else None,
+            "res": to_dev_bf16(torch, inp.residual, dev) if gated else None,
+        }
+        sets.append(st)
+    torch.cuda.synchronize()
+
+    def step(st):
+        dq.dq_quantize_fp8(st["x"], st["q"], st["sa"])
+        e_mid = torch.cuda.Event(enable_timing=True)
+        e_mid.record()
+        if gated:   # in place on the residual stream, as in the model
+            dq.dq_linear_fp8(st["q"], st["sa"], st["qw"], st["sw"], st["bias"], shape.epilogue,
+                             st["gate"], st["res"], out=st["res"])
+        else:
+            dq.dq_linear_fp8(st["q"], st["sa"], st["qw"], st["sw"], st["bias"], shape.epilogue,
+                             out=st["out"])
+        return e_mid
+
+    for i in range(warmup):
+        step(sets[i % n_sets])
+    torch.cuda.synchronize()
+    starts, mids, ends = [], [], []
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_begin.record()
+    for i in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        em = step(sets[i % n_sets])
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record()
+        starts.append(e0)
+        mids.append(em)
+        ends.append(e1)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_begin.elapsed_time(t_end)
+    q_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, mids)])
+    g_ms = np.array([a.elapsed_time(b) for a, b in zip(mids, ends)])
+    return {"total_ms": total_ms, "wall_s": wall, "quant_ms": q_ms, "gemm_ms": g_ms}
+
+
+def bench_dit_step(steps, warmup):
+    """All linears of one 1024^2 FLUX-dev denoising step (228 quantize + GEMM pairs), distinct
+    weights per block, timed end to end as one sequence on one stream."""
+    import torch
+    import fp8_dynamic_quant_amd as dq
+    from workloads import dit_step_device_inputs, workload
+
+    w = workload("flux-dit-step-1024")
+    dev = torch.device("cuda:0")
+    plan, acts, residuals = dit_step_device_inputs(w, dev, dq.dq_quantize_weight_fp8)
+    outs = {}
+    qbuf = {}
+    for lin in plan:
+        M, K, N = lin["M"], lin["K"], lin["N"]
+        if (M, K) not in qbuf:
+            qbuf[(M, K)] = (torch.empty((M, K), dtype=torch.uint8, device=dev),
+                            torch.empty((M,), dtype=torch.float32, device=dev))
+        if lin["epilogue"] != "gated_residual" and (M, N) not in outs:
+            outs[(M, N)] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def run():
+        for lin in plan:
+            M, K, N = lin["M"], lin["K"], lin["N"]
+            q, sa = qbuf[(M, K)]
+            dq.dq_quantize_fp8(acts[lin["act"]], q, sa)
+            if lin["epilogue"] == "gated_residual":
+                r = residuals[lin["residual"]]
+                dq.dq_linear_fp8(q, sa, lin["qw"], lin["sw"], lin["bias"], "gated_residual",
+                                 lin["gate"], r, out=r)
+            else:
+                dq.dq_linear_fp8(q, sa, lin["qw"], lin["sw"], lin["bias"], lin["epilogue"],
+                                 out=outs[(M, N)])
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = w.flops_per_step
+    wbytes = sum(l["N"] * l["K"] for l in plan)
+    return {"ms": ms, "tflops": flops / ms / 1e9, "linears": len(plan), "weight_bytes": wbytes}
+
+
+# ---------------------------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on the host
+# ---------------------------------------------------------------------------------------------
+
+def cpu_baseline(shape, seed, reps=2):
+    from threadpoolctl import threadpool_info
+    from oracle import linear_ref, quantize_rows
+    from workloads import bf16_bits_to_f32, make_linear_inputs
+
+    inp = make_linear_inputs(shape, seed)
+    qw, sw = quantize_rows(bf16_bits_to_f32(inp.w))       # weight prep, not timed
+    x = bf16_bits_to_f32(inp.x)
+    bias = bf16_bits_to_f32(inp.bias)
+    gate = None if inp.gate is None else bf16_bits_to_f32(inp.gate)
+    res = None if inp.residual is None else bf16_bits_to_f32(inp.residual)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        q, sa = quantize_rows(x)
+        y = linear_ref(q, sa, qw, sw, bias, shape.epilogue, gate, res)
+        times.append(time.perf_counter() - t0)
+        del y
+    t = float(np.mean(times))
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    return {
+        "value": round(shape.flops / t / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"the whole {shape.M}x{shape.K}x{shape.N} {shape.epilogue} step (quantize "
+                   f"x + exact float64 contraction + epilogue), mean of {reps} runs; "
+                   f"elementwise NumPy single-threaded, BLAS with {threads} threads"),
+        "seconds_per_step": round(t, 3),
+        "host_cpus_visible": os.cpu_count(),
+    }
+
+
+# ---------------------------------------------------------------------------------------------
+
+def calibrate_copy(nbytes=1 << 30):
+    """One plain device-to-device copy of known size (a reference for HBM byte counters)."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"calibration copy of {nbytes} bytes done")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="flux-mlp-up-1024")
+    ap.add_argument("--linear", type=int, default=0, help="index of the linear in the workload")
+    ap.add_argument("--sets", type=int, default=6, help="rotating input/output buffer sets")
+    ap.add_argument("--dit-steps", type=int, default=5)
+    ap.add_argument("--no-dit", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 1 GiB plain copy first (reference for HBM counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this path runs on a single MI355X and has no "
+              "multi-GPU mode (--gpus must be 1).", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    from workloads import workload
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import fp8_dynamic_quant_amd as dq
+
+    if args.calibrate_copy:
+        calibrate_copy()
+
+    w = workload(args.workload)
+    shape = w.linears[args.linear]
+    log(f"workload {w.name}[{args.linear}] M={shape.M} K={shape.K} N={shape.N} "
+        f"epilogue={shape.epilogue}; warmup {args.warmup}, steps {args.steps}")
+    r = bench_linear(shape, w.seed, args.steps, args.warmup, args.sets)
+    ms_per_step = r["total_ms"] / args.steps
+    value = shape.flops / ms_per_step / 1e9          # TFLOP/s
+    gemm_ms = float(np.mean(r["gemm_ms"]))
+    quant_ms = float(np.mean(r["quant_ms"]))
+    gemm_tflops = shape.flops / gemm_ms / 1e9
+    qbytes = 3 * shape.M * shape.K + 4 * shape.M
+    quant_gbps = qbytes / quant_ms / 1e6
+    log(f"step {ms_per_step * 1e3:.1f} us: quantize {quant_ms * 1e3:.1f} us "
+        f"({quant_gbps:.0f} GB/s), GEMM {gemm_ms * 1e3:.1f} us ({gemm_tflops:.0f} TFLOP/s)")
+
+    traffic = stored_traffic("gemm", w.name)
+    qtraffic = stored_traffic("quantize", w.name)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 in/out)",
+        "data": "synthetic",
+        "config": {"workload": w.name, "linear": shape.name, "M": shape.M, "K": shape.K,
+                   "N": shape.N, "epilogue": shape.epilogue, "rotating_sets": args.sets,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {
+            "kernel": f"gemm_fp8_256x256<{shape.epilogue}>",
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 2),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(gemm_ms * 1e3, 2),
+            "algorithmic_flop_per_launch": shape.flops,
+        },
+        "quantizer": {
+            "kernel": "quant_rows_reg",
+            "bound": "hbm",
+            "achieved": round(quant_gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(quant_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": qtraffic,
+            "avg_launch_us": round(quant_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": qbytes,
+        },
+    }
+    if not args.no_dit:
+        log("DiT step: generating 228 distinct FP8 weights on the device")
+        d = bench_dit_step(args.dit_steps, 2)
+        floor_ms = 13.74
+        res["dit_step"] = {"workload": "flux-dit-step-1024", "linears": d["linears"],
+                           "ms": round(d["ms"], 3), "tflops": round(d["tflops"], 1),
+                           "roofline_floor_ms": floor_ms,
+                           "frac": round(floor_ms / d["ms"], 4), "steps": args.dit_steps}
+        log(f"DiT step linears: {d['ms']:.2f} ms ({d['tflops']:.0f} TFLOP/s)")
+    if not args.no_cpu_baseline:
+        log("CPU baseline: timing the oracle on the host")
+        res["cpu_baseline"] = cpu_baseline(shape, w.seed)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

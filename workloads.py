@@ -150,13 +150,9 @@ class LinearInputs:
     outlier_cols: Optional[np.ndarray] = None
 
 
-def make_linear_inputs(shape: LinearShape, seed: int, index: int = 0,
-                       rows: Optional[slice] = None) -> LinearInputs:
-    """Draw the inputs of one linear from NumPy PCG64 seeded with [seed, index].
-
-    `rows` is not supported for partial generation; the whole tensor is always drawn so that
-    every consumer sees the same values.
-    """
+def make_linear_inputs(shape: LinearShape, seed: int, index: int = 0) -> LinearInputs:
+    """Draw the inputs of one linear from NumPy PCG64 seeded with [seed, index] (whole tensors,
+    so that every consumer sees the same values)."""
     rng = np.random.default_rng([seed, index])
     M, K, N = shape.M, shape.K, shape.N
     cols = rng.choice(K, shape.n_outliers, replace=False) if shape.n_outliers else np.zeros(0, np.int64)
@@ -190,3 +186,66 @@ def make_rows(M: int, K: int, seed: int, n_outliers: Optional[int] = None,
     if cols.size:
         x[:, cols] *= np.float32(factor)
     return f32_to_bf16_bits(x)
+
+
+# ---------------------------------------------------------------------------------------------
+# Full denoising step: inputs drawn on the device (8.6 GB of weights are too slow to draw on the
+# host). torch.Generator on the device, seeded 4_000_000 + 100 * block + 10 * stream + linear.
+# ---------------------------------------------------------------------------------------------
+
+def dit_step_plan(wl: Workload):
+    """Execution order of the 228 linears of one step: for each of the 19 double-stream blocks,
+    the image stream's then the text stream's QKV, proj, fc1, fc2; then for each of the 38
+    single-stream blocks, linear1 and linear2. Each entry names its shape and seed."""
+    by_name = {l.name: l for l in wl.linears}
+    plan = []
+    for b in range(19):
+        for si, stream in enumerate(("img", "txt")):
+            for li, part in enumerate(("qkv", "proj", "fc1", "fc2")):
+                plan.append((by_name[f"double.{stream}.{part}"], 100 * b + 10 * si + li, stream))
+    for b in range(38):
+        for li, part in enumerate(("linear1", "linear2")):
+            plan.append((by_name[f"single.{part}"], 100 * (19 + b) + 20 + li, "single"))
+    return plan
+
+
+def dit_step_device_inputs(wl: Workload, device, quantize_weight):
+    """Draw every input of one step on `device` and hand each bf16 weight to `quantize_weight`
+    (which returns its (codes, scales)); the bf16 weight is dropped afterwards.
+
+    Returns (plan, activations, residual_streams): plan entries are dicts with the shape, the
+    epilogue, the activation key, the residual key (gated linears), qw, sw, bias and gate."""
+    import torch
+    base = 4_000_000
+    acts, residuals = {}, {}
+    g = torch.Generator(device=device)
+    for l in wl.linears:
+        key = f"{l.M}x{l.K}"
+        if key in acts:
+            continue
+        g.manual_seed(base + 7 * l.M + l.K)
+        x = torch.randn((l.M, l.K), generator=g, device=device, dtype=torch.float32)
+        cols = torch.randperm(l.K, generator=g, device=device)[: l.n_outliers]
+        x[:, cols] *= l.outlier_factor
+        acts[key] = x.to(torch.bfloat16)
+        del x
+    for stream, M in (("img", 4096), ("txt", 512), ("single", 4608)):
+        g.manual_seed(base + 99 + M)
+        residuals[stream] = torch.randn((M, 3072), generator=g, device=device,
+                                        dtype=torch.float32).to(torch.bfloat16)
+    plan = []
+    for shape, sub, stream in dit_step_plan(wl):
+        g.manual_seed(base + sub)
+        w = (torch.randn((shape.N, shape.K), generator=g, device=device, dtype=torch.float32)
+             * 0.02).to(torch.bfloat16)
+        qw, sw = quantize_weight(w)
+        del w
+        bias = (torch.randn(shape.N, generator=g, device=device) * 0.01).to(torch.bfloat16)
+        gate = None
+        if shape.epilogue == "gated_residual":
+            gate = (1.0 + 0.1 * torch.randn(shape.N, generator=g, device=device)).to(torch.bfloat16)
+        plan.append({"name": shape.name, "M": shape.M, "K": shape.K, "N": shape.N,
+                     "epilogue": shape.epilogue, "act": f"{shape.M}x{shape.K}",
+                     "residual": stream if shape.epilogue == "gated_residual" else None,
+                     "qw": qw, "sw": sw, "bias": bias, "gate": gate, "seed": base + sub})
+    return plan, acts, residuals
