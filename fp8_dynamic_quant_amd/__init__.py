@@ -8,6 +8,10 @@ stream. Every step of the computation runs in the HIP kernels of libdq; there is
     q, scale   = dq_quantize_fp8(x)                # x: bf16 [M, K] on the GPU
     qw, w_scale = dq_quantize_weight_fp8(w)        # w: bf16 [N, K], once per weight
     out = dq_linear_fp8(q, scale, qw, w_scale, bias, "gelu_tanh")
+
+dq_linear_fp8 takes a workspace that lets workgroups share tiles (see include/dq.h). By default
+the binding keeps one zero-filled workspace per (device, stream) and grows it when a larger
+problem needs more; pass workspace=None to run without one, or a uint8 tensor of your own.
 """
 import ctypes
 import os
@@ -17,7 +21,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdq.so")
 
-DQ_OK, DQ_ERR_NULL, DQ_ERR_SHAPE, DQ_ERR_ALIGN, DQ_ERR_ALIAS, DQ_ERR_EPILOGUE, DQ_ERR_HIP = range(7)
+(DQ_OK, DQ_ERR_NULL, DQ_ERR_SHAPE, DQ_ERR_ALIGN, DQ_ERR_ALIAS, DQ_ERR_EPILOGUE, DQ_ERR_HIP,
+ DQ_ERR_WORKSPACE) = range(8)
 EPILOGUES = {"bias": 0, "gelu_tanh": 1, "gated_residual": 2}
 
 
@@ -48,8 +53,11 @@ def lib() -> ctypes.CDLL:
         L.dq_quantize_fp8.restype = i32
         L.dq_quantize_weight_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
         L.dq_quantize_weight_fp8.restype = i32
-        L.dq_linear_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp]
+        L.dq_linear_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp,
+                                    ctypes.c_uint64, vp]
         L.dq_linear_fp8.restype = i32
+        L.dq_linear_fp8_workspace_size.argtypes = [i64, i64, i64]
+        L.dq_linear_fp8_workspace_size.restype = ctypes.c_uint64
         L.dq_status_string.argtypes = [i32]
         L.dq_status_string.restype = ctypes.c_char_p
         L.dq_last_hip_error.argtypes = []
@@ -117,12 +125,35 @@ def dq_quantize_weight_fp8(w, qw=None, w_scale=None, stream=None):
     return _quantize(lib().dq_quantize_weight_fp8, "dq_quantize_weight_fp8", w, qw, w_scale, stream)
 
 
+def dq_linear_fp8_workspace_size(M, K, N):
+    """Bytes of workspace dq_linear_fp8 uses for an M x K -> N problem (0: invalid sizes)."""
+    return int(lib().dq_linear_fp8_workspace_size(int(M), int(K), int(N)))
+
+
+_WORKSPACES = {}
+
+
+def _cached_workspace(dev, stream, nbytes):
+    """The zero-filled workspace of (device, stream), grown to at least nbytes. Every completed
+    call leaves a workspace zeroed, and calls on one stream run in order, so it is reused."""
+    key = (dev.index, stream.cuda_stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        with torch.cuda.stream(stream):
+            ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def dq_linear_fp8(q, scale, qw, w_scale, bias=None, epilogue="bias", gate=None, residual=None,
-                  out=None, stream=None):
+                  out=None, stream=None, workspace="auto"):
     """W8A8 GEMM + fused epilogue -> bf16 [M, N].
 
     epilogue: "bias" | "gelu_tanh" | "gated_residual" (needs gate [N] and residual [M, N];
     out may be residual itself for an in-place update).
+    workspace: "auto" (a cached zero-filled buffer per device and stream), None, or a uint8
+    tensor of at least dq_linear_fp8_workspace_size(M, K, N) bytes that holds zeros before its
+    first use.
     """
     if epilogue not in EPILOGUES:
         raise ValueError(f"unknown epilogue {epilogue!r}")
@@ -150,11 +181,24 @@ def dq_linear_fp8(q, scale, qw, w_scale, bias=None, epilogue="bias", gate=None, 
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
     _need(out, "out", torch.bfloat16, (M, N), dev)
     with torch.cuda.device(dev):
+        st = stream if stream is not None else torch.cuda.current_stream(dev)
+        ws_bytes = 0
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError(f"workspace must be 'auto', None or a tensor, not {workspace!r}")
+            need = dq_linear_fp8_workspace_size(M, K, N)
+            workspace = _cached_workspace(dev, st, need) if (need and M > 0) else None
+        if workspace is not None:
+            if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 \
+                    or workspace.device != dev or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous uint8 tensor on the device")
+            ws_bytes = workspace.numel()
         _check(lib().dq_linear_fp8(_ptr(q), _ptr(scale), M, K, _ptr(qw), _ptr(w_scale), N,
                                    _ptr(bias), EPILOGUES[epilogue], _ptr(gate), _ptr(residual),
-                                   _ptr(out), _stream(stream, dev)), "dq_linear_fp8")
+                                   _ptr(out), _ptr(workspace), ws_bytes,
+                                   ctypes.c_void_p(st.cuda_stream)), "dq_linear_fp8")
     return out
 
 
-__all__ = ["dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8", "DQError", "EPILOGUES",
-           "lib", "LIB_PATH"]
+__all__ = ["dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
+           "dq_linear_fp8_workspace_size", "DQError", "EPILOGUES", "lib", "LIB_PATH"]

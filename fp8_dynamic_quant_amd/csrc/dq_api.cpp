@@ -52,6 +52,19 @@ int quantize_rows(const void* x, int64_t R, int64_t K, void* q, float* scale, vo
                                              static_cast<hipStream_t>(stream)));
 }
 
+// Sizes of dq_linear_fp8 (shared with the workspace size query).
+int check_linear_shape(int64_t M, int64_t K, int64_t N) {
+  // K < 2^24 keeps a 256-row tile of an operand inside one 32-bit buffer range
+  if (M < 0 || M > kMaxDim || K < 128 || K >= kMaxLinearK || (K % 128) != 0 || N < 64 ||
+      N > kMaxDim || (N % 64) != 0)
+    return DQ_ERR_SHAPE;
+  if ((M > 0 && K > kMaxElems / M) || K > kMaxElems / N || (M > 0 && N > kMaxElems / M))
+    return DQ_ERR_SHAPE;
+  // tile-steps are counted in 32-bit integers on the device
+  if (dq::linear_units(M, K, N) >= (int64_t(1) << 31)) return DQ_ERR_SHAPE;
+  return DQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -67,13 +80,10 @@ int dq_quantize_weight_fp8(const void* w, int64_t N, int64_t K, void* qw, float*
 
 int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const void* qw,
                   const float* w_scale, int64_t N, const void* bias, int epilogue,
-                  const void* gate, const void* residual, void* out, void* stream) {
-  // K < 2^24 keeps a 256-row tile of an operand inside one 32-bit buffer range
-  if (M < 0 || M > kMaxDim || K < 128 || K >= kMaxLinearK || (K % 128) != 0 || N < 64 ||
-      N > kMaxDim || (N % 64) != 0)
-    return DQ_ERR_SHAPE;
-  if ((M > 0 && K > kMaxElems / M) || K > kMaxElems / N || (M > 0 && N > kMaxElems / M))
-    return DQ_ERR_SHAPE;
+                  const void* gate, const void* residual, void* out, void* workspace,
+                  uint64_t workspace_bytes, void* stream) {
+  const int shape = check_linear_shape(M, K, N);
+  if (shape != DQ_OK) return shape;
   if (epilogue != DQ_EPI_BIAS && epilogue != DQ_EPI_GELU_TANH &&
       epilogue != DQ_EPI_GATED_RESIDUAL)
     return DQ_ERR_EPILOGUE;
@@ -88,6 +98,18 @@ int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const
   const uint64_t m = static_cast<uint64_t>(M), k = static_cast<uint64_t>(K),
                  n = static_cast<uint64_t>(N);
   const uint64_t out_bytes = 2 * m * n;
+  if (workspace) {
+    const uint64_t need = dq::linear_workspace_bytes(M, K, N);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
+      return DQ_ERR_WORKSPACE;
+    if (overlap(workspace, need, q, m * k) || overlap(workspace, need, scale, 4 * m) ||
+        overlap(workspace, need, qw, n * k) || overlap(workspace, need, w_scale, 4 * n) ||
+        overlap(workspace, need, bias, bias ? 2 * n : 0) ||
+        (gated && overlap(workspace, need, gate, 2 * n)) ||
+        (gated && overlap(workspace, need, residual, out_bytes)) ||
+        overlap(workspace, need, out, out_bytes))
+      return DQ_ERR_ALIAS;
+  }
   if (overlap(out, out_bytes, q, m * k) || overlap(out, out_bytes, scale, 4 * m) ||
       overlap(out, out_bytes, qw, n * k) || overlap(out, out_bytes, w_scale, 4 * n) ||
       overlap(out, out_bytes, bias, bias ? 2 * n : 0) ||
@@ -99,7 +121,12 @@ int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const
       static_cast<const uint16_t*>(bias), epilogue,
       gated ? static_cast<const uint16_t*>(gate) : nullptr,
       gated ? static_cast<const uint16_t*>(residual) : nullptr, static_cast<uint16_t*>(out),
-      static_cast<hipStream_t>(stream)));
+      workspace, static_cast<hipStream_t>(stream)));
+}
+
+uint64_t dq_linear_fp8_workspace_size(int64_t M, int64_t K, int64_t N) {
+  if (check_linear_shape(M, K, N) != DQ_OK) return 0;
+  return dq::linear_workspace_bytes(M, K, N);
 }
 
 const char* dq_status_string(int status) {
@@ -111,12 +138,13 @@ const char* dq_status_string(int status) {
     case DQ_ERR_ALIAS: return "an output overlaps an input";
     case DQ_ERR_EPILOGUE: return "unknown epilogue, or gate/residual missing for the gated one";
     case DQ_ERR_HIP: return "a HIP runtime call failed";
+    case DQ_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
     default: return "unknown status";
   }
 }
 
 int dq_last_hip_error(void) { return g_last_hip_error; }
 
-int dq_abi_version(void) { return 1; }
+int dq_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -11,10 +11,43 @@ namespace dq {
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t R, int64_t K, uint8_t* q, float* scale,
                                 hipStream_t stream);
 
-// FP8 GEMM + fused epilogue. Arguments are already validated. Returns the launch status.
+// ---------------------------------------------------------------------------------------------
+// GEMM work split, shared by the size query (host only, no GPU) and the launcher.
+//   tile  = 256 x 256 outputs; step = 128 of K; unit = one step of one tile.
+// With a workspace, G workgroups take equal shares of all units, G <= split_groups() <=
+// kMaxSplitGroups. Workspace layout, the same for every problem so that one workspace serves
+// calls of any size in turn:
+//   [0, kPartRegion)              two 256 x 256 fp32 partial tiles per workgroup (a share can
+//                                 cut a tile at its start and at its end)
+//   [kPartRegion, + 4 * tiles)    one arrival counter per tile, zero between calls
+// ---------------------------------------------------------------------------------------------
+constexpr int64_t kTileM = 256, kTileN = 256, kStepK = 128;
+constexpr int64_t kMaxSplitGroups = 256;
+constexpr int64_t kMinUnitsPerGroup = 4;
+constexpr int64_t kPartialBytes = kTileM * kTileN * 4;
+constexpr uint64_t kPartRegion = static_cast<uint64_t>(kMaxSplitGroups) * 2u * kPartialBytes;
+
+inline int64_t linear_tiles(int64_t M, int64_t N) {
+  return ((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN);
+}
+inline int64_t linear_units(int64_t M, int64_t K, int64_t N) {
+  return linear_tiles(M, N) * (K / kStepK);
+}
+inline int64_t split_groups(int64_t units) {
+  int64_t g = units / kMinUnitsPerGroup;
+  if (g < 1) g = 1;
+  return g < kMaxSplitGroups ? g : kMaxSplitGroups;
+}
+inline uint64_t linear_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+  (void)K;
+  return kPartRegion + ((static_cast<uint64_t>(linear_tiles(M, N)) * 4u + 255u) & ~uint64_t(255));
+}
+
+// FP8 GEMM + fused epilogue. Arguments are already validated; `workspace` is NULL or holds
+// linear_workspace_bytes(M, K, N) bytes. Returns the launch status.
 hipError_t launch_linear(const uint8_t* q, const float* scale, int64_t M, int64_t K,
                          const uint8_t* qw, const float* w_scale, int64_t N, const uint16_t* bias,
                          int epilogue, const uint16_t* gate, const uint16_t* residual,
-                         uint16_t* out, hipStream_t stream);
+                         uint16_t* out, void* workspace, hipStream_t stream);
 
 }  // namespace dq

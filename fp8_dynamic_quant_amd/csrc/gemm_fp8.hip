@@ -4,27 +4,41 @@
 //
 // Both operands are K-contiguous ("TN"), the operand layout the CDNA4 matrix cores read.
 //
-// Work decomposition (one workgroup = 4 wavefronts = 256 threads, one per SIMD):
-//   * workgroup tile 256 (M) x 256 (N); K is consumed 128 bytes per step;
-//   * a step's A tile (256 x 128 B) and B tile (256 x 128 B) are copied global -> LDS by
-//     buffer_load_dwordx4 ... lds (no registers involved); one instruction moves 8 rows x 128 B,
-//     i.e. whole 128-byte lines (copies touching half lines run at half the rate);
-//   * two 64 KiB LDS buffers: the copy of step s+2 is issued right after the barrier that retires
-//     the last fragment reads of step s, so each copy has a whole step to land;
-//   * LDS rows are 128 B; 16-byte chunk c of row r sits at chunk position c ^ (r & 7), so the 8
-//     lanes that read 8 consecutive rows at one K offset hit 8 different chunks (no conflicts);
-//   * wavefront (wm, wn) owns a 128 x 128 sub-tile: 4 x 4 blocks of 32 x 32 computed with
-//     V_MFMA_F32_32X32X64_F8F6F4, fp32 accumulators; the fragments of the next 64-wide K half are
-//     read into a second register set while the MFMAs of the current half run, two LDS reads
-//     issued under each of the first eight MFMAs;
-//   * the weight fragment is the instruction's first operand, so a lane holds 4 consecutive
-//     output columns per 8-column group; lanes l and l + 32 then swap halves (v_permlane32_swap)
-//     so that each lane owns 8 consecutive columns: residual loads and bf16 stores are 16 bytes;
-//   * tiles are numbered so that the workgroups on one XCD (hardware dispatch sends workgroup i
-//     to XCD i mod 8) cover one contiguous range of tiles, walked 4 tile rows at a time, and
-//     share A and B panels in that XCD's L2.
-// The copies are issued from inline assembly so that the compiler does not serialize the LDS
-// fragment reads behind them; every wait on them is explicit (s_waitcnt vmcnt).
+// Work decomposition
+//   * output tiles of 256 x 256, K consumed 128 bytes per step; a "unit" is one step of one tile;
+//   * a persistent grid of G <= (compute units) workgroups. Whole tiles are dealt round-robin
+//     (workgroup v takes tiles v, v + G, ...), so the workgroups of an XCD step through K
+//     together and share A and B slices in L2. When that leaves most compute units idle (few
+//     tiles, long K) and a workspace is given, the tiles from `tail0` on (here: all of them) are
+//     instead cut into G equal shares of units. The parts of a cut tile are summed in fp32
+//     through the workspace by the part that finishes last (an arrival counter per tile; no
+//     workgroup ever waits for another), adding the parts in workgroup order so the result does
+//     not depend on timing; parts travel with device-coherent (sc1) loads and stores, so no
+//     cache flush is needed;
+//   * workgroups are numbered so that the ones on one XCD (hardware dispatch sends workgroup b to
+//     XCD b mod 8) get consecutive numbers, hence neighbouring tiles, and tiles are walked 4 tile
+//     rows at a time, so an XCD's L2 serves the A and B panels its compute units share.
+//
+// Inside a workgroup (8 wavefronts, two per SIMD: waves w and w + 4 share a SIMD)
+//   * wave (g, q), g = w >> 2, q = w & 3, owns a 128 (M) x 64 (N) sub-tile: 4 x 2 blocks of
+//     32 x 32 from V_MFMA_F32_32X32X64_F8F6F4, fp32 accumulators;
+//   * group 1 runs one phase behind group 0, and every phase ends at a workgroup barrier, so in
+//     each phase one wave per SIMD issues 8 MFMAs (one 64-deep K half) while the other reads its
+//     next fragments from LDS (ping-pong);
+//   * each step's A tile (256 x 128 B) and B tile (256 x 128 B) go global -> LDS through
+//     buffer_load_dwordx4 ... lds (no registers involved), one instruction moving 8 rows x 128 B
+//     (whole 128-byte lines); the copies of step s + 1 are spread over three phases of step s,
+//     into the buffer step s - 1 used, and each wave waits for its own copies before the barrier
+//     that ends step s;
+//   * LDS rows are 128 B; 16-byte chunk c of row r sits at position c ^ ((r >> 1) & 7). A
+//     ds_read_b128 serves 16 lanes at a time, here 16 consecutive rows at one K offset, and with
+//     this key they land in 16 different 16-byte slots of a 256-byte bank period (no conflicts);
+//   * the weight fragment is the MFMA's first operand, so a lane holds 4 consecutive output
+//     columns per 8-column group; lanes l and l + 32 swap halves (v_permlane32_swap) so that each
+//     lane owns 8 consecutive columns: residual loads and bf16 stores are 16 bytes;
+//   * the tile's scales, bias and gate are copied to LDS with the first step of each share part.
+// The copies are issued from inline assembly so that the compiler does not serialize LDS reads
+// behind them; every wait on them is explicit (s_waitcnt vmcnt).
 //
 // The FP8 GEMM with a fused epilogue follows the page "Accelerarea generarii de imagini cu
 // FLUX 3 Image Klein pe GPU-urile Blackwell NVIDIA" (paragraph after "Tabelul 1"); the 8-bit
@@ -39,11 +53,16 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 256, kBN = 256, kBK = 128;
-constexpr int kThreads = 256;
-constexpr int kStageBytes = (kBM + kBN) * kBK;  // 64 KiB
+constexpr int kThreads = 512;
+constexpr int kStageBytes = (kBM + kBN) * kBK;  // 64 KiB: A tile, then B tile
+constexpr int kParamBytes = 4096;               // sa f32[256] | sw f32[256] | bias | gate (1 KiB each)
+constexpr int kParamBufs = 3;                   // part i of a share uses buffer i % 3
 constexpr int kGroupM = 4;                      // tile rows per group in the tile order
+constexpr int kPartFloats = kBM * kBN;
 
 enum { EPI_BIAS = 0, EPI_GELU_TANH = 1, EPI_GATED_RESIDUAL = 2 };
 
@@ -56,7 +75,12 @@ struct Params {
   const uint16_t* gate;      // [N] (gated only)
   const uint16_t* residual;  // [M, N] (gated only; may equal out)
   uint16_t* out;             // [M, N]
-  int M, N, K, tilesM, tilesN;
+  uint32_t* flags;           // [tiles] arrival counters (cut tiles only)
+  float* part;               // [groups][2][256 * 256] partial tiles (cut tiles only)
+  int M, N, K, tilesM, tilesN, nk, tiles;
+  int split;                 // 1: the tiles from tail0 on are cut into equal shares of units
+  int tail0;                 // first cut tile (a multiple of the grid size)
+  int tail_units;            // (tiles - tail0) * nk
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -90,44 +114,158 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
-// All copies of this wavefront have landed (vmcnt = 0; lgkm and exp counters untouched).
-__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// At most 16 copies of this wavefront still in flight.
-__device__ __forceinline__ void wait_copies_16() { __builtin_amdgcn_s_waitcnt(0x4F70); }
+// All vector memory operations of this wavefront done (vmcnt = 0; lgkm and exp untouched).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// This wavefront's LDS reads done, then the workgroup barrier. The lgkmcnt wait goes through
-// the builtin so that the compiler's own wait bookkeeping sees it; the asm is a compiler-level
-// memory barrier as well.
-__device__ __forceinline__ void barrier() {
+// Phase boundary: this wavefront's LDS reads done, then the workgroup barrier. No instruction
+// is scheduled across it (the MFMAs of a phase must stay in their phase).
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0xC07F);
   asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-// ---------------------------------------------------------------------------------------------
-// main loop pieces
-// ---------------------------------------------------------------------------------------------
-
+__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kBK + ((chunk ^ (row & 7)) << 4);
+  return row * kBK + ((chunk ^ swz_key(row)) << 4);
 }
 
-// Wavefront w copies rows [64 w, 64 w + 64) of both tiles of one step: 8 + 8 instructions of
-// 8 rows x 128 B each. Lane l lands in LDS slot l of its 1 KiB block (row l >> 3, chunk
-// position l & 7), so it fetches global chunk (l & 7) ^ (row & 7).
-__device__ __forceinline__ void stage_copy(uint8_t* st, v4i ra, v4i rb, uint32_t voff, uint32_t K,
-                                           int wave) {
-  const uint32_t la = lds_addr(st) + (uint32_t)(wave * 64 * kBK);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t off = voff + (uint32_t)(j * 8) * K;
-    copy_to_lds(ra, off, __builtin_amdgcn_readfirstlane(la + j * 1024));
-    copy_to_lds(rb, off, __builtin_amdgcn_readfirstlane(la + kBM * kBK + j * 1024));
+// ---------------------------------------------------------------------------------------------
+// schedule: shares, tiles, contributors
+// ---------------------------------------------------------------------------------------------
+
+// Units (tile steps) of the cut tiles held by workgroups 0 .. v - 1.
+__device__ __forceinline__ int share_begin(const Params& p, int v, int G) {
+  return (int)(((int64_t)v * p.tail_units) / G);
+}
+
+// The workgroup whose share holds unit u of the cut tiles.
+__device__ __forceinline__ int share_owner(const Params& p, int u, int G) {
+  return (int)((((int64_t)u + 1) * G - 1) / p.tail_units);
+}
+
+// Workgroup v's work: `whole` whole tiles v, v + G, ..., then units [sk0, sk1) of the cut tiles.
+struct Share {
+  int whole, sk0, sk1;
+};
+
+__device__ __forceinline__ Share share_of(const Params& p, int v, int G) {
+  Share sh;
+  if (p.split) {
+    sh.whole = p.tail0 / G;
+    sh.sk0 = share_begin(p, v, G);
+    sh.sk1 = share_begin(p, v + 1, G);
+  } else {
+    sh.whole = (p.tiles - v + G - 1) / G;
+    sh.sk0 = sh.sk1 = 0;
+  }
+  return sh;
+}
+
+// Tile and step of workgroup-local step S.
+__device__ __forceinline__ void step_of(const Params& p, const Share& sh, int v, int G, int S,
+                                        int& t, int& k) {
+  const int dp = sh.whole * p.nk;
+  if (S < dp) {
+    const int i = S / p.nk;
+    t = v + i * G;
+    k = S - i * p.nk;
+  } else {
+    const int su = sh.sk0 + (S - dp);
+    const int tt = su / p.nk;
+    t = p.tail0 + tt;
+    k = su - tt * p.nk;
   }
 }
 
+__device__ __forceinline__ void tile_origin(const Params& p, int t, int& m0, int& n0) {
+  const int per_group = kGroupM * p.tilesN;
+  const int grp = t / per_group;
+  const int first_m = grp * kGroupM;
+  const int gsz = (p.tilesM - first_m) < kGroupM ? (p.tilesM - first_m) : kGroupM;
+  const int tin = t - grp * per_group;
+  m0 = (first_m + tin % gsz) * kBM;
+  n0 = (tin / gsz) * kBN;
+}
+
+struct TileDesc {
+  int m0, n0;
+  v4i rsA, rsB;
+};
+
+// per-tile descriptors: rows past M (N) are out of range and read as zero
+__device__ __forceinline__ TileDesc tile_desc(const Params& p, int t) {
+  TileDesc d;
+  tile_origin(p, t, d.m0, d.n0);
+  const uint32_t rowsA = (uint32_t)(p.M - d.m0 < kBM ? p.M - d.m0 : kBM);
+  const uint32_t rowsB = (uint32_t)(p.N - d.n0 < kBN ? p.N - d.n0 : kBN);
+  d.rsA = buffer_rsrc(p.A + (size_t)d.m0 * (size_t)p.K, rowsA * (uint32_t)p.K);
+  d.rsB = buffer_rsrc(p.B + (size_t)d.n0 * (size_t)p.K, rowsB * (uint32_t)p.K);
+  return d;
+}
+
+// ---------------------------------------------------------------------------------------------
+// copies
+// ---------------------------------------------------------------------------------------------
+
+// Rows 64q + 8j .. + 8 of one operand of step k into the stage (8 rows x 128 B at lds_block +
+// 1 KiB j). Lane l lands in LDS slot l of the block (row l >> 3, position l & 7), so it fetches
+// global chunk (l & 7) ^ key(row); the chunk offset differs between even and odd j by dodd.
+__device__ __forceinline__ void copy_rows(v4i rs, uint32_t K, int k, uint32_t lds_block,
+                                          uint32_t voff0, uint32_t dodd, int j) {
+  const uint32_t off = voff0 + (uint32_t)k * kBK + (uint32_t)(j * 8) * K + ((j & 1) ? dodd : 0u);
+  copy_to_lds(rs, off, __builtin_amdgcn_readfirstlane(lds_block + (uint32_t)(j * 1024)));
+}
+
+// The copies of one step, in three parts:
+//   part 0 (group 0): A rows 64q + 8j, j < 6;  part 1 (group 1): B rows 64q + 8j, j < 6;
+//   part 2 (group 0): A and B rows 64q + 48 + 8j, j < 2.
+__device__ __forceinline__ void copy_part(const TileDesc& d, uint32_t K, int k, uint8_t* st,
+                                          uint32_t voff0, uint32_t dodd, int q, int part) {
+  const uint32_t la = lds_addr(st) + (uint32_t)(q * 64 * kBK);
+  const uint32_t lb = la + (uint32_t)(kBM * kBK);
+  if (part == 0) {
+#pragma unroll
+    for (int j = 0; j < 6; ++j) copy_rows(d.rsA, K, k, la, voff0, dodd, j);
+  } else if (part == 1) {
+#pragma unroll
+    for (int j = 0; j < 6; ++j) copy_rows(d.rsB, K, k, lb, voff0, dodd, j);
+  } else {
+#pragma unroll
+    for (int j = 6; j < 8; ++j) {
+      copy_rows(d.rsA, K, k, la, voff0, dodd, j);
+      copy_rows(d.rsB, K, k, lb, voff0, dodd, j);
+    }
+  }
+}
+
+// The tile's epilogue parameters into param buffer pb, one copy per group-0 wave (q).
+template <int EPI>
+__device__ __forceinline__ void copy_params(const Params& p, const TileDesc& d, uint8_t* pb, int q,
+                                            int lane) {
+  const uint32_t lp = __builtin_amdgcn_readfirstlane(lds_addr(pb) + (uint32_t)(q * 1024));
+  const uint32_t lo = (uint32_t)lane * 16u;
+  const uint32_t rows = (uint32_t)(p.M - d.m0 < kBM ? p.M - d.m0 : kBM);
+  const uint32_t cols = (uint32_t)(p.N - d.n0 < kBN ? p.N - d.n0 : kBN);
+  if (q == 0) {
+    copy_to_lds(buffer_rsrc(p.sa + d.m0, rows * 4u), lo, lp);
+  } else if (q == 1) {
+    copy_to_lds(buffer_rsrc(p.sw + d.n0, cols * 4u), lo, lp);
+  } else if (q == 2) {
+    copy_to_lds(buffer_rsrc(p.bias + d.n0, p.bias ? cols * 2u : 0u), lo, lp);
+  } else if (EPI == EPI_GATED_RESIDUAL) {
+    copy_to_lds(buffer_rsrc(p.gate + d.n0, cols * 2u), lo, lp);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// fragments and MFMA
+// ---------------------------------------------------------------------------------------------
+
 struct Frags {
-  v8i a[4];
-  v8i b[4];
+  v8i a[4];  // rows wm * 128 + 32 i + (lane & 31) of the A tile
+  v8i b[2];  // rows wn * 64 + 32 i + (lane & 31) of the B tile
 };
 
 // Fragments of K half h (64 bytes) of one staged step: lane l reads row l & 31 of each 32-row
@@ -138,36 +276,29 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, Frags& f, int h, i
   const int c0 = h * 4 + (lane >> 5) * 2;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint8_t* bb = st + kBM * kBK + (wn * 128 + i * 32) * kBK;
+    const uint8_t* ab = st + (wm * 128 + i * 32) * kBK;
+    const uint4 lo = *reinterpret_cast<const uint4*>(ab + swz(r, c0));
+    const uint4 hi = *reinterpret_cast<const uint4*>(ab + swz(r, c0 + 1));
+    f.a[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                   (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint8_t* bb = st + kBM * kBK + (wn * 64 + i * 32) * kBK;
     const uint4 lo = *reinterpret_cast<const uint4*>(bb + swz(r, c0));
     const uint4 hi = *reinterpret_cast<const uint4*>(bb + swz(r, c0 + 1));
     f.b[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    const uint8_t* ab = st + (wm * 128 + i * 32) * kBK;
-    const uint4 lo2 = *reinterpret_cast<const uint4*>(ab + swz(r, c0));
-    const uint4 hi2 = *reinterpret_cast<const uint4*>(ab + swz(r, c0 + 1));
-    f.a[i] = (v8i){(int)lo2.x, (int)lo2.y, (int)lo2.z, (int)lo2.w,
-                   (int)hi2.x, (int)hi2.y, (int)hi2.z, (int)hi2.w};
   }
 }
 
-__device__ __forceinline__ void mma16(const Frags& f, v16f (&acc)[4][4]) {
+__device__ __forceinline__ void mma8(const Frags& f, v16f (&acc)[2][4]) {
 #pragma unroll
-  for (int bn = 0; bn < 4; ++bn)
+  for (int bn = 0; bn < 2; ++bn)
 #pragma unroll
     for (int bm = 0; bm < 4; ++bm)
       acc[bn][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[bn], f.a[bm], acc[bn][bm],
                                                                      0, 0, 0, 0, 0, 0);
-}
-
-// Schedule: two LDS fragment reads under each of the first eight MFMAs, then the other eight.
-__device__ __forceinline__ void reads_under_mfma() {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -177,11 +308,9 @@ __device__ __forceinline__ void reads_under_mfma() {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two fp32 -> packed bf16, round to nearest even (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, bf2));
 }
 
 // 0.5 v (1 + tanh(u)) = v / (1 + exp(-2u)), u = sqrt(2/pi) (v + 0.044715 v^3); the exponential
@@ -201,15 +330,16 @@ __device__ __forceinline__ void swap_halves(float& a, float& b) {
   b = __uint_as_float(r[1]);
 }
 
-// The tile's scales, bias and gate are staged in LDS (one round trip for the workgroup). Then,
-// per pair of 8-column groups, each lane computes v for its 4 + 4 columns, swaps halves with
-// its partner lane (l <-> l + 32) so that it holds 8 consecutive columns of one group, applies
-// the activation or the gated residual there, and stores 16 bytes.
+// Per pair of 8-column groups, each lane computes v for its 4 + 4 columns, swaps halves with its
+// partner lane (l <-> l + 32) so that it holds 8 consecutive columns of one group, applies the
+// activation or the gated residual there, and stores 16 bytes.
 template <int EPI>
-__device__ __forceinline__ void epilogue(const v16f (&acc)[4][4], const Params& p, int m0, int n0,
-                                         int wm, int wn, int lane, const float* s_sa,
-                                         const float* s_sw, const uint16_t* s_b,
-                                         const uint16_t* s_g) {
+__device__ __forceinline__ void epilogue(const v16f (&acc)[2][4], const Params& p, int m0, int n0,
+                                         int wm, int wn, int lane, const uint8_t* pb) {
+  const float* s_sa = reinterpret_cast<const float*>(pb);
+  const float* s_sw = reinterpret_cast<const float*>(pb + 1024);
+  const uint16_t* s_b = reinterpret_cast<const uint16_t*>(pb + 2048);
+  const uint16_t* s_g = reinterpret_cast<const uint16_t*>(pb + 3072);
   const int hi = lane >> 5;
 #pragma unroll
   for (int bm = 0; bm < 4; ++bm) {
@@ -217,14 +347,14 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[4][4], const Params& 
     const int m = m0 + ml;
     const float sam = s_sa[ml];
 #pragma unroll
-    for (int bn = 0; bn < 4; ++bn) {
+    for (int bn = 0; bn < 2; ++bn) {
 #pragma unroll
       for (int gp = 0; gp < 2; ++gp) {
         float v[2][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int g = gp * 2 + h;
-          const int nl = wn * 128 + bn * 32 + g * 8 + hi * 4;
+          const int nl = wn * 64 + bn * 32 + g * 8 + hi * 4;
           const float4 swv = *reinterpret_cast<const float4*>(s_sw + nl);
           const uint2 bb = *reinterpret_cast<const uint2*>(s_b + nl);
           v[h][0] = fmaf(acc[bn][bm][g * 4 + 0] * sam, swv.x, bf16_lo(bb.x));
@@ -237,7 +367,7 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[4][4], const Params& 
         // (v[0] = columns 0-3, v[1] = columns 4-7) and lane l + 32 owns group 2gp + 1.
 #pragma unroll
         for (int j = 0; j < 4; ++j) swap_halves(v[0][j], v[1][j]);
-        const int nl = wn * 128 + bn * 32 + (gp * 2 + hi) * 8;
+        const int nl = wn * 64 + bn * 32 + (gp * 2 + hi) * 8;
         const int n = n0 + nl;
         float y[8] = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
         if (EPI == EPI_GELU_TANH) {
@@ -259,10 +389,10 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[4][4], const Params& 
           }
         }
         uint4 o;
-        o.x = f32_to_bf16(y[0]) | (f32_to_bf16(y[1]) << 16);
-        o.y = f32_to_bf16(y[2]) | (f32_to_bf16(y[3]) << 16);
-        o.z = f32_to_bf16(y[4]) | (f32_to_bf16(y[5]) << 16);
-        o.w = f32_to_bf16(y[6]) | (f32_to_bf16(y[7]) << 16);
+        o.x = pack_bf16(y[0], y[1]);
+        o.y = pack_bf16(y[2], y[3]);
+        o.z = pack_bf16(y[4], y[5]);
+        o.w = pack_bf16(y[6], y[7]);
         if (live) *reinterpret_cast<uint4*>(p.out + off) = o;
       }
     }
@@ -270,103 +400,216 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[4][4], const Params& 
 }
 
 // ---------------------------------------------------------------------------------------------
+// split tiles
+// ---------------------------------------------------------------------------------------------
+
+// Partial tiles live in a 128 MiB region addressed through one buffer descriptor; their loads
+// and stores carry the device-coherence bit (sc1), so they are seen across XCDs without
+// flushing or invalidating caches.
+constexpr int kCoherent = 16;  // sc1
+
+// A wave's 128 accumulators into partial tile `slot` (byte offset): wave-major, then 4-register
+// groups, then lanes, so that every store moves 1 KiB contiguous.
+__device__ __forceinline__ void store_part(const v16f (&acc)[2][4], __amdgpu_buffer_rsrc_t rs,
+                                           uint32_t slot, int wave, int lane) {
+  const uint32_t base = slot + (uint32_t)(wave * 32 * 64 + lane) * 16u;
+#pragma unroll
+  for (int g4 = 0; g4 < 32; ++g4) {
+    const int blk = g4 >> 2, e = (g4 & 3) * 4;
+    const v16f& a = acc[blk >> 2][blk & 3];
+    const v4i x = (v4i){__float_as_int(a[e]), __float_as_int(a[e + 1]), __float_as_int(a[e + 2]),
+                        __float_as_int(a[e + 3])};
+    __builtin_amdgcn_raw_buffer_store_b128(x, rs, base + (uint32_t)g4 * 1024u, 0, kCoherent);
+  }
+}
+
+// acc (+)= partial tile `slot`, four 4-register groups at a time so that few loads are in flight.
+template <bool FIRST>
+__device__ __forceinline__ void add_part(v16f (&acc)[2][4], __amdgpu_buffer_rsrc_t rs,
+                                         uint32_t slot, int wave, int lane) {
+  const uint32_t base = slot + (uint32_t)(wave * 32 * 64 + lane) * 16u;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    v4i x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      x[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, base + (uint32_t)(c * 4 + i) * 1024u, 0,
+                                                   kCoherent);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g4 = c * 4 + i;
+      const int blk = g4 >> 2, e = (g4 & 3) * 4;
+      v16f& a = acc[blk >> 2][blk & 3];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float y = __int_as_float(x[i][j]);
+        a[e + j] = FIRST ? y : a[e + j] + y;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Byte offset of workgroup c's partial tile (slot 0: the first tile its share cuts, 1: the last).
+__device__ __forceinline__ uint32_t part_slot(int c, int slot) {
+  return ((uint32_t)c * 2u + (uint32_t)slot) * (uint32_t)(kPartFloats * 4);
+}
+
+// This workgroup's part of cut tile t is in acc (both groups are done with its MFMAs). Store it
+// and count its arrival. The last part to arrive loads all parts, in workgroup order, into acc
+// and clears the tile's counter for the next call; it returns true and the caller applies the
+// epilogue.
+__device__ bool finish_split(v16f (&acc)[2][4], const Params& p, int t, int v, int G,
+                             const Share& sh, int wave, int lane, int* s_last) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      p.part, 0, (int)(2u * (uint32_t)kPartFloats * 4u * 256u), 0x00020000);
+  const int first_cut = p.tail0 + sh.sk0 / p.nk;
+  store_part(acc, rs, part_slot(v, t == first_cut ? 0 : 1), wave, lane);
+  wait_vmem();
+  phase_barrier();  // every wave's part is stored
+  const int tt = t - p.tail0;
+  const int vlo = share_owner(p, tt * p.nk, G);
+  const int vhi = share_owner(p, tt * p.nk + p.nk - 1, G);
+  if (threadIdx.x == 0) {
+    const uint32_t old =
+        __hip_atomic_fetch_add(p.flags + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_last = old == (uint32_t)(vhi - vlo);
+  }
+  phase_barrier();
+  if (!*s_last) return false;
+  for (int c = vlo; c <= vhi; ++c) {
+    const int slot = (t == p.tail0 + share_begin(p, c, G) / p.nk) ? 0 : 1;
+    if (c == vlo)
+      add_part<true>(acc, rs, part_slot(c, slot), wave, lane);
+    else
+      add_part<false>(acc, rs, part_slot(c, slot), wave, lane);
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(p.flags + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+// ---------------------------------------------------------------------------------------------
 // kernel
 // ---------------------------------------------------------------------------------------------
 
-__device__ __forceinline__ void tile_origin(const Params& p, int& m0, int& n0) {
-  const int T = p.tilesM * p.tilesN;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, loc = bid >> 3;
-  const int per = T >> 3, rem = T & 7;
-  const int t = xcd * per + (xcd < rem ? xcd : rem) + loc;
-  const int per_group = kGroupM * p.tilesN;
-  const int grp = t / per_group;
-  const int first_m = grp * kGroupM;
-  const int gsz = (p.tilesM - first_m) < kGroupM ? (p.tilesM - first_m) : kGroupM;
-  const int tin = t - grp * per_group;
-  m0 = (first_m + tin % gsz) * kBM;
-  n0 = (tin / gsz) * kBN;
-}
-
 template <int EPI>
-__global__ void __launch_bounds__(kThreads) gemm_fp8_256x256(Params p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes];
+__global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes + kParamBufs * kParamBytes];
+  __shared__ int s_last;
+  uint8_t* pbuf = lds + 2 * kStageBytes;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  int m0, n0;
-  tile_origin(p, m0, n0);
-
-  // per-tile descriptors: rows past M (N) are out of range and read as zero
-  const uint32_t rowsA = (uint32_t)(p.M - m0 < kBM ? p.M - m0 : kBM);
-  const uint32_t rowsB = (uint32_t)(p.N - n0 < kBN ? p.N - n0 : kBN);
-  const v4i rsA = buffer_rsrc(p.A + (size_t)m0 * (size_t)p.K, rowsA * (uint32_t)p.K);
-  const v4i rsB = buffer_rsrc(p.B + (size_t)n0 * (size_t)p.K, rowsB * (uint32_t)p.K);
-  const int lr = lane >> 3;
-  const uint32_t voff0 =
-      (uint32_t)(wave * 64 + lr) * (uint32_t)p.K + (uint32_t)(((lane & 7) ^ (lr & 7)) * 16);
+  const int g = wave >> 2, q = wave & 3;
+  const int wm = q >> 1, wn = (q & 1) * 2 + g;
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+  const int v = (G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b;
+  const int nk = p.nk;
+  const Share sh = share_of(p, v, G);
+  const int nsteps = sh.whole * nk + (sh.sk1 - sh.sk0);
+  const int dp = sh.whole * nk;
   const uint32_t uK = (uint32_t)p.K;
-  const int nk = p.K / kBK;
 
-  v16f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
-  Frags f0, f1;
+  // copy addressing of this lane: rows 64q + (lane >> 3) + 8j, chunk position lane & 7
+  const int row0 = q * 64 + (lane >> 3);
+  const uint32_t cE = (uint32_t)((lane & 7) ^ swz_key(row0));
+  const uint32_t cO = (uint32_t)((lane & 7) ^ swz_key(row0 + 8));
+  const uint32_t voff0 = (uint32_t)row0 * uK + cE * 16u;
+  const uint32_t dodd = (cO - cE) * 16u;  // added (mod 2^32) for odd j
 
-  stage_copy(lds, rsA, rsB, voff0, uK, wave);
-  if (nk > 1) {
-    stage_copy(lds + kStageBytes, rsA, rsB, voff0 + kBK, uK, wave);
-    wait_copies_16();  // step 0 landed, step 1 may still be in flight
+  // first step, with its tile's parameters
+  int t0, k0s;
+  step_of(p, sh, v, G, 0, t0, k0s);
+  TileDesc nd = tile_desc(p, t0);
+  if (g == 0) {
+    copy_part(nd, uK, k0s, lds, voff0, dodd, q, 0);
+    copy_part(nd, uK, k0s, lds, voff0, dodd, q, 2);
+    copy_params<EPI>(p, nd, pbuf, q, lane);
   } else {
-    wait_copies();
+    copy_part(nd, uK, k0s, lds, voff0, dodd, q, 1);
   }
-  barrier();
-  read_frags(lds, f0, 0, wm, wn, lane);
+  wait_vmem();
+  phase_barrier();
+  if (g == 1) phase_barrier();  // group 1 runs one phase behind
 
-  int s = 0;
-  for (; s + 1 < nk; ++s) {
-    uint8_t* cur = lds + (s & 1) * kStageBytes;
-    uint8_t* nxt = lds + ((s + 1) & 1) * kStageBytes;
-    read_frags(cur, f1, 1, wm, wn, lane);  // MMA on K half (s, 0) while reading (s, 1)
-    mma16(f0, acc);
-    reads_under_mfma();
-    wait_copies();                         // step s + 1 landed (the only copy in flight)
-    barrier();                             // for every wavefront; step s fully read
-    if (s + 2 < nk) stage_copy(cur, rsA, rsB, voff0 + (uint32_t)(s + 2) * kBK, uK, wave);
-    read_frags(nxt, f0, 0, wm, wn, lane);  // MMA on K half (s, 1) while reading (s + 1, 0)
-    mma16(f1, acc);
-    reads_under_mfma();
+  Frags f;
+  int S = 0;     // steps done; step S is in stage buffer S & 1
+  int part = 0;  // parts (runs of steps of one tile) done; part i's parameters in buffer i % 3
+  while (S < nsteps) {
+    int t, k0;
+    step_of(p, sh, v, G, S, t, k0);
+    const int len = S < dp ? nk : ((nk - k0) < (nsteps - S) ? nk - k0 : nsteps - S);
+    v16f acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
+    for (int j = 0; j < len; ++j, ++S) {
+      const uint8_t* st = lds + (S & 1) * kStageBytes;
+      uint8_t* st1 = lds + ((S + 1) & 1) * kStageBytes;
+      const bool more = S + 1 < nsteps;
+      int tn = t, kn = 0;
+      if (more) step_of(p, sh, v, G, S + 1, tn, kn);
+      const bool starts = more && (j + 1 == len);  // step S + 1 begins the next part
+      if (starts) nd = tile_desc(p, tn);
+      // phase A (G0: reads K half 0 | G1: MFMAs of the previous half)
+      if (more) copy_part(nd, uK, kn, st1, voff0, dodd, q, g);
+      read_frags(st, f, 0, wm, wn, lane);
+      phase_barrier();
+      // phase B (G0: MFMAs of K half 0 | G1: reads K half 0)
+      mma8(f, acc);
+      phase_barrier();
+      // phase C (G0: reads K half 1 | G1: MFMAs of K half 0)
+      if (more && g == 0) {
+        copy_part(nd, uK, kn, st1, voff0, dodd, q, 2);
+        if (starts) copy_params<EPI>(p, nd, pbuf + ((part + 1) % kParamBufs) * kParamBytes, q, lane);
+      }
+      read_frags(st, f, 1, wm, wn, lane);
+      if (g == 1) wait_vmem();  // group 1's copies of step S + 1 landed
+      phase_barrier();
+      // phase D (G0: MFMAs of K half 1 | G1: reads K half 1)
+      mma8(f, acc);
+      if (g == 0) wait_vmem();  // group 0's copies of step S + 1 landed
+      phase_barrier();
+    }
+    const bool cut = len != nk;
+    bool write = true;
+    if (cut) {
+      if (g == 0) phase_barrier();  // group 1's last MFMAs of this part are done
+      write = finish_split(acc, p, t, v, G, sh, wave, lane, &s_last);
+    }
+    if (write) {
+      int m0, n0;
+      tile_origin(p, t, m0, n0);
+      epilogue<EPI>(acc, p, m0, n0, wm, wn, lane, pbuf + (part % kParamBufs) * kParamBytes);
+    }
+    if (cut && g == 1) phase_barrier();  // back to one phase behind
+    ++part;
   }
-  read_frags(lds + (s & 1) * kStageBytes, f1, 1, wm, wn, lane);
-  mma16(f0, acc);
-  reads_under_mfma();
-  mma16(f1, acc);
-
-  // epilogue parameters of this tile, staged in the (now free) LDS
-  barrier();
-  float* s_sa = reinterpret_cast<float*>(lds);
-  float* s_sw = s_sa + kBM;
-  uint16_t* s_b = reinterpret_cast<uint16_t*>(s_sw + kBN);
-  uint16_t* s_g = s_b + kBN;
-  {
-    const int m = m0 + tid, n = n0 + tid;
-    s_sa[tid] = m < p.M ? p.sa[m] : 0.f;
-    s_sw[tid] = n < p.N ? p.sw[n] : 0.f;
-    s_b[tid] = (p.bias && n < p.N) ? p.bias[n] : (uint16_t)0;
-    if (EPI == EPI_GATED_RESIDUAL) s_g[tid] = n < p.N ? p.gate[n] : (uint16_t)0;
-  }
-  __syncthreads();
-  epilogue<EPI>(acc, p, m0, n0, wm, wn, lane, s_sa, s_sw, s_b, s_g);
+  if (g == 0) phase_barrier();  // matches group 1's extra barrier
 }
 
 template <int EPI>
-hipError_t launch_epi(const Params& p, hipStream_t stream) {
-  const int T = p.tilesM * p.tilesN;
-  hipLaunchKernelGGL(gemm_fp8_256x256<EPI>, dim3(T), dim3(kThreads), 0, stream, p);
+hipError_t launch_epi(const Params& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(gemm_fp8_pp<EPI>, dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+// Compute units of the current device, queried once per device.
+int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    __atomic_store_n(&cached[dev], n, __ATOMIC_RELAXED);
+  }
+  return n;
 }
 
 }  // namespace
@@ -374,7 +617,7 @@ hipError_t launch_epi(const Params& p, hipStream_t stream) {
 hipError_t launch_linear(const uint8_t* q, const float* scale, int64_t M, int64_t K,
                          const uint8_t* qw, const float* w_scale, int64_t N, const uint16_t* bias,
                          int epilogue, const uint16_t* gate, const uint16_t* residual,
-                         uint16_t* out, hipStream_t stream) {
+                         uint16_t* out, void* workspace, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   Params p;
   p.A = q;
@@ -388,12 +631,40 @@ hipError_t launch_linear(const uint8_t* q, const float* scale, int64_t M, int64_
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
-  p.tilesM = (p.M + kBM - 1) / kBM;
-  p.tilesN = (p.N + kBN - 1) / kBN;
+  p.tilesM = (int)((M + kBM - 1) / kBM);
+  p.tilesN = (int)((N + kBN - 1) / kBN);
+  p.nk = (int)(K / kBK);
+  p.tiles = (int)linear_tiles(M, N);
+  const int64_t units = linear_units(M, K, N);
+  const int cus = compute_units();
+  // Whole tiles keep every workgroup of an XCD at the same K offset, so an A or B slice fetched
+  // once is reused from L2; cut tiles lose that sharing. Tiles are cut only where whole tiles
+  // would leave most compute units idle: when a workgroup's whole-tile load is at least twice
+  // its equal share plus a few steps (few tiles, long K).
+  const int64_t whole_grid = p.tiles < cus ? p.tiles : cus;
+  const int64_t whole_steps = (p.tiles + whole_grid - 1) / whole_grid * p.nk;
+  const int64_t split_grid = split_groups(units) < cus ? split_groups(units) : cus;
+  const int64_t split_steps = (units + split_grid - 1) / split_grid;
+  int grid;
+  if (workspace && whole_steps >= 2 * split_steps + 16) {
+    grid = (int)split_grid;
+    p.split = 1;
+    p.tail0 = 0;
+    p.tail_units = p.tiles * p.nk;
+    p.part = static_cast<float*>(workspace);
+    p.flags = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + kPartRegion);
+  } else {
+    grid = (int)whole_grid;
+    p.split = 0;
+    p.tail0 = p.tiles;
+    p.tail_units = 0;
+    p.part = nullptr;
+    p.flags = nullptr;
+  }
   switch (epilogue) {
-    case EPI_BIAS: return launch_epi<EPI_BIAS>(p, stream);
-    case EPI_GELU_TANH: return launch_epi<EPI_GELU_TANH>(p, stream);
-    default: return launch_epi<EPI_GATED_RESIDUAL>(p, stream);
+    case EPI_BIAS: return launch_epi<EPI_BIAS>(p, grid, stream);
+    case EPI_GELU_TANH: return launch_epi<EPI_GELU_TANH>(p, grid, stream);
+    default: return launch_epi<EPI_GATED_RESIDUAL>(p, grid, stream);
   }
 }
 

@@ -31,12 +31,14 @@
  *     returns a nonzero DQ_ERR_* code and enqueues nothing. A failed kernel launch returns
  *     DQ_ERR_HIP and the HIP error code can be read with dq_last_hip_error(). Faults inside a
  *     kernel surface at the caller's next synchronization, as for any HIP kernel.
- *   - Calls are thread-safe; the library keeps no per-call state.
+ *   - Calls are thread-safe; the library keeps no per-call state (a workspace passed to
+ *     dq_linear_fp8 is the caller's, see there).
  *   - M = 0 is valid and enqueues nothing.
  */
 #ifndef DQ_H
 #define DQ_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -51,7 +53,8 @@ enum {
   DQ_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
   DQ_ERR_ALIAS = 4,     /* an output overlaps an input (other than out == residual) */
   DQ_ERR_EPILOGUE = 5,  /* unknown epilogue, or gate/residual missing for the gated one */
-  DQ_ERR_HIP = 6        /* a HIP runtime call failed; see dq_last_hip_error() */
+  DQ_ERR_HIP = 6,       /* a HIP runtime call failed; see dq_last_hip_error() */
+  DQ_ERR_WORKSPACE = 7  /* workspace too small or not 256-byte aligned */
 };
 
 /* Epilogues of dq_linear_fp8 (v = acc * scale[m] * w_scale[n] + bias[n]). */
@@ -105,15 +108,41 @@ int dq_quantize_weight_fp8(const void* w, int64_t N, int64_t K, void* qw, float*
  *   residual  bf16 [M, N]    required iff epilogue == DQ_EPI_GATED_RESIDUAL, else ignored;
  *                            may be the same pointer as out (in-place residual update)
  *   out       bf16 [M, N]    output
+ *   workspace                NULL (workspace_bytes ignored), or device memory of at least
+ *                            dq_linear_fp8_workspace_size(M, K, N) bytes, 256-byte aligned,
+ *                            overlapping no other argument
  *   acc[m,n] = sum_k dec(q[m,k]) * dec(qw[n,k]) accumulated by the FP8 matrix units into fp32;
  *   v = acc * scale[m] * w_scale[n] + bias[n], then the epilogue, rounded once to bf16 (nearest
  *   even).
+ *
+ * Work split: the output is cut into 256 x 256 tiles and each tile's K range into steps of 128.
+ * Without a workspace every workgroup computes whole tiles. With one, the library may instead
+ * give every workgroup an equal share of all tile-steps when whole tiles would leave most
+ * compute units idle (few tiles, long K): a tile is then split between workgroups, each part
+ * is summed in fp32 into the workspace and the last part to finish adds them up (in a fixed
+ * order, so the result does not depend on timing) and applies the epilogue.
+ * The workspace must hold zeros before its first use. Its layout is the same for every problem
+ * (the partial tiles first, then one arrival counter per tile), and every call that completes
+ * leaves all counters at zero again, so one zero fill at allocation is enough and one workspace
+ * serves calls of any size in turn. Calls that may run concurrently (other streams, overlapping
+ * graph nodes) must not share a workspace.
+ *
  * Requirements: 0 <= M < 2^31, 128 <= K < 2^24 with K % 128 == 0, 64 <= N < 2^31 with
- * N % 64 == 0, all pointers 16-byte aligned, out overlapping no input except out == residual.
+ * N % 64 == 0, all tensor pointers 16-byte aligned, out overlapping no input except
+ * out == residual.
  */
 int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const void* qw,
                   const float* w_scale, int64_t N, const void* bias, int epilogue,
-                  const void* gate, const void* residual, void* out, void* stream);
+                  const void* gate, const void* residual, void* out, void* workspace,
+                  uint64_t workspace_bytes, void* stream);
+
+/*
+ * dq_linear_fp8_workspace_size -- bytes of workspace dq_linear_fp8 uses for an M x K -> N
+ * problem (the same on every device), or 0 if the sizes break dq_linear_fp8's requirements:
+ * 128 MiB of partial tiles plus 4 bytes per 256 x 256 output tile, rounded up to 256 bytes.
+ * Needs no GPU.
+ */
+uint64_t dq_linear_fp8_workspace_size(int64_t M, int64_t K, int64_t N);
 
 /* Static English text for a status code (never NULL). */
 const char* dq_status_string(int status);
@@ -121,7 +150,7 @@ const char* dq_status_string(int status);
 /* The hipError_t behind the most recent DQ_ERR_HIP returned on the calling thread (0 if none). */
 int dq_last_hip_error(void);
 
-/* ABI version of this header (currently 1). */
+/* ABI version of this header (currently 2). */
 int dq_abi_version(void);
 
 #ifdef __cplusplus

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dq.h")
 LIB = os.path.join(ROOT, "fp8_dynamic_quant_amd", "libdq.so")
 
-OK, NULL, SHAPE, ALIGN, ALIAS, EPI, HIP = range(7)
+OK, NULL, SHAPE, ALIGN, ALIAS, EPI, HIP, WORKSPACE = range(8)
 BIAS, GELU, GATED = 0, 1, 2
 
 
@@ -24,7 +24,10 @@ def lib():
     i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     L.dq_quantize_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
     L.dq_quantize_weight_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
-    L.dq_linear_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp]
+    L.dq_linear_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp,
+                                ctypes.c_uint64, vp]
+    L.dq_linear_fp8_workspace_size.argtypes = [i64, i64, i64]
+    L.dq_linear_fp8_workspace_size.restype = ctypes.c_uint64
     L.dq_status_string.restype = ctypes.c_char_p
     L.dq_status_string.argtypes = [i32]
     return L
@@ -38,7 +41,8 @@ def _declared():
 def test_header_declares_the_three_entry_points():
     names = _declared()
     for n in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
-              "dq_status_string", "dq_last_hip_error", "dq_abi_version"):
+              "dq_linear_fp8_workspace_size", "dq_status_string", "dq_last_hip_error",
+              "dq_abi_version"):
         assert n in names
 
 
@@ -48,8 +52,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dq_abi_version() == 1
-    for st in range(7):
+    assert lib.dq_abi_version() == 2
+    for st in range(8):
         s = lib.dq_status_string(st)
         assert s and len(s) > 1
     assert lib.dq_status_string(12345) == b"unknown status"
@@ -88,9 +92,13 @@ def test_quantize_adjacent_buffers_are_not_aliases(lib):
 Aq, As, Wq, Ws, Bi, Ga, Re, Ou = (0x1000000 * i for i in range(1, 9))
 
 
+Wk = 0x9000000                                             # fake workspace, 256-byte aligned
+
+
 def lin(lib, M=64, K=256, N=128, q=Aq, sa=As, qw=Wq, sw=Ws, bias=Bi, epi=BIAS, gate=Ga,
-        res=Re, out=Ou):
-    return lib.dq_linear_fp8(q, sa, M, K, qw, sw, N, bias, epi, gate, res, out, None)
+        res=Re, out=Ou, ws=None, ws_bytes=0):
+    return lib.dq_linear_fp8(q, sa, M, K, qw, sw, N, bias, epi, gate, res, out, ws, ws_bytes,
+                             None)
 
 
 def test_linear_argument_checks(lib):
@@ -123,6 +131,31 @@ def test_linear_argument_checks(lib):
     assert lin(lib, epi=GATED, out=Re + 64) == ALIAS         # partial overlap with residual
 
 
+def test_workspace_size(lib):
+    size = lib.dq_linear_fp8_workspace_size
+    # a fixed region of 256 x 2 partial 256 x 256 fp32 tiles, then one 4-byte counter per
+    # 256 x 256 output tile, rounded up to 256 bytes
+    parts = 256 * 2 * 256 * 256 * 4
+    assert size(4608, 3072, 12288) == parts + 3584                # 18 x 48 tiles
+    assert size(64, 256, 512) == parts + 256                      # 2 tiles
+    assert size(512, 12288, 3072) == parts + 256                  # 24 tiles
+    assert size(16896, 3072, 12288) == parts + 12800              # 66 x 48 tiles, 12672 B
+    assert size(64, 192, 512) == 0                                # K % 128
+    assert size(64, 256, 96) == 0                                 # N % 64
+    assert size(-1, 256, 512) == 0
+    assert size(0, 256, 512) == parts                             # empty problems are valid
+
+
+def test_linear_workspace_checks(lib):
+    need = lib.dq_linear_fp8_workspace_size(64, 256, 128)
+    assert lin(lib, ws=Wk, ws_bytes=need - 1) == WORKSPACE
+    assert lin(lib, ws=Wk + 16, ws_bytes=need) == WORKSPACE      # not 256-byte aligned
+    assert lin(lib, ws=Aq, ws_bytes=need) == ALIAS               # workspace over the codes
+    assert lin(lib, ws=Ou, ws_bytes=need) == ALIAS               # workspace over the output
+    assert lin(lib, ws=Wk, ws_bytes=need, q=None) == NULL
+    assert lin(lib, M=0, ws=Wk, ws_bytes=0) == OK                # empty: nothing is checked
+
+
 def test_last_hip_error_untouched_by_argument_errors(lib):
     assert lin(lib, K=100) == SHAPE
     assert lib.dq_last_hip_error() == 0
@@ -130,9 +163,11 @@ def test_last_hip_error_untouched_by_argument_errors(lib):
 
 def test_python_binding_names_match_the_c_entry_points():
     import fp8_dynamic_quant_amd as dq
-    for name in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8"):
+    for name in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
+                 "dq_linear_fp8_workspace_size"):
         assert callable(getattr(dq, name))
-    assert dq.lib().dq_abi_version() == 1
+    assert dq.lib().dq_abi_version() == 2
+    assert dq.dq_linear_fp8_workspace_size(4608, 3072, 12288) == 3584 + 256 * 2 * 262144
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -35,23 +35,28 @@ def _bits_of(ref64):
     return (round_to_bf16(ref64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
-def _run_linear(q, sa, qw, sw, bias, epi, gate=None, residual=None, inplace=False):
+WS = ("auto", None)   # tile-sharing schedule through a workspace, and whole tiles only
+PART_REGION = 256 * 2 * 256 * 256 * 4   # workspace bytes before the per-tile arrival counters
+
+
+def _run_linear(q, sa, qw, sw, bias, epi, gate=None, residual=None, inplace=False, ws="auto"):
     """q, qw uint8; sa, sw float32; bias/gate/residual bf16 bit patterns (or None)."""
     tq, tsa, tqw, tsw = u8_to_dev(q), f32_to_dev(sa), u8_to_dev(qw), f32_to_dev(sw)
     tb = None if bias is None else bf16_to_dev(bias)
     tg = None if gate is None else bf16_to_dev(gate)
     tr = None if residual is None else bf16_to_dev(residual)
     out = tr if inplace else None
-    o = dq.dq_linear_fp8(tq, tsa, tqw, tsw, tb, epi, tg, tr, out=out)
+    o = dq.dq_linear_fp8(tq, tsa, tqw, tsw, tb, epi, tg, tr, out=out, workspace=ws)
     torch.cuda.synchronize()
     return o
 
 
-def _end_to_end(shape: LinearShape, seed, index=0, rows=None, inplace=False):
+def _end_to_end(shape: LinearShape, seed, index=0, rows=None, inplace=False, ws="auto"):
     """Quantize x and W on the GPU, run the linear on the GPU; compare codes/scales exactly and
     the outputs (all rows, or the sampled `rows`) within tolerance."""
     inp = make_linear_inputs(shape, seed, index)
-    announce(f"linear {shape.name} M={shape.M} K={shape.K} N={shape.N} epi={shape.epilogue}")
+    announce(f"linear {shape.name} M={shape.M} K={shape.K} N={shape.N} epi={shape.epilogue} "
+             f"workspace={ws}")
     tx, tw = bf16_to_dev(inp.x), bf16_to_dev(inp.w)
     q, sa = dq.dq_quantize_fp8(tx)
     qw, sw = dq.dq_quantize_weight_fp8(tw)
@@ -60,7 +65,7 @@ def _end_to_end(shape: LinearShape, seed, index=0, rows=None, inplace=False):
     if shape.epilogue == "gated_residual":
         tg, tr = bf16_to_dev(inp.gate), bf16_to_dev(inp.residual)
     out = dq.dq_linear_fp8(q, sa, qw, sw, tb, shape.epilogue, tg, tr,
-                           out=tr if inplace else None)
+                           out=tr if inplace else None, workspace=ws)
     torch.cuda.synchronize()
     del tx, tw
     rows = np.arange(shape.M) if rows is None else np.asarray(rows)
@@ -79,21 +84,33 @@ def _end_to_end(shape: LinearShape, seed, index=0, rows=None, inplace=False):
     return assert_within_tolerance(got, ref, what=f"{shape.name} {shape.epilogue}")
 
 
+@pytest.mark.parametrize("ws", WS)
 @pytest.mark.parametrize("epi", EPIS)
-def test_tiny_workload_all_epilogues(epi):
+def test_tiny_workload_all_epilogues(epi, ws):
     w = workload("tiny-64x256x512")
     base = w.linears[0]
     shape = LinearShape(base.name, base.M, base.K, base.N, epi, base.n_outliers,
                         base.outlier_factor)
-    _end_to_end(shape, w.seed)
+    _end_to_end(shape, w.seed, ws=ws)
 
 
 @pytest.mark.parametrize("M,K,N", [(300, 384, 320), (257, 128, 64), (1, 128, 64), (5, 256, 192),
                                    (513, 640, 576), (64, 3072, 512), (700, 1152, 1088)])
 @pytest.mark.parametrize("epi", EPIS)
-def test_tiles_and_ragged_tails(M, K, N, epi):
+@pytest.mark.parametrize("ws", WS)
+def test_tiles_and_ragged_tails(M, K, N, epi, ws):
     shape = LinearShape(f"ragged{M}x{K}x{N}", M, K, N, epi, max(1, K // 100), 30.0)
-    _end_to_end(shape, seed=1000 + M + K + N)
+    _end_to_end(shape, seed=1000 + M + K + N, ws=ws)
+
+
+@pytest.mark.parametrize("M,K,N", [(256, 8192, 256), (40, 4096, 192), (600, 5120, 448),
+                                   (256, 6400, 768)])
+def test_tiles_shared_by_many_workgroups(M, K, N):
+    """Few tiles and a long K: with a workspace each tile is cut into many parts (16 for one
+    tile of 64 steps) that the last arriving part sums; with 3 tiles of 50 steps over 37
+    workgroups, shares also straddle tile boundaries (a part at each end)."""
+    shape = LinearShape(f"split{M}x{K}x{N}", M, K, N, "gated_residual", K // 100, 30.0)
+    _end_to_end(shape, seed=2000 + M + K + N, ws="auto")
 
 
 def test_gated_in_place_equals_out_of_place():
@@ -122,9 +139,12 @@ def _narrow_codes(rng, shape):
     return (sign | (exp_field << 3) | mant).astype(np.uint8)
 
 
-@pytest.mark.parametrize("epi", ["bias", "gated_residual"])
-@pytest.mark.parametrize("M,K,N", [(256, 256, 256), (300, 1024, 320), (64, 128, 64)])
-def test_exact_inputs_are_bit_exact(M, K, N, epi):
+@pytest.mark.parametrize("ws", WS)
+@pytest.mark.parametrize("epi,M,K,N", [(e, M, K, N) for e in ("bias", "gated_residual")
+                                       for M, K, N in ((256, 256, 256), (300, 1024, 320),
+                                                       (64, 128, 64))]
+                         + [("bias", 256, 8192, 256), ("bias", 96, 6144, 320)])
+def test_exact_inputs_are_bit_exact(M, K, N, epi, ws):
     rng = np.random.default_rng(M + K + N)
     q = _narrow_codes(rng, (M, K))
     qw = _narrow_codes(rng, (N, K))
@@ -138,8 +158,8 @@ def test_exact_inputs_are_bit_exact(M, K, N, epi):
     if epi == "gated_residual":
         gate = f32_to_bf16_bits(np.ldexp(1.0, rng.integers(-1, 2, N)).astype(np.float32))
         res = f32_to_bf16_bits((rng.integers(-64, 64, (M, N)) * 2.0 ** -4).astype(np.float32))
-    announce(f"exact linear {M}x{K}x{N} {epi}")
-    out = _run_linear(q, sa, qw, sw, bias, epi, gate, res)
+    announce(f"exact linear {M}x{K}x{N} {epi} workspace={ws}")
+    out = _run_linear(q, sa, qw, sw, bias, epi, gate, res, ws=ws)
     ref = linear_ref(q, sa, qw, sw, bf16_bits_to_f32(bias), epi,
                      None if gate is None else bf16_bits_to_f32(gate),
                      None if res is None else bf16_bits_to_f32(res))
@@ -200,6 +220,9 @@ def test_one_hot_weights_decode_every_code():
     ("flux-single-block-1024", 0, False),
     ("flux-single-block-1024", 1, True),
     ("flux-mlp-up-2048", 0, False),
+    ("flux-dit-step-1024", 3, True),     # image-stream fc2: 4096 x 12288 -> 3072, 192 tiles
+    ("flux-dit-step-1024", 7, True),     # text-stream fc2: 512 x 12288 -> 3072, 24 tiles
+    ("flux-dit-step-1024", 6, False),    # text-stream fc1: 512 x 3072 -> 12288
 ])
 def test_full_size_workloads_sampled_rows(name, index, inplace):
     """Full-size launch exactly as the benchmark runs it; every code and scale is compared, and
@@ -223,3 +246,24 @@ def test_deterministic_and_m_zero():
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
     assert e.shape == (0, 640)
+
+
+def test_workspace_is_left_zeroed_and_reusable():
+    """An explicit workspace: after every completed call its arrival counters are zero again, so
+    back-to-back calls of different sizes can share it; results equal the whole-tile schedule
+    on exact inputs."""
+    rng = np.random.default_rng(11)
+    shapes = [(256, 8192, 256), (520, 2048, 640), (64, 128, 64)]
+    need = max(dq.dq_linear_fp8_workspace_size(M, K, N) for M, K, N in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for M, K, N in shapes:
+        announce(f"explicit workspace {M}x{K}x{N}")
+        q, qw = _narrow_codes(rng, (M, K)), _narrow_codes(rng, (N, K))
+        sa = np.ldexp(1.0, rng.integers(-5, -2, M)).astype(np.float32)
+        sw = np.ldexp(1.0, rng.integers(-5, -2, N)).astype(np.float32)
+        a = _run_linear(q, sa, qw, sw, None, "bias", ws=ws)
+        b = _run_linear(q, sa, qw, sw, None, "bias", ws=None)
+        assert torch.equal(a, b)
+        tiles = ((M + 255) // 256) * ((N + 255) // 256)
+        counters = ws[PART_REGION: PART_REGION + 4 * tiles].view(torch.int32)
+        assert int(counters.abs().sum().item()) == 0
