@@ -65,6 +65,32 @@ def test_every_bf16_pattern_at_scale_one():
     _assert_same(rows, "all bf16 |v|<=448 at scale 1")
 
 
+def _rows_below(amax_bits, K):
+    """Rows of length K that all hold amax (bf16 bits amax_bits) and, between them, every bf16
+    value of magnitude <= amax with both signs."""
+    mags = np.arange(0, int(amax_bits) + 1, dtype=np.uint32).astype(np.uint16)
+    vals = np.concatenate([mags, mags | np.uint16(0x8000)])
+    n = (vals.size + K - 2) // (K - 1)
+    pad = np.zeros(n * (K - 1) - vals.size, dtype=np.uint16)
+    body = np.concatenate([vals, pad]).reshape(n, K - 1)
+    return np.concatenate([np.full((n, 1), amax_bits, np.uint16), body], axis=1)
+
+
+@pytest.mark.parametrize("K", [3072, 16384])
+def test_every_value_below_many_scales(K):
+    """For amax spread over the whole bf16 range -- a subnormal scale (amax below 448 2^-126),
+    rows below 2^-60 (quotient formed from x 2^64 and scale 2^64), ordinary and huge ones --
+    every bf16 value with |x| <= amax, through the register-resident kernel (K = 3072) and the
+    two-pass one (K = 16384)."""
+    picks = [0x0001, 0x0080, 0x0300, 0x05A0, 0x0B40, 0x0C00, 0x0D07, 0x1A3C, 0x2180,
+             0x2199, 0x21A0, 0x2F11, 0x3B80, 0x3F80, 0x4080, 0x42F3, 0x43E0, 0x47AB,
+             0x5C01, 0x7F7F]
+    rng = np.random.default_rng(5)
+    picks += [int(v) for v in rng.integers(0x0100, 0x7F7F, 12)]
+    for a in picks:
+        _assert_same(_rows_below(np.uint16(a), K), f"every value below {a:#06x}, K={K}")
+
+
 def test_random_amax_rows_spanning_all_magnitudes():
     """2048 rows; row r holds its amax a_r (any positive finite bf16, subnormals included) and
     4095 random bf16 values with |v| <= a_r."""
