@@ -209,9 +209,14 @@ def dit_step_plan(wl: Workload):
     return plan
 
 
-def dit_step_device_inputs(wl: Workload, device, quantize_weight):
-    """Draw every input of one step on `device` and hand each bf16 weight to `quantize_weight`
-    (which returns its (codes, scales)); the bf16 weight is dropped afterwards.
+def dit_step_device_inputs(wl: Workload, device, quantize_weight, only=None,
+                           keep_weights=False):
+    """Draw the inputs of one step on `device` and hand each bf16 weight to `quantize_weight`
+    (which returns its (codes, scales)); the bf16 weight is dropped afterwards unless
+    keep_weights (then it is kept under "w").
+
+    only: None for all 228 linears, or a set of indices into dit_step_plan(wl) to draw (each
+    linear has its own seed, so a subset gets exactly the values the whole step gets).
 
     Returns (plan, activations, residual_streams): plan entries are dicts with the shape, the
     epilogue, the activation key, the residual key (gated linears), qw, sw, bias and gate."""
@@ -234,18 +239,24 @@ def dit_step_device_inputs(wl: Workload, device, quantize_weight):
         residuals[stream] = torch.randn((M, 3072), generator=g, device=device,
                                         dtype=torch.float32).to(torch.bfloat16)
     plan = []
-    for shape, sub, stream in dit_step_plan(wl):
+    for idx, (shape, sub, stream) in enumerate(dit_step_plan(wl)):
+        if only is not None and idx not in only:
+            continue
         g.manual_seed(base + sub)
         w = (torch.randn((shape.N, shape.K), generator=g, device=device, dtype=torch.float32)
              * 0.02).to(torch.bfloat16)
         qw, sw = quantize_weight(w)
-        del w
         bias = (torch.randn(shape.N, generator=g, device=device) * 0.01).to(torch.bfloat16)
         gate = None
         if shape.epilogue == "gated_residual":
             gate = (1.0 + 0.1 * torch.randn(shape.N, generator=g, device=device)).to(torch.bfloat16)
-        plan.append({"name": shape.name, "M": shape.M, "K": shape.K, "N": shape.N,
-                     "epilogue": shape.epilogue, "act": f"{shape.M}x{shape.K}",
-                     "residual": stream if shape.epilogue == "gated_residual" else None,
-                     "qw": qw, "sw": sw, "bias": bias, "gate": gate, "seed": base + sub})
+        entry = {"name": shape.name, "M": shape.M, "K": shape.K, "N": shape.N,
+                 "epilogue": shape.epilogue, "act": f"{shape.M}x{shape.K}",
+                 "residual": stream if shape.epilogue == "gated_residual" else None,
+                 "qw": qw, "sw": sw, "bias": bias, "gate": gate, "seed": base + sub,
+                 "plan_index": idx}
+        if keep_weights:
+            entry["w"] = w
+        del w
+        plan.append(entry)
     return plan, acts, residuals
