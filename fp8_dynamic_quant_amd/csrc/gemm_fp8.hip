@@ -423,21 +423,22 @@ __device__ __forceinline__ void store_part(const v16f (&acc)[2][4], __amdgpu_buf
   }
 }
 
-// acc (+)= partial tile `slot`, four 4-register groups at a time so that few loads are in flight.
+// acc (+)= partial tile `slot`, sixteen 4-register groups in flight at a time (the fragment
+// registers are free here), so a partial costs two memory round trips per wave.
 template <bool FIRST>
 __device__ __forceinline__ void add_part(v16f (&acc)[2][4], __amdgpu_buffer_rsrc_t rs,
                                          uint32_t slot, int wave, int lane) {
   const uint32_t base = slot + (uint32_t)(wave * 32 * 64 + lane) * 16u;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    v4i x[4];
+  for (int c = 0; c < 2; ++c) {
+    v4i x[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      x[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, base + (uint32_t)(c * 4 + i) * 1024u, 0,
+    for (int i = 0; i < 16; ++i)
+      x[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, base + (uint32_t)(c * 16 + i) * 1024u, 0,
                                                    kCoherent);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int g4 = c * 4 + i;
+    for (int i = 0; i < 16; ++i) {
+      const int g4 = c * 16 + i;
       const int blk = g4 >> 2, e = (g4 & 3) * 4;
       v16f& a = acc[blk >> 2][blk & 3];
 #pragma unroll
@@ -640,7 +641,7 @@ hipError_t launch_linear(const uint8_t* q, const float* scale, int64_t M, int64_
   // Whole tiles keep every workgroup of an XCD at the same K offset, so an A or B slice fetched
   // once is reused from L2; cut tiles lose that sharing. Tiles are cut only where whole tiles
   // would leave most compute units idle: when a workgroup's whole-tile load is at least twice
-  // its equal share plus a few steps (few tiles, long K).
+  // its equal share plus 16 steps (few tiles and a long K, e.g. the text stream's fc2).
   const int64_t whole_grid = p.tiles < cus ? p.tiles : cus;
   const int64_t whole_steps = (p.tiles + whole_grid - 1) / whole_grid * p.nk;
   const int64_t split_grid = split_groups(units) < cus ? split_groups(units) : cus;
