@@ -13,30 +13,24 @@ hipError_t launch_quantize_rows(const uint16_t* x, int64_t R, int64_t K, uint8_t
 
 // ---------------------------------------------------------------------------------------------
 // GEMM work split, shared by the size query (host only, no GPU) and the launcher.
-//   tile  = 256 x 256 outputs; step = 128 of K; unit = one step of one tile.
-// With a workspace, G workgroups take equal shares of all units, G <= split_groups() <=
-// kMaxSplitGroups. Workspace layout, the same for every problem so that one workspace serves
-// calls of any size in turn:
-//   [0, kPartRegion)              two 256 x 256 fp32 partial tiles per workgroup (a share can
-//                                 cut a tile at its start and at its end)
+//   tile = 256 x 256 outputs; step = 128 of K.
+// With a workspace, the tiles left over after the full rounds of whole tiles may be cut into
+// up to kMaxParts parts along K (see gemm_fp8.hip). Workspace layout, the same for every
+// problem so that one workspace serves calls of any size in turn:
+//   [0, kPartRegion)              one 256 x 256 fp32 partial tile per part
 //   [kPartRegion, + 4 * tiles)    one arrival counter per tile, zero between calls
 // ---------------------------------------------------------------------------------------------
 constexpr int64_t kTileM = 256, kTileN = 256, kStepK = 128;
-constexpr int64_t kMaxSplitGroups = 256;
-constexpr int64_t kMinUnitsPerGroup = 4;
+constexpr int64_t kMaxParts = 1024;
+constexpr int64_t kMaxSplits = 8;
 constexpr int64_t kPartialBytes = kTileM * kTileN * 4;
-constexpr uint64_t kPartRegion = static_cast<uint64_t>(kMaxSplitGroups) * 2u * kPartialBytes;
+constexpr uint64_t kPartRegion = static_cast<uint64_t>(kMaxParts) * kPartialBytes;
 
 inline int64_t linear_tiles(int64_t M, int64_t N) {
   return ((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN);
 }
 inline int64_t linear_units(int64_t M, int64_t K, int64_t N) {
   return linear_tiles(M, N) * (K / kStepK);
-}
-inline int64_t split_groups(int64_t units) {
-  int64_t g = units / kMinUnitsPerGroup;
-  if (g < 1) g = 1;
-  return g < kMaxSplitGroups ? g : kMaxSplitGroups;
 }
 inline uint64_t linear_workspace_bytes(int64_t M, int64_t K, int64_t N) {
   (void)K;

@@ -6,15 +6,17 @@
 //
 // Work decomposition
 //   * output tiles of 256 x 256, K consumed 128 bytes per step; a "unit" is one step of one tile;
-//   * a persistent grid of G <= (compute units) workgroups. Whole tiles are dealt round-robin
-//     (workgroup v takes tiles v, v + G, ...), so the workgroups of an XCD step through K
-//     together and share A and B slices in L2. When that leaves most compute units idle (few
-//     tiles, long K) and a workspace is given, the tiles from `tail0` on (here: all of them) are
-//     instead cut into G equal shares of units. The parts of a cut tile are summed in fp32
-//     through the workspace by the part that finishes last (an arrival counter per tile; no
-//     workgroup ever waits for another), adding the parts in workgroup order so the result does
-//     not depend on timing; parts travel with device-coherent (sc1) loads and stores, so no
-//     cache flush is needed;
+//   * a persistent grid of G <= (compute units) workgroups taking work items round-robin
+//     (workgroup v takes items v, v + G, ...), so the workgroups of an XCD hold neighbouring
+//     items, step through K together and share A and B slices in L2. The items are the tiles of
+//     the full rounds (T - T mod G of them), then the T mod G tiles left over. With a workspace
+//     the left-over tiles may be cut along K into s equal parts (s divides the step count, and
+//     is chosen on the host by counting steps), the parts ordered so that neighbouring
+//     workgroups hold neighbouring tiles at the same K range: the last round then keeps the
+//     compute units busy. The parts of a cut tile are summed in fp32 through the workspace by
+//     the part that finishes last (an arrival counter per tile; no workgroup ever waits for
+//     another), in part order, so the result does not depend on timing; parts travel with
+//     device-coherent (sc1) loads and stores, so no cache flush is needed;
 //   * workgroups are numbered so that the ones on one XCD (hardware dispatch sends workgroup b to
 //     XCD b mod 8) get consecutive numbers, hence neighbouring tiles, and tiles are walked 4 tile
 //     rows at a time, so an XCD's L2 serves the A and B panels its compute units share.
@@ -76,11 +78,12 @@ struct Params {
   const uint16_t* residual;  // [M, N] (gated only; may equal out)
   uint16_t* out;             // [M, N]
   uint32_t* flags;           // [tiles] arrival counters (cut tiles only)
-  float* part;               // [groups][2][256 * 256] partial tiles (cut tiles only)
+  float* part;               // [parts][256 * 256] partial tiles (cut tiles only)
   int M, N, K, tilesM, tilesN, nk, tiles;
-  int split;                 // 1: the tiles from tail0 on are cut into equal shares of units
-  int tail0;                 // first cut tile (a multiple of the grid size)
-  int tail_units;            // (tiles - tail0) * nk
+  int dp_tiles;              // tiles of the full rounds (a multiple of the grid size)
+  int tail_tiles;            // tiles - dp_tiles
+  int splits;                // parts per left-over tile (1: not cut)
+  int part_steps;            // nk / splits
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -135,47 +138,37 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 // schedule: shares, tiles, contributors
 // ---------------------------------------------------------------------------------------------
 
-// Units (tile steps) of the cut tiles held by workgroups 0 .. v - 1.
-__device__ __forceinline__ int share_begin(const Params& p, int v, int G) {
-  return (int)(((int64_t)v * p.tail_units) / G);
-}
-
-// The workgroup whose share holds unit u of the cut tiles.
-__device__ __forceinline__ int share_owner(const Params& p, int u, int G) {
-  return (int)((((int64_t)u + 1) * G - 1) / p.tail_units);
-}
-
-// Workgroup v's work: `whole` whole tiles v, v + G, ..., then units [sk0, sk1) of the cut tiles.
-struct Share {
-  int whole, sk0, sk1;
+// Workgroup v's items: n_dp whole tiles v, v + G, ... of the full rounds, then n_parts parts
+// p = v, v + G, ... of the left-over tiles (part p: tile dp_tiles + p % tail_tiles, steps
+// [j part_steps, (j + 1) part_steps), j = p / tail_tiles).
+struct Work {
+  int n_dp, n_parts;
 };
 
-__device__ __forceinline__ Share share_of(const Params& p, int v, int G) {
-  Share sh;
-  if (p.split) {
-    sh.whole = p.tail0 / G;
-    sh.sk0 = share_begin(p, v, G);
-    sh.sk1 = share_begin(p, v + 1, G);
-  } else {
-    sh.whole = (p.tiles - v + G - 1) / G;
-    sh.sk0 = sh.sk1 = 0;
-  }
-  return sh;
+__device__ __forceinline__ Work work_of(const Params& p, int v, int G) {
+  Work w;
+  w.n_dp = p.dp_tiles / G;
+  const int P = p.tail_tiles * p.splits;
+  w.n_parts = v < P ? (P - v + G - 1) / G : 0;
+  return w;
 }
 
-// Tile and step of workgroup-local step S.
-__device__ __forceinline__ void step_of(const Params& p, const Share& sh, int v, int G, int S,
-                                        int& t, int& k) {
-  const int dp = sh.whole * p.nk;
+// Tile, step and part (-1: a whole tile) of workgroup-local step S.
+__device__ __forceinline__ void step_of(const Params& p, const Work& w, int v, int G, int S,
+                                        int& t, int& k, int& part) {
+  const int dp = w.n_dp * p.nk;
   if (S < dp) {
     const int i = S / p.nk;
     t = v + i * G;
     k = S - i * p.nk;
+    part = -1;
   } else {
-    const int su = sh.sk0 + (S - dp);
-    const int tt = su / p.nk;
-    t = p.tail0 + tt;
-    k = su - tt * p.nk;
+    const int s2 = S - dp;
+    const int i = s2 / p.part_steps;
+    part = v + i * G;
+    const int j = part / p.tail_tiles;
+    t = p.dp_tiles + (part - j * p.tail_tiles);
+    k = j * p.part_steps + (s2 - i * p.part_steps);
   }
 }
 
@@ -451,39 +444,36 @@ __device__ __forceinline__ void add_part(v16f (&acc)[2][4], __amdgpu_buffer_rsrc
   }
 }
 
-// Byte offset of workgroup c's partial tile (slot 0: the first tile its share cuts, 1: the last).
-__device__ __forceinline__ uint32_t part_slot(int c, int slot) {
-  return ((uint32_t)c * 2u + (uint32_t)slot) * (uint32_t)(kPartFloats * 4);
+// Byte offset of the partial tile of part p.
+__device__ __forceinline__ uint32_t part_slot(int p) {
+  return (uint32_t)p * (uint32_t)(kPartFloats * 4);
 }
 
-// This workgroup's part of cut tile t is in acc (both groups are done with its MFMAs). Store it
-// and count its arrival. The last part to arrive loads all parts, in workgroup order, into acc
-// and clears the tile's counter for the next call; it returns true and the caller applies the
-// epilogue.
-__device__ bool finish_split(v16f (&acc)[2][4], const Params& p, int t, int v, int G,
-                             const Share& sh, int wave, int lane, int* s_last) {
+// Part `part` of left-over tile t is in acc (both groups are done with its MFMAs). Store it and
+// count its arrival. The last part to arrive loads all parts of the tile, in part order, into
+// acc and clears the tile's counter for the next call; it returns true and the caller applies
+// the epilogue.
+__device__ bool finish_split(v16f (&acc)[2][4], const Params& p, int t, int part, int wave,
+                             int lane, int* s_last) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      p.part, 0, (int)(2u * (uint32_t)kPartFloats * 4u * 256u), 0x00020000);
-  const int first_cut = p.tail0 + sh.sk0 / p.nk;
-  store_part(acc, rs, part_slot(v, t == first_cut ? 0 : 1), wave, lane);
+      p.part, 0, (int)kPartRegion, 0x00020000);
+  store_part(acc, rs, part_slot(part), wave, lane);
   wait_vmem();
   phase_barrier();  // every wave's part is stored
-  const int tt = t - p.tail0;
-  const int vlo = share_owner(p, tt * p.nk, G);
-  const int vhi = share_owner(p, tt * p.nk + p.nk - 1, G);
   if (threadIdx.x == 0) {
     const uint32_t old =
         __hip_atomic_fetch_add(p.flags + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_last = old == (uint32_t)(vhi - vlo);
+    *s_last = old == (uint32_t)(p.splits - 1);
   }
   phase_barrier();
   if (!*s_last) return false;
-  for (int c = vlo; c <= vhi; ++c) {
-    const int slot = (t == p.tail0 + share_begin(p, c, G) / p.nk) ? 0 : 1;
-    if (c == vlo)
-      add_part<true>(acc, rs, part_slot(c, slot), wave, lane);
+  const int tt = t - p.dp_tiles;
+  for (int j = 0; j < p.splits; ++j) {
+    const uint32_t slot = part_slot(j * p.tail_tiles + tt);
+    if (j == 0)
+      add_part<true>(acc, rs, slot, wave, lane);
     else
-      add_part<false>(acc, rs, part_slot(c, slot), wave, lane);
+      add_part<false>(acc, rs, slot, wave, lane);
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(p.flags + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -508,9 +498,10 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
   const int b = blockIdx.x;
   const int v = (G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b;
   const int nk = p.nk;
-  const Share sh = share_of(p, v, G);
-  const int nsteps = sh.whole * nk + (sh.sk1 - sh.sk0);
-  const int dp = sh.whole * nk;
+  const Work w = work_of(p, v, G);
+  const int dp = w.n_dp * nk;
+  const int nsteps = dp + w.n_parts * p.part_steps;
+  if (nsteps == 0) return;  // more workgroups than items (the whole workgroup leaves)
   const uint32_t uK = (uint32_t)p.K;
 
   // copy addressing of this lane: rows 64q + (lane >> 3) + 8j, chunk position lane & 7
@@ -521,8 +512,8 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
   const uint32_t dodd = (cO - cE) * 16u;  // added (mod 2^32) for odd j
 
   // first step, with its tile's parameters
-  int t0, k0s;
-  step_of(p, sh, v, G, 0, t0, k0s);
+  int t0, k0s, part0;
+  step_of(p, w, v, G, 0, t0, k0s, part0);
   TileDesc nd = tile_desc(p, t0);
   if (g == 0) {
     copy_part(nd, uK, k0s, lds, voff0, dodd, q, 0);
@@ -539,9 +530,9 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
   int S = 0;     // steps done; step S is in stage buffer S & 1
   int part = 0;  // parts (runs of steps of one tile) done; part i's parameters in buffer i % 3
   while (S < nsteps) {
-    int t, k0;
-    step_of(p, sh, v, G, S, t, k0);
-    const int len = S < dp ? nk : ((nk - k0) < (nsteps - S) ? nk - k0 : nsteps - S);
+    int t, k0, cutp;
+    step_of(p, w, v, G, S, t, k0, cutp);
+    const int len = S < dp ? nk : p.part_steps;
     v16f acc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -551,8 +542,8 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
       const uint8_t* st = lds + (S & 1) * kStageBytes;
       uint8_t* st1 = lds + ((S + 1) & 1) * kStageBytes;
       const bool more = S + 1 < nsteps;
-      int tn = t, kn = 0;
-      if (more) step_of(p, sh, v, G, S + 1, tn, kn);
+      int tn = t, kn = 0, pn = 0;
+      if (more) step_of(p, w, v, G, S + 1, tn, kn, pn);
       const bool starts = more && (j + 1 == len);  // step S + 1 begins the next part
       if (starts) nd = tile_desc(p, tn);
       // phase A (G0: reads K half 0 | G1: MFMAs of the previous half)
@@ -579,7 +570,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
     bool write = true;
     if (cut) {
       if (g == 0) phase_barrier();  // group 1's last MFMAs of this part are done
-      write = finish_split(acc, p, t, v, G, sh, wave, lane, &s_last);
+      write = finish_split(acc, p, t, cutp, wave, lane, &s_last);
     }
     if (write) {
       int m0, n0;
@@ -636,36 +627,54 @@ hipError_t launch_linear(const uint8_t* q, const float* scale, int64_t M, int64_
   p.tilesN = (int)((N + kBN - 1) / kBN);
   p.nk = (int)(K / kBK);
   p.tiles = (int)linear_tiles(M, N);
-  const int64_t units = linear_units(M, K, N);
   const int cus = compute_units();
-  // Whole tiles keep every workgroup of an XCD at the same K offset, so an A or B slice fetched
-  // once is reused from L2; cut tiles lose that sharing. Tiles are cut only where whole tiles
-  // would leave most compute units idle: when a workgroup's whole-tile load is at least twice
-  // its equal share plus 16 steps (few tiles and a long K, e.g. the text stream's fc2).
-  const int64_t whole_grid = p.tiles < cus ? p.tiles : cus;
-  const int64_t whole_steps = (p.tiles + whole_grid - 1) / whole_grid * p.nk;
-  const int64_t split_grid = split_groups(units) < cus ? split_groups(units) : cus;
-  const int64_t split_steps = (units + split_grid - 1) / split_grid;
-  int grid;
-  if (workspace && whole_steps >= 2 * split_steps + 16) {
-    grid = (int)split_grid;
-    p.split = 1;
-    p.tail0 = 0;
-    p.tail_units = p.tiles * p.nk;
-    p.part = static_cast<float*>(workspace);
-    p.flags = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + kPartRegion);
-  } else {
-    grid = (int)whole_grid;
-    p.split = 0;
-    p.tail0 = p.tiles;
-    p.tail_units = 0;
-    p.part = nullptr;
-    p.flags = nullptr;
+  // Full rounds of whole tiles, then the left-over tiles, cut into s parts along K when a
+  // workspace is given and a count of the work says it pays by 20 % or more. Counted in steps
+  // (one step is about 1.5 us on a busy chip): the last round takes ceil(left s / G) parts of
+  // nk / s steps per workgroup, every part stores a 256 x 256 fp32 partial tile, and the part
+  // that finishes a tile loads the s - 1 others; a partial tile moves at the compute unit's
+  // share of HBM bandwidth (at most about 60 GB/s for one unit, 5.6 TB/s for the chip).
+  int64_t grid = p.tiles < cus ? p.tiles : cus;
+  const int64_t rounds = workspace ? p.tiles / cus : 0;  // full rounds use every compute unit
+  const int64_t dp_tiles = rounds * cus, left = p.tiles - dp_tiles;
+  int64_t splits = 1;
+  if (workspace && left > 0) {
+    constexpr double kStepUs = 1.5, kUnitGBs = 60.0, kChipGBs = 5600.0;
+    const double whole = (double)p.nk;
+    double best = 0.8 * whole;
+    for (int64_t s = 2; s <= kMaxSplits; ++s) {
+      if (p.nk % s != 0 || left * s > kMaxParts) continue;
+      const int64_t active = left * s < cus ? left * s : cus;
+      const double unit_gbs = kChipGBs / (double)active < kUnitGBs ? kChipGBs / (double)active
+                                                                    : kUnitGBs;
+      const double part_steps_cost = (double)kPartialBytes / (unit_gbs * 1e3) / kStepUs;
+      const double per_unit = (double)((left * s + active - 1) / active);
+      const double cost = per_unit * ((double)(p.nk / s) + part_steps_cost) +
+                          (double)(s - 1) * part_steps_cost;
+      if (cost < best) {
+        best = cost;
+        splits = s;
+      }
+    }
+    if (dp_tiles == 0) grid = left * splits < cus ? left * splits : cus;
   }
+  p.dp_tiles = (int)dp_tiles;
+  p.tail_tiles = (int)left;
+  p.splits = (int)splits;
+  p.part_steps = (int)(p.nk / splits);
+  p.part = splits > 1 ? static_cast<float*>(workspace) : nullptr;
+  p.flags = splits > 1
+                ? reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + kPartRegion)
+                : nullptr;
+  if (!workspace) {  // whole tiles only: every tile is a left-over tile of round 0
+    p.dp_tiles = 0;
+    p.tail_tiles = p.tiles;
+  }
+  const int g = (int)grid;
   switch (epilogue) {
-    case EPI_BIAS: return launch_epi<EPI_BIAS>(p, grid, stream);
-    case EPI_GELU_TANH: return launch_epi<EPI_GELU_TANH>(p, grid, stream);
-    default: return launch_epi<EPI_GATED_RESIDUAL>(p, grid, stream);
+    case EPI_BIAS: return launch_epi<EPI_BIAS>(p, g, stream);
+    case EPI_GELU_TANH: return launch_epi<EPI_GELU_TANH>(p, g, stream);
+    default: return launch_epi<EPI_GATED_RESIDUAL>(p, g, stream);
   }
 }
 

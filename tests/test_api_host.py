@@ -133,9 +133,9 @@ def test_linear_argument_checks(lib):
 
 def test_workspace_size(lib):
     size = lib.dq_linear_fp8_workspace_size
-    # a fixed region of 256 x 2 partial 256 x 256 fp32 tiles, then one 4-byte counter per
+    # a fixed region of 1024 partial 256 x 256 fp32 tiles, then one 4-byte counter per
     # 256 x 256 output tile, rounded up to 256 bytes
-    parts = 256 * 2 * 256 * 256 * 4
+    parts = 1024 * 256 * 256 * 4
     assert size(4608, 3072, 12288) == parts + 3584                # 18 x 48 tiles
     assert size(64, 256, 512) == parts + 256                      # 2 tiles
     assert size(512, 12288, 3072) == parts + 256                  # 24 tiles
@@ -167,7 +167,7 @@ def test_python_binding_names_match_the_c_entry_points():
                  "dq_linear_fp8_workspace_size"):
         assert callable(getattr(dq, name))
     assert dq.lib().dq_abi_version() == 2
-    assert dq.dq_linear_fp8_workspace_size(4608, 3072, 12288) == 3584 + 256 * 2 * 262144
+    assert dq.dq_linear_fp8_workspace_size(4608, 3072, 12288) == 3584 + 1024 * 262144
 
 
 def test_python_binding_rejects_cpu_tensors():

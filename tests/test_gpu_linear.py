@@ -36,7 +36,7 @@ def _bits_of(ref64):
 
 
 WS = ("auto", None)   # tile-sharing schedule through a workspace, and whole tiles only
-PART_REGION = 256 * 2 * 256 * 256 * 4   # workspace bytes before the per-tile arrival counters
+PART_REGION = 1024 * 256 * 256 * 4      # workspace bytes before the per-tile arrival counters
 
 
 def _run_linear(q, sa, qw, sw, bias, epi, gate=None, residual=None, inplace=False, ws="auto"):
@@ -104,11 +104,11 @@ def test_tiles_and_ragged_tails(M, K, N, epi, ws):
 
 
 @pytest.mark.parametrize("M,K,N", [(256, 8192, 256), (40, 4096, 192), (600, 5120, 448),
-                                   (256, 6400, 768)])
+                                   (256, 6400, 768), (2304, 3072, 2560)])
 def test_tiles_shared_by_many_workgroups(M, K, N):
-    """Few tiles and a long K: with a workspace each tile is cut into many parts (16 for one
-    tile of 64 steps) that the last arriving part sums; with 3 tiles of 50 steps over 37
-    workgroups, shares also straddle tile boundaries (a part at each end)."""
+    """Few tiles and a long K: with a workspace each tile is cut along K into up to 8 parts
+    (8 for one tile of 64 steps, 5 for three tiles of 50 steps) that the last arriving part
+    sums."""
     shape = LinearShape(f"split{M}x{K}x{N}", M, K, N, "gated_residual", K // 100, 30.0)
     _end_to_end(shape, seed=2000 + M + K + N, ws="auto")
 
@@ -232,6 +232,18 @@ def test_full_size_workloads_sampled_rows(name, index, inplace):
     rng = np.random.default_rng(99)
     rows = np.unique(np.concatenate([[0, shape.M - 1], rng.choice(shape.M, 62, replace=False)]))
     _end_to_end(shape, w.seed, index, rows=rows, inplace=inplace)
+
+
+@pytest.mark.parametrize("M,K,N,epi", [(5120, 3072, 3584, "gelu_tanh"),
+                                       (4608, 3072, 12288, "bias")])
+def test_full_rounds_then_cut_tiles_sampled_rows(M, K, N, epi):
+    """More tiles than compute units: whole tiles for the full rounds, then the left-over tiles
+    (24 of 280; 96 of 864) cut along K; sampled rows against the oracle, both schedules."""
+    shape = LinearShape(f"rounds{M}x{K}x{N}", M, K, N, epi, K // 100, 30.0)
+    rng = np.random.default_rng(M + N)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 62, replace=False)]))
+    for ws in WS:
+        _end_to_end(shape, seed=3000 + M + N, rows=rows, ws=ws)
 
 
 def test_deterministic_and_m_zero():
