@@ -116,11 +116,11 @@ int dq_quantize_weight_fp8(const void* w, int64_t N, int64_t K, void* qw, float*
  *   even).
  *
  * Work split: the output is cut into 256 x 256 tiles and each tile's K range into steps of 128.
- * Without a workspace every workgroup computes whole tiles. With one, the library may instead
- * give every workgroup an equal share of all tile-steps when whole tiles would leave most
- * compute units idle (few tiles, long K): a tile is then split between workgroups, each part
- * is summed in fp32 into the workspace and the last part to finish adds them up (in a fixed
- * order, so the result does not depend on timing) and applies the epilogue.
+ * Without a workspace every workgroup computes whole tiles. With one, the tiles left over after
+ * the full rounds of whole tiles (one tile per compute unit per round) may each be cut along K
+ * into 2 to 8 equal parts, when a cost model of the device says that is faster: each part is
+ * summed in fp32 into the workspace and the last part of a tile to finish adds them up (in a
+ * fixed order, so the result does not depend on timing) and applies the epilogue.
  * The workspace must hold zeros before its first use. Its layout is the same for every problem
  * (the partial tiles first, then one arrival counter per tile), and every call that completes
  * leaves all counters at zero again, so one zero fill at allocation is enough and one workspace
@@ -139,7 +139,8 @@ int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const
 /*
  * dq_linear_fp8_workspace_size -- bytes of workspace dq_linear_fp8 uses for an M x K -> N
  * problem (the same on every device), or 0 if the sizes break dq_linear_fp8's requirements:
- * 128 MiB of partial tiles plus 4 bytes per 256 x 256 output tile, rounded up to 256 bytes.
+ * 256 MiB (1024 partial 256 x 256 fp32 tiles) plus 4 bytes per 256 x 256 output tile, rounded up
+ * to 256 bytes.
  * Needs no GPU.
  */
 uint64_t dq_linear_fp8_workspace_size(int64_t M, int64_t K, int64_t N);
