@@ -29,9 +29,13 @@
 //     next fragments from LDS (ping-pong);
 //   * each step's A tile (256 x 128 B) and B tile (256 x 128 B) go global -> LDS through
 //     buffer_load_dwordx4 ... lds (no registers involved), one instruction moving 8 rows x 128 B
-//     (whole 128-byte lines); the copies of step s + 1 are spread over three phases of step s,
-//     into the buffer step s - 1 used, and each wave waits for its own copies before the barrier
-//     that ends step s;
+//     (whole 128-byte lines), in four batches of 16 KiB, one per phase, each issued by that
+//     phase's reading wave after its LDS reads. Two stages: the A rows and group 1's B rows of
+//     step s + 1 go into the stage step s - 1 used, group 0's B rows of step s + 2 into the stage
+//     of step s once group 0 has read them, so every batch has two to four phases to land. A
+//     wave waits for its own batches (all but its last one) before the barrier that precedes
+//     their first reader. Issuing a phase's copies in one burst, or working out the next step
+//     with integer divisions, held the reading wave past the MFMAs of its phase;
 //   * LDS rows are 128 B; 16-byte chunk c of row r sits at position c ^ ((r >> 1) & 7). A
 //     ds_read_b128 serves 16 lanes at a time, here 16 consecutive rows at one K offset, and with
 //     this key they land in 16 different 16-byte slots of a 256-byte bank period (no conflicts);
@@ -119,6 +123,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // All vector memory operations of this wavefront done (vmcnt = 0; lgkm and exp untouched).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// All but the last four vector memory operations of this wavefront done (vmcnt <= 4). Memory
+// operations of one wavefront are counted off in the order they were issued.
+__device__ __forceinline__ void wait_vmem_but4() { __builtin_amdgcn_s_waitcnt(0x0F74); }
 
 // Phase boundary: this wavefront's LDS reads done, then the workgroup barrier. No instruction
 // is scheduled across it (the MFMAs of a phase must stay in their phase).
@@ -153,22 +160,36 @@ __device__ __forceinline__ Work work_of(const Params& p, int v, int G) {
   return w;
 }
 
-// Tile, step and part (-1: a whole tile) of workgroup-local step S.
-__device__ __forceinline__ void step_of(const Params& p, const Work& w, int v, int G, int S,
-                                        int& t, int& k, int& part) {
-  const int dp = w.n_dp * p.nk;
-  if (S < dp) {
-    const int i = S / p.nk;
-    t = v + i * G;
-    k = S - i * p.nk;
-    part = -1;
+// A position in a workgroup's sequence of steps: work item `item`, its tile t, its part of a
+// cut tile (-1: a whole tile), the K step k and the item's end step kend. Moving one step on costs an
+// increment; the divisions happen once per item.
+struct Cursor {
+  int item, t, cut, k, kend;
+};
+
+__device__ __forceinline__ void cursor_item(const Params& p, const Work& w, int v, int G,
+                                            Cursor& c) {
+  if (c.item < w.n_dp) {
+    c.t = v + c.item * G;
+    c.cut = -1;
+    c.k = 0;
+    c.kend = p.nk;
   } else {
-    const int s2 = S - dp;
-    const int i = s2 / p.part_steps;
-    part = v + i * G;
+    const int part = v + (c.item - w.n_dp) * G;
     const int j = part / p.tail_tiles;
-    t = p.dp_tiles + (part - j * p.tail_tiles);
-    k = j * p.part_steps + (s2 - i * p.part_steps);
+    c.t = p.dp_tiles + (part - j * p.tail_tiles);
+    c.cut = p.splits > 1 ? part : -1;
+    c.k = j * p.part_steps;
+    c.kend = c.k + p.part_steps;
+  }
+}
+
+// The next step; past the last one the cursor keeps its tile (and is not used).
+__device__ __forceinline__ void cursor_next(const Params& p, const Work& w, int v, int G,
+                                            Cursor& c) {
+  if (++c.k == c.kend) {
+    ++c.item;
+    if (c.item < w.n_dp + w.n_parts) cursor_item(p, w, v, G, c);
   }
 }
 
@@ -202,35 +223,26 @@ __device__ __forceinline__ TileDesc tile_desc(const Params& p, int t) {
 // copies
 // ---------------------------------------------------------------------------------------------
 
-// Rows 64q + 8j .. + 8 of one operand of step k into the stage (8 rows x 128 B at lds_block +
-// 1 KiB j). Lane l lands in LDS slot l of the block (row l >> 3, position l & 7), so it fetches
-// global chunk (l & 7) ^ key(row); the chunk offset differs between even and odd j by dodd.
-__device__ __forceinline__ void copy_rows(v4i rs, uint32_t K, int k, uint32_t lds_block,
-                                          uint32_t voff0, uint32_t dodd, int j) {
-  const uint32_t off = voff0 + (uint32_t)k * kBK + (uint32_t)(j * 8) * K + ((j & 1) ? dodd : 0u);
-  copy_to_lds(rs, off, __builtin_amdgcn_readfirstlane(lds_block + (uint32_t)(j * 1024)));
-}
-
-// The copies of one step, in three parts:
-//   part 0 (group 0): A rows 64q + 8j, j < 6;  part 1 (group 1): B rows 64q + 8j, j < 6;
-//   part 2 (group 0): A and B rows 64q + 48 + 8j, j < 2.
-__device__ __forceinline__ void copy_part(const TileDesc& d, uint32_t K, int k, uint8_t* st,
-                                          uint32_t voff0, uint32_t dodd, int q, int part) {
-  const uint32_t la = lds_addr(st) + (uint32_t)(q * 64 * kBK);
-  const uint32_t lb = la + (uint32_t)(kBM * kBK);
-  if (part == 0) {
+// One copy batch: 32 rows (4 x 8 rows of 128 B) of one operand of step k into stage st, 4
+// instructions per wavefront. The batches of a step, for group-0/1 wave q:
+//   0: A rows 64q + [0, 32)            1: A rows 64q + [32, 64)
+//   2: B rows that group 1 reads: 128 (q >> 1) + 64 + 32 (q & 1) + [0, 32)
+//   3: B rows that group 0 reads: 128 (q >> 1) + 32 (q & 1) + [0, 32)
+// Lane l lands in LDS slot l of an 8-row block (row l >> 3, position l & 7), so it fetches
+// global chunk (l & 7) ^ key(row); every batch starts at a multiple of 16 rows, so the key
+// depends only on l >> 3 and on the parity of the block (odd blocks add dodd to the offset).
+__device__ __forceinline__ void copy_batch(const TileDesc& d, uint32_t K, int k, uint8_t* st,
+                                           uint32_t vlane, uint32_t dodd, int q, int which) {
+  const int row = which < 2 ? q * 64 + which * 32
+                            : (q >> 1) * 128 + (q & 1) * 32 + (which == 2 ? 64 : 0);
+  const v4i rs = which < 2 ? d.rsA : d.rsB;
+  const uint32_t lds0 = lds_addr(st) + (which < 2 ? 0u : (uint32_t)(kBM * kBK)) +
+                        (uint32_t)(row * kBK);
+  const uint32_t off0 = (uint32_t)row * K + vlane + (uint32_t)k * kBK;
 #pragma unroll
-    for (int j = 0; j < 6; ++j) copy_rows(d.rsA, K, k, la, voff0, dodd, j);
-  } else if (part == 1) {
-#pragma unroll
-    for (int j = 0; j < 6; ++j) copy_rows(d.rsB, K, k, lb, voff0, dodd, j);
-  } else {
-#pragma unroll
-    for (int j = 6; j < 8; ++j) {
-      copy_rows(d.rsA, K, k, la, voff0, dodd, j);
-      copy_rows(d.rsB, K, k, lb, voff0, dodd, j);
-    }
-  }
+  for (int j = 0; j < 4; ++j)
+    copy_to_lds(rs, off0 + (uint32_t)(j * 8) * K + ((j & 1) ? dodd : 0u),
+                __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(j * 1024)));
 }
 
 // The tile's epilogue parameters into param buffer pb, one copy per group-0 wave (q).
@@ -396,7 +408,7 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[2][4], const Params& 
 // split tiles
 // ---------------------------------------------------------------------------------------------
 
-// Partial tiles live in a 128 MiB region addressed through one buffer descriptor; their loads
+// Partial tiles live in a 256 MiB region addressed through one buffer descriptor; their loads
 // and stores carry the device-coherence bit (sc1), so they are seen across XCDs without
 // flushing or invalidating caches.
 constexpr int kCoherent = 16;  // sc1
@@ -499,74 +511,113 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
   const int v = (G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b;
   const int nk = p.nk;
   const Work w = work_of(p, v, G);
-  const int dp = w.n_dp * nk;
-  const int nsteps = dp + w.n_parts * p.part_steps;
+  const int nsteps = w.n_dp * nk + w.n_parts * p.part_steps;
   if (nsteps == 0) return;  // more workgroups than items (the whole workgroup leaves)
   const uint32_t uK = (uint32_t)p.K;
 
-  // copy addressing of this lane: rows 64q + (lane >> 3) + 8j, chunk position lane & 7
-  const int row0 = q * 64 + (lane >> 3);
-  const uint32_t cE = (uint32_t)((lane & 7) ^ swz_key(row0));
-  const uint32_t cO = (uint32_t)((lane & 7) ^ swz_key(row0 + 8));
-  const uint32_t voff0 = (uint32_t)row0 * uK + cE * 16u;
-  const uint32_t dodd = (cO - cE) * 16u;  // added (mod 2^32) for odd j
+  // copy addressing of this lane: row (lane >> 3) of an 8-row block, chunk position lane & 7
+  const int r = lane >> 3;
+  const uint32_t cE = (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
+  const uint32_t cO = (uint32_t)((lane & 7) ^ (((r >> 1) + 4) & 7));
+  const uint32_t vlane = (uint32_t)r * uK + cE * 16u;
+  const uint32_t dodd = (cO - cE) * 16u;  // added (mod 2^32) in odd blocks
 
-  // first step, with its tile's parameters
-  int t0, k0s, part0;
-  step_of(p, w, v, G, 0, t0, k0s, part0);
-  TileDesc nd = tile_desc(p, t0);
-  if (g == 0) {
-    copy_part(nd, uK, k0s, lds, voff0, dodd, q, 0);
-    copy_part(nd, uK, k0s, lds, voff0, dodd, q, 2);
-    copy_params<EPI>(p, nd, pbuf, q, lane);
-  } else {
-    copy_part(nd, uK, k0s, lds, voff0, dodd, q, 1);
+  // Pipeline. Step S is read from stage S & 1 in four phases (group 1 runs one phase behind
+  // group 0, and the reading wave of each phase issues one batch after its LDS reads):
+  //   A: G0 reads K half 0 of S;  batch 0 of S + 1 (G0)   G0 waits for batch 2 of S
+  //   B: G1 reads K half 0 of S;  batch 1 of S + 1 (G1)
+  //   C: G0 reads K half 1 of S;  batch 2 of S + 1 (G0)
+  //   D: G1 reads K half 1 of S;  batch 3 of S + 2 (G1)   G0, G1 wait for batches 0, 1, 3 of S + 1
+  // Stage (S + 1) & 1 is free from phase A of S (step S - 1 was read by the end of D of S - 1);
+  // group 0's B rows of stage S & 1 are free from phase D of S (G0 reads them in A and C), so
+  // batch 3 runs one step ahead. Each batch has two to four phases to land, and each wave waits
+  // for its own batches (all but its last batch of four) before the barrier that precedes
+  // their first reader.
+  Cursor c1, c2;  // steps S + 1 and S + 2
+  TileDesc d1, d2;
+  {
+    Cursor c0;
+    c0.item = 0;
+    cursor_item(p, w, v, G, c0);
+    const TileDesc d0 = tile_desc(p, c0.t);
+    if (g == 0) {
+      copy_batch(d0, uK, c0.k, lds, vlane, dodd, q, 0);
+      copy_batch(d0, uK, c0.k, lds, vlane, dodd, q, 1);
+      copy_params<EPI>(p, d0, pbuf, q, lane);
+    } else {
+      copy_batch(d0, uK, c0.k, lds, vlane, dodd, q, 2);
+      copy_batch(d0, uK, c0.k, lds, vlane, dodd, q, 3);
+    }
+    c1 = c0;
+    cursor_next(p, w, v, G, c1);
+    d1 = c1.t != c0.t ? tile_desc(p, c1.t) : d0;
+    c2 = c1;
+    cursor_next(p, w, v, G, c2);
+    d2 = c2.t != c1.t ? tile_desc(p, c2.t) : d1;
   }
   wait_vmem();
   phase_barrier();
-  if (g == 1) phase_barrier();  // group 1 runs one phase behind
+  if (g == 1) {
+    if (nsteps > 1) copy_batch(d1, uK, c1.k, lds + kStageBytes, vlane, dodd, q, 3);
+    phase_barrier();  // group 1 runs one phase behind
+  }
 
   Frags f;
-  int S = 0;     // steps done; step S is in stage buffer S & 1
-  int part = 0;  // parts (runs of steps of one tile) done; part i's parameters in buffer i % 3
+  int S = 0;     // steps done; step S is in stage S & 1
+  int part = 0;  // items done; item i's parameters are in buffer i % 3
+  Cursor c = {0, 0, 0, 0, 0};
+  cursor_item(p, w, v, G, c);
   while (S < nsteps) {
-    int t, k0, cutp;
-    step_of(p, w, v, G, S, t, k0, cutp);
-    const int len = S < dp ? nk : p.part_steps;
+    const int t = c.t, cutp = c.cut, len = c.kend - c.k;
     v16f acc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
     for (int j = 0; j < len; ++j, ++S) {
-      const uint8_t* st = lds + (S & 1) * kStageBytes;
+      uint8_t* st = lds + (S & 1) * kStageBytes;
       uint8_t* st1 = lds + ((S + 1) & 1) * kStageBytes;
-      const bool more = S + 1 < nsteps;
-      int tn = t, kn = 0, pn = 0;
-      if (more) step_of(p, w, v, G, S + 1, tn, kn, pn);
-      const bool starts = more && (j + 1 == len);  // step S + 1 begins the next part
-      if (starts) nd = tile_desc(p, tn);
-      // phase A (G0: reads K half 0 | G1: MFMAs of the previous half)
-      if (more) copy_part(nd, uK, kn, st1, voff0, dodd, q, g);
+      const bool has1 = S + 1 < nsteps, has2 = S + 2 < nsteps;
+      const bool starts = has1 && (j + 1 == len);  // step S + 1 begins the next item
+      // phase A (G0) / B (G1): reads of K half 0, then batch g of step S + 1
       read_frags(st, f, 0, wm, wn, lane);
-      phase_barrier();
-      // phase B (G0: MFMAs of K half 0 | G1: reads K half 0)
-      mma8(f, acc);
-      phase_barrier();
-      // phase C (G0: reads K half 1 | G1: MFMAs of K half 0)
-      if (more && g == 0) {
-        copy_part(nd, uK, kn, st1, voff0, dodd, q, 2);
-        if (starts) copy_params<EPI>(p, nd, pbuf + ((part + 1) % kParamBufs) * kParamBytes, q, lane);
+      if (has1) copy_batch(d1, uK, c1.k, st1, vlane, dodd, q, g);
+      if (g == 0) {
+        if (has1) wait_vmem_but4(); else wait_vmem();  // batch 2 of step S landed
       }
-      read_frags(st, f, 1, wm, wn, lane);
-      if (g == 1) wait_vmem();  // group 1's copies of step S + 1 landed
       phase_barrier();
-      // phase D (G0: MFMAs of K half 1 | G1: reads K half 1)
+      // phase B (G0) / C (G1): MFMAs of K half 0
       mma8(f, acc);
-      if (g == 0) wait_vmem();  // group 0's copies of step S + 1 landed
+      phase_barrier();
+      // phase C (G0) / D (G1): reads of K half 1, then G0: parameters of the next item and
+      // batch 2 of S + 1; G1: batch 3 of S + 2 into this stage, then waits for batches 1, 3
+      read_frags(st, f, 1, wm, wn, lane);
+      if (g == 0) {
+        if (starts)
+          copy_params<EPI>(p, d1, pbuf + ((part + 1) % kParamBufs) * kParamBytes, q, lane);
+        if (has1) copy_batch(d1, uK, c1.k, st1, vlane, dodd, q, 2);
+      } else {
+        if (has2) {
+          copy_batch(d2, uK, c2.k, st, vlane, dodd, q, 3);
+          wait_vmem_but4();
+        } else {
+          wait_vmem();
+        }
+      }
+      phase_barrier();
+      // phase D (G0) / A of S + 1 (G1): MFMAs of K half 1; the cursors move on while the
+      // matrix unit works; G0 waits for batch 0 of S + 1
+      mma8(f, acc);
+      c1 = c2;
+      d1 = d2;
+      cursor_next(p, w, v, G, c2);
+      if (c2.t != c1.t && S + 3 < nsteps) d2 = tile_desc(p, c2.t);
+      if (g == 0) {
+        if (has1) wait_vmem_but4(); else wait_vmem();
+      }
       phase_barrier();
     }
-    const bool cut = len != nk;
+    const bool cut = cutp >= 0;
     bool write = true;
     if (cut) {
       if (g == 0) phase_barrier();  // group 1's last MFMAs of this part are done
@@ -579,6 +630,8 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
     }
     if (cut && g == 1) phase_barrier();  // back to one phase behind
     ++part;
+    ++c.item;
+    if (c.item < w.n_dp + w.n_parts) cursor_item(p, w, v, G, c);
   }
   if (g == 0) phase_barrier();  // matches group 1's extra barrier
 }
