@@ -223,26 +223,43 @@ __device__ __forceinline__ TileDesc tile_desc(const Params& p, int t) {
 // copies
 // ---------------------------------------------------------------------------------------------
 
-// One copy batch: 32 rows (4 x 8 rows of 128 B) of one operand of step k into stage st, 4
-// instructions per wavefront. The batches of a step, for group-0/1 wave q:
+// One copy batch: 32 rows (4 blocks of 8 rows x 128 B) of one operand of step k into stage st,
+// one instruction per block. The batches of a step, for wave q of the copying group:
 //   0: A rows 64q + [0, 32)            1: A rows 64q + [32, 64)
 //   2: B rows that group 1 reads: 128 (q >> 1) + 64 + 32 (q & 1) + [0, 32)
 //   3: B rows that group 0 reads: 128 (q >> 1) + 32 (q & 1) + [0, 32)
-// Lane l lands in LDS slot l of an 8-row block (row l >> 3, position l & 7), so it fetches
-// global chunk (l & 7) ^ key(row); every batch starts at a multiple of 16 rows, so the key
-// depends only on l >> 3 and on the parity of the block (odd blocks add dodd to the offset).
-__device__ __forceinline__ void copy_batch(const TileDesc& d, uint32_t K, int k, uint8_t* st,
-                                           uint32_t vlane, uint32_t dodd, int q, int which) {
+// Lane l lands in LDS slot l of a block (row l >> 3, position l & 7), so it fetches global chunk
+// (l & 7) ^ key(row); every batch starts at a multiple of 16 rows, so the key depends only on
+// l >> 3 and on the parity of the block (odd blocks add dodd to the offset). A batch with
+// `live` false copies from an empty range: its instructions still run (keeping the count of
+// outstanding copies fixed) and write zeros into a region nobody reads any more.
+struct Batch {
+  v4i rs;
+  uint32_t off0, lds0;
+};
+
+__device__ __forceinline__ Batch batch_of(const TileDesc& d, uint32_t K, int k, uint8_t* st,
+                                          uint32_t vlane, int q, int which, bool live) {
   const int row = which < 2 ? q * 64 + which * 32
                             : (q >> 1) * 128 + (q & 1) * 32 + (which == 2 ? 64 : 0);
-  const v4i rs = which < 2 ? d.rsA : d.rsB;
-  const uint32_t lds0 = lds_addr(st) + (which < 2 ? 0u : (uint32_t)(kBM * kBK)) +
-                        (uint32_t)(row * kBK);
-  const uint32_t off0 = (uint32_t)row * K + vlane + (uint32_t)k * kBK;
+  Batch b;
+  b.rs = which < 2 ? d.rsA : d.rsB;
+  if (!live) b.rs[2] = 0;
+  b.lds0 = lds_addr(st) + (which < 2 ? 0u : (uint32_t)(kBM * kBK)) + (uint32_t)(row * kBK);
+  b.off0 = (uint32_t)row * K + vlane + (uint32_t)k * kBK;
+  return b;
+}
+
+__device__ __forceinline__ void copy_block(const Batch& b, uint32_t K, uint32_t dodd, int j) {
+  copy_to_lds(b.rs, b.off0 + (uint32_t)(j * 8) * K + ((j & 1) ? dodd : 0u),
+              __builtin_amdgcn_readfirstlane(b.lds0 + (uint32_t)(j * 1024)));
+}
+
+__device__ __forceinline__ void copy_batch(const TileDesc& d, uint32_t K, int k, uint8_t* st,
+                                           uint32_t vlane, uint32_t dodd, int q, int which) {
+  const Batch b = batch_of(d, K, k, st, vlane, q, which, true);
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    copy_to_lds(rs, off0 + (uint32_t)(j * 8) * K + ((j & 1) ? dodd : 0u),
-                __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(j * 1024)));
+  for (int j = 0; j < 4; ++j) copy_block(b, K, dodd, j);
 }
 
 // The tile's epilogue parameters into param buffer pb, one copy per group-0 wave (q).
@@ -297,13 +314,20 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, Frags& f, int h, i
   }
 }
 
-__device__ __forceinline__ void mma8(const Frags& f, v16f (&acc)[2][4]) {
+// The 8 MFMAs of one K half, with the four copies of batch b issued one after each of the
+// first four: a copy instruction waits for the vector memory unit to take it, which here
+// overlaps the matrix unit's work instead of holding up the next phase.
+__device__ __forceinline__ void mma8_copy(const Frags& f, v16f (&acc)[2][4], const Batch& b,
+                                          uint32_t K, uint32_t dodd) {
 #pragma unroll
   for (int bn = 0; bn < 2; ++bn)
 #pragma unroll
-    for (int bm = 0; bm < 4; ++bm)
+    for (int bm = 0; bm < 4; ++bm) {
       acc[bn][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[bn], f.a[bm], acc[bn][bm],
                                                                      0, 0, 0, 0, 0, 0);
+      if (bn == 0) copy_block(b, K, dodd, bm);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -522,17 +546,19 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
   const uint32_t vlane = (uint32_t)r * uK + cE * 16u;
   const uint32_t dodd = (cO - cE) * 16u;  // added (mod 2^32) in odd blocks
 
-  // Pipeline. Step S is read from stage S & 1 in four phases (group 1 runs one phase behind
-  // group 0, and the reading wave of each phase issues one batch after its LDS reads):
-  //   A: G0 reads K half 0 of S;  batch 0 of S + 1 (G0)   G0 waits for batch 2 of S
-  //   B: G1 reads K half 0 of S;  batch 1 of S + 1 (G1)
-  //   C: G0 reads K half 1 of S;  batch 2 of S + 1 (G0)
-  //   D: G1 reads K half 1 of S;  batch 3 of S + 2 (G1)   G0, G1 wait for batches 0, 1, 3 of S + 1
+  // Pipeline. Step S is read from stage S & 1 in four phases; group 1 runs one phase behind
+  // group 0, so in every phase one wave per SIMD reads fragments and the other issues its MFMAs
+  // together with one copy batch (4 instructions):
+  //   phase A: G0 reads K half 0 of S   | G1 MFMAs (half 1 of S - 1) + batch 0 of S + 1
+  //   phase B: G1 reads K half 0 of S   | G0 MFMAs (half 0 of S)     + batch 1 of S + 1
+  //   phase C: G0 reads K half 1 of S   | G1 MFMAs (half 0 of S)     + batch 2 of S + 1
+  //   phase D: G1 reads K half 1 of S   | G0 MFMAs (half 1 of S)     + batch 3 of S + 2
   // Stage (S + 1) & 1 is free from phase A of S (step S - 1 was read by the end of D of S - 1);
-  // group 0's B rows of stage S & 1 are free from phase D of S (G0 reads them in A and C), so
-  // batch 3 runs one step ahead. Each batch has two to four phases to land, and each wave waits
-  // for its own batches (all but its last batch of four) before the barrier that precedes
-  // their first reader.
+  // group 0's B rows of stage S & 1 are free from phase D of S (G0 read them in A and C), so
+  // batch 3 runs one step ahead. Each wave waits for its own batches before the barrier that
+  // precedes their first reader: G1 at the end of D (batch 0), G0 at the end of D (batch 1, and
+  // batch 3 of the step before), G1 at the end of A (batch 2); every batch has two to four
+  // phases to land.
   Cursor c1, c2;  // steps S + 1 and S + 2
   TileDesc d1, d2;
   {
@@ -557,10 +583,10 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
   }
   wait_vmem();
   phase_barrier();
-  if (g == 1) {
-    if (nsteps > 1) copy_batch(d1, uK, c1.k, lds + kStageBytes, vlane, dodd, q, 3);
-    phase_barrier();  // group 1 runs one phase behind
-  }
+  // batch 3 of step 1 (G0, as in phase D of step -1) and batch 0 of step 1 (G1, as in its
+  // MFMA phase of step -1), then group 1 falls one phase behind
+  if (nsteps > 1) copy_batch(d1, uK, c1.k, lds + kStageBytes, vlane, dodd, q, g == 0 ? 3 : 0);
+  if (g == 1) phase_barrier();
 
   Frags f;
   int S = 0;     // steps done; step S is in stage S & 1
@@ -579,42 +605,31 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
       uint8_t* st1 = lds + ((S + 1) & 1) * kStageBytes;
       const bool has1 = S + 1 < nsteps, has2 = S + 2 < nsteps;
       const bool starts = has1 && (j + 1 == len);  // step S + 1 begins the next item
-      // phase A (G0) / B (G1): reads of K half 0, then batch g of step S + 1
+      // reads of K half 0 (G0: phase A, G1: phase B)
       read_frags(st, f, 0, wm, wn, lane);
-      if (has1) copy_batch(d1, uK, c1.k, st1, vlane, dodd, q, g);
-      if (g == 0) {
-        if (has1) wait_vmem_but4(); else wait_vmem();  // batch 2 of step S landed
-      }
       phase_barrier();
-      // phase B (G0) / C (G1): MFMAs of K half 0
-      mma8(f, acc);
+      // MFMAs of K half 0 with batch g + 1 of step S + 1 (G0: phase B, G1: phase C)
+      mma8_copy(f, acc, batch_of(d1, uK, c1.k, st1, vlane, q, g + 1, has1), uK, dodd);
       phase_barrier();
-      // phase C (G0) / D (G1): reads of K half 1, then G0: parameters of the next item and
-      // batch 2 of S + 1; G1: batch 3 of S + 2 into this stage, then waits for batches 1, 3
+      // reads of K half 1 (G0: phase C, G1: phase D); G0 starts the next item's parameters,
+      // G1 waits for its batch 0 of step S + 1
       read_frags(st, f, 1, wm, wn, lane);
       if (g == 0) {
         if (starts)
           copy_params<EPI>(p, d1, pbuf + ((part + 1) % kParamBufs) * kParamBytes, q, lane);
-        if (has1) copy_batch(d1, uK, c1.k, st1, vlane, dodd, q, 2);
       } else {
-        if (has2) {
-          copy_batch(d2, uK, c2.k, st, vlane, dodd, q, 3);
-          wait_vmem_but4();
-        } else {
-          wait_vmem();
-        }
+        if (has1) wait_vmem_but4(); else wait_vmem();
       }
       phase_barrier();
-      // phase D (G0) / A of S + 1 (G1): MFMAs of K half 1; the cursors move on while the
-      // matrix unit works; G0 waits for batch 0 of S + 1
-      mma8(f, acc);
+      // MFMAs of K half 1 (G0: phase D, G1: phase A of S + 1) with batch 3 (G0) or 0 (G1) of
+      // step S + 2, into this stage; the cursors move on meanwhile; then every wave waits for
+      // all but that batch
+      mma8_copy(f, acc, batch_of(d2, uK, c2.k, st, vlane, q, g == 0 ? 3 : 0, has2), uK, dodd);
       c1 = c2;
       d1 = d2;
       cursor_next(p, w, v, G, c2);
       if (c2.t != c1.t && S + 3 < nsteps) d2 = tile_desc(p, c2.t);
-      if (g == 0) {
-        if (has1) wait_vmem_but4(); else wait_vmem();
-      }
+      wait_vmem_but4();
       phase_barrier();
     }
     const bool cut = cutp >= 0;
@@ -634,6 +649,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
     if (c.item < w.n_dp + w.n_parts) cursor_item(p, w, v, G, c);
   }
   if (g == 0) phase_barrier();  // matches group 1's extra barrier
+  wait_vmem();                  // the empty batches of the last two steps
 }
 
 template <int EPI>
