@@ -9,9 +9,11 @@
 //   * a persistent grid of G <= (compute units) workgroups taking work items round-robin
 //     (workgroup v takes items v, v + G, ...), so the workgroups of an XCD hold neighbouring
 //     items, step through K together and share A and B slices in L2. The items are the tiles of
-//     the full rounds (T - T mod G of them), then the T mod G tiles left over. With a workspace
-//     the left-over tiles may be cut along K into s equal parts (s divides the step count, and
-//     is chosen on the host by counting steps), the parts ordered so that neighbouring
+//     the full rounds (T - T mod G of them), then the T mod G tiles left over. When the
+//     left-over tiles fit on half the compute units they run as two 256 x 128 halves each, in a
+//     second launch of the kernel built for that width (one wave then owns 128 x 32). With a
+//     workspace the left-over tiles may instead be cut along K into s equal parts (s divides the
+//     step count; the host picks by counting steps), the parts ordered so that neighbouring
 //     workgroups hold neighbouring tiles at the same K range: the last round then keeps the
 //     compute units busy. The parts of a cut tile are summed in fp32 through the workspace by
 //     the part that finishes last (an arrival counter per tile; no workgroup ever waits for
@@ -84,10 +86,12 @@ struct Params {
   uint32_t* flags;           // [tiles] arrival counters (cut tiles only)
   float* part;               // [parts][256 * 256] partial tiles (cut tiles only)
   int M, N, K, tilesM, tilesN, nk, tiles;
-  int dp_tiles;              // tiles of the full rounds (a multiple of the grid size)
-  int tail_tiles;            // tiles - dp_tiles
+  int dp_tiles;              // tiles of full rounds run by this launch (a multiple of the grid)
+  int tail0;                 // first left-over tile
+  int tail_tiles;            // left-over tiles run by this launch
   int splits;                // parts per left-over tile (1: not cut)
   int part_steps;            // nk / splits
+  int narrow;                // 1: each left-over tile runs as two 256 x 128 halves (not cut)
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -145,9 +149,10 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 // schedule: shares, tiles, contributors
 // ---------------------------------------------------------------------------------------------
 
-// Workgroup v's items: n_dp whole tiles v, v + G, ... of the full rounds, then n_parts parts
-// p = v, v + G, ... of the left-over tiles (part p: tile dp_tiles + p % tail_tiles, steps
-// [j part_steps, (j + 1) part_steps), j = p / tail_tiles).
+// Workgroup v's items: n_dp whole tiles v, v + G, ... of the full rounds, then n_parts items
+// u = v, v + G, ... of the left-over tiles: either parts (part u: tile tail0 + u % tail_tiles,
+// steps [j part_steps, (j + 1) part_steps), j = u / tail_tiles) or, with narrow, halves (half
+// u & 1, columns [128 (u & 1), + 128), of tile tail0 + (u >> 1)).
 struct Work {
   int n_dp, n_parts;
 };
@@ -155,41 +160,49 @@ struct Work {
 __device__ __forceinline__ Work work_of(const Params& p, int v, int G) {
   Work w;
   w.n_dp = p.dp_tiles / G;
-  const int P = p.tail_tiles * p.splits;
+  const int P = p.narrow ? 2 * p.tail_tiles : p.tail_tiles * p.splits;
   w.n_parts = v < P ? (P - v + G - 1) / G : 0;
   return w;
 }
 
 // A position in a workgroup's sequence of steps: work item `item`, its tile t, its part of a
-// cut tile (-1: a whole tile), the K step k and the item's end step kend. Moving one step on costs an
-// increment; the divisions happen once per item.
+// cut tile (-1: not cut), its half of a narrow tile (-1: full width), the K step k and the
+// item's end step kend. Moving one step on costs an increment; the divisions happen once per
+// item.
 struct Cursor {
-  int item, t, cut, k, kend;
+  int item, t, cut, half, k, kend;
 };
 
+template <int NB>
 __device__ __forceinline__ void cursor_item(const Params& p, const Work& w, int v, int G,
                                             Cursor& c) {
+  c.cut = -1;
+  c.half = -1;
+  c.k = 0;
+  c.kend = p.nk;
   if (c.item < w.n_dp) {
     c.t = v + c.item * G;
-    c.cut = -1;
-    c.k = 0;
-    c.kend = p.nk;
+  } else if (NB == 1) {  // a launch of narrow halves
+    const int u = v + (c.item - w.n_dp) * G;
+    c.t = p.tail0 + (u >> 1);
+    c.half = u & 1;
   } else {
     const int part = v + (c.item - w.n_dp) * G;
     const int j = part / p.tail_tiles;
-    c.t = p.dp_tiles + (part - j * p.tail_tiles);
-    c.cut = p.splits > 1 ? part : -1;
+    c.t = p.tail0 + (part - j * p.tail_tiles);
+    if (p.splits > 1) c.cut = part;
     c.k = j * p.part_steps;
     c.kend = c.k + p.part_steps;
   }
 }
 
 // The next step; past the last one the cursor keeps its tile (and is not used).
+template <int NB>
 __device__ __forceinline__ void cursor_next(const Params& p, const Work& w, int v, int G,
                                             Cursor& c) {
   if (++c.k == c.kend) {
     ++c.item;
-    if (c.item < w.n_dp + w.n_parts) cursor_item(p, w, v, G, c);
+    if (c.item < w.n_dp + w.n_parts) cursor_item<NB>(p, w, v, G, c);
   }
 }
 
@@ -204,18 +217,30 @@ __device__ __forceinline__ void tile_origin(const Params& p, int t, int& m0, int
 }
 
 struct TileDesc {
-  int m0, n0;
+  int m0, n0;  // origin of the tile (of the half, in a narrow launch)
   v4i rsA, rsB;
 };
 
-// per-tile descriptors: rows past M (N) are out of range and read as zero
-__device__ __forceinline__ TileDesc tile_desc(const Params& p, int t) {
+// Descriptors of a tile or of one half of it: rows past M (N) are out of range and read as
+// zero (a half entirely past N has an empty B range).
+// Origin of tile t, or of its 128-column half (half >= 0, narrow launches only).
+template <int NB>
+__device__ __forceinline__ void item_origin(const Params& p, int t, int half, int& m0, int& n0) {
+  tile_origin(p, t, m0, n0);
+  if (NB == 1) n0 += half * (kBN / 2);
+}
+
+template <int NB>
+__device__ __forceinline__ TileDesc tile_desc(const Params& p, int t, int half) {
   TileDesc d;
-  tile_origin(p, t, d.m0, d.n0);
-  const uint32_t rowsA = (uint32_t)(p.M - d.m0 < kBM ? p.M - d.m0 : kBM);
-  const uint32_t rowsB = (uint32_t)(p.N - d.n0 < kBN ? p.N - d.n0 : kBN);
-  d.rsA = buffer_rsrc(p.A + (size_t)d.m0 * (size_t)p.K, rowsA * (uint32_t)p.K);
-  d.rsB = buffer_rsrc(p.B + (size_t)d.n0 * (size_t)p.K, rowsB * (uint32_t)p.K);
+  item_origin<NB>(p, t, half, d.m0, d.n0);
+  const int m0 = d.m0, n0 = d.n0;
+  const int width = NB == 1 ? kBN / 2 : kBN;
+  const int rb = p.N - n0 < width ? p.N - n0 : width;
+  const uint32_t rowsA = (uint32_t)(p.M - m0 < kBM ? p.M - m0 : kBM);
+  const uint32_t rowsB = (uint32_t)(rb > 0 ? rb : 0);
+  d.rsA = buffer_rsrc(p.A + (size_t)m0 * (size_t)p.K, rowsA * (uint32_t)p.K);
+  d.rsB = buffer_rsrc(p.B + (size_t)(rb > 0 ? n0 : 0) * (size_t)p.K, rowsB * (uint32_t)p.K);
   return d;
 }
 
@@ -228,36 +253,65 @@ __device__ __forceinline__ TileDesc tile_desc(const Params& p, int t) {
 //   0: A rows 64q + [0, 32)            1: A rows 64q + [32, 64)
 //   2: B rows that group 1 reads: 128 (q >> 1) + 64 + 32 (q & 1) + [0, 32)
 //   3: B rows that group 0 reads: 128 (q >> 1) + 32 (q & 1) + [0, 32)
+// B rows sit in LDS at their tile row. In a narrow (256 x 128) tile group 0 reads tile rows
+// [0, 32) and [64, 96), group 1 rows [32, 64) and [96, 128); they sit at LDS rows [0, 64) and
+// [64, 128), inside the rows each group reads in a full tile, so that either kind of step can
+// follow the other in a stage. A narrow B batch has 16 rows per wave (tile rows
+// 64 (q >> 1) + 32 [group 1] + 16 (q & 1) + [0, 16), LDS rows 64 [group 1] + 16 q + [0, 16));
+// its two other instructions copy from an empty range into rows no narrow step reads (group 0:
+// [128, 192), group 1: [192, 256)), so that every batch is four instructions.
 // Lane l lands in LDS slot l of a block (row l >> 3, position l & 7), so it fetches global chunk
-// (l & 7) ^ key(row); every batch starts at a multiple of 16 rows, so the key depends only on
-// l >> 3 and on the parity of the block (odd blocks add dodd to the offset). A batch with
-// `live` false copies from an empty range: its instructions still run (keeping the count of
-// outstanding copies fixed) and write zeros into a region nobody reads any more.
+// (l & 7) ^ key(row); every block starts 16 LDS rows after a multiple of 16 plus 8 for odd
+// blocks, so the key depends only on l >> 3 and on the parity of the block (odd blocks add dodd
+// to the offset). A batch with `live` false copies from an empty range: its instructions still
+// run (keeping the count of outstanding copies fixed) and write zeros into a region nobody
+// reads any more.
 struct Batch {
-  v4i rs;
-  uint32_t off0, lds0;
+  v4i rs01, rs23;        // blocks 0-1 and 2-3
+  uint32_t off0, lds01, lds23;
 };
 
+template <int NB>
 __device__ __forceinline__ Batch batch_of(const TileDesc& d, uint32_t K, int k, uint8_t* st,
                                           uint32_t vlane, int q, int which, bool live) {
-  const int row = which < 2 ? q * 64 + which * 32
-                            : (q >> 1) * 128 + (q & 1) * 32 + (which == 2 ? 64 : 0);
   Batch b;
-  b.rs = which < 2 ? d.rsA : d.rsB;
-  if (!live) b.rs[2] = 0;
-  b.lds0 = lds_addr(st) + (which < 2 ? 0u : (uint32_t)(kBM * kBK)) + (uint32_t)(row * kBK);
-  b.off0 = (uint32_t)row * K + vlane + (uint32_t)k * kBK;
+  const uint32_t base = lds_addr(st);
+  int grow, lrow;
+  if (which < 2) {
+    grow = lrow = q * 64 + which * 32;
+    b.rs01 = d.rsA;
+  } else {
+    b.rs01 = d.rsB;
+    if (NB == 2) {
+      grow = lrow = (q >> 1) * 128 + (q & 1) * 32 + (which == 2 ? 64 : 0);
+    } else {
+      grow = (q >> 1) * 64 + (q & 1) * 16 + (which == 2 ? 32 : 0);
+      lrow = (which == 2 ? 64 : 0) + q * 16;
+    }
+  }
+  if (!live) b.rs01[2] = 0;
+  b.rs23 = b.rs01;
+  const uint32_t region = base + (which < 2 ? 0u : (uint32_t)(kBM * kBK));
+  b.lds01 = region + (uint32_t)(lrow * kBK);
+  b.lds23 = b.lds01 + 2048u;
+  if (NB == 1 && which >= 2) {  // narrow: blocks 2-3 are empty copies into unread rows
+    b.rs23[2] = 0;
+    b.lds23 = region + (uint32_t)(((which == 2 ? 192 : 128) + q * 16) * kBK);
+  }
+  b.off0 = (uint32_t)grow * K + vlane + (uint32_t)k * kBK;
   return b;
 }
 
 __device__ __forceinline__ void copy_block(const Batch& b, uint32_t K, uint32_t dodd, int j) {
-  copy_to_lds(b.rs, b.off0 + (uint32_t)(j * 8) * K + ((j & 1) ? dodd : 0u),
-              __builtin_amdgcn_readfirstlane(b.lds0 + (uint32_t)(j * 1024)));
+  copy_to_lds(j < 2 ? b.rs01 : b.rs23, b.off0 + (uint32_t)(j * 8) * K + ((j & 1) ? dodd : 0u),
+              __builtin_amdgcn_readfirstlane((j < 2 ? b.lds01 : b.lds23) +
+                                             (uint32_t)((j & 1) * 1024)));
 }
 
+template <int NB>
 __device__ __forceinline__ void copy_batch(const TileDesc& d, uint32_t K, int k, uint8_t* st,
                                            uint32_t vlane, uint32_t dodd, int q, int which) {
-  const Batch b = batch_of(d, K, k, st, vlane, q, which, true);
+  const Batch b = batch_of<NB>(d, K, k, st, vlane, q, which, true);
 #pragma unroll
   for (int j = 0; j < 4; ++j) copy_block(b, K, dodd, j);
 }
@@ -266,18 +320,23 @@ __device__ __forceinline__ void copy_batch(const TileDesc& d, uint32_t K, int k,
 template <int EPI>
 __device__ __forceinline__ void copy_params(const Params& p, const TileDesc& d, uint8_t* pb, int q,
                                             int lane) {
+  const int m0 = d.m0;
+  int n0 = d.n0;
   const uint32_t lp = __builtin_amdgcn_readfirstlane(lds_addr(pb) + (uint32_t)(q * 1024));
   const uint32_t lo = (uint32_t)lane * 16u;
-  const uint32_t rows = (uint32_t)(p.M - d.m0 < kBM ? p.M - d.m0 : kBM);
-  const uint32_t cols = (uint32_t)(p.N - d.n0 < kBN ? p.N - d.n0 : kBN);
+  const uint32_t rows = (uint32_t)(p.M - m0 < kBM ? p.M - m0 : kBM);
+  // columns of this tile that exist: none for a narrow half that lies past N
+  const int nc = p.N - n0 < kBN ? p.N - n0 : kBN;
+  const uint32_t cols = (uint32_t)(nc > 0 ? nc : 0);
+  if (nc <= 0) n0 = 0;
   if (q == 0) {
-    copy_to_lds(buffer_rsrc(p.sa + d.m0, rows * 4u), lo, lp);
+    copy_to_lds(buffer_rsrc(p.sa + m0, rows * 4u), lo, lp);
   } else if (q == 1) {
-    copy_to_lds(buffer_rsrc(p.sw + d.n0, cols * 4u), lo, lp);
+    copy_to_lds(buffer_rsrc(p.sw + n0, cols * 4u), lo, lp);
   } else if (q == 2) {
-    copy_to_lds(buffer_rsrc(p.bias + d.n0, p.bias ? cols * 2u : 0u), lo, lp);
+    copy_to_lds(buffer_rsrc(p.bias + n0, p.bias ? cols * 2u : 0u), lo, lp);
   } else if (EPI == EPI_GATED_RESIDUAL) {
-    copy_to_lds(buffer_rsrc(p.gate + d.n0, cols * 2u), lo, lp);
+    copy_to_lds(buffer_rsrc(p.gate + n0, cols * 2u), lo, lp);
   }
 }
 
@@ -287,11 +346,14 @@ __device__ __forceinline__ void copy_params(const Params& p, const TileDesc& d, 
 
 struct Frags {
   v8i a[4];  // rows wm * 128 + 32 i + (lane & 31) of the A tile
-  v8i b[2];  // rows wn * 64 + 32 i + (lane & 31) of the B tile
+  v8i b[2];  // B rows: full tile wn * 64 + 32 i + (lane & 31); narrow tile only b[0]
 };
 
 // Fragments of K half h (64 bytes) of one staged step: lane l reads row l & 31 of each 32-row
-// block, bytes [64 h + 32 (l >> 5), +32) -- the same K positions for A and B.
+// block, bytes [64 h + 32 (l >> 5), +32) -- the same K positions for A and B. NB is the number
+// of 32-column blocks per wave: 2 in a full tile; 1 in a narrow one, whose block (tile rows
+// 32 wn + [0, 32)) sits at LDS rows 64 g + 32 (q & 1) + [0, 32).
+template <int NB>
 __device__ __forceinline__ void read_frags(const uint8_t* st, Frags& f, int h, int wm, int wn,
                                            int lane) {
   const int r = lane & 31;
@@ -304,9 +366,11 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, Frags& f, int h, i
     f.a[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
+  // for NB == 1: 32 wn = 64 (q & 1) + 32 g, stored at 64 g + 32 (q & 1)
+  const int b0 = NB == 2 ? wn * 64 : (wn & 1) * 64 + (wn >> 1) * 32;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint8_t* bb = st + kBM * kBK + (wn * 64 + i * 32) * kBK;
+  for (int i = 0; i < NB; ++i) {
+    const uint8_t* bb = st + kBM * kBK + (b0 + i * 32) * kBK;
     const uint4 lo = *reinterpret_cast<const uint4*>(bb + swz(r, c0));
     const uint4 hi = *reinterpret_cast<const uint4*>(bb + swz(r, c0 + 1));
     f.b[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
@@ -314,13 +378,14 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, Frags& f, int h, i
   }
 }
 
-// The 8 MFMAs of one K half, with the four copies of batch b issued one after each of the
-// first four: a copy instruction waits for the vector memory unit to take it, which here
+// The MFMAs of one K half (8, or 4 in a narrow tile), with the four copies of batch b issued one
+// after each of the first four: a copy instruction waits for the vector memory unit to take it, which here
 // overlaps the matrix unit's work instead of holding up the next phase.
-__device__ __forceinline__ void mma8_copy(const Frags& f, v16f (&acc)[2][4], const Batch& b,
+template <int NB>
+__device__ __forceinline__ void mma8_copy(const Frags& f, v16f (&acc)[NB][4], const Batch& b,
                                           uint32_t K, uint32_t dodd) {
 #pragma unroll
-  for (int bn = 0; bn < 2; ++bn)
+  for (int bn = 0; bn < NB; ++bn)
 #pragma unroll
     for (int bm = 0; bm < 4; ++bm) {
       acc[bn][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[bn], f.a[bm], acc[bn][bm],
@@ -362,8 +427,8 @@ __device__ __forceinline__ void swap_halves(float& a, float& b) {
 // Per pair of 8-column groups, each lane computes v for its 4 + 4 columns, swaps halves with its
 // partner lane (l <-> l + 32) so that it holds 8 consecutive columns of one group, applies the
 // activation or the gated residual there, and stores 16 bytes.
-template <int EPI>
-__device__ __forceinline__ void epilogue(const v16f (&acc)[2][4], const Params& p, int m0, int n0,
+template <int EPI, int NB>
+__device__ __forceinline__ void epilogue(const v16f (&acc)[NB][4], const Params& p, int m0, int n0,
                                          int wm, int wn, int lane, const uint8_t* pb) {
   const float* s_sa = reinterpret_cast<const float*>(pb);
   const float* s_sw = reinterpret_cast<const float*>(pb + 1024);
@@ -376,14 +441,14 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[2][4], const Params& 
     const int m = m0 + ml;
     const float sam = s_sa[ml];
 #pragma unroll
-    for (int bn = 0; bn < 2; ++bn) {
+    for (int bn = 0; bn < NB; ++bn) {
 #pragma unroll
       for (int gp = 0; gp < 2; ++gp) {
         float v[2][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int g = gp * 2 + h;
-          const int nl = wn * 64 + bn * 32 + g * 8 + hi * 4;
+          const int nl = wn * 32 * NB + bn * 32 + g * 8 + hi * 4;
           const float4 swv = *reinterpret_cast<const float4*>(s_sw + nl);
           const uint2 bb = *reinterpret_cast<const uint2*>(s_b + nl);
           v[h][0] = fmaf(acc[bn][bm][g * 4 + 0] * sam, swv.x, bf16_lo(bb.x));
@@ -396,7 +461,7 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[2][4], const Params& 
         // (v[0] = columns 0-3, v[1] = columns 4-7) and lane l + 32 owns group 2gp + 1.
 #pragma unroll
         for (int j = 0; j < 4; ++j) swap_halves(v[0][j], v[1][j]);
-        const int nl = wn * 64 + bn * 32 + (gp * 2 + hi) * 8;
+        const int nl = wn * 32 * NB + bn * 32 + (gp * 2 + hi) * 8;
         const int n = n0 + nl;
         float y[8] = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
         if (EPI == EPI_GELU_TANH) {
@@ -503,7 +568,7 @@ __device__ bool finish_split(v16f (&acc)[2][4], const Params& p, int t, int part
   }
   phase_barrier();
   if (!*s_last) return false;
-  const int tt = t - p.dp_tiles;
+  const int tt = t - p.tail0;
   for (int j = 0; j < p.splits; ++j) {
     const uint32_t slot = part_slot(j * p.tail_tiles + tt);
     if (j == 0)
@@ -520,7 +585,12 @@ __device__ bool finish_split(v16f (&acc)[2][4], const Params& p, int t, int part
 // kernel
 // ---------------------------------------------------------------------------------------------
 
-template <int EPI>
+__device__ __forceinline__ bool same_tile(const Cursor& a, const Cursor& b) {
+  return a.t == b.t && a.half == b.half;
+}
+
+// NB = 2: whole tiles and cut parts; NB = 1: the narrow halves of left-over tiles.
+template <int EPI, int NB>
 __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes + kParamBufs * kParamBytes];
   __shared__ int s_last;
@@ -564,40 +634,42 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
   {
     Cursor c0;
     c0.item = 0;
-    cursor_item(p, w, v, G, c0);
-    const TileDesc d0 = tile_desc(p, c0.t);
+    cursor_item<NB>(p, w, v, G, c0);
+    const TileDesc d0 = tile_desc<NB>(p, c0.t, c0.half);
     if (g == 0) {
-      copy_batch(d0, uK, c0.k, lds, vlane, dodd, q, 0);
-      copy_batch(d0, uK, c0.k, lds, vlane, dodd, q, 1);
+      copy_batch<NB>(d0, uK, c0.k, lds, vlane, dodd, q, 0);
+      copy_batch<NB>(d0, uK, c0.k, lds, vlane, dodd, q, 1);
       copy_params<EPI>(p, d0, pbuf, q, lane);
     } else {
-      copy_batch(d0, uK, c0.k, lds, vlane, dodd, q, 2);
-      copy_batch(d0, uK, c0.k, lds, vlane, dodd, q, 3);
+      copy_batch<NB>(d0, uK, c0.k, lds, vlane, dodd, q, 2);
+      copy_batch<NB>(d0, uK, c0.k, lds, vlane, dodd, q, 3);
     }
     c1 = c0;
-    cursor_next(p, w, v, G, c1);
-    d1 = c1.t != c0.t ? tile_desc(p, c1.t) : d0;
+    cursor_next<NB>(p, w, v, G, c1);
+    d1 = same_tile(c1, c0) ? d0 : tile_desc<NB>(p, c1.t, c1.half);
     c2 = c1;
-    cursor_next(p, w, v, G, c2);
-    d2 = c2.t != c1.t ? tile_desc(p, c2.t) : d1;
+    cursor_next<NB>(p, w, v, G, c2);
+    d2 = same_tile(c2, c1) ? d1 : tile_desc<NB>(p, c2.t, c2.half);
   }
   wait_vmem();
   phase_barrier();
   // batch 3 of step 1 (G0, as in phase D of step -1) and batch 0 of step 1 (G1, as in its
   // MFMA phase of step -1), then group 1 falls one phase behind
-  if (nsteps > 1) copy_batch(d1, uK, c1.k, lds + kStageBytes, vlane, dodd, q, g == 0 ? 3 : 0);
+  if (nsteps > 1)
+    copy_batch<NB>(d1, uK, c1.k, lds + kStageBytes, vlane, dodd, q, g == 0 ? 3 : 0);
   if (g == 1) phase_barrier();
 
   Frags f;
   int S = 0;     // steps done; step S is in stage S & 1
   int part = 0;  // items done; item i's parameters are in buffer i % 3
-  Cursor c = {0, 0, 0, 0, 0};
-  cursor_item(p, w, v, G, c);
+  Cursor c;
+  c.item = 0;
+  cursor_item<NB>(p, w, v, G, c);
   while (S < nsteps) {
-    const int t = c.t, cutp = c.cut, len = c.kend - c.k;
-    v16f acc[2][4];
+    const int t = c.t, half = c.half, cutp = c.cut, len = c.kend - c.k;
+    v16f acc[NB][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
     for (int j = 0; j < len; ++j, ++S) {
@@ -606,14 +678,14 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
       const bool has1 = S + 1 < nsteps, has2 = S + 2 < nsteps;
       const bool starts = has1 && (j + 1 == len);  // step S + 1 begins the next item
       // reads of K half 0 (G0: phase A, G1: phase B)
-      read_frags(st, f, 0, wm, wn, lane);
+      read_frags<NB>(st, f, 0, wm, wn, lane);
       phase_barrier();
       // MFMAs of K half 0 with batch g + 1 of step S + 1 (G0: phase B, G1: phase C)
-      mma8_copy(f, acc, batch_of(d1, uK, c1.k, st1, vlane, q, g + 1, has1), uK, dodd);
+      mma8_copy<NB>(f, acc, batch_of<NB>(d1, uK, c1.k, st1, vlane, q, g + 1, has1), uK, dodd);
       phase_barrier();
       // reads of K half 1 (G0: phase C, G1: phase D); G0 starts the next item's parameters,
       // G1 waits for its batch 0 of step S + 1
-      read_frags(st, f, 1, wm, wn, lane);
+      read_frags<NB>(st, f, 1, wm, wn, lane);
       if (g == 0) {
         if (starts)
           copy_params<EPI>(p, d1, pbuf + ((part + 1) % kParamBufs) * kParamBytes, q, lane);
@@ -624,38 +696,56 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
       // MFMAs of K half 1 (G0: phase D, G1: phase A of S + 1) with batch 3 (G0) or 0 (G1) of
       // step S + 2, into this stage; the cursors move on meanwhile; then every wave waits for
       // all but that batch
-      mma8_copy(f, acc, batch_of(d2, uK, c2.k, st, vlane, q, g == 0 ? 3 : 0, has2), uK, dodd);
+      mma8_copy<NB>(f, acc, batch_of<NB>(d2, uK, c2.k, st, vlane, q, g == 0 ? 3 : 0, has2), uK,
+                    dodd);
       c1 = c2;
       d1 = d2;
-      cursor_next(p, w, v, G, c2);
-      if (c2.t != c1.t && S + 3 < nsteps) d2 = tile_desc(p, c2.t);
+      cursor_next<NB>(p, w, v, G, c2);
+      if (!same_tile(c2, c1) && S + 3 < nsteps) d2 = tile_desc<NB>(p, c2.t, c2.half);
       wait_vmem_but4();
       phase_barrier();
     }
-    const bool cut = cutp >= 0;
-    bool write = true;
-    if (cut) {
-      if (g == 0) phase_barrier();  // group 1's last MFMAs of this part are done
-      write = finish_split(acc, p, t, cutp, wave, lane, &s_last);
+    int m0, n0;
+    item_origin<NB>(p, t, half, m0, n0);
+    const uint8_t* pb = pbuf + (part % kParamBufs) * kParamBytes;
+    if constexpr (NB == 2) {
+      const bool cut = cutp >= 0;
+      bool write = true;
+      if (cut) {
+        if (g == 0) phase_barrier();  // group 1's last MFMAs of this part are done
+        write = finish_split(acc, p, t, cutp, wave, lane, &s_last);
+      }
+      if (write) epilogue<EPI, 2>(acc, p, m0, n0, wm, wn, lane, pb);
+      if (cut && g == 1) phase_barrier();  // back to one phase behind
+    } else {
+      epilogue<EPI, 1>(acc, p, m0, n0, wm, wn, lane, pb);
     }
-    if (write) {
-      int m0, n0;
-      tile_origin(p, t, m0, n0);
-      epilogue<EPI>(acc, p, m0, n0, wm, wn, lane, pbuf + (part % kParamBufs) * kParamBytes);
-    }
-    if (cut && g == 1) phase_barrier();  // back to one phase behind
     ++part;
     ++c.item;
-    if (c.item < w.n_dp + w.n_parts) cursor_item(p, w, v, G, c);
+    if (c.item < w.n_dp + w.n_parts) cursor_item<NB>(p, w, v, G, c);
   }
   if (g == 0) phase_barrier();  // matches group 1's extra barrier
   wait_vmem();                  // the empty batches of the last two steps
 }
 
 template <int EPI>
-hipError_t launch_epi(const Params& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(gemm_fp8_pp<EPI>, dim3(grid), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+hipError_t launch_epi(const Params& p, int grid, int narrow_grid, hipStream_t stream) {
+  if (grid > 0) {
+    Params a = p;
+    if (narrow_grid > 0) a.tail_tiles = 0;  // the halves run in the second launch
+    a.narrow = 0;
+    hipLaunchKernelGGL((gemm_fp8_pp<EPI, 2>), dim3(grid), dim3(kThreads), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (narrow_grid > 0) {
+    Params b = p;
+    b.dp_tiles = 0;
+    b.narrow = 1;
+    hipLaunchKernelGGL((gemm_fp8_pp<EPI, 1>), dim3(narrow_grid), dim3(kThreads), 0, stream, b);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 // Compute units of the current device, queried once per device.
@@ -697,53 +787,73 @@ hipError_t launch_linear(const uint8_t* q, const float* scale, int64_t M, int64_
   p.nk = (int)(K / kBK);
   p.tiles = (int)linear_tiles(M, N);
   const int cus = compute_units();
-  // Full rounds of whole tiles, then the left-over tiles, cut into s parts along K when a
-  // workspace is given and a count of the work says it pays by 20 % or more. Counted in steps
-  // (one step is about 1.5 us on a busy chip): the last round takes ceil(left s / G) parts of
-  // nk / s steps per workgroup, every part stores a 256 x 256 fp32 partial tile, and the part
-  // that finishes a tile loads the s - 1 others; a partial tile moves at the compute unit's
-  // share of HBM bandwidth (at most about 60 GB/s for one unit, 5.6 TB/s for the chip).
+  // Full rounds of whole tiles (one per compute unit), then the T mod G tiles left over, run
+  // one of three ways, chosen by counting steps of the last round:
+  //   whole tiles: nk steps;
+  //   narrow halves (when all halves fit on the device at once): a 256 x 128 half moves 3/4 of
+  //     a tile's operand bytes for half its MFMAs and takes about kNarrow of a tile's time;
+  //   with a workspace, each cut into s parts along K (s divides nk, s <= 8): the last round
+  //     takes ceil(left s / G) parts of nk / s steps per workgroup, every part stores a
+  //     256 x 256 fp32 partial tile and the part that finishes a tile loads the s - 1 others; a
+  //     partial tile moves at the compute unit's share of HBM bandwidth (at most about 60 GB/s
+  //     for one unit, 5.6 TB/s for the chip; one step is about 1.5 us on a busy chip). A cut
+  //     must win by 20 %.
   int64_t grid = p.tiles < cus ? p.tiles : cus;
-  const int64_t rounds = workspace ? p.tiles / cus : 0;  // full rounds use every compute unit
+  const int64_t rounds = p.tiles / cus;
   const int64_t dp_tiles = rounds * cus, left = p.tiles - dp_tiles;
   int64_t splits = 1;
-  if (workspace && left > 0) {
-    constexpr double kStepUs = 1.5, kUnitGBs = 60.0, kChipGBs = 5600.0;
-    const double whole = (double)p.nk;
-    double best = 0.8 * whole;
-    for (int64_t s = 2; s <= kMaxSplits; ++s) {
-      if (p.nk % s != 0 || left * s > kMaxParts) continue;
-      const int64_t active = left * s < cus ? left * s : cus;
-      const double unit_gbs = kChipGBs / (double)active < kUnitGBs ? kChipGBs / (double)active
-                                                                    : kUnitGBs;
-      const double part_steps_cost = (double)kPartialBytes / (unit_gbs * 1e3) / kStepUs;
-      const double per_unit = (double)((left * s + active - 1) / active);
-      const double cost = per_unit * ((double)(p.nk / s) + part_steps_cost) +
-                          (double)(s - 1) * part_steps_cost;
-      if (cost < best) {
-        best = cost;
-        splits = s;
+  int narrow = 0;
+  if (left > 0) {
+    constexpr double kNarrow = 0.7, kStepUs = 1.5, kUnitGBs = 60.0, kChipGBs = 5600.0;
+    double best = (double)p.nk;
+    if (2 * left <= cus && kNarrow * p.nk < best) {
+      best = kNarrow * p.nk;
+      narrow = 1;
+    }
+    if (workspace) {
+      double best_cut = 0.8 * best;
+      for (int64_t s = 2; s <= kMaxSplits; ++s) {
+        if (p.nk % s != 0 || left * s > kMaxParts) continue;
+        const int64_t active = left * s < cus ? left * s : cus;
+        const double unit_gbs = kChipGBs / (double)active < kUnitGBs
+                                    ? kChipGBs / (double)active
+                                    : kUnitGBs;
+        const double part_steps_cost = (double)kPartialBytes / (unit_gbs * 1e3) / kStepUs;
+        const double per_unit = (double)((left * s + active - 1) / active);
+        const double cost = per_unit * ((double)(p.nk / s) + part_steps_cost) +
+                            (double)(s - 1) * part_steps_cost;
+        if (cost < best_cut) {
+          best_cut = cost;
+          splits = s;
+          narrow = 0;
+        }
       }
     }
-    if (dp_tiles == 0) grid = left * splits < cus ? left * splits : cus;
+    if (dp_tiles == 0 && !narrow) {
+      const int64_t items = left * splits;
+      grid = items < cus ? items : cus;
+    }
+  }
+  int narrow_grid = 0;
+  if (narrow) {
+    narrow_grid = (int)(2 * left);
+    grid = dp_tiles > 0 ? cus : 0;
   }
   p.dp_tiles = (int)dp_tiles;
+  p.tail0 = (int)dp_tiles;
   p.tail_tiles = (int)left;
   p.splits = (int)splits;
   p.part_steps = (int)(p.nk / splits);
+  p.narrow = narrow;
   p.part = splits > 1 ? static_cast<float*>(workspace) : nullptr;
   p.flags = splits > 1
                 ? reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + kPartRegion)
                 : nullptr;
-  if (!workspace) {  // whole tiles only: every tile is a left-over tile of round 0
-    p.dp_tiles = 0;
-    p.tail_tiles = p.tiles;
-  }
   const int g = (int)grid;
   switch (epilogue) {
-    case EPI_BIAS: return launch_epi<EPI_BIAS>(p, g, stream);
-    case EPI_GELU_TANH: return launch_epi<EPI_GELU_TANH>(p, g, stream);
-    default: return launch_epi<EPI_GATED_RESIDUAL>(p, g, stream);
+    case EPI_BIAS: return launch_epi<EPI_BIAS>(p, g, narrow_grid, stream);
+    case EPI_GELU_TANH: return launch_epi<EPI_GELU_TANH>(p, g, narrow_grid, stream);
+    default: return launch_epi<EPI_GATED_RESIDUAL>(p, g, narrow_grid, stream);
   }
 }
 
