@@ -317,6 +317,9 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": {
             "kernel": f"gemm_fp8_pp<{shape.epilogue}>",
+            "timing": ("HIP events around each dq_linear_fp8 call on its stream; a call is one "
+                       "launch, or two when the tiles left after the full rounds run as "
+                       "256 x 128 halves (the second, narrow launch follows on the stream)"),
             "bound": "mfma",
             "achieved": round(gemm_tflops, 2),
             "peak": PEAK_FP8_TFLOPS,
