@@ -8,6 +8,7 @@ stream. Every step of the computation runs in the HIP kernels of libdq; there is
     q, scale   = dq_quantize_fp8(x)                # x: bf16 [M, K] on the GPU
     qw, w_scale = dq_quantize_weight_fp8(w)        # w: bf16 [N, K], once per weight
     out = dq_linear_fp8(q, scale, qw, w_scale, bias, "gelu_tanh")
+    q, scale, y = dq_layernorm_modulate_quantize_fp8(h, mod_scale, mod_shift)  # LN + modulate
 
 dq_linear_fp8 takes a workspace that lets workgroups share tiles (see include/dq.h). By default
 the binding keeps one zero-filled workspace per (device, stream) and grows it when a larger
@@ -22,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdq.so")
 
 (DQ_OK, DQ_ERR_NULL, DQ_ERR_SHAPE, DQ_ERR_ALIGN, DQ_ERR_ALIAS, DQ_ERR_EPILOGUE, DQ_ERR_HIP,
- DQ_ERR_WORKSPACE) = range(8)
+ DQ_ERR_WORKSPACE, DQ_ERR_VALUE) = range(9)
 EPILOGUES = {"bias": 0, "gelu_tanh": 1, "gated_residual": 2}
 
 
@@ -56,6 +57,9 @@ def lib() -> ctypes.CDLL:
         L.dq_linear_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp,
                                     ctypes.c_uint64, vp]
         L.dq_linear_fp8.restype = i32
+        L.dq_layernorm_modulate_quantize_fp8.argtypes = [vp, i64, i64, vp, vp, ctypes.c_float,
+                                                         vp, vp, vp, vp]
+        L.dq_layernorm_modulate_quantize_fp8.restype = i32
         L.dq_linear_fp8_workspace_size.argtypes = [i64, i64, i64]
         L.dq_linear_fp8_workspace_size.restype = ctypes.c_uint64
         L.dq_status_string.argtypes = [i32]
@@ -123,6 +127,40 @@ def dq_quantize_fp8(x, q=None, scale=None, stream=None):
 def dq_quantize_weight_fp8(w, qw=None, w_scale=None, stream=None):
     """Per-output-channel FP8 quantization: w bf16 [N, K] -> (codes [N, K], scale [N])."""
     return _quantize(lib().dq_quantize_weight_fp8, "dq_quantize_weight_fp8", w, qw, w_scale, stream)
+
+
+def dq_layernorm_modulate_quantize_fp8(x, mod_scale, mod_shift, eps=1e-6, store_y=True, q=None,
+                                       scale=None, y=None, stream=None):
+    """LayerNorm (no affine) + modulation + per-token FP8 quantization in one pass.
+
+    x bf16 [M, K]; mod_scale, mod_shift bf16 [K]. Returns (codes uint8 [M, K], scale float32
+    [M], y bf16 [M, K] or None): y = bf16(LN(x) * (1 + mod_scale) + mod_shift), and the codes
+    are y's per-row quantization. store_y=False skips writing y.
+    """
+    where = "dq_layernorm_modulate_quantize_fp8"
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError(f"{where}: input must be a 2-D tensor")
+    if x.device.type != "cuda":
+        raise ValueError(f"{where}: input must be on a GPU")
+    M, K = x.shape
+    dev = x.device
+    _need(x, "input", torch.bfloat16, (M, K), dev)
+    _need(mod_scale, "mod_scale", torch.bfloat16, (K,), dev)
+    _need(mod_shift, "mod_shift", torch.bfloat16, (K,), dev)
+    q = torch.empty((M, K), dtype=torch.uint8, device=dev) if q is None else q
+    scale = torch.empty((M,), dtype=torch.float32, device=dev) if scale is None else scale
+    _need(q, "codes", torch.uint8, (M, K), dev)
+    _need(scale, "scale", torch.float32, (M,), dev)
+    if store_y:
+        y = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if y is None else y
+        _need(y, "y", torch.bfloat16, (M, K), dev)
+    else:
+        y = None
+    with torch.cuda.device(dev):
+        _check(lib().dq_layernorm_modulate_quantize_fp8(
+            _ptr(x), M, K, _ptr(mod_scale), _ptr(mod_shift), float(eps), _ptr(y), _ptr(q),
+            _ptr(scale), _stream(stream, dev)), where)
+    return q, scale, y
 
 
 def dq_linear_fp8_workspace_size(M, K, N):
@@ -201,4 +239,5 @@ def dq_linear_fp8(q, scale, qw, w_scale, bias=None, epilogue="bias", gate=None, 
 
 
 __all__ = ["dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
+           "dq_layernorm_modulate_quantize_fp8",
            "dq_linear_fp8_workspace_size", "DQError", "EPILOGUES", "lib", "LIB_PATH"]

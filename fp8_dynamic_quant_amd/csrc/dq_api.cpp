@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 
 #include "dq_internal.h"
@@ -124,6 +125,35 @@ int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const
       workspace, static_cast<hipStream_t>(stream)));
 }
 
+int dq_layernorm_modulate_quantize_fp8(const void* x, int64_t M, int64_t K, const void* mod_scale,
+                                       const void* mod_shift, float eps, void* y_out, void* q,
+                                       float* scale, void* stream) {
+  if (M < 0 || M > kMaxDim || K < 8 || K > dq::kMaxModulateK || (K % 8) != 0) return DQ_ERR_SHAPE;
+  if (!std::isfinite(eps) || !(eps > 0.0f)) return DQ_ERR_VALUE;
+  if (M == 0) return DQ_OK;
+  if (!x || !mod_scale || !mod_shift || !q || !scale) return DQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(mod_scale) || !aligned16(mod_shift) || !aligned16(q) ||
+      !aligned16(scale) || (y_out && !aligned16(y_out)))
+    return DQ_ERR_ALIGN;
+  const uint64_t n = static_cast<uint64_t>(M) * static_cast<uint64_t>(K);
+  const uint64_t kb = 2 * static_cast<uint64_t>(K), sb = 4 * static_cast<uint64_t>(M);
+  const uint64_t yb = y_out ? 2 * n : 0;
+  // outputs against inputs, then outputs against each other
+  const void* ins[3] = {x, mod_scale, mod_shift};
+  const uint64_t in_bytes[3] = {2 * n, kb, kb};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(y_out, yb, ins[i], in_bytes[i]) || overlap(q, n, ins[i], in_bytes[i]) ||
+        overlap(scale, sb, ins[i], in_bytes[i]))
+      return DQ_ERR_ALIAS;
+  }
+  if (overlap(y_out, yb, q, n) || overlap(y_out, yb, scale, sb) || overlap(q, n, scale, sb))
+    return DQ_ERR_ALIAS;
+  return hip_status(dq::launch_ln_modulate_quantize(
+      static_cast<const uint16_t*>(x), M, K, static_cast<const uint16_t*>(mod_scale),
+      static_cast<const uint16_t*>(mod_shift), eps, static_cast<uint16_t*>(y_out),
+      static_cast<uint8_t*>(q), scale, static_cast<hipStream_t>(stream)));
+}
+
 uint64_t dq_linear_fp8_workspace_size(int64_t M, int64_t K, int64_t N) {
   if (check_linear_shape(M, K, N) != DQ_OK) return 0;
   return dq::linear_workspace_bytes(M, K, N);
@@ -139,12 +169,13 @@ const char* dq_status_string(int status) {
     case DQ_ERR_EPILOGUE: return "unknown epilogue, or gate/residual missing for the gated one";
     case DQ_ERR_HIP: return "a HIP runtime call failed";
     case DQ_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
+    case DQ_ERR_VALUE: return "a scalar argument is out of range";
     default: return "unknown status";
   }
 }
 
 int dq_last_hip_error(void) { return g_last_hip_error; }
 
-int dq_abi_version(void) { return 2; }
+int dq_abi_version(void) { return 3; }
 
 }  // extern "C"

@@ -11,6 +11,14 @@ namespace dq {
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t R, int64_t K, uint8_t* q, float* scale,
                                 hipStream_t stream);
 
+// LayerNorm (no affine) + modulation + per-row FP8 quantization of a bf16 [R, K] matrix,
+// K <= kMaxModulateK. y (bf16 [R, K]) is stored when non-null. Arguments are already validated.
+constexpr int64_t kMaxModulateK = 8192;
+hipError_t launch_ln_modulate_quantize(const uint16_t* x, int64_t R, int64_t K,
+                                       const uint16_t* mod_scale, const uint16_t* mod_shift,
+                                       float eps, uint16_t* y, uint8_t* q, float* scale,
+                                       hipStream_t stream);
+
 // ---------------------------------------------------------------------------------------------
 // GEMM work split, shared by the size query (host only, no GPU) and the launcher.
 //   tile = 256 x 256 outputs; step = 128 of K.

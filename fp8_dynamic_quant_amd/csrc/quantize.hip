@@ -186,6 +186,172 @@ __global__ void __launch_bounds__(256) quant_rows_loop(const uint16_t* __restric
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// LayerNorm + modulation + quantization of one row per wave (the row stays in registers)
+// ---------------------------------------------------------------------------------------------
+
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+
+// Sum over the wave; every lane returns lane 0's total, so all lanes use the same value.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+// Two fp32 -> packed bf16, round to nearest even (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){a, b}, bf2v));
+}
+
+// y for one 8-value chunk: (((x - mean0) - c) rstd) (1 + s) + t, rounded to bf16.
+__device__ __forceinline__ uint4 modulate8(uint4 v, uint4 ms, uint4 mt, float mean0, float c,
+                                           float rstd) {
+  const uint32_t xv[4] = {v.x, v.y, v.z, v.w};
+  const uint32_t sv[4] = {ms.x, ms.y, ms.z, ms.w};
+  const uint32_t tv[4] = {mt.x, mt.y, mt.z, mt.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float n0 = ((bf16_lo(xv[j]) - mean0) - c) * rstd;
+    const float n1 = ((bf16_hi(xv[j]) - mean0) - c) * rstd;
+    const float y0 = __builtin_fmaf(n0, 1.0f + bf16_lo(sv[j]), bf16_lo(tv[j]));
+    const float y1 = __builtin_fmaf(n1, 1.0f + bf16_hi(sv[j]), bf16_hi(tv[j]));
+    o[j] = pack2_bf16(y0, y1);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Lane l holds chunks l, l + 64, ... of its row (NCH per lane, K <= 512 NCH). Every sum is
+// fp32: each lane adds its values in order, then a wave butterfly.
+//   1. mean0 = (sum of the row) / K; its rounding error grows with |mean|, so
+//   2. c = (sum of (x - mean0)) / K corrects it: x - mean0 is exact for x near mean0, and
+//      d = (x - mean0) - c is then accurate relative to the row's spread, not to |mean|
+//      (rows with a large common offset keep their variance);
+//   3. var = (sum of d^2) / K; rstd = 1 / sqrt(var + eps), both IEEE;
+//   4. y = (d rstd) (1 + s) + t with one fma, rounded to bf16 in place of x;
+//   5. the bf16 row y is quantized exactly as quant_rows_reg does (amax, scale, codes).
+template <int NCH, bool kStoreY>
+__global__ void __launch_bounds__(256) ln_mod_quant_rows(
+    const uint16_t* __restrict__ x, int R, int K, const uint16_t* __restrict__ mscale,
+    const uint16_t* __restrict__ mshift, float eps, uint16_t* __restrict__ y,
+    uint8_t* __restrict__ q, float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= R) return;
+  const int C = K >> 3;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)row * (size_t)K);
+  const uint4* sr = reinterpret_cast<const uint4*>(mscale);
+  const uint4* tr = reinterpret_cast<const uint4*>(mshift);
+  uint4 v[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    v[i] = (c < C) ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  // 1. first mean (chunks past the row are zeros and add nothing)
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sum = (sum + bf16_lo(w[j])) + bf16_hi(w[j]);
+  }
+  const float mean0 = wave_sum(sum) / (float)K;
+  // 2. its correction, over the row's own values only
+  float es = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    if (lane + 64 * i < C) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) es = (es + (bf16_lo(w[j]) - mean0)) + (bf16_hi(w[j]) - mean0);
+    }
+  }
+  const float corr = wave_sum(es) / (float)K;
+  // 3. variance
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    if (lane + 64 * i < C) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float d0 = (bf16_lo(w[j]) - mean0) - corr, d1 = (bf16_hi(w[j]) - mean0) - corr;
+        ss = __builtin_fmaf(d0, d0, ss);
+        ss = __builtin_fmaf(d1, d1, ss);
+      }
+    }
+  }
+  const float var = wave_sum(ss) / (float)K;
+  const float rstd = 1.0f / __builtin_sqrtf(var + eps);
+  // 4. y in bf16, in place of x
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < C) v[i] = modulate8(v[i], sr[c], tr[c], mean0, corr, rstd);
+  }
+  if (kStoreY) {
+    uint4* yr = reinterpret_cast<uint4*>(y + (size_t)row * (size_t)K);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < C) yr[c] = v[i];
+    }
+  }
+  // 4. per-row quantization of the bf16 y (chunks past the row are zeros)
+  uint2* qr = reinterpret_cast<uint2*>(q + (size_t)row * (size_t)K);
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) mx = absmax4(mx, v[i]);
+  uint32_t m = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
+  m = __builtin_amdgcn_readfirstlane(wave_max(m));
+  const float amax = __uint_as_float(m << 16);
+  const float s = amax / kE4M3Max;
+  if (lane == 0) scale[row] = s;
+  if (m == 0) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < C) qr[c] = signs8(v[i]);
+    }
+  } else if (s < kFltMinNormal) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < C) qr[c] = encode8<1, false>(v[i], s, 0.0f);
+    }
+  } else if (amax < kTinyAmax) {
+    const float ss2 = s * 0x1p64f;
+    const float yy = 1.0f / ss2;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < C) qr[c] = encode8<0, true>(v[i], ss2, yy);
+    }
+  } else {
+    const float yy = 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < C) qr[c] = encode8<0, false>(v[i], s, yy);
+    }
+  }
+}
+
+template <int NCH>
+hipError_t launch_lnmq(const uint16_t* x, int R, int K, const uint16_t* ms, const uint16_t* mt,
+                       float eps, uint16_t* y, uint8_t* q, float* scale, hipStream_t st) {
+  if (y)
+    hipLaunchKernelGGL((ln_mod_quant_rows<NCH, true>), dim3((R + 3) / 4), dim3(256), 0, st, x, R,
+                       K, ms, mt, eps, y, q, scale);
+  else
+    hipLaunchKernelGGL((ln_mod_quant_rows<NCH, false>), dim3((R + 3) / 4), dim3(256), 0, st, x,
+                       R, K, ms, mt, eps, y, q, scale);
+  return hipGetLastError();
+}
+
 template <int NCH>
 hipError_t launch_reg(const uint16_t* x, int R, int K, uint8_t* q, float* scale, hipStream_t st) {
   hipLaunchKernelGGL(quant_rows_reg<NCH>, dim3((R + 3) / 4), dim3(256), 0, st, x, R, K, q, scale);
@@ -211,6 +377,22 @@ hipError_t launch_quantize_rows(const uint16_t* x, int64_t R, int64_t K, uint8_t
   if (nch <= 30) return launch_reg<30>(x, r, k, q, scale, stream);
   hipLaunchKernelGGL(quant_rows_loop, dim3((r + 3) / 4), dim3(256), 0, stream, x, r, k, q, scale);
   return hipGetLastError();
+}
+
+hipError_t launch_ln_modulate_quantize(const uint16_t* x, int64_t R, int64_t K,
+                                       const uint16_t* mod_scale, const uint16_t* mod_shift,
+                                       float eps, uint16_t* y, uint8_t* q, float* scale,
+                                       hipStream_t stream) {
+  if (R == 0) return hipSuccess;
+  const int r = (int)R, k = (int)K;
+  const int64_t nch = (K / 8 + 63) / 64;  // 16-byte chunks per lane; K <= 8192 gives <= 16
+  if (nch <= 1) return launch_lnmq<1>(x, r, k, mod_scale, mod_shift, eps, y, q, scale, stream);
+  if (nch <= 2) return launch_lnmq<2>(x, r, k, mod_scale, mod_shift, eps, y, q, scale, stream);
+  if (nch <= 4) return launch_lnmq<4>(x, r, k, mod_scale, mod_shift, eps, y, q, scale, stream);
+  if (nch <= 6) return launch_lnmq<6>(x, r, k, mod_scale, mod_shift, eps, y, q, scale, stream);
+  if (nch <= 8) return launch_lnmq<8>(x, r, k, mod_scale, mod_shift, eps, y, q, scale, stream);
+  if (nch <= 12) return launch_lnmq<12>(x, r, k, mod_scale, mod_shift, eps, y, q, scale, stream);
+  return launch_lnmq<16>(x, r, k, mod_scale, mod_shift, eps, y, q, scale, stream);
 }
 
 }  // namespace dq

@@ -54,7 +54,8 @@ enum {
   DQ_ERR_ALIAS = 4,     /* an output overlaps an input (other than out == residual) */
   DQ_ERR_EPILOGUE = 5,  /* unknown epilogue, or gate/residual missing for the gated one */
   DQ_ERR_HIP = 6,       /* a HIP runtime call failed; see dq_last_hip_error() */
-  DQ_ERR_WORKSPACE = 7  /* workspace too small or not 256-byte aligned */
+  DQ_ERR_WORKSPACE = 7, /* workspace too small or not 256-byte aligned */
+  DQ_ERR_VALUE = 8      /* a scalar argument is out of range (eps <= 0, or not finite) */
 };
 
 /* Epilogues of dq_linear_fp8 (v = acc * scale[m] * w_scale[n] + bias[n]). */
@@ -145,13 +146,46 @@ int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const
  */
 uint64_t dq_linear_fp8_workspace_size(int64_t M, int64_t K, int64_t N);
 
+/*
+ * dq_layernorm_modulate_quantize_fp8 -- a DiT block's LayerNorm and modulation folded into the
+ * per-token FP8 quantization of the next linear's input, in one pass over x:
+ *
+ *   n[m, k] = (x[m, k] - mean_m) / sqrt(var_m + eps)      mean, (biased) variance over k
+ *   y[m, k] = bf16( n[m, k] * (1 + mod_scale[k]) + mod_shift[k] )
+ *   scale[m], q[m, :] = per-row FP8 quantization of y, exactly as dq_quantize_fp8
+ *
+ * This is the kernel fusion that the page "Solucion de WaveSpeed para Acelerar la Generacion de
+ * Imagenes FLUX.1-dev" lists among the fixes for high per-image latency (its lists of bottlenecks
+ * and of the engine's innovations). The pages do not write the normalization out; the reading
+ * taken is the FLUX-style block's: LayerNorm without learned weight or bias (eps = 1e-6 there)
+ * and per-channel shift and scale from the block's modulation. The statistics and y are computed
+ * in fp32 and y is rounded to bf16 (nearest even), the activation the unfused step would store;
+ * the codes are a function of that bf16 y.
+ *
+ *   x          bf16 [M, K]  hidden states, one token per row
+ *   mod_scale  bf16 [K]     per-channel modulation scale (y uses 1 + mod_scale)
+ *   mod_shift  bf16 [K]     per-channel modulation shift
+ *   eps        float        added to the variance; finite and > 0 (else DQ_ERR_VALUE: a row
+ *                           of equal values would give 0/0)
+ *   y_out      bf16 [M, K]  the modulated activation, or NULL to skip storing it
+ *   q          uint8 [M, K] codes;  scale  fp32 [M] per-token scales (as dq_quantize_fp8)
+ *
+ * Requirements: 0 <= M < 2^31, 8 <= K <= 8192 with K % 8 == 0 (a row stays in registers), all
+ * pointers 16-byte aligned, no output (y_out, q, scale) overlapping an input or another output.
+ * Inputs must be finite and every modulated value must lie in bf16's finite range (the codes
+ * are unspecified otherwise). M = 0 enqueues nothing.
+ */
+int dq_layernorm_modulate_quantize_fp8(const void* x, int64_t M, int64_t K, const void* mod_scale,
+                                       const void* mod_shift, float eps, void* y_out, void* q,
+                                       float* scale, void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* dq_status_string(int status);
 
 /* The hipError_t behind the most recent DQ_ERR_HIP returned on the calling thread (0 if none). */
 int dq_last_hip_error(void);
 
-/* ABI version of this header (currently 2). */
+/* ABI version of this header (currently 3). */
 int dq_abi_version(void);
 
 #ifdef __cplusplus

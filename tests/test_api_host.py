@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dq.h")
 LIB = os.path.join(ROOT, "fp8_dynamic_quant_amd", "libdq.so")
 
-OK, NULL, SHAPE, ALIGN, ALIAS, EPI, HIP, WORKSPACE = range(8)
+OK, NULL, SHAPE, ALIGN, ALIAS, EPI, HIP, WORKSPACE, VALUE = range(9)
 BIAS, GELU, GATED = 0, 1, 2
 
 
@@ -26,6 +26,8 @@ def lib():
     L.dq_quantize_weight_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
     L.dq_linear_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp,
                                 ctypes.c_uint64, vp]
+    L.dq_layernorm_modulate_quantize_fp8.argtypes = [vp, i64, i64, vp, vp, ctypes.c_float, vp,
+                                                     vp, vp, vp]
     L.dq_linear_fp8_workspace_size.argtypes = [i64, i64, i64]
     L.dq_linear_fp8_workspace_size.restype = ctypes.c_uint64
     L.dq_status_string.restype = ctypes.c_char_p
@@ -38,9 +40,10 @@ def _declared():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(dq_\w+)\s*\(", text, re.M)))
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
+              "dq_layernorm_modulate_quantize_fp8",
               "dq_linear_fp8_workspace_size", "dq_status_string", "dq_last_hip_error",
               "dq_abi_version"):
         assert n in names
@@ -52,8 +55,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dq_abi_version() == 2
-    for st in range(8):
+    assert lib.dq_abi_version() == 3
+    for st in range(9):
         s = lib.dq_status_string(st)
         assert s and len(s) > 1
     assert lib.dq_status_string(12345) == b"unknown status"
@@ -87,6 +90,47 @@ def test_quantize_adjacent_buffers_are_not_aliases(lib):
     # x occupies [X, X + 2*4*64); codes right after it do not overlap
     # (the call is rejected for another reason so that nothing is launched)
     assert lib.dq_quantize_fp8(X, 4, 64, X + 2 * 4 * 64, None, None) == NULL
+
+
+MS, MT, Y = 0x40000000, 0x50000000, 0x60000000          # fake modulation vectors and y
+
+
+def lnmq(lib, M=4, K=64, x=X, ms=MS, mt=MT, eps=1e-6, y=Y, q=Q, s=S):
+    return lib.dq_layernorm_modulate_quantize_fp8(x, M, K, ms, mt, eps, y, q, s, None)
+
+
+def test_layernorm_modulate_argument_checks(lib):
+    assert lnmq(lib, M=0) == OK                             # empty: nothing to do
+    assert lnmq(lib, M=0, x=None, q=None) == OK
+    assert lnmq(lib, M=-1) == SHAPE
+    assert lnmq(lib, M=1 << 31) == SHAPE
+    assert lnmq(lib, K=0) == SHAPE
+    assert lnmq(lib, K=4) == SHAPE                          # K < 8
+    assert lnmq(lib, K=12) == SHAPE                         # K % 8
+    assert lnmq(lib, K=8192 + 8) == SHAPE                   # one row must fit the registers
+    assert lnmq(lib, M=0, K=12) == SHAPE                    # shapes are checked even when empty
+    assert lnmq(lib, eps=-1e-6) == VALUE
+    assert lnmq(lib, eps=0.0) == VALUE                      # 0/0 on a row of equal values
+    assert lnmq(lib, eps=float("nan")) == VALUE
+    assert lnmq(lib, eps=float("inf")) == VALUE
+    assert lnmq(lib, M=0, eps=-1.0) == VALUE
+    for name in ("x", "ms", "mt", "q", "s"):
+        assert lnmq(lib, **{name: None}) == NULL, name
+    for name in ("x", "ms", "mt", "y", "q"):
+        assert lnmq(lib, **{name: {"x": X, "ms": MS, "mt": MT, "y": Y, "q": Q}[name] + 8}) \
+            == ALIGN, name
+    assert lnmq(lib, s=S + 4) == ALIGN
+    assert lnmq(lib, q=X + 64) == ALIAS                     # codes inside x
+    assert lnmq(lib, y=X) == ALIAS                          # y over x (no in-place form)
+    assert lnmq(lib, s=MS) == ALIAS                         # scales over mod_scale
+    assert lnmq(lib, q=MT - 16) == ALIAS                    # codes run into mod_shift
+    assert lnmq(lib, s=Q + 64) == ALIAS                     # scales inside codes
+    assert lnmq(lib, q=Y + 2 * 4 * 64 - 16) == ALIAS        # codes inside y
+    # adjacent, non-overlapping buffers are fine; y = NULL is allowed (the call then fails on
+    # a NULL scale so that nothing is launched)
+    assert lnmq(lib, y=None, q=X + 2 * 4 * 64, s=None) == NULL
+    assert lnmq(lib, y=Y, q=Y + 2 * 4 * 64, s=None) == NULL
+    assert lib.dq_last_hip_error() == 0
 
 
 Aq, As, Wq, Ws, Bi, Ga, Re, Ou = (0x1000000 * i for i in range(1, 9))
@@ -164,9 +208,9 @@ def test_last_hip_error_untouched_by_argument_errors(lib):
 def test_python_binding_names_match_the_c_entry_points():
     import fp8_dynamic_quant_amd as dq
     for name in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
-                 "dq_linear_fp8_workspace_size"):
+                 "dq_layernorm_modulate_quantize_fp8", "dq_linear_fp8_workspace_size"):
         assert callable(getattr(dq, name))
-    assert dq.lib().dq_abi_version() == 2
+    assert dq.lib().dq_abi_version() == 3
     assert dq.dq_linear_fp8_workspace_size(4608, 3072, 12288) == 3584 + 1024 * 262144
 
 
@@ -176,6 +220,9 @@ def test_python_binding_rejects_cpu_tensors():
     x = torch.zeros(4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         dq.dq_quantize_fp8(x)
+    with pytest.raises(ValueError):
+        dq.dq_layernorm_modulate_quantize_fp8(x, torch.zeros(64, dtype=torch.bfloat16),
+                                              torch.zeros(64, dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         dq.dq_linear_fp8(torch.zeros(4, 128, dtype=torch.uint8), torch.zeros(4),
                          torch.zeros(64, 128, dtype=torch.uint8), torch.zeros(64))

@@ -1,0 +1,178 @@
+"""GPU parity of dq_layernorm_modulate_quantize_fp8 against the oracle.
+
+The kernel computes the row statistics and y in fp32, the oracle in float64. The kernel's sums
+run serially over at most K/64 + 8 values per lane and then over 6 butterfly levels, so each
+carries a relative error of at most gamma = h u / (1 - h u) with u = 2^-24 and h = K/64 + 14 (the
+classic bound for recursive summation). Following the kernel's steps (a first mean, a correction
+c = mean(x - mean0), d = (x - mean0) - c, the variance of d, rstd, one fma for y), its y before
+the bf16 rounding is within 2 gamma (|n (1 + scale)| + |1 + scale|) + 2 u |y| of the exact one
+(n the normalized value; the |1 + scale| term is c's absolute error, at most gamma times the
+row's spread, times rstd). That error is not relative to |y|: where n (1 + scale) and shift
+cancel, y is tiny and it spans many bf16 steps of y. Against the unrounded float64 y the bound is
+that plus half a bf16 step of the kernel's y (its rounding); the kernel's y must also meet the
+tolerance for bf16 outputs, 4e-3 * |ref| + 1e-3 * rms(ref), with the float64 y as ref. The two
+bf16 roundings differ by at most one step wherever the fp32 error is under a quarter step. The
+codes and scales are a function of the bf16 y alone: they must
+be bit-identical to the oracle's quantization of the kernel's own y, and identical to the
+oracle's codes on every row whose y came out the same.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_dynamic_quant_amd as dq
+from oracle import LN_EPS, layernorm_modulate, modulate_rows, quantize_rows
+from gpu_util import announce, bf16_to_dev, dev_to_bf16_bits, require_gpu
+from workloads import bf16_bits_to_f32, f32_to_bf16_bits, make_modulation, make_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _order_key(u16):
+    """bf16 bit patterns -> integers in value order, one apart for adjacent values (+0 = -0)."""
+    u = u16.astype(np.int64)
+    return np.where(u & 0x8000, 0x8000 - (u & 0x7FFF), 0x8000 + u)
+
+
+def _bf16_step(v):
+    """Spacing of bf16 values at |v| (8 significant bits); 0 at v = 0."""
+    m, e = np.frexp(np.abs(v))
+    return np.where(v == 0, 0.0, np.ldexp(1.0, e - 8))
+
+
+def _run(x16, s16, t16, eps=LN_EPS, store_y=True):
+    x, ms, mt = bf16_to_dev(x16), bf16_to_dev(s16), bf16_to_dev(t16)
+    q, sc, y = dq.dq_layernorm_modulate_quantize_fp8(x, ms, mt, eps=eps, store_y=store_y)
+    torch.cuda.synchronize()
+    return (q.cpu().numpy(), sc.cpu().numpy(),
+            None if y is None else dev_to_bf16_bits(y))
+
+
+def _check(x16, s16, t16, what, eps=LN_EPS, min_same_rows=0.0):
+    M, K = x16.shape
+    announce(f"layernorm+modulate+quantize {what} M={M} K={K} eps={eps}")
+    q, sc, y16 = _run(x16, s16, t16, eps)
+    oy, oq, osc = modulate_rows(bf16_bits_to_f32(x16), bf16_bits_to_f32(s16),
+                                bf16_bits_to_f32(t16), eps)
+    oy16 = f32_to_bf16_bits(oy)
+
+    # y: half a bf16 step plus the fp32 evaluation error of its terms, and the bf16 tolerance,
+    # against the unrounded float64 y
+    xf = bf16_bits_to_f32(x16)
+    sf, tf = bf16_bits_to_f32(s16).astype(np.float64), bf16_bits_to_f32(t16).astype(np.float64)
+    n = layernorm_modulate(xf, np.zeros(K), np.zeros(K), eps)
+    y64 = layernorm_modulate(xf, sf, tf, eps)
+    u = 2.0 ** -24
+    h = K / 64 + 14
+    gamma = h * u / (1 - h * u)
+    fp32_err = 2 * gamma * (np.abs(n * (1.0 + sf)) + np.abs(1.0 + sf)) + 2 * u * np.abs(y64)
+    yk = bf16_bits_to_f32(y16).astype(np.float64)
+    err = np.abs(yk - y64)
+    bound = 0.5 * _bf16_step(yk) + fp32_err
+    if not np.all(err <= bound):
+        r, c = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: y off at {(r, c)}: gpu={yk[r, c]!r} float64={y64[r, c]!r} "
+                             f"bound={bound[r, c]!r}")
+    rms = np.sqrt(np.mean(y64 * y64)) if y64.size else 0.0
+    tol = 4e-3 * np.abs(y64) + 1e-3 * rms
+    assert np.all(err <= tol), f"{what}: worst err/tol {np.max(err / tol):.3f}"
+    step = np.abs(_order_key(y16) - _order_key(oy16))
+    assert np.all((step <= 1) | (fp32_err > 0.25 * _bf16_step(y64))), \
+        f"{what}: the two bf16 roundings differ by more than a step outside cancellation"
+
+    # codes and scales: exact functions of the kernel's bf16 y
+    kq, ksc = quantize_rows(bf16_bits_to_f32(y16))
+    assert np.array_equal(sc.view(np.uint32), ksc.view(np.uint32)), \
+        f"{what}: {int(np.sum(sc.view(np.uint32) != ksc.view(np.uint32)))} scales differ"
+    if not np.array_equal(q, kq):
+        bad = np.argwhere(q != kq)
+        r, c = bad[0]
+        raise AssertionError(f"{what}: {len(bad)} codes differ; first at {(r, c)}: "
+                             f"y={bf16_bits_to_f32(y16)[r, c]!r} gpu={q[r, c]:#04x} "
+                             f"oracle={kq[r, c]:#04x}")
+
+    # rows whose y equals the oracle's carry the oracle's codes and scale
+    same = np.all(y16 == oy16, axis=1) if K else np.ones(M, bool)
+    assert np.array_equal(q[same], oq[same]), what
+    assert np.array_equal(sc[same].view(np.uint32), osc[same].view(np.uint32)), what
+    print(f"[{what}] y not bit-equal: {np.mean(step > 0):.2e} of elements, "
+          f"{np.mean(step > 1):.2e} more than one step; rows bit-equal: {same.mean():.3f}")
+    assert same.mean() >= min_same_rows, f"{what}: only {same.mean():.3f} of rows match exactly"
+
+    # skipping the y store leaves the codes and scales unchanged
+    q2, sc2, _ = _run(x16, s16, t16, eps, store_y=False)
+    assert np.array_equal(q2, q) and np.array_equal(sc2.view(np.uint32), sc.view(np.uint32)), \
+        f"{what}: codes depend on whether y is stored"
+    return np.mean(step > 0)
+
+
+def test_flux_hidden_state_1024px():
+    """A 1024 x 1024 image's 4096 image tokens + 512 text tokens at FLUX's hidden width 3072,
+    1% outlier channels 30x larger, modulation drawn at sigma 0.5."""
+    x = make_rows(4608, 3072, seed=11)
+    s, t = make_modulation(3072, seed=11)
+    frac = _check(x, s, t, "flux 4608x3072")
+    assert frac < 1e-3
+
+
+@pytest.mark.parametrize("M,K", [(1, 8), (3, 64), (7, 1000), (130, 3072), (5, 8192),
+                                 (33, 4104), (17, 512), (64, 2056), (2, 6144), (9, 520)])
+def test_shapes_and_ragged_rows(M, K):
+    """Every register-tile size the kernel has (one to sixteen 512-wide chunks per row), widths
+    that leave a partial chunk, and row counts that leave a partial workgroup."""
+    x = make_rows(M, K, seed=1000 + K, n_outliers=max(1, K // 100))
+    s, t = make_modulation(K, seed=K)
+    _check(x, s, t, f"{M}x{K}")
+
+
+def test_large_and_offset_rows():
+    """Rows with a large mean (100 + N(0,1): a one-pass E[x^2] - E[x]^2 would lose the variance)
+    and rows at the magnitude of a DiT residual stream's large activations (sigma 1000)."""
+    K = 3072
+    rng = np.random.default_rng(5)
+    a = 100.0 + rng.standard_normal((24, K)).astype(np.float32)
+    b = 1000.0 * rng.standard_normal((24, K)).astype(np.float32)
+    x = f32_to_bf16_bits(np.concatenate([a, b]))
+    s, t = make_modulation(K, seed=5)
+    _check(x, s, t, "offset and large rows")
+
+
+def test_degenerate_rows():
+    """Zero and constant rows (LayerNorm gives 0, so y = shift exactly), a row with one nonzero
+    value, and large eps."""
+    K = 1024
+    x = np.zeros((6, K), np.float32)
+    x[1, :] = 3.5
+    x[2, :] = -0.125
+    x[3, 17] = 5.0
+    x[4, :] = np.linspace(-1, 1, K, dtype=np.float32)
+    x[5, ::2], x[5, 1::2] = 2.0, -2.0
+    x16 = f32_to_bf16_bits(x)
+    s, t = make_modulation(K, seed=9)
+    _check(x16, s, t, "degenerate rows")
+    _check(x16, s, t, "degenerate rows, eps 1", eps=1.0)
+    q, sc, y16 = _run(x16, s, t)
+    assert np.array_equal(y16[0], t) and np.array_equal(y16[1], t) and np.array_equal(y16[2], t)
+
+
+def test_modulation_that_cancels():
+    """1 + scale = 0 and shift = 0 make every y zero: all-zero rows quantize to zero codes."""
+    K = 256
+    x = make_rows(8, K, seed=3)
+    s = f32_to_bf16_bits(np.full(K, -1.0, np.float32))
+    t = f32_to_bf16_bits(np.zeros(K, np.float32))
+    _check(x, s, t, "cancelling modulation")
+    q, sc, y16 = _run(x, s, t)
+    assert not np.any(y16 & 0x7FFF) and not np.any(q & 0x7F)
+
+
+def test_empty_input():
+    x = torch.empty((0, 3072), dtype=torch.bfloat16, device="cuda:0")
+    ms = torch.zeros(3072, dtype=torch.bfloat16, device="cuda:0")
+    q, sc, y = dq.dq_layernorm_modulate_quantize_fp8(x, ms, ms)
+    assert q.shape == (0, 3072) and sc.shape == (0,) and y.shape == (0, 3072)

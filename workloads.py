@@ -188,6 +188,16 @@ def make_rows(M: int, K: int, seed: int, n_outliers: Optional[int] = None,
     return f32_to_bf16_bits(x)
 
 
+def make_modulation(K: int, seed: int, sigma: float = 0.5):
+    """bf16 bit patterns of a block's per-channel modulation (scale [K], shift [K]): the block
+    applies y = n * (1 + scale) + shift. Both drawn as sigma * N(0,1) from PCG64 seeded with
+    [seed, 104729]; with sigma = 0.5 some channels have 1 + scale near zero or negative."""
+    rng = np.random.default_rng([seed, 104729])
+    scale = rng.standard_normal(K, dtype=np.float32) * np.float32(sigma)
+    shift = rng.standard_normal(K, dtype=np.float32) * np.float32(sigma)
+    return f32_to_bf16_bits(scale), f32_to_bf16_bits(shift)
+
+
 # ---------------------------------------------------------------------------------------------
 # Full denoising step: inputs drawn on the device (8.6 GB of weights are too slow to draw on the
 # host). torch.Generator on the device, seeded 4_000_000 + 100 * block + 10 * stream + linear.
