@@ -10,7 +10,8 @@ workload's shapes, resident in HBM before timing starts; several buffer sets rot
 brings the chip to the steady clock it holds under this load before the timed steps.
 
 Prints one JSON line: whole-step throughput (TFLOP/s), the GEMM kernel against the FP8 matrix
-peak, the quantize kernel against HBM bandwidth, the linears of a full FLUX-dev denoising step
+peak, the quantize kernel and the fused LayerNorm + modulation + quantize kernel against HBM
+bandwidth, the linears of a full FLUX-dev denoising step
 (ms), and the CPU oracle timed on the host as a baseline.
 """
 import argparse
@@ -33,6 +34,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {
     "gemm": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "gemm_fp8.hip"),
     "quantize": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "quantize.hip"),
+    "ln_modulate": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "quantize.hip"),
 }
 
 
@@ -144,6 +146,53 @@ def bench_linear(shape, seed, steps, warmup, n_sets):
     q_loop_ms = e0.elapsed_time(e1) / reps
     return {"total_ms": total_ms, "wall_s": wall, "quant_ms": q_ms, "gemm_ms": g_ms,
             "quant_loop_ms": q_loop_ms}
+
+
+def bench_modulate(M, K, steps, n_sets, seed=11):
+    """The fused LayerNorm + modulation + quantization over M x K hidden states, back to back over
+    rotating inputs: without storing y (what a block feeding only the next linear runs), with y,
+    and, for context, the unfused sequence (torch LayerNorm and modulation in bf16, then
+    dq_quantize_fp8). Returns microseconds per call."""
+    import torch
+    import torch.nn.functional as F
+    import fp8_dynamic_quant_amd as dq
+    from workloads import make_modulation, make_rows
+
+    dev = torch.device("cuda:0")
+    x16 = make_rows(M, K, seed)
+    s16, t16 = make_modulation(K, seed)
+    ms, mt = to_dev_bf16(torch, s16, dev), to_dev_bf16(torch, t16, dev)
+    sets = [{"x": to_dev_bf16(torch, x16, dev),
+             "q": torch.empty((M, K), dtype=torch.uint8, device=dev),
+             "s": torch.empty((M,), dtype=torch.float32, device=dev),
+             "y": torch.empty((M, K), dtype=torch.bfloat16, device=dev)} for _ in range(n_sets)]
+    torch.cuda.synchronize()
+
+    def fused(st, store_y):
+        dq.dq_layernorm_modulate_quantize_fp8(st["x"], ms, mt, store_y=store_y, q=st["q"],
+                                              scale=st["s"], y=st["y"] if store_y else None)
+
+    def unfused(st):
+        h = F.layer_norm(st["x"], (K,), eps=1e-6) * (1 + ms) + mt
+        dq.dq_quantize_fp8(h, st["q"], st["s"])
+
+    def timed(fn, reps):
+        for i in range(max(reps // 4, n_sets)):
+            fn(sets[i % n_sets])
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn(sets[i % n_sets])
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    reps = 4 * steps
+    return {"no_y_us": timed(lambda st: fused(st, False), reps),
+            "y_us": timed(lambda st: fused(st, True), reps),
+            "unfused_us": timed(unfused, max(reps // 4, 1))}
 
 
 def bench_dit_step(steps, warmup):
@@ -260,6 +309,7 @@ def main():
     ap.add_argument("--sets", type=int, default=6, help="rotating input/output buffer sets")
     ap.add_argument("--dit-steps", type=int, default=5)
     ap.add_argument("--no-dit", action="store_true")
+    ap.add_argument("--no-modulate", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB plain copy first (reference for HBM counters)")
@@ -342,6 +392,32 @@ def main():
             "algorithmic_bytes_per_launch": qbytes,
         },
     }
+    if not args.no_modulate:
+        Mm, Km = shape.M, shape.K
+        mo = bench_modulate(Mm, Km, args.steps, args.sets)
+        b_no_y = 3 * Mm * Km + 4 * Mm + 4 * Km       # read x, write codes and scales, read mod
+        b_y = b_no_y + 2 * Mm * Km                   # plus the bf16 y
+        gb_no_y = b_no_y / mo["no_y_us"] / 1e3
+        gb_y = b_y / mo["y_us"] / 1e3
+        log(f"LN+modulate+quantize {Mm}x{Km}: {mo['no_y_us']:.1f} us ({gb_no_y:.0f} GB/s), "
+            f"with y {mo['y_us']:.1f} us ({gb_y:.0f} GB/s); unfused {mo['unfused_us']:.1f} us")
+        res["ln_modulate_quantizer"] = {
+            "kernel": "ln_mod_quant_rows",
+            "timing": "back-to-back launches over rotating inputs, HIP events around the loop",
+            "shape": [Mm, Km],
+            "bound": "hbm",
+            "achieved": round(gb_no_y, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(gb_no_y / PEAK_HBM_GBPS, 4),
+            "traffic": stored_traffic("ln_modulate", w.name),
+            "avg_launch_us": round(mo["no_y_us"], 2),
+            "algorithmic_bytes_per_launch": b_no_y,
+            "with_y": {"avg_launch_us": round(mo["y_us"], 2), "achieved": round(gb_y, 1),
+                       "frac": round(gb_y / PEAK_HBM_GBPS, 4),
+                       "algorithmic_bytes_per_launch": b_y},
+            "unfused_torch_then_quantize_us": round(mo["unfused_us"], 2),
+        }
     if not args.no_dit:
         log("DiT step: generating 228 distinct FP8 weights on the device")
         d = bench_dit_step(args.dit_steps, 2)

@@ -190,15 +190,48 @@ __global__ void __launch_bounds__(256) quant_rows_loop(const uint16_t* __restric
 // LayerNorm + modulation + quantization of one row per wave (the row stays in registers)
 // ---------------------------------------------------------------------------------------------
 
+// Wave-wide reductions without LDS round trips: DPP moves combine lanes inside each 16-lane row
+// (quad_perm swaps of 1 and 2 lanes, then the half-row and row mirrors), after which every lane of
+// a row holds the same row total; the four row totals are read into scalar registers and combined
+// in a fixed order, so every lane returns the same value.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += __builtin_bit_cast(float, dpp<0xB1>(__builtin_bit_cast(int, v)));   // lanes ^ 1
+  v += __builtin_bit_cast(float, dpp<0x4E>(__builtin_bit_cast(int, v)));   // lanes ^ 2
+  v += __builtin_bit_cast(float, dpp<0x141>(__builtin_bit_cast(int, v)));  // half-row mirror
+  v += __builtin_bit_cast(float, dpp<0x140>(__builtin_bit_cast(int, v)));  // row mirror
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t m) {
+  m = umax(m, (uint32_t)dpp<0xB1>((int)m));
+  m = umax(m, (uint32_t)dpp<0x4E>((int)m));
+  m = umax(m, (uint32_t)dpp<0x141>((int)m));
+  m = umax(m, (uint32_t)dpp<0x140>((int)m));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)m, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)m, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)m, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)m, 48);
+  return umax(umax(r0, r1), umax(r2, r3));
+}
+
 typedef float f2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
-
-// Sum over the wave; every lane returns lane 0's total, so all lanes use the same value.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
-}
 
 // Two fp32 -> packed bf16, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
@@ -223,32 +256,51 @@ __device__ __forceinline__ uint4 modulate8(uint4 v, uint4 ms, uint4 mt, float me
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// Lane l holds chunks l, l + 64, ... of its row (NCH per lane, K <= 512 NCH). Every sum is
-// fp32: each lane adds its values in order, then a wave butterfly.
-//   1. mean0 = (sum of the row) / K; its rounding error grows with |mean|, so
-//   2. c = (sum of (x - mean0)) / K corrects it: x - mean0 is exact for x near mean0, and
-//      d = (x - mean0) - c is then accurate relative to the row's spread, not to |mean|
-//      (rows with a large common offset keep their variance);
-//   3. var = (sum of d^2) / K; rstd = 1 / sqrt(var + eps), both IEEE;
-//   4. y = (d rstd) (1 + s) + t with one fma, rounded to bf16 in place of x;
-//   5. the bf16 row y is quantized exactly as quant_rows_reg does (amax, scale, codes).
+// One row per wave, four rows per workgroup; lane l holds chunks l, l + 64, ... of its row (NCH
+// per lane, K <= 512 NCH). The workgroup's four rows share one copy of the modulation vectors in
+// LDS. Every sum is fp32: each lane adds
+// its values in order, then wave_sum.
+//   1. mean0 = (sum of the row) / K. Its rounding error grows with |mean|, so
+//   2. with e = x - mean0 (exact for x near mean0), c = (sum of e) / K and
+//      var = (sum of e^2) / K - c^2, both sums in one pass: c is tiny next to the row's spread,
+//      so nothing cancels, and d = e - c is accurate relative to the spread rather than to |mean|
+//      (rows with a large common offset keep their variance); rstd = 1 / sqrt(var + eps), IEEE;
+//   3. y = (d rstd) (1 + s) + t with one fma, rounded to bf16 in place of x;
+//   4. the bf16 row y is quantized exactly as quant_rows_reg does (amax, scale, codes).
+// Waves past the last row still take part in the workgroup barrier and store nothing.
 template <int NCH, bool kStoreY>
 __global__ void __launch_bounds__(256) ln_mod_quant_rows(
     const uint16_t* __restrict__ x, int R, int K, const uint16_t* __restrict__ mscale,
     const uint16_t* __restrict__ mshift, float eps, uint16_t* __restrict__ y,
     uint8_t* __restrict__ q, float* __restrict__ scale) {
+  constexpr int kFill = (64 * NCH + 255) / 256;  // chunks of each vector per thread
+  __shared__ uint4 smod[2][256 * kFill];
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= R) return;
+  const bool live = row < R;
   const int C = K >> 3;
-  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)row * (size_t)K);
-  const uint4* sr = reinterpret_cast<const uint4*>(mscale);
-  const uint4* tr = reinterpret_cast<const uint4*>(mshift);
+  // The modulation vectors go straight to LDS (16 bytes per lane, lane l of wave w at slot
+  // 256 f + 64 w + l), issued before the row loads. Slots past the row read chunk 0 and are
+  // never used.
+  {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int f = 0; f < kFill; ++f) {
+      const int c = threadIdx.x + 256 * f < C ? threadIdx.x + 256 * f : 0;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(mscale) + c,
+                                       (__attribute__((address_space(3))) void*)&smod[0][256 * f + 64 * w],
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(mshift) + c,
+                                       (__attribute__((address_space(3))) void*)&smod[1][256 * f + 64 * w],
+                                       16, 0, 0);
+    }
+  }
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)(live ? row : 0) * (size_t)K);
   uint4 v[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = lane + 64 * i;
-    v[i] = (c < C) ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
+    v[i] = (live && c < C) ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
   }
   // 1. first mean (chunks past the row are zeros and add nothing)
   float sum = 0.0f;
@@ -259,39 +311,33 @@ __global__ void __launch_bounds__(256) ln_mod_quant_rows(
     for (int j = 0; j < 4; ++j) sum = (sum + bf16_lo(w[j])) + bf16_hi(w[j]);
   }
   const float mean0 = wave_sum(sum) / (float)K;
-  // 2. its correction, over the row's own values only
-  float es = 0.0f;
+  // 2. correction and variance, over the row's own values only (chunks past it give e = 0)
+  float es = 0.0f, ss = 0.0f;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    if (lane + 64 * i < C) {
-      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    const float m = lane + 64 * i < C ? mean0 : 0.0f;
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) es = (es + (bf16_lo(w[j]) - mean0)) + (bf16_hi(w[j]) - mean0);
+    for (int j = 0; j < 4; ++j) {
+      const float e0 = bf16_lo(w[j]) - m, e1 = bf16_hi(w[j]) - m;
+      es = (es + e0) + e1;
+      ss = __builtin_fmaf(e0, e0, ss);
+      ss = __builtin_fmaf(e1, e1, ss);
     }
   }
   const float corr = wave_sum(es) / (float)K;
-  // 3. variance
-  float ss = 0.0f;
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    if (lane + 64 * i < C) {
-      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float d0 = (bf16_lo(w[j]) - mean0) - corr, d1 = (bf16_hi(w[j]) - mean0) - corr;
-        ss = __builtin_fmaf(d0, d0, ss);
-        ss = __builtin_fmaf(d1, d1, ss);
-      }
-    }
-  }
-  const float var = wave_sum(ss) / (float)K;
+  const float m2 = wave_sum(ss) / (float)K;
+  const float var = __builtin_fmaxf(__builtin_fmaf(-corr, corr, m2), 0.0f);
   const float rstd = 1.0f / __builtin_sqrtf(var + eps);
-  // 4. y in bf16, in place of x
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+  __syncthreads();                     // and every other wave's
+  // 3. y in bf16, in place of x
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = lane + 64 * i;
-    if (c < C) v[i] = modulate8(v[i], sr[c], tr[c], mean0, corr, rstd);
+    if (c < C) v[i] = modulate8(v[i], smod[0][c], smod[1][c], mean0, corr, rstd);
   }
+  if (!live) return;
   if (kStoreY) {
     uint4* yr = reinterpret_cast<uint4*>(y + (size_t)row * (size_t)K);
 #pragma unroll
@@ -306,7 +352,7 @@ __global__ void __launch_bounds__(256) ln_mod_quant_rows(
 #pragma unroll
   for (int i = 0; i < NCH; ++i) mx = absmax4(mx, v[i]);
   uint32_t m = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
-  m = __builtin_amdgcn_readfirstlane(wave_max(m));
+  m = wave_max_dpp(m);
   const float amax = __uint_as_float(m << 16);
   const float s = amax / kE4M3Max;
   if (lane == 0) scale[row] = s;

@@ -1,10 +1,10 @@
 """GPU parity of dq_layernorm_modulate_quantize_fp8 against the oracle.
 
 The kernel computes the row statistics and y in fp32, the oracle in float64. The kernel's sums
-run serially over at most K/64 + 8 values per lane and then over 6 butterfly levels, so each
-carries a relative error of at most gamma = h u / (1 - h u) with u = 2^-24 and h = K/64 + 14 (the
-classic bound for recursive summation). Following the kernel's steps (a first mean, a correction
-c = mean(x - mean0), d = (x - mean0) - c, the variance of d, rstd, one fma for y), its y before
+run serially over at most K/64 + 8 values per lane and then over 6 levels across the wave, so
+each carries a relative error of at most gamma = h u / (1 - h u) with u = 2^-24 and h = K/64 + 14
+(the classic bound for recursive summation). Following the kernel's steps (a first mean mean0,
+e = x - mean0, c = mean(e), var = mean(e^2) - c^2, rstd, d = e - c, one fma for y), its y before
 the bf16 rounding is within 2 gamma (|n (1 + scale)| + |1 + scale|) + 2 u |y| of the exact one
 (n the normalized value; the |1 + scale| term is c's absolute error, at most gamma times the
 row's spread, times rstd). That error is not relative to |y|: where n (1 + scale) and shift
