@@ -18,6 +18,9 @@ What it computes, and where the pages say so:
   * the block's LayerNorm and modulation folded into the activation quantizer (kernel fusion):
     page "Solucion de WaveSpeed para Acelerar la Generacion de Imagenes FLUX.1-dev", its lists
     of bottlenecks and of the engine's innovations (see `modulate.py` for the reading taken).
+  * the QKV projection with query/key normalization and rotary position embedding fused into
+    the GEMM's epilogue: page "Accelerarea generarii de imagini cu FLUX 3 Image Klein pe
+    GPU-urile Blackwell NVIDIA", the paragraph on the PrimsTS GEMMs (see `qkv.py`).
 
 The pages do not fix the granularity, the FP8 flavour, the scale formula or the rounding. The
 readings taken are: one scale per token (row of x) and per output channel (row of W); OCP E4M3
@@ -38,9 +41,13 @@ from .e4m3 import E4M3_MAX, decode_table, encode_e4m3
 from .quantize import quantize_rows
 from .linear import EPI_BIAS, EPI_GELU_TANH, EPI_GATED_RESIDUAL, gelu_tanh, linear_ref, round_to_bf16
 from .modulate import LN_EPS, layernorm_modulate, modulate_rows
+from .qkv import (HEAD_DIM, QK_NORM_EPS, linear_qkv_bf16, linear_qkv_ref, qkv_split_norm_rope,
+                  rms_norm, rope_pairs)
 
 __all__ = [
     "E4M3_MAX", "decode_table", "encode_e4m3", "quantize_rows",
     "EPI_BIAS", "EPI_GELU_TANH", "EPI_GATED_RESIDUAL", "gelu_tanh", "linear_ref", "round_to_bf16",
     "LN_EPS", "layernorm_modulate", "modulate_rows",
+    "HEAD_DIM", "QK_NORM_EPS", "linear_qkv_bf16", "linear_qkv_ref", "qkv_split_norm_rope",
+    "rms_norm", "rope_pairs",
 ]
