@@ -9,6 +9,7 @@ stream. Every step of the computation runs in the HIP kernels of libdq; there is
     qw, w_scale = dq_quantize_weight_fp8(w)        # w: bf16 [N, K], once per weight
     out = dq_linear_fp8(q, scale, qw, w_scale, bias, "gelu_tanh")
     q, scale, y = dq_layernorm_modulate_quantize_fp8(h, mod_scale, mod_shift)  # LN + modulate
+    oq, ok, ov = dq_linear_qkv_fp8(q, scale, qw, w_scale, heads, bias, norm_qk, cos, sin)
 
 dq_linear_fp8 takes a workspace that lets workgroups share tiles (see include/dq.h). By default
 the binding keeps one zero-filled workspace per (device, stream) and grows it when a larger
@@ -60,6 +61,9 @@ def lib() -> ctypes.CDLL:
         L.dq_layernorm_modulate_quantize_fp8.argtypes = [vp, i64, i64, vp, vp, ctypes.c_float,
                                                          vp, vp, vp, vp]
         L.dq_layernorm_modulate_quantize_fp8.restype = i32
+        L.dq_linear_qkv_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, vp,
+                                        ctypes.c_float, vp, vp, vp, vp, ctypes.c_uint64, vp]
+        L.dq_linear_qkv_fp8.restype = i32
         L.dq_linear_fp8_workspace_size.argtypes = [i64, i64, i64]
         L.dq_linear_fp8_workspace_size.restype = ctypes.c_uint64
         L.dq_status_string.argtypes = [i32]
@@ -171,6 +175,21 @@ def dq_linear_fp8_workspace_size(M, K, N):
 _WORKSPACES = {}
 
 
+def _resolve_workspace(workspace, dev, st, M, K, N):
+    """(workspace tensor or None, its size in bytes) for the 'auto' / None / tensor forms."""
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError(f"workspace must be 'auto', None or a tensor, not {workspace!r}")
+        need = dq_linear_fp8_workspace_size(M, K, N)
+        workspace = _cached_workspace(dev, st, need) if (need and M > 0) else None
+    if workspace is None:
+        return None, 0
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 \
+            or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the device")
+    return workspace, workspace.numel()
+
+
 def _cached_workspace(dev, stream, nbytes):
     """The zero-filled workspace of (device, stream), grown to at least nbytes. Every completed
     call leaves a workspace zeroed, and calls on one stream run in order, so it is reused."""
@@ -220,17 +239,7 @@ def dq_linear_fp8(q, scale, qw, w_scale, bias=None, epilogue="bias", gate=None, 
     _need(out, "out", torch.bfloat16, (M, N), dev)
     with torch.cuda.device(dev):
         st = stream if stream is not None else torch.cuda.current_stream(dev)
-        ws_bytes = 0
-        if isinstance(workspace, str):
-            if workspace != "auto":
-                raise ValueError(f"workspace must be 'auto', None or a tensor, not {workspace!r}")
-            need = dq_linear_fp8_workspace_size(M, K, N)
-            workspace = _cached_workspace(dev, st, need) if (need and M > 0) else None
-        if workspace is not None:
-            if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 \
-                    or workspace.device != dev or not workspace.is_contiguous():
-                raise ValueError("workspace must be a contiguous uint8 tensor on the device")
-            ws_bytes = workspace.numel()
+        workspace, ws_bytes = _resolve_workspace(workspace, dev, st, M, K, N)
         _check(lib().dq_linear_fp8(_ptr(q), _ptr(scale), M, K, _ptr(qw), _ptr(w_scale), N,
                                    _ptr(bias), EPILOGUES[epilogue], _ptr(gate), _ptr(residual),
                                    _ptr(out), _ptr(workspace), ws_bytes,
@@ -238,6 +247,52 @@ def dq_linear_fp8(q, scale, qw, w_scale, bias=None, epilogue="bias", gate=None, 
     return out
 
 
+HEAD_DIM = 128
+
+
+def dq_linear_qkv_fp8(q, scale, qw, w_scale, heads, bias, norm_qk, rope_cos, rope_sin, eps=1e-6,
+                      out=None, stream=None, workspace="auto"):
+    """W8A8 QKV projection with per-head query/key RMS norm and rotary embedding fused.
+
+    q uint8 [M, K], scale f32 [M], qw uint8 [3 heads 128, K], w_scale f32 [N], bias bf16 [N] or
+    None, norm_qk bf16 [2, 128] (query then key weights), rope_cos / rope_sin f32 [M, 64].
+    Returns (out_q, out_k, out_v), bf16 [heads, M, 128] each; `out` may supply the three.
+    """
+    where = "dq_linear_qkv_fp8"
+    if not isinstance(q, torch.Tensor) or q.dim() != 2 or not isinstance(qw, torch.Tensor) \
+            or qw.dim() != 2:
+        raise ValueError(f"{where}: q and qw must be 2-D tensors")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError(f"{where}: tensors must be on a GPU")
+    M, K = q.shape
+    heads = int(heads)
+    N = 3 * heads * HEAD_DIM
+    _need(q, "q", torch.uint8, (M, K), dev)
+    _need(scale, "scale", torch.float32, (M,), dev)
+    _need(qw, "qw", torch.uint8, (N, K), dev)
+    _need(w_scale, "w_scale", torch.float32, (N,), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, (N,), dev)
+    _need(norm_qk, "norm_qk", torch.bfloat16, (2, HEAD_DIM), dev)
+    _need(rope_cos, "rope_cos", torch.float32, (M, HEAD_DIM // 2), dev)
+    _need(rope_sin, "rope_sin", torch.float32, (M, HEAD_DIM // 2), dev)
+    if out is None:
+        out = tuple(torch.empty((heads, M, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+                    for _ in range(3))
+    for t, name in zip(out, ("out_q", "out_k", "out_v")):
+        _need(t, name, torch.bfloat16, (heads, M, HEAD_DIM), dev)
+    with torch.cuda.device(dev):
+        st = stream if stream is not None else torch.cuda.current_stream(dev)
+        workspace, ws_bytes = _resolve_workspace(workspace, dev, st, M, K, N)
+        _check(lib().dq_linear_qkv_fp8(_ptr(q), _ptr(scale), M, K, _ptr(qw), _ptr(w_scale), heads,
+                                       _ptr(bias), _ptr(norm_qk), _ptr(rope_cos), _ptr(rope_sin),
+                                       float(eps), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
+                                       _ptr(workspace), ws_bytes, ctypes.c_void_p(st.cuda_stream)),
+               where)
+    return tuple(out)
+
+
 __all__ = ["dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
-           "dq_layernorm_modulate_quantize_fp8",
+           "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8", "HEAD_DIM",
            "dq_linear_fp8_workspace_size", "DQError", "EPILOGUES", "lib", "LIB_PATH"]

@@ -154,6 +154,54 @@ int dq_layernorm_modulate_quantize_fp8(const void* x, int64_t M, int64_t K, cons
       static_cast<uint8_t*>(q), scale, static_cast<hipStream_t>(stream)));
 }
 
+int dq_linear_qkv_fp8(const void* q, const float* scale, int64_t M, int64_t K, const void* qw,
+                      const float* w_scale, int64_t heads, const void* bias, const void* norm_qk,
+                      const float* rope_cos, const float* rope_sin, float eps, void* out_q,
+                      void* out_k, void* out_v, void* workspace, uint64_t workspace_bytes,
+                      void* stream) {
+  if (heads < 1 || heads > kMaxDim / (3 * dq::kHeadDim)) return DQ_ERR_SHAPE;
+  const int64_t N = 3 * heads * dq::kHeadDim;
+  const int shape = check_linear_shape(M, K, N);
+  if (shape != DQ_OK) return shape;
+  if (!std::isfinite(eps) || !(eps > 0.0f)) return DQ_ERR_VALUE;
+  if (M == 0) return DQ_OK;
+  if (!q || !scale || !qw || !w_scale || !norm_qk || !rope_cos || !rope_sin || !out_q || !out_k ||
+      !out_v)
+    return DQ_ERR_NULL;
+  if (!aligned16(q) || !aligned16(scale) || !aligned16(qw) || !aligned16(w_scale) ||
+      (bias && !aligned16(bias)) || !aligned16(norm_qk) || !aligned16(rope_cos) ||
+      !aligned16(rope_sin) || !aligned16(out_q) || !aligned16(out_k) || !aligned16(out_v))
+    return DQ_ERR_ALIGN;
+  const uint64_t m = static_cast<uint64_t>(M), k = static_cast<uint64_t>(K),
+                 n = static_cast<uint64_t>(N);
+  const uint64_t rope_bytes = m * static_cast<uint64_t>(dq::kHeadDim / 2) * 4;
+  const void* ins[8] = {q, scale, qw, w_scale, bias, norm_qk, rope_cos, rope_sin};
+  const uint64_t in_bytes[8] = {m * k, 4 * m, n * k, 4 * n, bias ? 2 * n : 0,
+                                4 * static_cast<uint64_t>(dq::kHeadDim), rope_bytes, rope_bytes};
+  const uint64_t ob = 2 * m * (n / 3);  // one of the three outputs
+  void* outs[3] = {out_q, out_k, out_v};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 8; ++i)
+      if (overlap(outs[o], ob, ins[i], in_bytes[i])) return DQ_ERR_ALIAS;
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      if (overlap(outs[o], ob, outs[o2], ob)) return DQ_ERR_ALIAS;
+  }
+  if (workspace) {
+    const uint64_t need = dq::linear_workspace_bytes(M, K, N);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
+      return DQ_ERR_WORKSPACE;
+    for (int i = 0; i < 8; ++i)
+      if (overlap(workspace, need, ins[i], in_bytes[i])) return DQ_ERR_ALIAS;
+    for (int o = 0; o < 3; ++o)
+      if (overlap(workspace, need, outs[o], ob)) return DQ_ERR_ALIAS;
+  }
+  return hip_status(dq::launch_linear_qkv(
+      static_cast<const uint8_t*>(q), scale, M, K, static_cast<const uint8_t*>(qw), w_scale,
+      heads, static_cast<const uint16_t*>(bias), static_cast<const uint16_t*>(norm_qk), rope_cos,
+      rope_sin, eps, static_cast<uint16_t*>(out_q), static_cast<uint16_t*>(out_k),
+      static_cast<uint16_t*>(out_v), workspace, static_cast<hipStream_t>(stream)));
+}
+
 uint64_t dq_linear_fp8_workspace_size(int64_t M, int64_t K, int64_t N) {
   if (check_linear_shape(M, K, N) != DQ_OK) return 0;
   return dq::linear_workspace_bytes(M, K, N);
@@ -176,6 +224,6 @@ const char* dq_status_string(int status) {
 
 int dq_last_hip_error(void) { return g_last_hip_error; }
 
-int dq_abi_version(void) { return 3; }
+int dq_abi_version(void) { return 4; }
 
 }  // extern "C"

@@ -52,4 +52,14 @@ hipError_t launch_linear(const uint8_t* q, const float* scale, int64_t M, int64_
                          int epilogue, const uint16_t* gate, const uint16_t* residual,
                          uint16_t* out, void* workspace, hipStream_t stream);
 
+// FP8 GEMM with the QKV epilogue: N = 3 heads kHeadDim; query and key RMS-normalized per head
+// (weights norm_qk [2][kHeadDim]) and rotated pairwise by rope_cos/sin [M][kHeadDim / 2]; outputs
+// out_q/k/v [heads][M][kHeadDim]. Arguments are already validated.
+constexpr int64_t kHeadDim = 128;
+hipError_t launch_linear_qkv(const uint8_t* q, const float* scale, int64_t M, int64_t K,
+                             const uint8_t* qw, const float* w_scale, int64_t heads,
+                             const uint16_t* bias, const uint16_t* norm_qk, const float* rope_cos,
+                             const float* rope_sin, float eps, uint16_t* out_q, uint16_t* out_k,
+                             uint16_t* out_v, void* workspace, hipStream_t stream);
+
 }  // namespace dq

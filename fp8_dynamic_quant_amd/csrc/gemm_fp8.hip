@@ -72,7 +72,7 @@ constexpr int kParamBufs = 3;                   // part i of a share uses buffer
 constexpr int kGroupM = 4;                      // tile rows per group in the tile order
 constexpr int kPartFloats = kBM * kBN;
 
-enum { EPI_BIAS = 0, EPI_GELU_TANH = 1, EPI_GATED_RESIDUAL = 2 };
+enum { EPI_BIAS = 0, EPI_GELU_TANH = 1, EPI_GATED_RESIDUAL = 2, EPI_QKV = 3 };
 
 struct Params {
   const uint8_t* A;          // q  [M, K]
@@ -92,6 +92,15 @@ struct Params {
   int splits;                // parts per left-over tile (1: not cut)
   int part_steps;            // nk / splits
   int narrow;                // 1: each left-over tile runs as two 256 x 128 halves (not cut)
+  // QKV epilogue only: N = 3 heads 128; out_q/k/v [heads, M, 128]
+  const uint16_t* norm_qk;   // [2][128] query then key RMS-norm weights
+  const float* rope_cos;     // [M, 64]
+  const float* rope_sin;     // [M, 64]
+  uint16_t* out_q;
+  uint16_t* out_k;
+  uint16_t* out_v;
+  float qk_eps;
+  int heads;
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -337,6 +346,8 @@ __device__ __forceinline__ void copy_params(const Params& p, const TileDesc& d, 
     copy_to_lds(buffer_rsrc(p.bias + n0, p.bias ? cols * 2u : 0u), lo, lp);
   } else if (EPI == EPI_GATED_RESIDUAL) {
     copy_to_lds(buffer_rsrc(p.gate + n0, cols * 2u), lo, lp);
+  } else if (EPI == EPI_QKV) {
+    copy_to_lds(buffer_rsrc(p.norm_qk, 512u), lo, lp);
   }
 }
 
@@ -488,6 +499,124 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[NB][4], const Params&
         o.z = pack_bf16(y[4], y[5]);
         o.w = pack_bf16(y[6], y[7]);
         if (live) *reinterpret_cast<uint4*>(p.out + off) = o;
+      }
+    }
+  }
+}
+
+// QKV epilogue. The output row holds the query, key and value of `heads` heads of 128 channels
+// (in that order). v = acc sa sw + bias as in the plain epilogue; query and key channels are then
+// divided by their head's root mean square (over the head's 128 channels, plus eps) and scaled by
+// the query or key weight, and each channel pair (2i, 2i + 1) is turned by the token's angle:
+//   (a, b) -> (cos a - sin b, sin a + cos b),  cos, sin = rope_cos/sin[m, i];
+// value channels pass through. Every output goes head-major, out[(head M + m) 128 + channel],
+// rounded once to bf16.
+// A wave's columns lie inside one head, but a head spans several waves (2 with NB = 2, 4 with
+// NB = 1) of both groups, which the caller has aligned. Each wave writes its per-row sums of
+// squares to `scratch` (4 KiB, [wn][256 rows]); after one workgroup barrier, which every wave
+// reaches, each adds its head's sums in wave order, so all waves of a head use the same bits.
+template <int NB>
+__device__ __forceinline__ void epilogue_qkv(const v16f (&acc)[NB][4], const Params& p, int m0,
+                                             int n0, int wm, int wn, int lane, const uint8_t* pb,
+                                             float* scratch) {
+  const float* s_sa = reinterpret_cast<const float*>(pb);
+  const float* s_sw = reinterpret_cast<const float*>(pb + 1024);
+  const uint16_t* s_b = reinterpret_cast<const uint16_t*>(pb + 2048);
+  const uint16_t* s_w = reinterpret_cast<const uint16_t*>(pb + 3072);
+  const int hi = lane >> 5;
+  const int HD = p.heads * 128;
+  const int nw = n0 + wn * 32 * NB;            // this wave's first column (uniform)
+  const int region = nw / HD;                  // 0 query, 1 key, 2 value, 3: past N
+  const int head = (nw - region * HD) >> 7;
+  const int dw = (nw - region * HD) & 127;     // channel of that column inside its head
+  const bool normed = region < 2;
+  // v for 4 + 4 columns of 8-column groups 2 gp and 2 gp + 1 (before the half swap)
+  auto dequant = [&](int bm, int bn, int gp, float (&v)[2][4]) {
+    const float sam = s_sa[wm * 128 + bm * 32 + (lane & 31)];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int g = gp * 2 + h;
+      const int nl = wn * 32 * NB + bn * 32 + g * 8 + hi * 4;
+      const float4 swv = *reinterpret_cast<const float4*>(s_sw + nl);
+      const uint2 bb = *reinterpret_cast<const uint2*>(s_b + nl);
+      v[h][0] = fmaf(acc[bn][bm][g * 4 + 0] * sam, swv.x, bf16_lo(bb.x));
+      v[h][1] = fmaf(acc[bn][bm][g * 4 + 1] * sam, swv.y, bf16_hi(bb.x));
+      v[h][2] = fmaf(acc[bn][bm][g * 4 + 2] * sam, swv.z, bf16_lo(bb.y));
+      v[h][3] = fmaf(acc[bn][bm][g * 4 + 3] * sam, swv.w, bf16_hi(bb.y));
+    }
+  };
+  if (normed) {
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int bn = 0; bn < NB; ++bn)
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+          float v[2][4];
+          dequant(bm, bn, gp, v);
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ss = fmaf(v[h][j], v[h][j], ss);
+        }
+      // lanes l and l + 32 hold the two halves of the row's columns: lower + upper in both
+      float lo_s = ss, up_s = ss;
+      swap_halves(lo_s, up_s);
+      const float row_ss = lo_s + up_s;
+      if (hi == 0) scratch[wn * 256 + wm * 128 + bm * 32 + lane] = row_ss;
+    }
+  }
+  phase_barrier();  // every wave's sums are in LDS
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm) {
+    const int ml = wm * 128 + bm * 32 + (lane & 31);
+    const int m = m0 + ml;
+    const int mc = m < p.M ? m : p.M - 1;  // rows past M are computed but not stored
+    float rr = 1.0f;
+    if (normed) {
+      float t;
+      if (NB == 2) {
+        const int w0 = wn & ~1;
+        t = scratch[w0 * 256 + ml] + scratch[(w0 + 1) * 256 + ml];
+      } else {
+        t = ((scratch[ml] + scratch[256 + ml]) + scratch[512 + ml]) + scratch[768 + ml];
+      }
+      rr = 1.0f / __builtin_sqrtf(fmaf(t, 1.0f / 128.0f, p.qk_eps));
+    }
+#pragma unroll
+    for (int bn = 0; bn < NB; ++bn) {
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp) {
+        float v[2][4];
+        dequant(bm, bn, gp, v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) swap_halves(v[0][j], v[1][j]);
+        const int d = dw + bn * 32 + (gp * 2 + hi) * 8;  // channel of y[0] inside the head
+        float y[8] = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+        if (normed) {
+          const uint4 ww = *reinterpret_cast<const uint4*>(s_w + region * 128 + d);
+          const uint32_t wv[4] = {ww.x, ww.y, ww.z, ww.w};
+          const float4 c = *reinterpret_cast<const float4*>(p.rope_cos + (size_t)mc * 64 + (d >> 1));
+          const float4 sn = *reinterpret_cast<const float4*>(p.rope_sin + (size_t)mc * 64 + (d >> 1));
+          const float cs[4] = {c.x, c.y, c.z, c.w}, sv[4] = {sn.x, sn.y, sn.z, sn.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float a = (y[2 * j] * rr) * bf16_lo(wv[j]);
+            const float b = (y[2 * j + 1] * rr) * bf16_hi(wv[j]);
+            y[2 * j] = fmaf(cs[j], a, -(sv[j] * b));
+            y[2 * j + 1] = fmaf(sv[j], a, cs[j] * b);
+          }
+        }
+        uint4 o;
+        o.x = pack_bf16(y[0], y[1]);
+        o.y = pack_bf16(y[2], y[3]);
+        o.z = pack_bf16(y[4], y[5]);
+        o.w = pack_bf16(y[6], y[7]);
+        if (m < p.M && region < 3) {
+          uint16_t* out = region == 0 ? p.out_q : region == 1 ? p.out_k : p.out_v;
+          *reinterpret_cast<uint4*>(out + ((size_t)head * (size_t)p.M + (size_t)m) * 128 + d) = o;
+        }
       }
     }
   }
@@ -708,17 +837,30 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
     int m0, n0;
     item_origin<NB>(p, t, half, m0, n0);
     const uint8_t* pb = pbuf + (part % kParamBufs) * kParamBytes;
+    // the QKV epilogue exchanges sums between the groups, so like a cut tile it first aligns
+    // them; its scratch is the parameter buffer of the item after next (free until then)
+    float* scratch = reinterpret_cast<float*>(pbuf + ((part + 2) % kParamBufs) * kParamBytes);
     if constexpr (NB == 2) {
       const bool cut = cutp >= 0;
+      const bool align = cut || EPI == EPI_QKV;
       bool write = true;
-      if (cut) {
-        if (g == 0) phase_barrier();  // group 1's last MFMAs of this part are done
-        write = finish_split(acc, p, t, cutp, wave, lane, &s_last);
+      if (align && g == 0) phase_barrier();  // group 1's last MFMAs of this item are done
+      if (cut) write = finish_split(acc, p, t, cutp, wave, lane, &s_last);
+      if (write) {
+        if constexpr (EPI == EPI_QKV)
+          epilogue_qkv<2>(acc, p, m0, n0, wm, wn, lane, pb, scratch);
+        else
+          epilogue<EPI, 2>(acc, p, m0, n0, wm, wn, lane, pb);
       }
-      if (write) epilogue<EPI, 2>(acc, p, m0, n0, wm, wn, lane, pb);
-      if (cut && g == 1) phase_barrier();  // back to one phase behind
+      if (align && g == 1) phase_barrier();  // back to one phase behind
     } else {
-      epilogue<EPI, 1>(acc, p, m0, n0, wm, wn, lane, pb);
+      if constexpr (EPI == EPI_QKV) {
+        if (g == 0) phase_barrier();
+        epilogue_qkv<1>(acc, p, m0, n0, wm, wn, lane, pb, scratch);
+        if (g == 1) phase_barrier();
+      } else {
+        epilogue<EPI, 1>(acc, p, m0, n0, wm, wn, lane, pb);
+      }
     }
     ++part;
     ++c.item;
@@ -765,20 +907,10 @@ int compute_units() {
 
 }  // namespace
 
-hipError_t launch_linear(const uint8_t* q, const float* scale, int64_t M, int64_t K,
-                         const uint8_t* qw, const float* w_scale, int64_t N, const uint16_t* bias,
-                         int epilogue, const uint16_t* gate, const uint16_t* residual,
-                         uint16_t* out, void* workspace, hipStream_t stream) {
-  if (M == 0) return hipSuccess;
-  Params p;
-  p.A = q;
-  p.B = qw;
-  p.sa = scale;
-  p.sw = w_scale;
-  p.bias = bias;
-  p.gate = gate;
-  p.residual = residual;
-  p.out = out;
+// Sizes, the tile schedule (full rounds, then whole, narrow or cut left-over tiles) and the
+// launches for a Params whose pointers are set.
+static hipError_t schedule_and_launch(Params& p, int64_t M, int64_t K, int64_t N, int epilogue,
+                                      void* workspace, hipStream_t stream) {
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
@@ -853,8 +985,49 @@ hipError_t launch_linear(const uint8_t* q, const float* scale, int64_t M, int64_
   switch (epilogue) {
     case EPI_BIAS: return launch_epi<EPI_BIAS>(p, g, narrow_grid, stream);
     case EPI_GELU_TANH: return launch_epi<EPI_GELU_TANH>(p, g, narrow_grid, stream);
+    case EPI_QKV: return launch_epi<EPI_QKV>(p, g, narrow_grid, stream);
     default: return launch_epi<EPI_GATED_RESIDUAL>(p, g, narrow_grid, stream);
   }
+}
+
+hipError_t launch_linear(const uint8_t* q, const float* scale, int64_t M, int64_t K,
+                         const uint8_t* qw, const float* w_scale, int64_t N, const uint16_t* bias,
+                         int epilogue, const uint16_t* gate, const uint16_t* residual,
+                         uint16_t* out, void* workspace, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  Params p{};
+  p.A = q;
+  p.B = qw;
+  p.sa = scale;
+  p.sw = w_scale;
+  p.bias = bias;
+  p.gate = gate;
+  p.residual = residual;
+  p.out = out;
+  return schedule_and_launch(p, M, K, N, epilogue, workspace, stream);
+}
+
+hipError_t launch_linear_qkv(const uint8_t* q, const float* scale, int64_t M, int64_t K,
+                             const uint8_t* qw, const float* w_scale, int64_t heads,
+                             const uint16_t* bias, const uint16_t* norm_qk, const float* rope_cos,
+                             const float* rope_sin, float eps, uint16_t* out_q, uint16_t* out_k,
+                             uint16_t* out_v, void* workspace, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  Params p{};
+  p.A = q;
+  p.B = qw;
+  p.sa = scale;
+  p.sw = w_scale;
+  p.bias = bias;
+  p.norm_qk = norm_qk;
+  p.rope_cos = rope_cos;
+  p.rope_sin = rope_sin;
+  p.out_q = out_q;
+  p.out_k = out_k;
+  p.out_v = out_v;
+  p.qk_eps = eps;
+  p.heads = (int)heads;
+  return schedule_and_launch(p, M, K, 3 * heads * 128, EPI_QKV, workspace, stream);
 }
 
 }  // namespace dq

@@ -138,6 +138,42 @@ int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const
                   uint64_t workspace_bytes, void* stream);
 
 /*
+ * dq_linear_qkv_fp8 -- the attention input projection: the W8A8 GEMM of dq_linear_fp8 with an
+ * epilogue that splits the output into queries, keys and values, normalizes queries and keys per
+ * head and applies the rotary position embedding, all before the single rounding to bf16.
+ * The page "Accelerarea generarii de imagini cu FLUX 3 Image Klein pe GPU-urile Blackwell NVIDIA"
+ * names this fused epilogue (query/key/value projections with query/key normalization and
+ * rotary position embeddings, in its paragraph on the PrimsTS GEMMs); it gives no formula, and
+ * the reading taken is the FLUX-style attention input:
+ *
+ *   v[m, n] = acc[m, n] * scale[m] * w_scale[n] + bias[n],  n < N = 3 * heads * 128: the query,
+ *             key and value of `heads` heads of 128 channels, in that order
+ *   query / key head row r (128 channels):  r' = r / sqrt(mean(r^2) + eps) * norm_qk[0 / 1][:]
+ *   then each channel pair (2i, 2i + 1):    (a, b) -> (cos a - sin b, sin a + cos b),
+ *                                           cos = rope_cos[m, i], sin = rope_sin[m, i]
+ *   value head rows unchanged
+ *   out_q / out_k / out_v [head, m, c] = bf16 of the result (nearest even), head-major
+ *
+ *   q, scale, qw, w_scale  as dq_linear_fp8 (N = 3 * heads * 128)
+ *   bias        bf16 [N] or NULL (= zero bias)
+ *   norm_qk     bf16 [2][128]  query then key RMS-norm weights
+ *   rope_cos    float [M][64]  cosine of the angle of token m and channel pair i
+ *   rope_sin    float [M][64]  its sine
+ *   eps         float          added to the mean square; finite and > 0 (else DQ_ERR_VALUE)
+ *   out_q, out_k, out_v  bf16 [heads][M][128] each
+ *   workspace, workspace_bytes  as dq_linear_fp8 (size dq_linear_fp8_workspace_size(M, K, N))
+ *
+ * Everything after the contraction is fp32; the head's mean square is summed in fp32.
+ * Requirements: as dq_linear_fp8 for M, K and N = 3 * heads * 128 with 1 <= heads; every pointer
+ * 16-byte aligned; no output overlapping an input, another output or the workspace.
+ */
+int dq_linear_qkv_fp8(const void* q, const float* scale, int64_t M, int64_t K, const void* qw,
+                      const float* w_scale, int64_t heads, const void* bias, const void* norm_qk,
+                      const float* rope_cos, const float* rope_sin, float eps, void* out_q,
+                      void* out_k, void* out_v, void* workspace, uint64_t workspace_bytes,
+                      void* stream);
+
+/*
  * dq_linear_fp8_workspace_size -- bytes of workspace dq_linear_fp8 uses for an M x K -> N
  * problem (the same on every device), or 0 if the sizes break dq_linear_fp8's requirements:
  * 256 MiB (1024 partial 256 x 256 fp32 tiles) plus 4 bytes per 256 x 256 output tile, rounded up
@@ -185,7 +221,7 @@ const char* dq_status_string(int status);
 /* The hipError_t behind the most recent DQ_ERR_HIP returned on the calling thread (0 if none). */
 int dq_last_hip_error(void);
 
-/* ABI version of this header (currently 3). */
+/* ABI version of this header (currently 4). */
 int dq_abi_version(void);
 
 #ifdef __cplusplus

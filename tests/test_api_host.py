@@ -28,6 +28,8 @@ def lib():
                                 ctypes.c_uint64, vp]
     L.dq_layernorm_modulate_quantize_fp8.argtypes = [vp, i64, i64, vp, vp, ctypes.c_float, vp,
                                                      vp, vp, vp]
+    L.dq_linear_qkv_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, vp, ctypes.c_float,
+                                    vp, vp, vp, vp, ctypes.c_uint64, vp]
     L.dq_linear_fp8_workspace_size.argtypes = [i64, i64, i64]
     L.dq_linear_fp8_workspace_size.restype = ctypes.c_uint64
     L.dq_status_string.restype = ctypes.c_char_p
@@ -43,7 +45,7 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
-              "dq_layernorm_modulate_quantize_fp8",
+              "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8",
               "dq_linear_fp8_workspace_size", "dq_status_string", "dq_last_hip_error",
               "dq_abi_version"):
         assert n in names
@@ -55,7 +57,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dq_abi_version() == 3
+    assert lib.dq_abi_version() == 4
     for st in range(9):
         s = lib.dq_status_string(st)
         assert s and len(s) > 1
@@ -175,6 +177,53 @@ def test_linear_argument_checks(lib):
     assert lin(lib, epi=GATED, out=Re + 64) == ALIAS         # partial overlap with residual
 
 
+NQ, CS, SN, OQ, OK_, OV = (0x10000000 * i for i in range(10, 16))   # fake, far from the others
+
+
+def qkv(lib, M=64, K=256, heads=1, q=Aq, sa=As, qw=Wq, sw=Ws, bias=Bi, nqk=NQ, cos=CS, sin=SN,
+        eps=1e-6, oq=OQ, ok=OK_, ov=OV, ws=None, ws_bytes=0):
+    return lib.dq_linear_qkv_fp8(q, sa, M, K, qw, sw, heads, bias, nqk, cos, sin, eps, oq, ok, ov,
+                                 ws, ws_bytes, None)
+
+
+def test_linear_qkv_argument_checks(lib):
+    assert qkv(lib, M=0) == OK
+    assert qkv(lib, M=0, q=None, oq=None) == OK               # empty: pointers are not checked
+    assert qkv(lib, heads=0) == SHAPE
+    assert qkv(lib, heads=-2) == SHAPE
+    assert qkv(lib, heads=1 << 30) == SHAPE
+    assert qkv(lib, K=192) == SHAPE                          # K % 128
+    assert qkv(lib, M=-1) == SHAPE
+    assert qkv(lib, M=0, K=100) == SHAPE
+    assert qkv(lib, eps=0.0) == VALUE
+    assert qkv(lib, eps=-1.0) == VALUE
+    assert qkv(lib, eps=float("nan")) == VALUE
+    assert qkv(lib, M=0, eps=float("inf")) == VALUE
+    for name in ("q", "sa", "qw", "sw", "nqk", "cos", "sin", "oq", "ok", "ov"):
+        assert qkv(lib, **{name: None}) == NULL, name
+    base = dict(q=Aq, sa=As, qw=Wq, sw=Ws, bias=Bi, nqk=NQ, cos=CS, sin=SN, oq=OQ, ok=OK_, ov=OV)
+    for name, val in base.items():
+        assert qkv(lib, **{name: val + 8}) == ALIGN, name
+    # outputs are [heads, M, 128] bf16 = 16 KiB here; the fake inputs are far apart
+    assert qkv(lib, oq=Aq) == ALIAS                           # query output over the codes
+    assert qkv(lib, ok=CS + 64) == ALIAS                      # key output over the cosines
+    assert qkv(lib, ov=NQ - 1024) == ALIAS                    # value output runs into the weights
+    assert qkv(lib, ok=OQ + 16384 - 16) == ALIAS              # two outputs overlap
+    assert qkv(lib, ov=Bi) == ALIAS
+    # adjacent outputs are fine (the call then fails on the NULL codes, launching nothing)
+    assert qkv(lib, ok=OQ + 16384, ov=OQ + 32768, q=None) == NULL
+
+
+def test_linear_qkv_workspace_checks(lib):
+    need = lib.dq_linear_fp8_workspace_size(64, 256, 384)
+    assert qkv(lib, ws=Wk, ws_bytes=need - 1) == WORKSPACE
+    assert qkv(lib, ws=Wk + 16, ws_bytes=need) == WORKSPACE
+    assert qkv(lib, ws=Wk, ws_bytes=need, oq=Wk + 4096) == ALIAS
+    assert qkv(lib, ws=Wk, ws_bytes=need, cos=Wk + (1 << 20)) == ALIAS
+    assert qkv(lib, ws=Wk, ws_bytes=need, q=None) == NULL
+    assert lib.dq_last_hip_error() == 0
+
+
 def test_workspace_size(lib):
     size = lib.dq_linear_fp8_workspace_size
     # a fixed region of 1024 partial 256 x 256 fp32 tiles, then one 4-byte counter per
@@ -208,9 +257,10 @@ def test_last_hip_error_untouched_by_argument_errors(lib):
 def test_python_binding_names_match_the_c_entry_points():
     import fp8_dynamic_quant_amd as dq
     for name in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
-                 "dq_layernorm_modulate_quantize_fp8", "dq_linear_fp8_workspace_size"):
+                 "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8",
+                 "dq_linear_fp8_workspace_size"):
         assert callable(getattr(dq, name))
-    assert dq.lib().dq_abi_version() == 3
+    assert dq.lib().dq_abi_version() == 4
     assert dq.dq_linear_fp8_workspace_size(4608, 3072, 12288) == 3584 + 1024 * 262144
 
 

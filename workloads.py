@@ -198,6 +198,35 @@ def make_modulation(K: int, seed: int, sigma: float = 0.5):
     return f32_to_bf16_bits(scale), f32_to_bf16_bits(shift)
 
 
+def make_qk_norm(seed: int) -> np.ndarray:
+    """bf16 bit patterns of the query and key RMS-norm weights [2, 128]: 1 + 0.1 N(0,1), from
+    PCG64 seeded with [seed, 130363]."""
+    rng = np.random.default_rng([seed, 130363])
+    return f32_to_bf16_bits(np.float32(1.0) + rng.standard_normal((2, 128), dtype=np.float32)
+                            * np.float32(0.1))
+
+
+def make_rope(M: int, n_text: int = 512, grid_w: int = 64, axes=(16, 56, 56),
+              theta: float = 10000.0):
+    """cos and sin [M, 64] float32 of FLUX-style rotary angles. Token m < n_text is a text
+    token at position (0, 0, 0); token n_text + j is an image token at (0, j // grid_w,
+    j % grid_w). The 64 channel pairs are split over the three position axes (8, 28, 28 pairs);
+    pair p of an axis with d channels turns by position * theta^(-2p / d). These are inputs of
+    the attention projection (the model computes them from token positions), not part of the
+    quantized linear."""
+    n_text = min(n_text, M)
+    ids = np.zeros((M, 3), dtype=np.float64)
+    j = np.arange(M - n_text)
+    ids[n_text:, 1] = j // grid_w
+    ids[n_text:, 2] = j % grid_w
+    ang = []
+    for a, d in enumerate(axes):
+        omega = theta ** (-np.arange(0, d, 2, dtype=np.float64) / d)
+        ang.append(ids[:, a:a + 1] * omega[None, :])
+    ang = np.concatenate(ang, axis=1)
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
 # ---------------------------------------------------------------------------------------------
 # Full denoising step: inputs drawn on the device (8.6 GB of weights are too slow to draw on the
 # host). torch.Generator on the device, seeded 4_000_000 + 100 * block + 10 * stream + linear.
