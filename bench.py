@@ -11,7 +11,8 @@ brings the chip to the steady clock it holds under this load before the timed st
 
 Prints one JSON line: whole-step throughput (TFLOP/s), the GEMM kernel against the FP8 matrix
 peak, the quantize kernel and the fused LayerNorm + modulation + quantize kernel against HBM
-bandwidth, the linears of a full FLUX-dev denoising step
+bandwidth, the attention input projection with its fused query/key norm + rotary epilogue, the
+linears of a full FLUX-dev denoising step
 (ms), and the CPU oracle timed on the host as a baseline.
 """
 import argparse
@@ -195,6 +196,75 @@ def bench_modulate(M, K, steps, n_sets, seed=11):
             "unfused_us": timed(unfused, max(reps // 4, 1))}
 
 
+def bench_qkv(steps, warmup, n_sets, M=4096, K=3072, heads=24, seed=3200):
+    """The attention input projection of the image stream at 1024^2 (4096 tokens, 3072 -> 3 x 24
+    heads x 128) with the fused query/key RMS norm + rotary epilogue, against the same GEMM with
+    the plain bias epilogue and, for context, that GEMM followed by the torch ops the fusion
+    replaces. Event pairs around each call; returns microseconds per call."""
+    import torch
+    import torch.nn.functional as F
+    import fp8_dynamic_quant_amd as dq
+    from workloads import LinearShape, make_linear_inputs, make_qk_norm, make_rope
+
+    dev = torch.device("cuda:0")
+    N = 3 * heads * 128
+    shape = LinearShape("image.qkv", M, K, N, "bias", 31, 30.0)
+    inp = make_linear_inputs(shape, seed)
+    cos, sin = make_rope(M, n_text=0)
+    tcos = torch.from_numpy(cos).to(dev)
+    tsin = torch.from_numpy(sin).to(dev)
+    nqk = to_dev_bf16(torch, make_qk_norm(seed), dev)
+    sets = []
+    for _ in range(n_sets):
+        q, sa = dq.dq_quantize_fp8(to_dev_bf16(torch, inp.x, dev))
+        qw, sw = dq.dq_quantize_weight_fp8(to_dev_bf16(torch, inp.w, dev))
+        sets.append({"q": q, "sa": sa, "qw": qw, "sw": sw, "b": to_dev_bf16(torch, inp.bias, dev),
+                     "o": tuple(torch.empty((heads, M, 128), dtype=torch.bfloat16, device=dev)
+                                for _ in range(3)),
+                     "plain": torch.empty((M, N), dtype=torch.bfloat16, device=dev)})
+    torch.cuda.synchronize()
+    c2 = tcos[:, None, :]
+    s2 = tsin[:, None, :]
+
+    def fused(st):
+        dq.dq_linear_qkv_fp8(st["q"], st["sa"], st["qw"], st["sw"], heads, st["b"], nqk, tcos,
+                             tsin, out=st["o"])
+
+    def plain(st):
+        dq.dq_linear_fp8(st["q"], st["sa"], st["qw"], st["sw"], st["b"], "bias", out=st["plain"])
+
+    def unfused(st):
+        plain(st)
+        t = st["plain"].view(M, 3, heads, 128)
+        outs = []
+        for r in range(2):
+            h = F.rms_norm(t[:, r].float(), (128,), nqk[r].float(), eps=1e-6)
+            a, b = h[..., 0::2], h[..., 1::2]
+            rot = torch.stack((c2 * a - s2 * b, s2 * a + c2 * b), dim=-1).flatten(-2)
+            outs.append(rot.to(torch.bfloat16).transpose(0, 1).contiguous())
+        outs.append(t[:, 2].transpose(0, 1).contiguous())
+        return outs
+
+    def timed(fn, n):
+        for i in range(warmup):
+            fn(sets[i % n_sets])
+        torch.cuda.synchronize()
+        evs = []
+        for i in range(n):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn(sets[i % n_sets])
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+
+    return {"fused_us": timed(fused, steps), "plain_us": timed(plain, steps),
+            "unfused_us": timed(unfused, max(steps // 4, 5)), "flops": 2 * M * N * K,
+            "shape": [M, K, N], "heads": heads}
+
+
 def bench_dit_step(steps, warmup):
     """All linears of one 1024^2 FLUX-dev denoising step (228 quantize + GEMM pairs), distinct
     weights per block, timed end to end as one sequence on one stream."""
@@ -310,6 +380,7 @@ def main():
     ap.add_argument("--dit-steps", type=int, default=5)
     ap.add_argument("--no-dit", action="store_true")
     ap.add_argument("--no-modulate", action="store_true")
+    ap.add_argument("--no-qkv", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB plain copy first (reference for HBM counters)")
@@ -417,6 +488,25 @@ def main():
                        "frac": round(gb_y / PEAK_HBM_GBPS, 4),
                        "algorithmic_bytes_per_launch": b_y},
             "unfused_torch_then_quantize_us": round(mo["unfused_us"], 2),
+        }
+    if not args.no_qkv:
+        qk = bench_qkv(args.steps, min(args.warmup, 100), min(args.sets, 4))
+        tf = qk["flops"] / qk["fused_us"] / 1e6
+        log(f"QKV + norm + rotary {qk['shape']}: {qk['fused_us']:.1f} us ({tf:.0f} TFLOP/s); "
+            f"bias epilogue {qk['plain_us']:.1f} us; unfused {qk['unfused_us']:.1f} us")
+        res["qkv_linear"] = {
+            "kernel": "gemm_fp8_pp<qkv>",
+            "timing": "HIP events around each call, rotating inputs (1 or 2 launches per call)",
+            "shape": qk["shape"], "heads": qk["heads"],
+            "bound": "mfma",
+            "achieved": round(tf, 1),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+            "avg_launch_us": round(qk["fused_us"], 2),
+            "algorithmic_flop_per_launch": qk["flops"],
+            "bias_epilogue_us": round(qk["plain_us"], 2),
+            "unfused_torch_us": round(qk["unfused_us"], 2),
         }
     if not args.no_dit:
         log("DiT step: generating 228 distinct FP8 weights on the device")

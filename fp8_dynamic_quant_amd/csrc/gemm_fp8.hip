@@ -74,6 +74,20 @@ constexpr int kPartFloats = kBM * kBN;
 
 enum { EPI_BIAS = 0, EPI_GELU_TANH = 1, EPI_GATED_RESIDUAL = 2, EPI_QKV = 3 };
 
+// Arguments of the QKV epilogue only. They are read where they are used (the epilogue and the
+// parameter copy), through qkv_args(), so that they do not sit in scalar registers through the
+// MFMA loop (where they would be spilled).
+struct QkvArgs {
+  const uint16_t* norm_qk;   // [2][128] query then key RMS-norm weights
+  const float* rope_cos;     // [M, 64]
+  const float* rope_sin;     // [M, 64]
+  uint16_t* out_q;           // [heads, M, 128] each
+  uint16_t* out_k;
+  uint16_t* out_v;
+  float eps;
+  int heads;
+};
+
 struct Params {
   const uint8_t* A;          // q  [M, K]
   const uint8_t* B;          // qw [N, K]
@@ -92,16 +106,26 @@ struct Params {
   int splits;                // parts per left-over tile (1: not cut)
   int part_steps;            // nk / splits
   int narrow;                // 1: each left-over tile runs as two 256 x 128 halves (not cut)
-  // QKV epilogue only: N = 3 heads 128; out_q/k/v [heads, M, 128]
-  const uint16_t* norm_qk;   // [2][128] query then key RMS-norm weights
-  const float* rope_cos;     // [M, 64]
-  const float* rope_sin;     // [M, 64]
-  uint16_t* out_q;
-  uint16_t* out_k;
-  uint16_t* out_v;
-  float qk_eps;
-  int heads;
+  QkvArgs qkv;               // QKV epilogue only (N = 3 heads 128); read through qkv_args()
 };
+
+// The kernel's own copy of Params.qkv, read from the kernel argument segment at the point of
+// use: the empty asm hides where the pointer comes from, so the loads stay where they are.
+__device__ __forceinline__ QkvArgs qkv_args() {
+  typedef const __attribute__((address_space(4))) Params* KParams;
+  KParams kp = (KParams)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(kp));
+  QkvArgs a;
+  a.norm_qk = kp->qkv.norm_qk;
+  a.rope_cos = kp->qkv.rope_cos;
+  a.rope_sin = kp->qkv.rope_sin;
+  a.out_q = kp->qkv.out_q;
+  a.out_k = kp->qkv.out_k;
+  a.out_v = kp->qkv.out_v;
+  a.eps = kp->qkv.eps;
+  a.heads = kp->qkv.heads;
+  return a;
+}
 
 // ---------------------------------------------------------------------------------------------
 // memory helpers
@@ -347,7 +371,7 @@ __device__ __forceinline__ void copy_params(const Params& p, const TileDesc& d, 
   } else if (EPI == EPI_GATED_RESIDUAL) {
     copy_to_lds(buffer_rsrc(p.gate + n0, cols * 2u), lo, lp);
   } else if (EPI == EPI_QKV) {
-    copy_to_lds(buffer_rsrc(p.norm_qk, 512u), lo, lp);
+    copy_to_lds(buffer_rsrc(qkv_args().norm_qk, 512u), lo, lp);
   }
 }
 
@@ -512,11 +536,28 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[NB][4], const Params&
 // value channels pass through. Every output goes head-major, out[(head M + m) 128 + channel],
 // rounded once to bf16.
 // A wave's columns lie inside one head, but a head spans several waves (2 with NB = 2, 4 with
-// NB = 1) of both groups, which the caller has aligned. Each wave writes its per-row sums of
-// squares to `scratch` (4 KiB, [wn][256 rows]); after one workgroup barrier, which every wave
-// reaches, each adds its head's sums in wave order, so all waves of a head use the same bits.
+// NB = 1) of both groups, which the caller has aligned. A first pass turns the accumulators into
+// v in place and writes each row's sum of squares over the wave's columns to `scratch` (4 KiB,
+// [wn][256 rows]); after one workgroup barrier, which every wave reaches, each wave adds its
+// head's sums in wave order, so all waves of a head use the same bits, and finishes from v.
+// The rotary cosines and sines a lane needs for one unit (row block bm, column block bn): 4
+// pairs per gp, through a buffer descriptor whose range is empty for value columns (those loads
+// read zeros and touch no memory).
+__device__ __forceinline__ void rope_load(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                          int bm, int bn, int lane, int dw, v4i (&c)[2],
+                                          v4i (&sn)[2]) {
+  const uint32_t row_off = (uint32_t)(bm * 32 + (lane & 31)) * 256u;
+#pragma unroll
+  for (int gp = 0; gp < 2; ++gp) {
+    const uint32_t off =
+        row_off + (uint32_t)((dw + bn * 32 + (gp * 2 + (lane >> 5)) * 8) >> 1) * 4u;
+    c[gp] = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
+    sn[gp] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+  }
+}
+
 template <int NB>
-__device__ __forceinline__ void epilogue_qkv(const v16f (&acc)[NB][4], const Params& p, int m0,
+__device__ __forceinline__ void epilogue_qkv(v16f (&acc)[NB][4], const Params& p, int m0,
                                              int n0, int wm, int wn, int lane, const uint8_t* pb,
                                              float* scratch) {
   const float* s_sa = reinterpret_cast<const float*>(pb);
@@ -524,7 +565,8 @@ __device__ __forceinline__ void epilogue_qkv(const v16f (&acc)[NB][4], const Par
   const uint16_t* s_b = reinterpret_cast<const uint16_t*>(pb + 2048);
   const uint16_t* s_w = reinterpret_cast<const uint16_t*>(pb + 3072);
   const int hi = lane >> 5;
-  const int HD = p.heads * 128;
+  const QkvArgs qa = qkv_args();
+  const int HD = qa.heads * 128;
   const int nw = n0 + wn * 32 * NB;            // this wave's first column (uniform)
   const int region = nw / HD;                  // 0 query, 1 key, 2 value, 3: past N
   const int head = (nw - region * HD) >> 7;
@@ -545,21 +587,25 @@ __device__ __forceinline__ void epilogue_qkv(const v16f (&acc)[NB][4], const Par
       v[h][3] = fmaf(acc[bn][bm][g * 4 + 3] * sam, swv.w, bf16_hi(bb.y));
     }
   };
-  if (normed) {
+  // first pass: v into the accumulator registers, and the per-row sums of squares
 #pragma unroll
-    for (int bm = 0; bm < 4; ++bm) {
-      float ss = 0.0f;
+  for (int bm = 0; bm < 4; ++bm) {
+    float ss = 0.0f;
 #pragma unroll
-      for (int bn = 0; bn < NB; ++bn)
+    for (int bn = 0; bn < NB; ++bn)
 #pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
-          float v[2][4];
-          dequant(bm, bn, gp, v);
+      for (int gp = 0; gp < 2; ++gp) {
+        float v[2][4];
+        dequant(bm, bn, gp, v);
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ss = fmaf(v[h][j], v[h][j], ss);
-        }
+          for (int j = 0; j < 4; ++j) {
+            acc[bn][bm][(gp * 2 + h) * 4 + j] = v[h][j];
+            ss = fmaf(v[h][j], v[h][j], ss);
+          }
+      }
+    if (normed) {
       // lanes l and l + 32 hold the two halves of the row's columns: lower + upper in both
       float lo_s = ss, up_s = ss;
       swap_halves(lo_s, up_s);
@@ -567,12 +613,25 @@ __device__ __forceinline__ void epilogue_qkv(const v16f (&acc)[NB][4], const Par
       if (hi == 0) scratch[wn * 256 + wm * 128 + bm * 32 + lane] = row_ss;
     }
   }
+  // the rotary table rows of this wave's 128 rows (256 bytes each), through descriptors that
+  // end at row M (rows past it read zeros; they are computed, never stored); block 0's loads
+  // fly across the barrier, block bm + 1's while block bm is worked on
+  const int mw = m0 + wm * 128;
+  const int rows_w = p.M - mw < 128 ? (p.M - mw > 0 ? p.M - mw : 0) : 128;
+  const int tab_bytes = normed ? rows_w * 256 : 0;
+  const size_t tab0 = (size_t)(mw < p.M ? mw : 0) * 64;
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(qa.rope_cos + tab0), (short)0, tab_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsn = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(qa.rope_sin + tab0), (short)0, tab_bytes, 0x00020000);
+  // units (bm, bn) in order; each prefetches the next unit's tables
+  v4i cc[2], ss4[2];
+  rope_load(rc, rsn, 0, 0, lane, dw, cc, ss4);
   phase_barrier();  // every wave's sums are in LDS
 #pragma unroll
   for (int bm = 0; bm < 4; ++bm) {
     const int ml = wm * 128 + bm * 32 + (lane & 31);
     const int m = m0 + ml;
-    const int mc = m < p.M ? m : p.M - 1;  // rows past M are computed but not stored
     float rr = 1.0f;
     if (normed) {
       float t;
@@ -582,14 +641,20 @@ __device__ __forceinline__ void epilogue_qkv(const v16f (&acc)[NB][4], const Par
       } else {
         t = ((scratch[ml] + scratch[256 + ml]) + scratch[512 + ml]) + scratch[768 + ml];
       }
-      rr = 1.0f / __builtin_sqrtf(fmaf(t, 1.0f / 128.0f, p.qk_eps));
+      rr = 1.0f / __builtin_sqrtf(fmaf(t, 1.0f / 128.0f, qa.eps));
     }
 #pragma unroll
     for (int bn = 0; bn < NB; ++bn) {
+      const int nu = bm * NB + bn + 1;  // next unit
+      v4i cn[2], sn4[2];
+      if (nu < 4 * NB) rope_load(rc, rsn, nu / NB, nu % NB, lane, dw, cn, sn4);
 #pragma unroll
       for (int gp = 0; gp < 2; ++gp) {
         float v[2][4];
-        dequant(bm, bn, gp, v);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[h][j] = acc[bn][bm][(gp * 2 + h) * 4 + j];
 #pragma unroll
         for (int j = 0; j < 4; ++j) swap_halves(v[0][j], v[1][j]);
         const int d = dw + bn * 32 + (gp * 2 + hi) * 8;  // channel of y[0] inside the head
@@ -597,9 +662,11 @@ __device__ __forceinline__ void epilogue_qkv(const v16f (&acc)[NB][4], const Par
         if (normed) {
           const uint4 ww = *reinterpret_cast<const uint4*>(s_w + region * 128 + d);
           const uint32_t wv[4] = {ww.x, ww.y, ww.z, ww.w};
-          const float4 c = *reinterpret_cast<const float4*>(p.rope_cos + (size_t)mc * 64 + (d >> 1));
-          const float4 sn = *reinterpret_cast<const float4*>(p.rope_sin + (size_t)mc * 64 + (d >> 1));
-          const float cs[4] = {c.x, c.y, c.z, c.w}, sv[4] = {sn.x, sn.y, sn.z, sn.w};
+          const v4i c = cc[gp], sn = ss4[gp];
+          const float cs[4] = {__int_as_float(c[0]), __int_as_float(c[1]), __int_as_float(c[2]),
+                               __int_as_float(c[3])};
+          const float sv[4] = {__int_as_float(sn[0]), __int_as_float(sn[1]),
+                               __int_as_float(sn[2]), __int_as_float(sn[3])};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float a = (y[2 * j] * rr) * bf16_lo(wv[j]);
@@ -614,8 +681,15 @@ __device__ __forceinline__ void epilogue_qkv(const v16f (&acc)[NB][4], const Par
         o.z = pack_bf16(y[4], y[5]);
         o.w = pack_bf16(y[6], y[7]);
         if (m < p.M && region < 3) {
-          uint16_t* out = region == 0 ? p.out_q : region == 1 ? p.out_k : p.out_v;
+          uint16_t* out = region == 0 ? qa.out_q : region == 1 ? qa.out_k : qa.out_v;
           *reinterpret_cast<uint4*>(out + ((size_t)head * (size_t)p.M + (size_t)m) * 128 + d) = o;
+        }
+      }
+      if (nu < 4 * NB) {
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+          cc[gp] = cn[gp];
+          ss4[gp] = sn4[gp];
         }
       }
     }
@@ -1019,14 +1093,14 @@ hipError_t launch_linear_qkv(const uint8_t* q, const float* scale, int64_t M, in
   p.sa = scale;
   p.sw = w_scale;
   p.bias = bias;
-  p.norm_qk = norm_qk;
-  p.rope_cos = rope_cos;
-  p.rope_sin = rope_sin;
-  p.out_q = out_q;
-  p.out_k = out_k;
-  p.out_v = out_v;
-  p.qk_eps = eps;
-  p.heads = (int)heads;
+  p.qkv.norm_qk = norm_qk;
+  p.qkv.rope_cos = rope_cos;
+  p.qkv.rope_sin = rope_sin;
+  p.qkv.out_q = out_q;
+  p.qkv.out_k = out_k;
+  p.qkv.out_v = out_v;
+  p.qkv.eps = eps;
+  p.qkv.heads = (int)heads;
   return schedule_and_launch(p, M, K, 3 * heads * 128, EPI_QKV, workspace, stream);
 }
 
