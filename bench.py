@@ -36,6 +36,7 @@ KERNEL_SOURCES = {
     "gemm": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "gemm_fp8.hip"),
     "quantize": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "quantize.hip"),
     "ln_modulate": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "quantize.hip"),
+    "qkv": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "gemm_fp8.hip"),
 }
 
 
@@ -503,6 +504,7 @@ def main():
             "peak": PEAK_FP8_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+            "traffic": stored_traffic("qkv", w.name),
             "avg_launch_us": round(qk["fused_us"], 2),
             "algorithmic_flop_per_launch": qk["flops"],
             "bias_epilogue_us": round(qk["plain_us"], 2),
