@@ -10,6 +10,7 @@ stream. Every step of the computation runs in the HIP kernels of libdq; there is
     out = dq_linear_fp8(q, scale, qw, w_scale, bias, "gelu_tanh")
     q, scale, y = dq_layernorm_modulate_quantize_fp8(h, mod_scale, mod_shift)  # LN + modulate
     oq, ok, ov = dq_linear_qkv_fp8(q, scale, qw, w_scale, heads, bias, norm_qk, cos, sin)
+    o = dq_attention_fp8(*quantize_qkv_heads_fp8(oq, ok, ov))     # [S, heads, 128]
 
 dq_linear_fp8 takes a workspace that lets workgroups share tiles (see include/dq.h). By default
 the binding keeps one zero-filled workspace per (device, stream) and grows it when a larger
@@ -64,6 +65,10 @@ def lib() -> ctypes.CDLL:
         L.dq_linear_qkv_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, vp,
                                         ctypes.c_float, vp, vp, vp, vp, ctypes.c_uint64, vp]
         L.dq_linear_qkv_fp8.restype = i32
+        L.dq_quantize_v_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.dq_quantize_v_fp8.restype = i32
+        L.dq_attention_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp]
+        L.dq_attention_fp8.restype = i32
         L.dq_linear_fp8_workspace_size.argtypes = [i64, i64, i64]
         L.dq_linear_fp8_workspace_size.restype = ctypes.c_uint64
         L.dq_status_string.argtypes = [i32]
@@ -293,6 +298,58 @@ def dq_linear_qkv_fp8(q, scale, qw, w_scale, heads, bias, norm_qk, rope_cos, rop
     return tuple(out)
 
 
+def dq_quantize_v_fp8(v, vt=None, v_scale=None, stream=None):
+    """Per-(head, token) FP8 quantization of values bf16 [H, S, 128], codes written transposed:
+    returns (vt uint8 [H, 128, S], v_scale float32 [H, S]). S must be a multiple of 16."""
+    where = "dq_quantize_v_fp8"
+    if not isinstance(v, torch.Tensor) or v.dim() != 3 or v.device.type != "cuda":
+        raise ValueError(f"{where}: values must be a 3-D tensor on a GPU")
+    H, S, D = v.shape
+    dev = v.device
+    _need(v, "v", torch.bfloat16, (H, S, HEAD_DIM), dev)
+    vt = torch.empty((H, HEAD_DIM, S), dtype=torch.uint8, device=dev) if vt is None else vt
+    v_scale = torch.empty((H, S), dtype=torch.float32, device=dev) if v_scale is None else v_scale
+    _need(vt, "vt", torch.uint8, (H, HEAD_DIM, S), dev)
+    _need(v_scale, "v_scale", torch.float32, (H, S), dev)
+    with torch.cuda.device(dev):
+        _check(lib().dq_quantize_v_fp8(_ptr(v), H, S, _ptr(vt), _ptr(v_scale),
+                                       _stream(stream, dev)), where)
+    return vt, v_scale
+
+
+def quantize_qkv_heads_fp8(q, k, v, stream=None):
+    """Codes and scales of head-major bf16 q, k, v [H, S, 128] for dq_attention_fp8:
+    (q8, q_scale, k8, k_scale, vt8, v_scale)."""
+    H, S, _ = q.shape
+    q8, sq = dq_quantize_fp8(q.reshape(H * S, HEAD_DIM), stream=stream)
+    k8, sk = dq_quantize_fp8(k.reshape(H * S, HEAD_DIM), stream=stream)
+    vt, sv = dq_quantize_v_fp8(v, stream=stream)
+    return (q8.view(H, S, HEAD_DIM), sq.view(H, S), k8.view(H, S, HEAD_DIM), sk.view(H, S), vt,
+            sv)
+
+
+def dq_attention_fp8(q8, q_scale, k8, k_scale, vt8, v_scale, out=None, stream=None):
+    """Attention over FP8 queries, keys, values (codes [H, S, 128], values transposed
+    [H, 128, S], scales [H, S]) -> bf16 [S, H, 128]."""
+    where = "dq_attention_fp8"
+    if not isinstance(q8, torch.Tensor) or q8.dim() != 3 or q8.device.type != "cuda":
+        raise ValueError(f"{where}: query codes must be a 3-D tensor on a GPU")
+    H, S, _ = q8.shape
+    dev = q8.device
+    _need(q8, "q", torch.uint8, (H, S, HEAD_DIM), dev)
+    _need(k8, "k", torch.uint8, (H, S, HEAD_DIM), dev)
+    _need(vt8, "vt", torch.uint8, (H, HEAD_DIM, S), dev)
+    for t, name in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _need(t, name, torch.float32, (H, S), dev)
+    out = torch.empty((S, H, HEAD_DIM), dtype=torch.bfloat16, device=dev) if out is None else out
+    _need(out, "out", torch.bfloat16, (S, H, HEAD_DIM), dev)
+    with torch.cuda.device(dev):
+        _check(lib().dq_attention_fp8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(vt8),
+                                      _ptr(v_scale), H, S, _ptr(out), _stream(stream, dev)), where)
+    return out
+
+
 __all__ = ["dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
            "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8", "HEAD_DIM",
+           "dq_quantize_v_fp8", "dq_attention_fp8", "quantize_qkv_heads_fp8",
            "dq_linear_fp8_workspace_size", "DQError", "EPILOGUES", "lib", "LIB_PATH"]

@@ -202,6 +202,52 @@ int dq_linear_qkv_fp8(const void* q, const float* scale, int64_t M, int64_t K, c
       static_cast<uint16_t*>(out_v), workspace, static_cast<hipStream_t>(stream)));
 }
 
+// Sizes of the attention entry points: 1 <= S < 2^24 with S % 16 == 0 (or an empty problem),
+// 0 <= H < 65536, H S 128 < 2^47.
+static int check_attention_shape(int64_t H, int64_t S) {
+  if (H < 0 || H >= 65536 || S < 0 || S >= (int64_t(1) << 24) || (S % 16) != 0) return DQ_ERR_SHAPE;
+  if (H > 0 && S > kMaxElems / (H * dq::kHeadDim)) return DQ_ERR_SHAPE;
+  return DQ_OK;
+}
+
+int dq_quantize_v_fp8(const void* v, int64_t H, int64_t S, void* vt, float* v_scale,
+                      void* stream) {
+  const int shape = check_attention_shape(H, S);
+  if (shape != DQ_OK) return shape;
+  if (H == 0 || S == 0) return DQ_OK;
+  if (!v || !vt || !v_scale) return DQ_ERR_NULL;
+  if (!aligned16(v) || !aligned16(vt) || !aligned16(v_scale)) return DQ_ERR_ALIGN;
+  const uint64_t n = static_cast<uint64_t>(H) * static_cast<uint64_t>(S) * dq::kHeadDim;
+  const uint64_t sb = 4 * static_cast<uint64_t>(H) * static_cast<uint64_t>(S);
+  if (overlap(vt, n, v, 2 * n) || overlap(v_scale, sb, v, 2 * n) || overlap(vt, n, v_scale, sb))
+    return DQ_ERR_ALIAS;
+  return hip_status(dq::launch_quantize_v(static_cast<const uint16_t*>(v), H, S,
+                                          static_cast<uint8_t*>(vt), v_scale,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int dq_attention_fp8(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                     const void* vt, const float* v_scale, int64_t H, int64_t S, void* out,
+                     void* stream) {
+  const int shape = check_attention_shape(H, S);
+  if (shape != DQ_OK) return shape;
+  if (H == 0 || S == 0) return DQ_OK;
+  if (!q || !q_scale || !k || !k_scale || !vt || !v_scale || !out) return DQ_ERR_NULL;
+  if (!aligned16(q) || !aligned16(q_scale) || !aligned16(k) || !aligned16(k_scale) ||
+      !aligned16(vt) || !aligned16(v_scale) || !aligned16(out))
+    return DQ_ERR_ALIGN;
+  const uint64_t n = static_cast<uint64_t>(H) * static_cast<uint64_t>(S) * dq::kHeadDim;
+  const uint64_t sb = 4 * static_cast<uint64_t>(H) * static_cast<uint64_t>(S);
+  const void* ins[6] = {q, q_scale, k, k_scale, vt, v_scale};
+  const uint64_t in_bytes[6] = {n, sb, n, sb, n, sb};
+  for (int i = 0; i < 6; ++i)
+    if (overlap(out, 2 * n, ins[i], in_bytes[i])) return DQ_ERR_ALIAS;
+  return hip_status(dq::launch_attention(
+      static_cast<const uint8_t*>(q), q_scale, static_cast<const uint8_t*>(k), k_scale,
+      static_cast<const uint8_t*>(vt), v_scale, H, S, static_cast<uint16_t*>(out),
+      static_cast<hipStream_t>(stream)));
+}
+
 uint64_t dq_linear_fp8_workspace_size(int64_t M, int64_t K, int64_t N) {
   if (check_linear_shape(M, K, N) != DQ_OK) return 0;
   return dq::linear_workspace_bytes(M, K, N);
@@ -224,6 +270,6 @@ const char* dq_status_string(int status) {
 
 int dq_last_hip_error(void) { return g_last_hip_error; }
 
-int dq_abi_version(void) { return 4; }
+int dq_abi_version(void) { return 5; }
 
 }  // extern "C"

@@ -174,6 +174,46 @@ int dq_linear_qkv_fp8(const void* q, const float* scale, int64_t M, int64_t K, c
                       void* stream);
 
 /*
+ * dq_quantize_v_fp8 -- per-(head, token) FP8 quantization of attention values, codes written
+ * transposed for dq_attention_fp8.
+ *
+ *   v        bf16 [H, S, 128]   values, one row of 128 channels per (head, token)
+ *   vt       uint8 [H, 128, S]  E4M3 codes, keys contiguous per channel
+ *   v_scale  float [H, S]       per-row scales
+ *   Codes and scales of each row are exactly those of dq_quantize_fp8 on that row.
+ * Queries and keys need no special form: dq_quantize_fp8 on the [H * S, 128] view gives their
+ * codes [H, S, 128] and scales [H, S].
+ * Requirements: 0 <= H < 65536, 0 <= S < 2^24 with S % 16 == 0, pointers 16-byte aligned, no
+ * overlap. Inputs must be finite.
+ */
+int dq_quantize_v_fp8(const void* v, int64_t H, int64_t S, void* vt, float* v_scale,
+                      void* stream);
+
+/*
+ * dq_attention_fp8 -- attention over FP8 queries, keys and values, one head at a time:
+ *
+ *   t[i, j] = (dec(q_i) q_scale_i) . (dec(k_j) k_scale_j) / sqrt(128)
+ *   o_i     = sum_j softmax_j(t[i, :]) v_scale_j dec(v_j)          (no mask: every token sees all)
+ *
+ * The pages treat FP8 attention as the next lever after the quantized GEMMs (page "Accelerarea
+ * generarii de imagini cu FLUX 3 Image Klein pe GPU-urile Blackwell NVIDIA": attention is about
+ * 60 % of the DiT's time at 2048 x 2048; page "Optimizacion de la inferencia de FLUX 3 Image
+ * Klein en GPUs NVIDIA Blackwell", section "Como funciona": query, key and value in FP8). They do
+ * not write it out; the reading taken quantizes each (head, token) row as the linear layer's
+ * activations, multiplies queries by keys on the FP8 matrix units (fp32 accumulation), keeps the
+ * softmax in fp32 (base 2, online over blocks of keys) and rounds each weight times its value
+ * scale to bf16 for a bf16 matrix product with the decoded values (exact in bf16).
+ *
+ *   q, k      uint8 [H, S, 128]  codes;  q_scale, k_scale  float [H, S]
+ *   vt        uint8 [H, 128, S]  codes (from dq_quantize_v_fp8);  v_scale  float [H, S]
+ *   out       bf16 [S, H, 128]   token-major (row s holds the H heads' outputs in order)
+ * Requirements: as dq_quantize_v_fp8; out overlapping no input.
+ */
+int dq_attention_fp8(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                     const void* vt, const float* v_scale, int64_t H, int64_t S, void* out,
+                     void* stream);
+
+/*
  * dq_linear_fp8_workspace_size -- bytes of workspace dq_linear_fp8 uses for an M x K -> N
  * problem (the same on every device), or 0 if the sizes break dq_linear_fp8's requirements:
  * 256 MiB (1024 partial 256 x 256 fp32 tiles) plus 4 bytes per 256 x 256 output tile, rounded up
@@ -221,7 +261,7 @@ const char* dq_status_string(int status);
 /* The hipError_t behind the most recent DQ_ERR_HIP returned on the calling thread (0 if none). */
 int dq_last_hip_error(void);
 
-/* ABI version of this header (currently 4). */
+/* ABI version of this header (currently 5). */
 int dq_abi_version(void);
 
 #ifdef __cplusplus

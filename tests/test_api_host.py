@@ -30,6 +30,8 @@ def lib():
                                                      vp, vp, vp]
     L.dq_linear_qkv_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, vp, ctypes.c_float,
                                     vp, vp, vp, vp, ctypes.c_uint64, vp]
+    L.dq_quantize_v_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.dq_attention_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp]
     L.dq_linear_fp8_workspace_size.argtypes = [i64, i64, i64]
     L.dq_linear_fp8_workspace_size.restype = ctypes.c_uint64
     L.dq_status_string.restype = ctypes.c_char_p
@@ -46,7 +48,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
               "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8",
-              "dq_linear_fp8_workspace_size", "dq_status_string", "dq_last_hip_error",
+              "dq_quantize_v_fp8", "dq_attention_fp8", "dq_linear_fp8_workspace_size", "dq_status_string", "dq_last_hip_error",
               "dq_abi_version"):
         assert n in names
 
@@ -57,7 +59,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dq_abi_version() == 4
+    assert lib.dq_abi_version() == 5
     for st in range(9):
         s = lib.dq_status_string(st)
         assert s and len(s) > 1
@@ -224,6 +226,50 @@ def test_linear_qkv_workspace_checks(lib):
     assert lib.dq_last_hip_error() == 0
 
 
+AQ, ASQ, AK, ASK, AV, ASV, AO = (0x20000000 * i for i in range(20, 27))   # fake, far apart
+
+
+def attn(lib, H=2, S=64, q=AQ, sq=ASQ, k=AK, sk=ASK, vt=AV, sv=ASV, out=AO):
+    return lib.dq_attention_fp8(q, sq, k, sk, vt, sv, H, S, out, None)
+
+
+def test_attention_argument_checks(lib):
+    assert attn(lib, S=0) == OK
+    assert attn(lib, H=0, q=None) == OK                      # empty: pointers are not checked
+    assert attn(lib, S=24) == SHAPE                          # S % 16
+    assert attn(lib, S=-16) == SHAPE
+    assert attn(lib, H=-1) == SHAPE
+    assert attn(lib, H=65536) == SHAPE
+    assert attn(lib, S=1 << 24) == SHAPE
+    assert attn(lib, S=0, H=3) == OK
+    for name in ("q", "sq", "k", "sk", "vt", "sv", "out"):
+        assert attn(lib, **{name: None}) == NULL, name
+    base = dict(q=AQ, sq=ASQ, k=AK, sk=ASK, vt=AV, sv=ASV, out=AO)
+    for name, val in base.items():
+        assert attn(lib, **{name: val + 4}) == ALIGN, name
+    # out is S H 128 bf16 = 32 KiB here
+    assert attn(lib, out=AQ) == ALIAS
+    assert attn(lib, out=ASV - 1024) == ALIAS
+    assert attn(lib, out=AV + 16) == ALIAS
+    assert attn(lib, out=AQ + 2 * 64 * 128, sq=None) == NULL        # right after q: no alias
+
+
+def test_quantize_v_argument_checks(lib):
+    f = lib.dq_quantize_v_fp8
+    V, VT, SV = 0x30000000, 0x40000000, 0x50000000
+    assert f(V, 0, 64, VT, SV, None) == OK
+    assert f(V, 2, 0, VT, SV, None) == OK
+    assert f(V, 2, 40, VT, SV, None) == SHAPE                # S % 16
+    assert f(None, 2, 64, VT, SV, None) == NULL
+    assert f(V, 2, 64, None, SV, None) == NULL
+    assert f(V, 2, 64, VT, None, None) == NULL
+    assert f(V + 2, 2, 64, VT, SV, None) == ALIGN
+    assert f(V, 2, 64, VT + 8, SV, None) == ALIGN
+    assert f(V, 2, 64, V + 1024, SV, None) == ALIAS          # codes inside v
+    assert f(V, 2, 64, VT, VT + 256, None) == ALIAS          # scales inside codes
+    assert lib.dq_last_hip_error() == 0
+
+
 def test_workspace_size(lib):
     size = lib.dq_linear_fp8_workspace_size
     # a fixed region of 1024 partial 256 x 256 fp32 tiles, then one 4-byte counter per
@@ -258,9 +304,9 @@ def test_python_binding_names_match_the_c_entry_points():
     import fp8_dynamic_quant_amd as dq
     for name in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
                  "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8",
-                 "dq_linear_fp8_workspace_size"):
+                 "dq_quantize_v_fp8", "dq_attention_fp8", "dq_linear_fp8_workspace_size"):
         assert callable(getattr(dq, name))
-    assert dq.lib().dq_abi_version() == 4
+    assert dq.lib().dq_abi_version() == 5
     assert dq.dq_linear_fp8_workspace_size(4608, 3072, 12288) == 3584 + 1024 * 262144
 
 
