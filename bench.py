@@ -266,6 +266,47 @@ def bench_qkv(steps, warmup, n_sets, M=4096, K=3072, heads=24, seed=3200):
             "shape": [M, K, N], "heads": heads}
 
 
+def bench_attention(steps, warmup, n_sets, H=24, S=4608, seed=11):
+    """Joint text + image attention of a FLUX block at 1024^2 (24 heads, 4608 tokens): the FP8
+    attention kernel (codes already quantized), the quantization of q, k and v, and, for
+    context, torch's bf16 scaled_dot_product_attention on the same bf16 inputs."""
+    import torch
+    import torch.nn.functional as F
+    import fp8_dynamic_quant_amd as dq
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    sets = []
+    for _ in range(n_sets):
+        q, k, v = (torch.randn((H, S, 128), generator=gen, device=dev).to(torch.bfloat16)
+                   for _ in range(3))
+        sets.append({"bf": (q, k, v), "fp8": dq.quantize_qkv_heads_fp8(q, k, v),
+                     "out": torch.empty((S, H, 128), dtype=torch.bfloat16, device=dev)})
+    torch.cuda.synchronize()
+
+    def timed(fn, n):
+        for i in range(warmup):
+            fn(sets[i % n_sets])
+        torch.cuda.synchronize()
+        evs = []
+        for i in range(n):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn(sets[i % n_sets])
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+
+    attn = timed(lambda st: dq.dq_attention_fp8(*st["fp8"], out=st["out"]), steps)
+    quant = timed(lambda st: dq.quantize_qkv_heads_fp8(*st["bf"]), steps)
+    sdpa = timed(lambda st: F.scaled_dot_product_attention(*(t[None] for t in st["bf"])), steps)
+    return {"attn_us": attn, "quant_us": quant, "sdpa_us": sdpa, "flops": 4 * H * S * S * 128,
+            "H": H, "S": S}
+
+
 def bench_dit_step(steps, warmup):
     """All linears of one 1024^2 FLUX-dev denoising step (228 quantize + GEMM pairs), distinct
     weights per block, timed end to end as one sequence on one stream."""
@@ -382,6 +423,7 @@ def main():
     ap.add_argument("--no-dit", action="store_true")
     ap.add_argument("--no-modulate", action="store_true")
     ap.add_argument("--no-qkv", action="store_true")
+    ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB plain copy first (reference for HBM counters)")
@@ -509,6 +551,28 @@ def main():
             "algorithmic_flop_per_launch": qk["flops"],
             "bias_epilogue_us": round(qk["plain_us"], 2),
             "unfused_torch_us": round(qk["unfused_us"], 2),
+        }
+    if not args.no_attention:
+        at = bench_attention(args.steps, min(args.warmup, 50), 3)
+        tf = at["flops"] / at["attn_us"] / 1e6
+        # half the work on the FP8 matrix units (5.0 PF), half on bf16 (2.5 PF)
+        mixed_peak = 4.0 / (2.0 / PEAK_FP8_TFLOPS + 2.0 / (PEAK_FP8_TFLOPS / 2))
+        log(f"FP8 attention H={at['H']} S={at['S']}: {at['attn_us']:.1f} us ({tf:.0f} TFLOP/s); "
+            f"q/k/v quantization {at['quant_us']:.1f} us; torch bf16 SDPA {at['sdpa_us']:.1f} us")
+        res["attention"] = {
+            "kernel": "attn_fp8",
+            "timing": "HIP events around each call, rotating inputs",
+            "shape": {"heads": at["H"], "tokens": at["S"], "head_dim": 128},
+            "bound": "mfma",
+            "achieved": round(tf, 1),
+            "peak": round(mixed_peak, 1),
+            "peak_note": "q k^T on FP8 (5.0 PF), p v on bf16 (2.5 PF): 4 / (2/5.0 + 2/2.5) PF",
+            "unit": "TFLOP/s",
+            "frac": round(tf / mixed_peak, 4),
+            "avg_launch_us": round(at["attn_us"], 2),
+            "algorithmic_flop_per_launch": at["flops"],
+            "qkv_quantization_us": round(at["quant_us"], 2),
+            "torch_bf16_sdpa_us": round(at["sdpa_us"], 2),
         }
     if not args.no_dit:
         log("DiT step: generating 228 distinct FP8 weights on the device")

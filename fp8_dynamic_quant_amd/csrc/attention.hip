@@ -25,8 +25,9 @@
 //   1. logits: 2 x 2 FP8 matrix ops (32 keys x 32 queries x 64 channels each, keys as the
 //      first operand), so lane l holds query l & 31 and keys 8 g + 4 (l >> 5) + j;
 //   2. online softmax in base 2: t = s sk_j (sq_i log2(e) / sqrt(128)); the row max takes the
-//      lane and its partner l ^ 32; the running output and sum are rescaled by 2^(m - m');
-//      p = 2^(t - m'); keys past S are masked;
+//      lane and its partner l ^ 32; the running max m (and with it the output and the sum,
+//      rescaled by 2^(m - m')) moves only when a block's max exceeds it by more than 8, so the
+//      rescale is rare after the first blocks; p = 2^(t - m) <= 2^8; keys past S are masked;
 //   3. P V: p sv_j rounded to bf16 becomes the second operand of 16 bf16 matrix ops (32
 //      channels x 32 queries x 16 keys) after one half swap between partner lanes (the
 //      logits' layout holds keys 0-3 and 8-11 of a 16-key chunk in the lower lane, 4-7 and 12-15
@@ -184,14 +185,14 @@ __device__ __forceinline__ void load_values(const AttnArgs& a, int h, int kb, in
                               : make_uint4(0u, 0u, 0u, 0u);
 }
 
-// 8 codes (two dwords) -> 8 bf16 (exact).
+// 8 codes (two dwords) -> 8 bf16: gfx950's scaled conversion, two codes per instruction, at
+// scale 1 (exact; checked on the hardware for every code and both halves of a dword).
+template <bool kHi>
+__device__ __forceinline__ uint32_t decode2(uint32_t d) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, kHi));
+}
 __device__ __forceinline__ uint4 decode8(uint32_t d0, uint32_t d1) {
-  const f2v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)d0, false);
-  const f2v b = __builtin_amdgcn_cvt_pk_f32_fp8((int)d0, true);
-  const f2v c = __builtin_amdgcn_cvt_pk_f32_fp8((int)d1, false);
-  const f2v d = __builtin_amdgcn_cvt_pk_f32_fp8((int)d1, true);
-  return make_uint4(pack_bf16(a.x, a.y), pack_bf16(b.x, b.y), pack_bf16(c.x, c.y),
-                    pack_bf16(d.x, d.y));
+  return make_uint4(decode2<false>(d0), decode2<true>(d0), decode2<false>(d1), decode2<true>(d1));
 }
 
 // The decoded values into an LDS stage, [channel][key] bf16, 128-byte rows, swizzled.
@@ -209,7 +210,9 @@ __device__ __forceinline__ void store_values(uint8_t* stage, int tid, const uint
   }
 }
 
-__global__ void __launch_bounds__(256) attn_fp8(AttnArgs a) {
+// Two waves per SIMD: without the bound the compiler spends 280 registers (one wave per SIMD);
+// asking for three spills to scratch and measured slower.
+__global__ void __launch_bounds__(256, 2) attn_fp8(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t sK[2][kKB * kD];      // 2 x 8 KiB codes
   __shared__ __attribute__((aligned(1024))) uint8_t sV[2][kD * kKB * 2];  // 2 x 16 KiB bf16
   __shared__ __attribute__((aligned(16))) float sSK[2][kKB];
@@ -277,9 +280,11 @@ __global__ void __launch_bounds__(256) attn_fp8(AttnArgs a) {
                                                                 0);
       }
     }
-    // 2. softmax in base 2
-    float t[2][16];
-    float mx = -__builtin_inff();
+    // 2. softmax in base 2: u = s sk, t = u sqc (sqc >= 0, so max t = sqc max u); the running
+    //    max m moves only when a block's max exceeds it by more than 8 (weights stay <= 2^8,
+    //    harmless in fp32 and bf16), and the rescale runs only when some lane of the wave moved
+    v16f (&u)[2] = s;  // u = s sk, in place
+    float mxu = -__builtin_inff();
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -287,29 +292,38 @@ __global__ void __launch_bounds__(256) attn_fp8(AttnArgs a) {
         const float4 sk4 = *reinterpret_cast<const float4*>(&sSK[st][32 * kh + 8 * g + 4 * hi]);
         const float skv[4] = {sk4.x, sk4.y, sk4.z, sk4.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          t[kh][4 * g + j] = (s[kh][4 * g + j] * skv[j]) * sqc;
-          mx = fmaxf(mx, t[kh][4 * g + j]);
-        }
+        for (int j = 0; j < 4; ++j) u[kh][4 * g + j] *= skv[j];
       }
-    if ((kb + 1) * kKB > S) {  // the last block: keys past S take no weight
-      mx = -__builtin_inff();
+    const bool tail = (kb + 1) * kKB > S;  // the last block: keys past S take no weight
+    if (tail) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = kb * kKB + 32 * kh + 8 * (v >> 2) + 4 * hi + (v & 3);
-          if (key >= S) t[kh][v] = -__builtin_inff();
-          mx = fmaxf(mx, t[kh][v]);
+          if (key < S) mxu = fmaxf(mxu, u[kh][v]);
         }
+    } else {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mxu = fmaxf(mxu, u[kh][v]);
     }
     {
-      float a0 = mx, b0 = mx;
+      float a0 = mxu, b0 = mxu;
       swap_halves(a0, b0);
-      mx = fmaxf(a0, b0);
+      mxu = fmaxf(a0, b0);
     }
-    const float mn = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    const float mx = mxu * sqc;
+    const bool move = mx > m + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+      const float mn = move ? mx : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] *= alpha;
+      m = mn;
+    }
     float ps = 0.0f;
     uint32_t pk[2][4][2];  // bf16 pairs of p sv: [kh][g][j pair]
 #pragma unroll
@@ -321,7 +335,8 @@ __global__ void __launch_bounds__(256) attn_fp8(AttnArgs a) {
         float p[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(t[kh][4 * g + j] - mn);
+          p[j] = __builtin_amdgcn_exp2f(fmaf(u[kh][4 * g + j], sqc, -m));
+          if (tail && kb * kKB + 32 * kh + 8 * g + 4 * hi + j >= S) p[j] = 0.0f;
           ps += p[j];
         }
         pk[kh][g][0] = pack_bf16(p[0] * svv[0], p[1] * svv[1]);
@@ -332,10 +347,7 @@ __global__ void __launch_bounds__(256) attn_fp8(AttnArgs a) {
       swap_halves(a0, b0);
       ps = a0 + b0;
     }
-    lsum = fmaf(lsum, alpha, ps);
-    m = mn;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] *= alpha;
+    lsum += ps;
     // 3. P V
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
