@@ -37,6 +37,7 @@ KERNEL_SOURCES = {
     "quantize": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "quantize.hip"),
     "ln_modulate": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "quantize.hip"),
     "qkv": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "gemm_fp8.hip"),
+    "attention": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "attention.hip"),
 }
 
 
@@ -569,6 +570,7 @@ def main():
             "peak_note": "q k^T on FP8 (5.0 PF), p v on bf16 (2.5 PF): 4 / (2/5.0 + 2/2.5) PF",
             "unit": "TFLOP/s",
             "frac": round(tf / mixed_peak, 4),
+            "traffic": stored_traffic("attention", w.name),
             "avg_launch_us": round(at["attn_us"], 2),
             "algorithmic_flop_per_launch": at["flops"],
             "qkv_quantization_us": round(at["quant_us"], 2),

@@ -329,6 +329,43 @@ __global__ void __launch_bounds__(256) ln_mod_quant_rows(
   }
 }
 
+// Rows of at most 128 values (16 chunks): four rows per wave, one 16-lane DPP row each (lane
+// l & 15 holds chunk l & 15 of row 4 (wave index) + (l >> 4)), so no lane idles. The scale and
+// the codes are exactly quant_rows_reg's.
+__global__ void __launch_bounds__(256) quant_rows_small(const uint16_t* __restrict__ x, int R,
+                                                        int K, uint8_t* __restrict__ q,
+                                                        float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int row = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+  const int c = lane & 15, C = K >> 3;
+  const bool live = row < R && c < C;
+  const uint4 v = live ? reinterpret_cast<const uint4*>(x + (size_t)row * (size_t)K)[c]
+                       : make_uint4(0u, 0u, 0u, 0u);
+  uint32_t mx = absmax4(0u, v);
+  uint32_t m = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
+  m = umax(m, (uint32_t)dpp<0xB1>((int)m));
+  m = umax(m, (uint32_t)dpp<0x4E>((int)m));
+  m = umax(m, (uint32_t)dpp<0x141>((int)m));
+  m = umax(m, (uint32_t)dpp<0x140>((int)m));
+  if (row >= R) return;
+  const float amax = __uint_as_float(m << 16);
+  const float s = amax / kE4M3Max;
+  if (c == 0) scale[row] = s;
+  if (c >= C) return;
+  uint2 code;
+  if (m == 0) {
+    code = signs8(v);
+  } else if (s < kFltMinNormal) {
+    code = encode8<1, false>(v, s, 0.0f);
+  } else if (amax < kTinyAmax) {
+    const float ss = s * 0x1p64f;
+    code = encode8<0, true>(v, ss, 1.0f / ss);
+  } else {
+    code = encode8<0, false>(v, s, 1.0f / s);
+  }
+  reinterpret_cast<uint2*>(q + (size_t)row * (size_t)K)[c] = code;
+}
+
 template <int NCH>
 hipError_t launch_lnmq(const uint16_t* x, int R, int K, const uint16_t* ms, const uint16_t* mt,
                        float eps, uint16_t* y, uint8_t* q, float* scale, hipStream_t st) {
@@ -354,6 +391,11 @@ hipError_t launch_quantize_rows(const uint16_t* x, int64_t R, int64_t K, uint8_t
   if (R == 0) return hipSuccess;
   const int r = (int)R, k = (int)K;
   const int64_t nch = (K / 8 + 63) / 64;  // 16-byte chunks per lane
+  if (K <= 128) {  // four rows per wave
+    hipLaunchKernelGGL(quant_rows_small, dim3((unsigned)((R + 15) / 16)), dim3(256), 0, stream, x, r,
+                       k, q, scale);
+    return hipGetLastError();
+  }
   if (nch <= 1) return launch_reg<1>(x, r, k, q, scale, stream);
   if (nch <= 2) return launch_reg<2>(x, r, k, q, scale, stream);
   if (nch <= 3) return launch_reg<3>(x, r, k, q, scale, stream);
