@@ -37,6 +37,8 @@
 #include "dq_internal.h"
 #include "e4m3_codec.h"
 
+#include <type_traits>
+
 namespace dq {
 namespace {
 
@@ -250,7 +252,10 @@ __global__ void __launch_bounds__(256, 2) attn_fp8(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = (v16f){};
 
-  for (int kb = 0; kb < nblk; ++kb) {
+  // One key block; kTail marks the last block when S is not a multiple of 64 (the only one whose
+  // keys past S must take no weight), a separate instance so that full blocks carry no masking.
+  auto step = [&](const int kb, auto tail_tag) {
+    constexpr bool tail = decltype(tail_tag)::value;
     const int st = kb & 1;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's key copies of block kb
     __syncthreads();                     // every wave's copies and stores of block kb
@@ -294,8 +299,7 @@ __global__ void __launch_bounds__(256, 2) attn_fp8(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) u[kh][4 * g + j] *= skv[j];
       }
-    const bool tail = (kb + 1) * kKB > S;  // the last block: keys past S take no weight
-    if (tail) {
+    if constexpr (tail) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -336,7 +340,8 @@ __global__ void __launch_bounds__(256, 2) attn_fp8(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           p[j] = __builtin_amdgcn_exp2f(fmaf(u[kh][4 * g + j], sqc, -m));
-          if (tail && kb * kKB + 32 * kh + 8 * g + 4 * hi + j >= S) p[j] = 0.0f;
+          if constexpr (tail)
+            if (kb * kKB + 32 * kh + 8 * g + 4 * hi + j >= S) p[j] = 0.0f;
           ps += p[j];
         }
         pk[kh][g][0] = pack_bf16(p[0] * svv[0], p[1] * svv[1]);
@@ -369,7 +374,10 @@ __global__ void __launch_bounds__(256, 2) attn_fp8(AttnArgs a) {
       if (tid < kKB) sSK[st ^ 1][tid] = scn;
       else if (tid < 2 * kKB) sSV[st ^ 1][tid - kKB] = scn;
     }
-  }
+  };
+  const int nfull = S / kKB;
+  for (int kb = 0; kb < nfull; ++kb) step(kb, std::false_type{});
+  if (nfull < nblk) step(nfull, std::true_type{});
 
   // o / sum, [channel][query] -> out[query][h][channel]
   const float inv = 1.0f / lsum;
