@@ -67,8 +67,11 @@ def lib() -> ctypes.CDLL:
         L.dq_linear_qkv_fp8.restype = i32
         L.dq_quantize_v_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
         L.dq_quantize_v_fp8.restype = i32
-        L.dq_attention_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp]
+        L.dq_attention_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp,
+                                       ctypes.c_uint64, i64, vp]
         L.dq_attention_fp8.restype = i32
+        L.dq_attention_fp8_workspace_size.argtypes = [i64, i64]
+        L.dq_attention_fp8_workspace_size.restype = ctypes.c_uint64
         L.dq_linear_fp8_workspace_size.argtypes = [i64, i64, i64]
         L.dq_linear_fp8_workspace_size.restype = ctypes.c_uint64
         L.dq_status_string.argtypes = [i32]
@@ -195,10 +198,12 @@ def _resolve_workspace(workspace, dev, st, M, K, N):
     return workspace, workspace.numel()
 
 
-def _cached_workspace(dev, stream, nbytes):
-    """The zero-filled workspace of (device, stream), grown to at least nbytes. Every completed
-    call leaves a workspace zeroed, and calls on one stream run in order, so it is reused."""
-    key = (dev.index, stream.cuda_stream)
+def _cached_workspace(dev, stream, nbytes, kind="linear"):
+    """The zero-filled workspace of (device, stream, kind), grown to at least nbytes. Every
+    completed call leaves its workspace's counters zeroed, and calls on one stream run in order,
+    so it is reused. The linear layers and attention keep separate workspaces (their counters
+    sit at different places)."""
+    key = (dev.index, stream.cuda_stream, kind)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
         with torch.cuda.stream(stream):
@@ -328,9 +333,19 @@ def quantize_qkv_heads_fp8(q, k, v, stream=None):
             sv)
 
 
-def dq_attention_fp8(q8, q_scale, k8, k_scale, vt8, v_scale, out=None, stream=None):
+def dq_attention_fp8_workspace_size(H, S):
+    """Bytes of workspace dq_attention_fp8 may use for H heads of S tokens (0: invalid sizes)."""
+    return int(lib().dq_attention_fp8_workspace_size(int(H), int(S)))
+
+
+def dq_attention_fp8(q8, q_scale, k8, k_scale, vt8, v_scale, out=None, stream=None,
+                     workspace="auto", max_workgroups=0):
     """Attention over FP8 queries, keys, values (codes [H, S, 128], values transposed
-    [H, 128, S], scales [H, S]) -> bf16 [S, H, 128]."""
+    [H, 128, S], scales [H, S]) -> bf16 [S, H, 128].
+
+    workspace: "auto" (a zero-filled buffer cached per device and stream), None (whole tiles per
+    workgroup) or a zero-initialized uint8 tensor of dq_attention_fp8_workspace_size(H, S) bytes.
+    max_workgroups: 0 (one per compute unit) or a lower cap on the workgroups launched."""
     where = "dq_attention_fp8"
     if not isinstance(q8, torch.Tensor) or q8.dim() != 3 or q8.device.type != "cuda":
         raise ValueError(f"{where}: query codes must be a 3-D tensor on a GPU")
@@ -344,12 +359,26 @@ def dq_attention_fp8(q8, q_scale, k8, k_scale, vt8, v_scale, out=None, stream=No
     out = torch.empty((S, H, HEAD_DIM), dtype=torch.bfloat16, device=dev) if out is None else out
     _need(out, "out", torch.bfloat16, (S, H, HEAD_DIM), dev)
     with torch.cuda.device(dev):
+        st = torch.cuda.current_stream(dev) if stream is None else stream
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError(f"workspace must be 'auto', None or a tensor, not {workspace!r}")
+            need = dq_attention_fp8_workspace_size(H, S)
+            workspace = _cached_workspace(dev, st, need, "attention") if (need and H * S) else None
+        if workspace is not None and (not isinstance(workspace, torch.Tensor)
+                                      or workspace.dtype != torch.uint8 or workspace.device != dev
+                                      or not workspace.is_contiguous()):
+            raise ValueError("workspace must be a contiguous uint8 tensor on the device")
+        ws_bytes = 0 if workspace is None else workspace.numel()
         _check(lib().dq_attention_fp8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(vt8),
-                                      _ptr(v_scale), H, S, _ptr(out), _stream(stream, dev)), where)
+                                      _ptr(v_scale), H, S, _ptr(out),
+                                      None if workspace is None else _ptr(workspace), ws_bytes,
+                                      int(max_workgroups), _stream(st, dev)), where)
     return out
 
 
 __all__ = ["dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
            "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8", "HEAD_DIM",
-           "dq_quantize_v_fp8", "dq_attention_fp8", "quantize_qkv_heads_fp8",
+           "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
+           "quantize_qkv_heads_fp8",
            "dq_linear_fp8_workspace_size", "DQError", "EPILOGUES", "lib", "LIB_PATH"]

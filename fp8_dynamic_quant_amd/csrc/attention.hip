@@ -14,8 +14,10 @@
 // quant_v_t: one workgroup quantizes 64 tokens of one head (4 lanes per token, the row scale as
 // dq_quantize_fp8 computes it, the same encoder) and writes the codes transposed through LDS.
 //
-// attn_fp8: one workgroup (4 waves) takes 128 queries of one head; wave w owns 32 of them and
-// keeps their codes in registers. Keys come in blocks of 64, double-buffered in LDS:
+// attn_fp8: a tile is 256 queries of one head; a workgroup (8 waves, one per compute unit)
+// works on one tile at a time, wave w owning 32 of its queries with their codes in registers
+// (the work split across workgroups is described at the kernel). Keys come in blocks of 64,
+// double-buffered in LDS:
 //   * K codes by global -> LDS copies (16 bytes per lane), 16-byte chunk c of key row r stored
 //     at slot c ^ ((r >> 1) & 7) so that 16 rows read at one offset hit 16 different slots;
 //   * V codes through registers, decoded once per workgroup to bf16 (exact: every E4M3 value is
@@ -49,9 +51,13 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 typedef float f2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 constexpr int kD = kHeadDim;   // 128 channels per head
-constexpr int kQB = 128;       // queries per workgroup
+constexpr int kWaves = 8;      // wavefronts per workgroup, two per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQB = 32 * kWaves;  // queries per workgroup (32 per wave)
 constexpr int kKB = 64;        // keys per block
 
 // ---------------------------------------------------------------------------------------------
@@ -135,9 +141,27 @@ struct AttnArgs {
   const uint8_t* vt8;  // [H, 128, S]
   const float* sv;     // [H, S]
   uint16_t* out;       // [S, H, 128]
+  uint8_t* ws;         // split schedule: arrival counters, then partial results (else unused)
+  uint32_t ws_bytes;
   int H, S;
+  int qtiles;          // ceil(S / 128): query tiles per head
+  int nblk;            // ceil(S / 64): key blocks per tile
+  int split;           // 1: workgroups take runs of key blocks, cutting tiles; 0: whole tiles
   float c;             // log2(e) / sqrt(128)
 };
+
+// Split schedule. The workspace opens with one arrival counter per workgroup boundary, then two
+// partial results per boundary for the tile cut there (side 0: its first key blocks, side 1: its
+// last ones). A partial holds, per wave and lane, the 64 unnormalized output sums as 16-byte
+// groups (lane minor), then (m, sum) of the lane's query.
+constexpr int kMaxGroups = 512;
+constexpr uint32_t kFlagBytes = 4096;  // kMaxGroups counters, padded
+constexpr uint32_t kPartBytes = kThreads * (64 + 2) * 4;
+constexpr int kCoherent = 16;  // sc1: loads and stores coherent across XCDs
+
+__device__ __forceinline__ uint32_t part_offset(int boundary, int side) {
+  return kFlagBytes + (uint32_t)(2 * boundary + side) * kPartBytes;
+}
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
@@ -158,33 +182,48 @@ __device__ __forceinline__ void swap_halves(float& a, float& b) {
   b = __uint_as_float(y);
 }
 
-// Key block kb (64 rows of 128 bytes) into an LDS stage: wave w fills 16-byte slots
-// [128 w, 128 w + 128) with two copies; slot n is row n >> 3, position n & 7, which holds chunk
-// (n & 7) ^ key(row). Rows past S read row S - 1 (their logits are masked).
-__device__ __forceinline__ void copy_keys(const AttnArgs& a, int h, int kb, uint8_t* stage,
-                                          int w, int l) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int n = w * 128 + i * 64 + l;
-    const int r = n >> 3, p = n & 7;
-    const int key = kb * kKB + r < a.S ? kb * kKB + r : a.S - 1;
-    const uint8_t* src = a.k8 + ((size_t)h * (size_t)a.S + (size_t)key) * kD + swz(r, p) * 16;
-    __builtin_amdgcn_global_load_lds(
-        src, (__attribute__((address_space(3))) void*)(stage + (w * 128 + i * 64) * 16), 16, 0,
-        0);
-  }
+// Global addresses of one key block of one head.
+struct Blk {
+  const uint8_t* k;   // codes of its first key
+  const uint8_t* v;   // value codes of channel 0 at its first key (channel c is c S bytes on)
+  const float* sk;    // scale of its first key
+  const float* sv;
+  int key0;           // index of its first key
+};
+
+__device__ __forceinline__ Blk block_at(const AttnArgs& a, int h, int kb) {
+  const size_t hs = (size_t)h * (size_t)a.S, k0 = (size_t)kb * kKB;
+  return Blk{a.k8 + (hs + k0) * kD, a.vt8 + hs * kD + k0, a.sk + hs + k0, a.sv + hs + k0,
+             kb * kKB};
+}
+__device__ __forceinline__ Blk next_block(Blk b) {
+  return Blk{b.k + kKB * kD, b.v + kKB, b.sk + kKB, b.sv + kKB, b.key0 + kKB};
 }
 
-// Value codes of block kb: thread tid takes channel tid >> 1, keys 32 (tid & 1) + [0, 32).
-// S is a multiple of 16, so a 16-key chunk is either inside the sequence or past it (zeros).
-__device__ __forceinline__ void load_values(const AttnArgs& a, int h, int kb, int tid,
-                                            uint4 (&vr)[2]) {
-  const int ch = tid >> 1, k0 = kb * kKB + 32 * (tid & 1);
-  const uint8_t* row = a.vt8 + ((size_t)h * kD + ch) * (size_t)a.S;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    vr[i] = k0 + 16 * i < a.S ? *reinterpret_cast<const uint4*>(row + k0 + 16 * i)
-                              : make_uint4(0u, 0u, 0u, 0u);
+// A key block (64 rows of 128 bytes) into an LDS stage, one 16-byte copy per thread: wave w
+// fills slots [64 w, 64 w + 64); slot n is row n >> 3, position n & 7, which holds chunk
+// (n & 7) ^ key(row). Rows past S read row S - 1 (their logits are masked).
+__device__ __forceinline__ void copy_keys(const Blk& b, int S, uint8_t* stage, int w, int l) {
+  const int n = w * 64 + l;
+  const int r = n >> 3, p = n & 7;
+  const int row = b.key0 + r < S ? r : S - 1 - b.key0;
+  const uint8_t* src = b.k + row * kD + swz(r, p) * 16;
+  __builtin_amdgcn_global_load_lds(
+      src, (__attribute__((address_space(3))) void*)(stage + w * 64 * 16), 16, 0, 0);
+}
+
+// Value codes of a block: thread tid takes channel tid >> 2, keys 16 (tid & 3) + [0, 16); vrow
+// is that row offset, (tid >> 2) S + 16 (tid & 3). S is a multiple of 16, so the 16 keys are
+// either inside the sequence or past it (zeros).
+__device__ __forceinline__ uint4 load_values(const Blk& b, int S, int tid, size_t vrow) {
+  return b.key0 + 16 * (tid & 3) < S ? *reinterpret_cast<const uint4*>(b.v + vrow)
+                                     : make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The block's key scale (threads 0-63) or value scale (threads 64-127) of key tid & 63, 0 past S.
+__device__ __forceinline__ float load_scale(const Blk& b, int S, int tid) {
+  const int j = tid & (kKB - 1);
+  return tid < 2 * kKB && b.key0 + j < S ? (tid < kKB ? b.sk : b.sv)[j] : 0.0f;
 }
 
 // 8 codes (two dwords) -> 8 bf16: gfx950's scaled conversion, two codes per instruction, at
@@ -198,92 +237,139 @@ __device__ __forceinline__ uint4 decode8(uint32_t d0, uint32_t d1) {
 }
 
 // The decoded values into an LDS stage, [channel][key] bf16, 128-byte rows, swizzled.
-__device__ __forceinline__ void store_values(uint8_t* stage, int tid, const uint4 (&vr)[2]) {
-  const int ch = tid >> 1, hf = tid & 1;
+__device__ __forceinline__ void store_values(uint8_t* stage, int tid, const uint4 vr) {
+  const int ch = tid >> 2, q = tid & 3;
+  const uint32_t d[4] = {vr.x, vr.y, vr.z, vr.w};
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t d[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int chunk = 4 * hf + 2 * i + j;  // 8 keys = 16 bytes
-      *reinterpret_cast<uint4*>(stage + ch * 128 + swz(ch, chunk) * 16) =
-          decode8(d[2 * j], d[2 * j + 1]);
-    }
+  for (int j = 0; j < 2; ++j) {
+    const int chunk = 2 * q + j;  // 8 keys = 16 bytes
+    *reinterpret_cast<uint4*>(stage + ch * 128 + swz(ch, chunk) * 16) =
+        decode8(d[2 * j], d[2 * j + 1]);
   }
 }
 
-// Two waves per SIMD: without the bound the compiler spends 280 registers (one wave per SIMD);
-// asking for three spills to scratch and measured slower.
-__global__ void __launch_bounds__(256, 2) attn_fp8(AttnArgs a) {
+// One workgroup of 8 waves per compute unit (two per SIMD; the bound keeps the registers within
+// what two waves may hold). Two workgroups of 4 waves each on a unit ran unevenly: the waves of
+// the one dispatched first win the issue arbitration and finish early, and the other then runs
+// alone at lower throughput.
+//
+// Schedule: the (tile, key block) units, tile-major (tile = head * qtiles + query tile), are cut
+// into gridDim.x contiguous runs, one per workgroup: runs of whole tiles, or with a workspace
+// (split = 1) runs of equal length that may start or end inside a tile. A run is then a piece A
+// (the last blocks of a tile begun by the previous run), a piece B (the first blocks of a tile
+// that the next run finishes) and whole tiles; it takes A, then B, then the whole tiles, so both
+// cut tiles are settled early. Every run holds at least one whole tile's length of units, so a
+// tile is cut at most once. A cut piece stores its unnormalized result and counts its arrival;
+// the second to arrive adds the other's result to its own in a fixed order (side 0 first), so the
+// output does not depend on which arrives first, and zeroes the counter for the next call.
+__global__ void __launch_bounds__(kThreads, 1) attn_fp8(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t sK[2][kKB * kD];      // 2 x 8 KiB codes
   __shared__ __attribute__((aligned(1024))) uint8_t sV[2][kD * kKB * 2];  // 2 x 16 KiB bf16
   __shared__ __attribute__((aligned(16))) float sSK[2][kKB];
   __shared__ __attribute__((aligned(16))) float sSV[2][kKB];
-  const int h = blockIdx.y, q0 = blockIdx.x * kQB;
+  __shared__ int s_last;
   const int tid = threadIdx.x, l = tid & 63, hi = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int S = a.S;
-  const int qi = q0 + 32 * w + (l & 31);
-  const bool qlive = qi < S;
+  const int S = a.S, nb = a.nblk;
 
-  // this lane's query: channels [64 dh + 32 hi, +32) for the two 64-channel halves
+  // This workgroup's run. Consecutive workgroup ids go round-robin over the 8 XCDs; renumbering
+  // gives each XCD a contiguous stretch of runs, so its L2 serves the keys of few heads.
+  const int G = gridDim.x;
+  const int g = (G & 7) == 0 ? (int)(blockIdx.x & 7u) * (G >> 3) + (int)(blockIdx.x >> 3)
+                             : (int)blockIdx.x;
+  const int64_t T = (int64_t)a.H * a.qtiles;
+  int64_t u0, u1;
+  if (a.split) {
+    u0 = T * nb * g / G;
+    u1 = T * nb * (g + 1) / G;
+  } else {
+    u0 = T * g / G * nb;
+    u1 = T * (g + 1) / G * nb;
+  }
+  const int tA = (int)(u0 / nb), kA = (int)(u0 % nb);  // piece A: blocks [kA, nb) of tile tA
+  const int tB = (int)(u1 / nb), kB = (int)(u1 % nb);  // piece B: blocks [0, kB) of tile tB
+  const int tF = kA > 0 ? tA + 1 : tA;                 // whole tiles [tF, tB)
+  const int npieces = 2 + (tB - tF);
+  // piece p (0: A, 1: B, 2 + i: whole tile tF + i) -> tile and block range; false if empty
+  auto piece = [&](int p, int& t, int& k0, int& k1) -> bool {
+    if (p == 0) {
+      t = tA, k0 = kA, k1 = nb;
+      return kA > 0;
+    }
+    if (p == 1) {
+      t = tB, k0 = 0, k1 = kB;
+      return kB > 0;
+    }
+    t = tF + p - 2, k0 = 0, k1 = nb;
+    return true;
+  };
+  auto next_piece = [&](int p, int& t, int& k0, int& k1) -> int {
+    for (++p; p < npieces; ++p)
+      if (piece(p, t, k0, k1)) break;
+    return p;
+  };
+
+  // per-wave state of the current tile
   v8i qf[2];
-  {
+  float sqc = 0.0f, m = 0.0f, lsum = 0.0f;
+  int qi = 0;
+  bool qlive = false;
+  v16f o[4];
+  auto start_tile = [&](int t) {
+    const int h = t / a.qtiles, q0 = (t - h * a.qtiles) * kQB;
+    qi = q0 + 32 * w + (l & 31);
+    qlive = qi < S;
+    // this lane's query: channels [64 dh + 32 hi, +32) for the two 64-channel halves
     const uint8_t* qrow = a.q8 + ((size_t)h * (size_t)S + (size_t)(qlive ? qi : 0)) * kD;
 #pragma unroll
     for (int dh = 0; dh < 2; ++dh)
       qf[dh] = qlive ? *reinterpret_cast<const v8i*>(qrow + 64 * dh + 32 * hi) : (v8i){};
-  }
-  const float sqc = qlive ? a.sq[(size_t)h * (size_t)S + qi] * a.c : 0.0f;
-
-  const int nblk = (S + kKB - 1) / kKB;
-  // block 0 into stage 0
-  {
-    copy_keys(a, h, 0, sK[0], w, l);
-    uint4 vr[2];
-    load_values(a, h, 0, tid, vr);
-    store_values(sV[0], tid, vr);
-    if (tid < kKB) sSK[0][tid] = tid < S ? a.sk[(size_t)h * (size_t)S + tid] : 0.0f;
-    else if (tid < 2 * kKB) sSV[0][tid - kKB] = tid - kKB < S ? a.sv[(size_t)h * (size_t)S + tid - kKB] : 0.0f;
-  }
-
-  float m = -__builtin_inff(), lsum = 0.0f;
-  v16f o[4];
+    sqc = qlive ? a.sq[(size_t)h * (size_t)S + qi] * a.c : 0.0f;
+    m = -__builtin_inff();
+    lsum = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = (v16f){};
+    for (int i = 0; i < 4; ++i) o[i] = (v16f){};
+  };
 
-  // One key block; kTail marks the last block when S is not a multiple of 64 (the only one whose
-  // keys past S must take no weight), a separate instance so that full blocks carry no masking.
-  auto step = [&](const int kb, auto tail_tag) {
+  // One key block of head h in stage st; the block (hn, kbn) goes into the other stage when
+  // `more`. kTail marks the last block when S is not a multiple of 64 (the only one whose keys
+  // past S must take no weight), a separate instance so that full blocks carry no masking.
+  const size_t vrow = (size_t)(tid >> 2) * (size_t)S + 16 * (tid & 3);
+  auto step = [&](const int kb, const int st, const bool more, const Blk& bn, auto tail_tag) {
     constexpr bool tail = decltype(tail_tag)::value;
-    const int st = kb & 1;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's key copies of block kb
     __syncthreads();                     // every wave's copies and stores of block kb
-    const bool more = kb + 1 < nblk;
-    uint4 vr[2];
+    uint4 vr = make_uint4(0u, 0u, 0u, 0u);
     float scn = 0.0f;
     if (more) {
-      copy_keys(a, h, kb + 1, sK[st ^ 1], w, l);
-      load_values(a, h, kb + 1, tid, vr);
-      const int j = (kb + 1) * kKB + (tid & (kKB - 1));
-      if (tid < 2 * kKB && j < S) scn = (tid < kKB ? a.sk : a.sv)[(size_t)h * (size_t)S + j];
+      vr = load_values(bn, S, tid, vrow);
+      scn = load_scale(bn, S, tid);
     }
-    // 1. logits, [key][query]
-    v16f s[2];
+    // 1. logits, [key][query]. The next block's key copies into the other stage are issued only
+    //    after this block's key fragments are read: the compiler cannot tell the two stages of
+    //    sK apart and would otherwise wait for the copies before the first read.
+    v8i kf[2][2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      s[kh] = (v16f){};
       const int r = 32 * kh + (l & 31);
 #pragma unroll
       for (int dh = 0; dh < 2; ++dh) {
         const int c0 = 4 * dh + 2 * hi;
         const uint4 lo = *reinterpret_cast<const uint4*>(sK[st] + r * kD + swz(r, c0) * 16);
         const uint4 up = *reinterpret_cast<const uint4*>(sK[st] + r * kD + swz(r, c0 + 1) * 16);
-        const v8i kf = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                             (int)up.x, (int)up.y, (int)up.z, (int)up.w};
-        s[kh] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[dh], s[kh], 0, 0, 0, 0, 0,
-                                                                0);
+        kf[kh][dh] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                           (int)up.x, (int)up.y, (int)up.z, (int)up.w};
       }
+    }
+    if (more) copy_keys(bn, S, sK[st ^ 1], w, l);
+    v16f s[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      s[kh] = (v16f){};
+#pragma unroll
+      for (int dh = 0; dh < 2; ++dh)
+        s[kh] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[kh][dh], qf[dh], s[kh], 0, 0,
+                                                                0, 0, 0, 0);
     }
     // 2. softmax in base 2: u = s sk, t = u sqc (sqc >= 0, so max t = sqc max u); the running
     //    max m moves only when a block's max exceeds it by more than 8 (weights stay <= 2^8,
@@ -293,11 +379,11 @@ __global__ void __launch_bounds__(256, 2) attn_fp8(AttnArgs a) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 sk4 = *reinterpret_cast<const float4*>(&sSK[st][32 * kh + 8 * g + 4 * hi]);
+      for (int gq = 0; gq < 4; ++gq) {
+        const float4 sk4 = *reinterpret_cast<const float4*>(&sSK[st][32 * kh + 8 * gq + 4 * hi]);
         const float skv[4] = {sk4.x, sk4.y, sk4.z, sk4.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) u[kh][4 * g + j] *= skv[j];
+        for (int j = 0; j < 4; ++j) u[kh][4 * gq + j] *= skv[j];
       }
     if constexpr (tail) {
 #pragma unroll
@@ -329,23 +415,23 @@ __global__ void __launch_bounds__(256, 2) attn_fp8(AttnArgs a) {
       m = mn;
     }
     float ps = 0.0f;
-    uint32_t pk[2][4][2];  // bf16 pairs of p sv: [kh][g][j pair]
+    uint32_t pk[2][4][2];  // bf16 pairs of p sv: [kh][gq][j pair]
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 sv4 = *reinterpret_cast<const float4*>(&sSV[st][32 * kh + 8 * g + 4 * hi]);
+      for (int gq = 0; gq < 4; ++gq) {
+        const float4 sv4 = *reinterpret_cast<const float4*>(&sSV[st][32 * kh + 8 * gq + 4 * hi]);
         const float svv[4] = {sv4.x, sv4.y, sv4.z, sv4.w};
         float p[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(fmaf(u[kh][4 * g + j], sqc, -m));
+          p[j] = __builtin_amdgcn_exp2f(fmaf(u[kh][4 * gq + j], sqc, -m));
           if constexpr (tail)
-            if (kb * kKB + 32 * kh + 8 * g + 4 * hi + j >= S) p[j] = 0.0f;
+            if (kb * kKB + 32 * kh + 8 * gq + 4 * hi + j >= S) p[j] = 0.0f;
           ps += p[j];
         }
-        pk[kh][g][0] = pack_bf16(p[0] * svv[0], p[1] * svv[1]);
-        pk[kh][g][1] = pack_bf16(p[2] * svv[2], p[3] * svv[3]);
+        pk[kh][gq][0] = pack_bf16(p[0] * svv[0], p[1] * svv[1]);
+        pk[kh][gq][1] = pack_bf16(p[2] * svv[2], p[3] * svv[3]);
       }
     {
       float a0 = ps, b0 = ps;
@@ -375,29 +461,151 @@ __global__ void __launch_bounds__(256, 2) attn_fp8(AttnArgs a) {
       else if (tid < 2 * kKB) sSV[st ^ 1][tid - kKB] = scn;
     }
   };
-  const int nfull = S / kKB;
-  for (int kb = 0; kb < nfull; ++kb) step(kb, std::false_type{});
-  if (nfull < nblk) step(nfull, std::true_type{});
+
+  // A cut piece: store this workgroup's part, count it; the second part to arrive loads the
+  // other, adds the two and returns true (it then writes the output).
+  auto settle_cut = [&](int boundary, int side) -> bool {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(a.ws, 0, (int)a.ws_bytes, 0x00020000);
+    const uint32_t lane_off = (uint32_t)(w * 64 + l) * 16u;
+    {
+      const uint32_t base = part_offset(boundary, side);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 x = make_float4(o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2],
+                                       o[db][4 * q4 + 3]);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, x), rs,
+                                                 base + (uint32_t)(4 * db + q4) * (kThreads * 16u) + lane_off,
+                                                 0, kCoherent);
+        }
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, make_float2(m, lsum)), rs,
+                                            base + kThreads * 256u + (uint32_t)(w * 64 + l) * 8u, 0,
+                                            kCoherent);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the part is stored
+    __syncthreads();
+    uint32_t* flags = reinterpret_cast<uint32_t*>(a.ws);
+    if (tid == 0) {
+      const uint32_t old =
+          __hip_atomic_fetch_add(flags + boundary, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = old == 1u;
+    }
+    __syncthreads();
+    if (!s_last) return false;
+    const uint32_t base = part_offset(boundary, side ^ 1);
+    v4u x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      x[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, base + (uint32_t)i * (kThreads * 16u) + lane_off, 0,
+                                                   kCoherent);
+    const v2u ml = __builtin_amdgcn_raw_buffer_load_b64(
+        rs, base + kThreads * 256u + (uint32_t)(w * 64 + l) * 8u, 0, kCoherent);
+    const float m_o = __uint_as_float(ml[0]), l_o = __uint_as_float(ml[1]);
+    // side 0 is always the first operand of the sum
+    const float m0 = side == 0 ? m : m_o, m1 = side == 0 ? m_o : m;
+    const float mn = fmaxf(m0, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m0 - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
+    const float l0 = side == 0 ? lsum : l_o, l1 = side == 0 ? l_o : lsum;
+    lsum = fmaf(l0, a0, __fmul_rn(l1, a1));
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float other = __uint_as_float(x[4 * db + (e >> 2)][e & 3]);
+        const float v0 = side == 0 ? o[db][e] : other, v1 = side == 0 ? other : o[db][e];
+        o[db][e] = fmaf(v0, a0, __fmul_rn(v1, a1));
+      }
+    if (tid == 0)
+      __hip_atomic_store(flags + boundary, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+  };
 
   // o / sum, [channel][query] -> out[query][h][channel]
-  const float inv = 1.0f / lsum;
+  auto write_out = [&](int h) {
+    const float inv = 1.0f / lsum;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int gp = 0; gp < 2; ++gp) {
-      float v0[4], v1[4];
+      for (int gp = 0; gp < 2; ++gp) {
+        float v0[4], v1[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v0[j] = o[db][(2 * gp) * 4 + j] * inv;
-        v1[j] = o[db][(2 * gp + 1) * 4 + j] * inv;
-        swap_halves(v0[j], v1[j]);
+        for (int j = 0; j < 4; ++j) {
+          v0[j] = o[db][(2 * gp) * 4 + j] * inv;
+          v1[j] = o[db][(2 * gp + 1) * 4 + j] * inv;
+          swap_halves(v0[j], v1[j]);
+        }
+        const uint4 ov = make_uint4(pack_bf16(v0[0], v0[1]), pack_bf16(v0[2], v0[3]),
+                                    pack_bf16(v1[0], v1[1]), pack_bf16(v1[2], v1[3]));
+        if (qlive)
+          *reinterpret_cast<uint4*>(a.out + ((size_t)qi * (size_t)a.H + h) * kD + 32 * db +
+                                    16 * gp + 8 * hi) = ov;
       }
-      const uint4 ov = make_uint4(pack_bf16(v0[0], v0[1]), pack_bf16(v0[2], v0[3]),
-                                  pack_bf16(v1[0], v1[1]), pack_bf16(v1[2], v1[3]));
-      if (qlive)
-        *reinterpret_cast<uint4*>(a.out + ((size_t)qi * (size_t)a.H + h) * kD + 32 * db + 16 * gp +
-                                  8 * hi) = ov;
+  };
+
+  int t, k0, k1;
+  int p = piece(0, t, k0, k1) ? 0 : next_piece(0, t, k0, k1);
+  if (p >= npieces) return;  // an empty run (the host never launches one)
+  // the run's first block into stage 0
+  Blk bc = block_at(a, t / a.qtiles, k0);
+  {
+    copy_keys(bc, S, sK[0], w, l);
+    store_values(sV[0], tid, load_values(bc, S, tid, vrow));
+    const float sc = load_scale(bc, S, tid);
+    if (tid < kKB) sSK[0][tid] = sc;
+    else if (tid < 2 * kKB) sSV[0][tid - kKB] = sc;
+  }
+  int st = 0;
+  const int nfull = S / kKB;  // blocks without keys past S; block nfull (if any) is the last
+  for (;;) {
+    start_tile(t);
+    const int h = t / a.qtiles;
+    int tn = t, k0n = 0, k1n = 0;
+    const int pn = next_piece(p, tn, k0n, k1n);
+    // the block after kb: the next one of this piece, else the first of the next piece
+    auto after = [&](int kb, bool& more) -> Blk {
+      const bool last = kb + 1 == k1;
+      more = !last || pn < npieces;
+      return !last ? next_block(bc) : block_at(a, more ? tn / a.qtiles : 0, k0n);
+    };
+    // full blocks, then (kept out of the loop so that the two instances do not meet in one
+    // loop body) the partial last block
+    const int kfull = k1 < nfull ? k1 : nfull;
+    for (int kb = k0; kb < kfull; ++kb) {
+      bool more;
+      const Blk bn = after(kb, more);
+      step(kb, st, more, bn, std::false_type{});
+      bc = bn;
+      st ^= 1;
     }
+    if (k1 > nfull) {
+      bool more;
+      const Blk bn = after(nfull, more);
+      step(nfull, st, more, bn, std::true_type{});
+      bc = bn;
+      st ^= 1;
+    }
+    // p == 0 is piece A (side 1 of boundary g), p == 1 piece B (side 0 of boundary g + 1)
+    if (p >= 2 || settle_cut(p == 0 ? g : g + 1, p == 0 ? 1 : 0)) write_out(h);
+    if (pn >= npieces) break;
+    p = pn, t = tn, k0 = k0n, k1 = k1n;
+  }
+}
+
+// Compute units of the current device, queried once per device.
+int device_compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    __atomic_store_n(&cached[dev], n, __ATOMIC_RELAXED);
+  }
+  return n;
 }
 
 }  // namespace
@@ -412,7 +620,8 @@ hipError_t launch_quantize_v(const uint16_t* v, int64_t H, int64_t S, uint8_t* v
 
 hipError_t launch_attention(const uint8_t* q8, const float* sq, const uint8_t* k8, const float* sk,
                             const uint8_t* vt8, const float* sv, int64_t H, int64_t S,
-                            uint16_t* out, hipStream_t stream) {
+                            uint16_t* out, void* workspace, int64_t max_workgroups,
+                            hipStream_t stream) {
   if (H == 0 || S == 0) return hipSuccess;
   AttnArgs a;
   a.q8 = q8;
@@ -424,10 +633,25 @@ hipError_t launch_attention(const uint8_t* q8, const float* sq, const uint8_t* k
   a.out = out;
   a.H = (int)H;
   a.S = (int)S;
+  a.qtiles = (int)((S + kQB - 1) / kQB);
+  a.nblk = (int)((S + kKB - 1) / kKB);
   a.c = 1.4426950408889634f / 11.313708498984761f;  // log2(e) / sqrt(128)
-  hipLaunchKernelGGL(attn_fp8, dim3((unsigned)((S + kQB - 1) / kQB), (unsigned)H), dim3(256), 0,
-                     stream, a);
+  const int64_t tiles = H * a.qtiles;
+  int64_t cap = device_compute_units();  // one workgroup per compute unit
+  if (max_workgroups > 0 && max_workgroups < cap) cap = max_workgroups;
+  if (workspace && cap > kMaxGroups) cap = kMaxGroups;
+  const int64_t grid = tiles < cap ? tiles : cap;
+  a.split = workspace != nullptr && tiles > grid;
+  a.ws = static_cast<uint8_t*>(workspace);
+  a.ws_bytes = a.split ? (uint32_t)attention_workspace_bytes(H, S) : 0u;
+  hipLaunchKernelGGL(attn_fp8, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+uint64_t attention_workspace_bytes(int64_t H, int64_t S) {
+  const int64_t tiles = H * ((S + kQB - 1) / kQB);
+  const int64_t groups = tiles < kMaxGroups ? tiles : kMaxGroups;
+  return kFlagBytes + 2 * (uint64_t)groups * kPartBytes;
 }
 
 }  // namespace dq

@@ -228,9 +228,11 @@ int dq_quantize_v_fp8(const void* v, int64_t H, int64_t S, void* vt, float* v_sc
 
 int dq_attention_fp8(const void* q, const float* q_scale, const void* k, const float* k_scale,
                      const void* vt, const float* v_scale, int64_t H, int64_t S, void* out,
+                     void* workspace, uint64_t workspace_bytes, int64_t max_workgroups,
                      void* stream) {
   const int shape = check_attention_shape(H, S);
   if (shape != DQ_OK) return shape;
+  if (max_workgroups < 0) return DQ_ERR_VALUE;
   if (H == 0 || S == 0) return DQ_OK;
   if (!q || !q_scale || !k || !k_scale || !vt || !v_scale || !out) return DQ_ERR_NULL;
   if (!aligned16(q) || !aligned16(q_scale) || !aligned16(k) || !aligned16(k_scale) ||
@@ -242,10 +244,23 @@ int dq_attention_fp8(const void* q, const float* q_scale, const void* k, const f
   const uint64_t in_bytes[6] = {n, sb, n, sb, n, sb};
   for (int i = 0; i < 6; ++i)
     if (overlap(out, 2 * n, ins[i], in_bytes[i])) return DQ_ERR_ALIAS;
+  if (workspace) {
+    const uint64_t need = dq::attention_workspace_bytes(H, S);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
+      return DQ_ERR_WORKSPACE;
+    for (int i = 0; i < 6; ++i)
+      if (overlap(workspace, need, ins[i], in_bytes[i])) return DQ_ERR_ALIAS;
+    if (overlap(workspace, need, out, 2 * n)) return DQ_ERR_ALIAS;
+  }
   return hip_status(dq::launch_attention(
       static_cast<const uint8_t*>(q), q_scale, static_cast<const uint8_t*>(k), k_scale,
-      static_cast<const uint8_t*>(vt), v_scale, H, S, static_cast<uint16_t*>(out),
-      static_cast<hipStream_t>(stream)));
+      static_cast<const uint8_t*>(vt), v_scale, H, S, static_cast<uint16_t*>(out), workspace,
+      max_workgroups, static_cast<hipStream_t>(stream)));
+}
+
+uint64_t dq_attention_fp8_workspace_size(int64_t H, int64_t S) {
+  if (check_attention_shape(H, S) != DQ_OK) return 0;
+  return dq::attention_workspace_bytes(H, S);
 }
 
 uint64_t dq_linear_fp8_workspace_size(int64_t M, int64_t K, int64_t N) {
@@ -270,6 +285,6 @@ const char* dq_status_string(int status) {
 
 int dq_last_hip_error(void) { return g_last_hip_error; }
 
-int dq_abi_version(void) { return 5; }
+int dq_abi_version(void) { return 6; }
 
 }  // extern "C"

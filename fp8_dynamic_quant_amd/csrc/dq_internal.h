@@ -65,11 +65,15 @@ hipError_t launch_linear_qkv(const uint8_t* q, const float* scale, int64_t M, in
 // FP8 attention (attention.hip). S % 16 == 0 and 1 <= S, H.
 //   launch_quantize_v: v bf16 [H, S, kHeadDim] -> codes transposed [H, kHeadDim, S], scales [H, S]
 //   launch_attention:  q, k codes [H, S, kHeadDim] and scales [H, S], v as above ->
-//                      out bf16 [S, H, kHeadDim]
+//                      out bf16 [S, H, kHeadDim]; workspace NULL or at least
+//                      attention_workspace_bytes(H, S) bytes (zero before first use), max_workgroups
+//                      0 (two per compute unit) or a lower cap
 hipError_t launch_quantize_v(const uint16_t* v, int64_t H, int64_t S, uint8_t* vt, float* sv,
                              hipStream_t stream);
 hipError_t launch_attention(const uint8_t* q8, const float* sq, const uint8_t* k8, const float* sk,
                             const uint8_t* vt8, const float* sv, int64_t H, int64_t S,
-                            uint16_t* out, hipStream_t stream);
+                            uint16_t* out, void* workspace, int64_t max_workgroups,
+                            hipStream_t stream);
+uint64_t attention_workspace_bytes(int64_t H, int64_t S);
 
 }  // namespace dq

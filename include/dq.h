@@ -207,11 +207,37 @@ int dq_quantize_v_fp8(const void* v, int64_t H, int64_t S, void* vt, float* v_sc
  *   q, k      uint8 [H, S, 128]  codes;  q_scale, k_scale  float [H, S]
  *   vt        uint8 [H, 128, S]  codes (from dq_quantize_v_fp8);  v_scale  float [H, S]
  *   out       bf16 [S, H, 128]   token-major (row s holds the H heads' outputs in order)
- * Requirements: as dq_quantize_v_fp8; out overlapping no input.
+ *   workspace           NULL (workspace_bytes ignored), or device memory of at least
+ *                       dq_attention_fp8_workspace_size(H, S) bytes, 256-byte aligned, overlapping
+ *                       no other argument
+ *   max_workgroups      0 for the default (one workgroup per compute unit, all resident at
+ *                       once), or a lower cap on the workgroups launched
+ *
+ * Work split: a tile is 256 queries of one head against all S keys, in blocks of 64 keys. When
+ * there are no more tiles than workgroups, each workgroup computes one tile. Otherwise, without a
+ * workspace each workgroup computes a contiguous run of whole tiles; with one, the tiles' key
+ * blocks are dealt out in equal contiguous runs, so a tile may be cut between two neighbouring
+ * workgroups: each part stores its unnormalized fp32 result and (running max, sum) in the
+ * workspace, and the part that finishes second merges the two in a fixed order (the result does
+ * not depend on timing; it can differ in the last bits from an uncut run). The workspace must
+ * hold zeros before its first use; every call that completes leaves its counters at zero, so one
+ * zero fill at allocation is enough, and one workspace serves calls of any size up to the one it
+ * was sized for. Calls that may run concurrently must not share a workspace.
+ * Requirements: as dq_quantize_v_fp8; out overlapping no input; max_workgroups >= 0
+ * (DQ_ERR_VALUE otherwise).
  */
 int dq_attention_fp8(const void* q, const float* q_scale, const void* k, const float* k_scale,
                      const void* vt, const float* v_scale, int64_t H, int64_t S, void* out,
+                     void* workspace, uint64_t workspace_bytes, int64_t max_workgroups,
                      void* stream);
+
+/*
+ * dq_attention_fp8_workspace_size -- bytes of workspace dq_attention_fp8 may use for H heads of
+ * S tokens, or 0 if the sizes break its requirements: 4 KiB of counters plus two 132 KiB partial
+ * results per workgroup boundary, for at most min(H ceil(S / 256), 512) workgroups (at most
+ * about 132 MiB). Needs no GPU.
+ */
+uint64_t dq_attention_fp8_workspace_size(int64_t H, int64_t S);
 
 /*
  * dq_linear_fp8_workspace_size -- bytes of workspace dq_linear_fp8 uses for an M x K -> N
@@ -261,7 +287,7 @@ const char* dq_status_string(int status);
 /* The hipError_t behind the most recent DQ_ERR_HIP returned on the calling thread (0 if none). */
 int dq_last_hip_error(void);
 
-/* ABI version of this header (currently 5). */
+/* ABI version of this header (currently 6). */
 int dq_abi_version(void);
 
 #ifdef __cplusplus

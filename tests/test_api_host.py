@@ -31,7 +31,10 @@ def lib():
     L.dq_linear_qkv_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, vp, ctypes.c_float,
                                     vp, vp, vp, vp, ctypes.c_uint64, vp]
     L.dq_quantize_v_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
-    L.dq_attention_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp]
+    L.dq_attention_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, ctypes.c_uint64,
+                                   i64, vp]
+    L.dq_attention_fp8_workspace_size.argtypes = [i64, i64]
+    L.dq_attention_fp8_workspace_size.restype = ctypes.c_uint64
     L.dq_linear_fp8_workspace_size.argtypes = [i64, i64, i64]
     L.dq_linear_fp8_workspace_size.restype = ctypes.c_uint64
     L.dq_status_string.restype = ctypes.c_char_p
@@ -48,7 +51,8 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
               "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8",
-              "dq_quantize_v_fp8", "dq_attention_fp8", "dq_linear_fp8_workspace_size", "dq_status_string", "dq_last_hip_error",
+              "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
+              "dq_linear_fp8_workspace_size", "dq_status_string", "dq_last_hip_error",
               "dq_abi_version"):
         assert n in names
 
@@ -59,7 +63,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dq_abi_version() == 5
+    assert lib.dq_abi_version() == 6
     for st in range(9):
         s = lib.dq_status_string(st)
         assert s and len(s) > 1
@@ -229,8 +233,9 @@ def test_linear_qkv_workspace_checks(lib):
 AQ, ASQ, AK, ASK, AV, ASV, AO = (0x20000000 * i for i in range(20, 27))   # fake, far apart
 
 
-def attn(lib, H=2, S=64, q=AQ, sq=ASQ, k=AK, sk=ASK, vt=AV, sv=ASV, out=AO):
-    return lib.dq_attention_fp8(q, sq, k, sk, vt, sv, H, S, out, None)
+def attn(lib, H=2, S=64, q=AQ, sq=ASQ, k=AK, sk=ASK, vt=AV, sv=ASV, out=AO, ws=None, ws_bytes=0,
+         max_wg=0):
+    return lib.dq_attention_fp8(q, sq, k, sk, vt, sv, H, S, out, ws, ws_bytes, max_wg, None)
 
 
 def test_attention_argument_checks(lib):
@@ -252,6 +257,30 @@ def test_attention_argument_checks(lib):
     assert attn(lib, out=ASV - 1024) == ALIAS
     assert attn(lib, out=AV + 16) == ALIAS
     assert attn(lib, out=AQ + 2 * 64 * 128, sq=None) == NULL        # right after q: no alias
+    assert attn(lib, max_wg=-1) == VALUE
+    assert attn(lib, max_wg=-1, S=0) == VALUE                       # checked before the size
+
+
+AW = 0x20000000 * 30
+
+
+def test_attention_workspace(lib):
+    size = lib.dq_attention_fp8_workspace_size
+    part = 8 * 64 * 66 * 4                              # one workgroup's partial result
+    assert part == 135168
+    assert size(24, 4608) == 4096 + 2 * 432 * part      # 24 heads x 18 query tiles of 256
+    assert size(2, 64) == 4096 + 2 * 2 * part
+    assert size(64, 1 << 16) == 4096 + 2 * 512 * part   # at most 512 workgroups
+    assert size(0, 64) == 4096 and size(3, 0) == 4096
+    assert size(2, 24) == 0 and size(-1, 64) == 0
+    need = size(2, 64)
+    assert attn(lib, ws=AW, ws_bytes=need - 1) == WORKSPACE
+    assert attn(lib, ws=AW + 16, ws_bytes=need) == WORKSPACE     # not 256-byte aligned
+    assert attn(lib, ws=AQ, ws_bytes=need) == ALIAS              # over the query codes
+    assert attn(lib, ws=AO - 256, ws_bytes=need) == ALIAS        # into the output
+    assert attn(lib, ws=AW, ws_bytes=need, q=None) == NULL
+    assert attn(lib, S=0, ws=AW + 16, ws_bytes=0) == OK          # empty: nothing is checked
+    assert lib.dq_last_hip_error() == 0
 
 
 def test_quantize_v_argument_checks(lib):
@@ -304,9 +333,10 @@ def test_python_binding_names_match_the_c_entry_points():
     import fp8_dynamic_quant_amd as dq
     for name in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
                  "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8",
-                 "dq_quantize_v_fp8", "dq_attention_fp8", "dq_linear_fp8_workspace_size"):
+                 "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
+                 "dq_linear_fp8_workspace_size"):
         assert callable(getattr(dq, name))
-    assert dq.lib().dq_abi_version() == 5
+    assert dq.lib().dq_abi_version() == 6
     assert dq.dq_linear_fp8_workspace_size(4608, 3072, 12288) == 3584 + 1024 * 262144
 
 

@@ -48,20 +48,20 @@ def _inputs(H, S, seed, scale=1.0, outlier=0.0):
     return out
 
 
-def _run(q16, k16, v16):
+def _run(q16, k16, v16, **kw):
     H, S, _ = q16.shape
     q8, sq, k8, sk, vt, sv = dq.quantize_qkv_heads_fp8(bf16_to_dev(q16), bf16_to_dev(k16),
                                                        bf16_to_dev(v16))
-    o = dq.dq_attention_fp8(q8, sq, k8, sk, vt, sv)
+    o = dq.dq_attention_fp8(q8, sq, k8, sk, vt, sv, **kw)
     torch.cuda.synchronize()
     return (q8.cpu().numpy(), sq.cpu().numpy(), k8.cpu().numpy(), sk.cpu().numpy(),
             vt.cpu().numpy(), sv.cpu().numpy(), dev_to_f64(o))
 
 
-def _check(q16, k16, v16, what, rows=None):
+def _check(q16, k16, v16, what, rows=None, **kw):
     H, S, _ = q16.shape
-    announce(f"attention {what} H={H} S={S}")
-    gq8, gsq, gk8, gsk, gvt, gsv, o = _run(q16, k16, v16)
+    announce(f"attention {what} H={H} S={S} {kw}")
+    gq8, gsq, gk8, gsk, gvt, gsv, o = _run(q16, k16, v16, **kw)
     # codes and scales against the oracle's own quantization
     (q8, sq), (k8, sk), (v8, sv) = (quantize_heads(bf16_bits_to_f32(x)) for x in (q16, k16, v16))
     assert np.array_equal(gq8, q8) and np.array_equal(gsq.view(np.uint32), sq.view(np.uint32))
@@ -153,3 +153,40 @@ def test_deterministic_and_empty():
                             torch.empty((3, D, 0), dtype=torch.uint8, device="cuda:0"),
                             torch.empty((3, 0), device="cuda:0"))
     assert e.shape == (0, 3, D)
+
+
+# (H, S, max_workgroups): tiles = H ceil(S / 256) above the cap cut tiles between neighbouring
+# workgroups; caps that are multiples of 8 also renumber workgroups by XCD.
+SPLIT_CASES = [(3, 128, 2), (2, 272, 3), (4, 1040, 5), (3, 1040, 8), (1, 4608, 16), (5, 400, 7),
+               (4, 512, 8)]
+
+
+@pytest.mark.parametrize("H,S,cap", SPLIT_CASES)
+def test_cut_tiles(H, S, cap):
+    """Runs of key blocks that start and end inside tiles (two parts merged through the
+    workspace), ragged last blocks, and one tile per workgroup (4 x 512 with 8)."""
+    q, k, v = _inputs(H, S, 12)
+    ws = torch.zeros(dq.dq_attention_fp8_workspace_size(H, S), dtype=torch.uint8,
+                     device="cuda:0")
+    o = _check(q, k, v, f"cut {H}x{S} cap {cap}", workspace=ws, max_workgroups=cap)
+    assert int(ws[:4096].count_nonzero()) == 0, "arrival counters left non-zero"
+    again = _run(q, k, v, workspace=ws, max_workgroups=cap)[-1]
+    assert np.array_equal(o, again), "cut tiles: result depends on the run"
+    assert int(ws[:4096].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("H,S,cap", [(3, 128, 2), (4, 1040, 5), (3, 1040, 8)])
+def test_whole_tile_runs_without_workspace(H, S, cap):
+    """More tiles than workgroups and no workspace: each workgroup takes whole tiles."""
+    q, k, v = _inputs(H, S, 13)
+    _check(q, k, v, f"whole runs {H}x{S} cap {cap}", workspace=None, max_workgroups=cap)
+
+
+def test_flux_attention_cut_and_uncut_agree():
+    """The default schedule on 24 x 4608 (tiles cut between workgroups) against whole tiles per
+    workgroup: both within the bound of the oracle (sampled), and close to each other."""
+    q, k, v = _inputs(24, 4608, 14)
+    a = _run(q, k, v)[-1]
+    b = _run(q, k, v, workspace=None)[-1]
+    d = np.abs(a - b)
+    assert np.max(d) <= 2.0 ** -7 * np.max(np.abs(b)), np.max(d)
