@@ -14,7 +14,7 @@
 // quant_v_t: one workgroup quantizes 64 tokens of one head (4 lanes per token, the row scale as
 // dq_quantize_fp8 computes it, the same encoder) and writes the codes transposed through LDS.
 //
-// attn_fp8: a tile is 256 queries of one head; a workgroup (8 waves, one per compute unit)
+// attn_fp8: a tile is 384 queries of one head; a workgroup (12 waves, one per compute unit)
 // works on one tile at a time, wave w owning 32 of its queries with their codes in registers
 // (the work split across workgroups is described at the kernel). Keys come in blocks of 64,
 // double-buffered in LDS:
@@ -55,7 +55,7 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 constexpr int kD = kHeadDim;   // 128 channels per head
-constexpr int kWaves = 8;      // wavefronts per workgroup, two per SIMD
+constexpr int kWaves = 12;     // wavefronts per workgroup, three per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQB = 32 * kWaves;  // queries per workgroup (32 per wave)
 constexpr int kKB = 64;        // keys per block
@@ -154,7 +154,7 @@ struct AttnArgs {
 // partial results per boundary for the tile cut there (side 0: its first key blocks, side 1: its
 // last ones). A partial holds, per wave and lane, the 64 unnormalized output sums as 16-byte
 // groups (lane minor), then (m, sum) of the lane's query.
-constexpr int kMaxGroups = 512;
+constexpr int kMaxGroups = 256;
 constexpr uint32_t kFlagBytes = 4096;  // kMaxGroups counters, padded
 constexpr uint32_t kPartBytes = kThreads * (64 + 2) * 4;
 constexpr int kCoherent = 16;  // sc1: loads and stores coherent across XCDs
@@ -167,6 +167,34 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >>
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){a, b}, bf2v));
+}
+
+// Lane n of each row of 16 lanes, to every lane of that row (DPP row_newbcast; folded into the
+// multiply that uses it).
+template <int N>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               0x150 + N, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_bcast(float v, int n) {  // n a constant after unrolling
+  switch (n) {
+    case 0: return row_bcast<0>(v);
+    case 1: return row_bcast<1>(v);
+    case 2: return row_bcast<2>(v);
+    case 3: return row_bcast<3>(v);
+    case 4: return row_bcast<4>(v);
+    case 5: return row_bcast<5>(v);
+    case 6: return row_bcast<6>(v);
+    case 7: return row_bcast<7>(v);
+    case 8: return row_bcast<8>(v);
+    case 9: return row_bcast<9>(v);
+    case 10: return row_bcast<10>(v);
+    case 11: return row_bcast<11>(v);
+    case 12: return row_bcast<12>(v);
+    case 13: return row_bcast<13>(v);
+    case 14: return row_bcast<14>(v);
+    default: return row_bcast<15>(v);
+  }
 }
 
 // Exchange a's value in lanes 32..63 with b's value in lanes 0..31.
@@ -200,10 +228,14 @@ __device__ __forceinline__ Blk next_block(Blk b) {
   return Blk{b.k + kKB * kD, b.v + kKB, b.sk + kKB, b.sv + kKB, b.key0 + kKB};
 }
 
-// A key block (64 rows of 128 bytes) into an LDS stage, one 16-byte copy per thread: wave w
-// fills slots [64 w, 64 w + 64); slot n is row n >> 3, position n & 7, which holds chunk
-// (n & 7) ^ key(row). Rows past S read row S - 1 (their logits are masked).
+// A block of key or value codes is 8 KiB: the first kMoveThreads threads move it, 16 bytes each.
+constexpr int kMoveThreads = kKB * kD / 16;
+
+// A key block (64 rows of 128 bytes) into an LDS stage, one 16-byte copy per thread of waves
+// 0-7: wave w fills slots [64 w, 64 w + 64); slot n is row n >> 3, position n & 7, which holds
+// chunk (n & 7) ^ key(row). Rows past S read row S - 1 (their logits are masked).
 __device__ __forceinline__ void copy_keys(const Blk& b, int S, uint8_t* stage, int w, int l) {
+  if (w >= kMoveThreads / 64) return;
   const int n = w * 64 + l;
   const int r = n >> 3, p = n & 7;
   const int row = b.key0 + r < S ? r : S - 1 - b.key0;
@@ -215,9 +247,11 @@ __device__ __forceinline__ void copy_keys(const Blk& b, int S, uint8_t* stage, i
 // Value codes of a block: thread tid takes channel tid >> 2, keys 16 (tid & 3) + [0, 16); vrow
 // is that row offset, (tid >> 2) S + 16 (tid & 3). S is a multiple of 16, so the 16 keys are
 // either inside the sequence or past it (zeros).
+// Threads past kMoveThreads load nothing.
 __device__ __forceinline__ uint4 load_values(const Blk& b, int S, int tid, size_t vrow) {
-  return b.key0 + 16 * (tid & 3) < S ? *reinterpret_cast<const uint4*>(b.v + vrow)
-                                     : make_uint4(0u, 0u, 0u, 0u);
+  return tid < kMoveThreads && b.key0 + 16 * (tid & 3) < S
+             ? *reinterpret_cast<const uint4*>(b.v + vrow)
+             : make_uint4(0u, 0u, 0u, 0u);
 }
 
 // The block's key scale (threads 0-63) or value scale (threads 64-127) of key tid & 63, 0 past S.
@@ -238,6 +272,7 @@ __device__ __forceinline__ uint4 decode8(uint32_t d0, uint32_t d1) {
 
 // The decoded values into an LDS stage, [channel][key] bf16, 128-byte rows, swizzled.
 __device__ __forceinline__ void store_values(uint8_t* stage, int tid, const uint4 vr) {
+  if (tid >= kMoveThreads) return;
   const int ch = tid >> 2, q = tid & 3;
   const uint32_t d[4] = {vr.x, vr.y, vr.z, vr.w};
 #pragma unroll
@@ -248,10 +283,10 @@ __device__ __forceinline__ void store_values(uint8_t* stage, int tid, const uint
   }
 }
 
-// One workgroup of 8 waves per compute unit (two per SIMD; the bound keeps the registers within
-// what two waves may hold). Two workgroups of 4 waves each on a unit ran unevenly: the waves of
-// the one dispatched first win the issue arbitration and finish early, and the other then runs
-// alone at lower throughput.
+// One workgroup of 12 waves per compute unit (three per SIMD; the bound keeps the registers
+// within what three waves may hold). Several smaller workgroups on a unit ran unevenly: the waves
+// of the one dispatched first win the issue arbitration and finish early, and the others then
+// run at lower throughput.
 //
 // Schedule: the (tile, key block) units, tile-major (tile = head * qtiles + query tile), are cut
 // into gridDim.x contiguous runs, one per workgroup: runs of whole tiles, or with a workspace
@@ -265,8 +300,7 @@ __device__ __forceinline__ void store_values(uint8_t* stage, int tid, const uint
 __global__ void __launch_bounds__(kThreads, 1) attn_fp8(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t sK[2][kKB * kD];      // 2 x 8 KiB codes
   __shared__ __attribute__((aligned(1024))) uint8_t sV[2][kD * kKB * 2];  // 2 x 16 KiB bf16
-  __shared__ __attribute__((aligned(16))) float sSK[2][kKB];
-  __shared__ __attribute__((aligned(16))) float sSV[2][kKB];
+  __shared__ __attribute__((aligned(16))) float sSC[2][2][kKB];  // [stage][key, value][key]
   __shared__ int s_last;
   const int tid = threadIdx.x, l = tid & 63, hi = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -334,7 +368,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8(AttnArgs a) {
   // One key block of head h in stage st; the block (hn, kbn) goes into the other stage when
   // `more`. kTail marks the last block when S is not a multiple of 64 (the only one whose keys
   // past S must take no weight), a separate instance so that full blocks carry no masking.
-  const size_t vrow = (size_t)(tid >> 2) * (size_t)S + 16 * (tid & 3);
+  const size_t vrow = (size_t)((tid >> 2) & (kD - 1)) * (size_t)S + 16 * (tid & 3);
   auto step = [&](const int kb, const int st, const bool more, const Blk& bn, auto tail_tag) {
     constexpr bool tail = decltype(tail_tag)::value;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's key copies of block kb
@@ -374,17 +408,21 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8(AttnArgs a) {
     // 2. softmax in base 2: u = s sk, t = u sqc (sqc >= 0, so max t = sqc max u); the running
     //    max m moves only when a block's max exceeds it by more than 8 (weights stay <= 2^8,
     //    harmless in fp32 and bf16), and the rescale runs only when some lane of the wave moved
+    //    The block's scales come in one 16-byte read per lane: lane 16 r + n holds the key
+    //    (n < 8) or value (n >= 8) scales of keys 32 kh + 8 g + 4 (r >> 1) + [0, 4), with
+    //    kh = (n >> 2) & 1 and g = n & 3, i.e. the four keys that lanes of half r >> 1 hold in
+    //    register group (kh, g); a row broadcast from lane n of the row hands them to every lane.
+    const float4 sc4 = *reinterpret_cast<const float4*>(
+        &sSC[st][(l >> 3) & 1][32 * ((l >> 2) & 1) + 8 * (l & 3) + 4 * hi]);
+    const float sc[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
     v16f (&u)[2] = s;  // u = s sk, in place
     float mxu = -__builtin_inff();
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const float4 sk4 = *reinterpret_cast<const float4*>(&sSK[st][32 * kh + 8 * gq + 4 * hi]);
-        const float skv[4] = {sk4.x, sk4.y, sk4.z, sk4.w};
+      for (int gq = 0; gq < 4; ++gq)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) u[kh][4 * gq + j] *= skv[j];
-      }
+        for (int j = 0; j < 4; ++j) u[kh][4 * gq + j] *= row_bcast(sc[j], 4 * kh + gq);
     if constexpr (tail) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
@@ -406,40 +444,33 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8(AttnArgs a) {
     }
     const float mx = mxu * sqc;
     const bool move = mx > m + 8.0f;
-    if (__builtin_amdgcn_ballot_w64(move) != 0) {
-      const float mn = move ? mx : m;
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
-      lsum *= alpha;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] *= alpha;
-      m = mn;
-    }
+    const float mn = move ? mx : m;
     float ps = 0.0f;
     uint32_t pk[2][4][2];  // bf16 pairs of p sv: [kh][gq][j pair]
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const float4 sv4 = *reinterpret_cast<const float4*>(&sSV[st][32 * kh + 8 * gq + 4 * hi]);
-        const float svv[4] = {sv4.x, sv4.y, sv4.z, sv4.w};
         float p[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(fmaf(u[kh][4 * gq + j], sqc, -m));
+          p[j] = __builtin_amdgcn_exp2f(fmaf(u[kh][4 * gq + j], sqc, -mn));
           if constexpr (tail)
             if (kb * kKB + 32 * kh + 8 * gq + 4 * hi + j >= S) p[j] = 0.0f;
           ps += p[j];
         }
-        pk[kh][gq][0] = pack_bf16(p[0] * svv[0], p[1] * svv[1]);
-        pk[kh][gq][1] = pack_bf16(p[2] * svv[2], p[3] * svv[3]);
+        const int n = 8 + 4 * kh + gq;
+        pk[kh][gq][0] = pack_bf16(p[0] * row_bcast(sc[0], n), p[1] * row_bcast(sc[1], n));
+        pk[kh][gq][1] = pack_bf16(p[2] * row_bcast(sc[2], n), p[3] * row_bcast(sc[3], n));
       }
     {
       float a0 = ps, b0 = ps;
       swap_halves(a0, b0);
       ps = a0 + b0;
     }
-    lsum += ps;
-    // 3. P V
+    // P V operands: weights of keys [16 kc, +16) after the half swap (done here, ahead of the
+    // branch below, so that the products above stay next to their scale broadcasts)
+    bf8v pb[4];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const int kh = kc >> 1, c2 = kc & 1;
@@ -447,18 +478,30 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8(AttnArgs a) {
       uint32_t y0 = pk[kh][2 * c2 + 1][0], y1 = pk[kh][2 * c2 + 1][1];
       swap_halves(x0, y0);
       swap_halves(x1, y1);
-      const bf8v pb = __builtin_bit_cast(bf8v, make_uint4(x0, x1, y0, y1));
+      pb[kc] = __builtin_bit_cast(bf8v, make_uint4(x0, x1, y0, y1));
+    }
+    // rescale by 2^(m - m') when the max moved (2^0 = 1 otherwise); the output only when some
+    // lane of the wave moved, which is rare after the first blocks
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    lsum = lsum * alpha + ps;
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] *= alpha;
+    }
+    m = mn;
+    // 3. P V
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const int r = 32 * db + (l & 31);
         const bf8v vf = *reinterpret_cast<const bf8v*>(sV[st] + r * 128 + swz(r, 2 * kc + hi) * 16);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kc], o[db], 0, 0, 0);
       }
     }
     if (more) {
       store_values(sV[st ^ 1], tid, vr);
-      if (tid < kKB) sSK[st ^ 1][tid] = scn;
-      else if (tid < 2 * kKB) sSV[st ^ 1][tid - kKB] = scn;
+      if (tid < 2 * kKB) sSC[st ^ 1][tid >> 6][tid & (kKB - 1)] = scn;
     }
   };
 
@@ -553,8 +596,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8(AttnArgs a) {
     copy_keys(bc, S, sK[0], w, l);
     store_values(sV[0], tid, load_values(bc, S, tid, vrow));
     const float sc = load_scale(bc, S, tid);
-    if (tid < kKB) sSK[0][tid] = sc;
-    else if (tid < 2 * kKB) sSV[0][tid - kKB] = sc;
+    if (tid < 2 * kKB) sSC[0][tid >> 6][tid & (kKB - 1)] = sc;
   }
   int st = 0;
   const int nfull = S / kKB;  // blocks without keys past S; block nfull (if any) is the last

@@ -213,7 +213,7 @@ int dq_quantize_v_fp8(const void* v, int64_t H, int64_t S, void* vt, float* v_sc
  *   max_workgroups      0 for the default (one workgroup per compute unit, all resident at
  *                       once), or a lower cap on the workgroups launched
  *
- * Work split: a tile is 256 queries of one head against all S keys, in blocks of 64 keys. When
+ * Work split: a tile is 384 queries of one head against all S keys, in blocks of 64 keys. When
  * there are no more tiles than workgroups, each workgroup computes one tile. Otherwise, without a
  * workspace each workgroup computes a contiguous run of whole tiles; with one, the tiles' key
  * blocks are dealt out in equal contiguous runs, so a tile may be cut between two neighbouring
@@ -233,9 +233,9 @@ int dq_attention_fp8(const void* q, const float* q_scale, const void* k, const f
 
 /*
  * dq_attention_fp8_workspace_size -- bytes of workspace dq_attention_fp8 may use for H heads of
- * S tokens, or 0 if the sizes break its requirements: 4 KiB of counters plus two 132 KiB partial
- * results per workgroup boundary, for at most min(H ceil(S / 256), 512) workgroups (at most
- * about 132 MiB). Needs no GPU.
+ * S tokens, or 0 if the sizes break its requirements: 4 KiB of counters plus two 198 KiB partial
+ * results per workgroup boundary, for at most min(H ceil(S / 384), 256) workgroups (at most
+ * about 99 MiB). Needs no GPU.
  */
 uint64_t dq_attention_fp8_workspace_size(int64_t H, int64_t S);
 

@@ -266,11 +266,12 @@ AW = 0x20000000 * 30
 
 def test_attention_workspace(lib):
     size = lib.dq_attention_fp8_workspace_size
-    part = 8 * 64 * 66 * 4                              # one workgroup's partial result
-    assert part == 135168
-    assert size(24, 4608) == 4096 + 2 * 432 * part      # 24 heads x 18 query tiles of 256
+    part = 12 * 64 * 66 * 4                             # one workgroup's partial result
+    assert part == 202752
+    assert size(4, 4608) == 4096 + 2 * 48 * part        # 4 heads x 12 query tiles of 384
+    assert size(24, 4608) == 4096 + 2 * 256 * part      # at most 256 workgroups
     assert size(2, 64) == 4096 + 2 * 2 * part
-    assert size(64, 1 << 16) == 4096 + 2 * 512 * part   # at most 512 workgroups
+    assert size(64, 1 << 16) == 4096 + 2 * 256 * part
     assert size(0, 64) == 4096 and size(3, 0) == 4096
     assert size(2, 24) == 0 and size(-1, 64) == 0
     need = size(2, 64)

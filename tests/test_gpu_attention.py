@@ -155,9 +155,9 @@ def test_deterministic_and_empty():
     assert e.shape == (0, 3, D)
 
 
-# (H, S, max_workgroups): tiles = H ceil(S / 256) above the cap cut tiles between neighbouring
+# (H, S, max_workgroups): tiles = H ceil(S / 384) above the cap cut tiles between neighbouring
 # workgroups; caps that are multiples of 8 also renumber workgroups by XCD.
-SPLIT_CASES = [(3, 128, 2), (2, 272, 3), (4, 1040, 5), (3, 1040, 8), (1, 4608, 16), (5, 400, 7),
+SPLIT_CASES = [(3, 128, 2), (3, 272, 2), (4, 1040, 5), (3, 1040, 8), (2, 4608, 16), (5, 400, 7),
                (4, 512, 8)]
 
 
