@@ -294,9 +294,10 @@ __device__ __forceinline__ void store_values(uint8_t* stage, int tid, const uint
 // (the last blocks of a tile begun by the previous run), a piece B (the first blocks of a tile
 // that the next run finishes) and whole tiles; it takes A, then B, then the whole tiles, so both
 // cut tiles are settled early. Every run holds at least one whole tile's length of units, so a
-// tile is cut at most once. A cut piece stores its unnormalized result and counts its arrival;
-// the second to arrive adds the other's result to its own in a fixed order (side 0 first), so the
-// output does not depend on which arrives first, and zeroes the counter for the next call.
+// tile is cut at most once. A cut piece stores its unnormalized result and counts its arrival
+// (unless it sees the other part in already); the second to arrive adds the other's result to its
+// own in a fixed order (side 0 first), so the output does not depend on which arrives first, and
+// zeroes the counter for the next call.
 __global__ void __launch_bounds__(kThreads, 1) attn_fp8(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t sK[2][kKB * kD];      // 2 x 8 KiB codes
   __shared__ __attribute__((aligned(1024))) uint8_t sV[2][kD * kKB * 2];  // 2 x 16 KiB bf16
@@ -506,12 +507,24 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8(AttnArgs a) {
   };
 
   // A cut piece: store this workgroup's part, count it; the second part to arrive loads the
-  // other, adds the two and returns true (it then writes the output).
+  // other, adds the two and returns true (it then writes the output). Side 0 (a run's piece B,
+  // taken after its piece A) usually arrives second, so it first looks whether side 1 is in
+  // already and then skips storing its own part.
   auto settle_cut = [&](int boundary, int side) -> bool {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(a.ws, 0, (int)a.ws_bytes, 0x00020000);
     const uint32_t lane_off = (uint32_t)(w * 64 + l) * 16u;
-    {
+    uint32_t* flags = reinterpret_cast<uint32_t*>(a.ws);
+    bool in = false;  // the other part is stored and counted
+    if (side == 0) {
+      if (tid == 0)
+        s_last = __hip_atomic_load(flags + boundary, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT) == 1u;
+      __syncthreads();
+      in = s_last;
+      __syncthreads();  // s_last is written again below
+    }
+    if (!in) {
       const uint32_t base = part_offset(boundary, side);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
@@ -519,24 +532,23 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8(AttnArgs a) {
         for (int q4 = 0; q4 < 4; ++q4) {
           const float4 x = make_float4(o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2],
                                        o[db][4 * q4 + 3]);
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, x), rs,
-                                                 base + (uint32_t)(4 * db + q4) * (kThreads * 16u) + lane_off,
-                                                 0, kCoherent);
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(v4u, x), rs,
+              base + (uint32_t)(4 * db + q4) * (kThreads * 16u) + lane_off, 0, kCoherent);
         }
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, make_float2(m, lsum)), rs,
                                             base + kThreads * 256u + (uint32_t)(w * 64 + l) * 8u, 0,
                                             kCoherent);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the part is stored
+      __syncthreads();
+      if (tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(flags + boundary, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        s_last = old == 1u;
+      }
+      __syncthreads();
+      if (!s_last) return false;
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the part is stored
-    __syncthreads();
-    uint32_t* flags = reinterpret_cast<uint32_t*>(a.ws);
-    if (tid == 0) {
-      const uint32_t old =
-          __hip_atomic_fetch_add(flags + boundary, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = old == 1u;
-    }
-    __syncthreads();
-    if (!s_last) return false;
     const uint32_t base = part_offset(boundary, side ^ 1);
     v4u x[16];
 #pragma unroll

@@ -217,9 +217,10 @@ int dq_quantize_v_fp8(const void* v, int64_t H, int64_t S, void* vt, float* v_sc
  * there are no more tiles than workgroups, each workgroup computes one tile. Otherwise, without a
  * workspace each workgroup computes a contiguous run of whole tiles; with one, the tiles' key
  * blocks are dealt out in equal contiguous runs, so a tile may be cut between two neighbouring
- * workgroups: each part stores its unnormalized fp32 result and (running max, sum) in the
- * workspace, and the part that finishes second merges the two in a fixed order (the result does
- * not depend on timing; it can differ in the last bits from an uncut run). The workspace must
+ * workgroups: the part that finishes first stores its unnormalized fp32 result and (running
+ * max, sum) in the workspace (both do when they finish together), and the part that finishes
+ * second merges the two in a fixed order (the result does not depend on timing; it can differ
+ * in the last bits from an uncut run). The workspace must
  * hold zeros before its first use; every call that completes leaves its counters at zero, so one
  * zero fill at allocation is enough, and one workspace serves calls of any size up to the one it
  * was sized for. Calls that may run concurrently must not share a workspace.
