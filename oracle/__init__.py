@@ -21,6 +21,8 @@ What it computes, and where the pages say so:
   * the QKV projection with query/key normalization and rotary position embedding fused into
     the GEMM's epilogue: page "Accelerarea generarii de imagini cu FLUX 3 Image Klein pe
     GPU-urile Blackwell NVIDIA", the paragraph on the PrimsTS GEMMs (see `qkv.py`).
+  * attention over FP8 queries, keys and values (see `attention.py`) and the block-scaled
+    (MX) FP8 linear layer, the gfx950 analogue of the pages' NVFP4 (see `mx.py`).
 
 The pages do not fix the granularity, the FP8 flavour, the scale formula or the rounding. The
 readings taken are: one scale per token (row of x) and per output channel (row of W); OCP E4M3
@@ -43,6 +45,7 @@ from .linear import EPI_BIAS, EPI_GELU_TANH, EPI_GATED_RESIDUAL, gelu_tanh, line
 from .modulate import LN_EPS, layernorm_modulate, modulate_rows
 from .qkv import (HEAD_DIM, QK_NORM_EPS, linear_qkv_bf16, linear_qkv_ref, qkv_split_norm_rope,
                   rms_norm, rope_pairs)
+from .mx import MX_BLOCK, dequantize_mx, linear_mx_ref, quantize_mx, shared_exponent
 
 __all__ = [
     "E4M3_MAX", "decode_table", "encode_e4m3", "quantize_rows",
@@ -50,4 +53,5 @@ __all__ = [
     "LN_EPS", "layernorm_modulate", "modulate_rows",
     "HEAD_DIM", "QK_NORM_EPS", "linear_qkv_bf16", "linear_qkv_ref", "qkv_split_norm_rope",
     "rms_norm", "rope_pairs",
+    "MX_BLOCK", "dequantize_mx", "linear_mx_ref", "quantize_mx", "shared_exponent",
 ]
