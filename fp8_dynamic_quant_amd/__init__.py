@@ -72,6 +72,10 @@ def lib() -> ctypes.CDLL:
         L.dq_attention_fp8.restype = i32
         L.dq_attention_fp8_workspace_size.argtypes = [i64, i64]
         L.dq_attention_fp8_workspace_size.restype = ctypes.c_uint64
+        L.dq_quantize_mx_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.dq_quantize_mx_fp8.restype = i32
+        L.dq_linear_mx_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp]
+        L.dq_linear_mx_fp8.restype = i32
         L.dq_linear_fp8_workspace_size.argtypes = [i64, i64, i64]
         L.dq_linear_fp8_workspace_size.restype = ctypes.c_uint64
         L.dq_status_string.argtypes = [i32]
@@ -377,8 +381,57 @@ def dq_attention_fp8(q8, q_scale, k8, k_scale, vt8, v_scale, out=None, stream=No
     return out
 
 
+MX_BLOCK = 32
+
+
+def dq_quantize_mx_fp8(x, q=None, scales=None, stream=None):
+    """Block-scaled (MX) FP8 quantization of bf16 x [M, K] (K % 32 == 0): E4M3 codes [M, K] and
+    one E8M0 scale byte per 32 values, [M, K / 32]."""
+    where = "dq_quantize_mx_fp8"
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError(f"{where}: x must be a 2-D tensor")
+    M, K = x.shape
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (M, K), dev)
+    q = torch.empty((M, K), dtype=torch.uint8, device=dev) if q is None else q
+    scales = torch.empty((M, K // MX_BLOCK), dtype=torch.uint8, device=dev) if scales is None \
+        else scales
+    _need(q, "q", torch.uint8, (M, K), dev)
+    _need(scales, "scales", torch.uint8, (M, K // MX_BLOCK), dev)
+    with torch.cuda.device(dev):
+        _check(lib().dq_quantize_mx_fp8(_ptr(x), M, K, _ptr(q), _ptr(scales),
+                                        _stream(stream, dev)), where)
+    return q, scales
+
+
+def dq_linear_mx_fp8(qa, sa, qw, sw, bias=None, epilogue="bias", out=None, stream=None):
+    """Block-scaled FP8 linear layer -> bf16 [M, N]: codes qa [M, K], qw [N, K] and their scale
+    bytes sa [M, K / 32], sw [N, K / 32] (dq_quantize_mx_fp8); epilogue "bias" or "gelu_tanh"."""
+    where = "dq_linear_mx_fp8"
+    if not isinstance(qa, torch.Tensor) or qa.dim() != 2 or not isinstance(qw, torch.Tensor):
+        raise ValueError(f"{where}: qa and qw must be 2-D tensors")
+    M, K = qa.shape
+    N = qw.shape[0]
+    dev = qa.device
+    _need(qa, "qa", torch.uint8, (M, K), dev)
+    _need(qw, "qw", torch.uint8, (N, K), dev)
+    _need(sa, "sa", torch.uint8, (M, K // MX_BLOCK), dev)
+    _need(sw, "sw", torch.uint8, (N, K // MX_BLOCK), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, (N,), dev)
+    if epilogue not in ("bias", "gelu_tanh"):
+        raise ValueError(f"{where}: epilogue must be 'bias' or 'gelu_tanh'")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
+    _need(out, "out", torch.bfloat16, (M, N), dev)
+    with torch.cuda.device(dev):
+        _check(lib().dq_linear_mx_fp8(_ptr(qa), _ptr(sa), M, K, _ptr(qw), _ptr(sw), N,
+                                      _ptr(bias), EPILOGUES[epilogue], _ptr(out),
+                                      _stream(stream, dev)), where)
+    return out
+
+
 __all__ = ["dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
            "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8", "HEAD_DIM",
            "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
-           "quantize_qkv_heads_fp8",
+           "quantize_qkv_heads_fp8", "dq_quantize_mx_fp8", "dq_linear_mx_fp8", "MX_BLOCK",
            "dq_linear_fp8_workspace_size", "DQError", "EPILOGUES", "lib", "LIB_PATH"]

@@ -14,7 +14,8 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdq.so")
-SOURCES = ["csrc/dq_api.cpp", "csrc/quantize.hip", "csrc/gemm_fp8.hip", "csrc/attention.hip"]
+SOURCES = ["csrc/dq_api.cpp", "csrc/quantize.hip", "csrc/gemm_fp8.hip", "csrc/attention.hip",
+           "csrc/gemm_mx.hip"]
 ARCH = "gfx950"
 
 # -O3, no fast-math and no denormal flushing (the quantizer relies on IEEE fp32 division with

@@ -258,6 +258,50 @@ int dq_attention_fp8(const void* q, const float* q_scale, const void* k, const f
       max_workgroups, static_cast<hipStream_t>(stream)));
 }
 
+int dq_quantize_mx_fp8(const void* x, int64_t M, int64_t K, void* q, void* scales,
+                       void* stream) {
+  if (M < 0 || M > kMaxDim || K < 32 || K > kMaxDim || (K % 32) != 0) return DQ_ERR_SHAPE;
+  if (M > 0 && K > kMaxElems / M) return DQ_ERR_SHAPE;
+  if (M == 0) return DQ_OK;
+  if (!x || !q || !scales) return DQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q)) return DQ_ERR_ALIGN;
+  const uint64_t n = static_cast<uint64_t>(M) * static_cast<uint64_t>(K);
+  if (overlap(q, n, x, 2 * n) || overlap(scales, n / 32, x, 2 * n) ||
+      overlap(scales, n / 32, q, n))
+    return DQ_ERR_ALIAS;
+  return hip_status(dq::launch_quantize_mx(static_cast<const uint16_t*>(x), M, K,
+                                           static_cast<uint8_t*>(q),
+                                           static_cast<uint8_t*>(scales),
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int dq_linear_mx_fp8(const void* qa, const void* sa, int64_t M, int64_t K, const void* qw,
+                     const void* sw, int64_t N, const void* bias, int epilogue, void* out,
+                     void* stream) {
+  const int shape = check_linear_shape(M, K, N);
+  if (shape != DQ_OK) return shape;
+  if (epilogue != DQ_EPI_BIAS && epilogue != DQ_EPI_GELU_TANH) return DQ_ERR_EPILOGUE;
+  // one tile per workgroup: the grid must stay within 2^31 workgroups
+  if (((M + 255) / 256) * ((N + 255) / 256) > kMaxDim) return DQ_ERR_SHAPE;
+  if (M == 0) return DQ_OK;
+  if (!qa || !sa || !qw || !sw || !out) return DQ_ERR_NULL;
+  if (!aligned16(qa) || !aligned16(qw) || !aligned16(out) || (bias && !aligned16(bias)) ||
+      (reinterpret_cast<uintptr_t>(sa) & 3u) != 0 || (reinterpret_cast<uintptr_t>(sw) & 3u) != 0)
+    return DQ_ERR_ALIGN;
+  const uint64_t m = static_cast<uint64_t>(M), k = static_cast<uint64_t>(K),
+                 n = static_cast<uint64_t>(N);
+  const uint64_t out_bytes = 2 * m * n;
+  if (overlap(out, out_bytes, qa, m * k) || overlap(out, out_bytes, sa, m * k / 32) ||
+      overlap(out, out_bytes, qw, n * k) || overlap(out, out_bytes, sw, n * k / 32) ||
+      overlap(out, out_bytes, bias, bias ? 2 * n : 0))
+    return DQ_ERR_ALIAS;
+  return hip_status(dq::launch_linear_mx(
+      static_cast<const uint8_t*>(qa), static_cast<const uint8_t*>(sa), M, K,
+      static_cast<const uint8_t*>(qw), static_cast<const uint8_t*>(sw), N,
+      static_cast<const uint16_t*>(bias), epilogue == DQ_EPI_GELU_TANH ? 1 : 0,
+      static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
+}
+
 uint64_t dq_attention_fp8_workspace_size(int64_t H, int64_t S) {
   if (check_attention_shape(H, S) != DQ_OK) return 0;
   return dq::attention_workspace_bytes(H, S);
@@ -285,6 +329,6 @@ const char* dq_status_string(int status) {
 
 int dq_last_hip_error(void) { return g_last_hip_error; }
 
-int dq_abi_version(void) { return 6; }
+int dq_abi_version(void) { return 7; }
 
 }  // extern "C"

@@ -76,4 +76,15 @@ hipError_t launch_attention(const uint8_t* q8, const float* sq, const uint8_t* k
                             hipStream_t stream);
 uint64_t attention_workspace_bytes(int64_t H, int64_t S);
 
+// Block-scaled (MX) FP8 (gemm_mx.hip): E4M3 codes with one E8M0 scale byte per 32 values along K.
+//   launch_quantize_mx: x bf16 [R, K] (K % 32 == 0) -> codes [R, K], scale bytes [R, K / 32]
+//   launch_linear_mx:   codes and scale bytes of A [M, K] and W [N, K] (K % 128 == 0,
+//                       N % 64 == 0), bias bf16 [N] or null, epilogue 0 bias / 1 GELU-tanh ->
+//                       out bf16 [M, N]
+hipError_t launch_quantize_mx(const uint16_t* x, int64_t R, int64_t K, uint8_t* q, uint8_t* scale,
+                              hipStream_t stream);
+hipError_t launch_linear_mx(const uint8_t* qa, const uint8_t* sa, int64_t M, int64_t K,
+                            const uint8_t* qw, const uint8_t* sw, int64_t N, const uint16_t* bias,
+                            int epilogue, uint16_t* out, hipStream_t stream);
+
 }  // namespace dq

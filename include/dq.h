@@ -233,6 +233,44 @@ int dq_attention_fp8(const void* q, const float* q_scale, const void* k, const f
                      void* stream);
 
 /*
+ * dq_quantize_mx_fp8 -- block-scaled (MX) FP8 quantization: every 32 consecutive values of a row
+ * share one power-of-two scale.
+ *
+ * The pages run the linears in NVFP4 on Blackwell, a format with a shared scale per small block
+ * (page "Accelerarea generarii de imagini cu FLUX 3 Image Klein pe GPU-urile Blackwell NVIDIA",
+ * its paragraph on NVFP4 against BF16). The block format gfx950's matrix units execute is the
+ * OCP Microscaling one; its definition with E4M3 elements is the one taken:
+ *   shared exponent e = floor(log2(max |x| of the block)) - 8, clamped to [-127, 127]
+ *                       (-127 for an all-zero block);
+ *   q = E4M3 nearest to x / 2^e (ties to even), magnitudes past 448 saturating to 448;
+ *   scale byte = e + 127 (E8M0).
+ *
+ *   x       bf16 [M, K]       row-major; 32 <= K < 2^31, K % 32 == 0, M K < 2^47
+ *   q       uint8 [M, K]      codes
+ *   scales  uint8 [M, K / 32] scale bytes, row-major
+ * x and q 16-byte aligned; no overlap. Inputs must be finite.
+ */
+int dq_quantize_mx_fp8(const void* x, int64_t M, int64_t K, void* q, void* scales, void* stream);
+
+/*
+ * dq_linear_mx_fp8 -- the block-scaled linear layer on gfx950's scaled FP8 matrix instruction:
+ *
+ *   y[m, n] = sum over blocks b of 2^(ea[m, b] + ew[n, b]) sum_{k in b} dec(qa[m, k]) dec(qw[n, k])
+ *   out[m, n] = bf16(epilogue(y[m, n] + bias[n]))      accumulation in fp32, one rounding
+ *
+ *   qa, sa   codes [M, K] and scale bytes [M, K / 32] of the activations (dq_quantize_mx_fp8)
+ *   qw, sw   codes [N, K] and scale bytes [N, K / 32] of the weights (the same routine)
+ *   bias     bf16 [N] or NULL;  epilogue DQ_EPI_BIAS or DQ_EPI_GELU_TANH
+ *   out      bf16 [M, N]
+ * Requirements: as dq_linear_fp8 (128 <= K < 2^24, K % 128 == 0, N % 64 == 0); codes, bias and
+ * out 16-byte aligned, scale arrays 4-byte aligned; out overlapping no input. One workgroup per
+ * 256 x 256 output tile.
+ */
+int dq_linear_mx_fp8(const void* qa, const void* sa, int64_t M, int64_t K, const void* qw,
+                     const void* sw, int64_t N, const void* bias, int epilogue, void* out,
+                     void* stream);
+
+/*
  * dq_attention_fp8_workspace_size -- bytes of workspace dq_attention_fp8 may use for H heads of
  * S tokens, or 0 if the sizes break its requirements: 4 KiB of counters plus two 198 KiB partial
  * results per workgroup boundary, for at most min(H ceil(S / 384), 256) workgroups (at most
@@ -288,7 +326,7 @@ const char* dq_status_string(int status);
 /* The hipError_t behind the most recent DQ_ERR_HIP returned on the calling thread (0 if none). */
 int dq_last_hip_error(void);
 
-/* ABI version of this header (currently 6). */
+/* ABI version of this header (currently 7). */
 int dq_abi_version(void);
 
 #ifdef __cplusplus

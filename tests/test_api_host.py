@@ -35,6 +35,8 @@ def lib():
                                    i64, vp]
     L.dq_attention_fp8_workspace_size.argtypes = [i64, i64]
     L.dq_attention_fp8_workspace_size.restype = ctypes.c_uint64
+    L.dq_quantize_mx_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.dq_linear_mx_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp]
     L.dq_linear_fp8_workspace_size.argtypes = [i64, i64, i64]
     L.dq_linear_fp8_workspace_size.restype = ctypes.c_uint64
     L.dq_status_string.restype = ctypes.c_char_p
@@ -52,6 +54,7 @@ def test_header_declares_the_entry_points():
     for n in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
               "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8",
               "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
+              "dq_quantize_mx_fp8", "dq_linear_mx_fp8",
               "dq_linear_fp8_workspace_size", "dq_status_string", "dq_last_hip_error",
               "dq_abi_version"):
         assert n in names
@@ -63,7 +66,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dq_abi_version() == 6
+    assert lib.dq_abi_version() == 7
     for st in range(9):
         s = lib.dq_status_string(st)
         assert s and len(s) > 1
@@ -284,6 +287,48 @@ def test_attention_workspace(lib):
     assert lib.dq_last_hip_error() == 0
 
 
+MX_X, MX_Q, MX_S, MX_W, MX_SW, MX_O = (0x20000000 * i for i in range(40, 46))   # fake, far apart
+
+
+def test_quantize_mx_argument_checks(lib):
+    f = lib.dq_quantize_mx_fp8
+    assert f(MX_X, 0, 64, MX_Q, MX_S, None) == OK                # empty
+    assert f(MX_X, 4, 48, MX_Q, MX_S, None) == SHAPE             # K % 32
+    assert f(MX_X, 4, 16, MX_Q, MX_S, None) == SHAPE             # K < 32
+    assert f(MX_X, -1, 64, MX_Q, MX_S, None) == SHAPE
+    assert f(None, 4, 64, MX_Q, MX_S, None) == NULL
+    assert f(MX_X, 4, 64, None, MX_S, None) == NULL
+    assert f(MX_X, 4, 64, MX_Q, None, None) == NULL
+    assert f(MX_X + 8, 4, 64, MX_Q, MX_S, None) == ALIGN
+    assert f(MX_X, 4, 64, MX_Q + 8, MX_S, None) == ALIGN
+    assert f(MX_X, 4, 64, MX_X + 256, MX_S, None) == ALIAS       # codes inside x
+    assert f(MX_X, 4, 64, MX_Q, MX_Q + 16, None) == ALIAS        # scales inside the codes
+    assert lib.dq_last_hip_error() == 0
+
+
+def mxlin(lib, M=64, K=256, N=128, qa=MX_Q, sa=MX_S, qw=MX_W, sw=MX_SW, bias=None, epi=0, out=MX_O):
+    return lib.dq_linear_mx_fp8(qa, sa, M, K, qw, sw, N, bias, epi, out, None)
+
+
+def test_linear_mx_argument_checks(lib):
+    assert mxlin(lib, M=0) == OK
+    assert mxlin(lib, K=96) == SHAPE                             # K % 128
+    assert mxlin(lib, K=1 << 24) == SHAPE
+    assert mxlin(lib, N=96) == SHAPE                             # N % 64
+    assert mxlin(lib, M=-1) == SHAPE
+    assert mxlin(lib, epi=2) == EPI                              # gated residual: not offered
+    assert mxlin(lib, epi=7) == EPI
+    for name in ("qa", "sa", "qw", "sw", "out"):
+        assert mxlin(lib, **{name: None}) == NULL, name
+    assert mxlin(lib, qa=MX_Q + 8) == ALIGN
+    assert mxlin(lib, sa=MX_S + 2) == ALIGN                      # scale dwords: 4-byte aligned
+    assert mxlin(lib, out=MX_O + 8) == ALIGN
+    assert mxlin(lib, bias=MX_O + 0x100000 + 8) == ALIGN
+    assert mxlin(lib, out=MX_Q) == ALIAS                         # output over the codes
+    assert mxlin(lib, out=MX_SW - 64) == ALIAS                   # output into the weight scales
+    assert lib.dq_last_hip_error() == 0
+
+
 def test_quantize_v_argument_checks(lib):
     f = lib.dq_quantize_v_fp8
     V, VT, SV = 0x30000000, 0x40000000, 0x50000000
@@ -335,9 +380,9 @@ def test_python_binding_names_match_the_c_entry_points():
     for name in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
                  "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8",
                  "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
-                 "dq_linear_fp8_workspace_size"):
+                 "dq_quantize_mx_fp8", "dq_linear_mx_fp8", "dq_linear_fp8_workspace_size"):
         assert callable(getattr(dq, name))
-    assert dq.lib().dq_abi_version() == 6
+    assert dq.lib().dq_abi_version() == 7
     assert dq.dq_linear_fp8_workspace_size(4608, 3072, 12288) == 3584 + 1024 * 262144
 
 
