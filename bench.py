@@ -38,6 +38,7 @@ KERNEL_SOURCES = {
     "ln_modulate": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "quantize.hip"),
     "qkv": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "gemm_fp8.hip"),
     "attention": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "attention.hip"),
+    "mx_linear": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "gemm_mx.hip"),
 }
 
 
@@ -308,6 +309,70 @@ def bench_attention(steps, warmup, n_sets, H=24, S=4608, seed=11):
             "H": H, "S": S}
 
 
+def bench_mx(shape, seed, steps, warmup, n_sets):
+    """The block-scaled (MX) FP8 path on the benchmark linear's shape: per-32 block quantization
+    of the activations, then the GEMM on the scaled FP8 matrix instruction, weights quantized
+    once; the per-row FP8 GEMM on the same inputs is timed beside it. Event pairs around each
+    call; returns microseconds per call."""
+    import torch
+    import fp8_dynamic_quant_amd as dq
+    from workloads import make_linear_inputs
+
+    dev = torch.device("cuda:0")
+    M, K, N = shape.M, shape.K, shape.N
+    inp = make_linear_inputs(shape, seed)
+    epi = "gelu_tanh" if shape.epilogue == "gelu_tanh" else "bias"
+    wb = to_dev_bf16(torch, inp.w, dev)
+    qw, sw = dq.dq_quantize_mx_fp8(wb)
+    rq, rs = dq.dq_quantize_weight_fp8(wb)
+    bias = to_dev_bf16(torch, inp.bias, dev)
+    xb = to_dev_bf16(torch, inp.x, dev)
+    sets = []
+    for i in range(n_sets):
+        x = xb if i == 0 else (xb * (1.0 + 0.01 * i)).to(torch.bfloat16)
+        qa, sa = dq.dq_quantize_mx_fp8(x)
+        q8, s8 = dq.dq_quantize_fp8(x)
+        sets.append({"x": x, "qa": qa, "sa": sa, "q8": q8, "s8": s8,
+                     "out": torch.empty((M, N), dtype=torch.bfloat16, device=dev)})
+    torch.cuda.synchronize()
+
+    def timed(fn, n):
+        for i in range(warmup):
+            fn(sets[i % n_sets])
+        torch.cuda.synchronize()
+        evs = []
+        for i in range(n):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn(sets[i % n_sets])
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+
+    gemm = timed(lambda st: dq.dq_linear_mx_fp8(st["qa"], st["sa"], qw, sw, bias, epi,
+                                                out=st["out"]), steps)
+    # the quantizer (a few microseconds) as back-to-back launches, one event pair around the loop
+    n_q = 4 * steps
+    for i in range(warmup):
+        dq.dq_quantize_mx_fp8(sets[i % n_sets]["x"], sets[i % n_sets]["qa"], sets[i % n_sets]["sa"])
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n_q):
+        dq.dq_quantize_mx_fp8(sets[i % n_sets]["x"], sets[i % n_sets]["qa"], sets[i % n_sets]["sa"])
+    e1.record()
+    torch.cuda.synchronize()
+    quant = e0.elapsed_time(e1) * 1e3 / n_q
+    rowwise = timed(lambda st: dq.dq_linear_fp8(st["q8"], st["s8"], rq, rs, bias, epi,
+                                                out=st["out"]), steps)
+    return {"gemm_us": gemm, "quant_us": quant, "rowwise_us": rowwise,
+            "flops": 2 * M * N * K, "shape": [M, K, N], "epilogue": epi,
+            "quant_bytes": M * K * 2 + M * K + M * K // 32}
+
+
 def bench_dit_step(steps, warmup):
     """All linears of one 1024^2 FLUX-dev denoising step (228 quantize + GEMM pairs), distinct
     weights per block, timed end to end as one sequence on one stream."""
@@ -425,6 +490,7 @@ def main():
     ap.add_argument("--no-modulate", action="store_true")
     ap.add_argument("--no-qkv", action="store_true")
     ap.add_argument("--no-attention", action="store_true")
+    ap.add_argument("--no-mx", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB plain copy first (reference for HBM counters)")
@@ -575,6 +641,29 @@ def main():
             "algorithmic_flop_per_launch": at["flops"],
             "qkv_quantization_us": round(at["quant_us"], 2),
             "torch_bf16_sdpa_us": round(at["sdpa_us"], 2),
+        }
+    if not args.no_mx:
+        mx = bench_mx(shape, w.seed, args.steps, min(args.warmup, 100), min(args.sets, 4))
+        tf = mx["flops"] / mx["gemm_us"] / 1e6
+        gbq = mx["quant_bytes"] / mx["quant_us"] / 1e3
+        log(f"MX (block-scaled) FP8 {mx['shape']} {mx['epilogue']}: GEMM {mx['gemm_us']:.1f} us "
+            f"({tf:.0f} TFLOP/s), quantizer {mx['quant_us']:.1f} us ({gbq:.0f} GB/s); per-row FP8 "
+            f"GEMM {mx['rowwise_us']:.1f} us")
+        res["mx_linear"] = {
+            "kernel": "gemm_mx<%s>" % mx["epilogue"],
+            "timing": "HIP events around each call, rotating inputs",
+            "shape": mx["shape"], "epilogue": mx["epilogue"],
+            "bound": "mfma",
+            "achieved": round(tf, 1),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+            "traffic": stored_traffic("mx_linear", w.name),
+            "avg_launch_us": round(mx["gemm_us"], 2),
+            "algorithmic_flop_per_launch": mx["flops"],
+            "quantizer_us": round(mx["quant_us"], 2),
+            "quantizer_gbps": round(gbq, 1),
+            "rowwise_fp8_gemm_us": round(mx["rowwise_us"], 2),
         }
     if not args.no_dit:
         log("DiT step: generating 228 distinct FP8 weights on the device")

@@ -11,7 +11,8 @@
 //   element = E4M3 nearest (ties to even) to x / 2^shared, saturating at 448,
 //   scale byte = shared + 127.
 //
-// quant_mx_rows: a thread takes 8 values (16 bytes); the 4 threads of a block are a DPP quad.
+// quant_mx_rows: a thread takes 8 values (16 bytes) at a time, four chunks in flight; the 4
+// threads of a block are a DPP quad.
 // The block's amax is a bf16, so floor(log2(amax)) is its exponent field minus 127 (a zero or
 // subnormal amax has field 0 and clamps to -127): the scale byte is max(field - 8, 0). x / 2^shared
 // is a product by a power of two, exact in fp32 (below 2^-126 it may round, far under half of
@@ -73,24 +74,38 @@ __device__ __forceinline__ uint32_t encode4(uint32_t w0, uint32_t w1, float y) {
   return (uint32_t)r;
 }
 
+// Thread t of a workgroup takes the 16-byte chunks u = 1024 b + 256 i + t, i = 0..3 (four loads
+// in flight); the 4 threads of an MX block are a DPP quad.
+constexpr int kQuantUnroll = 4;
+
 __global__ void __launch_bounds__(256) quant_mx_rows(const uint16_t* __restrict__ x, int64_t n8,
                                                      uint8_t* __restrict__ q,
                                                      uint8_t* __restrict__ scale) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const bool live = t < n8;  // n8 is a multiple of 4: a quad is live or not as a whole
-  const uint4 v = live ? reinterpret_cast<const uint4*>(x)[t] : make_uint4(0u, 0u, 0u, 0u);
-  uint32_t mx = absmax_pair(absmax_pair(absmax_pair(absmax_pair(0u, v.x), v.y), v.z), v.w);
-  uint32_t m = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
-  uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false);
-  m = m > o ? m : o;
-  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false);
-  m = m > o ? m : o;
-  if (!live) return;
-  const uint32_t field = (m >> 7) & 0xFFu;            // bf16 exponent field of the block amax
-  const uint32_t byte = field > 8u ? field - 8u : 0u;  // shared + 127
-  const float y = __uint_as_float((254u - byte) << 23);  // 2^-shared (byte <= 246 for bf16)
-  reinterpret_cast<uint2*>(q)[t] = make_uint2(encode4(v.x, v.y, y), encode4(v.z, v.w, y));
-  if ((threadIdx.x & 3) == 0) scale[t >> 2] = (uint8_t)byte;
+  const int64_t base = (int64_t)blockIdx.x * (256 * kQuantUnroll) + threadIdx.x;
+  uint4 v[kQuantUnroll];
+#pragma unroll
+  for (int i = 0; i < kQuantUnroll; ++i) {
+    const int64_t t = base + 256 * i;  // n8 is a multiple of 4: a quad is live or not as a whole
+    v[i] = t < n8 ? reinterpret_cast<const uint4*>(x)[t] : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int i = 0; i < kQuantUnroll; ++i) {
+    const int64_t t = base + 256 * i;
+    uint32_t mx = absmax_pair(absmax_pair(absmax_pair(absmax_pair(0u, v[i].x), v[i].y), v[i].z),
+                              v[i].w);
+    uint32_t m = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
+    uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false);
+    m = m > o ? m : o;
+    o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false);
+    m = m > o ? m : o;
+    if (t >= n8) continue;
+    const uint32_t field = (m >> 7) & 0xFFu;            // bf16 exponent field of the block amax
+    const uint32_t byte = field > 8u ? field - 8u : 0u;  // shared + 127
+    const float y = __uint_as_float((254u - byte) << 23);  // 2^-shared (byte <= 246 for bf16)
+    reinterpret_cast<uint2*>(q)[t] =
+        make_uint2(encode4(v[i].x, v[i].y, y), encode4(v[i].z, v[i].w, y));
+    if ((threadIdx.x & 3) == 0) scale[t >> 2] = (uint8_t)byte;
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -233,17 +248,18 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mx(MxArgs a) {
     for (int i = 0; i < 4; ++i) sa4[i] = sc[wm * 128 + 32 * i + (l & 31)] >> (8 * hi);
 #pragma unroll
     for (int i = 0; i < 2; ++i) sw2[i] = sc[kTM + wn * 64 + 32 * i + (l & 31)] >> (8 * hi);
+    // both K halves' fragments first (their reads overlap), then the 16 matrix ops
+    v8i fa[2][4], fw[2][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int c0 = 4 * h + hi;  // chunks c0 (registers 0-3) and c0 + 2 (registers 4-7)
-      v8i fa[4], fw[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = wm * 128 + 32 * i + (l & 31);
         const uint4 lo = *reinterpret_cast<const uint4*>(st + r * kTK + swz(r, c0) * 16);
         const uint4 up = *reinterpret_cast<const uint4*>(st + r * kTK + swz(r, c0 + 2) * 16);
-        fa[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                      (int)up.x, (int)up.y, (int)up.z, (int)up.w};
+        fa[h][i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                         (int)up.x, (int)up.y, (int)up.z, (int)up.w};
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -251,21 +267,23 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mx(MxArgs a) {
         const uint8_t* wt = st + kTileBytes;
         const uint4 lo = *reinterpret_cast<const uint4*>(wt + r * kTK + swz(r, c0) * 16);
         const uint4 up = *reinterpret_cast<const uint4*>(wt + r * kTK + swz(r, c0 + 2) * 16);
-        fw[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                      (int)up.x, (int)up.y, (int)up.z, (int)up.w};
+        fw[h][i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                         (int)up.x, (int)up.y, (int)up.z, (int)up.w};
       }
-#pragma unroll
-      for (int bn = 0; bn < 2; ++bn)
-#pragma unroll
-        for (int bm = 0; bm < 4; ++bm) {
-          if (h == 0)
-            acc[bn][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                fw[bn], fa[bm], acc[bn][bm], 0, 0, 0, (int)sw2[bn], 0, (int)sa4[bm]);
-          else
-            acc[bn][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                fw[bn], fa[bm], acc[bn][bm], 0, 0, 2, (int)sw2[bn], 2, (int)sa4[bm]);
-        }
     }
+    // the byte select (2h) is an immediate of the instruction
+#pragma unroll
+    for (int bn = 0; bn < 2; ++bn)
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+        acc[bn][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            fw[0][bn], fa[0][bm], acc[bn][bm], 0, 0, 0, (int)sw2[bn], 0, (int)sa4[bm]);
+#pragma unroll
+    for (int bn = 0; bn < 2; ++bn)
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+        acc[bn][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            fw[1][bn], fa[1][bm], acc[bn][bm], 0, 0, 2, (int)sw2[bn], 2, (int)sa4[bm]);
   }
 
   // epilogue: lane holds output row m (its column in the instruction's layout) and columns
@@ -321,8 +339,9 @@ hipError_t launch_quantize_mx(const uint16_t* x, int64_t R, int64_t K, uint8_t* 
                               hipStream_t stream) {
   const int64_t n8 = R * K / 8;
   if (n8 == 0) return hipSuccess;
-  hipLaunchKernelGGL(quant_mx_rows, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, x,
-                     n8, q, scale);
+  const int64_t per_wg = 256 * kQuantUnroll;
+  hipLaunchKernelGGL(quant_mx_rows, dim3((unsigned)((n8 + per_wg - 1) / per_wg)), dim3(256), 0,
+                     stream, x, n8, q, scale);
   return hipGetLastError();
 }
 
