@@ -287,48 +287,55 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mx(MxArgs a) {
   }
 
   // epilogue: lane holds output row m (its column in the instruction's layout) and columns
-  // 32 bn + 8 g + 4 hi + j of the wave's 64
+  // 32 bn + 8 g + 4 hi + j of the wave's 64. The four 16-byte stores that cover a row's 64
+  // columns (one 128-byte line) are issued back to back.
+  float bv[2][2][8];
 #pragma unroll
-  for (int bn = 0; bn < 2; ++bn) {
-    const int nb = n0 + wn * 64 + 32 * bn;
-    if (nb >= a.N) continue;  // N is a multiple of 64: a wave's columns are all in or all out
+  for (int bn = 0; bn < 2; ++bn)
 #pragma unroll
     for (int gp = 0; gp < 2; ++gp) {
-      const int n = nb + 16 * gp + 8 * hi;
-      float bv[8];
-      if (a.bias) {
+      const int n = n0 + wn * 64 + 32 * bn + 16 * gp + 8 * hi;
+      if (a.bias && n < a.N) {
         const uint4 b4 = *reinterpret_cast<const uint4*>(a.bias + n);
         const uint32_t bw[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          bv[2 * j] = __uint_as_float(bw[j] << 16);
-          bv[2 * j + 1] = __uint_as_float(bw[j] & 0xFFFF0000u);
+          bv[bn][gp][2 * j] = __uint_as_float(bw[j] << 16);
+          bv[bn][gp][2 * j + 1] = __uint_as_float(bw[j] & 0xFFFF0000u);
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bv[j] = 0.0f;
+        for (int j = 0; j < 8; ++j) bv[bn][gp][j] = 0.0f;
       }
+    }
+  // N is a multiple of 64: a wave's 64 columns are all in or all out
+  if (n0 + wn * 64 < a.N) {
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm) {
-        const int m = m0 + wm * 128 + 32 * bm + (l & 31);
-        float v0[4], v1[4];
+    for (int bm = 0; bm < 4; ++bm) {
+      const int m = m0 + wm * 128 + 32 * bm + (l & 31);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v0[j] = acc[bn][bm][(2 * gp) * 4 + j];
-          v1[j] = acc[bn][bm][(2 * gp + 1) * 4 + j];
-          swap_halves(v0[j], v1[j]);
+      for (int bn = 0; bn < 2; ++bn)
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+          const int n = n0 + wn * 64 + 32 * bn + 16 * gp + 8 * hi;
+          float v0[4], v1[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v0[j] = acc[bn][bm][(2 * gp) * 4 + j];
+            v1[j] = acc[bn][bm][(2 * gp + 1) * 4 + j];
+            swap_halves(v0[j], v1[j]);
+          }
+          float y[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            y[j] += bv[bn][gp][j];
+            if (EPI == 1) y[j] = gelu_tanh(y[j]);
+          }
+          if (m < a.M)
+            *reinterpret_cast<uint4*>(a.out + (size_t)m * (size_t)a.N + n) =
+                make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]),
+                           pack_bf16(y[6], y[7]));
         }
-        float y[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          y[j] += bv[j];
-          if (EPI == 1) y[j] = gelu_tanh(y[j]);
-        }
-        if (m < a.M)
-          *reinterpret_cast<uint4*>(a.out + (size_t)m * (size_t)a.N + n) =
-              make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]),
-                         pack_bf16(y[6], y[7]));
-      }
     }
   }
 }
