@@ -119,6 +119,14 @@ def test_mlp_up_full_size_sampled_rows():
     _end_to_end(4608, 3072, 12288, "gelu_tanh", seed=3, rows=rows)
 
 
+def test_more_tiles_than_compute_units_ragged():
+    """4608 x 3648 (18 x 15 tiles, the last tile column 64 wide): more tiles than compute units,
+    so workgroups of the second round take the tiles of the last tile rows."""
+    rows = np.unique(np.concatenate([[0, 4095, 4096, 4607],
+                                     np.random.default_rng(6).choice(4608, 44, replace=False)]))
+    _end_to_end(4608, 256, 3648, "bias", seed=4, rows=rows)
+
+
 def _small_codes(rng, shape):
     """Codes of values in [1, 2) with random signs."""
     mant = rng.integers(0, 8, size=shape)
