@@ -246,6 +246,40 @@ def test_full_rounds_then_cut_tiles_sampled_rows(M, K, N, epi):
         _end_to_end(shape, seed=3000 + M + N, rows=rows, ws=ws)
 
 
+# The longest K the linear layer accepts is below 2^24 (a 256-row operand tile stays within one
+# 32-bit buffer range); 131070 K steps of 128 (= 2 3 5 17 257) also let a tile be cut into 2, 3,
+# 5 or 6 parts.
+K_LONGEST = 131070 * 128
+
+
+def _chunked_ref(contract_chunk, K, chunk):
+    """Sum of the oracle's float64 values over K chunks (the layer is linear in each K range; the
+    oracle's exact contraction takes at most 131072 terms per call)."""
+    ref = None
+    for k0 in range(0, K, chunk):
+        part = contract_chunk(k0, min(K, k0 + chunk))
+        ref = part if ref is None else ref + part
+    return ref
+
+
+def test_longest_k():
+    """M = 3, K = 16776960, N = 64 (one tile, 131070 K steps): whole tile and cut into parts,
+    random codes, power-of-two scales, against the oracle summed over K chunks."""
+    rng = np.random.default_rng(31)
+    M, K, N = 3, K_LONGEST, 64
+    q = rng.integers(0, 256, size=(M, K), dtype=np.uint8)
+    qw = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x01
+    qw[(qw & 0x7F) == 0x7F] = 0x02
+    sa = np.ldexp(1.0, rng.integers(-12, -6, M)).astype(np.float32)
+    sw = np.ldexp(1.0, rng.integers(-12, -6, N)).astype(np.float32)
+    announce(f"linear longest K {M}x{K}x{N}")
+    ref = _chunked_ref(lambda a, b: linear_ref(q[:, a:b], sa, qw[:, a:b], sw), K, 131072)
+    for ws in WS:
+        got = dev_to_f64(_run_linear(q, sa, qw, sw, None, "bias", ws=ws))
+        assert_within_tolerance(got, ref, what=f"longest K workspace={ws}")
+
+
 def test_deterministic_and_m_zero():
     shape = LinearShape("det", 513, 768, 640, "gelu_tanh", 8, 30.0)
     inp = make_linear_inputs(shape, 5)

@@ -127,6 +127,28 @@ def test_more_tiles_than_compute_units_ragged():
     _end_to_end(4608, 256, 3648, "bias", seed=4, rows=rows)
 
 
+def test_longest_k():
+    """M = 3, K = 16776960 (the longest the layer accepts: 131070 steps of 128), N = 64: random
+    codes and scale bytes 127 +- 6, against the oracle summed over K chunks of 131072."""
+    rng = np.random.default_rng(32)
+    M, K, N = 3, 131070 * 128, 64
+    q = rng.integers(0, 256, size=(M, K), dtype=np.uint8)
+    qw = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x01
+    qw[(qw & 0x7F) == 0x7F] = 0x02
+    s = (127 + rng.integers(-6, 7, (M, K // 32))).astype(np.uint8)
+    sw = (127 + rng.integers(-6, 7, (N, K // 32))).astype(np.uint8)
+    announce(f"mx longest K {M}x{K}x{N}")
+    out = dev_to_f64(_linear(q, s, qw, sw, None, "bias"))
+    ref = None
+    for k0 in range(0, K, 131072):
+        k1 = min(K, k0 + 131072)
+        part = linear_mx_ref(q[:, k0:k1], s[:, k0 // 32:k1 // 32], qw[:, k0:k1],
+                             sw[:, k0 // 32:k1 // 32])
+        ref = part if ref is None else ref + part
+    assert_within_tolerance(out, ref, what="mx longest K")
+
+
 def _small_codes(rng, shape):
     """Codes of values in [1, 2) with random signs."""
     mant = rng.integers(0, 8, size=shape)

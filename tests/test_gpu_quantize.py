@@ -140,7 +140,7 @@ def test_edge_rows():
 
 
 @pytest.mark.parametrize("M,K", [(1, 8), (3, 24), (5, 520), (7, 1000), (4, 4104), (9, 512),
-                                 (13, 16392), (2, 24576), (33, 12288)])
+                                 (13, 16392), (2, 24576), (33, 12288), (2, (1 << 24) + 8)])
 def test_ragged_shapes(M, K):
     x = make_rows(M, K, seed=M * 7 + K, n_outliers=max(1, K // 100))
     _assert_same(x, f"ragged {M}x{K}")
