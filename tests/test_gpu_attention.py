@@ -69,8 +69,14 @@ def _check(q16, k16, v16, what, rows=None, **kw):
     assert np.array_equal(gvt, v8.transpose(0, 2, 1)), "value codes differ"
     assert np.array_equal(gsv.view(np.uint32), sv.view(np.uint32))
     rows = np.arange(S) if rows is None else np.asarray(rows)
+    _assert_attention(o[rows].transpose(1, 0, 2), q8, sq, k8, sk, v8, sv, rows, what)
+    return o
+
+
+def _assert_attention(got, q8, sq, k8, sk, v8, sv, rows, what):
+    """got [H, n, D]: the outputs of queries `rows` against the oracle's attention of the oracle's
+    codes (q8, sq, k8, sk, v8, sv of those H heads), within the bound of the module docstring."""
     ref = attention_ref(q8[:, rows], sq[:, rows], k8, sk, v8, sv)        # [H, n, D]
-    got = o[rows].transpose(1, 0, 2)                                     # [S, H, D] -> [H, n, D]
     table = decode_table()
     qd = table[q8[:, rows]] * sq[:, rows, None].astype(np.float64)
     kd = table[k8] * sk[..., None].astype(np.float64)
@@ -89,7 +95,35 @@ def _check(q16, k16, v16, what, rows=None, **kw):
     rel = np.sqrt(np.mean((got - ref) ** 2) / np.mean(ref ** 2))
     print(f"[{what}] worst err/bound {np.max(err / bound):.3f}, rms error / rms output {rel:.2e}, "
           f"max eps {eps.max():.2e}")
-    return o
+
+
+def test_offsets_past_two_gigabytes():
+    """256 heads x 65536 tokens: the codes of the last head start 2^31 - 2^23 bytes in, so its
+    key, value and output addresses pass 2^31. Inputs drawn on the device from a seeded
+    generator; the first and last heads' codes and scales against the oracle's quantization of
+    those heads, and 6 sampled queries of each against the oracle's attention."""
+    H, S = 256, 65536
+    announce(f"attention offsets past 2 GiB H={H} S={S}")
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(77)
+    x16 = [torch.randn((H, S, D), generator=g, device="cuda:0").to(torch.bfloat16)
+           for _ in range(3)]
+    q8, sq, k8, sk, vt, sv = dq.quantize_qkv_heads_fp8(*x16)
+    o = dq.dq_attention_fp8(q8, sq, k8, sk, vt, sv)
+    torch.cuda.synchronize()
+    heads = [0, H - 1]
+    rows = np.array([0, 1, 4095, 32768, S - 385, S - 1])
+    got = o[torch.as_tensor(rows, device="cuda:0")][:, heads].float().cpu().numpy()
+    got = got.astype(np.float64).transpose(1, 0, 2)                      # [2, n, D]
+    bits = [x[heads].view(torch.int16).cpu().numpy().view(np.uint16) for x in x16]
+    (oq, osq), (ok, osk), (ov, osv) = (quantize_heads(bf16_bits_to_f32(b)) for b in bits)
+    assert np.array_equal(q8[heads].cpu().numpy(), oq)
+    assert np.array_equal(sq[heads].cpu().numpy().view(np.uint32), osq.view(np.uint32))
+    assert np.array_equal(k8[heads].cpu().numpy(), ok)
+    assert np.array_equal(sk[heads].cpu().numpy().view(np.uint32), osk.view(np.uint32))
+    assert np.array_equal(vt[heads].cpu().numpy(), ov.transpose(0, 2, 1)), "value codes differ"
+    assert np.array_equal(sv[heads].cpu().numpy().view(np.uint32), osv.view(np.uint32))
+    _assert_attention(got, oq, osq, ok, osk, ov, osv, rows, "offsets past 2 GiB")
 
 
 @pytest.mark.parametrize("H,S", [(1, 16), (2, 48), (1, 64), (2, 80), (3, 128), (2, 144),
