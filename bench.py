@@ -2,18 +2,24 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one pass of the hot path over one batch: per-token FP8 quantization of the bf16
-activations (dq_quantize_fp8) followed by the FP8 GEMM with its fused epilogue (dq_linear_fp8).
-Weights are quantized once, off the timed path. Inputs are seeded synthetic tensors of the
-workload's shapes, resident in HBM before timing starts; several buffer sets rotate so that the
-256 MB last-level cache does not hold a step's inputs. The default warm-up (300 untimed steps)
-brings the chip to the steady clock it holds under this load before the timed steps.
+The default workload is the whole linear sequence of one 1024^2 FLUX-dev denoising step: 228
+dynamically quantized linears (19 double-stream blocks with an image and a text stream, 38
+single-stream blocks), each a per-token FP8 quantization of its bf16 activations
+(dq_quantize_fp8) followed by the FP8 GEMM with its fused epilogue (dq_linear_fp8), with distinct
+weights per block (8.6 GB of FP8 codes, quantized once off the timed path). A step is one pass
+over that sequence; W untimed steps, then K timed steps between two HIP events on the stream.
+`value` is the step's TFLOP/s; `roofline` is the step's dominant kernel, the GEMM of the
+single-stream blocks' first linear (4608 x 3072 -> 21504), timed by event pairs around each of
+its calls in the timed steps.
 
-Prints one JSON line: whole-step throughput (TFLOP/s), the GEMM kernel against the FP8 matrix
-peak, the quantize kernel and the fused LayerNorm + modulation + quantize kernel against HBM
-bandwidth, the attention input projection with its fused query/key norm + rotary epilogue, the
-linears of a full FLUX-dev denoising step
-(ms), and the CPU oracle timed on the host as a baseline.
+After the headline, one leg per further configuration (the tiny linear, the MLP up-projection at
+1024^2 and at 2048^2, the single-stream block pair), each quantize + GEMM over rotating buffer
+sets; then the fused kernels (LayerNorm + modulation + quantize, the QKV projection with its
+norm + rotary epilogue, FP8 attention, the block-scaled FP8 GEMM); then the CPU oracle timed on
+the host on a bounded sample of the step, and on the four single configurations whole.
+Every input is a seeded synthetic tensor resident in HBM before timing starts.
+
+Prints one JSON line.
 """
 import argparse
 import hashlib
@@ -76,10 +82,9 @@ def bench_linear(shape, seed, steps, warmup, n_sets):
     """Time `steps` steps of quantize + linear. Returns a dict of timings."""
     import torch
     import fp8_dynamic_quant_amd as dq
-    from workloads import make_linear_inputs
 
     dev = torch.device("cuda:0")
-    inp = make_linear_inputs(shape, seed)
+    inp = linear_inputs(shape, seed)
     M, K, N = shape.M, shape.K, shape.N
     gated = shape.epilogue == "gated_residual"
     sets = []
@@ -316,11 +321,10 @@ def bench_mx(shape, seed, steps, warmup, n_sets):
     call; returns microseconds per call."""
     import torch
     import fp8_dynamic_quant_amd as dq
-    from workloads import make_linear_inputs
 
     dev = torch.device("cuda:0")
     M, K, N = shape.M, shape.K, shape.N
-    inp = make_linear_inputs(shape, seed)
+    inp = linear_inputs(shape, seed)
     epi = "gelu_tanh" if shape.epilogue == "gelu_tanh" else "bias"
     wb = to_dev_bf16(torch, inp.w, dev)
     qw, sw = dq.dq_quantize_mx_fp8(wb)
@@ -373,9 +377,38 @@ def bench_mx(shape, seed, steps, warmup, n_sets):
             "quant_bytes": M * K * 2 + M * K + M * K // 32}
 
 
-def bench_dit_step(steps, warmup):
+def linear_bytes(M, K, N, epilogue):
+    """Compulsory HBM bytes of one FP8 GEMM + epilogue: both code matrices, the bf16 output, the
+    scales, bias (and gate + residual when gated)."""
+    b = M * K + N * K + 2 * M * N + 4 * M + 4 * N + 2 * N
+    if epilogue == "gated_residual":
+        b += 2 * M * N + 2 * N
+    return b
+
+
+def quantizer_bytes(M, K):
+    """Algorithmic bytes of one per-row quantization: read bf16, write codes and fp32 scales."""
+    return 3 * M * K + 4 * M
+
+
+def dit_floor_ms(w):
+    """Roofline floor of one step: per linear max(FLOP / FP8 peak, bytes / HBM), plus every
+    quantizer's bytes at HBM bandwidth."""
+    t = 0.0
+    for l, r in zip(w.linears, w.repeat):
+        t += r * max(l.flops / (PEAK_FP8_TFLOPS * 1e12),
+                     linear_bytes(l.M, l.K, l.N, l.epilogue) / (PEAK_HBM_GBPS * 1e9))
+        t += r * quantizer_bytes(l.M, l.K) / (PEAK_HBM_GBPS * 1e9)
+    return t * 1e3
+
+
+def bench_dit_step(steps, warmup, breakdown_steps=2, focus="single.linear1"):
     """All linears of one 1024^2 FLUX-dev denoising step (228 quantize + GEMM pairs), distinct
-    weights per block, timed end to end as one sequence on one stream."""
+    weights per block, timed end to end as one sequence on one stream.
+
+    The timed steps carry one HIP event pair around each GEMM call of the `focus` linear (the
+    step's dominant kernel), on the stream the kernels run on. After them, `breakdown_steps`
+    further steps carry event pairs around every call, for the per-linear table."""
     import torch
     import fp8_dynamic_quant_amd as dq
     from workloads import dit_step_device_inputs, workload
@@ -394,11 +427,21 @@ def bench_dit_step(steps, warmup):
             outs[(M, N)] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
-    def run():
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def run(marks=None, all_calls=False):
         for lin in plan:
             M, K, N = lin["M"], lin["K"], lin["N"]
             q, sa = qbuf[(M, K)]
+            timed_call = marks is not None and (all_calls or lin["name"] == focus)
+            if timed_call and all_calls:
+                e0 = ev()
+                e0.record()
             dq.dq_quantize_fp8(acts[lin["act"]], q, sa)
+            if timed_call:
+                e1 = ev()
+                e1.record()
             if lin["epilogue"] == "gated_residual":
                 r = residuals[lin["residual"]]
                 dq.dq_linear_fp8(q, sa, lin["qw"], lin["sw"], lin["bias"], "gated_residual",
@@ -406,59 +449,142 @@ def bench_dit_step(steps, warmup):
             else:
                 dq.dq_linear_fp8(q, sa, lin["qw"], lin["sw"], lin["bias"], lin["epilogue"],
                                  out=outs[(M, N)])
+            if timed_call:
+                e2 = ev()
+                e2.record()
+                marks.append((lin["name"], e0 if all_calls else None, e1, e2))
 
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
+    focus_marks = []
+    t0, t1 = ev(), ev()
+    t0.record()
     for _ in range(steps):
-        run()
-    e1.record()
+        run(focus_marks)
+    t1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    flops = w.flops_per_step
-    wbytes = sum(l["N"] * l["K"] for l in plan)
-    return {"ms": ms, "tflops": flops / ms / 1e9, "linears": len(plan), "weight_bytes": wbytes}
+    ms = t0.elapsed_time(t1) / steps
+    focus_us = float(np.mean([a.elapsed_time(b) for _, _, a, b in focus_marks])) * 1e3
+
+    marks = []
+    for _ in range(breakdown_steps):
+        run(marks, all_calls=True)
+    torch.cuda.synchronize()
+    by = {}
+    for name, e0, e1, e2 in marks:
+        d = by.setdefault(name, {"quant": [], "gemm": []})
+        d["quant"].append(e0.elapsed_time(e1) * 1e3)
+        d["gemm"].append(e1.elapsed_time(e2) * 1e3)
+    table = {}
+    for l, rep in zip(w.linears, w.repeat):
+        d = by[l.name]
+        g_us, q_us = float(np.mean(d["gemm"])), float(np.mean(d["quant"]))
+        tf = l.flops / g_us / 1e6
+        qgb = quantizer_bytes(l.M, l.K) / q_us / 1e3
+        table[l.name] = {
+            "shape": [l.M, l.K, l.N], "epilogue": l.epilogue, "per_step": rep,
+            "gemm_us": round(g_us, 2), "gemm_tflops": round(tf, 1),
+            "gemm_frac": round(tf / PEAK_FP8_TFLOPS, 4),
+            "quant_us": round(q_us, 2), "quant_gbps": round(qgb, 1),
+            "quant_frac": round(qgb / PEAK_HBM_GBPS, 4),
+            "ms_per_step": round(rep * (g_us + q_us) / 1e3, 3),
+        }
+    return {"ms": ms, "tflops": w.flops_per_step / ms / 1e9, "linears": len(plan),
+            "weight_bytes": sum(l["N"] * l["K"] for l in plan), "flops": w.flops_per_step,
+            "floor_ms": dit_floor_ms(w), "focus": focus, "focus_gemm_us": focus_us,
+            "focus_calls": len(focus_marks), "breakdown": table}
 
 
 # ---------------------------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, on the host
 # ---------------------------------------------------------------------------------------------
 
-def cpu_baseline(shape, seed, reps=2):
-    from threadpoolctl import threadpool_info
-    from oracle import linear_ref, quantize_rows
-    from workloads import bf16_bits_to_f32, make_linear_inputs
+_INPUTS = {}
 
-    inp = make_linear_inputs(shape, seed)
-    qw, sw = quantize_rows(bf16_bits_to_f32(inp.w))       # weight prep, not timed
+
+def linear_inputs(shape, seed):
+    """Seeded host inputs of one linear, drawn once per (shape, seed) and shared by the GPU legs
+    and the CPU baseline."""
+    from workloads import make_linear_inputs
+    key = (shape, seed)
+    if key not in _INPUTS:
+        _INPUTS[key] = make_linear_inputs(shape, seed)
+    return _INPUTS[key]
+
+
+def blas_threads():
+    from threadpoolctl import threadpool_info
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    return int(max([i.get("num_threads", 1) for i in blas] or [1]))
+
+
+def cpu_oracle_linear(shape, seed):
+    """Time the oracle on one linear as it stands: quantize x per token, then the exact float64
+    contraction and the epilogue (weights quantized beforehand, untimed). Returns seconds for the
+    quantization and for the linear."""
+    from oracle import linear_ref, quantize_rows
+    from workloads import bf16_bits_to_f32
+
+    inp = linear_inputs(shape, seed)
+    qw, sw = quantize_rows(bf16_bits_to_f32(inp.w))
     x = bf16_bits_to_f32(inp.x)
     bias = bf16_bits_to_f32(inp.bias)
     gate = None if inp.gate is None else bf16_bits_to_f32(inp.gate)
     res = None if inp.residual is None else bf16_bits_to_f32(inp.residual)
-    times = []
-    for _ in range(reps):
-        t0 = time.perf_counter()
-        q, sa = quantize_rows(x)
-        y = linear_ref(q, sa, qw, sw, bias, shape.epilogue, gate, res)
-        times.append(time.perf_counter() - t0)
-        del y
-    t = float(np.mean(times))
-    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-    threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    t0 = time.perf_counter()
+    q, sa = quantize_rows(x)
+    t1 = time.perf_counter()
+    y = linear_ref(q, sa, qw, sw, bias, shape.epilogue, gate, res)
+    t2 = time.perf_counter()
+    del y
+    return t1 - t0, t2 - t1
+
+
+def cpu_baseline_dit(m_cap=1024, n_cap=3072):
+    """The oracle on a bounded sample of the DiT step: each of its 10 linear shapes with its first
+    min(M, m_cap) tokens and min(N, n_cap) output channels (full K), drawn from the same
+    distributions; the quantization time is scaled by M / M' and the linear's by (M N) / (M' N'),
+    then summed with each shape's multiplicity per step."""
+    from workloads import workload
+    w = workload("flux-dit-step-1024")
+    total, work = 0.0, 0.0
+    for i, (l, rep) in enumerate(zip(w.linears, w.repeat)):
+        m, n = min(l.M, m_cap), min(l.N, n_cap)
+        sl = type(l)(l.name, m, l.K, n, l.epilogue, l.n_outliers, l.outlier_factor)
+        tq, tl = cpu_oracle_linear(sl, 100 + i)
+        work += tq + tl
+        total += rep * (tq * l.M / m + tl * (l.M * l.N) / (m * n))
+    threads = blas_threads()
     return {
-        "value": round(shape.flops / t / 1e12, 6),
+        "value": round(w.flops_per_step / total / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": threads,
         "kind": "oracle",
-        "sample": (f"the whole {shape.M}x{shape.K}x{shape.N} {shape.epilogue} step (quantize "
-                   f"x + exact float64 contraction + epilogue), mean of {reps} runs; "
-                   f"elementwise NumPy single-threaded, BLAS with {threads} threads"),
-        "seconds_per_step": round(t, 3),
+        "sample": (f"each of the step's 10 linear shapes once on its first min(M, {m_cap}) tokens "
+                   f"and min(N, {n_cap}) output channels (full K), quantize x + exact float64 "
+                   f"contraction + epilogue, extrapolated by rows and columns and summed with "
+                   f"multiplicity (19 or 38) to one 228-linear step; elementwise NumPy "
+                   f"single-threaded, BLAS with {threads} threads; {work:.1f} s of CPU work"),
+        "seconds_per_step": round(total, 2),
         "host_cpus_visible": os.cpu_count(),
     }
+
+
+def cpu_oracle_configs(configs):
+    """The oracle timed on whole configurations (every linear of each), as it stands."""
+    res = {}
+    for name, w in configs:
+        t = 0.0
+        parts = {}
+        for l in w.linears:
+            tq, tl = cpu_oracle_linear(l, w.seed)
+            parts[l.name] = {"quant_s": round(tq, 3), "linear_s": round(tl, 3)}
+            t += tq + tl
+        flops = sum(l.flops for l in w.linears)
+        res[name] = {"seconds": round(t, 3), "tflops": round(flops / t / 1e12, 6), "parts": parts}
+        log(f"CPU oracle {name}: {t:.2f} s ({flops / t / 1e12:.4f} TFLOP/s)")
+    return res
 
 
 # ---------------------------------------------------------------------------------------------
@@ -475,23 +601,53 @@ def calibrate_copy(nbytes=1 << 30):
     log(f"calibration copy of {nbytes} bytes done")
 
 
+def linear_leg(shape, seed, steps, warmup, n_sets, traffic_key=None):
+    """Quantize + GEMM of one linear (bench_linear) as a JSON object: the quantizer against HBM
+    bandwidth, the GEMM against the FP8 matrix peak."""
+    r = bench_linear(shape, seed, steps, warmup, n_sets)
+    step_ms = r["total_ms"] / steps
+    gemm_ms = float(np.mean(r["gemm_ms"]))
+    quant_ms = float(r["quant_loop_ms"])
+    qbytes = quantizer_bytes(shape.M, shape.K)
+    tf = shape.flops / gemm_ms / 1e9
+    gb = qbytes / quant_ms / 1e6
+    log(f"{shape.name} {shape.M}x{shape.K}->{shape.N} {shape.epilogue}: step {step_ms * 1e3:.1f} us; "
+        f"quantize {quant_ms * 1e3:.2f} us ({gb:.0f} GB/s), GEMM {gemm_ms * 1e3:.1f} us "
+        f"({tf:.0f} TFLOP/s)")
+    return {
+        "shape": [shape.M, shape.K, shape.N], "epilogue": shape.epilogue,
+        "step_us": round(step_ms * 1e3, 2),
+        "gemm": {"kernel": f"gemm_fp8_pp<{shape.epilogue}>", "bound": "mfma",
+                 "avg_launch_us": round(gemm_ms * 1e3, 2), "achieved": round(tf, 1),
+                 "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                 "algorithmic_flop_per_launch": shape.flops,
+                 "traffic": stored_traffic("gemm", traffic_key) if traffic_key else None},
+        "quantizer": {"kernel": "quant_rows", "bound": "hbm",
+                      "avg_launch_us": round(quant_ms * 1e3, 2), "achieved": round(gb, 1),
+                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gb / PEAK_HBM_GBPS, 4),
+                      "algorithmic_bytes_per_launch": qbytes,
+                      "traffic": stored_traffic("quantize", traffic_key) if traffic_key else None},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    # The chip's clock settles over the first tens of milliseconds of dense FP8 work: 300
-    # untimed steps (about 60 ms) reach the steady state that the timed steps then measure.
-    ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--workload", default="flux-mlp-up-1024")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="flux-dit-step-1024",
+                    help="flux-dit-step-1024 (the whole step) or a single-linear workload")
     ap.add_argument("--linear", type=int, default=0, help="index of the linear in the workload")
     ap.add_argument("--sets", type=int, default=6, help="rotating input/output buffer sets")
-    ap.add_argument("--dit-steps", type=int, default=5)
-    ap.add_argument("--no-dit", action="store_true")
+    ap.add_argument("--leg-steps", type=int, default=30, help="timed calls per leg")
+    ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--no-modulate", action="store_true")
     ap.add_argument("--no-qkv", action="store_true")
     ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--no-mx", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-configs", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB plain copy first (reference for HBM counters)")
     args = ap.parse_args()
@@ -506,76 +662,85 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    import fp8_dynamic_quant_amd as dq
+    import fp8_dynamic_quant_amd as dq  # noqa: F401  (fails loudly when libdq.so is missing)
 
     if args.calibrate_copy:
         calibrate_copy()
 
     w = workload(args.workload)
-    shape = w.linears[args.linear]
-    log(f"workload {w.name}[{args.linear}] M={shape.M} K={shape.K} N={shape.N} "
-        f"epilogue={shape.epilogue}; warmup {args.warmup}, steps {args.steps}")
-    r = bench_linear(shape, w.seed, args.steps, args.warmup, args.sets)
-    ms_per_step = r["total_ms"] / args.steps
-    value = shape.flops / ms_per_step / 1e9          # TFLOP/s
-    gemm_ms = float(np.mean(r["gemm_ms"]))
-    quant_ms = float(r["quant_loop_ms"])
-    quant_in_step_ms = float(np.mean(r["quant_ms"]))
-    gemm_tflops = shape.flops / gemm_ms / 1e9
-    qbytes = 3 * shape.M * shape.K + 4 * shape.M
-    quant_gbps = qbytes / quant_ms / 1e6
-    log(f"step {ms_per_step * 1e3:.1f} us: quantize {quant_ms * 1e3:.1f} us "
-        f"({quant_gbps:.0f} GB/s; {quant_in_step_ms * 1e3:.1f} us between events inside steps), "
-        f"GEMM {gemm_ms * 1e3:.1f} us ({gemm_tflops:.0f} TFLOP/s)")
-
-    traffic = stored_traffic("gemm", w.name)
-    qtraffic = stored_traffic("quantize", w.name)
-    res = {
-        "metric": METRIC,
-        "value": round(value, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 in/out)",
-        "data": "synthetic",
-        "config": {"workload": w.name, "linear": shape.name, "M": shape.M, "K": shape.K,
-                   "N": shape.N, "epilogue": shape.epilogue, "rotating_sets": args.sets,
-                   "parallelism": "none (1 GPU)"},
-        "roofline": {
-            "kernel": f"gemm_fp8_pp<{shape.epilogue}>",
-            "timing": ("HIP events around each dq_linear_fp8 call on its stream; a call is one "
-                       "launch, or two when the tiles left after the full rounds run as "
-                       "256 x 128 halves (the second, narrow launch follows on the stream)"),
-            "bound": "mfma",
-            "achieved": round(gemm_tflops, 2),
-            "peak": PEAK_FP8_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
-            "traffic": traffic,
-            "avg_launch_us": round(gemm_ms * 1e3, 2),
-            "algorithmic_flop_per_launch": shape.flops,
-        },
-        "quantizer": {
-            "kernel": "quant_rows_reg",
-            "timing": "back-to-back launches over rotating inputs, HIP events around the loop",
-            "bound": "hbm",
-            "achieved": round(quant_gbps, 1),
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": round(quant_gbps / PEAK_HBM_GBPS, 4),
-            "traffic": qtraffic,
-            "avg_launch_us": round(quant_ms * 1e3, 2),
-            "algorithmic_bytes_per_launch": qbytes,
-        },
-    }
+    res = {"metric": METRIC}
+    ls = args.leg_steps
+    if w.name == "flux-dit-step-1024":
+        log(f"DiT step: drawing 228 distinct weights on the device; warmup {args.warmup}, "
+            f"steps {args.steps}")
+        d = bench_dit_step(args.steps, args.warmup)
+        focus = next(l for l in w.linears if l.name == d["focus"])
+        ftf = focus.flops / d["focus_gemm_us"] / 1e6
+        log(f"DiT step linears: {d['ms']:.3f} ms ({d['tflops']:.0f} TFLOP/s; floor "
+            f"{d['floor_ms']:.2f} ms); {d['focus']} GEMM {d['focus_gemm_us']:.1f} us "
+            f"({ftf:.0f} TFLOP/s)")
+        for name, row in d["breakdown"].items():
+            log(f"  {name:16s} x{row['per_step']}: GEMM {row['gemm_us']:7.1f} us "
+                f"({row['gemm_tflops']:6.0f} TFLOP/s)  quantize {row['quant_us']:6.1f} us "
+                f"({row['quant_gbps']:5.0f} GB/s)  -> {row['ms_per_step']:.2f} ms/step")
+        res.update({
+            "value": round(d["tflops"], 3), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(d["ms"], 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "fp8_e4m3 (fp32 accumulate, bf16 in/out)", "data": "synthetic",
+            "config": {"workload": w.name, "linears_per_step": d["linears"],
+                       "flop_per_step": d["flops"], "weight_bytes_fp8": d["weight_bytes"],
+                       "parallelism": "none (1 GPU)"},
+            "roofline": {
+                "kernel": f"gemm_fp8_pp<bias> on {d['focus']} {list(focus_shape(focus))}",
+                "timing": (f"HIP event pair around each of the {d['focus_calls']} "
+                           f"{d['focus']} dq_linear_fp8 calls of the timed steps, on the stream "
+                           f"the kernels run on"),
+                "bound": "mfma", "achieved": round(ftf, 2), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ftf / PEAK_FP8_TFLOPS, 4),
+                "traffic": stored_traffic("gemm", "flux-single-block-1024"),
+                "avg_launch_us": round(d["focus_gemm_us"], 2),
+                "algorithmic_flop_per_launch": focus.flops,
+            },
+            "dit_step": {"ms": round(d["ms"], 4), "tflops": round(d["tflops"], 1),
+                         "roofline_floor_ms": round(d["floor_ms"], 3),
+                         "frac": round(d["floor_ms"] / d["ms"], 4),
+                         "breakdown_timing": "event pairs around every call of 2 further steps",
+                         "breakdown": d["breakdown"]},
+        })
+    else:
+        shape = w.linears[args.linear]
+        log(f"workload {w.name}[{args.linear}] M={shape.M} K={shape.K} N={shape.N} "
+            f"epilogue={shape.epilogue}; warmup {args.warmup}, steps {args.steps}")
+        leg = linear_leg(shape, w.seed, args.steps, args.warmup, args.sets, w.name)
+        ms_per_step = leg["step_us"] / 1e3
+        res.update({
+            "value": round(shape.flops / ms_per_step / 1e9, 3), "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate, bf16 in/out)",
+            "data": "synthetic",
+            "config": {"workload": w.name, "linear": shape.name, "M": shape.M, "K": shape.K,
+                       "N": shape.N, "epilogue": shape.epilogue, "rotating_sets": args.sets,
+                       "parallelism": "none (1 GPU)"},
+            "roofline": dict(leg["gemm"], timing=(
+                "HIP events around each dq_linear_fp8 call on its stream (one launch, or two "
+                "when the left-over tiles run as 256 x 128 halves)")),
+            "quantizer": leg["quantizer"],
+        })
+    cfg_names = ["tiny-64x256x512", "flux-mlp-up-1024", "flux-single-block-1024",
+                 "flux-mlp-up-2048"]
+    if not args.no_configs and w.name == "flux-dit-step-1024":
+        res["configs"] = {}
+        for name in cfg_names:
+            cw = workload(name)
+            res["configs"][name] = {l.name: linear_leg(l, cw.seed, ls, 20, args.sets, name)
+                                    for l in cw.linears}
+    shape = workload("flux-mlp-up-1024").linears[0]
+    seed = workload("flux-mlp-up-1024").seed
     if not args.no_modulate:
         Mm, Km = shape.M, shape.K
-        mo = bench_modulate(Mm, Km, args.steps, args.sets)
+        mo = bench_modulate(Mm, Km, ls, args.sets)
         b_no_y = 3 * Mm * Km + 4 * Mm + 4 * Km       # read x, write codes and scales, read mod
         b_y = b_no_y + 2 * Mm * Km                   # plus the bf16 y
         gb_no_y = b_no_y / mo["no_y_us"] / 1e3
@@ -585,42 +750,34 @@ def main():
         res["ln_modulate_quantizer"] = {
             "kernel": "ln_mod_quant_rows",
             "timing": "back-to-back launches over rotating inputs, HIP events around the loop",
-            "shape": [Mm, Km],
-            "bound": "hbm",
-            "achieved": round(gb_no_y, 1),
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": round(gb_no_y / PEAK_HBM_GBPS, 4),
-            "traffic": stored_traffic("ln_modulate", w.name),
-            "avg_launch_us": round(mo["no_y_us"], 2),
-            "algorithmic_bytes_per_launch": b_no_y,
+            "shape": [Mm, Km], "bound": "hbm", "achieved": round(gb_no_y, 1),
+            "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gb_no_y / PEAK_HBM_GBPS, 4),
+            "traffic": stored_traffic("ln_modulate", "flux-mlp-up-1024"),
+            "avg_launch_us": round(mo["no_y_us"], 2), "algorithmic_bytes_per_launch": b_no_y,
             "with_y": {"avg_launch_us": round(mo["y_us"], 2), "achieved": round(gb_y, 1),
                        "frac": round(gb_y / PEAK_HBM_GBPS, 4),
                        "algorithmic_bytes_per_launch": b_y},
             "unfused_torch_then_quantize_us": round(mo["unfused_us"], 2),
         }
     if not args.no_qkv:
-        qk = bench_qkv(args.steps, min(args.warmup, 100), min(args.sets, 4))
+        qk = bench_qkv(ls, 20, min(args.sets, 4))
         tf = qk["flops"] / qk["fused_us"] / 1e6
         log(f"QKV + norm + rotary {qk['shape']}: {qk['fused_us']:.1f} us ({tf:.0f} TFLOP/s); "
             f"bias epilogue {qk['plain_us']:.1f} us; unfused {qk['unfused_us']:.1f} us")
         res["qkv_linear"] = {
             "kernel": "gemm_fp8_pp<qkv>",
             "timing": "HIP events around each call, rotating inputs (1 or 2 launches per call)",
-            "shape": qk["shape"], "heads": qk["heads"],
-            "bound": "mfma",
-            "achieved": round(tf, 1),
-            "peak": PEAK_FP8_TFLOPS,
-            "unit": "TFLOP/s",
+            "shape": qk["shape"], "heads": qk["heads"], "bound": "mfma",
+            "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / PEAK_FP8_TFLOPS, 4),
-            "traffic": stored_traffic("qkv", w.name),
+            "traffic": stored_traffic("qkv", "flux-mlp-up-1024"),
             "avg_launch_us": round(qk["fused_us"], 2),
             "algorithmic_flop_per_launch": qk["flops"],
             "bias_epilogue_us": round(qk["plain_us"], 2),
             "unfused_torch_us": round(qk["unfused_us"], 2),
         }
     if not args.no_attention:
-        at = bench_attention(args.steps, min(args.warmup, 50), 3)
+        at = bench_attention(ls, 20, 3)
         tf = at["flops"] / at["attn_us"] / 1e6
         # half the work on the FP8 matrix units (5.0 PF), half on bf16 (2.5 PF)
         mixed_peak = 4.0 / (2.0 / PEAK_FP8_TFLOPS + 2.0 / (PEAK_FP8_TFLOPS / 2))
@@ -630,20 +787,17 @@ def main():
             "kernel": "attn_fp8",
             "timing": "HIP events around each call, rotating inputs",
             "shape": {"heads": at["H"], "tokens": at["S"], "head_dim": 128},
-            "bound": "mfma",
-            "achieved": round(tf, 1),
-            "peak": round(mixed_peak, 1),
+            "bound": "mfma", "achieved": round(tf, 1), "peak": round(mixed_peak, 1),
             "peak_note": "q k^T on FP8 (5.0 PF), p v on bf16 (2.5 PF): 4 / (2/5.0 + 2/2.5) PF",
-            "unit": "TFLOP/s",
-            "frac": round(tf / mixed_peak, 4),
-            "traffic": stored_traffic("attention", w.name),
+            "unit": "TFLOP/s", "frac": round(tf / mixed_peak, 4),
+            "traffic": stored_traffic("attention", "flux-mlp-up-1024"),
             "avg_launch_us": round(at["attn_us"], 2),
             "algorithmic_flop_per_launch": at["flops"],
             "qkv_quantization_us": round(at["quant_us"], 2),
             "torch_bf16_sdpa_us": round(at["sdpa_us"], 2),
         }
     if not args.no_mx:
-        mx = bench_mx(shape, w.seed, args.steps, min(args.warmup, 100), min(args.sets, 4))
+        mx = bench_mx(shape, seed, ls, 20, min(args.sets, 4))
         tf = mx["flops"] / mx["gemm_us"] / 1e6
         gbq = mx["quant_bytes"] / mx["quant_us"] / 1e3
         log(f"MX (block-scaled) FP8 {mx['shape']} {mx['epilogue']}: GEMM {mx['gemm_us']:.1f} us "
@@ -652,32 +806,39 @@ def main():
         res["mx_linear"] = {
             "kernel": "gemm_mx<%s>" % mx["epilogue"],
             "timing": "HIP events around each call, rotating inputs",
-            "shape": mx["shape"], "epilogue": mx["epilogue"],
-            "bound": "mfma",
-            "achieved": round(tf, 1),
-            "peak": PEAK_FP8_TFLOPS,
-            "unit": "TFLOP/s",
+            "shape": mx["shape"], "epilogue": mx["epilogue"], "bound": "mfma",
+            "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / PEAK_FP8_TFLOPS, 4),
-            "traffic": stored_traffic("mx_linear", w.name),
+            "traffic": stored_traffic("mx_linear", "flux-mlp-up-1024"),
             "avg_launch_us": round(mx["gemm_us"], 2),
             "algorithmic_flop_per_launch": mx["flops"],
             "quantizer_us": round(mx["quant_us"], 2),
             "quantizer_gbps": round(gbq, 1),
             "rowwise_fp8_gemm_us": round(mx["rowwise_us"], 2),
         }
-    if not args.no_dit:
-        log("DiT step: generating 228 distinct FP8 weights on the device")
-        d = bench_dit_step(args.dit_steps, 2)
-        floor_ms = 13.74
-        res["dit_step"] = {"workload": "flux-dit-step-1024", "linears": d["linears"],
-                           "ms": round(d["ms"], 3), "tflops": round(d["tflops"], 1),
-                           "roofline_floor_ms": floor_ms,
-                           "frac": round(floor_ms / d["ms"], 4), "steps": args.dit_steps}
-        log(f"DiT step linears: {d['ms']:.2f} ms ({d['tflops']:.0f} TFLOP/s)")
     if not args.no_cpu_baseline:
         log("CPU baseline: timing the oracle on the host")
-        res["cpu_baseline"] = cpu_baseline(shape, w.seed)
+        if w.name == "flux-dit-step-1024":
+            res["cpu_baseline"] = cpu_baseline_dit()
+        else:
+            t = sum(cpu_oracle_linear(w.linears[args.linear], w.seed))
+            fl = w.linears[args.linear].flops
+            res["cpu_baseline"] = {"value": round(fl / t / 1e12, 6), "unit": "TFLOP/s",
+                                   "cores": blas_threads(), "kind": "oracle",
+                                   "sample": "the whole linear once (quantize x + exact float64 "
+                                             "contraction + epilogue)",
+                                   "seconds_per_step": round(t, 3),
+                                   "host_cpus_visible": os.cpu_count()}
+        log(f"CPU oracle: {res['cpu_baseline']['value']} TFLOP/s "
+            f"({res['cpu_baseline']['seconds_per_step']} s per step)")
+        if not args.no_cpu_configs:
+            res["cpu_oracle_configs"] = cpu_oracle_configs(
+                [(n, workload(n)) for n in cfg_names])
     print(json.dumps(res), flush=True)
+
+
+def focus_shape(l):
+    return (l.M, l.K, l.N)
 
 
 if __name__ == "__main__":
