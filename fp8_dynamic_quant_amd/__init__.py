@@ -180,7 +180,8 @@ def dq_layernorm_modulate_quantize_fp8(x, mod_scale, mod_shift, eps=1e-6, store_
 
 
 def dq_linear_fp8_workspace_size(M, K, N):
-    """Bytes of workspace dq_linear_fp8 uses for an M x K -> N problem (0: invalid sizes)."""
+    """Bytes of workspace the schedule dq_linear_fp8 prefers for an M x K -> N problem on the
+    current device (0: no workspace needed, or invalid sizes)."""
     return int(lib().dq_linear_fp8_workspace_size(int(M), int(K), int(N)))
 
 
@@ -222,10 +223,25 @@ def dq_linear_fp8(q, scale, qw, w_scale, bias=None, epilogue="bias", gate=None, 
 
     epilogue: "bias" | "gelu_tanh" | "gated_residual" (needs gate [N] and residual [M, N];
     out may be residual itself for an in-place update).
-    workspace: "auto" (a cached zero-filled buffer per device and stream), None, or a uint8
-    tensor of at least dq_linear_fp8_workspace_size(M, K, N) bytes that holds zeros before its
-    first use.
+    workspace: "auto" (a cached zero-filled buffer per device and stream, of the size the
+    preferred schedule uses), None (no tile is cut), or a uint8 tensor whose first 4096 bytes
+    hold zeros before its first use; its size is a budget (include/dq.h).
     """
+    dev, M, K, N, gate, residual, out = _linear_args(q, scale, qw, w_scale, bias, epilogue, gate,
+                                                     residual, out)
+    with torch.cuda.device(dev):
+        st = stream if stream is not None else torch.cuda.current_stream(dev)
+        workspace, ws_bytes = _resolve_workspace(workspace, dev, st, M, K, N)
+        _check(lib().dq_linear_fp8(_ptr(q), _ptr(scale), M, K, _ptr(qw), _ptr(w_scale), N,
+                                   _ptr(bias), EPILOGUES[epilogue], _ptr(gate), _ptr(residual),
+                                   _ptr(out), _ptr(workspace), ws_bytes,
+                                   ctypes.c_void_p(st.cuda_stream)), "dq_linear_fp8")
+    return out
+
+
+def _linear_args(q, scale, qw, w_scale, bias, epilogue, gate, residual, out):
+    """Checks of dq_linear_fp8's tensors; allocates out when None. Returns (device, M, K, N,
+    gate, residual, out)."""
     if epilogue not in EPILOGUES:
         raise ValueError(f"unknown epilogue {epilogue!r}")
     if not isinstance(q, torch.Tensor) or q.dim() != 2 or not isinstance(qw, torch.Tensor) \
@@ -251,14 +267,7 @@ def dq_linear_fp8(q, scale, qw, w_scale, bias=None, epilogue="bias", gate=None, 
         gate = residual = None
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
     _need(out, "out", torch.bfloat16, (M, N), dev)
-    with torch.cuda.device(dev):
-        st = stream if stream is not None else torch.cuda.current_stream(dev)
-        workspace, ws_bytes = _resolve_workspace(workspace, dev, st, M, K, N)
-        _check(lib().dq_linear_fp8(_ptr(q), _ptr(scale), M, K, _ptr(qw), _ptr(w_scale), N,
-                                   _ptr(bias), EPILOGUES[epilogue], _ptr(gate), _ptr(residual),
-                                   _ptr(out), _ptr(workspace), ws_bytes,
-                                   ctypes.c_void_p(st.cuda_stream)), "dq_linear_fp8")
-    return out
+    return dev, M, K, N, gate, residual, out
 
 
 HEAD_DIM = 128

@@ -79,10 +79,16 @@ int dq_quantize_weight_fp8(const void* w, int64_t N, int64_t K, void* qw, float*
   return quantize_rows(w, N, K, qw, w_scale, stream);
 }
 
-int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const void* qw,
-                  const float* w_scale, int64_t N, const void* bias, int epilogue,
-                  const void* gate, const void* residual, void* out, void* workspace,
-                  uint64_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Everything dq_linear_fp8 checks, for the workspace range [workspace, + workspace_bytes) (NULL:
+// none). Returns DQ_OK, or the status to return with nothing enqueued.
+int check_linear_args(const void* q, const float* scale, int64_t M, int64_t K, const void* qw,
+                      const float* w_scale, int64_t N, const void* bias, int epilogue,
+                      const void* gate, const void* residual, const void* out,
+                      const void* workspace, uint64_t workspace_bytes) {
   const int shape = check_linear_shape(M, K, N);
   if (shape != DQ_OK) return shape;
   if (epilogue != DQ_EPI_BIAS && epilogue != DQ_EPI_GELU_TANH &&
@@ -100,15 +106,14 @@ int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const
                  n = static_cast<uint64_t>(N);
   const uint64_t out_bytes = 2 * m * n;
   if (workspace) {
-    const uint64_t need = dq::linear_workspace_bytes(M, K, N);
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
-      return DQ_ERR_WORKSPACE;
-    if (overlap(workspace, need, q, m * k) || overlap(workspace, need, scale, 4 * m) ||
-        overlap(workspace, need, qw, n * k) || overlap(workspace, need, w_scale, 4 * n) ||
-        overlap(workspace, need, bias, bias ? 2 * n : 0) ||
-        (gated && overlap(workspace, need, gate, 2 * n)) ||
-        (gated && overlap(workspace, need, residual, out_bytes)) ||
-        overlap(workspace, need, out, out_bytes))
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DQ_ERR_WORKSPACE;
+    const uint64_t wb = workspace_bytes;
+    if (overlap(workspace, wb, q, m * k) || overlap(workspace, wb, scale, 4 * m) ||
+        overlap(workspace, wb, qw, n * k) || overlap(workspace, wb, w_scale, 4 * n) ||
+        overlap(workspace, wb, bias, bias ? 2 * n : 0) ||
+        (gated && overlap(workspace, wb, gate, 2 * n)) ||
+        (gated && overlap(workspace, wb, residual, out_bytes)) ||
+        overlap(workspace, wb, out, out_bytes))
       return DQ_ERR_ALIAS;
   }
   if (overlap(out, out_bytes, q, m * k) || overlap(out, out_bytes, scale, 4 * m) ||
@@ -117,12 +122,27 @@ int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const
       (gated && overlap(out, out_bytes, gate, 2 * n)))
     return DQ_ERR_ALIAS;
   if (gated && residual != out && overlap(out, out_bytes, residual, out_bytes)) return DQ_ERR_ALIAS;
+  return DQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const void* qw,
+                  const float* w_scale, int64_t N, const void* bias, int epilogue,
+                  const void* gate, const void* residual, void* out, void* workspace,
+                  uint64_t workspace_bytes, void* stream) {
+  const int st = check_linear_args(q, scale, M, K, qw, w_scale, N, bias, epilogue, gate, residual,
+                                   out, workspace, workspace_bytes);
+  if (st != DQ_OK || M == 0) return st;
+  const bool gated = epilogue == DQ_EPI_GATED_RESIDUAL;
   return hip_status(dq::launch_linear(
       static_cast<const uint8_t*>(q), scale, M, K, static_cast<const uint8_t*>(qw), w_scale, N,
       static_cast<const uint16_t*>(bias), epilogue,
       gated ? static_cast<const uint16_t*>(gate) : nullptr,
       gated ? static_cast<const uint16_t*>(residual) : nullptr, static_cast<uint16_t*>(out),
-      workspace, static_cast<hipStream_t>(stream)));
+      workspace, workspace ? workspace_bytes : 0, static_cast<hipStream_t>(stream)));
 }
 
 int dq_layernorm_modulate_quantize_fp8(const void* x, int64_t M, int64_t K, const void* mod_scale,
@@ -187,19 +207,18 @@ int dq_linear_qkv_fp8(const void* q, const float* scale, int64_t M, int64_t K, c
       if (overlap(outs[o], ob, outs[o2], ob)) return DQ_ERR_ALIAS;
   }
   if (workspace) {
-    const uint64_t need = dq::linear_workspace_bytes(M, K, N);
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
-      return DQ_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DQ_ERR_WORKSPACE;
     for (int i = 0; i < 8; ++i)
-      if (overlap(workspace, need, ins[i], in_bytes[i])) return DQ_ERR_ALIAS;
+      if (overlap(workspace, workspace_bytes, ins[i], in_bytes[i])) return DQ_ERR_ALIAS;
     for (int o = 0; o < 3; ++o)
-      if (overlap(workspace, need, outs[o], ob)) return DQ_ERR_ALIAS;
+      if (overlap(workspace, workspace_bytes, outs[o], ob)) return DQ_ERR_ALIAS;
   }
   return hip_status(dq::launch_linear_qkv(
       static_cast<const uint8_t*>(q), scale, M, K, static_cast<const uint8_t*>(qw), w_scale,
       heads, static_cast<const uint16_t*>(bias), static_cast<const uint16_t*>(norm_qk), rope_cos,
       rope_sin, eps, static_cast<uint16_t*>(out_q), static_cast<uint16_t*>(out_k),
-      static_cast<uint16_t*>(out_v), workspace, static_cast<hipStream_t>(stream)));
+      static_cast<uint16_t*>(out_v), workspace, workspace ? workspace_bytes : 0,
+      static_cast<hipStream_t>(stream)));
 }
 
 // Sizes of the attention entry points: 1 <= S < 2^24 with S % 16 == 0 (or an empty problem),
@@ -321,7 +340,7 @@ const char* dq_status_string(int status) {
     case DQ_ERR_ALIAS: return "an output overlaps an input";
     case DQ_ERR_EPILOGUE: return "unknown epilogue, or gate/residual missing for the gated one";
     case DQ_ERR_HIP: return "a HIP runtime call failed";
-    case DQ_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
+    case DQ_ERR_WORKSPACE: return "workspace not 256-byte aligned";
     case DQ_ERR_VALUE: return "a scalar argument is out of range";
     default: return "unknown status";
   }
@@ -329,6 +348,6 @@ const char* dq_status_string(int status) {
 
 int dq_last_hip_error(void) { return g_last_hip_error; }
 
-int dq_abi_version(void) { return 7; }
+int dq_abi_version(void) { return 8; }
 
 }  // extern "C"

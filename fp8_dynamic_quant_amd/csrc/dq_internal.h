@@ -20,19 +20,22 @@ hipError_t launch_ln_modulate_quantize(const uint16_t* x, int64_t R, int64_t K,
                                        hipStream_t stream);
 
 // ---------------------------------------------------------------------------------------------
-// GEMM work split, shared by the size query (host only, no GPU) and the launcher.
+// GEMM work split, shared by the size query (host only, no GPU needed) and the launchers.
 //   tile = 256 x 256 outputs; step = 128 of K.
 // With a workspace, the tiles left over after the full rounds of whole tiles may be cut into
-// up to kMaxParts parts along K (see gemm_fp8.hip). Workspace layout, the same for every
-// problem so that one workspace serves calls of any size in turn:
-//   [0, kPartRegion)              one 256 x 256 fp32 partial tile per part
-//   [kPartRegion, + 4 * tiles)    one arrival counter per tile, zero between calls
+// up to kMaxSplits parts along K (see gemm_fp8.hip). Workspace layout:
+//   [0, kCounterBytes)                      one arrival counter per left-over tile (at most
+//                                           kMaxCutTiles), zero between calls
+//   [kCounterBytes, + parts * kPartialBytes) one 256 x 256 fp32 partial tile per part
+// The counters sit at the same place for every problem, so one workspace serves calls of any
+// size in turn; only they must hold zeros (the partial tiles are written before they are read).
 // ---------------------------------------------------------------------------------------------
 constexpr int64_t kTileM = 256, kTileN = 256, kStepK = 128;
 constexpr int64_t kMaxParts = 1024;
 constexpr int64_t kMaxSplits = 8;
-constexpr int64_t kPartialBytes = kTileM * kTileN * 4;
-constexpr uint64_t kPartRegion = static_cast<uint64_t>(kMaxParts) * kPartialBytes;
+constexpr int64_t kMaxCutTiles = 1024;
+constexpr uint64_t kCounterBytes = 4 * kMaxCutTiles;
+constexpr uint64_t kPartialBytes = kTileM * kTileN * 4;
 
 inline int64_t linear_tiles(int64_t M, int64_t N) {
   return ((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN);
@@ -40,17 +43,20 @@ inline int64_t linear_tiles(int64_t M, int64_t N) {
 inline int64_t linear_units(int64_t M, int64_t K, int64_t N) {
   return linear_tiles(M, N) * (K / kStepK);
 }
-inline uint64_t linear_workspace_bytes(int64_t M, int64_t K, int64_t N) {
-  (void)K;
-  return kPartRegion + ((static_cast<uint64_t>(linear_tiles(M, N)) * 4u + 255u) & ~uint64_t(255));
-}
+
+// Workspace bytes of the schedule the launcher picks for an M x K -> N problem on the current
+// device when its workspace is unbounded: 0 when it cuts no tile, else kCounterBytes plus one
+// partial tile per part. A smaller workspace makes the launcher pick the best schedule that
+// fits in it.
+uint64_t linear_workspace_bytes(int64_t M, int64_t K, int64_t N);
 
 // FP8 GEMM + fused epilogue. Arguments are already validated; `workspace` is NULL or holds
-// linear_workspace_bytes(M, K, N) bytes. Returns the launch status.
+// `workspace_bytes` bytes (counters zero). Returns the launch status.
 hipError_t launch_linear(const uint8_t* q, const float* scale, int64_t M, int64_t K,
                          const uint8_t* qw, const float* w_scale, int64_t N, const uint16_t* bias,
                          int epilogue, const uint16_t* gate, const uint16_t* residual,
-                         uint16_t* out, void* workspace, hipStream_t stream);
+                         uint16_t* out, void* workspace, uint64_t workspace_bytes,
+                         hipStream_t stream);
 
 // FP8 GEMM with the QKV epilogue: N = 3 heads kHeadDim; query and key RMS-normalized per head
 // (weights norm_qk [2][kHeadDim]) and rotated pairwise by rope_cos/sin [M][kHeadDim / 2]; outputs
@@ -60,7 +66,8 @@ hipError_t launch_linear_qkv(const uint8_t* q, const float* scale, int64_t M, in
                              const uint8_t* qw, const float* w_scale, int64_t heads,
                              const uint16_t* bias, const uint16_t* norm_qk, const float* rope_cos,
                              const float* rope_sin, float eps, uint16_t* out_q, uint16_t* out_k,
-                             uint16_t* out_v, void* workspace, hipStream_t stream);
+                             uint16_t* out_v, void* workspace, uint64_t workspace_bytes,
+                             hipStream_t stream);
 
 // FP8 attention (attention.hip). S % 16 == 0 and 1 <= S, H.
 //   launch_quantize_v: v bf16 [H, S, kHeadDim] -> codes transposed [H, kHeadDim, S], scales [H, S]

@@ -97,8 +97,9 @@ struct Params {
   const uint16_t* gate;      // [N] (gated only)
   const uint16_t* residual;  // [M, N] (gated only; may equal out)
   uint16_t* out;             // [M, N]
-  uint32_t* flags;           // [tiles] arrival counters (cut tiles only)
+  uint32_t* flags;           // [left-over tiles] arrival counters (cut tiles only)
   float* part;               // [parts][256 * 256] partial tiles (cut tiles only)
+  uint32_t part_bytes;       // bytes of the partial tiles
   int M, N, K, tilesM, tilesN, nk, tiles;
   int dp_tiles;              // tiles of full rounds run by this launch (a multiple of the grid)
   int tail0;                 // first left-over tile
@@ -700,7 +701,7 @@ __device__ __forceinline__ void epilogue_qkv(v16f (&acc)[NB][4], const Params& p
 // split tiles
 // ---------------------------------------------------------------------------------------------
 
-// Partial tiles live in a 256 MiB region addressed through one buffer descriptor; their loads
+// Partial tiles live in one region addressed through one buffer descriptor; their loads
 // and stores carry the device-coherence bit (sc1), so they are seen across XCDs without
 // flushing or invalidating caches.
 constexpr int kCoherent = 16;  // sc1
@@ -760,13 +761,14 @@ __device__ __forceinline__ uint32_t part_slot(int p) {
 __device__ bool finish_split(v16f (&acc)[2][4], const Params& p, int t, int part, int wave,
                              int lane, int* s_last) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      p.part, 0, (int)kPartRegion, 0x00020000);
+      p.part, 0, (int)p.part_bytes, 0x00020000);
   store_part(acc, rs, part_slot(part), wave, lane);
   wait_vmem();
   phase_barrier();  // every wave's part is stored
   if (threadIdx.x == 0) {
     const uint32_t old =
-        __hip_atomic_fetch_add(p.flags + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(p.flags + (t - p.tail0), 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     *s_last = old == (uint32_t)(p.splits - 1);
   }
   phase_barrier();
@@ -780,7 +782,7 @@ __device__ bool finish_split(v16f (&acc)[2][4], const Params& p, int t, int part
       add_part<false>(acc, rs, slot, wave, lane);
   }
   if (threadIdx.x == 0)
-    __hip_atomic_store(p.flags + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.flags + (t - p.tail0), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
 }
 
@@ -981,10 +983,78 @@ int compute_units() {
 
 }  // namespace
 
-// Sizes, the tile schedule (full rounds, then whole, narrow or cut left-over tiles) and the
-// launches for a Params whose pointers are set.
+// The schedule of one problem: full rounds of whole tiles (one per compute unit per round), then
+// the T mod G tiles left over, run whole, as narrow halves in a second launch, or cut along K.
+struct Plan {
+  int64_t grid = 0;        // workgroups of the launch of whole tiles / parts (0: none)
+  int64_t narrow_grid = 0; // workgroups of the launch of narrow halves (0: none)
+  int64_t dp_tiles = 0, left = 0, splits = 1;
+  int narrow = 0;
+  uint64_t workspace = 0;  // workspace bytes the plan uses
+};
+
+// Chosen by counting steps of the last round:
+//   whole tiles: nk steps;
+//   narrow halves (when all halves fit on the device at once): a 256 x 128 half moves 3/4 of
+//     a tile's operand bytes for half its MFMAs and takes about kNarrow of a tile's time;
+//   cut into s parts along K (s divides nk, s <= 8), when the parts' partial tiles fit in
+//     `budget` bytes of workspace: the last round takes ceil(left s / G) parts of nk / s steps
+//     per workgroup, every part stores a 256 x 256 fp32 partial tile and the part that
+//     finishes a tile loads the s - 1 others; a partial tile moves at the compute unit's share
+//     of HBM bandwidth (at most about 60 GB/s for one unit, 5.6 TB/s for the chip; one step is
+//     about 1.5 us on a busy chip). A cut must win by 20 %.
+static Plan choose_plan(int64_t M, int64_t K, int64_t N, int64_t cus, uint64_t budget) {
+  Plan pl;
+  const int64_t tiles = linear_tiles(M, N), nk = K / kBK;
+  pl.grid = tiles < cus ? tiles : cus;
+  const int64_t rounds = tiles / cus;
+  pl.dp_tiles = rounds * cus;
+  pl.left = tiles - pl.dp_tiles;
+  const int64_t left = pl.left;
+  if (left > 0) {
+    constexpr double kNarrow = 0.7, kStepUs = 1.5, kUnitGBs = 60.0, kChipGBs = 5600.0;
+    double best = (double)nk;
+    if (2 * left <= cus && kNarrow * nk < best) {
+      best = kNarrow * nk;
+      pl.narrow = 1;
+    }
+    if (left <= kMaxCutTiles) {
+      double best_cut = 0.8 * best;
+      for (int64_t s = 2; s <= kMaxSplits; ++s) {
+        if (nk % s != 0 || left * s > kMaxParts) continue;
+        if (kCounterBytes + (uint64_t)(left * s) * kPartialBytes > budget) continue;
+        const int64_t active = left * s < cus ? left * s : cus;
+        const double unit_gbs = kChipGBs / (double)active < kUnitGBs
+                                    ? kChipGBs / (double)active
+                                    : kUnitGBs;
+        const double part_steps_cost = (double)kPartialBytes / (unit_gbs * 1e3) / kStepUs;
+        const double per_unit = (double)((left * s + active - 1) / active);
+        const double cost = per_unit * ((double)(nk / s) + part_steps_cost) +
+                            (double)(s - 1) * part_steps_cost;
+        if (cost < best_cut) {
+          best_cut = cost;
+          pl.splits = s;
+          pl.narrow = 0;
+        }
+      }
+    }
+    if (pl.dp_tiles == 0 && !pl.narrow) {
+      const int64_t items = left * pl.splits;
+      pl.grid = items < cus ? items : cus;
+    }
+  }
+  if (pl.narrow) {
+    pl.narrow_grid = 2 * left;
+    pl.grid = pl.dp_tiles > 0 ? cus : 0;
+  }
+  if (pl.splits > 1) pl.workspace = kCounterBytes + (uint64_t)(left * pl.splits) * kPartialBytes;
+  return pl;
+}
+
+// Sizes and schedule into a Params whose pointers are set, then the launches.
 static hipError_t schedule_and_launch(Params& p, int64_t M, int64_t K, int64_t N, int epilogue,
-                                      void* workspace, hipStream_t stream) {
+                                      void* workspace, uint64_t workspace_bytes,
+                                      hipStream_t stream) {
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
@@ -992,82 +1062,36 @@ static hipError_t schedule_and_launch(Params& p, int64_t M, int64_t K, int64_t N
   p.tilesN = (int)((N + kBN - 1) / kBN);
   p.nk = (int)(K / kBK);
   p.tiles = (int)linear_tiles(M, N);
-  const int cus = compute_units();
-  // Full rounds of whole tiles (one per compute unit), then the T mod G tiles left over, run
-  // one of three ways, chosen by counting steps of the last round:
-  //   whole tiles: nk steps;
-  //   narrow halves (when all halves fit on the device at once): a 256 x 128 half moves 3/4 of
-  //     a tile's operand bytes for half its MFMAs and takes about kNarrow of a tile's time;
-  //   with a workspace, each cut into s parts along K (s divides nk, s <= 8): the last round
-  //     takes ceil(left s / G) parts of nk / s steps per workgroup, every part stores a
-  //     256 x 256 fp32 partial tile and the part that finishes a tile loads the s - 1 others; a
-  //     partial tile moves at the compute unit's share of HBM bandwidth (at most about 60 GB/s
-  //     for one unit, 5.6 TB/s for the chip; one step is about 1.5 us on a busy chip). A cut
-  //     must win by 20 %.
-  int64_t grid = p.tiles < cus ? p.tiles : cus;
-  const int64_t rounds = p.tiles / cus;
-  const int64_t dp_tiles = rounds * cus, left = p.tiles - dp_tiles;
-  int64_t splits = 1;
-  int narrow = 0;
-  if (left > 0) {
-    constexpr double kNarrow = 0.7, kStepUs = 1.5, kUnitGBs = 60.0, kChipGBs = 5600.0;
-    double best = (double)p.nk;
-    if (2 * left <= cus && kNarrow * p.nk < best) {
-      best = kNarrow * p.nk;
-      narrow = 1;
-    }
-    if (workspace) {
-      double best_cut = 0.8 * best;
-      for (int64_t s = 2; s <= kMaxSplits; ++s) {
-        if (p.nk % s != 0 || left * s > kMaxParts) continue;
-        const int64_t active = left * s < cus ? left * s : cus;
-        const double unit_gbs = kChipGBs / (double)active < kUnitGBs
-                                    ? kChipGBs / (double)active
-                                    : kUnitGBs;
-        const double part_steps_cost = (double)kPartialBytes / (unit_gbs * 1e3) / kStepUs;
-        const double per_unit = (double)((left * s + active - 1) / active);
-        const double cost = per_unit * ((double)(p.nk / s) + part_steps_cost) +
-                            (double)(s - 1) * part_steps_cost;
-        if (cost < best_cut) {
-          best_cut = cost;
-          splits = s;
-          narrow = 0;
-        }
-      }
-    }
-    if (dp_tiles == 0 && !narrow) {
-      const int64_t items = left * splits;
-      grid = items < cus ? items : cus;
-    }
-  }
-  int narrow_grid = 0;
-  if (narrow) {
-    narrow_grid = (int)(2 * left);
-    grid = dp_tiles > 0 ? cus : 0;
-  }
-  p.dp_tiles = (int)dp_tiles;
-  p.tail0 = (int)dp_tiles;
-  p.tail_tiles = (int)left;
-  p.splits = (int)splits;
-  p.part_steps = (int)(p.nk / splits);
-  p.narrow = narrow;
-  p.part = splits > 1 ? static_cast<float*>(workspace) : nullptr;
-  p.flags = splits > 1
-                ? reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + kPartRegion)
-                : nullptr;
-  const int g = (int)grid;
+  const Plan pl = choose_plan(M, K, N, compute_units(), workspace ? workspace_bytes : 0);
+  p.dp_tiles = (int)pl.dp_tiles;
+  p.tail0 = (int)pl.dp_tiles;
+  p.tail_tiles = (int)pl.left;
+  p.splits = (int)pl.splits;
+  p.part_steps = (int)(p.nk / pl.splits);
+  p.narrow = pl.narrow;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  p.flags = pl.splits > 1 ? reinterpret_cast<uint32_t*>(ws) : nullptr;
+  p.part = pl.splits > 1 ? reinterpret_cast<float*>(ws + kCounterBytes) : nullptr;
+  p.part_bytes = pl.splits > 1 ? (uint32_t)(pl.workspace - kCounterBytes) : 0u;
+  const int g = (int)pl.grid, ng = (int)pl.narrow_grid;
   switch (epilogue) {
-    case EPI_BIAS: return launch_epi<EPI_BIAS>(p, g, narrow_grid, stream);
-    case EPI_GELU_TANH: return launch_epi<EPI_GELU_TANH>(p, g, narrow_grid, stream);
-    case EPI_QKV: return launch_epi<EPI_QKV>(p, g, narrow_grid, stream);
-    default: return launch_epi<EPI_GATED_RESIDUAL>(p, g, narrow_grid, stream);
+    case EPI_BIAS: return launch_epi<EPI_BIAS>(p, g, ng, stream);
+    case EPI_GELU_TANH: return launch_epi<EPI_GELU_TANH>(p, g, ng, stream);
+    case EPI_QKV: return launch_epi<EPI_QKV>(p, g, ng, stream);
+    default: return launch_epi<EPI_GATED_RESIDUAL>(p, g, ng, stream);
   }
+}
+
+uint64_t linear_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+  if (M == 0) return 0;
+  return choose_plan(M, K, N, compute_units(), ~uint64_t(0)).workspace;
 }
 
 hipError_t launch_linear(const uint8_t* q, const float* scale, int64_t M, int64_t K,
                          const uint8_t* qw, const float* w_scale, int64_t N, const uint16_t* bias,
                          int epilogue, const uint16_t* gate, const uint16_t* residual,
-                         uint16_t* out, void* workspace, hipStream_t stream) {
+                         uint16_t* out, void* workspace, uint64_t workspace_bytes,
+                         hipStream_t stream) {
   if (M == 0) return hipSuccess;
   Params p{};
   p.A = q;
@@ -1078,14 +1102,15 @@ hipError_t launch_linear(const uint8_t* q, const float* scale, int64_t M, int64_
   p.gate = gate;
   p.residual = residual;
   p.out = out;
-  return schedule_and_launch(p, M, K, N, epilogue, workspace, stream);
+  return schedule_and_launch(p, M, K, N, epilogue, workspace, workspace_bytes, stream);
 }
 
 hipError_t launch_linear_qkv(const uint8_t* q, const float* scale, int64_t M, int64_t K,
                              const uint8_t* qw, const float* w_scale, int64_t heads,
                              const uint16_t* bias, const uint16_t* norm_qk, const float* rope_cos,
                              const float* rope_sin, float eps, uint16_t* out_q, uint16_t* out_k,
-                             uint16_t* out_v, void* workspace, hipStream_t stream) {
+                             uint16_t* out_v, void* workspace, uint64_t workspace_bytes,
+                             hipStream_t stream) {
   if (M == 0) return hipSuccess;
   Params p{};
   p.A = q;
@@ -1101,7 +1126,8 @@ hipError_t launch_linear_qkv(const uint8_t* q, const float* scale, int64_t M, in
   p.qkv.out_v = out_v;
   p.qkv.eps = eps;
   p.qkv.heads = (int)heads;
-  return schedule_and_launch(p, M, K, 3 * heads * 128, EPI_QKV, workspace, stream);
+  return schedule_and_launch(p, M, K, 3 * heads * 128, EPI_QKV, workspace, workspace_bytes,
+                             stream);
 }
 
 }  // namespace dq

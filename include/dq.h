@@ -54,7 +54,7 @@ enum {
   DQ_ERR_ALIAS = 4,     /* an output overlaps an input (other than out == residual) */
   DQ_ERR_EPILOGUE = 5,  /* unknown epilogue, or gate/residual missing for the gated one */
   DQ_ERR_HIP = 6,       /* a HIP runtime call failed; see dq_last_hip_error() */
-  DQ_ERR_WORKSPACE = 7, /* workspace too small or not 256-byte aligned */
+  DQ_ERR_WORKSPACE = 7, /* workspace not 256-byte aligned */
   DQ_ERR_VALUE = 8      /* a scalar argument is out of range (eps <= 0, or not finite) */
 };
 
@@ -109,9 +109,9 @@ int dq_quantize_weight_fp8(const void* w, int64_t N, int64_t K, void* qw, float*
  *   residual  bf16 [M, N]    required iff epilogue == DQ_EPI_GATED_RESIDUAL, else ignored;
  *                            may be the same pointer as out (in-place residual update)
  *   out       bf16 [M, N]    output
- *   workspace                NULL (workspace_bytes ignored), or device memory of at least
- *                            dq_linear_fp8_workspace_size(M, K, N) bytes, 256-byte aligned,
- *                            overlapping no other argument
+ *   workspace                NULL (workspace_bytes ignored), or workspace_bytes bytes of device
+ *                            memory, 256-byte aligned, overlapping no other argument, whose
+ *                            first 4096 bytes hold zeros (see below)
  *   acc[m,n] = sum_k dec(q[m,k]) * dec(qw[n,k]) accumulated by the FP8 matrix units into fp32;
  *   v = acc * scale[m] * w_scale[n] + bias[n], then the epilogue, rounded once to bf16 (nearest
  *   even).
@@ -122,11 +122,14 @@ int dq_quantize_weight_fp8(const void* w, int64_t N, int64_t K, void* qw, float*
  * into 2 to 8 equal parts, when a cost model of the device says that is faster: each part is
  * summed in fp32 into the workspace and the last part of a tile to finish adds them up (in a
  * fixed order, so the result does not depend on timing) and applies the epilogue.
- * The workspace must hold zeros before its first use. Its layout is the same for every problem
- * (the partial tiles first, then one arrival counter per tile), and every call that completes
- * leaves all counters at zero again, so one zero fill at allocation is enough and one workspace
- * serves calls of any size in turn. Calls that may run concurrently (other streams, overlapping
- * graph nodes) must not share a workspace.
+ * Workspace layout: bytes [0, 4096) are one arrival counter per cut tile, at the same place for
+ * every problem; they must hold zeros before the first use, and every call that completes
+ * leaves them at zero again, so one zero fill at allocation is enough and one workspace serves
+ * calls of any size in turn. The 256 KiB partial tiles follow. workspace_bytes is a budget: the
+ * library picks the fastest schedule whose partial tiles fit in it, so a workspace of
+ * dq_linear_fp8_workspace_size(M, K, N) bytes gives the schedule it prefers, and a smaller one
+ * (or none) a schedule that needs no more. Calls that may run concurrently (other streams,
+ * overlapping graph nodes) must not share a workspace.
  *
  * Requirements: 0 <= M < 2^31, 128 <= K < 2^24 with K % 128 == 0, 64 <= N < 2^31 with
  * N % 64 == 0, all tensor pointers 16-byte aligned, out overlapping no input except
@@ -161,7 +164,8 @@ int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const
  *   rope_sin    float [M][64]  its sine
  *   eps         float          added to the mean square; finite and > 0 (else DQ_ERR_VALUE)
  *   out_q, out_k, out_v  bf16 [heads][M][128] each
- *   workspace, workspace_bytes  as dq_linear_fp8 (size dq_linear_fp8_workspace_size(M, K, N))
+ *   workspace, workspace_bytes  as dq_linear_fp8 (its preferred size is
+ *                               dq_linear_fp8_workspace_size(M, K, N))
  *
  * Everything after the contraction is fp32; the head's mean square is summed in fp32.
  * Requirements: as dq_linear_fp8 for M, K and N = 3 * heads * 128 with 1 <= heads; every pointer
@@ -279,11 +283,11 @@ int dq_linear_mx_fp8(const void* qa, const void* sa, int64_t M, int64_t K, const
 uint64_t dq_attention_fp8_workspace_size(int64_t H, int64_t S);
 
 /*
- * dq_linear_fp8_workspace_size -- bytes of workspace dq_linear_fp8 uses for an M x K -> N
- * problem (the same on every device), or 0 if the sizes break dq_linear_fp8's requirements:
- * 256 MiB (1024 partial 256 x 256 fp32 tiles) plus 4 bytes per 256 x 256 output tile, rounded up
- * to 256 bytes.
- * Needs no GPU.
+ * dq_linear_fp8_workspace_size -- bytes of workspace the schedule dq_linear_fp8 (and
+ * dq_linear_qkv_fp8, with N = 3 * heads * 128) prefers for an M x K -> N problem on the current
+ * device: 0 when that schedule cuts no tile (then no workspace is needed), else 4096 bytes of
+ * counters plus 256 KiB per part of the cut tiles. Returns 0 for sizes dq_linear_fp8 rejects.
+ * It queries the current device's compute unit count (256 when no device is visible).
  */
 uint64_t dq_linear_fp8_workspace_size(int64_t M, int64_t K, int64_t N);
 

@@ -66,7 +66,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dq_abi_version() == 7
+    assert lib.dq_abi_version() == 8
     for st in range(9):
         s = lib.dq_status_string(st)
         assert s and len(s) > 1
@@ -224,8 +224,7 @@ def test_linear_qkv_argument_checks(lib):
 
 
 def test_linear_qkv_workspace_checks(lib):
-    need = lib.dq_linear_fp8_workspace_size(64, 256, 384)
-    assert qkv(lib, ws=Wk, ws_bytes=need - 1) == WORKSPACE
+    need = 4096 + 4 * 256 * 256 * 4                           # a budget of four partial tiles
     assert qkv(lib, ws=Wk + 16, ws_bytes=need) == WORKSPACE
     assert qkv(lib, ws=Wk, ws_bytes=need, oq=Wk + 4096) == ALIAS
     assert qkv(lib, ws=Wk, ws_bytes=need, cos=Wk + (1 << 20)) == ALIAS
@@ -346,26 +345,35 @@ def test_quantize_v_argument_checks(lib):
 
 
 def test_workspace_size(lib):
+    """The workspace of the schedule dq_linear_fp8 prefers: 0 when it cuts no tile, else 4096
+    bytes of arrival counters plus one 256 x 256 fp32 partial tile (256 KiB) per part. With no
+    GPU visible the query assumes 256 compute units."""
     size = lib.dq_linear_fp8_workspace_size
-    # a fixed region of 1024 partial 256 x 256 fp32 tiles, then one 4-byte counter per
-    # 256 x 256 output tile, rounded up to 256 bytes
-    parts = 1024 * 256 * 256 * 4
-    assert size(4608, 3072, 12288) == parts + 3584                # 18 x 48 tiles
-    assert size(64, 256, 512) == parts + 256                      # 2 tiles
-    assert size(512, 12288, 3072) == parts + 256                  # 24 tiles
-    assert size(16896, 3072, 12288) == parts + 12800              # 66 x 48 tiles, 12672 B
+    part = 256 * 256 * 4
+    # 24 tiles of 96 steps: each cut into 4 parts (96 partial tiles)
+    assert size(512, 12288, 3072) == 4096 + 96 * part
+    # 864 tiles: 96 left over after three rounds run as narrow halves, no cut
+    assert size(4608, 3072, 12288) == 0
+    assert size(64, 256, 512) == 0                                # 2 tiles of 2 steps
+    assert size(16896, 3072, 12288) == 0                          # 3168 tiles, 96 left over
+    assert size(256, 8192, 256) == 4096 + 4 * part                # one tile of 64 steps, 4 parts
+    for M, K, N in [(40, 4096, 192), (600, 5120, 448), (256, 6400, 768), (2304, 3072, 2560)]:
+        s = size(M, K, N)
+        assert s == 0 or (s > 4096 and (s - 4096) % part == 0), (M, K, N, s)
     assert size(64, 192, 512) == 0                                # K % 128
     assert size(64, 256, 96) == 0                                 # N % 64
     assert size(-1, 256, 512) == 0
-    assert size(0, 256, 512) == parts                             # empty problems are valid
+    assert size(0, 256, 512) == 0                                 # empty problems need none
 
 
 def test_linear_workspace_checks(lib):
-    need = lib.dq_linear_fp8_workspace_size(64, 256, 128)
-    assert lin(lib, ws=Wk, ws_bytes=need - 1) == WORKSPACE
+    need = lib.dq_linear_fp8_workspace_size(256, 8192, 256)
+    # the size is a budget (a smaller workspace runs a schedule that fits), so only its
+    # alignment and its overlap with the other arguments are errors
     assert lin(lib, ws=Wk + 16, ws_bytes=need) == WORKSPACE      # not 256-byte aligned
     assert lin(lib, ws=Aq, ws_bytes=need) == ALIAS               # workspace over the codes
     assert lin(lib, ws=Ou, ws_bytes=need) == ALIAS               # workspace over the output
+    assert lin(lib, ws=Aq - 4096, ws_bytes=4097) == ALIAS        # its last byte on the codes
     assert lin(lib, ws=Wk, ws_bytes=need, q=None) == NULL
     assert lin(lib, M=0, ws=Wk, ws_bytes=0) == OK                # empty: nothing is checked
 
@@ -382,8 +390,8 @@ def test_python_binding_names_match_the_c_entry_points():
                  "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
                  "dq_quantize_mx_fp8", "dq_linear_mx_fp8", "dq_linear_fp8_workspace_size"):
         assert callable(getattr(dq, name))
-    assert dq.lib().dq_abi_version() == 7
-    assert dq.dq_linear_fp8_workspace_size(4608, 3072, 12288) == 3584 + 1024 * 262144
+    assert dq.lib().dq_abi_version() == 8
+    assert dq.dq_linear_fp8_workspace_size(512, 12288, 3072) == 4096 + 96 * 262144
 
 
 def test_python_binding_rejects_cpu_tensors():
