@@ -59,6 +59,9 @@ def lib() -> ctypes.CDLL:
         L.dq_linear_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp,
                                     ctypes.c_uint64, vp]
         L.dq_linear_fp8.restype = i32
+        L.dq_linear_fp8_noalloc.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp,
+                                            vp]
+        L.dq_linear_fp8_noalloc.restype = i32
         L.dq_layernorm_modulate_quantize_fp8.argtypes = [vp, i64, i64, vp, vp, ctypes.c_float,
                                                          vp, vp, vp, vp]
         L.dq_layernorm_modulate_quantize_fp8.restype = i32
@@ -236,6 +239,22 @@ def dq_linear_fp8(q, scale, qw, w_scale, bias=None, epilogue="bias", gate=None, 
                                    _ptr(bias), EPILOGUES[epilogue], _ptr(gate), _ptr(residual),
                                    _ptr(out), _ptr(workspace), ws_bytes,
                                    ctypes.c_void_p(st.cuda_stream)), "dq_linear_fp8")
+    return out
+
+
+def dq_linear_fp8_noalloc(q, scale, qw, w_scale, bias=None, epilogue="bias", gate=None,
+                          residual=None, out=None, stream=None):
+    """dq_linear_fp8 on the library's own device scratch: the library allocates nothing (pass
+    `out` to allocate nothing here either). Calls that may overlap on one GPU race."""
+    dev, M, K, N, gate, residual, out = _linear_args(q, scale, qw, w_scale, bias, epilogue, gate,
+                                                     residual, out)
+    with torch.cuda.device(dev):
+        st = stream if stream is not None else torch.cuda.current_stream(dev)
+        _check(lib().dq_linear_fp8_noalloc(_ptr(q), _ptr(scale), M, K, _ptr(qw), _ptr(w_scale), N,
+                                           _ptr(bias), EPILOGUES[epilogue], _ptr(gate),
+                                           _ptr(residual), _ptr(out),
+                                           ctypes.c_void_p(st.cuda_stream)),
+               "dq_linear_fp8_noalloc")
     return out
 
 
@@ -439,7 +458,7 @@ def dq_linear_mx_fp8(qa, sa, qw, sw, bias=None, epilogue="bias", out=None, strea
     return out
 
 
-__all__ = ["dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
+__all__ = ["dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8", "dq_linear_fp8_noalloc",
            "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8", "HEAD_DIM",
            "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
            "quantize_qkv_heads_fp8", "dq_quantize_mx_fp8", "dq_linear_mx_fp8", "MX_BLOCK",

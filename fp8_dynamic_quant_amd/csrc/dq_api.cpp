@@ -145,6 +145,22 @@ int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const
       workspace, workspace ? workspace_bytes : 0, static_cast<hipStream_t>(stream)));
 }
 
+int dq_linear_fp8_noalloc(const void* q, const float* scale, int64_t M, int64_t K,
+                          const void* qw, const float* w_scale, int64_t N, const void* bias,
+                          int epilogue, const void* gate, const void* residual, void* out,
+                          void* stream) {
+  const int st = check_linear_args(q, scale, M, K, qw, w_scale, N, bias, epilogue, gate, residual,
+                                   out, nullptr, 0);
+  if (st != DQ_OK || M == 0) return st;
+  const bool gated = epilogue == DQ_EPI_GATED_RESIDUAL;
+  return hip_status(dq::launch_linear_noalloc(
+      static_cast<const uint8_t*>(q), scale, M, K, static_cast<const uint8_t*>(qw), w_scale, N,
+      static_cast<const uint16_t*>(bias), epilogue,
+      gated ? static_cast<const uint16_t*>(gate) : nullptr,
+      gated ? static_cast<const uint16_t*>(residual) : nullptr, static_cast<uint16_t*>(out),
+      static_cast<hipStream_t>(stream)));
+}
+
 int dq_layernorm_modulate_quantize_fp8(const void* x, int64_t M, int64_t K, const void* mod_scale,
                                        const void* mod_shift, float eps, void* y_out, void* q,
                                        float* scale, void* stream) {

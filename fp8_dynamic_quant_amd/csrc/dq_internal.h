@@ -58,6 +58,15 @@ hipError_t launch_linear(const uint8_t* q, const float* scale, int64_t M, int64_
                          uint16_t* out, void* workspace, uint64_t workspace_bytes,
                          hipStream_t stream);
 
+// The same GEMM with the library's own device scratch (kNoAllocScratchBytes per device, held
+// until the process ends) in place of a caller workspace: nothing is allocated.
+constexpr uint64_t kNoAllocParts = 128;
+constexpr uint64_t kNoAllocScratchBytes = kCounterBytes + kNoAllocParts * kPartialBytes;
+hipError_t launch_linear_noalloc(const uint8_t* q, const float* scale, int64_t M, int64_t K,
+                                 const uint8_t* qw, const float* w_scale, int64_t N,
+                                 const uint16_t* bias, int epilogue, const uint16_t* gate,
+                                 const uint16_t* residual, uint16_t* out, hipStream_t stream);
+
 // FP8 GEMM with the QKV epilogue: N = 3 heads kHeadDim; query and key RMS-normalized per head
 // (weights norm_qk [2][kHeadDim]) and rotated pairwise by rope_cos/sin [M][kHeadDim / 2]; outputs
 // out_q/k/v [heads][M][kHeadDim]. Arguments are already validated.

@@ -55,6 +55,9 @@
 // "Cuantizacion Dinamica FP8".
 #include "dq_internal.h"
 
+#include <atomic>
+#include <mutex>
+
 namespace dq {
 namespace {
 
@@ -1103,6 +1106,66 @@ hipError_t launch_linear(const uint8_t* q, const float* scale, int64_t M, int64_
   p.residual = residual;
   p.out = out;
   return schedule_and_launch(p, M, K, N, epilogue, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------------------------
+// allocation-free entry: the library's own scratch in place of a caller workspace
+// ---------------------------------------------------------------------------------------------
+
+// The scratch: arrival counters, then room for kNoAllocParts partial tiles. Every GPU the
+// library runs on holds its own copy until the process ends; all calls on one GPU share it.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+// Clears the arrival counters before a call that cuts tiles (a call cut short elsewhere could
+// have left them nonzero): a fill kernel, so that a captured graph holds no memset node.
+namespace {
+__global__ void __launch_bounds__(256) clear_counters(uint32_t* c, int n) {
+  for (int i = threadIdx.x; i < n; i += 256) c[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+// The device address of the current device's scratch, looked up once per device (with that
+// device current) and kept. The array's name is only a host-side stand-in for it.
+static hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (ptr == nullptr) {
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (ptr == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return hipSuccess;
+}
+
+hipError_t launch_linear_noalloc(const uint8_t* q, const float* scale, int64_t M, int64_t K,
+                                 const uint8_t* qw, const float* w_scale, int64_t N,
+                                 const uint16_t* bias, int epilogue, const uint16_t* gate,
+                                 const uint16_t* residual, uint16_t* out, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  void* ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  if (choose_plan(M, K, N, compute_units(), kNoAllocScratchBytes).splits > 1) {
+    hipLaunchKernelGGL(clear_counters, dim3(1), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(ws), (int)kMaxCutTiles);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_linear(q, scale, M, K, qw, w_scale, N, bias, epilogue, gate, residual, out, ws,
+                       kNoAllocScratchBytes, stream);
 }
 
 hipError_t launch_linear_qkv(const uint8_t* q, const float* scale, int64_t M, int64_t K,

@@ -141,6 +141,25 @@ int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const
                   uint64_t workspace_bytes, void* stream);
 
 /*
+ * dq_linear_fp8_noalloc -- dq_linear_fp8 for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). The same
+ * arguments without a workspace, the same result, and no hipMalloc, hipFree or allocating
+ * library call: in place of a caller workspace the K-cut schedule uses the library's own device
+ * scratch, a static array of 4096 + 128 * 256 KiB bytes (32 MiB + 4 KiB) that each GPU the
+ * library runs on holds until the process ends. The scratch bounds the schedule, not the
+ * problem: a problem whose preferred cut would need more than the scratch holds runs the best
+ * schedule that fits (whole tiles or narrow halves need none), so every size dq_linear_fp8
+ * accepts is accepted and every size it rejects is rejected with the same status. Before a call
+ * that cuts tiles the scratch's arrival counters are cleared by a small kernel on `stream`.
+ * All calls on one GPU share its scratch: calls that may overlap on one GPU (several streams,
+ * several host threads, overlapping graph nodes) race and must be serialized by the caller.
+ */
+int dq_linear_fp8_noalloc(const void* q, const float* scale, int64_t M, int64_t K,
+                          const void* qw, const float* w_scale, int64_t N, const void* bias,
+                          int epilogue, const void* gate, const void* residual, void* out,
+                          void* stream);
+
+/*
  * dq_linear_qkv_fp8 -- the attention input projection: the W8A8 GEMM of dq_linear_fp8 with an
  * epilogue that splits the output into queries, keys and values, normalizes queries and keys per
  * head and applies the rotary position embedding, all before the single rounding to bf16.

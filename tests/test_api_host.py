@@ -26,6 +26,7 @@ def lib():
     L.dq_quantize_weight_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
     L.dq_linear_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp,
                                 ctypes.c_uint64, vp]
+    L.dq_linear_fp8_noalloc.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp]
     L.dq_layernorm_modulate_quantize_fp8.argtypes = [vp, i64, i64, vp, vp, ctypes.c_float, vp,
                                                      vp, vp, vp]
     L.dq_linear_qkv_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, vp, ctypes.c_float,
@@ -378,6 +379,30 @@ def test_linear_workspace_checks(lib):
     assert lin(lib, M=0, ws=Wk, ws_bytes=0) == OK                # empty: nothing is checked
 
 
+def noalloc(lib, M=64, K=256, N=128, q=Aq, sa=As, qw=Wq, sw=Ws, bias=Bi, epi=BIAS, gate=Ga,
+            res=Re, out=Ou):
+    return lib.dq_linear_fp8_noalloc(q, sa, M, K, qw, sw, N, bias, epi, gate, res, out, None)
+
+
+def test_noalloc_argument_checks(lib):
+    """The allocation-free linear refuses exactly what dq_linear_fp8 refuses, before any HIP
+    call (its scratch limits the schedule, never the problem)."""
+    assert noalloc(lib, M=0) == OK
+    assert noalloc(lib, K=192) == SHAPE
+    assert noalloc(lib, K=1 << 24) == SHAPE
+    assert noalloc(lib, N=96) == SHAPE
+    assert noalloc(lib, M=-1) == SHAPE
+    assert noalloc(lib, epi=3) == EPI
+    assert noalloc(lib, epi=GATED, gate=None) == EPI
+    assert noalloc(lib, q=None) == NULL
+    assert noalloc(lib, out=None) == NULL
+    assert noalloc(lib, qw=Wq + 8) == ALIGN
+    assert noalloc(lib, out=Aq) == ALIAS
+    assert noalloc(lib, epi=GATED, res=Ou + 2) == ALIGN
+    assert noalloc(lib, epi=GATED, res=Ou + 16) == ALIAS        # residual overlaps out, not equal
+    assert lib.dq_last_hip_error() == 0
+
+
 def test_last_hip_error_untouched_by_argument_errors(lib):
     assert lin(lib, K=100) == SHAPE
     assert lib.dq_last_hip_error() == 0
@@ -386,7 +411,7 @@ def test_last_hip_error_untouched_by_argument_errors(lib):
 def test_python_binding_names_match_the_c_entry_points():
     import fp8_dynamic_quant_amd as dq
     for name in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
-                 "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8",
+                 "dq_linear_fp8_noalloc", "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8",
                  "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
                  "dq_quantize_mx_fp8", "dq_linear_mx_fp8", "dq_linear_fp8_workspace_size"):
         assert callable(getattr(dq, name))
