@@ -377,6 +377,83 @@ def bench_mx(shape, seed, steps, warmup, n_sets):
             "quant_bytes": M * K * 2 + M * K + M * K // 32}
 
 
+def bench_text_stream(steps, n_sets=4, seed=21):
+    """The double-stream linears at 1024^2 three ways, quantized inputs already in place: the
+    image stream's linear alone (4096 rows), the text stream's alone (512 rows), and both in one
+    segmented call over the joint 4608 rows. Weights rotate over n_sets sets (cold, as in the
+    step). Event pairs around each call; returns microseconds per call."""
+    import torch
+    import fp8_dynamic_quant_amd as dq
+    from workloads import workload
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    w = workload("flux-dit-step-1024")
+    res = {}
+    for part in ("qkv", "proj", "fc1", "fc2"):
+        img = next(l for l in w.linears if l.name == f"double.img.{part}")
+        txt = next(l for l in w.linears if l.name == f"double.txt.{part}")
+        K, N, epi = img.K, img.N, img.epilogue
+        gated = epi == "gated_residual"
+        x = torch.randn((4608, K), generator=gen, device=dev).to(torch.bfloat16)
+        q, sa = dq.dq_quantize_fp8(x)
+        del x
+        sets = []
+        for _ in range(n_sets):
+            ws = []
+            for _ in range(2):
+                wt = (torch.randn((N, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+                qw, sw = dq.dq_quantize_weight_fp8(wt)
+                del wt
+                b = (torch.randn(N, generator=gen, device=dev) * 0.01).to(torch.bfloat16)
+                g = (1 + 0.1 * torch.randn(N, generator=gen, device=dev)).to(torch.bfloat16)
+                ws.append((qw, sw, b, g))
+            sets.append(ws)
+        out = torch.randn((4608, N), generator=gen, device=dev).to(torch.bfloat16)
+        qt, st_, qi, si = q[:512], sa[:512], q[512:], sa[512:]
+        ot, oi = out[:512], out[512:]
+
+        def one(qq, ss, wsb, o):
+            qw, sw, b, g = wsb
+            dq.dq_linear_fp8(qq, ss, qw, sw, b, epi, g if gated else None, o if gated else None,
+                             out=o)
+
+        def joint(st):
+            dq.dq_linear_fp8_segmented(q, sa, [512, 4096], [st[0][0], st[1][0]],
+                                       [st[0][1], st[1][1]], [st[0][2], st[1][2]], epi,
+                                       [st[0][3], st[1][3]] if gated else None,
+                                       out if gated else None, out=out)
+
+        def timed(fn):
+            for i in range(10):
+                fn(sets[i % n_sets])
+            torch.cuda.synchronize()
+            evs = []
+            for i in range(steps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn(sets[i % n_sets])
+                e1.record()
+                evs.append((e0, e1))
+            torch.cuda.synchronize()
+            return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+
+        qt, st_, qi, si = qt.contiguous(), st_.contiguous(), qi.contiguous(), si.contiguous()
+        ot, oi = ot.contiguous(), oi.contiguous()
+        r = {"image_us": timed(lambda st: one(qi, si, st[1], oi)),
+             "text_us": timed(lambda st: one(qt, st_, st[0], ot)),
+             "joint_us": timed(joint)}
+        r["text_marginal_us"] = r["joint_us"] - r["image_us"]
+        r["separate_us"] = r["image_us"] + r["text_us"]
+        r["flops_joint"] = img.flops + txt.flops
+        res[part] = {k: (round(v, 2) if isinstance(v, float) else v) for k, v in r.items()}
+        del sets, q, sa, out
+        torch.cuda.empty_cache()
+    return res
+
+
 def linear_bytes(M, K, N, epilogue):
     """Compulsory HBM bytes of one FP8 GEMM + epilogue: both code matrices, the bf16 output, the
     scales, bias (and gate + residual when gated)."""
@@ -403,56 +480,67 @@ def dit_floor_ms(w):
 
 
 def bench_dit_step(steps, warmup, breakdown_steps=2, focus="single.linear1"):
-    """All linears of one 1024^2 FLUX-dev denoising step (228 quantize + GEMM pairs), distinct
-    weights per block, timed end to end as one sequence on one stream.
+    """All linears of one 1024^2 FLUX-dev denoising step, distinct weights per block, timed end
+    to end as one sequence on one stream: per double-stream block four calls over the joint
+    sequence (512 text + 4096 image rows, one quantization and one segmented linear each, the
+    text and image weights as two row segments), per single-stream block two (228 weights in
+    152 quantize + linear pairs).
 
-    The timed steps carry one HIP event pair around each GEMM call of the `focus` linear (the
-    step's dominant kernel), on the stream the kernels run on. After them, `breakdown_steps`
-    further steps carry event pairs around every call, for the per-linear table."""
+    The timed steps carry one HIP event pair around each linear call of `focus` (the step's
+    dominant kernel), on the stream the kernels run on. After them, `breakdown_steps` further
+    steps carry event pairs around every call, for the per-call table."""
     import torch
     import fp8_dynamic_quant_amd as dq
     from workloads import dit_step_device_inputs, workload
 
     w = workload("flux-dit-step-1024")
     dev = torch.device("cuda:0")
-    plan, acts, residuals = dit_step_device_inputs(w, dev, dq.dq_quantize_weight_fp8)
+    calls, acts, residuals = dit_step_device_inputs(w, dev, dq.dq_quantize_weight_fp8)
     outs = {}
     qbuf = {}
-    for lin in plan:
-        M, K, N = lin["M"], lin["K"], lin["N"]
+    for c in calls:
+        M, K, N = c["M"], c["K"], c["N"]
         if (M, K) not in qbuf:
             qbuf[(M, K)] = (torch.empty((M, K), dtype=torch.uint8, device=dev),
                             torch.empty((M,), dtype=torch.float32, device=dev))
-        if lin["epilogue"] != "gated_residual" and (M, N) not in outs:
+        if c["epilogue"] != "gated_residual" and (M, N) not in outs:
             outs[(M, N)] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
+    def linear(c, q, sa):
+        segs = c["segments"]
+        gated = c["epilogue"] == "gated_residual"
+        out = residuals[c["residual"]] if gated else outs[(c["M"], c["N"])]
+        if len(segs) == 1:
+            s0 = segs[0]
+            dq.dq_linear_fp8(q, sa, s0["qw"], s0["sw"], s0["bias"], c["epilogue"],
+                             s0["gate"], out if gated else None, out=out)
+        else:
+            dq.dq_linear_fp8_segmented(q, sa, [g["rows"] for g in segs], [g["qw"] for g in segs],
+                                       [g["sw"] for g in segs], [g["bias"] for g in segs],
+                                       c["epilogue"],
+                                       [g["gate"] for g in segs] if gated else None,
+                                       out if gated else None, out=out)
+
     def run(marks=None, all_calls=False):
-        for lin in plan:
-            M, K, N = lin["M"], lin["K"], lin["N"]
-            q, sa = qbuf[(M, K)]
-            timed_call = marks is not None and (all_calls or lin["name"] == focus)
+        for c in calls:
+            q, sa = qbuf[(c["M"], c["K"])]
+            timed_call = marks is not None and (all_calls or c["name"] == focus)
             if timed_call and all_calls:
                 e0 = ev()
                 e0.record()
-            dq.dq_quantize_fp8(acts[lin["act"]], q, sa)
+            dq.dq_quantize_fp8(acts[c["act"]], q, sa)
             if timed_call:
                 e1 = ev()
                 e1.record()
-            if lin["epilogue"] == "gated_residual":
-                r = residuals[lin["residual"]]
-                dq.dq_linear_fp8(q, sa, lin["qw"], lin["sw"], lin["bias"], "gated_residual",
-                                 lin["gate"], r, out=r)
-            else:
-                dq.dq_linear_fp8(q, sa, lin["qw"], lin["sw"], lin["bias"], lin["epilogue"],
-                                 out=outs[(M, N)])
+            linear(c, q, sa)
             if timed_call:
                 e2 = ev()
                 e2.record()
-                marks.append((lin["name"], e0 if all_calls else None, e1, e2))
+                marks.append((c["name"], e0 if all_calls else None, e1, e2))
 
     for _ in range(warmup):
         run()
@@ -477,28 +565,30 @@ def bench_dit_step(steps, warmup, breakdown_steps=2, focus="single.linear1"):
         d["quant"].append(e0.elapsed_time(e1) * 1e3)
         d["gemm"].append(e1.elapsed_time(e2) * 1e3)
     table = {}
-    for l, rep in zip(w.linears, w.repeat):
-        d = by[l.name]
+    for c in calls:
+        if c["name"] in table:
+            table[c["name"]]["per_step"] += 1
+            continue
+        d = by[c["name"]]
         g_us, q_us = float(np.mean(d["gemm"])), float(np.mean(d["quant"]))
-        tf = l.flops / g_us / 1e6
-        qgb = quantizer_bytes(l.M, l.K) / q_us / 1e3
-        table[l.name] = {
-            "shape": [l.M, l.K, l.N], "epilogue": l.epilogue, "per_step": rep,
+        tf = c["flops"] / g_us / 1e6
+        qgb = quantizer_bytes(c["M"], c["K"]) / q_us / 1e3
+        table[c["name"]] = {
+            "shape": [c["M"], c["K"], c["N"]], "epilogue": c["epilogue"],
+            "segments": [g["rows"] for g in c["segments"]], "per_step": 1,
             "gemm_us": round(g_us, 2), "gemm_tflops": round(tf, 1),
             "gemm_frac": round(tf / PEAK_FP8_TFLOPS, 4),
             "quant_us": round(q_us, 2), "quant_gbps": round(qgb, 1),
             "quant_frac": round(qgb / PEAK_HBM_GBPS, 4),
-            "ms_per_step": round(rep * (g_us + q_us) / 1e3, 3),
         }
-    return {"ms": ms, "tflops": w.flops_per_step / ms / 1e9, "linears": len(plan),
-            "weight_bytes": sum(l["N"] * l["K"] for l in plan), "flops": w.flops_per_step,
-            "floor_ms": dit_floor_ms(w), "focus": focus, "focus_gemm_us": focus_us,
-            "focus_calls": len(focus_marks), "breakdown": table}
+    for row in table.values():
+        row["ms_per_step"] = round(row["per_step"] * (row["gemm_us"] + row["quant_us"]) / 1e3, 3)
+    return {"ms": ms, "tflops": w.flops_per_step / ms / 1e9, "calls": len(calls),
+            "linears": sum(len(c["segments"]) for c in calls),
+            "weight_bytes": sum(g["qw"].numel() for c in calls for g in c["segments"]),
+            "flops": w.flops_per_step, "floor_ms": dit_floor_ms(w), "focus": focus,
+            "focus_gemm_us": focus_us, "focus_calls": len(focus_marks), "breakdown": table}
 
-
-# ---------------------------------------------------------------------------------------------
-# CPU baseline: the oracle as it stands, on the host
-# ---------------------------------------------------------------------------------------------
 
 _INPUTS = {}
 
@@ -642,6 +732,7 @@ def main():
     ap.add_argument("--sets", type=int, default=6, help="rotating input/output buffer sets")
     ap.add_argument("--leg-steps", type=int, default=30, help="timed calls per leg")
     ap.add_argument("--no-configs", action="store_true")
+    ap.add_argument("--no-text-stream", action="store_true")
     ap.add_argument("--no-modulate", action="store_true")
     ap.add_argument("--no-qkv", action="store_true")
     ap.add_argument("--no-attention", action="store_true")
@@ -680,7 +771,7 @@ def main():
             f"{d['floor_ms']:.2f} ms); {d['focus']} GEMM {d['focus_gemm_us']:.1f} us "
             f"({ftf:.0f} TFLOP/s)")
         for name, row in d["breakdown"].items():
-            log(f"  {name:16s} x{row['per_step']}: GEMM {row['gemm_us']:7.1f} us "
+            log(f"  {name:16s} x{row['per_step']} {row['segments']}: GEMM {row['gemm_us']:7.1f} us "
                 f"({row['gemm_tflops']:6.0f} TFLOP/s)  quantize {row['quant_us']:6.1f} us "
                 f"({row['quant_gbps']:5.0f} GB/s)  -> {row['ms_per_step']:.2f} ms/step")
         res.update({
@@ -689,6 +780,7 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "fp8_e4m3 (fp32 accumulate, bf16 in/out)", "data": "synthetic",
             "config": {"workload": w.name, "linears_per_step": d["linears"],
+                       "launch_pairs_per_step": d["calls"],
                        "flop_per_step": d["flops"], "weight_bytes_fp8": d["weight_bytes"],
                        "parallelism": "none (1 GPU)"},
             "roofline": {
@@ -705,7 +797,9 @@ def main():
             "dit_step": {"ms": round(d["ms"], 4), "tflops": round(d["tflops"], 1),
                          "roofline_floor_ms": round(d["floor_ms"], 3),
                          "frac": round(d["floor_ms"] / d["ms"], 4),
-                         "breakdown_timing": "event pairs around every call of 2 further steps",
+                         "breakdown_timing": ("event pairs around every call of 2 further "
+                                              "steps; a double-block call covers the text and "
+                                              "the image stream (two row segments)"),
                          "breakdown": d["breakdown"]},
         })
     else:
@@ -728,6 +822,15 @@ def main():
                 "when the left-over tiles run as 256 x 128 halves)")),
             "quantizer": leg["quantizer"],
         })
+    if not args.no_text_stream and w.name == "flux-dit-step-1024":
+        ts = bench_text_stream(ls)
+        for part, r in ts.items():
+            log(f"double.{part}: image {r['image_us']:.1f} us, text {r['text_us']:.1f} us, "
+                f"separate {r['separate_us']:.1f} us; joint segmented {r['joint_us']:.1f} us "
+                f"(text adds {r['text_marginal_us']:.1f} us)")
+        res["text_stream"] = {"timing": "HIP event pair around each call, weights rotating over "
+                                        "4 sets, codes already quantized",
+                              "linears": ts}
     cfg_names = ["tiny-64x256x512", "flux-mlp-up-1024", "flux-single-block-1024",
                  "flux-mlp-up-2048"]
     if not args.no_configs and w.name == "flux-dit-step-1024":

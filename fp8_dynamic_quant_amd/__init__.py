@@ -62,6 +62,11 @@ def lib() -> ctypes.CDLL:
         L.dq_linear_fp8_noalloc.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp,
                                             vp]
         L.dq_linear_fp8_noalloc.restype = i32
+        L.dq_linear_fp8_segmented.argtypes = [vp, vp, i64, i64, vp, vp, vp, i64, vp, i32, vp, vp,
+                                              vp, vp, ctypes.c_uint64, vp]
+        L.dq_linear_fp8_segmented.restype = i32
+        L.dq_linear_fp8_segmented_workspace_size.argtypes = [i64, vp, i64, i64]
+        L.dq_linear_fp8_segmented_workspace_size.restype = ctypes.c_uint64
         L.dq_layernorm_modulate_quantize_fp8.argtypes = [vp, i64, i64, vp, vp, ctypes.c_float,
                                                          vp, vp, vp, vp]
         L.dq_layernorm_modulate_quantize_fp8.restype = i32
@@ -255,6 +260,54 @@ def dq_linear_fp8_noalloc(q, scale, qw, w_scale, bias=None, epilogue="bias", gat
                                            _ptr(residual), _ptr(out),
                                            ctypes.c_void_p(st.cuda_stream)),
                "dq_linear_fp8_noalloc")
+    return out
+
+
+def dq_linear_fp8_segmented_workspace_size(seg_rows, K, N):
+    """Bytes of workspace the preferred schedule of a segmented linear uses (0: none, or invalid
+    sizes)."""
+    rows = (ctypes.c_int64 * len(seg_rows))(*[int(r) for r in seg_rows])
+    return int(lib().dq_linear_fp8_segmented_workspace_size(len(seg_rows), rows, int(K), int(N)))
+
+
+def dq_linear_fp8_segmented(q, scale, seg_rows, qws, w_scales, biases, epilogue="bias",
+                            gates=None, residual=None, out=None, stream=None, workspace="auto"):
+    """The linear over row segments with one weight each, in one launch -> bf16 [M, N].
+
+    q uint8 [M, K], scale f32 [M] for the whole sequence; seg_rows: row counts summing to M;
+    qws / w_scales / biases (/ gates for "gated_residual"): one tensor per segment (a bias may
+    be None). residual and out cover all M rows (out may be residual).
+    """
+    where = "dq_linear_fp8_segmented"
+    nseg = len(seg_rows)
+    if not (1 <= nseg <= 4) or len(qws) != nseg or len(w_scales) != nseg or len(biases) != nseg:
+        raise ValueError(f"{where}: 1 to 4 segments, one weight, scale and bias each")
+    if epilogue == "gated_residual" and (gates is None or len(gates) != nseg):
+        raise ValueError(f"{where}: gated_residual needs one gate per segment")
+    M = sum(int(r) for r in seg_rows)
+    if not isinstance(q, torch.Tensor) or q.dim() != 2 or q.shape[0] != M:
+        raise ValueError(f"{where}: q must be [sum(seg_rows), K]")
+    for i in range(nseg):   # each segment's tensors against the shared ones
+        dev, _, K, N, _, residual, out = _linear_args(
+            q, scale, qws[i], w_scales[i], biases[i], epilogue,
+            gates[i] if epilogue == "gated_residual" else None, residual, out)
+    VP = ctypes.c_void_p * nseg
+    rows = (ctypes.c_int64 * nseg)(*[int(r) for r in seg_rows])
+    ptrs = [VP(*[t.data_ptr() if t is not None else None for t in ts])
+            for ts in (qws, w_scales, biases)]
+    gp = VP(*[t.data_ptr() for t in gates]) if epilogue == "gated_residual" else None
+    with torch.cuda.device(dev):
+        st = stream if stream is not None else torch.cuda.current_stream(dev)
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError(f"workspace must be 'auto', None or a tensor, not {workspace!r}")
+            need = dq_linear_fp8_segmented_workspace_size(seg_rows, K, N)
+            workspace = _cached_workspace(dev, st, need) if (need and M > 0) else None
+        workspace, ws_bytes = _resolve_workspace(workspace, dev, st, M, K, N)
+        _check(lib().dq_linear_fp8_segmented(_ptr(q), _ptr(scale), K, nseg, rows, ptrs[0],
+                                             ptrs[1], N, ptrs[2], EPILOGUES[epilogue], gp,
+                                             _ptr(residual), _ptr(out), _ptr(workspace),
+                                             ws_bytes, ctypes.c_void_p(st.cuda_stream)), where)
     return out
 
 
@@ -459,6 +512,7 @@ def dq_linear_mx_fp8(qa, sa, qw, sw, bias=None, epilogue="bias", out=None, strea
 
 
 __all__ = ["dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8", "dq_linear_fp8_noalloc",
+           "dq_linear_fp8_segmented", "dq_linear_fp8_segmented_workspace_size",
            "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8", "HEAD_DIM",
            "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
            "quantize_qkv_heads_fp8", "dq_quantize_mx_fp8", "dq_linear_mx_fp8", "MX_BLOCK",

@@ -145,6 +145,82 @@ int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const
       workspace, workspace ? workspace_bytes : 0, static_cast<hipStream_t>(stream)));
 }
 
+// Checks of dq_linear_fp8_segmented; on success *M_out is the total row count.
+static int check_segmented(const void* q, const float* scale, int64_t K, int64_t nseg,
+                           const int64_t* seg_rows, const void* const* qw,
+                           const float* const* w_scale, int64_t N, const void* const* bias,
+                           int epilogue, const void* const* gate, const void* residual,
+                           const void* out, const void* workspace, uint64_t workspace_bytes,
+                           int64_t* M_out) {
+  if (nseg < 1 || nseg > dq::kMaxSegments) return DQ_ERR_SHAPE;
+  if (!seg_rows || !qw || !w_scale || !bias) return DQ_ERR_NULL;
+  int64_t M = 0, tiles_m = 0;
+  for (int64_t i = 0; i < nseg; ++i) {
+    if (seg_rows[i] < 0 || seg_rows[i] > kMaxDim - M) return DQ_ERR_SHAPE;
+    M += seg_rows[i];
+    tiles_m += (seg_rows[i] + dq::kTileM - 1) / dq::kTileM;
+  }
+  const int shape = check_linear_shape(M, K, N);
+  if (shape != DQ_OK) return shape;
+  if (tiles_m * ((N + dq::kTileN - 1) / dq::kTileN) * (K / dq::kStepK) >= (int64_t(1) << 31))
+    return DQ_ERR_SHAPE;
+  if (epilogue != DQ_EPI_BIAS && epilogue != DQ_EPI_GELU_TANH &&
+      epilogue != DQ_EPI_GATED_RESIDUAL)
+    return DQ_ERR_EPILOGUE;
+  const bool gated = epilogue == DQ_EPI_GATED_RESIDUAL;
+  if (gated && (!gate || !residual)) return DQ_ERR_EPILOGUE;
+  *M_out = M;
+  if (M == 0) return DQ_OK;
+  // every segment's weight, scales, bias and gate with the shared row-indexed tensors, as
+  // dq_linear_fp8 checks them
+  for (int64_t i = 0; i < nseg; ++i) {
+    if (gated && !gate[i]) return DQ_ERR_EPILOGUE;
+    const int st = check_linear_args(q, scale, M, K, qw[i], w_scale[i], N, bias[i], epilogue,
+                                     gated ? gate[i] : nullptr, residual, out, workspace,
+                                     workspace_bytes);
+    if (st != DQ_OK) return st;
+  }
+  return DQ_OK;
+}
+
+int dq_linear_fp8_segmented(const void* q, const float* scale, int64_t K, int64_t nseg,
+                            const int64_t* seg_rows, const void* const* qw,
+                            const float* const* w_scale, int64_t N, const void* const* bias,
+                            int epilogue, const void* const* gate, const void* residual,
+                            void* out, void* workspace, uint64_t workspace_bytes, void* stream) {
+  int64_t M = 0;
+  const int st = check_segmented(q, scale, K, nseg, seg_rows, qw, w_scale, N, bias, epilogue,
+                                 gate, residual, out, workspace, workspace_bytes, &M);
+  if (st != DQ_OK || M == 0) return st;
+  const bool gated = epilogue == DQ_EPI_GATED_RESIDUAL;
+  const uint8_t* w[dq::kMaxSegments];
+  const float* ws[dq::kMaxSegments];
+  const uint16_t* b[dq::kMaxSegments];
+  const uint16_t* g[dq::kMaxSegments];
+  for (int64_t i = 0; i < nseg; ++i) {
+    w[i] = static_cast<const uint8_t*>(qw[i]);
+    ws[i] = w_scale[i];
+    b[i] = static_cast<const uint16_t*>(bias[i]);
+    g[i] = gated ? static_cast<const uint16_t*>(gate[i]) : nullptr;
+  }
+  return hip_status(dq::launch_linear_segmented(
+      static_cast<const uint8_t*>(q), scale, nseg, seg_rows, K, w, ws, N, b, epilogue, g,
+      gated ? static_cast<const uint16_t*>(residual) : nullptr, static_cast<uint16_t*>(out),
+      workspace, workspace ? workspace_bytes : 0, static_cast<hipStream_t>(stream)));
+}
+
+uint64_t dq_linear_fp8_segmented_workspace_size(int64_t nseg, const int64_t* seg_rows, int64_t K,
+                                                int64_t N) {
+  if (nseg < 1 || nseg > dq::kMaxSegments || !seg_rows) return 0;
+  int64_t M = 0;
+  for (int64_t i = 0; i < nseg; ++i) {
+    if (seg_rows[i] < 0 || seg_rows[i] > kMaxDim - M) return 0;
+    M += seg_rows[i];
+  }
+  if (check_linear_shape(M, K, N) != DQ_OK) return 0;
+  return dq::linear_segmented_workspace_bytes(nseg, seg_rows, K, N);
+}
+
 int dq_linear_fp8_noalloc(const void* q, const float* scale, int64_t M, int64_t K,
                           const void* qw, const float* w_scale, int64_t N, const void* bias,
                           int epilogue, const void* gate, const void* residual, void* out,

@@ -58,6 +58,22 @@ hipError_t launch_linear(const uint8_t* q, const float* scale, int64_t M, int64_
                          uint16_t* out, void* workspace, uint64_t workspace_bytes,
                          hipStream_t stream);
 
+// The GEMM over nseg <= kMaxSegments row segments of q (seg_rows, a host array; segment s is
+// rows [sum of seg_rows[< s], + seg_rows[s]) of q, scale, residual and out) each with its own
+// weight, scales, bias and gate (host arrays of device pointers), in one launch. Arguments are
+// already validated.
+constexpr int64_t kMaxSegments = 4;
+hipError_t launch_linear_segmented(const uint8_t* q, const float* scale, int64_t nseg,
+                                   const int64_t* seg_rows, int64_t K,
+                                   const uint8_t* const* qw, const float* const* w_scale,
+                                   int64_t N, const uint16_t* const* bias, int epilogue,
+                                   const uint16_t* const* gate, const uint16_t* residual,
+                                   uint16_t* out, void* workspace, uint64_t workspace_bytes,
+                                   hipStream_t stream);
+// linear_workspace_bytes for a segmented problem.
+uint64_t linear_segmented_workspace_bytes(int64_t nseg, const int64_t* seg_rows, int64_t K,
+                                          int64_t N);
+
 // The same GEMM with the library's own device scratch (kNoAllocScratchBytes per device, held
 // until the process ends) in place of a caller workspace: nothing is allocated.
 constexpr uint64_t kNoAllocParts = 128;

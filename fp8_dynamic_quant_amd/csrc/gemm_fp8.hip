@@ -74,6 +74,7 @@ constexpr int kParamBytes = 4096;               // sa f32[256] | sw f32[256] | b
 constexpr int kParamBufs = 3;                   // part i of a share uses buffer i % 3
 constexpr int kGroupM = 4;                      // tile rows per group in the tile order
 constexpr int kPartFloats = kBM * kBN;
+constexpr int kMaxSeg = (int)kMaxSegments;      // row segments with their own weights
 
 enum { EPI_BIAS = 0, EPI_GELU_TANH = 1, EPI_GATED_RESIDUAL = 2, EPI_QKV = 3 };
 
@@ -91,13 +92,22 @@ struct QkvArgs {
   int heads;
 };
 
+// Row segments: rows [row0[s], row0[s + 1]) of q, scale, residual and out use the weight of
+// segment s. A segment's tile rows are its own (a tile never spans two segments): segment s
+// owns tile rows [trow0[s], trow0[s + 1]). Read where used, through seg_args().
+struct SegArgs {
+  const uint8_t* B[kMaxSeg];       // qw [N, K] of each segment
+  const float* sw[kMaxSeg];        // [N]
+  const uint16_t* bias[kMaxSeg];   // [N] or null
+  const uint16_t* gate[kMaxSeg];   // [N] (gated only)
+  int row0[kMaxSeg + 1];
+  int trow0[kMaxSeg + 1];
+  int nseg;
+};
+
 struct Params {
   const uint8_t* A;          // q  [M, K]
-  const uint8_t* B;          // qw [N, K]
   const float* sa;           // [M]
-  const float* sw;           // [N]
-  const uint16_t* bias;      // [N] or null
-  const uint16_t* gate;      // [N] (gated only)
   const uint16_t* residual;  // [M, N] (gated only; may equal out)
   uint16_t* out;             // [M, N]
   uint32_t* flags;           // [left-over tiles] arrival counters (cut tiles only)
@@ -111,6 +121,7 @@ struct Params {
   int part_steps;            // nk / splits
   int narrow;                // 1: each left-over tile runs as two 256 x 128 halves (not cut)
   QkvArgs qkv;               // QKV epilogue only (N = 3 heads 128); read through qkv_args()
+  SegArgs seg;               // per-segment weights and rows; read through seg_args()
 };
 
 // The kernel's own copy of Params.qkv, read from the kernel argument segment at the point of
@@ -129,6 +140,17 @@ __device__ __forceinline__ QkvArgs qkv_args() {
   a.eps = kp->qkv.eps;
   a.heads = kp->qkv.heads;
   return a;
+}
+
+typedef const __attribute__((address_space(4))) SegArgs* KSeg;
+
+// The kernel's own copy of Params.seg, in the kernel argument segment (scalar loads at the point
+// of use, as for qkv_args()).
+__device__ __forceinline__ KSeg seg_args() {
+  typedef const __attribute__((address_space(4))) Params* KParams;
+  KParams kp = (KParams)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(kp));
+  return &kp->seg;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -152,6 +174,20 @@ __device__ __forceinline__ void copy_to_lds(v4i rsrc, uint32_t voff, uint32_t ld
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %3\n\t"
       "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(lds_base)
+      : "memory");
+}
+
+// 4 bytes per lane from global memory straight into LDS at lds_base + 4 * lane (64 lanes: 256
+// bytes). Any 4-byte aligned source works.
+__device__ __forceinline__ void copy_to_lds_b32(v4i rsrc, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(voff), "s"(rsrc), "s"(lds_base)
@@ -243,41 +279,59 @@ __device__ __forceinline__ void cursor_next(const Params& p, const Work& w, int 
   }
 }
 
-__device__ __forceinline__ void tile_origin(const Params& p, int t, int& m0, int& n0) {
+// Geometry of a work item: its origin, the end of its row segment and the segment.
+struct Geo {
+  int m0, n0, mend, s;
+};
+
+// Tile t: tile rows are walked kGroupM at a time (every column of a group of tile rows, then the
+// next group); tile row tr belongs to the last segment whose first tile row is <= tr.
+__device__ __forceinline__ Geo tile_geo(const Params& p, int t) {
   const int per_group = kGroupM * p.tilesN;
   const int grp = t / per_group;
   const int first_m = grp * kGroupM;
   const int gsz = (p.tilesM - first_m) < kGroupM ? (p.tilesM - first_m) : kGroupM;
   const int tin = t - grp * per_group;
-  m0 = (first_m + tin % gsz) * kBM;
-  n0 = (tin / gsz) * kBN;
+  const int tr = first_m + tin % gsz;
+  const KSeg sg = seg_args();
+  int s = 0;
+  for (int i = 1; i < sg->nseg; ++i)
+    if (tr >= sg->trow0[i]) s = i;
+  Geo g;
+  g.s = s;
+  g.m0 = sg->row0[s] + (tr - sg->trow0[s]) * kBM;
+  g.mend = sg->row0[s + 1];
+  g.n0 = (tin / gsz) * kBN;
+  return g;
+}
+
+// Tile t, or its 128-column half (half >= 0, narrow launches only).
+template <int NB>
+__device__ __forceinline__ Geo item_geo(const Params& p, int t, int half) {
+  Geo g = tile_geo(p, t);
+  if (NB == 1) g.n0 += half * (kBN / 2);
+  return g;
 }
 
 struct TileDesc {
-  int m0, n0;  // origin of the tile (of the half, in a narrow launch)
+  Geo g;  // origin of the tile (of the half, in a narrow launch), segment end, segment
   v4i rsA, rsB;
 };
 
-// Descriptors of a tile or of one half of it: rows past M (N) are out of range and read as
-// zero (a half entirely past N has an empty B range).
-// Origin of tile t, or of its 128-column half (half >= 0, narrow launches only).
-template <int NB>
-__device__ __forceinline__ void item_origin(const Params& p, int t, int half, int& m0, int& n0) {
-  tile_origin(p, t, m0, n0);
-  if (NB == 1) n0 += half * (kBN / 2);
-}
-
+// Descriptors of a tile or of one half of it: rows past the segment end (columns past N) are out
+// of range and read as zero (a half entirely past N has an empty B range).
 template <int NB>
 __device__ __forceinline__ TileDesc tile_desc(const Params& p, int t, int half) {
   TileDesc d;
-  item_origin<NB>(p, t, half, d.m0, d.n0);
-  const int m0 = d.m0, n0 = d.n0;
+  d.g = item_geo<NB>(p, t, half);
+  const int m0 = d.g.m0, n0 = d.g.n0;
   const int width = NB == 1 ? kBN / 2 : kBN;
   const int rb = p.N - n0 < width ? p.N - n0 : width;
-  const uint32_t rowsA = (uint32_t)(p.M - m0 < kBM ? p.M - m0 : kBM);
+  const uint32_t rowsA = (uint32_t)(d.g.mend - m0 < kBM ? d.g.mend - m0 : kBM);
   const uint32_t rowsB = (uint32_t)(rb > 0 ? rb : 0);
   d.rsA = buffer_rsrc(p.A + (size_t)m0 * (size_t)p.K, rowsA * (uint32_t)p.K);
-  d.rsB = buffer_rsrc(p.B + (size_t)(rb > 0 ? n0 : 0) * (size_t)p.K, rowsB * (uint32_t)p.K);
+  d.rsB = buffer_rsrc(seg_args()->B[d.g.s] + (size_t)(rb > 0 ? n0 : 0) * (size_t)p.K,
+                      rowsB * (uint32_t)p.K);
   return d;
 }
 
@@ -357,23 +411,29 @@ __device__ __forceinline__ void copy_batch(const TileDesc& d, uint32_t K, int k,
 template <int EPI>
 __device__ __forceinline__ void copy_params(const Params& p, const TileDesc& d, uint8_t* pb, int q,
                                             int lane) {
-  const int m0 = d.m0;
-  int n0 = d.n0;
+  const int m0 = d.g.m0;
+  int n0 = d.g.n0;
   const uint32_t lp = __builtin_amdgcn_readfirstlane(lds_addr(pb) + (uint32_t)(q * 1024));
   const uint32_t lo = (uint32_t)lane * 16u;
-  const uint32_t rows = (uint32_t)(p.M - m0 < kBM ? p.M - m0 : kBM);
+  const uint32_t rows = (uint32_t)(d.g.mend - m0 < kBM ? d.g.mend - m0 : kBM);
+  const KSeg sg = seg_args();
+  const int s = d.g.s;
   // columns of this tile that exist: none for a narrow half that lies past N
   const int nc = p.N - n0 < kBN ? p.N - n0 : kBN;
   const uint32_t cols = (uint32_t)(nc > 0 ? nc : 0);
   if (nc <= 0) n0 = 0;
   if (q == 0) {
-    copy_to_lds(buffer_rsrc(p.sa + m0, rows * 4u), lo, lp);
+    // a segment may start at any row, so the scales move 4 bytes per lane (4 x 64 of them)
+    const v4i rs = buffer_rsrc(p.sa + m0, rows * 4u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) copy_to_lds_b32(rs, (uint32_t)(j * 256 + lane * 4), lp + j * 256u);
   } else if (q == 1) {
-    copy_to_lds(buffer_rsrc(p.sw + n0, cols * 4u), lo, lp);
+    copy_to_lds(buffer_rsrc(sg->sw[s] + n0, cols * 4u), lo, lp);
   } else if (q == 2) {
-    copy_to_lds(buffer_rsrc(p.bias + n0, p.bias ? cols * 2u : 0u), lo, lp);
+    const uint16_t* bias = sg->bias[s];
+    copy_to_lds(buffer_rsrc(bias + n0, bias ? cols * 2u : 0u), lo, lp);
   } else if (EPI == EPI_GATED_RESIDUAL) {
-    copy_to_lds(buffer_rsrc(p.gate + n0, cols * 2u), lo, lp);
+    copy_to_lds(buffer_rsrc(sg->gate[s] + n0, cols * 2u), lo, lp);
   } else if (EPI == EPI_QKV) {
     copy_to_lds(buffer_rsrc(qkv_args().norm_qk, 512u), lo, lp);
   }
@@ -468,7 +528,7 @@ __device__ __forceinline__ void swap_halves(float& a, float& b) {
 // activation or the gated residual there, and stores 16 bytes.
 template <int EPI, int NB>
 __device__ __forceinline__ void epilogue(const v16f (&acc)[NB][4], const Params& p, int m0, int n0,
-                                         int wm, int wn, int lane, const uint8_t* pb) {
+                                         int mend, int wm, int wn, int lane, const uint8_t* pb) {
   const float* s_sa = reinterpret_cast<const float*>(pb);
   const float* s_sw = reinterpret_cast<const float*>(pb + 1024);
   const uint16_t* s_b = reinterpret_cast<const uint16_t*>(pb + 2048);
@@ -507,7 +567,7 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[NB][4], const Params&
 #pragma unroll
           for (int j = 0; j < 8; ++j) y[j] = gelu_tanh(y[j]);
         }
-        const bool live = m < p.M && n < p.N;
+        const bool live = m < mend && n < p.N;
         const size_t off = (size_t)m * (size_t)p.N + (size_t)n;
         if (EPI == EPI_GATED_RESIDUAL) {
           const uint4 gg = *reinterpret_cast<const uint4*>(s_g + nl);
@@ -913,8 +973,8 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
       wait_vmem_but4();
       phase_barrier();
     }
-    int m0, n0;
-    item_origin<NB>(p, t, half, m0, n0);
+    const Geo gi = item_geo<NB>(p, t, half);
+    const int m0 = gi.m0, n0 = gi.n0;
     const uint8_t* pb = pbuf + (part % kParamBufs) * kParamBytes;
     // the QKV epilogue exchanges sums between the groups, so like a cut tile it first aligns
     // them; its scratch is the parameter buffer of the item after next (free until then)
@@ -929,7 +989,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
         if constexpr (EPI == EPI_QKV)
           epilogue_qkv<2>(acc, p, m0, n0, wm, wn, lane, pb, scratch);
         else
-          epilogue<EPI, 2>(acc, p, m0, n0, wm, wn, lane, pb);
+          epilogue<EPI, 2>(acc, p, m0, n0, gi.mend, wm, wn, lane, pb);
       }
       if (align && g == 1) phase_barrier();  // back to one phase behind
     } else {
@@ -938,7 +998,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
         epilogue_qkv<1>(acc, p, m0, n0, wm, wn, lane, pb, scratch);
         if (g == 1) phase_barrier();
       } else {
-        epilogue<EPI, 1>(acc, p, m0, n0, wm, wn, lane, pb);
+        epilogue<EPI, 1>(acc, p, m0, n0, gi.mend, wm, wn, lane, pb);
       }
     }
     ++part;
@@ -1006,9 +1066,9 @@ struct Plan {
 //     finishes a tile loads the s - 1 others; a partial tile moves at the compute unit's share
 //     of HBM bandwidth (at most about 60 GB/s for one unit, 5.6 TB/s for the chip; one step is
 //     about 1.5 us on a busy chip). A cut must win by 20 %.
-static Plan choose_plan(int64_t M, int64_t K, int64_t N, int64_t cus, uint64_t budget) {
+static Plan choose_plan(int64_t tilesM, int64_t K, int64_t N, int64_t cus, uint64_t budget) {
   Plan pl;
-  const int64_t tiles = linear_tiles(M, N), nk = K / kBK;
+  const int64_t tiles = tilesM * ((N + kBN - 1) / kBN), nk = K / kBK;
   pl.grid = tiles < cus ? tiles : cus;
   const int64_t rounds = tiles / cus;
   pl.dp_tiles = rounds * cus;
@@ -1054,18 +1114,18 @@ static Plan choose_plan(int64_t M, int64_t K, int64_t N, int64_t cus, uint64_t b
   return pl;
 }
 
-// Sizes and schedule into a Params whose pointers are set, then the launches.
+// Sizes and schedule into a Params whose pointers and segments are set, then the launches.
 static hipError_t schedule_and_launch(Params& p, int64_t M, int64_t K, int64_t N, int epilogue,
                                       void* workspace, uint64_t workspace_bytes,
                                       hipStream_t stream) {
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
-  p.tilesM = (int)((M + kBM - 1) / kBM);
+  p.tilesM = p.seg.trow0[p.seg.nseg];
   p.tilesN = (int)((N + kBN - 1) / kBN);
   p.nk = (int)(K / kBK);
-  p.tiles = (int)linear_tiles(M, N);
-  const Plan pl = choose_plan(M, K, N, compute_units(), workspace ? workspace_bytes : 0);
+  p.tiles = p.tilesM * p.tilesN;
+  const Plan pl = choose_plan(p.tilesM, K, N, compute_units(), workspace ? workspace_bytes : 0);
   p.dp_tiles = (int)pl.dp_tiles;
   p.tail0 = (int)pl.dp_tiles;
   p.tail_tiles = (int)pl.left;
@@ -1085,9 +1145,33 @@ static hipError_t schedule_and_launch(Params& p, int64_t M, int64_t K, int64_t N
   }
 }
 
+// Row segments of nseg sizes (host array) into p.seg's rows and tile rows; the caller sets the
+// per-segment pointers. Returns the total number of rows.
+static int64_t set_segments(Params& p, int64_t nseg, const int64_t* rows) {
+  p.seg.nseg = (int)nseg;
+  int64_t r = 0, tr = 0;
+  for (int64_t i = 0; i < nseg; ++i) {
+    p.seg.row0[i] = (int)r;
+    p.seg.trow0[i] = (int)tr;
+    r += rows[i];
+    tr += (rows[i] + kBM - 1) / kBM;
+  }
+  p.seg.row0[nseg] = (int)r;
+  p.seg.trow0[nseg] = (int)tr;
+  return r;
+}
+
 uint64_t linear_workspace_bytes(int64_t M, int64_t K, int64_t N) {
   if (M == 0) return 0;
-  return choose_plan(M, K, N, compute_units(), ~uint64_t(0)).workspace;
+  return choose_plan((M + kBM - 1) / kBM, K, N, compute_units(), ~uint64_t(0)).workspace;
+}
+
+uint64_t linear_segmented_workspace_bytes(int64_t nseg, const int64_t* rows, int64_t K,
+                                          int64_t N) {
+  int64_t tiles_m = 0;
+  for (int64_t i = 0; i < nseg; ++i) tiles_m += (rows[i] + kBM - 1) / kBM;
+  if (tiles_m == 0) return 0;
+  return choose_plan(tiles_m, K, N, compute_units(), ~uint64_t(0)).workspace;
 }
 
 hipError_t launch_linear(const uint8_t* q, const float* scale, int64_t M, int64_t K,
@@ -1095,16 +1179,30 @@ hipError_t launch_linear(const uint8_t* q, const float* scale, int64_t M, int64_
                          int epilogue, const uint16_t* gate, const uint16_t* residual,
                          uint16_t* out, void* workspace, uint64_t workspace_bytes,
                          hipStream_t stream) {
-  if (M == 0) return hipSuccess;
+  return launch_linear_segmented(q, scale, 1, &M, K, &qw, &w_scale, N, &bias, epilogue, &gate,
+                                 residual, out, workspace, workspace_bytes, stream);
+}
+
+hipError_t launch_linear_segmented(const uint8_t* q, const float* scale, int64_t nseg,
+                                   const int64_t* seg_rows, int64_t K,
+                                   const uint8_t* const* qw, const float* const* w_scale,
+                                   int64_t N, const uint16_t* const* bias, int epilogue,
+                                   const uint16_t* const* gate, const uint16_t* residual,
+                                   uint16_t* out, void* workspace, uint64_t workspace_bytes,
+                                   hipStream_t stream) {
   Params p{};
+  const int64_t M = set_segments(p, nseg, seg_rows);
+  if (M == 0) return hipSuccess;
   p.A = q;
-  p.B = qw;
   p.sa = scale;
-  p.sw = w_scale;
-  p.bias = bias;
-  p.gate = gate;
   p.residual = residual;
   p.out = out;
+  for (int64_t i = 0; i < nseg; ++i) {
+    p.seg.B[i] = qw[i];
+    p.seg.sw[i] = w_scale[i];
+    p.seg.bias[i] = bias[i];
+    p.seg.gate[i] = gate[i];
+  }
   return schedule_and_launch(p, M, K, N, epilogue, workspace, workspace_bytes, stream);
 }
 
@@ -1158,7 +1256,7 @@ hipError_t launch_linear_noalloc(const uint8_t* q, const float* scale, int64_t M
   void* ws = nullptr;
   hipError_t e = scratch_address(&ws);
   if (e != hipSuccess) return e;
-  if (choose_plan(M, K, N, compute_units(), kNoAllocScratchBytes).splits > 1) {
+  if (choose_plan((M + kBM - 1) / kBM, K, N, compute_units(), kNoAllocScratchBytes).splits > 1) {
     hipLaunchKernelGGL(clear_counters, dim3(1), dim3(256), 0, stream,
                        static_cast<uint32_t*>(ws), (int)kMaxCutTiles);
     e = hipGetLastError();
@@ -1176,11 +1274,12 @@ hipError_t launch_linear_qkv(const uint8_t* q, const float* scale, int64_t M, in
                              hipStream_t stream) {
   if (M == 0) return hipSuccess;
   Params p{};
+  set_segments(p, 1, &M);
   p.A = q;
-  p.B = qw;
   p.sa = scale;
-  p.sw = w_scale;
-  p.bias = bias;
+  p.seg.B[0] = qw;
+  p.seg.sw[0] = w_scale;
+  p.seg.bias[0] = bias;
   p.qkv.norm_qk = norm_qk;
   p.qkv.rope_cos = rope_cos;
   p.qkv.rope_sin = rope_sin;

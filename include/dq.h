@@ -141,6 +141,43 @@ int dq_linear_fp8(const void* q, const float* scale, int64_t M, int64_t K, const
                   uint64_t workspace_bytes, void* stream);
 
 /*
+ * dq_linear_fp8_segmented -- dq_linear_fp8 over a token sequence made of row segments that each
+ * have their own weight, in one launch. FLUX-dev is a hybrid of multimodal and parallel
+ * transformer blocks (page "WaveSpeedAI X DataCrunch: Inferencia de Imagenes FLUX en Tiempo Real
+ * en B200", section "FLUX-Dev"); the reading taken for its multimodal (double-stream) blocks is
+ * the public architecture's: text and image tokens form one joint sequence for attention, but
+ * every linear layer has one weight for the text tokens and another for the image tokens. One
+ * call runs both: the text stream's few tiles then fill the compute units the image stream's
+ * last round leaves idle, instead of running as a separate, mostly idle launch.
+ *
+ *   q, scale   uint8 [M, K] codes and float [M] scales of the whole sequence (dq_quantize_fp8
+ *              quantizes each row on its own, so one call covers every segment)
+ *   nseg       1 <= nseg <= 4 segments; seg_rows[s] >= 0 (HOST array) is the row count of
+ *              segment s: rows [seg_rows[0] + ... + seg_rows[s - 1], + seg_rows[s]); M is their
+ *              sum
+ *   qw[s], w_scale[s], bias[s], gate[s]  HOST arrays of nseg DEVICE pointers: segment s's
+ *              weight codes [N, K], scales [N], bias [N] (NULL = zero), gate [N] (required iff
+ *              gated; gate itself may be NULL otherwise)
+ *   epilogue, residual, out, workspace, workspace_bytes  as dq_linear_fp8, over all M rows
+ * Row m of out is exactly what dq_linear_fp8 gives for that row with its segment's weight (a
+ * tile never spans two segments).
+ * Requirements: as dq_linear_fp8 for M, K, N and every segment's tensors; the preferred
+ * workspace size is dq_linear_fp8_segmented_workspace_size(nseg, seg_rows, K, N).
+ */
+int dq_linear_fp8_segmented(const void* q, const float* scale, int64_t K, int64_t nseg,
+                            const int64_t* seg_rows, const void* const* qw,
+                            const float* const* w_scale, int64_t N, const void* const* bias,
+                            int epilogue, const void* const* gate, const void* residual,
+                            void* out, void* workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * dq_linear_fp8_segmented_workspace_size -- dq_linear_fp8_workspace_size for a segmented call
+ * (0 for invalid sizes).
+ */
+uint64_t dq_linear_fp8_segmented_workspace_size(int64_t nseg, const int64_t* seg_rows, int64_t K,
+                                                int64_t N);
+
+/*
  * dq_linear_fp8_noalloc -- dq_linear_fp8 for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). The same
  * arguments without a workspace, the same result, and no hipMalloc, hipFree or allocating

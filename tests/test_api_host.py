@@ -27,6 +27,10 @@ def lib():
     L.dq_linear_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp,
                                 ctypes.c_uint64, vp]
     L.dq_linear_fp8_noalloc.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp]
+    L.dq_linear_fp8_segmented.argtypes = [vp, vp, i64, i64, vp, vp, vp, i64, vp, i32, vp, vp, vp,
+                                          vp, ctypes.c_uint64, vp]
+    L.dq_linear_fp8_segmented_workspace_size.argtypes = [i64, vp, i64, i64]
+    L.dq_linear_fp8_segmented_workspace_size.restype = ctypes.c_uint64
     L.dq_layernorm_modulate_quantize_fp8.argtypes = [vp, i64, i64, vp, vp, ctypes.c_float, vp,
                                                      vp, vp, vp]
     L.dq_linear_qkv_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, vp, ctypes.c_float,
@@ -403,6 +407,58 @@ def test_noalloc_argument_checks(lib):
     assert lib.dq_last_hip_error() == 0
 
 
+W2q, W2s, B2, G2 = (0x1000000 * i for i in range(10, 14))   # the second segment's tensors
+
+
+def seg(lib, rows=(64, 32), K=256, N=128, q=Aq, sa=As, qw=(Wq, W2q), sw=(Ws, W2s), bias=(Bi, B2),
+        epi=BIAS, gate=(Ga, G2), res=Re, out=Ou, ws=None, ws_bytes=0, arrays=True):
+    n = len(rows)
+    R = ctypes.c_int64 * max(n, 1)
+    arr = lambda t: (ctypes.c_void_p * len(t))(*t) if (arrays and t is not None) else None
+    return lib.dq_linear_fp8_segmented(q, sa, K, n, R(*rows) if arrays else None, arr(qw),
+                                       arr(sw), N, arr(bias), epi, arr(gate), res, out, ws,
+                                       ws_bytes, None)
+
+
+def test_segmented_argument_checks(lib):
+    """Every segment's tensors are checked as dq_linear_fp8 checks its weight, before any HIP
+    call; rows are counted per segment."""
+    assert seg(lib, rows=(0, 0)) == OK                           # empty: nothing launched
+    assert seg(lib, rows=()) == SHAPE                            # no segment
+    assert seg(lib, rows=(1,) * 5, qw=(Wq,) * 5, sw=(Ws,) * 5, bias=(Bi,) * 5,
+               gate=(Ga,) * 5) == SHAPE                          # more than four
+    assert seg(lib, rows=(64, -1)) == SHAPE
+    assert seg(lib, K=192) == SHAPE
+    assert seg(lib, N=96) == SHAPE
+    assert seg(lib, arrays=False) == NULL                        # host arrays missing
+    assert seg(lib, epi=5) == EPI
+    assert seg(lib, epi=GATED, gate=(Ga, None)) == EPI           # a segment without a gate
+    assert seg(lib, epi=GATED, res=None) == EPI
+    assert seg(lib, qw=(Wq, None)) == NULL
+    assert seg(lib, sw=(Ws + 4, W2s)) == ALIGN
+    assert seg(lib, bias=(Bi, B2 + 2)) == ALIGN
+    assert seg(lib, out=W2q) == ALIAS                            # out over the second weight
+    assert seg(lib, ws=Wk + 64, ws_bytes=4096) == WORKSPACE
+    assert seg(lib, ws=Ou - 256, ws_bytes=4096) == ALIAS
+    assert lib.dq_last_hip_error() == 0
+
+
+def test_segmented_workspace_size(lib):
+    size = lib.dq_linear_fp8_segmented_workspace_size
+    R = ctypes.c_int64 * 2
+    part = 256 * 256 * 4
+    # 512 text rows + 4096 image rows: 18 tile rows, as one 4608-row problem
+    assert size(2, R(512, 4096), 12288, 3072) == lib.dq_linear_fp8_workspace_size(4608, 12288, 3072)
+    # two segments of 256 rows and one tile each: 2 tiles of 64 steps
+    assert size(2, R(256, 256), 8192, 256) == lib.dq_linear_fp8_workspace_size(512, 8192, 256)
+    # segments round up to whole tile rows of their own: 257 + 1 rows are 3 tile rows, not 2
+    s = size(2, R(257, 1), 8192, 256)
+    assert s == lib.dq_linear_fp8_workspace_size(768, 8192, 256) and (s - 4096) % part == 0
+    assert size(0, R(1, 1), 256, 128) == 0
+    assert size(2, None, 256, 128) == 0
+    assert size(2, R(64, 64), 192, 128) == 0
+
+
 def test_last_hip_error_untouched_by_argument_errors(lib):
     assert lin(lib, K=100) == SHAPE
     assert lib.dq_last_hip_error() == 0
@@ -411,7 +467,8 @@ def test_last_hip_error_untouched_by_argument_errors(lib):
 def test_python_binding_names_match_the_c_entry_points():
     import fp8_dynamic_quant_amd as dq
     for name in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
-                 "dq_linear_fp8_noalloc", "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8",
+                 "dq_linear_fp8_noalloc", "dq_linear_fp8_segmented",
+                 "dq_linear_fp8_segmented_workspace_size", "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8",
                  "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
                  "dq_quantize_mx_fp8", "dq_linear_mx_fp8", "dq_linear_fp8_workspace_size"):
         assert callable(getattr(dq, name))

@@ -1,11 +1,14 @@
 """GPU parity on the full DiT step exactly as the benchmark builds it.
 
-The benchmark draws the 228 linears of a 1024^2 FLUX-dev denoising step on the device (distinct
-weights per block). Here the first and last double-stream blocks (image and text streams, all
-four linears each) and the first and last single-stream blocks (both linears) are drawn with
-the same seeds, run through dq_quantize_weight_fp8 / dq_quantize_fp8 / dq_linear_fp8 as in
-the step (gated linears in place on their residual stream), copied back, and checked: every
-code and scale bit-exact against the oracle, and the outputs of 32 sampled rows within
+The benchmark draws the 228 weights of a 1024^2 FLUX-dev denoising step on the device (distinct
+weights per block) and runs the step as 152 quantize + linear pairs: each double-stream linear is
+one segmented call over the joint sequence (512 text rows, then 4096 image rows, with the text and
+the image weight), each single-stream linear a plain call over the 4608 rows. Here the first,
+middle and last double-stream blocks (all four calls each) and the first, middle and last
+single-stream blocks (both calls) are drawn with the same seeds, run through
+dq_quantize_weight_fp8 / dq_quantize_fp8 / dq_linear_fp8_segmented or dq_linear_fp8 as in the
+step (gated linears in place on their residual stream), copied back, and checked: every code and
+scale bit-exact against the oracle, and the outputs of sampled rows of every segment within
 |out - ref| <= 4e-3 |ref| + 1e-3 rms(ref).
 """
 import numpy as np
@@ -15,9 +18,12 @@ import torch
 import fp8_dynamic_quant_amd as dq
 from oracle import linear_ref, quantize_rows
 from gpu_util import announce, assert_within_tolerance, dev_to_bf16_bits, require_gpu
-from workloads import bf16_bits_to_f32, dit_step_device_inputs, dit_step_plan, workload
+from workloads import bf16_bits_to_f32, dit_step_calls, dit_step_device_inputs, workload
 
 pytestmark = pytest.mark.gpu
+
+DOUBLE_BLOCKS = (0, 9, 18)
+SINGLE_BLOCKS = (0, 19, 37)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -25,60 +31,68 @@ def _gpu():
     require_gpu()
 
 
-def _selected(plan_list):
-    """Plan indices of double blocks 0 and 18 (8 linears each) and single blocks 0 and 37."""
+def _selected(calls):
     picks = set()
-    for idx, (shape, sub, stream) in enumerate(plan_list):
-        block = sub // 100 - (19 if stream == "single" else 0)
-        if stream == "single":
-            if block in (0, 37):
-                picks.add(idx)
-        elif block in (0, 18):
-            picks.add(idx)
+    for i, c in enumerate(calls):
+        blocks = DOUBLE_BLOCKS if c["name"].startswith("double") else SINGLE_BLOCKS
+        if c["block"] in blocks:
+            picks.add(i)
     return picks
 
 
 def test_dit_step_sampled_blocks():
     w = workload("flux-dit-step-1024")
-    plan_list = dit_step_plan(w)
-    only = _selected(plan_list)
-    assert len(only) == 2 * 8 + 2 * 2
+    only = _selected(dit_step_calls(w))
+    assert len(only) == 3 * 4 + 3 * 2
     dev = torch.device("cuda:0")
-    announce(f"DiT step: drawing {len(only)} linears on the device")
-    plan, acts, residuals = dit_step_device_inputs(w, dev, dq.dq_quantize_weight_fp8, only=only,
-                                                   keep_weights=True)
+    announce(f"DiT step: drawing the weights of {len(only)} calls on the device")
+    calls, acts, residuals = dit_step_device_inputs(w, dev, dq.dq_quantize_weight_fp8, only=only,
+                                                    keep_weights=True)
     rng = np.random.default_rng(1234)
     host_x = {k: dev_to_bf16_bits(v) for k, v in acts.items()}
-    for lin in plan:
-        M, K, N, epi = lin["M"], lin["K"], lin["N"], lin["epilogue"]
-        announce(f"DiT linear #{lin['plan_index']} {lin['name']} {M}x{K}->{N} {epi}")
-        x = acts[lin["act"]]
-        q, sa = dq.dq_quantize_fp8(x)
+    for c in calls:
+        M, K, N, epi = c["M"], c["K"], c["N"], c["epilogue"]
+        segs = c["segments"]
+        announce(f"DiT call #{c['call_index']} {c['name']} block {c['block']} {M}x{K}->{N} {epi} "
+                 f"segments {[g['rows'] for g in segs]}")
+        q, sa = dq.dq_quantize_fp8(acts[c["act"]])
+        gated = epi == "gated_residual"
         res_before = None
-        if epi == "gated_residual":
-            r = residuals[lin["residual"]]
+        if gated:
+            r = residuals[c["residual"]]
             res_before = dev_to_bf16_bits(r)
-            out = dq.dq_linear_fp8(q, sa, lin["qw"], lin["sw"], lin["bias"], epi, lin["gate"], r,
-                                   out=r)
+        if len(segs) == 1:
+            g0 = segs[0]
+            out = dq.dq_linear_fp8(q, sa, g0["qw"], g0["sw"], g0["bias"], epi, g0["gate"],
+                                   r if gated else None, out=r if gated else None)
         else:
-            out = dq.dq_linear_fp8(q, sa, lin["qw"], lin["sw"], lin["bias"], epi)
+            out = dq.dq_linear_fp8_segmented(
+                q, sa, [g["rows"] for g in segs], [g["qw"] for g in segs],
+                [g["sw"] for g in segs], [g["bias"] for g in segs], epi,
+                [g["gate"] for g in segs] if gated else None, r if gated else None,
+                out=r if gated else None)
         torch.cuda.synchronize()
-        # weights: codes and scales of every output channel
-        wq, ws = quantize_rows(bf16_bits_to_f32(dev_to_bf16_bits(lin["w"])))
-        assert np.array_equal(lin["qw"].cpu().numpy(), wq), "weight codes differ"
-        assert np.array_equal(lin["sw"].cpu().numpy().view(np.uint32), ws.view(np.uint32))
-        # activations: every row
-        xq, xs = quantize_rows(bf16_bits_to_f32(host_x[lin["act"]]))
+        # activations: every row of the joint sequence
+        xq, xs = quantize_rows(bf16_bits_to_f32(host_x[c["act"]]))
         assert np.array_equal(q.cpu().numpy(), xq), "activation codes differ"
         assert np.array_equal(sa.cpu().numpy().view(np.uint32), xs.view(np.uint32))
-        # outputs: sampled rows
-        rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 30, replace=False)]))
-        bias = bf16_bits_to_f32(dev_to_bf16_bits(lin["bias"]))
-        gate = res = None
-        if epi == "gated_residual":
-            gate = bf16_bits_to_f32(dev_to_bf16_bits(lin["gate"]))
-            res = bf16_bits_to_f32(res_before[rows])
-        ref = linear_ref(xq[rows], xs[rows], wq, ws, bias, epi, gate, res)
-        got = bf16_bits_to_f32(dev_to_bf16_bits(out)[rows]).astype(np.float64)
-        assert_within_tolerance(got, ref, what=f"{lin['name']} #{lin['plan_index']}")
-        del lin["w"]
+        got_all = dev_to_bf16_bits(out)
+        r0 = 0
+        for g in segs:
+            n = g["rows"]
+            # weights: codes and scales of every output channel
+            wq, ws = quantize_rows(bf16_bits_to_f32(dev_to_bf16_bits(g["w"])))
+            assert np.array_equal(g["qw"].cpu().numpy(), wq), f"{g['name']}: weight codes differ"
+            assert np.array_equal(g["sw"].cpu().numpy().view(np.uint32), ws.view(np.uint32))
+            # outputs: the segment's first and last rows and 30 sampled ones
+            rows = r0 + np.unique(np.concatenate([[0, n - 1], rng.choice(n, 30, replace=False)]))
+            bias = bf16_bits_to_f32(dev_to_bf16_bits(g["bias"]))
+            gate = res = None
+            if gated:
+                gate = bf16_bits_to_f32(dev_to_bf16_bits(g["gate"]))
+                res = bf16_bits_to_f32(res_before[rows])
+            ref = linear_ref(xq[rows], xs[rows], wq, ws, bias, epi, gate, res)
+            got = bf16_bits_to_f32(got_all[rows]).astype(np.float64)
+            assert_within_tolerance(got, ref, what=f"{g['name']} #{g['plan_index']}")
+            del g["w"]
+            r0 += n

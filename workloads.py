@@ -248,54 +248,97 @@ def dit_step_plan(wl: Workload):
     return plan
 
 
+def dit_step_calls(wl: Workload):
+    """The step as launched: for each of the 19 double-stream blocks, its QKV, proj, fc1 and fc2
+    each as ONE call over the joint sequence of 512 text rows then 4096 image rows, with the text
+    and the image weight as two row segments; then for each of the 38 single-stream blocks,
+    linear1 and linear2 over the 4608 rows. Each call lists its segments as (shape, seed offset,
+    index in dit_step_plan)."""
+    plan = dit_step_plan(wl)
+    calls = []
+    for b in range(19):
+        for li, part in enumerate(("qkv", "proj", "fc1", "fc2")):
+            segs = []
+            for si, stream in ((1, "txt"), (0, "img")):
+                idx = b * 8 + si * 4 + li
+                shape, sub, _ = plan[idx]
+                assert shape.name == f"double.{stream}.{part}"
+                segs.append((shape, sub, idx))
+            calls.append({"name": f"double.{part}", "block": b, "segments": segs,
+                          "residual": "joint"})
+    for b in range(38):
+        for li, part in enumerate(("linear1", "linear2")):
+            idx = 19 * 8 + 2 * b + li
+            shape, sub, _ = plan[idx]
+            calls.append({"name": f"single.{part}", "block": b, "segments": [(shape, sub, idx)],
+                          "residual": "single"})
+    for c in calls:
+        first = c["segments"][0][0]
+        c.update(M=sum(sh.M for sh, _, _ in c["segments"]), K=first.K, N=first.N,
+                 epilogue=first.epilogue, act=f"{sum(sh.M for sh, _, _ in c['segments'])}x{first.K}",
+                 flops=sum(sh.flops for sh, _, _ in c["segments"]))
+    return calls
+
+
 def dit_step_device_inputs(wl: Workload, device, quantize_weight, only=None,
                            keep_weights=False):
     """Draw the inputs of one step on `device` and hand each bf16 weight to `quantize_weight`
     (which returns its (codes, scales)); the bf16 weight is dropped afterwards unless
     keep_weights (then it is kept under "w").
 
-    only: None for all 228 linears, or a set of indices into dit_step_plan(wl) to draw (each
-    linear has its own seed, so a subset gets exactly the values the whole step gets).
+    only: None for every call of dit_step_calls(wl), or a set of indices into that list (each
+    weight has its own seed, so a subset gets exactly the values the whole step gets).
 
-    Returns (plan, activations, residual_streams): plan entries are dicts with the shape, the
-    epilogue, the activation key, the residual key (gated linears), qw, sw, bias and gate."""
+    Returns (calls, activations, residual_streams). Each call is a dit_step_calls entry whose
+    "segments" are dicts with the segment's rows and its qw, sw, bias and gate. Activations are
+    one [4608, K] buffer per K (the joint sequence; the single-stream blocks use the same 4608
+    rows); the residual streams are the double blocks' joint [4608, 3072] and the single
+    blocks' [4608, 3072], both updated in place by the gated linears."""
     import torch
     base = 4_000_000
+    calls = dit_step_calls(wl)
     acts, residuals = {}, {}
     g = torch.Generator(device=device)
-    for l in wl.linears:
-        key = f"{l.M}x{l.K}"
+    for c in calls:
+        key = c["act"]
         if key in acts:
             continue
-        g.manual_seed(base + 7 * l.M + l.K)
-        x = torch.randn((l.M, l.K), generator=g, device=device, dtype=torch.float32)
-        cols = torch.randperm(l.K, generator=g, device=device)[: l.n_outliers]
-        x[:, cols] *= l.outlier_factor
+        shape = c["segments"][0][0]
+        M, K = c["M"], c["K"]
+        g.manual_seed(base + 7 * M + K)
+        x = torch.randn((M, K), generator=g, device=device, dtype=torch.float32)
+        cols = torch.randperm(K, generator=g, device=device)[: shape.n_outliers]
+        x[:, cols] *= shape.outlier_factor
         acts[key] = x.to(torch.bfloat16)
         del x
-    for stream, M in (("img", 4096), ("txt", 512), ("single", 4608)):
-        g.manual_seed(base + 99 + M)
-        residuals[stream] = torch.randn((M, 3072), generator=g, device=device,
+    for stream in ("joint", "single"):
+        g.manual_seed(base + 99 + (1 if stream == "joint" else 2))
+        residuals[stream] = torch.randn((4608, 3072), generator=g, device=device,
                                         dtype=torch.float32).to(torch.bfloat16)
-    plan = []
-    for idx, (shape, sub, stream) in enumerate(dit_step_plan(wl)):
-        if only is not None and idx not in only:
+    out = []
+    for ci, c in enumerate(calls):
+        if only is not None and ci not in only:
             continue
-        g.manual_seed(base + sub)
-        w = (torch.randn((shape.N, shape.K), generator=g, device=device, dtype=torch.float32)
-             * 0.02).to(torch.bfloat16)
-        qw, sw = quantize_weight(w)
-        bias = (torch.randn(shape.N, generator=g, device=device) * 0.01).to(torch.bfloat16)
-        gate = None
-        if shape.epilogue == "gated_residual":
-            gate = (1.0 + 0.1 * torch.randn(shape.N, generator=g, device=device)).to(torch.bfloat16)
-        entry = {"name": shape.name, "M": shape.M, "K": shape.K, "N": shape.N,
-                 "epilogue": shape.epilogue, "act": f"{shape.M}x{shape.K}",
-                 "residual": stream if shape.epilogue == "gated_residual" else None,
-                 "qw": qw, "sw": sw, "bias": bias, "gate": gate, "seed": base + sub,
-                 "plan_index": idx}
-        if keep_weights:
-            entry["w"] = w
-        del w
-        plan.append(entry)
-    return plan, acts, residuals
+        segs = []
+        for shape, sub, idx in c["segments"]:
+            g.manual_seed(base + sub)
+            w = (torch.randn((shape.N, shape.K), generator=g, device=device,
+                             dtype=torch.float32) * 0.02).to(torch.bfloat16)
+            qw, sw = quantize_weight(w)
+            bias = (torch.randn(shape.N, generator=g, device=device) * 0.01).to(torch.bfloat16)
+            gate = None
+            if shape.epilogue == "gated_residual":
+                gate = (1.0 + 0.1 * torch.randn(shape.N, generator=g, device=device)).to(
+                    torch.bfloat16)
+            seg = {"name": shape.name, "rows": shape.M, "qw": qw, "sw": sw, "bias": bias,
+                   "gate": gate, "seed": base + sub, "plan_index": idx}
+            if keep_weights:
+                seg["w"] = w
+            del w
+            segs.append(seg)
+        entry = dict(c)
+        entry["segments"] = segs
+        entry["call_index"] = ci
+        entry["residual"] = c["residual"] if c["epilogue"] == "gated_residual" else None
+        out.append(entry)
+    return out, acts, residuals
