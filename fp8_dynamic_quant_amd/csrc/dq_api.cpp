@@ -392,8 +392,8 @@ int dq_linear_mx_fp8(const void* qa, const void* sa, int64_t M, int64_t K, const
   const int shape = check_linear_shape(M, K, N);
   if (shape != DQ_OK) return shape;
   if (epilogue != DQ_EPI_BIAS && epilogue != DQ_EPI_GELU_TANH) return DQ_ERR_EPILOGUE;
-  // one tile per workgroup: the grid must stay within 2^31 workgroups
-  if (((M + 255) / 256) * ((N + 255) / 256) > kMaxDim) return DQ_ERR_SHAPE;
+  // one 512-thread workgroup per tile: the grid's work-item count must fit in 32 bits
+  if (((M + 255) / 256) * ((N + 255) / 256) >= (int64_t(1) << 23)) return DQ_ERR_SHAPE;
   if (M == 0) return DQ_OK;
   if (!qa || !sa || !qw || !sw || !out) return DQ_ERR_NULL;
   if (!aligned16(qa) || !aligned16(qw) || !aligned16(out) || (bias && !aligned16(bias)) ||

@@ -75,36 +75,48 @@ __device__ __forceinline__ uint32_t encode4(uint32_t w0, uint32_t w1, float y) {
 }
 
 // Thread t of a workgroup takes the 16-byte chunks u = 1024 b + 256 i + t, i = 0..3 (four loads
-// in flight); the 4 threads of an MX block are a DPP quad.
+// in flight, non-temporal: x is read once); the 4 threads of an MX block are a DPP quad. A
+// workgroup steps through chunk groups b = blockIdx.x, + gridDim.x, ... (at most kMaxGroups
+// workgroups, so that any size fits a dispatch's 32-bit work-item count).
 constexpr int kQuantUnroll = 4;
+constexpr int64_t kMaxGroups = int64_t(1) << 20;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ void __launch_bounds__(256) quant_mx_rows(const uint16_t* __restrict__ x, int64_t n8,
                                                      uint8_t* __restrict__ q,
                                                      uint8_t* __restrict__ scale) {
-  const int64_t base = (int64_t)blockIdx.x * (256 * kQuantUnroll) + threadIdx.x;
-  uint4 v[kQuantUnroll];
+  for (int64_t grp = blockIdx.x; grp * (256 * kQuantUnroll) < n8; grp += gridDim.x) {
+    const int64_t base = grp * (256 * kQuantUnroll) + threadIdx.x;
+    uint4 v[kQuantUnroll];
 #pragma unroll
-  for (int i = 0; i < kQuantUnroll; ++i) {
-    const int64_t t = base + 256 * i;  // n8 is a multiple of 4: a quad is live or not as a whole
-    v[i] = t < n8 ? reinterpret_cast<const uint4*>(x)[t] : make_uint4(0u, 0u, 0u, 0u);
-  }
+    for (int i = 0; i < kQuantUnroll; ++i) {
+      const int64_t t = base + 256 * i;  // n8 is a multiple of 4: a quad is live or not as a whole
+      if (t < n8) {
+        const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x) + t);
+        v[i] = make_uint4(r[0], r[1], r[2], r[3]);
+      } else {
+        v[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
 #pragma unroll
-  for (int i = 0; i < kQuantUnroll; ++i) {
-    const int64_t t = base + 256 * i;
-    uint32_t mx = absmax_pair(absmax_pair(absmax_pair(absmax_pair(0u, v[i].x), v[i].y), v[i].z),
-                              v[i].w);
-    uint32_t m = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
-    uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false);
-    m = m > o ? m : o;
-    o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false);
-    m = m > o ? m : o;
-    if (t >= n8) continue;
-    const uint32_t field = (m >> 7) & 0xFFu;            // bf16 exponent field of the block amax
-    const uint32_t byte = field > 8u ? field - 8u : 0u;  // shared + 127
-    const float y = __uint_as_float((254u - byte) << 23);  // 2^-shared (byte <= 246 for bf16)
-    reinterpret_cast<uint2*>(q)[t] =
-        make_uint2(encode4(v[i].x, v[i].y, y), encode4(v[i].z, v[i].w, y));
-    if ((threadIdx.x & 3) == 0) scale[t >> 2] = (uint8_t)byte;
+    for (int i = 0; i < kQuantUnroll; ++i) {
+      const int64_t t = base + 256 * i;
+      uint32_t mx = absmax_pair(absmax_pair(absmax_pair(absmax_pair(0u, v[i].x), v[i].y), v[i].z),
+                                v[i].w);
+      uint32_t m = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
+      uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false);
+      m = m > o ? m : o;
+      o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false);
+      m = m > o ? m : o;
+      if (t >= n8) continue;
+      const uint32_t field = (m >> 7) & 0xFFu;            // bf16 exponent field of the block amax
+      const uint32_t byte = field > 8u ? field - 8u : 0u;  // shared + 127
+      const float y = __uint_as_float((254u - byte) << 23);  // 2^-shared (byte <= 246 for bf16)
+      reinterpret_cast<uint2*>(q)[t] =
+          make_uint2(encode4(v[i].x, v[i].y, y), encode4(v[i].z, v[i].w, y));
+      if ((threadIdx.x & 3) == 0) scale[t >> 2] = (uint8_t)byte;
+    }
   }
 }
 
@@ -347,8 +359,9 @@ hipError_t launch_quantize_mx(const uint16_t* x, int64_t R, int64_t K, uint8_t* 
   const int64_t n8 = R * K / 8;
   if (n8 == 0) return hipSuccess;
   const int64_t per_wg = 256 * kQuantUnroll;
-  hipLaunchKernelGGL(quant_mx_rows, dim3((unsigned)((n8 + per_wg - 1) / per_wg)), dim3(256), 0,
-                     stream, x, n8, q, scale);
+  const int64_t groups = (n8 + per_wg - 1) / per_wg;
+  hipLaunchKernelGGL(quant_mx_rows, dim3((unsigned)(groups < kMaxGroups ? groups : kMaxGroups)),
+                     dim3(256), 0, stream, x, n8, q, scale);
   return hipGetLastError();
 }
 

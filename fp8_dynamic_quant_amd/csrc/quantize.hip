@@ -40,71 +40,99 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t m) {
 }
 
 
-// Register-resident version: lane l holds chunks l, l+64, ..., l+64*(NCH-1) of its row.
-template <int NCH>
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes of x, read once: a non-temporal load, so the stream of activations does not push the
+// codes (which the GEMM reads next) and the weights out of the caches.
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
+// Workgroups of a row-group grid: at most this many are launched and each steps through row
+// groups b, b + gridDim.x, ..., so that any row count fits the 32-bit work-item count of a
+// dispatch.
+constexpr int64_t kMaxRowGroups = int64_t(1) << 20;
+
+// Register-resident version: WPR waves share a row (4 / WPR rows per 256-thread workgroup); lane
+// l of the row's wave p holds chunks 64 p + l + 64 WPR i, i < NCH, loaded once. Each wave takes
+// its chunks' magnitude max; with WPR > 1 the row's waves combine theirs through LDS (two
+// buffers, so one barrier per row group suffices).
+template <int NCH, int WPR>
 __global__ void __launch_bounds__(256) quant_rows_reg(const uint16_t* __restrict__ x, int R, int K,
                                                       uint8_t* __restrict__ q,
                                                       float* __restrict__ scale) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= R) return;
+  constexpr int kRows = 4 / WPR;
+  __shared__ uint32_t smax[2][4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rl = w / WPR, part = w % WPR;
   const int C = K >> 3;
-  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)row * (size_t)K);
-  uint2* qr = reinterpret_cast<uint2*>(q + (size_t)row * (size_t)K);
-
-  uint4 v[NCH];
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = lane + 64 * i;
-    v[i] = (c < C) ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
-  }
-  uint32_t mx = 0;
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) mx = absmax4(mx, v[i]);
-  uint32_t m = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
-  m = __builtin_amdgcn_readfirstlane(wave_max(m));
-
-  const float amax = __uint_as_float(m << 16);
-  const float s = amax / kE4M3Max;
-  if (lane == 0) scale[row] = s;
-
-  if (m == 0) {
+  int it = 0;
+  for (int64_t grp = blockIdx.x; grp * kRows < R; grp += gridDim.x, ++it) {
+    const int64_t row = grp * kRows + rl;
+    const bool live = row < R;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)(live ? row : 0) * (size_t)K);
+    uint2* qr = reinterpret_cast<uint2*>(q + (size_t)(live ? row : 0) * (size_t)K);
+    uint4 v[NCH];
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = lane + 64 * i;
-      if (c < C) qr[c] = signs8(v[i]);
+      const int c = part * 64 + lane + 64 * WPR * i;
+      v[i] = (live && c < C) ? load_nt(xr + c) : make_uint4(0u, 0u, 0u, 0u);
     }
-  } else if (s < kFltMinNormal) {
+    uint32_t mx = 0;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = lane + 64 * i;
-      if (c < C) qr[c] = encode8<1, false>(v[i], s, 0.0f);
+    for (int i = 0; i < NCH; ++i) mx = absmax4(mx, v[i]);
+    uint32_t m = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
+    m = wave_max(m);
+    if (WPR > 1) {
+      if (lane == 0) smax[it & 1][w] = m;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < WPR; ++j) {
+        const uint32_t o = smax[it & 1][rl * WPR + j];
+        m = m > o ? m : o;
+      }
     }
-  } else if (amax < kTinyAmax) {
-    const float ss = s * 0x1p64f;
-    const float y = 1.0f / ss;
+    m = __builtin_amdgcn_readfirstlane(m);
+    if (!live) continue;
+    const float amax = __uint_as_float(m << 16);
+    const float s = amax / kE4M3Max;
+    if (lane == 0 && part == 0) scale[row] = s;
+    if (m == 0) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = lane + 64 * i;
-      if (c < C) qr[c] = encode8<0, true>(v[i], ss, y);
-    }
-  } else {
-    const float y = 1.0f / s;
+      for (int i = 0; i < NCH; ++i) {
+        const int c = part * 64 + lane + 64 * WPR * i;
+        if (c < C) qr[c] = signs8(v[i]);
+      }
+    } else if (s < kFltMinNormal) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = lane + 64 * i;
-      if (c < C) qr[c] = encode8<0, false>(v[i], s, y);
+      for (int i = 0; i < NCH; ++i) {
+        const int c = part * 64 + lane + 64 * WPR * i;
+        if (c < C) qr[c] = encode8<1, false>(v[i], s, 0.0f);
+      }
+    } else if (amax < kTinyAmax) {
+      const float ss = s * 0x1p64f;
+      const float y = 1.0f / ss;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = part * 64 + lane + 64 * WPR * i;
+        if (c < C) qr[c] = encode8<0, true>(v[i], ss, y);
+      }
+    } else {
+      const float y = 1.0f / s;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = part * 64 + lane + 64 * WPR * i;
+        if (c < C) qr[c] = encode8<0, false>(v[i], s, y);
+      }
     }
   }
 }
 
-// Any K: two passes over the row (the second pass usually hits in L2).
-__global__ void __launch_bounds__(256) quant_rows_loop(const uint16_t* __restrict__ x, int R, int K,
-                                                       uint8_t* __restrict__ q,
-                                                       float* __restrict__ scale) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= R) return;
+// One row, any K: two passes over it (the second pass usually hits in L2).
+__device__ __forceinline__ void quant_row_loop(const uint16_t* __restrict__ x, int64_t row, int K,
+                                               uint8_t* __restrict__ q, float* __restrict__ scale,
+                                               int lane) {
   const int C = K >> 3;
   const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)row * (size_t)K);
   uint2* qr = reinterpret_cast<uint2*>(q + (size_t)row * (size_t)K);
@@ -127,6 +155,15 @@ __global__ void __launch_bounds__(256) quant_rows_loop(const uint16_t* __restric
     const float y = 1.0f / s;
     for (int c = lane; c < C; c += 64) qr[c] = encode8<0, false>(xr[c], s, y);
   }
+}
+
+__global__ void __launch_bounds__(256) quant_rows_loop(const uint16_t* __restrict__ x, int R, int K,
+                                                       uint8_t* __restrict__ q,
+                                                       float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < R;
+       row += (int64_t)gridDim.x * 4)
+    quant_row_loop(x, row, K, q, scale, lane);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -219,12 +256,10 @@ __global__ void __launch_bounds__(256) ln_mod_quant_rows(
   constexpr int kFill = (64 * NCH + 255) / 256;  // chunks of each vector per thread
   __shared__ uint4 smod[2][256 * kFill];
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const bool live = row < R;
   const int C = K >> 3;
   // The modulation vectors go straight to LDS (16 bytes per lane, lane l of wave w at slot
-  // 256 f + 64 w + l), issued before the row loads. Slots past the row read chunk 0 and are
-  // never used.
+  // 256 f + 64 w + l), issued before the first row's loads; they serve every row group the
+  // workgroup takes. Slots past the row read chunk 0 and are never used.
   {
     const int w = threadIdx.x >> 6;
 #pragma unroll
@@ -238,93 +273,101 @@ __global__ void __launch_bounds__(256) ln_mod_quant_rows(
                                        16, 0, 0);
     }
   }
-  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)(live ? row : 0) * (size_t)K);
-  uint4 v[NCH];
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = lane + 64 * i;
-    v[i] = (live && c < C) ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
-  }
-  // 1. first mean (chunks past the row are zeros and add nothing)
-  float sum = 0.0f;
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sum = (sum + bf16_lo(w[j])) + bf16_hi(w[j]);
-  }
-  const float mean0 = wave_sum(sum) / (float)K;
-  // 2. correction and variance, over the row's own values only (chunks past it give e = 0)
-  float es = 0.0f, ss = 0.0f;
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const float m = lane + 64 * i < C ? mean0 : 0.0f;
-    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float e0 = bf16_lo(w[j]) - m, e1 = bf16_hi(w[j]) - m;
-      es = (es + e0) + e1;
-      ss = __builtin_fmaf(e0, e0, ss);
-      ss = __builtin_fmaf(e1, e1, ss);
-    }
-  }
-  const float corr = wave_sum(es) / (float)K;
-  const float m2 = wave_sum(ss) / (float)K;
-  const float var = __builtin_fmaxf(__builtin_fmaf(-corr, corr, m2), 0.0f);
-  const float rstd = 1.0f / __builtin_sqrtf(var + eps);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
-  __syncthreads();                     // and every other wave's
-  // 3. y in bf16, in place of x
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = lane + 64 * i;
-    if (c < C) v[i] = modulate8(v[i], smod[0][c], smod[1][c], mean0, corr, rstd);
-  }
-  if (!live) return;
-  if (kStoreY) {
-    uint4* yr = reinterpret_cast<uint4*>(y + (size_t)row * (size_t)K);
+  bool first = true;
+  for (int64_t grp = blockIdx.x; grp * 4 < R; grp += gridDim.x) {
+    const int64_t row = grp * 4 + (threadIdx.x >> 6);
+    const bool live = row < R;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)(live ? row : 0) * (size_t)K);
+    uint4 v[NCH];
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = lane + 64 * i;
-      if (c < C) yr[c] = v[i];
+      v[i] = (live && c < C) ? load_nt(xr + c) : make_uint4(0u, 0u, 0u, 0u);
     }
-  }
-  // 4. per-row quantization of the bf16 y (chunks past the row are zeros)
-  uint2* qr = reinterpret_cast<uint2*>(q + (size_t)row * (size_t)K);
-  uint32_t mx = 0;
+    // 1. first mean (chunks past the row are zeros and add nothing)
+    float sum = 0.0f;
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) mx = absmax4(mx, v[i]);
-  uint32_t m = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
-  m = wave_max_dpp(m);
-  const float amax = __uint_as_float(m << 16);
-  const float s = amax / kE4M3Max;
-  if (lane == 0) scale[row] = s;
-  if (m == 0) {
+    for (int i = 0; i < NCH; ++i) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sum = (sum + bf16_lo(w[j])) + bf16_hi(w[j]);
+    }
+    const float mean0 = wave_sum(sum) / (float)K;
+    // 2. correction and variance, over the row's own values only (chunks past it give e = 0)
+    float es = 0.0f, ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const float m = lane + 64 * i < C ? mean0 : 0.0f;
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float e0 = bf16_lo(w[j]) - m, e1 = bf16_hi(w[j]) - m;
+        es = (es + e0) + e1;
+        ss = __builtin_fmaf(e0, e0, ss);
+        ss = __builtin_fmaf(e1, e1, ss);
+      }
+    }
+    const float corr = wave_sum(es) / (float)K;
+    const float m2 = wave_sum(ss) / (float)K;
+    const float var = __builtin_fmaxf(__builtin_fmaf(-corr, corr, m2), 0.0f);
+    const float rstd = 1.0f / __builtin_sqrtf(var + eps);
+    if (first) {                           // the same for every wave of the workgroup
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+      __syncthreads();                     // and every other wave's
+      first = false;
+    }
+    // 3. y in bf16, in place of x
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = lane + 64 * i;
-      if (c < C) qr[c] = signs8(v[i]);
+      if (c < C) v[i] = modulate8(v[i], smod[0][c], smod[1][c], mean0, corr, rstd);
     }
-  } else if (s < kFltMinNormal) {
+    if (!live) continue;
+    if (kStoreY) {
+      uint4* yr = reinterpret_cast<uint4*>(y + (size_t)row * (size_t)K);
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = lane + 64 * i;
-      if (c < C) qr[c] = encode8<1, false>(v[i], s, 0.0f);
+      for (int i = 0; i < NCH; ++i) {
+        const int c = lane + 64 * i;
+        if (c < C) yr[c] = v[i];
+      }
     }
-  } else if (amax < kTinyAmax) {
-    const float ss2 = s * 0x1p64f;
-    const float yy = 1.0f / ss2;
+    // 4. per-row quantization of the bf16 y (chunks past the row are zeros)
+    uint2* qr = reinterpret_cast<uint2*>(q + (size_t)row * (size_t)K);
+    uint32_t mx = 0;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = lane + 64 * i;
-      if (c < C) qr[c] = encode8<0, true>(v[i], ss2, yy);
-    }
-  } else {
-    const float yy = 1.0f / s;
+    for (int i = 0; i < NCH; ++i) mx = absmax4(mx, v[i]);
+    uint32_t m = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
+    m = wave_max_dpp(m);
+    const float amax = __uint_as_float(m << 16);
+    const float s = amax / kE4M3Max;
+    if (lane == 0) scale[row] = s;
+    if (m == 0) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = lane + 64 * i;
-      if (c < C) qr[c] = encode8<0, false>(v[i], s, yy);
+      for (int i = 0; i < NCH; ++i) {
+        const int c = lane + 64 * i;
+        if (c < C) qr[c] = signs8(v[i]);
+      }
+    } else if (s < kFltMinNormal) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = lane + 64 * i;
+        if (c < C) qr[c] = encode8<1, false>(v[i], s, 0.0f);
+      }
+    } else if (amax < kTinyAmax) {
+      const float ss2 = s * 0x1p64f;
+      const float yy = 1.0f / ss2;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = lane + 64 * i;
+        if (c < C) qr[c] = encode8<0, true>(v[i], ss2, yy);
+      }
+    } else {
+      const float yy = 1.0f / s;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = lane + 64 * i;
+        if (c < C) qr[c] = encode8<0, false>(v[i], s, yy);
+      }
     }
   }
 }
@@ -336,77 +379,94 @@ __global__ void __launch_bounds__(256) quant_rows_small(const uint16_t* __restri
                                                         int K, uint8_t* __restrict__ q,
                                                         float* __restrict__ scale) {
   const int lane = threadIdx.x & 63;
-  const int row = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
   const int c = lane & 15, C = K >> 3;
-  const bool live = row < R && c < C;
-  const uint4 v = live ? reinterpret_cast<const uint4*>(x + (size_t)row * (size_t)K)[c]
-                       : make_uint4(0u, 0u, 0u, 0u);
-  uint32_t mx = absmax4(0u, v);
-  uint32_t m = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
-  m = umax(m, (uint32_t)dpp<0xB1>((int)m));
-  m = umax(m, (uint32_t)dpp<0x4E>((int)m));
-  m = umax(m, (uint32_t)dpp<0x141>((int)m));
-  m = umax(m, (uint32_t)dpp<0x140>((int)m));
-  if (row >= R) return;
-  const float amax = __uint_as_float(m << 16);
-  const float s = amax / kE4M3Max;
-  if (c == 0) scale[row] = s;
-  if (c >= C) return;
-  uint2 code;
-  if (m == 0) {
-    code = signs8(v);
-  } else if (s < kFltMinNormal) {
-    code = encode8<1, false>(v, s, 0.0f);
-  } else if (amax < kTinyAmax) {
-    const float ss = s * 0x1p64f;
-    code = encode8<0, true>(v, ss, 1.0f / ss);
-  } else {
-    code = encode8<0, false>(v, s, 1.0f / s);
+  for (int64_t grp = blockIdx.x; grp * 16 < R; grp += gridDim.x) {
+    const int64_t row = (grp * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+    const bool live = row < R && c < C;
+    const uint4 v = live ? load_nt(reinterpret_cast<const uint4*>(x + (size_t)row * (size_t)K) + c)
+                         : make_uint4(0u, 0u, 0u, 0u);
+    uint32_t mx = absmax4(0u, v);
+    uint32_t m = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
+    m = umax(m, (uint32_t)dpp<0xB1>((int)m));
+    m = umax(m, (uint32_t)dpp<0x4E>((int)m));
+    m = umax(m, (uint32_t)dpp<0x141>((int)m));
+    m = umax(m, (uint32_t)dpp<0x140>((int)m));
+    if (row >= R) continue;
+    const float amax = __uint_as_float(m << 16);
+    const float s = amax / kE4M3Max;
+    if (c == 0) scale[row] = s;
+    if (c >= C) continue;
+    uint2 code;
+    if (m == 0) {
+      code = signs8(v);
+    } else if (s < kFltMinNormal) {
+      code = encode8<1, false>(v, s, 0.0f);
+    } else if (amax < kTinyAmax) {
+      const float ss = s * 0x1p64f;
+      code = encode8<0, true>(v, ss, 1.0f / ss);
+    } else {
+      code = encode8<0, false>(v, s, 1.0f / s);
+    }
+    reinterpret_cast<uint2*>(q + (size_t)row * (size_t)K)[c] = code;
   }
-  reinterpret_cast<uint2*>(q + (size_t)row * (size_t)K)[c] = code;
+}
+
+// Workgroups for `groups` row groups: one per group, at most kMaxRowGroups.
+inline dim3 group_grid(int64_t groups) {
+  return dim3((unsigned)(groups < kMaxRowGroups ? groups : kMaxRowGroups));
 }
 
 template <int NCH>
 hipError_t launch_lnmq(const uint16_t* x, int R, int K, const uint16_t* ms, const uint16_t* mt,
                        float eps, uint16_t* y, uint8_t* q, float* scale, hipStream_t st) {
+  const dim3 grid = group_grid(((int64_t)R + 3) / 4);
   if (y)
-    hipLaunchKernelGGL((ln_mod_quant_rows<NCH, true>), dim3((R + 3) / 4), dim3(256), 0, st, x, R,
-                       K, ms, mt, eps, y, q, scale);
+    hipLaunchKernelGGL((ln_mod_quant_rows<NCH, true>), grid, dim3(256), 0, st, x, R, K, ms, mt,
+                       eps, y, q, scale);
   else
-    hipLaunchKernelGGL((ln_mod_quant_rows<NCH, false>), dim3((R + 3) / 4), dim3(256), 0, st, x,
-                       R, K, ms, mt, eps, y, q, scale);
+    hipLaunchKernelGGL((ln_mod_quant_rows<NCH, false>), grid, dim3(256), 0, st, x, R, K, ms, mt,
+                       eps, y, q, scale);
   return hipGetLastError();
 }
 
-template <int NCH>
+template <int NCH, int WPR>
 hipError_t launch_reg(const uint16_t* x, int R, int K, uint8_t* q, float* scale, hipStream_t st) {
-  hipLaunchKernelGGL(quant_rows_reg<NCH>, dim3((R + 3) / 4), dim3(256), 0, st, x, R, K, q, scale);
+  constexpr int kRows = 4 / WPR;
+  hipLaunchKernelGGL((quant_rows_reg<NCH, WPR>), group_grid(((int64_t)R + kRows - 1) / kRows),
+                     dim3(256), 0, st, x, R, K, q, scale);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Rows of up to 128 values: four rows per wave. Otherwise one, two or four waves per row (a
+// row's 16-byte chunks spread over 64, 128 or 256 lanes, at most 8 per lane up to 8192 values,
+// 16 up to 32768), so that each lane keeps few chunks in flight and every row of a large launch
+// is resident at once (measured: 4608 x 15360 in 38 us with four waves per row, 48 us with one);
+// longer rows take two passes.
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t R, int64_t K, uint8_t* q, float* scale,
                                 hipStream_t stream) {
   if (R == 0) return hipSuccess;
   const int r = (int)R, k = (int)K;
-  const int64_t nch = (K / 8 + 63) / 64;  // 16-byte chunks per lane
-  if (K <= 128) {  // four rows per wave
-    hipLaunchKernelGGL(quant_rows_small, dim3((unsigned)((R + 15) / 16)), dim3(256), 0, stream, x, r,
-                       k, q, scale);
+  const int64_t C = K / 8;  // 16-byte chunks per row
+  if (K <= 128) {
+    hipLaunchKernelGGL(quant_rows_small, group_grid((R + 15) / 16), dim3(256), 0, stream, x, r, k,
+                       q, scale);
     return hipGetLastError();
   }
-  if (nch <= 1) return launch_reg<1>(x, r, k, q, scale, stream);
-  if (nch <= 2) return launch_reg<2>(x, r, k, q, scale, stream);
-  if (nch <= 3) return launch_reg<3>(x, r, k, q, scale, stream);
-  if (nch <= 4) return launch_reg<4>(x, r, k, q, scale, stream);
-  if (nch <= 6) return launch_reg<6>(x, r, k, q, scale, stream);
-  if (nch <= 8) return launch_reg<8>(x, r, k, q, scale, stream);
-  if (nch <= 12) return launch_reg<12>(x, r, k, q, scale, stream);
-  if (nch <= 16) return launch_reg<16>(x, r, k, q, scale, stream);
-  if (nch <= 24) return launch_reg<24>(x, r, k, q, scale, stream);
-  if (nch <= 30) return launch_reg<30>(x, r, k, q, scale, stream);
-  hipLaunchKernelGGL(quant_rows_loop, dim3((r + 3) / 4), dim3(256), 0, stream, x, r, k, q, scale);
+  if (C <= 64) return launch_reg<1, 1>(x, r, k, q, scale, stream);
+  if (C <= 128) return launch_reg<2, 1>(x, r, k, q, scale, stream);
+  if (C <= 256) return launch_reg<4, 1>(x, r, k, q, scale, stream);
+  if (C <= 384) return launch_reg<3, 2>(x, r, k, q, scale, stream);
+  if (C <= 512) return launch_reg<4, 2>(x, r, k, q, scale, stream);
+  if (C <= 768) return launch_reg<6, 2>(x, r, k, q, scale, stream);
+  if (C <= 1024) return launch_reg<8, 2>(x, r, k, q, scale, stream);
+  if (C <= 1536) return launch_reg<6, 4>(x, r, k, q, scale, stream);
+  if (C <= 2048) return launch_reg<8, 4>(x, r, k, q, scale, stream);
+  if (C <= 3072) return launch_reg<12, 4>(x, r, k, q, scale, stream);
+  if (C <= 4096) return launch_reg<16, 4>(x, r, k, q, scale, stream);
+  hipLaunchKernelGGL(quant_rows_loop, group_grid((R + 3) / 4), dim3(256), 0, stream, x, r, k, q,
+                     scale);
   return hipGetLastError();
 }
 

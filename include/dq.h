@@ -324,7 +324,7 @@ int dq_quantize_mx_fp8(const void* x, int64_t M, int64_t K, void* q, void* scale
  *   out      bf16 [M, N]
  * Requirements: as dq_linear_fp8 (128 <= K < 2^24, K % 128 == 0, N % 64 == 0); codes, bias and
  * out 16-byte aligned, scale arrays 4-byte aligned; out overlapping no input. One workgroup per
- * 256 x 256 output tile.
+ * 256 x 256 output tile, so fewer than 2^23 tiles (DQ_ERR_SHAPE otherwise).
  */
 int dq_linear_mx_fp8(const void* qa, const void* sa, int64_t M, int64_t K, const void* qw,
                      const void* sw, int64_t N, const void* bias, int epilogue, void* out,

@@ -320,6 +320,9 @@ def test_linear_mx_argument_checks(lib):
     assert mxlin(lib, K=1 << 24) == SHAPE
     assert mxlin(lib, N=96) == SHAPE                             # N % 64
     assert mxlin(lib, M=-1) == SHAPE
+    # one 512-thread workgroup per 256 x 256 tile: fewer than 2^23 tiles
+    assert mxlin(lib, M=1 << 20, K=128, N=1 << 19) == SHAPE        # 4096 x 2048 tiles
+    assert mxlin(lib, M=1 << 20, K=128, N=(1 << 19) - 256, qa=None) == NULL  # one tile column less
     assert mxlin(lib, epi=2) == EPI                              # gated residual: not offered
     assert mxlin(lib, epi=7) == EPI
     for name in ("qa", "sa", "qw", "sw", "out"):

@@ -116,7 +116,9 @@ def test_flux_hidden_state_1024px():
     1% outlier channels 30x larger, modulation drawn at sigma 0.5."""
     x = make_rows(4608, 3072, seed=11)
     s, t = make_modulation(3072, seed=11)
-    frac = _check(x, s, t, "flux 4608x3072")
+    # measured: 5.6e-5 of the y values differ from the oracle's by one bf16 step, so 84.5 % of
+    # the rows come out bit-equal (and carry the oracle's codes and scale); require 75 %
+    frac = _check(x, s, t, "flux 4608x3072", min_same_rows=0.75)
     assert frac < 1e-3
 
 
@@ -169,6 +171,28 @@ def test_modulation_that_cancels():
     _check(x, s, t, "cancelling modulation")
     q, sc, y16 = _run(x, s, t)
     assert not np.any(y16 & 0x7FFF) and not np.any(q & 0x7F)
+
+
+def test_more_row_groups_than_workgroups():
+    """4 * 2^20 + 5 rows of 8 values: four rows per workgroup and at most 2^20 workgroups, so
+    workgroups 0 and 1 take the last two row groups on a second pass (the modulation vectors in
+    LDS serve both). Sampled rows, including those around the wrap, against the oracle."""
+    M, K = 4 * (1 << 20) + 5, 8
+    x16 = make_rows(M, K, seed=41, n_outliers=0)
+    s16, t16 = make_modulation(K, 41)
+    announce(f"layernorm+modulate+quantize {M}x{K}: more row groups than workgroups")
+    q, sc, y16 = _run(x16, s16, t16)
+    wrap = 4 * (1 << 20)
+    rows = np.concatenate([np.arange(8), np.arange(wrap - 8, M),
+                           np.random.default_rng(5).choice(M, 256, replace=False)])
+    kq, ksc = quantize_rows(bf16_bits_to_f32(y16[rows]))
+    assert np.array_equal(q[rows], kq)
+    assert np.array_equal(sc[rows].view(np.uint32), ksc.view(np.uint32))
+    y64 = layernorm_modulate(bf16_bits_to_f32(x16[rows]), bf16_bits_to_f32(s16).astype(np.float64),
+                             bf16_bits_to_f32(t16).astype(np.float64), LN_EPS)
+    yk = bf16_bits_to_f32(y16[rows]).astype(np.float64)
+    rms = np.sqrt(np.mean(y64 * y64))
+    assert np.all(np.abs(yk - y64) <= 4e-3 * np.abs(y64) + 1e-3 * rms)
 
 
 def test_empty_input():

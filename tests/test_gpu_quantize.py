@@ -139,8 +139,12 @@ def test_edge_rows():
     _assert_same(x, "edge rows")
 
 
+# every row layout of the kernel: four rows per wave (K <= 128), one wave per row (K <= 2048),
+# two (K <= 8192), four (K <= 32768), and two passes beyond; at and just past each boundary
 @pytest.mark.parametrize("M,K", [(1, 8), (3, 24), (5, 520), (7, 1000), (4, 4104), (9, 512),
-                                 (13, 16392), (2, 24576), (33, 12288), (2, (1 << 24) + 8)])
+                                 (13, 16392), (2, 24576), (33, 12288), (2, (1 << 24) + 8),
+                                 (5, 2048), (6, 2056), (3, 3072), (7, 3080), (6, 8192), (3, 8200),
+                                 (5, 15360), (2, 32768), (3, 32776)])
 def test_ragged_shapes(M, K):
     x = make_rows(M, K, seed=M * 7 + K, n_outliers=max(1, K // 100))
     _assert_same(x, f"ragged {M}x{K}")
@@ -161,6 +165,26 @@ def test_full_size_workloads(name, index):
     inp = make_linear_inputs(shape, w.seed, index)
     _assert_same(inp.x, f"{name}[{index}] x {shape.M}x{shape.K}")
     _assert_same(inp.w, f"{name}[{index}] w {shape.N}x{shape.K}", weight=True)
+
+
+def test_more_row_groups_than_workgroups():
+    """4 * 2^20 + 5 rows of 136 values: one wave per row, four rows per workgroup, and at most
+    2^20 workgroups, so the last two row groups are taken by workgroups 0 and 1 on their second
+    pass. The first rows, the rows around the wrap and the last rows are checked exactly."""
+    M, K = 4 * (1 << 20) + 5, 136
+    announce(f"quantize {M}x{K}: more row groups than workgroups")
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(77)
+    x = torch.randn((M, K), generator=g, device="cuda:0").to(torch.bfloat16)
+    q, sc = dq.dq_quantize_fp8(x)
+    torch.cuda.synchronize()
+    wrap = 4 * (1 << 20)
+    rows = np.concatenate([np.arange(8), np.arange(wrap - 8, M),
+                           np.random.default_rng(3).choice(M, 64, replace=False)])
+    xs = x[torch.from_numpy(rows).to("cuda:0")].contiguous().view(torch.int16).cpu().numpy()
+    oq, osc = quantize_rows(bf16_bits_to_f32(xs.view(np.uint16)))
+    assert np.array_equal(q.cpu().numpy()[rows], oq)
+    assert np.array_equal(sc.cpu().numpy()[rows].view(np.uint32), osc.view(np.uint32))
 
 
 def test_deterministic():
