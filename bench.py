@@ -44,7 +44,7 @@ KERNEL_SOURCES = {
     "ln_modulate": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "quantize.hip"),
     "qkv": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "gemm_fp8.hip"),
     "attention": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "attention.hip"),
-    "mx_linear": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "gemm_mx.hip"),
+    "mx_linear": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "gemm_fp8.hip"),
 }
 
 
@@ -907,7 +907,7 @@ def main():
             f"({tf:.0f} TFLOP/s), quantizer {mx['quant_us']:.1f} us ({gbq:.0f} GB/s); per-row FP8 "
             f"GEMM {mx['rowwise_us']:.1f} us")
         res["mx_linear"] = {
-            "kernel": "gemm_mx<%s>" % mx["epilogue"],
+            "kernel": "gemm_fp8_pp<mx_%s>" % mx["epilogue"],
             "timing": "HIP events around each call, rotating inputs",
             "shape": mx["shape"], "epilogue": mx["epilogue"], "bound": "mfma",
             "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",

@@ -76,7 +76,21 @@ constexpr int kGroupM = 4;                      // tile rows per group in the ti
 constexpr int kPartFloats = kBM * kBN;
 constexpr int kMaxSeg = (int)kMaxSegments;      // row segments with their own weights
 
-enum { EPI_BIAS = 0, EPI_GELU_TANH = 1, EPI_GATED_RESIDUAL = 2, EPI_QKV = 3 };
+enum { EPI_BIAS = 0, EPI_GELU_TANH = 1, EPI_GATED_RESIDUAL = 2, EPI_QKV = 3,
+       EPI_MX_BIAS = 4, EPI_MX_GELU_TANH = 5 };
+
+// Block-scaled (MX) operands: E4M3 codes with one E8M0 scale byte per 32 values along K. Each
+// K step then also stages the 4 scale bytes (one dword) of every A and B row of the tile, after
+// the codes of the stage: for each group of 32 tile rows (A rows, then B rows) a 256-byte slot
+// whose first 128 bytes hold the 32 rows' dwords (a copy instruction moves 64 lanes' dwords and
+// its upper 32 lanes fill the rest with zeros, so no lane needs to be switched off).
+constexpr int kScaleBytes = 4096;
+__host__ __device__ constexpr bool is_mx(int epi) { return epi >= EPI_MX_BIAS; }
+__host__ __device__ constexpr int stage_bytes(int epi) {
+  return kStageBytes + (is_mx(epi) ? kScaleBytes : 0);
+}
+// Copy instructions per batch: four of codes, plus one of scales in MX mode.
+__host__ __device__ constexpr int batch_ops(int epi) { return is_mx(epi) ? 5 : 4; }
 
 // Arguments of the QKV epilogue only. They are read where they are used (the epilogue and the
 // parameter copy), through qkv_args(), so that they do not sit in scalar registers through the
@@ -113,6 +127,8 @@ struct Params {
   uint32_t* flags;           // [left-over tiles] arrival counters (cut tiles only)
   float* part;               // [parts][256 * 256] partial tiles (cut tiles only)
   uint32_t part_bytes;       // bytes of the partial tiles
+  const uint8_t* mxa;        // MX only: A's scale bytes [M, K / 32]
+  const uint8_t* mxw;        // MX only: B's scale bytes [N, K / 32]
   int M, N, K, tilesM, tilesN, nk, tiles;
   int dp_tiles;              // tiles of full rounds run by this launch (a multiple of the grid)
   int tail0;                 // first left-over tile
@@ -200,9 +216,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // All vector memory operations of this wavefront done (vmcnt = 0; lgkm and exp untouched).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// All but the last four vector memory operations of this wavefront done (vmcnt <= 4). Memory
-// operations of one wavefront are counted off in the order they were issued.
-__device__ __forceinline__ void wait_vmem_but4() { __builtin_amdgcn_s_waitcnt(0x0F74); }
+// All but the last N (one batch: 4, or 5 in MX mode) vector memory operations of this wavefront
+// done (vmcnt <= N). Memory operations of one wavefront are counted off in the order they were
+// issued.
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() { __builtin_amdgcn_s_waitcnt(0x0F70 | N); }
 
 // Phase boundary: this wavefront's LDS reads done, then the workgroup barrier. No instruction
 // is scheduled across it (the MFMAs of a phase must stay in their phase).
@@ -316,11 +334,12 @@ __device__ __forceinline__ Geo item_geo(const Params& p, int t, int half) {
 struct TileDesc {
   Geo g;  // origin of the tile (of the half, in a narrow launch), segment end, segment
   v4i rsA, rsB;
+  v4i rsSA, rsSB;  // MX only: the tile rows' scale bytes
 };
 
 // Descriptors of a tile or of one half of it: rows past the segment end (columns past N) are out
 // of range and read as zero (a half entirely past N has an empty B range).
-template <int NB>
+template <int NB, bool MX>
 __device__ __forceinline__ TileDesc tile_desc(const Params& p, int t, int half) {
   TileDesc d;
   d.g = item_geo<NB>(p, t, half);
@@ -332,6 +351,11 @@ __device__ __forceinline__ TileDesc tile_desc(const Params& p, int t, int half) 
   d.rsA = buffer_rsrc(p.A + (size_t)m0 * (size_t)p.K, rowsA * (uint32_t)p.K);
   d.rsB = buffer_rsrc(seg_args()->B[d.g.s] + (size_t)(rb > 0 ? n0 : 0) * (size_t)p.K,
                       rowsB * (uint32_t)p.K);
+  if (MX) {
+    const uint32_t kb = (uint32_t)p.K / 32u;
+    d.rsSA = buffer_rsrc(p.mxa + (size_t)m0 * kb, rowsA * kb);
+    d.rsSB = buffer_rsrc(p.mxw + (size_t)(rb > 0 ? n0 : 0) * kb, rowsB * kb);
+  }
   return d;
 }
 
@@ -360,9 +384,11 @@ __device__ __forceinline__ TileDesc tile_desc(const Params& p, int t, int half) 
 struct Batch {
   v4i rs01, rs23;        // blocks 0-1 and 2-3
   uint32_t off0, lds01, lds23;
+  v4i rsS;               // MX only: the batch's 32 rows' scale dwords of step k (lanes 0-31)
+  uint32_t soff, slds;
 };
 
-template <int NB>
+template <int NB, bool MX>
 __device__ __forceinline__ Batch batch_of(const TileDesc& d, uint32_t K, int k, uint8_t* st,
                                           uint32_t vlane, int q, int which, bool live) {
   Batch b;
@@ -390,7 +416,25 @@ __device__ __forceinline__ Batch batch_of(const TileDesc& d, uint32_t K, int k, 
     b.lds23 = region + (uint32_t)(((which == 2 ? 192 : 128) + q * 16) * kBK);
   }
   b.off0 = (uint32_t)grow * K + vlane + (uint32_t)k * kBK;
+  if (MX) {
+    // lane i < n fetches the dword of tile row grow + i, the other lanes read past the range;
+    // n = 32 rows per slot, or 16 for the B rows of a narrow half (16 per batch there)
+    const bool n16 = NB == 1 && which >= 2;
+    b.rsS = which < 2 ? d.rsSA : d.rsSB;
+    if (!live) b.rsS[2] = 0;
+    const uint32_t kb = K / 32u;
+    const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    b.soff = lane < (n16 ? 16u : 32u) ? ((uint32_t)grow + lane) * kb + (uint32_t)k * 4u
+                                      : 0xFFFFFFF0u;
+    b.slds = base + (uint32_t)kStageBytes + (which < 2 ? 0u : 2048u) +
+             (uint32_t)(n16 ? grow >> 4 : grow >> 5) * 256u;
+  }
   return b;
+}
+
+// The scale dwords of a batch (MX): lanes 0-31 one row each (no branch: see batch_of).
+__device__ __forceinline__ void copy_scales(const Batch& b) {
+  copy_to_lds_b32(b.rsS, b.soff, __builtin_amdgcn_readfirstlane(b.slds));
 }
 
 __device__ __forceinline__ void copy_block(const Batch& b, uint32_t K, uint32_t dodd, int j) {
@@ -399,12 +443,13 @@ __device__ __forceinline__ void copy_block(const Batch& b, uint32_t K, uint32_t 
                                              (uint32_t)((j & 1) * 1024)));
 }
 
-template <int NB>
+template <int NB, bool MX>
 __device__ __forceinline__ void copy_batch(const TileDesc& d, uint32_t K, int k, uint8_t* st,
                                            uint32_t vlane, uint32_t dodd, int q, int which) {
-  const Batch b = batch_of<NB>(d, K, k, st, vlane, q, which, true);
+  const Batch b = batch_of<NB, MX>(d, K, k, st, vlane, q, which, true);
 #pragma unroll
   for (int j = 0; j < 4; ++j) copy_block(b, K, dodd, j);
+  if (MX) copy_scales(b);
 }
 
 // The tile's epilogue parameters into param buffer pb, one copy per group-0 wave (q).
@@ -422,7 +467,9 @@ __device__ __forceinline__ void copy_params(const Params& p, const TileDesc& d, 
   const int nc = p.N - n0 < kBN ? p.N - n0 : kBN;
   const uint32_t cols = (uint32_t)(nc > 0 ? nc : 0);
   if (nc <= 0) n0 = 0;
-  if (q == 0) {
+  if (is_mx(EPI) && q != 2) {
+    // block-scaled operands carry their scales with the codes: only the bias is copied
+  } else if (q == 0) {
     // a segment may start at any row, so the scales move 4 bytes per lane (4 x 64 of them)
     const v4i rs = buffer_rsrc(p.sa + m0, rows * 4u);
 #pragma unroll
@@ -446,22 +493,28 @@ __device__ __forceinline__ void copy_params(const Params& p, const TileDesc& d, 
 struct Frags {
   v8i a[4];  // rows wm * 128 + 32 i + (lane & 31) of the A tile
   v8i b[2];  // B rows: full tile wn * 64 + 32 i + (lane & 31); narrow tile only b[0]
+  uint32_t sa[4], sb[2];  // MX only: those rows' scale dwords, shifted right by 8 (lane >> 5)
 };
 
 // Fragments of K half h (64 bytes) of one staged step: lane l reads row l & 31 of each 32-row
 // block, bytes [64 h + 32 (l >> 5), +32) -- the same K positions for A and B. NB is the number
 // of 32-column blocks per wave: 2 in a full tile; 1 in a narrow one, whose block (tile rows
 // 32 wn + [0, 32)) sits at LDS rows 64 g + 32 (q & 1) + [0, 32).
-template <int NB>
+// In MX mode the scaled instruction takes a row's 64 codes as two blocks of 32, registers 0-3 of
+// lanes l and l + 32 holding the first block and registers 4-7 the second: lane l reads chunks
+// 4 h + (l >> 5) and 4 h + 2 + (l >> 5) (16 codes each), and with K half 0 the rows' scale
+// dwords, of which the instruction selects byte 2 h.
+template <int NB, bool MX>
 __device__ __forceinline__ void read_frags(const uint8_t* st, Frags& f, int h, int wm, int wn,
                                            int lane) {
   const int r = lane & 31;
-  const int c0 = h * 4 + (lane >> 5) * 2;
+  const int c0 = MX ? h * 4 + (lane >> 5) : h * 4 + (lane >> 5) * 2;
+  const int dc = MX ? 2 : 1;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint8_t* ab = st + (wm * 128 + i * 32) * kBK;
     const uint4 lo = *reinterpret_cast<const uint4*>(ab + swz(r, c0));
-    const uint4 hi = *reinterpret_cast<const uint4*>(ab + swz(r, c0 + 1));
+    const uint4 hi = *reinterpret_cast<const uint4*>(ab + swz(r, c0 + dc));
     f.a[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
@@ -471,25 +524,43 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, Frags& f, int h, i
   for (int i = 0; i < NB; ++i) {
     const uint8_t* bb = st + kBM * kBK + (b0 + i * 32) * kBK;
     const uint4 lo = *reinterpret_cast<const uint4*>(bb + swz(r, c0));
-    const uint4 hi = *reinterpret_cast<const uint4*>(bb + swz(r, c0 + 1));
+    const uint4 hi = *reinterpret_cast<const uint4*>(bb + swz(r, c0 + dc));
     f.b[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  if (MX && h == 0) {  // 256-byte slots (A rows from 0, B rows from 2048)
+    const uint32_t* sc = reinterpret_cast<const uint32_t*>(st + kStageBytes);
+    const int sh = 8 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.sa[i] = sc[64 * (wm * 4 + i) + r] >> sh;
+    if (NB == 2) {  // a slot per 32 rows
+#pragma unroll
+      for (int i = 0; i < NB; ++i) f.sb[i] = sc[512 + 64 * ((b0 >> 5) + i) + r] >> sh;
+    } else {        // narrow half: the wave's B rows are tile rows 32 wn + [0, 32), 16 per slot
+      const int tr = 32 * wn + r;
+      f.sb[0] = sc[512 + 64 * (tr >> 4) + (tr & 15)] >> sh;
+    }
   }
 }
 
 // The MFMAs of one K half (8, or 4 in a narrow tile), with the four copies of batch b issued one
 // after each of the first four: a copy instruction waits for the vector memory unit to take it, which here
 // overlaps the matrix unit's work instead of holding up the next phase.
-template <int NB>
+template <int NB, bool MX, int H>
 __device__ __forceinline__ void mma8_copy(const Frags& f, v16f (&acc)[NB][4], const Batch& b,
                                           uint32_t K, uint32_t dodd) {
 #pragma unroll
   for (int bn = 0; bn < NB; ++bn)
 #pragma unroll
     for (int bm = 0; bm < 4; ++bm) {
-      acc[bn][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[bn], f.a[bm], acc[bn][bm],
-                                                                     0, 0, 0, 0, 0, 0);
+      if (MX)
+        acc[bn][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            f.b[bn], f.a[bm], acc[bn][bm], 0, 0, 2 * H, (int)f.sb[bn], 2 * H, (int)f.sa[bm]);
+      else
+        acc[bn][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            f.b[bn], f.a[bm], acc[bn][bm], 0, 0, 0, 0, 0, 0);
       if (bn == 0) copy_block(b, K, dodd, bm);
+      if (MX && bn == NB - 1 && bm == 0) copy_scales(b);
       __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -550,10 +621,17 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[NB][4], const Params&
           const int nl = wn * 32 * NB + bn * 32 + g * 8 + hi * 4;
           const float4 swv = *reinterpret_cast<const float4*>(s_sw + nl);
           const uint2 bb = *reinterpret_cast<const uint2*>(s_b + nl);
-          v[h][0] = fmaf(acc[bn][bm][g * 4 + 0] * sam, swv.x, bf16_lo(bb.x));
-          v[h][1] = fmaf(acc[bn][bm][g * 4 + 1] * sam, swv.y, bf16_hi(bb.x));
-          v[h][2] = fmaf(acc[bn][bm][g * 4 + 2] * sam, swv.z, bf16_lo(bb.y));
-          v[h][3] = fmaf(acc[bn][bm][g * 4 + 3] * sam, swv.w, bf16_hi(bb.y));
+          if (is_mx(EPI)) {  // the block scales were applied by the matrix instruction
+            v[h][0] = acc[bn][bm][g * 4 + 0] + bf16_lo(bb.x);
+            v[h][1] = acc[bn][bm][g * 4 + 1] + bf16_hi(bb.x);
+            v[h][2] = acc[bn][bm][g * 4 + 2] + bf16_lo(bb.y);
+            v[h][3] = acc[bn][bm][g * 4 + 3] + bf16_hi(bb.y);
+          } else {
+            v[h][0] = fmaf(acc[bn][bm][g * 4 + 0] * sam, swv.x, bf16_lo(bb.x));
+            v[h][1] = fmaf(acc[bn][bm][g * 4 + 1] * sam, swv.y, bf16_hi(bb.x));
+            v[h][2] = fmaf(acc[bn][bm][g * 4 + 2] * sam, swv.z, bf16_lo(bb.y));
+            v[h][3] = fmaf(acc[bn][bm][g * 4 + 3] * sam, swv.w, bf16_hi(bb.y));
+          }
         }
         // Before: lane l < 32 holds columns [0, 4) of group 2gp in v[0] and of group 2gp+1 in
         // v[1]; lane l + 32 holds columns [4, 8) of both. After the swap lane l owns group 2gp
@@ -563,7 +641,7 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[NB][4], const Params&
         const int nl = wn * 32 * NB + bn * 32 + (gp * 2 + hi) * 8;
         const int n = n0 + nl;
         float y[8] = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
-        if (EPI == EPI_GELU_TANH) {
+        if (EPI == EPI_GELU_TANH || EPI == EPI_MX_GELU_TANH) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) y[j] = gelu_tanh(y[j]);
         }
@@ -860,9 +938,12 @@ __device__ __forceinline__ bool same_tile(const Cursor& a, const Cursor& b) {
 // NB = 2: whole tiles and cut parts; NB = 1: the narrow halves of left-over tiles.
 template <int EPI, int NB>
 __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes + kParamBufs * kParamBytes];
+  constexpr bool MX = is_mx(EPI);
+  constexpr int kStage = stage_bytes(EPI);
+  constexpr int kOps = batch_ops(EPI);
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStage + kParamBufs * kParamBytes];
   __shared__ int s_last;
-  uint8_t* pbuf = lds + 2 * kStageBytes;
+  uint8_t* pbuf = lds + 2 * kStage;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -903,28 +984,28 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
     Cursor c0;
     c0.item = 0;
     cursor_item<NB>(p, w, v, G, c0);
-    const TileDesc d0 = tile_desc<NB>(p, c0.t, c0.half);
+    const TileDesc d0 = tile_desc<NB, MX>(p, c0.t, c0.half);
     if (g == 0) {
-      copy_batch<NB>(d0, uK, c0.k, lds, vlane, dodd, q, 0);
-      copy_batch<NB>(d0, uK, c0.k, lds, vlane, dodd, q, 1);
+      copy_batch<NB, MX>(d0, uK, c0.k, lds, vlane, dodd, q, 0);
+      copy_batch<NB, MX>(d0, uK, c0.k, lds, vlane, dodd, q, 1);
       copy_params<EPI>(p, d0, pbuf, q, lane);
     } else {
-      copy_batch<NB>(d0, uK, c0.k, lds, vlane, dodd, q, 2);
-      copy_batch<NB>(d0, uK, c0.k, lds, vlane, dodd, q, 3);
+      copy_batch<NB, MX>(d0, uK, c0.k, lds, vlane, dodd, q, 2);
+      copy_batch<NB, MX>(d0, uK, c0.k, lds, vlane, dodd, q, 3);
     }
     c1 = c0;
     cursor_next<NB>(p, w, v, G, c1);
-    d1 = same_tile(c1, c0) ? d0 : tile_desc<NB>(p, c1.t, c1.half);
+    d1 = same_tile(c1, c0) ? d0 : tile_desc<NB, MX>(p, c1.t, c1.half);
     c2 = c1;
     cursor_next<NB>(p, w, v, G, c2);
-    d2 = same_tile(c2, c1) ? d1 : tile_desc<NB>(p, c2.t, c2.half);
+    d2 = same_tile(c2, c1) ? d1 : tile_desc<NB, MX>(p, c2.t, c2.half);
   }
   wait_vmem();
   phase_barrier();
   // batch 3 of step 1 (G0, as in phase D of step -1) and batch 0 of step 1 (G1, as in its
   // MFMA phase of step -1), then group 1 falls one phase behind
   if (nsteps > 1)
-    copy_batch<NB>(d1, uK, c1.k, lds + kStageBytes, vlane, dodd, q, g == 0 ? 3 : 0);
+    copy_batch<NB, MX>(d1, uK, c1.k, lds + kStage, vlane, dodd, q, g == 0 ? 3 : 0);
   if (g == 1) phase_barrier();
 
   Frags f;
@@ -941,36 +1022,36 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
     for (int j = 0; j < len; ++j, ++S) {
-      uint8_t* st = lds + (S & 1) * kStageBytes;
-      uint8_t* st1 = lds + ((S + 1) & 1) * kStageBytes;
+      uint8_t* st = lds + (S & 1) * kStage;
+      uint8_t* st1 = lds + ((S + 1) & 1) * kStage;
       const bool has1 = S + 1 < nsteps, has2 = S + 2 < nsteps;
       const bool starts = has1 && (j + 1 == len);  // step S + 1 begins the next item
       // reads of K half 0 (G0: phase A, G1: phase B)
-      read_frags<NB>(st, f, 0, wm, wn, lane);
+      read_frags<NB, MX>(st, f, 0, wm, wn, lane);
       phase_barrier();
       // MFMAs of K half 0 with batch g + 1 of step S + 1 (G0: phase B, G1: phase C)
-      mma8_copy<NB>(f, acc, batch_of<NB>(d1, uK, c1.k, st1, vlane, q, g + 1, has1), uK, dodd);
+      mma8_copy<NB, MX, 0>(f, acc, batch_of<NB, MX>(d1, uK, c1.k, st1, vlane, q, g + 1, has1), uK, dodd);
       phase_barrier();
       // reads of K half 1 (G0: phase C, G1: phase D); G0 starts the next item's parameters,
       // G1 waits for its batch 0 of step S + 1
-      read_frags<NB>(st, f, 1, wm, wn, lane);
+      read_frags<NB, MX>(st, f, 1, wm, wn, lane);
       if (g == 0) {
         if (starts)
           copy_params<EPI>(p, d1, pbuf + ((part + 1) % kParamBufs) * kParamBytes, q, lane);
       } else {
-        if (has1) wait_vmem_but4(); else wait_vmem();
+        if (has1) wait_vmem_but<kOps>(); else wait_vmem();
       }
       phase_barrier();
       // MFMAs of K half 1 (G0: phase D, G1: phase A of S + 1) with batch 3 (G0) or 0 (G1) of
       // step S + 2, into this stage; the cursors move on meanwhile; then every wave waits for
       // all but that batch
-      mma8_copy<NB>(f, acc, batch_of<NB>(d2, uK, c2.k, st, vlane, q, g == 0 ? 3 : 0, has2), uK,
+      mma8_copy<NB, MX, 1>(f, acc, batch_of<NB, MX>(d2, uK, c2.k, st, vlane, q, g == 0 ? 3 : 0, has2), uK,
                     dodd);
       c1 = c2;
       d1 = d2;
       cursor_next<NB>(p, w, v, G, c2);
-      if (!same_tile(c2, c1) && S + 3 < nsteps) d2 = tile_desc<NB>(p, c2.t, c2.half);
-      wait_vmem_but4();
+      if (!same_tile(c2, c1) && S + 3 < nsteps) d2 = tile_desc<NB, MX>(p, c2.t, c2.half);
+      wait_vmem_but<kOps>();
       phase_barrier();
     }
     const Geo gi = item_geo<NB>(p, t, half);
@@ -1141,6 +1222,8 @@ static hipError_t schedule_and_launch(Params& p, int64_t M, int64_t K, int64_t N
     case EPI_BIAS: return launch_epi<EPI_BIAS>(p, g, ng, stream);
     case EPI_GELU_TANH: return launch_epi<EPI_GELU_TANH>(p, g, ng, stream);
     case EPI_QKV: return launch_epi<EPI_QKV>(p, g, ng, stream);
+    case EPI_MX_BIAS: return launch_epi<EPI_MX_BIAS>(p, g, ng, stream);
+    case EPI_MX_GELU_TANH: return launch_epi<EPI_MX_GELU_TANH>(p, g, ng, stream);
     default: return launch_epi<EPI_GATED_RESIDUAL>(p, g, ng, stream);
   }
 }
@@ -1204,6 +1287,23 @@ hipError_t launch_linear_segmented(const uint8_t* q, const float* scale, int64_t
     p.seg.gate[i] = gate[i];
   }
   return schedule_and_launch(p, M, K, N, epilogue, workspace, workspace_bytes, stream);
+}
+
+// Block-scaled (MX) linear: the same kernel in MX mode (no workspace, so the left-over tiles of
+// the last round run whole or as narrow halves, never cut).
+hipError_t launch_linear_mx(const uint8_t* qa, const uint8_t* sa, int64_t M, int64_t K,
+                            const uint8_t* qw, const uint8_t* sw, int64_t N, const uint16_t* bias,
+                            int epilogue, uint16_t* out, hipStream_t stream) {
+  Params p{};
+  if (set_segments(p, 1, &M) == 0) return hipSuccess;
+  p.A = qa;
+  p.out = out;
+  p.mxa = sa;
+  p.mxw = sw;
+  p.seg.B[0] = qw;
+  p.seg.bias[0] = bias;
+  return schedule_and_launch(p, M, K, N, epilogue == 1 ? EPI_MX_GELU_TANH : EPI_MX_BIAS, nullptr,
+                             0, stream);
 }
 
 // ---------------------------------------------------------------------------------------------
