@@ -42,6 +42,8 @@ KERNEL_SOURCES = {
     "gemm": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "gemm_fp8.hip"),
     "quantize": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "quantize.hip"),
     "ln_modulate": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "quantize.hip"),
+    "ln_modulate_y": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "quantize.hip"),
+    "mx_quantize": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "gemm_mx.hip"),
     "qkv": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "gemm_fp8.hip"),
     "attention": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "attention.hip"),
     "mx_linear": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "gemm_fp8.hip"),
@@ -580,6 +582,8 @@ def bench_dit_step(steps, warmup, breakdown_steps=2, focus="single.linear1"):
             "gemm_frac": round(tf / PEAK_FP8_TFLOPS, 4),
             "quant_us": round(q_us, 2), "quant_gbps": round(qgb, 1),
             "quant_frac": round(qgb / PEAK_HBM_GBPS, 4),
+            "gemm_traffic": stored_traffic("gemm", f"flux-dit-step-1024/{c['name']}"),
+            "quant_traffic": stored_traffic("quantize", f"flux-dit-step-1024/{c['name']}"),
         }
     for row in table.values():
         row["ms_per_step"] = round(row["per_step"] * (row["gemm_us"] + row["quant_us"]) / 1e3, 3)
@@ -790,7 +794,7 @@ def main():
                            f"the kernels run on"),
                 "bound": "mfma", "achieved": round(ftf, 2), "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ftf / PEAK_FP8_TFLOPS, 4),
-                "traffic": stored_traffic("gemm", "flux-single-block-1024"),
+                "traffic": stored_traffic("gemm", f"flux-dit-step-1024/{d['focus']}"),
                 "avg_launch_us": round(d["focus_gemm_us"], 2),
                 "algorithmic_flop_per_launch": focus.flops,
             },
@@ -806,7 +810,8 @@ def main():
         shape = w.linears[args.linear]
         log(f"workload {w.name}[{args.linear}] M={shape.M} K={shape.K} N={shape.N} "
             f"epilogue={shape.epilogue}; warmup {args.warmup}, steps {args.steps}")
-        leg = linear_leg(shape, w.seed, args.steps, args.warmup, args.sets, w.name)
+        leg = linear_leg(shape, w.seed, args.steps, args.warmup, args.sets,
+                         f"{w.name}/{shape.name}")
         ms_per_step = leg["step_us"] / 1e3
         res.update({
             "value": round(shape.flops / ms_per_step / 1e9, 3), "unit": "TFLOP/s",
@@ -837,7 +842,8 @@ def main():
         res["configs"] = {}
         for name in cfg_names:
             cw = workload(name)
-            res["configs"][name] = {l.name: linear_leg(l, cw.seed, ls, 20, args.sets, name)
+            res["configs"][name] = {l.name: linear_leg(l, cw.seed, ls, 20, args.sets,
+                                                       f"{name}/{l.name}")
                                     for l in cw.linears}
     shape = workload("flux-mlp-up-1024").linears[0]
     seed = workload("flux-mlp-up-1024").seed
@@ -855,11 +861,12 @@ def main():
             "timing": "back-to-back launches over rotating inputs, HIP events around the loop",
             "shape": [Mm, Km], "bound": "hbm", "achieved": round(gb_no_y, 1),
             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gb_no_y / PEAK_HBM_GBPS, 4),
-            "traffic": stored_traffic("ln_modulate", "flux-mlp-up-1024"),
+            "traffic": stored_traffic("ln_modulate", "fused-1024"),
             "avg_launch_us": round(mo["no_y_us"], 2), "algorithmic_bytes_per_launch": b_no_y,
             "with_y": {"avg_launch_us": round(mo["y_us"], 2), "achieved": round(gb_y, 1),
                        "frac": round(gb_y / PEAK_HBM_GBPS, 4),
-                       "algorithmic_bytes_per_launch": b_y},
+                       "algorithmic_bytes_per_launch": b_y,
+                       "traffic": stored_traffic("ln_modulate_y", "fused-1024")},
             "unfused_torch_then_quantize_us": round(mo["unfused_us"], 2),
         }
     if not args.no_qkv:
@@ -873,7 +880,7 @@ def main():
             "shape": qk["shape"], "heads": qk["heads"], "bound": "mfma",
             "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / PEAK_FP8_TFLOPS, 4),
-            "traffic": stored_traffic("qkv", "flux-mlp-up-1024"),
+            "traffic": stored_traffic("qkv", "fused-1024"),
             "avg_launch_us": round(qk["fused_us"], 2),
             "algorithmic_flop_per_launch": qk["flops"],
             "bias_epilogue_us": round(qk["plain_us"], 2),
@@ -893,7 +900,7 @@ def main():
             "bound": "mfma", "achieved": round(tf, 1), "peak": round(mixed_peak, 1),
             "peak_note": "q k^T on FP8 (5.0 PF), p v on bf16 (2.5 PF): 4 / (2/5.0 + 2/2.5) PF",
             "unit": "TFLOP/s", "frac": round(tf / mixed_peak, 4),
-            "traffic": stored_traffic("attention", "flux-mlp-up-1024"),
+            "traffic": stored_traffic("attention", "fused-1024"),
             "avg_launch_us": round(at["attn_us"], 2),
             "algorithmic_flop_per_launch": at["flops"],
             "qkv_quantization_us": round(at["quant_us"], 2),
@@ -912,11 +919,12 @@ def main():
             "shape": mx["shape"], "epilogue": mx["epilogue"], "bound": "mfma",
             "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / PEAK_FP8_TFLOPS, 4),
-            "traffic": stored_traffic("mx_linear", "flux-mlp-up-1024"),
+            "traffic": stored_traffic("mx_linear", "fused-1024"),
             "avg_launch_us": round(mx["gemm_us"], 2),
             "algorithmic_flop_per_launch": mx["flops"],
             "quantizer_us": round(mx["quant_us"], 2),
             "quantizer_gbps": round(gbq, 1),
+            "quantizer_traffic": stored_traffic("mx_quantize", "fused-1024"),
             "rowwise_fp8_gemm_us": round(mx["rowwise_us"], 2),
         }
     if not args.no_cpu_baseline:
