@@ -9,14 +9,15 @@ single-stream blocks), each a per-token FP8 quantization of its bf16 activations
 weights per block (8.6 GB of FP8 codes, quantized once off the timed path). A step is one pass
 over that sequence; W untimed steps, then K timed steps between two HIP events on the stream.
 `value` is the step's TFLOP/s; `roofline` is the step's dominant kernel, the GEMM of the
-single-stream blocks' first linear (4608 x 3072 -> 21504), timed by event pairs around each of
-its calls in the timed steps.
+single-stream blocks' first linear (4608 x 3072 -> 21504), timed by an event pair around one of
+its calls in each timed step.
 
 After the headline, one leg per further configuration (the tiny linear, the MLP up-projection at
 1024^2 and at 2048^2, the single-stream block pair), each quantize + GEMM over rotating buffer
 sets; then the fused kernels (LayerNorm + modulation + quantize, the QKV projection with its
 norm + rotary epilogue, FP8 attention, the block-scaled FP8 GEMM); then the CPU oracle timed on
-the host on a bounded sample of the step, and on the four single configurations whole.
+the host on a bounded sample of the step, and on the four single configurations whole. Every
+leg is timed as back-to-back calls with one event pair around the loop.
 Every input is a seeded synthetic tensor resident in HBM before timing starts.
 
 Prints one JSON line.
@@ -80,6 +81,25 @@ def to_dev_bf16(torch, u16, dev):
     return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
+def loop_us(fn, sets, reps, warmup):
+    """Microseconds per call of `fn` over `reps` back-to-back calls on the rotating `sets`, with one
+    HIP event pair around the loop on the current stream (after `warmup` untimed calls and a
+    synchronization). An event between two launches keeps the second from starting under the
+    first one's tail and adds about 10 us of idle time, so calls are not bracketed one by one."""
+    import torch
+    for i in range(warmup):
+        fn(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(sets[i % len(sets)])
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
 def bench_linear(shape, seed, steps, warmup, n_sets):
     """Time `steps` steps of quantize + linear. Returns a dict of timings."""
     import torch
@@ -107,56 +127,28 @@ def bench_linear(shape, seed, steps, warmup, n_sets):
         sets.append(st)
     torch.cuda.synchronize()
 
-    def step(st):
+    def quantize(st):
         dq.dq_quantize_fp8(st["x"], st["q"], st["sa"])
-        e_mid = torch.cuda.Event(enable_timing=True)
-        e_mid.record()
+
+    def linear(st):
         if gated:   # in place on the residual stream, as in the model
             dq.dq_linear_fp8(st["q"], st["sa"], st["qw"], st["sw"], st["bias"], shape.epilogue,
                              st["gate"], st["res"], out=st["res"])
         else:
             dq.dq_linear_fp8(st["q"], st["sa"], st["qw"], st["sw"], st["bias"], shape.epilogue,
                              out=st["out"])
-        return e_mid
 
-    for i in range(warmup):
-        step(sets[i % n_sets])
-    torch.cuda.synchronize()
-    starts, mids, ends = [], [], []
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    def step(st):
+        quantize(st)
+        linear(st)
+
     wall0 = time.perf_counter()
-    t_begin.record()
-    for i in range(steps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        em = step(sets[i % n_sets])
-        e1 = torch.cuda.Event(enable_timing=True)
-        e1.record()
-        starts.append(e0)
-        mids.append(em)
-        ends.append(e1)
-    t_end.record()
-    torch.cuda.synchronize()
+    step_us = loop_us(step, sets, steps, warmup)
     wall = time.perf_counter() - wall0
-    total_ms = t_begin.elapsed_time(t_end)
-    q_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, mids)])
-    g_ms = np.array([a.elapsed_time(b) for a, b in zip(mids, ends)])
-    # the quantizer alone, back to back (its launches are short, so per-launch events would
-    # mostly time the events themselves)
-    reps = 4 * steps
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(reps):
-        st = sets[i % n_sets]
-        dq.dq_quantize_fp8(st["x"], st["q"], st["sa"])
-    e1.record()
-    torch.cuda.synchronize()
-    q_loop_ms = e0.elapsed_time(e1) / reps
-    return {"total_ms": total_ms, "wall_s": wall, "quant_ms": q_ms, "gemm_ms": g_ms,
-            "quant_loop_ms": q_loop_ms}
+    gemm_us = loop_us(linear, sets, steps, n_sets)
+    # the quantizer's launches are short: four times as many
+    quant_us = loop_us(quantize, sets, 4 * steps, n_sets)
+    return {"step_us": step_us, "wall_s": wall, "gemm_us": gemm_us, "quant_us": quant_us}
 
 
 def bench_modulate(M, K, steps, n_sets, seed=11):
@@ -188,17 +180,7 @@ def bench_modulate(M, K, steps, n_sets, seed=11):
         dq.dq_quantize_fp8(h, st["q"], st["s"])
 
     def timed(fn, reps):
-        for i in range(max(reps // 4, n_sets)):
-            fn(sets[i % n_sets])
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(reps):
-            fn(sets[i % n_sets])
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps * 1e3
+        return loop_us(fn, sets, reps, max(reps // 4, n_sets))
 
     reps = 4 * steps
     return {"no_y_us": timed(lambda st: fused(st, False), reps),
@@ -210,7 +192,8 @@ def bench_qkv(steps, warmup, n_sets, M=4096, K=3072, heads=24, seed=3200):
     """The attention input projection of the image stream at 1024^2 (4096 tokens, 3072 -> 3 x 24
     heads x 128) with the fused query/key RMS norm + rotary epilogue, against the same GEMM with
     the plain bias epilogue and, for context, that GEMM followed by the torch ops the fusion
-    replaces. Event pairs around each call; returns microseconds per call."""
+    replaces. Back-to-back calls, one event pair around each loop; returns microseconds per
+    call."""
     import torch
     import torch.nn.functional as F
     import fp8_dynamic_quant_amd as dq
@@ -256,19 +239,7 @@ def bench_qkv(steps, warmup, n_sets, M=4096, K=3072, heads=24, seed=3200):
         return outs
 
     def timed(fn, n):
-        for i in range(warmup):
-            fn(sets[i % n_sets])
-        torch.cuda.synchronize()
-        evs = []
-        for i in range(n):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn(sets[i % n_sets])
-            e1.record()
-            evs.append((e0, e1))
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        return loop_us(fn, sets, n, warmup)
 
     return {"fused_us": timed(fused, steps), "plain_us": timed(plain, steps),
             "unfused_us": timed(unfused, max(steps // 4, 5)), "flops": 2 * M * N * K,
@@ -295,19 +266,7 @@ def bench_attention(steps, warmup, n_sets, H=24, S=4608, seed=11):
     torch.cuda.synchronize()
 
     def timed(fn, n):
-        for i in range(warmup):
-            fn(sets[i % n_sets])
-        torch.cuda.synchronize()
-        evs = []
-        for i in range(n):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn(sets[i % n_sets])
-            e1.record()
-            evs.append((e0, e1))
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        return loop_us(fn, sets, n, warmup)
 
     attn = timed(lambda st: dq.dq_attention_fp8(*st["fp8"], out=st["out"]), steps)
     quant = timed(lambda st: dq.quantize_qkv_heads_fp8(*st["bf"]), steps)
@@ -319,8 +278,8 @@ def bench_attention(steps, warmup, n_sets, H=24, S=4608, seed=11):
 def bench_mx(shape, seed, steps, warmup, n_sets):
     """The block-scaled (MX) FP8 path on the benchmark linear's shape: per-32 block quantization
     of the activations, then the GEMM on the scaled FP8 matrix instruction, weights quantized
-    once; the per-row FP8 GEMM on the same inputs is timed beside it. Event pairs around each
-    call; returns microseconds per call."""
+    once; the per-row FP8 GEMM on the same inputs is timed beside it. Back-to-back calls, one
+    event pair around each loop; returns microseconds per call."""
     import torch
     import fp8_dynamic_quant_amd as dq
 
@@ -343,35 +302,13 @@ def bench_mx(shape, seed, steps, warmup, n_sets):
     torch.cuda.synchronize()
 
     def timed(fn, n):
-        for i in range(warmup):
-            fn(sets[i % n_sets])
-        torch.cuda.synchronize()
-        evs = []
-        for i in range(n):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn(sets[i % n_sets])
-            e1.record()
-            evs.append((e0, e1))
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        return loop_us(fn, sets, n, warmup)
 
     gemm = timed(lambda st: dq.dq_linear_mx_fp8(st["qa"], st["sa"], qw, sw, bias, epi,
                                                 out=st["out"]), steps)
-    # the quantizer (a few microseconds) as back-to-back launches, one event pair around the loop
-    n_q = 4 * steps
-    for i in range(warmup):
-        dq.dq_quantize_mx_fp8(sets[i % n_sets]["x"], sets[i % n_sets]["qa"], sets[i % n_sets]["sa"])
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(n_q):
-        dq.dq_quantize_mx_fp8(sets[i % n_sets]["x"], sets[i % n_sets]["qa"], sets[i % n_sets]["sa"])
-    e1.record()
-    torch.cuda.synchronize()
-    quant = e0.elapsed_time(e1) * 1e3 / n_q
+    # the quantizer's launches are short: four times as many
+    quant = loop_us(lambda st: dq.dq_quantize_mx_fp8(st["x"], st["qa"], st["sa"]), sets,
+                    4 * steps, warmup)
     rowwise = timed(lambda st: dq.dq_linear_fp8(st["q8"], st["s8"], rq, rs, bias, epi,
                                                 out=st["out"]), steps)
     return {"gemm_us": gemm, "quant_us": quant, "rowwise_us": rowwise,
@@ -383,7 +320,7 @@ def bench_text_stream(steps, n_sets=4, seed=21):
     """The double-stream linears at 1024^2 three ways, quantized inputs already in place: the
     image stream's linear alone (4096 rows), the text stream's alone (512 rows), and both in one
     segmented call over the joint 4608 rows. Weights rotate over n_sets sets (cold, as in the
-    step). Event pairs around each call; returns microseconds per call."""
+    step). Back-to-back calls, one event pair around each loop; returns microseconds per call."""
     import torch
     import fp8_dynamic_quant_amd as dq
     from workloads import workload
@@ -428,19 +365,7 @@ def bench_text_stream(steps, n_sets=4, seed=21):
                                        out if gated else None, out=out)
 
         def timed(fn):
-            for i in range(10):
-                fn(sets[i % n_sets])
-            torch.cuda.synchronize()
-            evs = []
-            for i in range(steps):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-                fn(sets[i % n_sets])
-                e1.record()
-                evs.append((e0, e1))
-            torch.cuda.synchronize()
-            return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+            return loop_us(fn, sets, steps, 10)
 
         qt, st_, qi, si = qt.contiguous(), st_.contiguous(), qi.contiguous(), si.contiguous()
         ot, oi = ot.contiguous(), oi.contiguous()
@@ -488,9 +413,10 @@ def bench_dit_step(steps, warmup, breakdown_steps=2, focus="single.linear1"):
     text and image weights as two row segments), per single-stream block two (228 weights in
     152 quantize + linear pairs).
 
-    The timed steps carry one HIP event pair around each linear call of `focus` (the step's
-    dominant kernel), on the stream the kernels run on. After them, `breakdown_steps` further
-    steps carry event pairs around every call, for the per-call table."""
+    Each timed step carries one HIP event pair, around one call of `focus` (the step's dominant
+    kernel; step k times its k-th call, cycling), on the stream the kernels run on. After them,
+    `breakdown_steps` further steps carry event pairs around every call, for the per-call
+    table."""
     import torch
     import fp8_dynamic_quant_amd as dq
     from workloads import dit_step_device_inputs, workload
@@ -527,39 +453,49 @@ def bench_dit_step(steps, warmup, breakdown_steps=2, focus="single.linear1"):
                                        [g["gate"] for g in segs] if gated else None,
                                        out if gated else None, out=out)
 
-    def run(marks=None, all_calls=False):
-        for c in calls:
+    focus_at = [i for i, c in enumerate(calls) if c["name"] == focus]
+
+    def run(marks=None, all_calls=False, pick=-1, pool=None):
+        # events come from `pool`, created before the step is enqueued
+        for i, c in enumerate(calls):
             q, sa = qbuf[(c["M"], c["K"])]
-            timed_call = marks is not None and (all_calls or c["name"] == focus)
+            timed_call = marks is not None and (all_calls or i == pick)
+            e0 = None
             if timed_call and all_calls:
-                e0 = ev()
+                e0 = pool.pop()
                 e0.record()
             dq.dq_quantize_fp8(acts[c["act"]], q, sa)
             if timed_call:
-                e1 = ev()
+                e1 = pool.pop()
                 e1.record()
             linear(c, q, sa)
             if timed_call:
-                e2 = ev()
+                e2 = pool.pop()
                 e2.record()
-                marks.append((c["name"], e0 if all_calls else None, e1, e2))
+                marks.append((c["name"], e0, e1, e2))
 
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
     focus_marks = []
+    pool = [ev() for _ in range(2 * steps)]
     t0, t1 = ev(), ev()
     t0.record()
-    for _ in range(steps):
-        run(focus_marks)
+    for k in range(steps):
+        # one event pair per step, on a different call of the focus linear each step: an event
+        # between two launches keeps the second from starting under the first one's tail, so a
+        # pair around every call would itself lengthen the step (about 12 us per pair)
+        run(focus_marks, pick=focus_at[k % len(focus_at)], pool=pool)
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
     focus_us = float(np.mean([a.elapsed_time(b) for _, _, a, b in focus_marks])) * 1e3
 
     marks = []
+    pool = [ev() for _ in range(3 * len(calls) * breakdown_steps)]
+    torch.cuda.synchronize()
     for _ in range(breakdown_steps):
-        run(marks, all_calls=True)
+        run(marks, all_calls=True, pool=pool)
     torch.cuda.synchronize()
     by = {}
     for name, e0, e1, e2 in marks:
@@ -635,31 +571,28 @@ def cpu_oracle_linear(shape, seed):
     return t1 - t0, t2 - t1
 
 
-def cpu_baseline_dit(m_cap=1024, n_cap=3072):
-    """The oracle on a bounded sample of the DiT step: each of its 10 linear shapes with its first
-    min(M, m_cap) tokens and min(N, n_cap) output channels (full K), drawn from the same
-    distributions; the quantization time is scaled by M / M' and the linear's by (M N) / (M' N'),
-    then summed with each shape's multiplicity per step."""
+def cpu_baseline_dit():
+    """The oracle on a bounded sample of the DiT step: each of its 10 linear shapes once, whole
+    (one block's worth: the four double-stream linears of the image and of the text stream, the
+    two single-stream linears), drawn from the same distributions, each time multiplied by the
+    shape's multiplicity per step (19 or 38)."""
     from workloads import workload
     w = workload("flux-dit-step-1024")
     total, work = 0.0, 0.0
     for i, (l, rep) in enumerate(zip(w.linears, w.repeat)):
-        m, n = min(l.M, m_cap), min(l.N, n_cap)
-        sl = type(l)(l.name, m, l.K, n, l.epilogue, l.n_outliers, l.outlier_factor)
-        tq, tl = cpu_oracle_linear(sl, 100 + i)
+        tq, tl = cpu_oracle_linear(l, 100 + i)
         work += tq + tl
-        total += rep * (tq * l.M / m + tl * (l.M * l.N) / (m * n))
+        total += rep * (tq + tl)
     threads = blas_threads()
     return {
         "value": round(w.flops_per_step / total / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"each of the step's 10 linear shapes once on its first min(M, {m_cap}) tokens "
-                   f"and min(N, {n_cap}) output channels (full K), quantize x + exact float64 "
-                   f"contraction + epilogue, extrapolated by rows and columns and summed with "
-                   f"multiplicity (19 or 38) to one 228-linear step; elementwise NumPy "
-                   f"single-threaded, BLAS with {threads} threads; {work:.1f} s of CPU work"),
+        "sample": (f"each of the step's 10 linear shapes once, whole: quantize x + exact float64 "
+                   f"contraction + epilogue, times its multiplicity (19 or 38) to one "
+                   f"228-linear step; elementwise NumPy single-threaded, BLAS with {threads} "
+                   f"threads; {work:.1f} s of CPU work"),
         "seconds_per_step": round(total, 2),
         "host_cpus_visible": os.cpu_count(),
     }
@@ -699,15 +632,15 @@ def linear_leg(shape, seed, steps, warmup, n_sets, traffic_key=None):
     """Quantize + GEMM of one linear (bench_linear) as a JSON object: the quantizer against HBM
     bandwidth, the GEMM against the FP8 matrix peak."""
     r = bench_linear(shape, seed, steps, warmup, n_sets)
-    step_ms = r["total_ms"] / steps
-    gemm_ms = float(np.mean(r["gemm_ms"]))
-    quant_ms = float(r["quant_loop_ms"])
+    step_ms = r["step_us"] / 1e3
+    gemm_ms = r["gemm_us"] / 1e3
+    quant_ms = r["quant_us"] / 1e3
     qbytes = quantizer_bytes(shape.M, shape.K)
     tf = shape.flops / gemm_ms / 1e9
     gb = qbytes / quant_ms / 1e6
-    log(f"{shape.name} {shape.M}x{shape.K}->{shape.N} {shape.epilogue}: step {step_ms * 1e3:.1f} us; "
-        f"quantize {quant_ms * 1e3:.2f} us ({gb:.0f} GB/s), GEMM {gemm_ms * 1e3:.1f} us "
-        f"({tf:.0f} TFLOP/s)")
+    log(f"{shape.name} {shape.M}x{shape.K}->{shape.N} {shape.epilogue}: "
+        f"step {step_ms * 1e3:.1f} us; quantize {quant_ms * 1e3:.2f} us ({gb:.0f} GB/s), "
+        f"GEMM {gemm_ms * 1e3:.1f} us ({tf:.0f} TFLOP/s)")
     return {
         "shape": [shape.M, shape.K, shape.N], "epilogue": shape.epilogue,
         "step_us": round(step_ms * 1e3, 2),
@@ -789,9 +722,9 @@ def main():
                        "parallelism": "none (1 GPU)"},
             "roofline": {
                 "kernel": f"gemm_fp8_pp<bias> on {d['focus']} {list(focus_shape(focus))}",
-                "timing": (f"HIP event pair around each of the {d['focus_calls']} "
-                           f"{d['focus']} dq_linear_fp8 calls of the timed steps, on the stream "
-                           f"the kernels run on"),
+                "timing": (f"HIP event pair around one {d['focus']} dq_linear_fp8 call in each "
+                           f"timed step (a different block's call each step, "
+                           f"{d['focus_calls']} calls), on the stream the kernels run on"),
                 "bound": "mfma", "achieved": round(ftf, 2), "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ftf / PEAK_FP8_TFLOPS, 4),
                 "traffic": stored_traffic("gemm", f"flux-dit-step-1024/{d['focus']}"),
@@ -823,8 +756,9 @@ def main():
                        "N": shape.N, "epilogue": shape.epilogue, "rotating_sets": args.sets,
                        "parallelism": "none (1 GPU)"},
             "roofline": dict(leg["gemm"], timing=(
-                "HIP events around each dq_linear_fp8 call on its stream (one launch, or two "
-                "when the left-over tiles run as 256 x 128 halves)")),
+                "back-to-back dq_linear_fp8 calls over rotating inputs (one launch each, or two "
+                "when the left-over tiles run as 256 x 128 halves), one HIP event pair around "
+                "the loop on the stream the kernels run on")),
             "quantizer": leg["quantizer"],
         })
     if not args.no_text_stream and w.name == "flux-dit-step-1024":
@@ -833,8 +767,8 @@ def main():
             log(f"double.{part}: image {r['image_us']:.1f} us, text {r['text_us']:.1f} us, "
                 f"separate {r['separate_us']:.1f} us; joint segmented {r['joint_us']:.1f} us "
                 f"(text adds {r['text_marginal_us']:.1f} us)")
-        res["text_stream"] = {"timing": "HIP event pair around each call, weights rotating over "
-                                        "4 sets, codes already quantized",
+        res["text_stream"] = {"timing": "back-to-back calls, weights rotating over 4 sets, codes "
+                                        "already quantized, one HIP event pair around the loop",
                               "linears": ts}
     cfg_names = ["tiny-64x256x512", "flux-mlp-up-1024", "flux-single-block-1024",
                  "flux-mlp-up-2048"]
@@ -876,7 +810,8 @@ def main():
             f"bias epilogue {qk['plain_us']:.1f} us; unfused {qk['unfused_us']:.1f} us")
         res["qkv_linear"] = {
             "kernel": "gemm_fp8_pp<qkv>",
-            "timing": "HIP events around each call, rotating inputs (1 or 2 launches per call)",
+            "timing": ("back-to-back calls over rotating inputs (1 or 2 launches per call), one "
+                       "HIP event pair around the loop"),
             "shape": qk["shape"], "heads": qk["heads"], "bound": "mfma",
             "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / PEAK_FP8_TFLOPS, 4),
@@ -895,7 +830,7 @@ def main():
             f"q/k/v quantization {at['quant_us']:.1f} us; torch bf16 SDPA {at['sdpa_us']:.1f} us")
         res["attention"] = {
             "kernel": "attn_fp8",
-            "timing": "HIP events around each call, rotating inputs",
+            "timing": "back-to-back calls over rotating inputs, one HIP event pair around the loop",
             "shape": {"heads": at["H"], "tokens": at["S"], "head_dim": 128},
             "bound": "mfma", "achieved": round(tf, 1), "peak": round(mixed_peak, 1),
             "peak_note": "q k^T on FP8 (5.0 PF), p v on bf16 (2.5 PF): 4 / (2/5.0 + 2/2.5) PF",
@@ -915,7 +850,7 @@ def main():
             f"GEMM {mx['rowwise_us']:.1f} us")
         res["mx_linear"] = {
             "kernel": "gemm_fp8_pp<mx_%s>" % mx["epilogue"],
-            "timing": "HIP events around each call, rotating inputs",
+            "timing": "back-to-back calls over rotating inputs, one HIP event pair around the loop",
             "shape": mx["shape"], "epilogue": mx["epilogue"], "bound": "mfma",
             "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / PEAK_FP8_TFLOPS, 4),
