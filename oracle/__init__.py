@@ -22,7 +22,8 @@ What it computes, and where the pages say so:
     the GEMM's epilogue: page "Accelerarea generarii de imagini cu FLUX 3 Image Klein pe
     GPU-urile Blackwell NVIDIA", the paragraph on the PrimsTS GEMMs (see `qkv.py`).
   * attention over FP8 queries, keys and values (see `attention.py`) and the block-scaled
-    (MX) FP8 linear layer, the gfx950 analogue of the pages' NVFP4 (see `mx.py`).
+    (MX) linear layers with FP8 and FP4 elements, the gfx950 analogue of the pages' NVFP4 (see
+    `mx.py` and `mxfp4.py`).
 
 The pages do not fix the granularity, the FP8 flavour, the scale formula or the rounding. The
 readings taken are: one scale per token (row of x) and per output channel (row of W); OCP E4M3
