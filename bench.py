@@ -36,6 +36,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 matrix peak
+PEAK_FP4_TFLOPS = 10100.0     # MI355X dense FP4 (and FP6) matrix peak
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E bandwidth
 METRIC = "FP8-DQ linear TFLOP/s & % FP8 MFMA peak; quantizer GB/s; DiT-step linears ms"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -48,6 +49,8 @@ KERNEL_SOURCES = {
     "qkv": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "gemm_fp8.hip"),
     "attention": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "attention.hip"),
     "mx_linear": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "gemm_fp8.hip"),
+    "mxfp4_linear": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "gemm_fp8.hip"),
+    "mxfp4_quantize": os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", "gemm_mx.hip"),
 }
 
 
@@ -276,10 +279,11 @@ def bench_attention(steps, warmup, n_sets, H=24, S=4608, seed=11):
 
 
 def bench_mx(shape, seed, steps, warmup, n_sets):
-    """The block-scaled (MX) FP8 path on the benchmark linear's shape: per-32 block quantization
-    of the activations, then the GEMM on the scaled FP8 matrix instruction, weights quantized
-    once; the per-row FP8 GEMM on the same inputs is timed beside it. Back-to-back calls, one
-    event pair around each loop; returns microseconds per call."""
+    """The block-scaled (MX) paths on the benchmark linear's shape: per-32 block quantization of
+    the activations, then the GEMM on the scaled matrix instruction with FP8 (E4M3) and with FP4
+    (E2M1) elements, weights quantized once; the per-row FP8 GEMM on the same inputs is timed
+    beside them. Back-to-back calls, one event pair around each loop; returns microseconds per
+    call."""
     import torch
     import fp8_dynamic_quant_amd as dq
 
@@ -289,6 +293,7 @@ def bench_mx(shape, seed, steps, warmup, n_sets):
     epi = "gelu_tanh" if shape.epilogue == "gelu_tanh" else "bias"
     wb = to_dev_bf16(torch, inp.w, dev)
     qw, sw = dq.dq_quantize_mx_fp8(wb)
+    qw4, sw4 = dq.dq_quantize_mxfp4(wb)
     rq, rs = dq.dq_quantize_weight_fp8(wb)
     bias = to_dev_bf16(torch, inp.bias, dev)
     xb = to_dev_bf16(torch, inp.x, dev)
@@ -296,8 +301,9 @@ def bench_mx(shape, seed, steps, warmup, n_sets):
     for i in range(n_sets):
         x = xb if i == 0 else (xb * (1.0 + 0.01 * i)).to(torch.bfloat16)
         qa, sa = dq.dq_quantize_mx_fp8(x)
+        q4, s4 = dq.dq_quantize_mxfp4(x)
         q8, s8 = dq.dq_quantize_fp8(x)
-        sets.append({"x": x, "qa": qa, "sa": sa, "q8": q8, "s8": s8,
+        sets.append({"x": x, "qa": qa, "sa": sa, "q4": q4, "s4": s4, "q8": q8, "s8": s8,
                      "out": torch.empty((M, N), dtype=torch.bfloat16, device=dev)})
     torch.cuda.synchronize()
 
@@ -311,9 +317,15 @@ def bench_mx(shape, seed, steps, warmup, n_sets):
                     4 * steps, warmup)
     rowwise = timed(lambda st: dq.dq_linear_fp8(st["q8"], st["s8"], rq, rs, bias, epi,
                                                 out=st["out"]), steps)
+    gemm4 = timed(lambda st: dq.dq_linear_mxfp4(st["q4"], st["s4"], qw4, sw4, bias, epi,
+                                                out=st["out"]), steps)
+    quant4 = loop_us(lambda st: dq.dq_quantize_mxfp4(st["x"], st["q4"], st["s4"]), sets,
+                     4 * steps, warmup)
     return {"gemm_us": gemm, "quant_us": quant, "rowwise_us": rowwise,
+            "fp4_gemm_us": gemm4, "fp4_quant_us": quant4,
             "flops": 2 * M * N * K, "shape": [M, K, N], "epilogue": epi,
-            "quant_bytes": M * K * 2 + M * K + M * K // 32}
+            "quant_bytes": M * K * 2 + M * K + M * K // 32,
+            "fp4_quant_bytes": M * K * 2 + M * K // 2 + M * K // 32}
 
 
 def bench_text_stream(steps, n_sets=4, seed=21):
@@ -861,6 +873,26 @@ def main():
             "quantizer_gbps": round(gbq, 1),
             "quantizer_traffic": stored_traffic("mx_quantize", "fused-1024"),
             "rowwise_fp8_gemm_us": round(mx["rowwise_us"], 2),
+        }
+        tf4 = mx["flops"] / mx["fp4_gemm_us"] / 1e6
+        gb4 = mx["fp4_quant_bytes"] / mx["fp4_quant_us"] / 1e3
+        log(f"MXFP4 (block-scaled E2M1) {mx['shape']} {mx['epilogue']}: GEMM "
+            f"{mx['fp4_gemm_us']:.1f} us ({tf4:.0f} TFLOP/s), quantizer {mx['fp4_quant_us']:.1f} us "
+            f"({gb4:.0f} GB/s)")
+        res["mxfp4_linear"] = {
+            "kernel": "gemm_fp8_pp<mx4_%s>" % mx["epilogue"],
+            "timing": ("back-to-back calls over rotating inputs, one HIP event pair around the "
+                       "loop"),
+            "shape": mx["shape"], "epilogue": mx["epilogue"], "bound": "mfma",
+            "achieved": round(tf4, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf4 / PEAK_FP4_TFLOPS, 4),
+            "traffic": stored_traffic("mxfp4_linear", "fused-1024"),
+            "avg_launch_us": round(mx["fp4_gemm_us"], 2),
+            "algorithmic_flop_per_launch": mx["flops"],
+            "quantizer_us": round(mx["fp4_quant_us"], 2),
+            "quantizer_gbps": round(gb4, 1),
+            "quantizer_algorithmic_bytes": mx["fp4_quant_bytes"],
+            "quantizer_traffic": stored_traffic("mxfp4_quantize", "fused-1024"),
         }
     if not args.no_cpu_baseline:
         log("CPU baseline: timing the oracle on the host")

@@ -84,6 +84,10 @@ def lib() -> ctypes.CDLL:
         L.dq_quantize_mx_fp8.restype = i32
         L.dq_linear_mx_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp]
         L.dq_linear_mx_fp8.restype = i32
+        L.dq_quantize_mxfp4.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.dq_quantize_mxfp4.restype = i32
+        L.dq_linear_mxfp4.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp]
+        L.dq_linear_mxfp4.restype = i32
         L.dq_linear_fp8_workspace_size.argtypes = [i64, i64, i64]
         L.dq_linear_fp8_workspace_size.restype = ctypes.c_uint64
         L.dq_status_string.argtypes = [i32]
@@ -511,9 +515,58 @@ def dq_linear_mx_fp8(qa, sa, qw, sw, bias=None, epilogue="bias", out=None, strea
     return out
 
 
+def dq_quantize_mxfp4(x, q=None, scales=None, stream=None):
+    """Block-scaled FP4 (MXFP4) quantization of bf16 x [M, K] (K % 32 == 0): E2M1 codes, two per
+    byte, [M, K / 2] (element 2j in the low nibble of byte j), and one E8M0 scale byte per 32
+    values, [M, K / 32]."""
+    where = "dq_quantize_mxfp4"
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError(f"{where}: x must be a 2-D tensor")
+    M, K = x.shape
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (M, K), dev)
+    q = torch.empty((M, K // 2), dtype=torch.uint8, device=dev) if q is None else q
+    scales = torch.empty((M, K // MX_BLOCK), dtype=torch.uint8, device=dev) if scales is None \
+        else scales
+    _need(q, "q", torch.uint8, (M, K // 2), dev)
+    _need(scales, "scales", torch.uint8, (M, K // MX_BLOCK), dev)
+    with torch.cuda.device(dev):
+        _check(lib().dq_quantize_mxfp4(_ptr(x), M, K, _ptr(q), _ptr(scales),
+                                       _stream(stream, dev)), where)
+    return q, scales
+
+
+def dq_linear_mxfp4(qa, sa, qw, sw, bias=None, epilogue="bias", out=None, stream=None):
+    """MXFP4 linear layer -> bf16 [M, N]: packed codes qa [M, K / 2], qw [N, K / 2] and their
+    scale bytes sa [M, K / 32], sw [N, K / 32] (dq_quantize_mxfp4); epilogue "bias" or
+    "gelu_tanh"."""
+    where = "dq_linear_mxfp4"
+    if not isinstance(qa, torch.Tensor) or qa.dim() != 2 or not isinstance(qw, torch.Tensor):
+        raise ValueError(f"{where}: qa and qw must be 2-D tensors")
+    M, K = qa.shape[0], 2 * qa.shape[1]
+    N = qw.shape[0]
+    dev = qa.device
+    _need(qa, "qa", torch.uint8, (M, K // 2), dev)
+    _need(qw, "qw", torch.uint8, (N, K // 2), dev)
+    _need(sa, "sa", torch.uint8, (M, K // MX_BLOCK), dev)
+    _need(sw, "sw", torch.uint8, (N, K // MX_BLOCK), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, (N,), dev)
+    if epilogue not in ("bias", "gelu_tanh"):
+        raise ValueError(f"{where}: epilogue must be 'bias' or 'gelu_tanh'")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
+    _need(out, "out", torch.bfloat16, (M, N), dev)
+    with torch.cuda.device(dev):
+        _check(lib().dq_linear_mxfp4(_ptr(qa), _ptr(sa), M, K, _ptr(qw), _ptr(sw), N,
+                                     _ptr(bias), EPILOGUES[epilogue], _ptr(out),
+                                     _stream(stream, dev)), where)
+    return out
+
+
 __all__ = ["dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8", "dq_linear_fp8_noalloc",
            "dq_linear_fp8_segmented", "dq_linear_fp8_segmented_workspace_size",
            "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8", "HEAD_DIM",
            "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
            "quantize_qkv_heads_fp8", "dq_quantize_mx_fp8", "dq_linear_mx_fp8", "MX_BLOCK",
+           "dq_quantize_mxfp4", "dq_linear_mxfp4",
            "dq_linear_fp8_workspace_size", "DQError", "EPILOGUES", "lib", "LIB_PATH"]

@@ -392,7 +392,7 @@ int dq_linear_mx_fp8(const void* qa, const void* sa, int64_t M, int64_t K, const
   const int shape = check_linear_shape(M, K, N);
   if (shape != DQ_OK) return shape;
   if (epilogue != DQ_EPI_BIAS && epilogue != DQ_EPI_GELU_TANH) return DQ_ERR_EPILOGUE;
-  // one 512-thread workgroup per tile: the grid's work-item count must fit in 32 bits
+  // the block-scaled limit on output tiles
   if (((M + 255) / 256) * ((N + 255) / 256) >= (int64_t(1) << 23)) return DQ_ERR_SHAPE;
   if (M == 0) return DQ_OK;
   if (!qa || !sa || !qw || !sw || !out) return DQ_ERR_NULL;
@@ -407,6 +407,49 @@ int dq_linear_mx_fp8(const void* qa, const void* sa, int64_t M, int64_t K, const
       overlap(out, out_bytes, bias, bias ? 2 * n : 0))
     return DQ_ERR_ALIAS;
   return hip_status(dq::launch_linear_mx(
+      static_cast<const uint8_t*>(qa), static_cast<const uint8_t*>(sa), M, K,
+      static_cast<const uint8_t*>(qw), static_cast<const uint8_t*>(sw), N,
+      static_cast<const uint16_t*>(bias), epilogue == DQ_EPI_GELU_TANH ? 1 : 0,
+      static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
+}
+
+int dq_quantize_mxfp4(const void* x, int64_t M, int64_t K, void* q, void* scales, void* stream) {
+  if (M < 0 || M > kMaxDim || K < 32 || K > kMaxDim || (K % 32) != 0) return DQ_ERR_SHAPE;
+  if (M > 0 && K > kMaxElems / M) return DQ_ERR_SHAPE;
+  if (M == 0) return DQ_OK;
+  if (!x || !q || !scales) return DQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q)) return DQ_ERR_ALIGN;
+  const uint64_t n = static_cast<uint64_t>(M) * static_cast<uint64_t>(K);
+  if (overlap(q, n / 2, x, 2 * n) || overlap(scales, n / 32, x, 2 * n) ||
+      overlap(scales, n / 32, q, n / 2))
+    return DQ_ERR_ALIAS;
+  return hip_status(dq::launch_quantize_mxfp4(static_cast<const uint16_t*>(x), M, K,
+                                              static_cast<uint8_t*>(q),
+                                              static_cast<uint8_t*>(scales),
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int dq_linear_mxfp4(const void* qa, const void* sa, int64_t M, int64_t K, const void* qw,
+                    const void* sw, int64_t N, const void* bias, int epilogue, void* out,
+                    void* stream) {
+  const int shape = check_linear_shape(M, K, N);
+  if (shape != DQ_OK) return shape;
+  if ((K % 256) != 0) return DQ_ERR_SHAPE;  // a K step is 128 bytes of codes: 256 values
+  if (epilogue != DQ_EPI_BIAS && epilogue != DQ_EPI_GELU_TANH) return DQ_ERR_EPILOGUE;
+  if (((M + 255) / 256) * ((N + 255) / 256) >= (int64_t(1) << 23)) return DQ_ERR_SHAPE;
+  if (M == 0) return DQ_OK;
+  if (!qa || !sa || !qw || !sw || !out) return DQ_ERR_NULL;
+  if (!aligned16(qa) || !aligned16(qw) || !aligned16(out) || (bias && !aligned16(bias)) ||
+      (reinterpret_cast<uintptr_t>(sa) & 7u) != 0 || (reinterpret_cast<uintptr_t>(sw) & 7u) != 0)
+    return DQ_ERR_ALIGN;
+  const uint64_t m = static_cast<uint64_t>(M), k = static_cast<uint64_t>(K),
+                 n = static_cast<uint64_t>(N);
+  const uint64_t out_bytes = 2 * m * n;
+  if (overlap(out, out_bytes, qa, m * k / 2) || overlap(out, out_bytes, sa, m * k / 32) ||
+      overlap(out, out_bytes, qw, n * k / 2) || overlap(out, out_bytes, sw, n * k / 32) ||
+      overlap(out, out_bytes, bias, bias ? 2 * n : 0))
+    return DQ_ERR_ALIAS;
+  return hip_status(dq::launch_linear_mxfp4(
       static_cast<const uint8_t*>(qa), static_cast<const uint8_t*>(sa), M, K,
       static_cast<const uint8_t*>(qw), static_cast<const uint8_t*>(sw), N,
       static_cast<const uint16_t*>(bias), epilogue == DQ_EPI_GELU_TANH ? 1 : 0,
@@ -440,6 +483,6 @@ const char* dq_status_string(int status) {
 
 int dq_last_hip_error(void) { return g_last_hip_error; }
 
-int dq_abi_version(void) { return 8; }
+int dq_abi_version(void) { return 9; }
 
 }  // extern "C"

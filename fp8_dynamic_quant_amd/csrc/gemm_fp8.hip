@@ -77,15 +77,22 @@ constexpr int kPartFloats = kBM * kBN;
 constexpr int kMaxSeg = (int)kMaxSegments;      // row segments with their own weights
 
 enum { EPI_BIAS = 0, EPI_GELU_TANH = 1, EPI_GATED_RESIDUAL = 2, EPI_QKV = 3,
-       EPI_MX_BIAS = 4, EPI_MX_GELU_TANH = 5 };
+       EPI_MX_BIAS = 4, EPI_MX_GELU_TANH = 5, EPI_MX4_BIAS = 6, EPI_MX4_GELU_TANH = 7 };
 
 // Block-scaled (MX) operands: E4M3 codes with one E8M0 scale byte per 32 values along K. Each
 // K step then also stages the 4 scale bytes (one dword) of every A and B row of the tile, after
 // the codes of the stage: for each group of 32 tile rows (A rows, then B rows) a 256-byte slot
 // whose first 128 bytes hold the 32 rows' dwords (a copy instruction moves 64 lanes' dwords and
 // its upper 32 lanes fill the rest with zeros, so no lane needs to be switched off).
+// With FP4 (E2M1) elements (EPI_MX4_*) the operands are two codes per byte, so a step of 128 bytes
+// per row is 256 values along K and its 8 scale bytes are two dwords per row: lanes 0-31 of the
+// copy move the first dword of 32 rows, lanes 32-63 the second, filling the whole slot.
 constexpr int kScaleBytes = 4096;
 __host__ __device__ constexpr bool is_mx(int epi) { return epi >= EPI_MX_BIAS; }
+// 0: per-row scales; 1: MX with E4M3 elements; 2: MX with E2M1 elements
+__host__ __device__ constexpr int mx_kind(int epi) {
+  return epi >= EPI_MX4_BIAS ? 2 : epi >= EPI_MX_BIAS ? 1 : 0;
+}
 __host__ __device__ constexpr int stage_bytes(int epi) {
   return kStageBytes + (is_mx(epi) ? kScaleBytes : 0);
 }
@@ -339,7 +346,7 @@ struct TileDesc {
 
 // Descriptors of a tile or of one half of it: rows past the segment end (columns past N) are out
 // of range and read as zero (a half entirely past N has an empty B range).
-template <int NB, bool MX>
+template <int NB, int MX>
 __device__ __forceinline__ TileDesc tile_desc(const Params& p, int t, int half) {
   TileDesc d;
   d.g = item_geo<NB>(p, t, half);
@@ -352,7 +359,8 @@ __device__ __forceinline__ TileDesc tile_desc(const Params& p, int t, int half) 
   d.rsB = buffer_rsrc(seg_args()->B[d.g.s] + (size_t)(rb > 0 ? n0 : 0) * (size_t)p.K,
                       rowsB * (uint32_t)p.K);
   if (MX) {
-    const uint32_t kb = (uint32_t)p.K / 32u;
+    // scale bytes per row: K / 32 values; p.K counts bytes, two values each with FP4
+    const uint32_t kb = (uint32_t)p.K / (MX == 2 ? 16u : 32u);
     d.rsSA = buffer_rsrc(p.mxa + (size_t)m0 * kb, rowsA * kb);
     d.rsSB = buffer_rsrc(p.mxw + (size_t)(rb > 0 ? n0 : 0) * kb, rowsB * kb);
   }
@@ -388,7 +396,7 @@ struct Batch {
   uint32_t soff, slds;
 };
 
-template <int NB, bool MX>
+template <int NB, int MX>
 __device__ __forceinline__ Batch batch_of(const TileDesc& d, uint32_t K, int k, uint8_t* st,
                                           uint32_t vlane, int q, int which, bool live) {
   Batch b;
@@ -418,14 +426,21 @@ __device__ __forceinline__ Batch batch_of(const TileDesc& d, uint32_t K, int k, 
   b.off0 = (uint32_t)grow * K + vlane + (uint32_t)k * kBK;
   if (MX) {
     // lane i < n fetches the dword of tile row grow + i, the other lanes read past the range;
-    // n = 32 rows per slot, or 16 for the B rows of a narrow half (16 per batch there)
+    // n = 32 rows per slot, or 16 for the B rows of a narrow half (16 per batch there). With
+    // FP4 elements lane 32 + i fetches the same row's second dword of the step.
     const bool n16 = NB == 1 && which >= 2;
     b.rsS = which < 2 ? d.rsSA : d.rsSB;
     if (!live) b.rsS[2] = 0;
-    const uint32_t kb = K / 32u;
     const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    b.soff = lane < (n16 ? 16u : 32u) ? ((uint32_t)grow + lane) * kb + (uint32_t)k * 4u
-                                      : 0xFFFFFFF0u;
+    const uint32_t n = n16 ? 16u : 32u;
+    if (MX == 2) {
+      const uint32_t kb = K / 16u, r = lane & 31u;
+      b.soff = r < n ? ((uint32_t)grow + r) * kb + (uint32_t)k * 8u + (lane >> 5) * 4u
+                     : 0xFFFFFFF0u;
+    } else {
+      const uint32_t kb = K / 32u;
+      b.soff = lane < n ? ((uint32_t)grow + lane) * kb + (uint32_t)k * 4u : 0xFFFFFFF0u;
+    }
     b.slds = base + (uint32_t)kStageBytes + (which < 2 ? 0u : 2048u) +
              (uint32_t)(n16 ? grow >> 4 : grow >> 5) * 256u;
   }
@@ -443,7 +458,7 @@ __device__ __forceinline__ void copy_block(const Batch& b, uint32_t K, uint32_t 
                                              (uint32_t)((j & 1) * 1024)));
 }
 
-template <int NB, bool MX>
+template <int NB, int MX>
 __device__ __forceinline__ void copy_batch(const TileDesc& d, uint32_t K, int k, uint8_t* st,
                                            uint32_t vlane, uint32_t dodd, int q, int which) {
   const Batch b = batch_of<NB, MX>(d, K, k, st, vlane, q, which, true);
@@ -494,6 +509,7 @@ struct Frags {
   v8i a[4];  // rows wm * 128 + 32 i + (lane & 31) of the A tile
   v8i b[2];  // B rows: full tile wn * 64 + 32 i + (lane & 31); narrow tile only b[0]
   uint32_t sa[4], sb[2];  // MX only: those rows' scale dwords, shifted right by 8 (lane >> 5)
+                          // (with FP4 elements: the dword of the K half read)
 };
 
 // Fragments of K half h (64 bytes) of one staged step: lane l reads row l & 31 of each 32-row
@@ -503,8 +519,11 @@ struct Frags {
 // In MX mode the scaled instruction takes a row's 64 codes as two blocks of 32, registers 0-3 of
 // lanes l and l + 32 holding the first block and registers 4-7 the second: lane l reads chunks
 // 4 h + (l >> 5) and 4 h + 2 + (l >> 5) (16 codes each), and with K half 0 the rows' scale
-// dwords, of which the instruction selects byte 2 h.
-template <int NB, bool MX>
+// dwords, of which the instruction selects byte 2 h. With FP4 elements the same two chunks are
+// the operands of two instructions (64 values each: registers 0-3 of lanes l and l + 32 the
+// first, registers 4-7 the second), and each K half reads the rows' dword of its 4 blocks, of
+// which the two instructions select bytes 0 and 2.
+template <int NB, int MX>
 __device__ __forceinline__ void read_frags(const uint8_t* st, Frags& f, int h, int wm, int wn,
                                            int lane) {
   const int r = lane & 31;
@@ -528,17 +547,18 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, Frags& f, int h, i
     f.b[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
-  if (MX && h == 0) {  // 256-byte slots (A rows from 0, B rows from 2048)
+  if (MX && (MX == 2 || h == 0)) {  // 256-byte slots (A rows from 0, B rows from 2048)
     const uint32_t* sc = reinterpret_cast<const uint32_t*>(st + kStageBytes);
     const int sh = 8 * (lane >> 5);
+    const int hd = MX == 2 ? 32 * h : 0;  // FP4: the K half's dword sits 32 dwords further
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.sa[i] = sc[64 * (wm * 4 + i) + r] >> sh;
+    for (int i = 0; i < 4; ++i) f.sa[i] = sc[64 * (wm * 4 + i) + hd + r] >> sh;
     if (NB == 2) {  // a slot per 32 rows
 #pragma unroll
-      for (int i = 0; i < NB; ++i) f.sb[i] = sc[512 + 64 * ((b0 >> 5) + i) + r] >> sh;
+      for (int i = 0; i < NB; ++i) f.sb[i] = sc[512 + 64 * ((b0 >> 5) + i) + hd + r] >> sh;
     } else {        // narrow half: the wave's B rows are tile rows 32 wn + [0, 32), 16 per slot
       const int tr = 32 * wn + r;
-      f.sb[0] = sc[512 + 64 * (tr >> 4) + (tr & 15)] >> sh;
+      f.sb[0] = sc[512 + 64 * (tr >> 4) + hd + (tr & 15)] >> sh;
     }
   }
 }
@@ -546,14 +566,21 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, Frags& f, int h, i
 // The MFMAs of one K half (8, or 4 in a narrow tile), with the four copies of batch b issued one
 // after each of the first four: a copy instruction waits for the vector memory unit to take it, which here
 // overlaps the matrix unit's work instead of holding up the next phase.
-template <int NB, bool MX, int H>
+template <int NB, int MX, int H>
 __device__ __forceinline__ void mma8_copy(const Frags& f, v16f (&acc)[NB][4], const Batch& b,
                                           uint32_t K, uint32_t dodd) {
 #pragma unroll
   for (int bn = 0; bn < NB; ++bn)
 #pragma unroll
     for (int bm = 0; bm < 4; ++bm) {
-      if (MX)
+      if (MX == 2) {  // E2M1 operands, format 4: registers 0-3, then 4-7
+        const v8i b1 = __builtin_shufflevector(f.b[bn], f.b[bn], 4, 5, 6, 7, 0, 1, 2, 3);
+        const v8i a1 = __builtin_shufflevector(f.a[bm], f.a[bm], 4, 5, 6, 7, 0, 1, 2, 3);
+        acc[bn][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            f.b[bn], f.a[bm], acc[bn][bm], 4, 4, 0, (int)f.sb[bn], 0, (int)f.sa[bm]);
+        acc[bn][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            b1, a1, acc[bn][bm], 4, 4, 2, (int)f.sb[bn], 2, (int)f.sa[bm]);
+      } else if (MX)
         acc[bn][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             f.b[bn], f.a[bm], acc[bn][bm], 0, 0, 2 * H, (int)f.sb[bn], 2 * H, (int)f.sa[bm]);
       else
@@ -641,7 +668,7 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[NB][4], const Params&
         const int nl = wn * 32 * NB + bn * 32 + (gp * 2 + hi) * 8;
         const int n = n0 + nl;
         float y[8] = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
-        if (EPI == EPI_GELU_TANH || EPI == EPI_MX_GELU_TANH) {
+        if (EPI == EPI_GELU_TANH || EPI == EPI_MX_GELU_TANH || EPI == EPI_MX4_GELU_TANH) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) y[j] = gelu_tanh(y[j]);
         }
@@ -938,7 +965,7 @@ __device__ __forceinline__ bool same_tile(const Cursor& a, const Cursor& b) {
 // NB = 2: whole tiles and cut parts; NB = 1: the narrow halves of left-over tiles.
 template <int EPI, int NB>
 __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
-  constexpr bool MX = is_mx(EPI);
+  constexpr int MX = mx_kind(EPI);
   constexpr int kStage = stage_bytes(EPI);
   constexpr int kOps = batch_ops(EPI);
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStage + kParamBufs * kParamBytes];
@@ -1224,6 +1251,8 @@ static hipError_t schedule_and_launch(Params& p, int64_t M, int64_t K, int64_t N
     case EPI_QKV: return launch_epi<EPI_QKV>(p, g, ng, stream);
     case EPI_MX_BIAS: return launch_epi<EPI_MX_BIAS>(p, g, ng, stream);
     case EPI_MX_GELU_TANH: return launch_epi<EPI_MX_GELU_TANH>(p, g, ng, stream);
+    case EPI_MX4_BIAS: return launch_epi<EPI_MX4_BIAS>(p, g, ng, stream);
+    case EPI_MX4_GELU_TANH: return launch_epi<EPI_MX4_GELU_TANH>(p, g, ng, stream);
     default: return launch_epi<EPI_GATED_RESIDUAL>(p, g, ng, stream);
   }
 }
@@ -1304,6 +1333,24 @@ hipError_t launch_linear_mx(const uint8_t* qa, const uint8_t* sa, int64_t M, int
   p.seg.bias[0] = bias;
   return schedule_and_launch(p, M, K, N, epilogue == 1 ? EPI_MX_GELU_TANH : EPI_MX_BIAS, nullptr,
                              0, stream);
+}
+
+// MXFP4 linear: the same kernel in MX mode with E2M1 operands. p.K counts bytes (K / 2), so a
+// K step of 128 bytes per row covers 256 values and 8 scale bytes.
+hipError_t launch_linear_mxfp4(const uint8_t* qa, const uint8_t* sa, int64_t M, int64_t K,
+                               const uint8_t* qw, const uint8_t* sw, int64_t N,
+                               const uint16_t* bias, int epilogue, uint16_t* out,
+                               hipStream_t stream) {
+  Params p{};
+  if (set_segments(p, 1, &M) == 0) return hipSuccess;
+  p.A = qa;
+  p.out = out;
+  p.mxa = sa;
+  p.mxw = sw;
+  p.seg.B[0] = qw;
+  p.seg.bias[0] = bias;
+  return schedule_and_launch(p, M, K / 2, N, epilogue == 1 ? EPI_MX4_GELU_TANH : EPI_MX4_BIAS,
+                             nullptr, 0, stream);
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -1,4 +1,4 @@
-// Block-scaled (MX) FP8 linear layer for gfx950: activations and weights in E4M3 with one
+// Block-scaled (MX) quantizers for gfx950: activations and weights in E4M3 (or E2M1) with one
 // power-of-two scale (an E8M0 byte) per 32 values along K, multiplied by gfx950's scaled matrix
 // instruction, which applies each operand's block scale itself.
 //
@@ -102,7 +102,71 @@ __global__ void __launch_bounds__(256) quant_mx_rows(const uint16_t* __restrict_
   }
 }
 
+// MXFP4: the same blocks with E2M1 elements. Shared exponent floor(log2(amax)) - 2, so the scale
+// byte is max(field - 2, 0); x / 2^shared is again a product by a power of two (values it pushes
+// below fp32's range are under a quarter, E2M1's rounding point to zero, and keep their sign).
+// The hardware's packed FP4 conversion rounds to the nearest E2M1 value with ties to even,
+// saturates at 6 and keeps the sign of zero: it is used with scale 1 on the scaled values (it
+// agrees bit for bit with that definition on every bf16 value, measured). Two codes per byte,
+// element 2j in the low nibble of byte j: a thread's 8 values give one dword of codes.
+template <int J>
+__device__ __forceinline__ uint32_t cvt_fp4_pair(uint32_t r, uint32_t w, float y) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __uint_as_float(w << 16) * y,
+                                                  __uint_as_float(w & 0xFFFF0000u) * y, 1.0f, J);
+}
+
+__global__ void __launch_bounds__(256) quant_mx4_rows(const uint16_t* __restrict__ x, int64_t n8,
+                                                      uint32_t* __restrict__ q,
+                                                      uint8_t* __restrict__ scale) {
+  for (int64_t grp = blockIdx.x; grp * (256 * kQuantUnroll) < n8; grp += gridDim.x) {
+    const int64_t base = grp * (256 * kQuantUnroll) + threadIdx.x;
+    uint4 v[kQuantUnroll];
+#pragma unroll
+    for (int i = 0; i < kQuantUnroll; ++i) {
+      const int64_t t = base + 256 * i;  // n8 is a multiple of 4: a quad is live or not as a whole
+      if (t < n8) {
+        const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x) + t);
+        v[i] = make_uint4(r[0], r[1], r[2], r[3]);
+      } else {
+        v[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kQuantUnroll; ++i) {
+      const int64_t t = base + 256 * i;
+      uint32_t mx = absmax_pair(absmax_pair(absmax_pair(absmax_pair(0u, v[i].x), v[i].y), v[i].z),
+                                v[i].w);
+      uint32_t m = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
+      uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false);
+      m = m > o ? m : o;
+      o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false);
+      m = m > o ? m : o;
+      if (t >= n8) continue;
+      const uint32_t field = (m >> 7) & 0xFFu;            // bf16 exponent field of the block amax
+      const uint32_t byte = field > 2u ? field - 2u : 0u;  // shared + 127
+      const float y = __uint_as_float((254u - byte) << 23);  // 2^-shared (byte <= 252 for bf16)
+      uint32_t r = cvt_fp4_pair<0>(0u, v[i].x, y);
+      r = cvt_fp4_pair<1>(r, v[i].y, y);
+      r = cvt_fp4_pair<2>(r, v[i].z, y);
+      r = cvt_fp4_pair<3>(r, v[i].w, y);
+      q[t] = r;
+      if ((threadIdx.x & 3) == 0) scale[t >> 2] = (uint8_t)byte;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_mxfp4(const uint16_t* x, int64_t R, int64_t K, uint8_t* q,
+                                 uint8_t* scale, hipStream_t stream) {
+  const int64_t n8 = R * K / 8;
+  if (n8 == 0) return hipSuccess;
+  const int64_t per_wg = 256 * kQuantUnroll;
+  const int64_t groups = (n8 + per_wg - 1) / per_wg;
+  hipLaunchKernelGGL(quant_mx4_rows, dim3((unsigned)(groups < kMaxGroups ? groups : kMaxGroups)),
+                     dim3(256), 0, stream, x, n8, reinterpret_cast<uint32_t*>(q), scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_mx(const uint16_t* x, int64_t R, int64_t K, uint8_t* q, uint8_t* scale,
                               hipStream_t stream) {

@@ -323,12 +323,54 @@ int dq_quantize_mx_fp8(const void* x, int64_t M, int64_t K, void* q, void* scale
  *   bias     bf16 [N] or NULL;  epilogue DQ_EPI_BIAS or DQ_EPI_GELU_TANH
  *   out      bf16 [M, N]
  * Requirements: as dq_linear_fp8 (128 <= K < 2^24, K % 128 == 0, N % 64 == 0); codes, bias and
- * out 16-byte aligned, scale arrays 4-byte aligned; out overlapping no input. One workgroup per
- * 256 x 256 output tile, so fewer than 2^23 tiles (DQ_ERR_SHAPE otherwise).
+ * out 16-byte aligned, scale arrays 4-byte aligned; out overlapping no input; fewer than 2^23
+ * output tiles of 256 x 256 (DQ_ERR_SHAPE otherwise).
  */
 int dq_linear_mx_fp8(const void* qa, const void* sa, int64_t M, int64_t K, const void* qw,
                      const void* sw, int64_t N, const void* bias, int epilogue, void* out,
                      void* stream);
+
+/*
+ * dq_quantize_mxfp4 -- block-scaled FP4 (MXFP4) quantization: every 32 consecutive values of a
+ * row share one power-of-two scale, each value is a 4-bit E2M1 code.
+ *
+ * The pages run FLUX 3 Image Klein's linears with 4-bit weights and activations and a shared
+ * scale per small block (NVFP4, page "Accelerarea generarii de imagini cu FLUX 3 Image Klein pe
+ * GPU-urile Blackwell NVIDIA", its paragraph on NVFP4 against BF16; page "Optimizacion de la
+ * inferencia de FLUX 3 Image Klein en GPUs NVIDIA Blackwell", section "Como funciona"). The
+ * 4-bit block format gfx950's matrix units execute is OCP MX with E2M1 elements (magnitudes
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes 0..7, sign in bit 3); its definition is the one taken:
+ *   shared exponent e = floor(log2(max |x| of the block)) - 2, clamped to [-127, 127]
+ *                       (-127 for an all-zero block);
+ *   q = E2M1 nearest to x / 2^e (ties to the even code), magnitudes past 6 saturating to 6,
+ *       the sign kept (also when the value rounds to zero);
+ *   scale byte = e + 127 (E8M0).
+ *
+ *   x       bf16 [M, K]       row-major; 32 <= K < 2^31, K % 32 == 0, M K < 2^47
+ *   q       uint8 [M, K / 2]  two codes per byte: element 2j in the low nibble of byte j
+ *   scales  uint8 [M, K / 32] scale bytes, row-major
+ * x and q 16-byte aligned; no overlap. Inputs must be finite.
+ */
+int dq_quantize_mxfp4(const void* x, int64_t M, int64_t K, void* q, void* scales, void* stream);
+
+/*
+ * dq_linear_mxfp4 -- the MXFP4 linear layer on gfx950's scaled matrix instruction with 4-bit
+ * operands (twice the rate of its FP8 form):
+ *
+ *   y[m, n] = sum over blocks b of 2^(ea[m, b] + ew[n, b]) sum_{k in b} dec(qa[m, k]) dec(qw[n, k])
+ *   out[m, n] = bf16(epilogue(y[m, n] + bias[n]))      accumulation in fp32, one rounding
+ *
+ *   qa, sa   codes [M, K / 2] and scale bytes [M, K / 32] of the activations (dq_quantize_mxfp4)
+ *   qw, sw   codes [N, K / 2] and scale bytes [N, K / 32] of the weights (the same routine)
+ *   bias     bf16 [N] or NULL;  epilogue DQ_EPI_BIAS or DQ_EPI_GELU_TANH
+ *   out      bf16 [M, N]
+ * Requirements: 256 <= K < 2^24, K % 256 == 0, N % 64 == 0, fewer than 2^23 output tiles of
+ * 256 x 256 (DQ_ERR_SHAPE otherwise); codes, bias and out 16-byte aligned, scale arrays 8-byte
+ * aligned; out overlapping no input.
+ */
+int dq_linear_mxfp4(const void* qa, const void* sa, int64_t M, int64_t K, const void* qw,
+                    const void* sw, int64_t N, const void* bias, int epilogue, void* out,
+                    void* stream);
 
 /*
  * dq_attention_fp8_workspace_size -- bytes of workspace dq_attention_fp8 may use for H heads of
@@ -386,7 +428,7 @@ const char* dq_status_string(int status);
 /* The hipError_t behind the most recent DQ_ERR_HIP returned on the calling thread (0 if none). */
 int dq_last_hip_error(void);
 
-/* ABI version of this header (currently 7). */
+/* ABI version of this header (currently 9). */
 int dq_abi_version(void);
 
 #ifdef __cplusplus

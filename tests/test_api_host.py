@@ -42,6 +42,8 @@ def lib():
     L.dq_attention_fp8_workspace_size.restype = ctypes.c_uint64
     L.dq_quantize_mx_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
     L.dq_linear_mx_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp]
+    L.dq_quantize_mxfp4.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.dq_linear_mxfp4.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp]
     L.dq_linear_fp8_workspace_size.argtypes = [i64, i64, i64]
     L.dq_linear_fp8_workspace_size.restype = ctypes.c_uint64
     L.dq_status_string.restype = ctypes.c_char_p
@@ -59,7 +61,7 @@ def test_header_declares_the_entry_points():
     for n in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
               "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8",
               "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
-              "dq_quantize_mx_fp8", "dq_linear_mx_fp8",
+              "dq_quantize_mx_fp8", "dq_linear_mx_fp8", "dq_quantize_mxfp4", "dq_linear_mxfp4",
               "dq_linear_fp8_workspace_size", "dq_status_string", "dq_last_hip_error",
               "dq_abi_version"):
         assert n in names
@@ -71,7 +73,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dq_abi_version() == 8
+    assert lib.dq_abi_version() == 9
     for st in range(9):
         s = lib.dq_status_string(st)
         assert s and len(s) > 1
@@ -336,6 +338,46 @@ def test_linear_mx_argument_checks(lib):
     assert lib.dq_last_hip_error() == 0
 
 
+def test_quantize_mxfp4_argument_checks(lib):
+    f = lib.dq_quantize_mxfp4
+    assert f(MX_X, 0, 64, MX_Q, MX_S, None) == OK                # empty
+    assert f(MX_X, 4, 48, MX_Q, MX_S, None) == SHAPE             # K % 32
+    assert f(MX_X, 4, 16, MX_Q, MX_S, None) == SHAPE             # K < 32
+    assert f(MX_X, -1, 64, MX_Q, MX_S, None) == SHAPE
+    assert f(None, 4, 64, MX_Q, MX_S, None) == NULL
+    assert f(MX_X, 4, 64, None, MX_S, None) == NULL
+    assert f(MX_X, 4, 64, MX_Q, None, None) == NULL
+    assert f(MX_X + 8, 4, 64, MX_Q, MX_S, None) == ALIGN
+    assert f(MX_X, 4, 64, MX_Q + 8, MX_S, None) == ALIGN
+    assert f(MX_X, 4, 64, MX_X + 256, MX_S, None) == ALIAS       # codes inside x
+    assert f(MX_X, 4, 64, MX_Q, MX_Q + 127, None) == ALIAS       # 4 rows x 32 code bytes
+
+
+def mx4lin(lib, M=64, K=256, N=128, qa=MX_Q, sa=MX_S, qw=MX_W, sw=MX_SW, bias=None, epi=0,
+           out=MX_O):
+    return lib.dq_linear_mxfp4(qa, sa, M, K, qw, sw, N, bias, epi, out, None)
+
+
+def test_linear_mxfp4_argument_checks(lib):
+    assert mx4lin(lib, M=0) == OK
+    assert mx4lin(lib, K=128) == SHAPE                           # K % 256
+    assert mx4lin(lib, K=384) == SHAPE
+    assert mx4lin(lib, K=1 << 24) == SHAPE
+    assert mx4lin(lib, N=96) == SHAPE                            # N % 64
+    assert mx4lin(lib, M=-1) == SHAPE
+    assert mx4lin(lib, M=1 << 20, K=256, N=1 << 19) == SHAPE      # 4096 x 2048 tiles
+    assert mx4lin(lib, epi=2) == EPI                             # gated residual: not offered
+    for name in ("qa", "sa", "qw", "sw", "out"):
+        assert mx4lin(lib, **{name: None}) == NULL, name
+    assert mx4lin(lib, qa=MX_Q + 8) == ALIGN
+    assert mx4lin(lib, sa=MX_S + 4) == ALIGN                     # scale pairs: 8-byte aligned
+    assert mx4lin(lib, sw=MX_SW + 4) == ALIGN
+    assert mx4lin(lib, out=MX_O + 8) == ALIGN
+    assert mx4lin(lib, out=MX_Q) == ALIAS                        # output over the codes
+    assert mx4lin(lib, out=MX_SW - 64) == ALIAS                  # output into the weight scales
+
+
+
 def test_quantize_v_argument_checks(lib):
     f = lib.dq_quantize_v_fp8
     V, VT, SV = 0x30000000, 0x40000000, 0x50000000
@@ -473,9 +515,10 @@ def test_python_binding_names_match_the_c_entry_points():
                  "dq_linear_fp8_noalloc", "dq_linear_fp8_segmented",
                  "dq_linear_fp8_segmented_workspace_size", "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8",
                  "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
-                 "dq_quantize_mx_fp8", "dq_linear_mx_fp8", "dq_linear_fp8_workspace_size"):
+                 "dq_quantize_mx_fp8", "dq_linear_mx_fp8", "dq_quantize_mxfp4", "dq_linear_mxfp4",
+                 "dq_linear_fp8_workspace_size"):
         assert callable(getattr(dq, name))
-    assert dq.lib().dq_abi_version() == 8
+    assert dq.lib().dq_abi_version() == 9
     assert dq.dq_linear_fp8_workspace_size(512, 12288, 3072) == 4096 + 96 * 262144
 
 
