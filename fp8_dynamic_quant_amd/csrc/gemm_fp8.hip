@@ -563,33 +563,46 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, Frags& f, int h, i
   }
 }
 
-// The MFMAs of one K half (8, or 4 in a narrow tile), with the four copies of batch b issued one
-// after each of the first four: a copy instruction waits for the vector memory unit to take it, which here
-// overlaps the matrix unit's work instead of holding up the next phase.
-template <int NB, int MX, int H>
-__device__ __forceinline__ void mma8_copy(const Frags& f, v16f (&acc)[NB][4], const Batch& b,
-                                          uint32_t K, uint32_t dodd) {
+// One pass of the MFMAs of a K half over the wave's blocks; with E2M1 operands pass P (0 or 1)
+// takes fragment registers 4P .. 4P + 3 and scale byte 2P. The first pass issues the batch's
+// copies: one after each of its first four MFMAs (a copy instruction waits for the vector memory
+// unit to take it, which here overlaps the matrix unit's work instead of holding up the next
+// phase), and the scale copy after the fifth.
+template <int NB, int MX, int H, int P>
+__device__ __forceinline__ void mma_pass(const Frags& f, v16f (&acc)[NB][4], const Batch& b,
+                                         uint32_t K, uint32_t dodd) {
 #pragma unroll
   for (int bn = 0; bn < NB; ++bn)
 #pragma unroll
     for (int bm = 0; bm < 4; ++bm) {
-      if (MX == 2) {  // E2M1 operands, format 4: registers 0-3, then 4-7
-        const v8i b1 = __builtin_shufflevector(f.b[bn], f.b[bn], 4, 5, 6, 7, 0, 1, 2, 3);
-        const v8i a1 = __builtin_shufflevector(f.a[bm], f.a[bm], 4, 5, 6, 7, 0, 1, 2, 3);
+      if (MX == 2) {
+        const v8i bv = P == 0 ? f.b[bn]
+                              : __builtin_shufflevector(f.b[bn], f.b[bn], 4, 5, 6, 7, 0, 1, 2, 3);
+        const v8i av = P == 0 ? f.a[bm]
+                              : __builtin_shufflevector(f.a[bm], f.a[bm], 4, 5, 6, 7, 0, 1, 2, 3);
         acc[bn][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            f.b[bn], f.a[bm], acc[bn][bm], 4, 4, 0, (int)f.sb[bn], 0, (int)f.sa[bm]);
-        acc[bn][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            b1, a1, acc[bn][bm], 4, 4, 2, (int)f.sb[bn], 2, (int)f.sa[bm]);
-      } else if (MX)
+            bv, av, acc[bn][bm], 4, 4, 2 * P, (int)f.sb[bn], 2 * P, (int)f.sa[bm]);
+      } else if (MX) {
         acc[bn][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             f.b[bn], f.a[bm], acc[bn][bm], 0, 0, 2 * H, (int)f.sb[bn], 2 * H, (int)f.sa[bm]);
-      else
+      } else {
         acc[bn][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             f.b[bn], f.a[bm], acc[bn][bm], 0, 0, 0, 0, 0, 0);
-      if (bn == 0) copy_block(b, K, dodd, bm);
-      if (MX && bn == NB - 1 && bm == 0) copy_scales(b);
+      }
+      if (P == 0 && bn == 0) copy_block(b, K, dodd, bm);
+      if (MX && P == 0 && bn == NB - 1 && bm == 0) copy_scales(b);
       __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+// The MFMAs of one K half (8, or 4 in a narrow tile; twice as many with E2M1 operands, all
+// blocks' first instructions before the second ones, so that none waits for the accumulator of
+// the one before) with the copies of batch b.
+template <int NB, int MX, int H>
+__device__ __forceinline__ void mma8_copy(const Frags& f, v16f (&acc)[NB][4], const Batch& b,
+                                          uint32_t K, uint32_t dodd) {
+  mma_pass<NB, MX, H, 0>(f, acc, b, K, dodd);
+  if constexpr (MX == 2) mma_pass<NB, MX, H, 1>(f, acc, b, K, dodd);
 }
 
 // ---------------------------------------------------------------------------------------------
