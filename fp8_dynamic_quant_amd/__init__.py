@@ -86,8 +86,11 @@ def lib() -> ctypes.CDLL:
         L.dq_linear_mx_fp8.restype = i32
         L.dq_quantize_mxfp4.argtypes = [vp, i64, i64, vp, vp, vp]
         L.dq_quantize_mxfp4.restype = i32
-        L.dq_linear_mxfp4.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp]
+        L.dq_linear_mxfp4.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp]
         L.dq_linear_mxfp4.restype = i32
+        L.dq_linear_mxfp4_segmented.argtypes = [vp, vp, i64, i64, vp, vp, vp, i64, vp, i32, vp,
+                                                vp, vp, vp]
+        L.dq_linear_mxfp4_segmented.restype = i32
         L.dq_linear_fp8_workspace_size.argtypes = [i64, i64, i64]
         L.dq_linear_fp8_workspace_size.restype = ctypes.c_uint64
         L.dq_status_string.argtypes = [i32]
@@ -536,13 +539,13 @@ def dq_quantize_mxfp4(x, q=None, scales=None, stream=None):
     return q, scales
 
 
-def dq_linear_mxfp4(qa, sa, qw, sw, bias=None, epilogue="bias", out=None, stream=None):
-    """MXFP4 linear layer -> bf16 [M, N]: packed codes qa [M, K / 2], qw [N, K / 2] and their
-    scale bytes sa [M, K / 32], sw [N, K / 32] (dq_quantize_mxfp4); epilogue "bias" or
-    "gelu_tanh"."""
-    where = "dq_linear_mxfp4"
+def _mxfp4_args(qa, sa, qw, sw, bias, epilogue, gate, residual, out, where):
+    """Checks of one MXFP4 weight's tensors against the shared ones; allocates out when None.
+    Returns (device, M, K, N, out)."""
     if not isinstance(qa, torch.Tensor) or qa.dim() != 2 or not isinstance(qw, torch.Tensor):
         raise ValueError(f"{where}: qa and qw must be 2-D tensors")
+    if epilogue not in EPILOGUES:
+        raise ValueError(f"{where}: unknown epilogue {epilogue!r}")
     M, K = qa.shape[0], 2 * qa.shape[1]
     N = qw.shape[0]
     dev = qa.device
@@ -552,14 +555,61 @@ def dq_linear_mxfp4(qa, sa, qw, sw, bias=None, epilogue="bias", out=None, stream
     _need(sw, "sw", torch.uint8, (N, K // MX_BLOCK), dev)
     if bias is not None:
         _need(bias, "bias", torch.bfloat16, (N,), dev)
-    if epilogue not in ("bias", "gelu_tanh"):
-        raise ValueError(f"{where}: epilogue must be 'bias' or 'gelu_tanh'")
+    if epilogue == "gated_residual":
+        if gate is None or residual is None:
+            raise ValueError(f"{where}: gated_residual needs gate and residual")
+        _need(gate, "gate", torch.bfloat16, (N,), dev)
+        _need(residual, "residual", torch.bfloat16, (M, N), dev)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
     _need(out, "out", torch.bfloat16, (M, N), dev)
+    return dev, M, K, N, out
+
+
+def dq_linear_mxfp4(qa, sa, qw, sw, bias=None, epilogue="bias", gate=None, residual=None,
+                    out=None, stream=None):
+    """MXFP4 linear layer -> bf16 [M, N]: packed codes qa [M, K / 2], qw [N, K / 2] and their
+    scale bytes sa [M, K / 32], sw [N, K / 32] (dq_quantize_mxfp4); epilogue "bias",
+    "gelu_tanh" or "gated_residual" (gate [N], residual [M, N]; out may be the residual)."""
+    where = "dq_linear_mxfp4"
+    dev, M, K, N, out = _mxfp4_args(qa, sa, qw, sw, bias, epilogue, gate, residual, out, where)
+    gated = epilogue == "gated_residual"
     with torch.cuda.device(dev):
         _check(lib().dq_linear_mxfp4(_ptr(qa), _ptr(sa), M, K, _ptr(qw), _ptr(sw), N,
-                                     _ptr(bias), EPILOGUES[epilogue], _ptr(out),
+                                     _ptr(bias), EPILOGUES[epilogue],
+                                     _ptr(gate) if gated else None,
+                                     _ptr(residual) if gated else None, _ptr(out),
                                      _stream(stream, dev)), where)
+    return out
+
+
+def dq_linear_mxfp4_segmented(qa, sa, seg_rows, qws, sws, biases, epilogue="bias", gates=None,
+                              residual=None, out=None, stream=None):
+    """The MXFP4 linear over row segments with one weight each, in one launch -> bf16 [M, N].
+    qa [M, K / 2] and sa [M, K / 32] for the whole sequence; seg_rows sums to M; qws / sws /
+    biases (/ gates for "gated_residual"): one tensor per segment (a bias may be None)."""
+    where = "dq_linear_mxfp4_segmented"
+    nseg = len(seg_rows)
+    if not (1 <= nseg <= 4) or len(qws) != nseg or len(sws) != nseg or len(biases) != nseg:
+        raise ValueError(f"{where}: 1 to 4 segments, one weight, scale and bias each")
+    gated = epilogue == "gated_residual"
+    if gated and (gates is None or len(gates) != nseg):
+        raise ValueError(f"{where}: gated_residual needs one gate per segment")
+    M = sum(int(r) for r in seg_rows)
+    if not isinstance(qa, torch.Tensor) or qa.dim() != 2 or qa.shape[0] != M:
+        raise ValueError(f"{where}: qa must be [sum(seg_rows), K / 2]")
+    for i in range(nseg):
+        dev, _, K, N, out = _mxfp4_args(qa, sa, qws[i], sws[i], biases[i], epilogue,
+                                        gates[i] if gated else None, residual, out, where)
+    VP = ctypes.c_void_p * nseg
+    rows = (ctypes.c_int64 * nseg)(*[int(r) for r in seg_rows])
+    ptrs = [VP(*[t.data_ptr() if t is not None else None for t in ts])
+            for ts in (qws, sws, biases)]
+    gp = VP(*[t.data_ptr() for t in gates]) if gated else None
+    with torch.cuda.device(dev):
+        _check(lib().dq_linear_mxfp4_segmented(_ptr(qa), _ptr(sa), K, nseg, rows, ptrs[0],
+                                               ptrs[1], N, ptrs[2], EPILOGUES[epilogue], gp,
+                                               _ptr(residual) if gated else None, _ptr(out),
+                                               _stream(stream, dev)), where)
     return out
 
 
@@ -568,5 +618,5 @@ __all__ = ["dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8", "dq_lin
            "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8", "HEAD_DIM",
            "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
            "quantize_qkv_heads_fp8", "dq_quantize_mx_fp8", "dq_linear_mx_fp8", "MX_BLOCK",
-           "dq_quantize_mxfp4", "dq_linear_mxfp4",
+           "dq_quantize_mxfp4", "dq_linear_mxfp4", "dq_linear_mxfp4_segmented",
            "dq_linear_fp8_workspace_size", "DQError", "EPILOGUES", "lib", "LIB_PATH"]

@@ -429,17 +429,24 @@ int dq_quantize_mxfp4(const void* x, int64_t M, int64_t K, void* q, void* scales
                                               static_cast<hipStream_t>(stream)));
 }
 
-int dq_linear_mxfp4(const void* qa, const void* sa, int64_t M, int64_t K, const void* qw,
-                    const void* sw, int64_t N, const void* bias, int epilogue, void* out,
-                    void* stream) {
+// The checks of one MXFP4 segment (its weight, scales, bias and gate) with the shared
+// row-indexed tensors, over all M rows.
+static int check_mxfp4_args(const void* qa, const void* sa, int64_t M, int64_t K, const void* qw,
+                            const void* sw, int64_t N, const void* bias, int epilogue,
+                            const void* gate, const void* residual, const void* out) {
   const int shape = check_linear_shape(M, K, N);
   if (shape != DQ_OK) return shape;
   if ((K % 256) != 0) return DQ_ERR_SHAPE;  // a K step is 128 bytes of codes: 256 values
-  if (epilogue != DQ_EPI_BIAS && epilogue != DQ_EPI_GELU_TANH) return DQ_ERR_EPILOGUE;
+  if (epilogue != DQ_EPI_BIAS && epilogue != DQ_EPI_GELU_TANH &&
+      epilogue != DQ_EPI_GATED_RESIDUAL)
+    return DQ_ERR_EPILOGUE;
+  const bool gated = epilogue == DQ_EPI_GATED_RESIDUAL;
+  if (gated && (!gate || !residual)) return DQ_ERR_EPILOGUE;
   if (((M + 255) / 256) * ((N + 255) / 256) >= (int64_t(1) << 23)) return DQ_ERR_SHAPE;
   if (M == 0) return DQ_OK;
   if (!qa || !sa || !qw || !sw || !out) return DQ_ERR_NULL;
   if (!aligned16(qa) || !aligned16(qw) || !aligned16(out) || (bias && !aligned16(bias)) ||
+      (gated && !aligned16(gate)) || (gated && !aligned16(residual)) ||
       (reinterpret_cast<uintptr_t>(sa) & 7u) != 0 || (reinterpret_cast<uintptr_t>(sw) & 7u) != 0)
     return DQ_ERR_ALIGN;
   const uint64_t m = static_cast<uint64_t>(M), k = static_cast<uint64_t>(K),
@@ -447,13 +454,62 @@ int dq_linear_mxfp4(const void* qa, const void* sa, int64_t M, int64_t K, const 
   const uint64_t out_bytes = 2 * m * n;
   if (overlap(out, out_bytes, qa, m * k / 2) || overlap(out, out_bytes, sa, m * k / 32) ||
       overlap(out, out_bytes, qw, n * k / 2) || overlap(out, out_bytes, sw, n * k / 32) ||
-      overlap(out, out_bytes, bias, bias ? 2 * n : 0))
+      overlap(out, out_bytes, bias, bias ? 2 * n : 0) ||
+      (gated && overlap(out, out_bytes, gate, 2 * n)))
     return DQ_ERR_ALIAS;
-  return hip_status(dq::launch_linear_mxfp4(
-      static_cast<const uint8_t*>(qa), static_cast<const uint8_t*>(sa), M, K,
-      static_cast<const uint8_t*>(qw), static_cast<const uint8_t*>(sw), N,
-      static_cast<const uint16_t*>(bias), epilogue == DQ_EPI_GELU_TANH ? 1 : 0,
-      static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
+  if (gated && residual != out && overlap(out, out_bytes, residual, out_bytes)) return DQ_ERR_ALIAS;
+  return DQ_OK;
+}
+
+int dq_linear_mxfp4_segmented(const void* qa, const void* sa, int64_t K, int64_t nseg,
+                              const int64_t* seg_rows, const void* const* qw,
+                              const void* const* sw, int64_t N, const void* const* bias,
+                              int epilogue, const void* const* gate, const void* residual,
+                              void* out, void* stream) {
+  if (nseg < 1 || nseg > dq::kMaxSegments) return DQ_ERR_SHAPE;
+  if (!seg_rows || !qw || !sw || !bias) return DQ_ERR_NULL;
+  int64_t M = 0, tiles_m = 0;
+  for (int64_t i = 0; i < nseg; ++i) {
+    if (seg_rows[i] < 0 || seg_rows[i] > kMaxDim - M) return DQ_ERR_SHAPE;
+    M += seg_rows[i];
+    tiles_m += (seg_rows[i] + dq::kTileM - 1) / dq::kTileM;
+  }
+  const bool gated = epilogue == DQ_EPI_GATED_RESIDUAL;
+  if (gated && !gate) return DQ_ERR_EPILOGUE;
+  for (int64_t i = 0; i < nseg; ++i) {
+    if (gated && !gate[i]) return DQ_ERR_EPILOGUE;
+    const int st = check_mxfp4_args(qa, sa, M, K, qw[i], sw[i], N, bias[i], epilogue,
+                                     gated ? gate[i] : nullptr, residual, out);
+    if (st != DQ_OK) return st;
+  }
+  if (tiles_m * ((N + dq::kTileN - 1) / dq::kTileN) >= (int64_t(1) << 23)) return DQ_ERR_SHAPE;
+  if (M == 0) return DQ_OK;
+  const uint8_t* w[dq::kMaxSegments];
+  const uint8_t* ws[dq::kMaxSegments];
+  const uint16_t* b[dq::kMaxSegments];
+  const uint16_t* g[dq::kMaxSegments];
+  for (int64_t i = 0; i < nseg; ++i) {
+    w[i] = static_cast<const uint8_t*>(qw[i]);
+    ws[i] = static_cast<const uint8_t*>(sw[i]);
+    b[i] = static_cast<const uint16_t*>(bias[i]);
+    g[i] = gated ? static_cast<const uint16_t*>(gate[i]) : nullptr;
+  }
+  return hip_status(dq::launch_linear_mxfp4_segmented(
+      static_cast<const uint8_t*>(qa), static_cast<const uint8_t*>(sa), nseg, seg_rows, K, w, ws,
+      N, b, epilogue, g, static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(out),
+      static_cast<hipStream_t>(stream)));
+}
+
+int dq_linear_mxfp4(const void* qa, const void* sa, int64_t M, int64_t K, const void* qw,
+                    const void* sw, int64_t N, const void* bias, int epilogue, const void* gate,
+                    const void* residual, void* out, void* stream) {
+  const void* w[1] = {qw};
+  const void* s[1] = {sw};
+  const void* b[1] = {bias};
+  const void* g[1] = {gate};
+  const int64_t rows[1] = {M};
+  return dq_linear_mxfp4_segmented(qa, sa, K, 1, rows, w, s, N, b, epilogue, g, residual, out,
+                                   stream);
 }
 
 uint64_t dq_attention_fp8_workspace_size(int64_t H, int64_t S) {
@@ -483,6 +539,6 @@ const char* dq_status_string(int status) {
 
 int dq_last_hip_error(void) { return g_last_hip_error; }
 
-int dq_abi_version(void) { return 9; }
+int dq_abi_version(void) { return 10; }
 
 }  // extern "C"

@@ -122,10 +122,18 @@ hipError_t launch_linear_mx(const uint8_t* qa, const uint8_t* sa, int64_t M, int
 // Block-scaled FP4 (MXFP4): E2M1 codes, two per byte (element 2j in the low nibble of byte j),
 // with one E8M0 scale byte per 32 values along K.
 //   launch_quantize_mxfp4: x bf16 [R, K] (K % 32 == 0) -> codes [R, K / 2], scales [R, K / 32]
-//   launch_linear_mxfp4:   codes [M, K / 2] / [N, K / 2] and scales of A and W (K % 256 == 0,
-//                          N % 64 == 0), bias bf16 [N] or null, epilogue 0 bias / 1 GELU-tanh
+//   launch_linear_mxfp4_segmented: codes [M, K / 2] and scales of A over nseg row segments, each
+//                          with its own W codes [N, K / 2], scales, bias (or null) and gate
+//                          (K % 256 == 0, N % 64 == 0); epilogue 0 bias / 1 GELU-tanh / 2 gated
+//                          residual -> out bf16 [M, N]
 hipError_t launch_quantize_mxfp4(const uint16_t* x, int64_t R, int64_t K, uint8_t* q,
                                  uint8_t* scale, hipStream_t stream);
+hipError_t launch_linear_mxfp4_segmented(const uint8_t* qa, const uint8_t* sa, int64_t nseg,
+                                         const int64_t* seg_rows, int64_t K,
+                                         const uint8_t* const* qw, const uint8_t* const* sw,
+                                         int64_t N, const uint16_t* const* bias, int epilogue,
+                                         const uint16_t* const* gate, const uint16_t* residual,
+                                         uint16_t* out, hipStream_t stream);
 hipError_t launch_linear_mxfp4(const uint8_t* qa, const uint8_t* sa, int64_t M, int64_t K,
                                const uint8_t* qw, const uint8_t* sw, int64_t N,
                                const uint16_t* bias, int epilogue, uint16_t* out,

@@ -77,7 +77,8 @@ constexpr int kPartFloats = kBM * kBN;
 constexpr int kMaxSeg = (int)kMaxSegments;      // row segments with their own weights
 
 enum { EPI_BIAS = 0, EPI_GELU_TANH = 1, EPI_GATED_RESIDUAL = 2, EPI_QKV = 3,
-       EPI_MX_BIAS = 4, EPI_MX_GELU_TANH = 5, EPI_MX4_BIAS = 6, EPI_MX4_GELU_TANH = 7 };
+       EPI_MX_BIAS = 4, EPI_MX_GELU_TANH = 5, EPI_MX_GATED = 6,
+       EPI_MX4_BIAS = 7, EPI_MX4_GELU_TANH = 8, EPI_MX4_GATED = 9 };
 
 // Block-scaled (MX) operands: E4M3 codes with one E8M0 scale byte per 32 values along K. Each
 // K step then also stages the 4 scale bytes (one dword) of every A and B row of the tile, after
@@ -92,6 +93,10 @@ __host__ __device__ constexpr bool is_mx(int epi) { return epi >= EPI_MX_BIAS; }
 // 0: per-row scales; 1: MX with E4M3 elements; 2: MX with E2M1 elements
 __host__ __device__ constexpr int mx_kind(int epi) {
   return epi >= EPI_MX4_BIAS ? 2 : epi >= EPI_MX_BIAS ? 1 : 0;
+}
+// The output step after dequantization: EPI_BIAS, EPI_GELU_TANH, EPI_GATED_RESIDUAL (or EPI_QKV)
+__host__ __device__ constexpr int act_of(int epi) {
+  return epi < EPI_MX_BIAS ? epi : (epi - EPI_MX_BIAS) % 3;
 }
 __host__ __device__ constexpr int stage_bytes(int epi) {
   return kStageBytes + (is_mx(epi) ? kScaleBytes : 0);
@@ -134,8 +139,7 @@ struct Params {
   uint32_t* flags;           // [left-over tiles] arrival counters (cut tiles only)
   float* part;               // [parts][256 * 256] partial tiles (cut tiles only)
   uint32_t part_bytes;       // bytes of the partial tiles
-  const uint8_t* mxa;        // MX only: A's scale bytes [M, K / 32]
-  const uint8_t* mxw;        // MX only: B's scale bytes [N, K / 32]
+  const uint8_t* mxa;        // MX only: A's scale bytes [M, K / 32] (B's: in seg.sw, per segment)
   int M, N, K, tilesM, tilesN, nk, tiles;
   int dp_tiles;              // tiles of full rounds run by this launch (a multiple of the grid)
   int tail0;                 // first left-over tile
@@ -359,10 +363,12 @@ __device__ __forceinline__ TileDesc tile_desc(const Params& p, int t, int half) 
   d.rsB = buffer_rsrc(seg_args()->B[d.g.s] + (size_t)(rb > 0 ? n0 : 0) * (size_t)p.K,
                       rowsB * (uint32_t)p.K);
   if (MX) {
-    // scale bytes per row: K / 32 values; p.K counts bytes, two values each with FP4
+    // scale bytes per row: K / 32 values; p.K counts bytes, two values each with FP4. A
+    // segment's weight scale bytes sit where its per-channel scales would.
     const uint32_t kb = (uint32_t)p.K / (MX == 2 ? 16u : 32u);
+    const uint8_t* sw = reinterpret_cast<const uint8_t*>(seg_args()->sw[d.g.s]);
     d.rsSA = buffer_rsrc(p.mxa + (size_t)m0 * kb, rowsA * kb);
-    d.rsSB = buffer_rsrc(p.mxw + (size_t)(rb > 0 ? n0 : 0) * kb, rowsB * kb);
+    d.rsSB = buffer_rsrc(sw + (size_t)(rb > 0 ? n0 : 0) * kb, rowsB * kb);
   }
   return d;
 }
@@ -482,8 +488,8 @@ __device__ __forceinline__ void copy_params(const Params& p, const TileDesc& d, 
   const int nc = p.N - n0 < kBN ? p.N - n0 : kBN;
   const uint32_t cols = (uint32_t)(nc > 0 ? nc : 0);
   if (nc <= 0) n0 = 0;
-  if (is_mx(EPI) && q != 2) {
-    // block-scaled operands carry their scales with the codes: only the bias is copied
+  if (is_mx(EPI) && q < 2) {
+    // block-scaled operands carry their scales with the codes: only bias and gate are copied
   } else if (q == 0) {
     // a segment may start at any row, so the scales move 4 bytes per lane (4 x 64 of them)
     const v4i rs = buffer_rsrc(p.sa + m0, rows * 4u);
@@ -494,7 +500,7 @@ __device__ __forceinline__ void copy_params(const Params& p, const TileDesc& d, 
   } else if (q == 2) {
     const uint16_t* bias = sg->bias[s];
     copy_to_lds(buffer_rsrc(bias + n0, bias ? cols * 2u : 0u), lo, lp);
-  } else if (EPI == EPI_GATED_RESIDUAL) {
+  } else if (act_of(EPI) == EPI_GATED_RESIDUAL) {
     copy_to_lds(buffer_rsrc(sg->gate[s] + n0, cols * 2u), lo, lp);
   } else if (EPI == EPI_QKV) {
     copy_to_lds(buffer_rsrc(qkv_args().norm_qk, 512u), lo, lp);
@@ -681,13 +687,13 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[NB][4], const Params&
         const int nl = wn * 32 * NB + bn * 32 + (gp * 2 + hi) * 8;
         const int n = n0 + nl;
         float y[8] = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
-        if (EPI == EPI_GELU_TANH || EPI == EPI_MX_GELU_TANH || EPI == EPI_MX4_GELU_TANH) {
+        if (act_of(EPI) == EPI_GELU_TANH) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) y[j] = gelu_tanh(y[j]);
         }
         const bool live = m < mend && n < p.N;
         const size_t off = (size_t)m * (size_t)p.N + (size_t)n;
-        if (EPI == EPI_GATED_RESIDUAL) {
+        if (act_of(EPI) == EPI_GATED_RESIDUAL) {
           const uint4 gg = *reinterpret_cast<const uint4*>(s_g + nl);
           uint4 rr = make_uint4(0u, 0u, 0u, 0u);
           if (live) rr = *reinterpret_cast<const uint4*>(p.residual + off);
@@ -1266,6 +1272,7 @@ static hipError_t schedule_and_launch(Params& p, int64_t M, int64_t K, int64_t N
     case EPI_MX_GELU_TANH: return launch_epi<EPI_MX_GELU_TANH>(p, g, ng, stream);
     case EPI_MX4_BIAS: return launch_epi<EPI_MX4_BIAS>(p, g, ng, stream);
     case EPI_MX4_GELU_TANH: return launch_epi<EPI_MX4_GELU_TANH>(p, g, ng, stream);
+    case EPI_MX4_GATED: return launch_epi<EPI_MX4_GATED>(p, g, ng, stream);
     default: return launch_epi<EPI_GATED_RESIDUAL>(p, g, ng, stream);
   }
 }
@@ -1341,29 +1348,38 @@ hipError_t launch_linear_mx(const uint8_t* qa, const uint8_t* sa, int64_t M, int
   p.A = qa;
   p.out = out;
   p.mxa = sa;
-  p.mxw = sw;
   p.seg.B[0] = qw;
+  p.seg.sw[0] = reinterpret_cast<const float*>(sw);
   p.seg.bias[0] = bias;
   return schedule_and_launch(p, M, K, N, epilogue == 1 ? EPI_MX_GELU_TANH : EPI_MX_BIAS, nullptr,
                              0, stream);
 }
 
-// MXFP4 linear: the same kernel in MX mode with E2M1 operands. p.K counts bytes (K / 2), so a
-// K step of 128 bytes per row covers 256 values and 8 scale bytes.
-hipError_t launch_linear_mxfp4(const uint8_t* qa, const uint8_t* sa, int64_t M, int64_t K,
-                               const uint8_t* qw, const uint8_t* sw, int64_t N,
-                               const uint16_t* bias, int epilogue, uint16_t* out,
-                               hipStream_t stream) {
+// MXFP4 linear over row segments with their own weights: the same kernel in MX mode with E2M1
+// operands. p.K counts bytes (K / 2), so a K step of 128 bytes per row covers 256 values and 8
+// scale bytes.
+hipError_t launch_linear_mxfp4_segmented(const uint8_t* qa, const uint8_t* sa, int64_t nseg,
+                                         const int64_t* seg_rows, int64_t K,
+                                         const uint8_t* const* qw, const uint8_t* const* sw,
+                                         int64_t N, const uint16_t* const* bias, int epilogue,
+                                         const uint16_t* const* gate, const uint16_t* residual,
+                                         uint16_t* out, hipStream_t stream) {
   Params p{};
-  if (set_segments(p, 1, &M) == 0) return hipSuccess;
+  const int64_t M = set_segments(p, nseg, seg_rows);
+  if (M == 0) return hipSuccess;
   p.A = qa;
-  p.out = out;
   p.mxa = sa;
-  p.mxw = sw;
-  p.seg.B[0] = qw;
-  p.seg.bias[0] = bias;
-  return schedule_and_launch(p, M, K / 2, N, epilogue == 1 ? EPI_MX4_GELU_TANH : EPI_MX4_BIAS,
-                             nullptr, 0, stream);
+  p.residual = residual;
+  p.out = out;
+  for (int64_t i = 0; i < nseg; ++i) {
+    p.seg.B[i] = qw[i];
+    p.seg.sw[i] = reinterpret_cast<const float*>(sw[i]);
+    p.seg.bias[i] = bias[i];
+    p.seg.gate[i] = gate[i];
+  }
+  const int epi = epilogue == 1 ? EPI_MX4_GELU_TANH
+                  : epilogue == 2 ? EPI_MX4_GATED : EPI_MX4_BIAS;
+  return schedule_and_launch(p, M, K / 2, N, epi, nullptr, 0, stream);
 }
 
 // ---------------------------------------------------------------------------------------------

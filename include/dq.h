@@ -358,19 +358,42 @@ int dq_quantize_mxfp4(const void* x, int64_t M, int64_t K, void* q, void* scales
  * operands (twice the rate of its FP8 form):
  *
  *   y[m, n] = sum over blocks b of 2^(ea[m, b] + ew[n, b]) sum_{k in b} dec(qa[m, k]) dec(qw[n, k])
- *   out[m, n] = bf16(epilogue(y[m, n] + bias[n]))      accumulation in fp32, one rounding
+ *   v[m, n] = y[m, n] + bias[n]                          accumulation in fp32
+ *   out[m, n] = bf16(v)                                  DQ_EPI_BIAS
+ *             = bf16(gelu_tanh(v))                       DQ_EPI_GELU_TANH
+ *             = bf16(residual[m, n] + gate[n] v)         DQ_EPI_GATED_RESIDUAL
  *
  *   qa, sa   codes [M, K / 2] and scale bytes [M, K / 32] of the activations (dq_quantize_mxfp4)
  *   qw, sw   codes [N, K / 2] and scale bytes [N, K / 32] of the weights (the same routine)
- *   bias     bf16 [N] or NULL;  epilogue DQ_EPI_BIAS or DQ_EPI_GELU_TANH
- *   out      bf16 [M, N]
+ *   bias     bf16 [N] or NULL;  gate bf16 [N] and residual bf16 [M, N] for the gated epilogue
+ *            (ignored otherwise); out bf16 [M, N], which may be the residual itself
  * Requirements: 256 <= K < 2^24, K % 256 == 0, N % 64 == 0, fewer than 2^23 output tiles of
- * 256 x 256 (DQ_ERR_SHAPE otherwise); codes, bias and out 16-byte aligned, scale arrays 8-byte
- * aligned; out overlapping no input.
+ * 256 x 256 (DQ_ERR_SHAPE otherwise); codes, bias, gate, residual and out 16-byte aligned, scale
+ * arrays 8-byte aligned; out overlapping no input but the residual.
  */
 int dq_linear_mxfp4(const void* qa, const void* sa, int64_t M, int64_t K, const void* qw,
-                    const void* sw, int64_t N, const void* bias, int epilogue, void* out,
-                    void* stream);
+                    const void* sw, int64_t N, const void* bias, int epilogue, const void* gate,
+                    const void* residual, void* out, void* stream);
+
+/*
+ * dq_linear_mxfp4_segmented -- dq_linear_mxfp4 over a sequence of up to 4 row segments, each with
+ * its own weight, in one launch: the MXFP4 form of dq_linear_fp8_segmented (a double-stream
+ * block's text and image tokens, page "WaveSpeedAI X DataCrunch: Inferencia de Imagenes FLUX en
+ * Tiempo Real en B200", section "FLUX-Dev").
+ *
+ *   qa, sa     codes [M, K / 2] and scale bytes [M, K / 32] of the whole sequence
+ *   nseg       1 <= nseg <= 4; seg_rows[s] >= 0 (HOST array): the row count of segment s, M
+ *              their sum
+ *   qw[s], sw[s], bias[s], gate[s]  HOST arrays of nseg DEVICE pointers: segment s's codes
+ *              [N, K / 2], scale bytes [N, K / 32], bias [N] (NULL = zero), gate [N] (gated only)
+ *   epilogue, residual, out  as dq_linear_mxfp4, over all M rows
+ * Row m of out is exactly what dq_linear_mxfp4 gives for that row with its segment's weight.
+ */
+int dq_linear_mxfp4_segmented(const void* qa, const void* sa, int64_t K, int64_t nseg,
+                              const int64_t* seg_rows, const void* const* qw,
+                              const void* const* sw, int64_t N, const void* const* bias,
+                              int epilogue, const void* const* gate, const void* residual,
+                              void* out, void* stream);
 
 /*
  * dq_attention_fp8_workspace_size -- bytes of workspace dq_attention_fp8 may use for H heads of
@@ -428,7 +451,7 @@ const char* dq_status_string(int status);
 /* The hipError_t behind the most recent DQ_ERR_HIP returned on the calling thread (0 if none). */
 int dq_last_hip_error(void);
 
-/* ABI version of this header (currently 9). */
+/* ABI version of this header (currently 10). */
 int dq_abi_version(void);
 
 #ifdef __cplusplus

@@ -27,7 +27,7 @@ dequantized matrices in float64.
 """
 import numpy as np
 
-from .linear import EPI_BIAS, EPI_GELU_TANH, gelu_tanh
+from .linear import EPI_BIAS, EPI_GATED_RESIDUAL, EPI_GELU_TANH, gelu_tanh
 
 MX_BLOCK = 32
 FP4_EMAX = 2           # 6 = 1.5 * 2^2
@@ -106,11 +106,12 @@ def dequantize_mxfp4(packed, scales):
     return (vals * np.ldexp(1.0, s)[..., None]).reshape(R, K)
 
 
-def linear_mxfp4_ref(qa, sa, qw, sw, bias=None, epilogue=EPI_BIAS):
+def linear_mxfp4_ref(qa, sa, qw, sw, bias=None, epilogue=EPI_BIAS, gate=None, residual=None):
     """float64 [M, N] value of the MXFP4 linear layer before the bf16 rounding.
 
     qa uint8 [M, K / 2] and sa uint8 [M, K / 32]; qw uint8 [N, K / 2] and sw uint8 [N, K / 32];
-    bias float [N] (bf16 values) or None."""
+    bias float [N] (bf16 values) or None. The epilogues are the per-row layer's: v itself,
+    gelu_tanh(v), or residual + gate v (gate [N], residual [M, N], bf16 values)."""
     a = dequantize_mxfp4(qa, sa)
     w = dequantize_mxfp4(qw, sw)
     v = a @ w.T
@@ -120,4 +121,9 @@ def linear_mxfp4_ref(qa, sa, qw, sw, bias=None, epilogue=EPI_BIAS):
         return v
     if epilogue == EPI_GELU_TANH:
         return gelu_tanh(v)
+    if epilogue == EPI_GATED_RESIDUAL:
+        if gate is None or residual is None:
+            raise ValueError("linear_mxfp4_ref: the gated epilogue needs gate and residual")
+        return (np.asarray(residual, dtype=np.float64)
+                + np.asarray(gate, dtype=np.float64).reshape(1, -1) * v)
     raise ValueError(f"linear_mxfp4_ref: unsupported epilogue {epilogue!r}")

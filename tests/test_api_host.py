@@ -43,7 +43,9 @@ def lib():
     L.dq_quantize_mx_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
     L.dq_linear_mx_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp]
     L.dq_quantize_mxfp4.argtypes = [vp, i64, i64, vp, vp, vp]
-    L.dq_linear_mxfp4.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp]
+    L.dq_linear_mxfp4.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp]
+    L.dq_linear_mxfp4_segmented.argtypes = [vp, vp, i64, i64, vp, vp, vp, i64, vp, i32, vp, vp,
+                                            vp, vp]
     L.dq_linear_fp8_workspace_size.argtypes = [i64, i64, i64]
     L.dq_linear_fp8_workspace_size.restype = ctypes.c_uint64
     L.dq_status_string.restype = ctypes.c_char_p
@@ -62,6 +64,7 @@ def test_header_declares_the_entry_points():
               "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8",
               "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
               "dq_quantize_mx_fp8", "dq_linear_mx_fp8", "dq_quantize_mxfp4", "dq_linear_mxfp4",
+              "dq_linear_mxfp4_segmented",
               "dq_linear_fp8_workspace_size", "dq_status_string", "dq_last_hip_error",
               "dq_abi_version"):
         assert n in names
@@ -73,7 +76,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dq_abi_version() == 9
+    assert lib.dq_abi_version() == 10
     for st in range(9):
         s = lib.dq_status_string(st)
         assert s and len(s) > 1
@@ -293,7 +296,7 @@ def test_attention_workspace(lib):
     assert lib.dq_last_hip_error() == 0
 
 
-MX_X, MX_Q, MX_S, MX_W, MX_SW, MX_O = (0x20000000 * i for i in range(40, 46))   # fake, far apart
+MX_X, MX_Q, MX_S, MX_W, MX_SW, MX_O, MX_G, MX_R = (0x20000000 * i for i in range(40, 48))  # fake
 
 
 def test_quantize_mx_argument_checks(lib):
@@ -354,8 +357,8 @@ def test_quantize_mxfp4_argument_checks(lib):
 
 
 def mx4lin(lib, M=64, K=256, N=128, qa=MX_Q, sa=MX_S, qw=MX_W, sw=MX_SW, bias=None, epi=0,
-           out=MX_O):
-    return lib.dq_linear_mxfp4(qa, sa, M, K, qw, sw, N, bias, epi, out, None)
+           gate=None, res=None, out=MX_O):
+    return lib.dq_linear_mxfp4(qa, sa, M, K, qw, sw, N, bias, epi, gate, res, out, None)
 
 
 def test_linear_mxfp4_argument_checks(lib):
@@ -366,7 +369,14 @@ def test_linear_mxfp4_argument_checks(lib):
     assert mx4lin(lib, N=96) == SHAPE                            # N % 64
     assert mx4lin(lib, M=-1) == SHAPE
     assert mx4lin(lib, M=1 << 20, K=256, N=1 << 19) == SHAPE      # 4096 x 2048 tiles
-    assert mx4lin(lib, epi=2) == EPI                             # gated residual: not offered
+    assert mx4lin(lib, epi=3) == EPI                             # the QKV epilogue: not offered
+    assert mx4lin(lib, epi=2) == EPI                             # gated without gate/residual
+    assert mx4lin(lib, epi=2, gate=MX_G) == EPI
+    assert mx4lin(lib, epi=2, res=MX_R) == EPI
+    assert mx4lin(lib, epi=2, gate=MX_G + 8, res=MX_R) == ALIGN
+    assert mx4lin(lib, epi=2, gate=MX_G, res=MX_R + 8) == ALIGN
+    assert mx4lin(lib, epi=2, gate=MX_O + 64, res=MX_R) == ALIAS  # gate inside the output
+    assert mx4lin(lib, epi=2, gate=MX_G, res=MX_O + 64) == ALIAS  # residual shifted over it
     for name in ("qa", "sa", "qw", "sw", "out"):
         assert mx4lin(lib, **{name: None}) == NULL, name
     assert mx4lin(lib, qa=MX_Q + 8) == ALIGN
@@ -375,6 +385,40 @@ def test_linear_mxfp4_argument_checks(lib):
     assert mx4lin(lib, out=MX_O + 8) == ALIGN
     assert mx4lin(lib, out=MX_Q) == ALIAS                        # output over the codes
     assert mx4lin(lib, out=MX_SW - 64) == ALIAS                  # output into the weight scales
+    assert lib.dq_last_hip_error() == 0
+
+
+def test_linear_mxfp4_segmented_argument_checks(lib):
+    """Row segments of one MXFP4 activation matrix, each with its own weights: the per-call rules
+    hold for every segment, and the segment list itself is checked."""
+    Arr = ctypes.c_void_p * 4
+    rows = (ctypes.c_int64 * 4)(64, 0, 37, 256)
+    qw = Arr(MX_W, MX_W + 0x100000, MX_W + 0x200000, MX_W + 0x300000)
+    sw = Arr(MX_SW, MX_SW + 0x100000, MX_SW + 0x200000, MX_SW + 0x300000)
+    nob = Arr(None, None, None, None)
+    gates = Arr(MX_G, MX_G + 4096, MX_G + 8192, MX_G + 12288)
+    f = lib.dq_linear_mxfp4_segmented
+
+    def call(nseg=4, seg=rows, w=qw, s=sw, b=nob, epi=0, g=None, res=None, out=MX_O, K=256):
+        return f(MX_Q, MX_S, K, nseg, seg, w, s, 128, b, epi, g, res, out, None)
+    zero = (ctypes.c_int64 * 2)(0, 0)
+    assert call(nseg=2, seg=zero) == OK                          # every segment empty
+    assert call(nseg=0) == SHAPE
+    assert call(nseg=65) == SHAPE
+    assert call(nseg=2, seg=(ctypes.c_int64 * 2)(64, -1)) == SHAPE
+    assert call(K=128) == SHAPE
+    assert call(seg=None) == NULL
+    assert call(w=None) == NULL
+    assert call(s=None) == NULL
+    assert call(b=None) == NULL
+    assert call(w=Arr(MX_W, None, MX_W, MX_W)) == NULL           # a NULL weight in the list
+    assert call(s=Arr(MX_SW, MX_SW, MX_SW + 4, MX_SW)) == ALIGN  # a misaligned scale array
+    assert call(epi=2, res=MX_R) == EPI                          # gated, no gate list
+    assert call(epi=2, g=Arr(MX_G, MX_G, None, MX_G), res=MX_R) == EPI
+    assert call(epi=2, g=gates) == EPI                           # no residual
+    assert call(epi=2, g=Arr(MX_G, MX_G, MX_G + 8, MX_G), res=MX_R) == ALIGN
+    assert call(b=Arr(None, MX_O + 32, None, None)) == ALIAS     # a bias inside the output
+    assert lib.dq_last_hip_error() == 0
 
 
 
@@ -516,9 +560,9 @@ def test_python_binding_names_match_the_c_entry_points():
                  "dq_linear_fp8_segmented_workspace_size", "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8",
                  "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
                  "dq_quantize_mx_fp8", "dq_linear_mx_fp8", "dq_quantize_mxfp4", "dq_linear_mxfp4",
-                 "dq_linear_fp8_workspace_size"):
+                 "dq_linear_mxfp4_segmented", "dq_linear_fp8_workspace_size"):
         assert callable(getattr(dq, name))
-    assert dq.lib().dq_abi_version() == 9
+    assert dq.lib().dq_abi_version() == 10
     assert dq.dq_linear_fp8_workspace_size(512, 12288, 3072) == 4096 + 96 * 262144
 
 

@@ -1,4 +1,5 @@
-"""GPU parity of the MXFP4 path (dq_quantize_mxfp4, dq_linear_mxfp4) against the oracle.
+"""GPU parity of the MXFP4 path (dq_quantize_mxfp4, dq_linear_mxfp4, its segmented form) against
+the oracle.
 
 Packed codes and scale bytes must equal the oracle's bit for bit. The linear layer's output is
 compared with the oracle's float64 value of the layer on the same codes and scales within the
@@ -12,7 +13,7 @@ import pytest
 import torch
 
 import fp8_dynamic_quant_amd as dq
-from oracle import EPI_BIAS, EPI_GELU_TANH, round_to_bf16
+from oracle import EPI_BIAS, EPI_GATED_RESIDUAL, EPI_GELU_TANH, round_to_bf16
 from oracle.mxfp4 import (decode_fp4_table, dequantize_mxfp4, linear_mxfp4_ref, pack_fp4,
                           quantize_mxfp4)
 from gpu_util import (announce, assert_within_tolerance, bf16_to_dev, dev_to_bf16_bits, dev_to_f64,
@@ -21,7 +22,7 @@ from workloads import bf16_bits_to_f32, f32_to_bf16_bits, make_rows
 
 pytestmark = pytest.mark.gpu
 
-EPI = {"bias": EPI_BIAS, "gelu_tanh": EPI_GELU_TANH}
+EPI = {"bias": EPI_BIAS, "gelu_tanh": EPI_GELU_TANH, "gated_residual": EPI_GATED_RESIDUAL}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -234,3 +235,113 @@ def test_deterministic_and_m_zero():
                            torch.empty((0, 16), dtype=torch.uint8, device="cuda:0"),
                            u8_to_dev(qw), u8_to_dev(sw))
     assert e.shape == (0, 128)
+
+
+def _seg_inputs(seg_rows, K, N, seed):
+    """bf16 bit patterns: x [M, K] (N(0,1), a few outlier columns x30), per segment W [N, K]
+    (0.02 N(0,1)), bias (0.01 N(0,1)) and gate (1 + 0.1 N(0,1)) [N]; residual [M, N] N(0,1)."""
+    rng = np.random.default_rng(seed)
+    M = sum(seg_rows)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[:, rng.choice(K, max(1, K // 100), replace=False)] *= 30.0
+    segs = []
+    for _ in seg_rows:
+        w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+        b = (rng.standard_normal(N) * 0.01).astype(np.float32)
+        g = (1.0 + rng.standard_normal(N) * 0.1).astype(np.float32)
+        segs.append((f32_to_bf16_bits(w), f32_to_bf16_bits(b), f32_to_bf16_bits(g)))
+    res = f32_to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    return f32_to_bf16_bits(x), segs, res
+
+
+def _check_segments(seg_rows, K, N, epi, seed, sample=None):
+    """dq_linear_mxfp4_segmented against one dq_linear_mxfp4 per segment on the same codes (the
+    same tiles over the same K steps: the same bits) and against the oracle per segment. The
+    gated epilogue runs in place (out is the residual)."""
+    announce(f"mxfp4 segmented rows {seg_rows} K={K} N={N} {epi}")
+    x, segs, res = _seg_inputs(seg_rows, K, N, seed)
+    gated = epi == "gated_residual"
+    q, s = dq.dq_quantize_mxfp4(bf16_to_dev(x))
+    qws, sws, bs, gs, oracle_w = [], [], [], [], []
+    for w, b, g in segs:
+        qw, sw = dq.dq_quantize_mxfp4(bf16_to_dev(w))
+        qws.append(qw)
+        sws.append(sw)
+        bs.append(bf16_to_dev(b))
+        gs.append(bf16_to_dev(g))
+        oracle_w.append(quantize_mxfp4(bf16_bits_to_f32(w)))
+    r = bf16_to_dev(res) if gated else None
+    out = dq.dq_linear_mxfp4_segmented(q, s, seg_rows, qws, sws, bs, epi,
+                                       gs if gated else None, r, out=r)
+    parts, r0 = [], 0
+    for i, n in enumerate(seg_rows):
+        if n:
+            rr = bf16_to_dev(res[r0:r0 + n]) if gated else None
+            parts.append((r0, n, dq.dq_linear_mxfp4(q[r0:r0 + n].clone(), s[r0:r0 + n].clone(),
+                                                    qws[i], sws[i], bs[i], epi,
+                                                    gs[i] if gated else None, rr, out=rr)))
+        r0 += n
+    torch.cuda.synchronize()
+    for r0, n, o in parts:
+        assert torch.equal(out[r0:r0 + n], o), f"rows {r0}..{r0 + n}: not the bits of one call"
+    got = dev_to_f64(out)
+    gq, gsc = q.cpu().numpy(), s.cpu().numpy()
+    for i, (oqw, osw) in enumerate(oracle_w):
+        assert np.array_equal(qws[i].cpu().numpy(), oqw) and np.array_equal(sws[i].cpu().numpy(), osw)
+    r0 = 0
+    for i, n in enumerate(seg_rows):
+        rows = np.arange(r0, r0 + n)
+        if sample is not None and n > sample:
+            rows = np.unique(np.concatenate([rows[:8], rows[-8:],
+                                             np.random.default_rng(i).choice(rows, sample)]))
+        r0 += n
+        if rows.size == 0:
+            continue
+        w, b, g = segs[i]
+        oq, osc = quantize_mxfp4(bf16_bits_to_f32(x[rows]))
+        assert np.array_equal(gq[rows], oq) and np.array_equal(gsc[rows], osc)
+        ref = linear_mxfp4_ref(oq, osc, *oracle_w[i], bf16_bits_to_f32(b), EPI[epi],
+                               bf16_bits_to_f32(g) if gated else None,
+                               bf16_bits_to_f32(res[rows]) if gated else None)
+        assert_within_tolerance(got[rows], ref, what=f"mxfp4 segment {i} rows {rows[0]}..")
+
+
+@pytest.mark.parametrize("M,K,N", [(64, 256, 64), (300, 768, 320), (513, 512, 192)])
+def test_gated_residual_in_place(M, K, N):
+    _check_segments([M], K, N, "gated_residual", seed=20)
+
+
+def test_gated_residual_separate_output():
+    """The gated epilogue with an output other than the residual: the residual is left as it
+    was."""
+    M, K, N = 200, 512, 128
+    x, segs, res = _seg_inputs([M], K, N, seed=21)
+    w, b, g = segs[0]
+    announce("mxfp4 gated, separate output")
+    q, s = dq.dq_quantize_mxfp4(bf16_to_dev(x))
+    qw, sw = dq.dq_quantize_mxfp4(bf16_to_dev(w))
+    r = bf16_to_dev(res)
+    out = dq.dq_linear_mxfp4(q, s, qw, sw, bf16_to_dev(b), "gated_residual", bf16_to_dev(g), r)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_to_bf16_bits(r), res)
+    oq, osc = quantize_mxfp4(bf16_bits_to_f32(x))
+    ref = linear_mxfp4_ref(oq, osc, *quantize_mxfp4(bf16_bits_to_f32(w)), bf16_bits_to_f32(b),
+                           EPI_GATED_RESIDUAL, bf16_bits_to_f32(g), bf16_bits_to_f32(res))
+    assert_within_tolerance(dev_to_f64(out), ref, what="mxfp4 gated separate output")
+
+
+@pytest.mark.parametrize("epi", ["bias", "gelu_tanh", "gated_residual"])
+def test_segments_two(epi):
+    _check_segments([300, 77], 512, 320, epi, seed=22)
+
+
+def test_segments_ragged_and_empty():
+    """Four segments, one empty, none a multiple of 256 rows: each has its own tile rows."""
+    _check_segments([1, 255, 0, 257], 256, 192, "gated_residual", seed=23)
+
+
+@pytest.mark.parametrize("K,N,epi", [(3072, 3072, "bias"), (12288, 3072, "gated_residual")])
+def test_segments_flux_joint_sequence(K, N, epi):
+    """The 1024^2 double-stream shapes: 4096 image and 512 text tokens in one launch (sampled
+    rows of the image segment, every text row)."""
+    _check_segments([4096, 512], K, N, epi, seed=24, sample=48)

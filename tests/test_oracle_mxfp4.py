@@ -155,3 +155,29 @@ def test_block_scales_and_permutation_weights():
     a_val = decode_fp4_table()[ca[:, perm]]
     scale = np.ldexp(1.0, sa[:, b].astype(int) - 127 + sw[np.arange(N), b].astype(int) - 127)
     assert np.array_equal(got, a_val * scale * 6.0)
+
+
+def test_gated_residual_epilogue():
+    """The gated epilogue against the bias one: gate 0 returns the residual exactly, gate 1 with
+    a zero residual the bias epilogue's value, and a hand-worked row r + g (sum + bias)."""
+    from oracle import EPI_GATED_RESIDUAL
+    rng = np.random.default_rng(13)
+    M, N, K = 6, 8, 64
+    ca = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    cw = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    sa = rng.integers(124, 131, size=(M, K // MX_BLOCK)).astype(np.uint8)
+    sw = rng.integers(124, 131, size=(N, K // MX_BLOCK)).astype(np.uint8)
+    bias = _bf16(rng.standard_normal(N))
+    res = _bf16(rng.standard_normal((M, N)))
+    args = (pack_fp4(ca), sa, pack_fp4(cw), sw, bias)
+    v = linear_mxfp4_ref(*args, EPI_BIAS)
+    assert np.array_equal(linear_mxfp4_ref(*args, EPI_GATED_RESIDUAL, np.zeros(N), res), res)
+    assert np.array_equal(linear_mxfp4_ref(*args, EPI_GATED_RESIDUAL, np.ones(N),
+                                           np.zeros((M, N))), v)
+    # one weight row of code 2 (1.0) at K position 0 only, unit scales: v = a[:, 0] + bias
+    cw1 = np.zeros((1, K), np.uint8); cw1[0, 0] = 2
+    ca1 = np.zeros((2, K), np.uint8); ca1[0, 0], ca1[1, 0] = 5, 14     # 3.0 and -4.0
+    one = np.full((2, K // MX_BLOCK), 127, np.uint8)
+    g = linear_mxfp4_ref(pack_fp4(ca1), one, pack_fp4(cw1), one[:1], np.array([0.5]),
+                         EPI_GATED_RESIDUAL, np.array([2.0]), np.array([[1.0], [-1.0]]))
+    assert g.ravel().tolist() == [1.0 + 2.0 * 3.5, -1.0 + 2.0 * (-3.5)]
