@@ -407,23 +407,48 @@ def quantizer_bytes(M, K):
     return 3 * M * K + 4 * M
 
 
-def dit_floor_ms(w):
-    """Roofline floor of one step: per linear max(FLOP / FP8 peak, bytes / HBM), plus every
+def linear_bytes_mxfp4(M, K, N, epilogue):
+    """Compulsory HBM bytes of one MXFP4 GEMM + epilogue: both packed code matrices (K / 2 bytes
+    a row), their scale bytes (K / 32 a row), the bf16 output, bias (and gate + residual)."""
+    b = (M + N) * (K // 2 + K // 32) + 2 * M * N + 2 * N
+    if epilogue == "gated_residual":
+        b += 2 * M * N + 2 * N
+    return b
+
+
+def quantizer_bytes_mxfp4(M, K):
+    """Algorithmic bytes of one MXFP4 quantization: read bf16, write packed codes and scale
+    bytes."""
+    return 2 * M * K + M * K // 2 + M * K // 32
+
+
+FORMATS = {
+    # weight quantizer, peak of the GEMM, its bytes, the activation quantizer's bytes
+    "fp8": ("dq_quantize_weight_fp8", PEAK_FP8_TFLOPS, linear_bytes, quantizer_bytes),
+    "mxfp4": ("dq_quantize_mxfp4", PEAK_FP4_TFLOPS, linear_bytes_mxfp4, quantizer_bytes_mxfp4),
+}
+
+
+def dit_floor_ms(w, fmt="fp8"):
+    """Roofline floor of one step: per linear max(FLOP / matrix peak, bytes / HBM), plus every
     quantizer's bytes at HBM bandwidth."""
+    _, peak, lbytes, qbytes = FORMATS[fmt]
     t = 0.0
     for l, r in zip(w.linears, w.repeat):
-        t += r * max(l.flops / (PEAK_FP8_TFLOPS * 1e12),
-                     linear_bytes(l.M, l.K, l.N, l.epilogue) / (PEAK_HBM_GBPS * 1e9))
-        t += r * quantizer_bytes(l.M, l.K) / (PEAK_HBM_GBPS * 1e9)
+        t += r * max(l.flops / (peak * 1e12),
+                     lbytes(l.M, l.K, l.N, l.epilogue) / (PEAK_HBM_GBPS * 1e9))
+        t += r * qbytes(l.M, l.K) / (PEAK_HBM_GBPS * 1e9)
     return t * 1e3
 
 
-def bench_dit_step(steps, warmup, breakdown_steps=2, focus="single.linear1"):
+def bench_dit_step(steps, warmup, breakdown_steps=2, focus="single.linear1", fmt="fp8"):
     """All linears of one 1024^2 FLUX-dev denoising step, distinct weights per block, timed end
     to end as one sequence on one stream: per double-stream block four calls over the joint
     sequence (512 text + 4096 image rows, one quantization and one segmented linear each, the
     text and image weights as two row segments), per single-stream block two (228 weights in
-    152 quantize + linear pairs).
+    152 quantize + linear pairs). fmt "fp8": per-row FP8 codes (dq_quantize_fp8,
+    dq_linear_fp8[_segmented]); "mxfp4": block-scaled E2M1 (dq_quantize_mxfp4,
+    dq_linear_mxfp4[_segmented]) on the same inputs.
 
     Each timed step carries one HIP event pair, around one call of `focus` (the step's dominant
     kernel; step k times its k-th call, cycling), on the stream the kernels run on. After them,
@@ -435,14 +460,21 @@ def bench_dit_step(steps, warmup, breakdown_steps=2, focus="single.linear1"):
 
     w = workload("flux-dit-step-1024")
     dev = torch.device("cuda:0")
-    calls, acts, residuals = dit_step_device_inputs(w, dev, dq.dq_quantize_weight_fp8)
+    wq_name, peak, _, qbytes = FORMATS[fmt]
+    fp4 = fmt == "mxfp4"
+    calls, acts, residuals = dit_step_device_inputs(w, dev, getattr(dq, wq_name))
+    quantize = dq.dq_quantize_mxfp4 if fp4 else dq.dq_quantize_fp8
+    one_linear = dq.dq_linear_mxfp4 if fp4 else dq.dq_linear_fp8
+    seg_linear = dq.dq_linear_mxfp4_segmented if fp4 else dq.dq_linear_fp8_segmented
     outs = {}
     qbuf = {}
     for c in calls:
         M, K, N = c["M"], c["K"], c["N"]
         if (M, K) not in qbuf:
-            qbuf[(M, K)] = (torch.empty((M, K), dtype=torch.uint8, device=dev),
-                            torch.empty((M,), dtype=torch.float32, device=dev))
+            qbuf[(M, K)] = ((torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+                             torch.empty((M, K // 32), dtype=torch.uint8, device=dev)) if fp4
+                            else (torch.empty((M, K), dtype=torch.uint8, device=dev),
+                                  torch.empty((M,), dtype=torch.float32, device=dev)))
         if c["epilogue"] != "gated_residual" and (M, N) not in outs:
             outs[(M, N)] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
@@ -456,14 +488,13 @@ def bench_dit_step(steps, warmup, breakdown_steps=2, focus="single.linear1"):
         out = residuals[c["residual"]] if gated else outs[(c["M"], c["N"])]
         if len(segs) == 1:
             s0 = segs[0]
-            dq.dq_linear_fp8(q, sa, s0["qw"], s0["sw"], s0["bias"], c["epilogue"],
-                             s0["gate"], out if gated else None, out=out)
+            one_linear(q, sa, s0["qw"], s0["sw"], s0["bias"], c["epilogue"],
+                       s0["gate"], out if gated else None, out=out)
         else:
-            dq.dq_linear_fp8_segmented(q, sa, [g["rows"] for g in segs], [g["qw"] for g in segs],
-                                       [g["sw"] for g in segs], [g["bias"] for g in segs],
-                                       c["epilogue"],
-                                       [g["gate"] for g in segs] if gated else None,
-                                       out if gated else None, out=out)
+            seg_linear(q, sa, [g["rows"] for g in segs], [g["qw"] for g in segs],
+                       [g["sw"] for g in segs], [g["bias"] for g in segs], c["epilogue"],
+                       [g["gate"] for g in segs] if gated else None,
+                       out if gated else None, out=out)
 
     focus_at = [i for i, c in enumerate(calls) if c["name"] == focus]
 
@@ -476,7 +507,7 @@ def bench_dit_step(steps, warmup, breakdown_steps=2, focus="single.linear1"):
             if timed_call and all_calls:
                 e0 = pool.pop()
                 e0.record()
-            dq.dq_quantize_fp8(acts[c["act"]], q, sa)
+            quantize(acts[c["act"]], q, sa)
             if timed_call:
                 e1 = pool.pop()
                 e1.record()
@@ -522,23 +553,26 @@ def bench_dit_step(steps, warmup, breakdown_steps=2, focus="single.linear1"):
         d = by[c["name"]]
         g_us, q_us = float(np.mean(d["gemm"])), float(np.mean(d["quant"]))
         tf = c["flops"] / g_us / 1e6
-        qgb = quantizer_bytes(c["M"], c["K"]) / q_us / 1e3
+        qgb = qbytes(c["M"], c["K"]) / q_us / 1e3
         table[c["name"]] = {
             "shape": [c["M"], c["K"], c["N"]], "epilogue": c["epilogue"],
             "segments": [g["rows"] for g in c["segments"]], "per_step": 1,
             "gemm_us": round(g_us, 2), "gemm_tflops": round(tf, 1),
-            "gemm_frac": round(tf / PEAK_FP8_TFLOPS, 4),
+            "gemm_frac": round(tf / peak, 4),
             "quant_us": round(q_us, 2), "quant_gbps": round(qgb, 1),
             "quant_frac": round(qgb / PEAK_HBM_GBPS, 4),
-            "gemm_traffic": stored_traffic("gemm", f"flux-dit-step-1024/{c['name']}"),
-            "quant_traffic": stored_traffic("quantize", f"flux-dit-step-1024/{c['name']}"),
         }
+        if not fp4:
+            table[c["name"]]["gemm_traffic"] = stored_traffic(
+                "gemm", f"flux-dit-step-1024/{c['name']}")
+            table[c["name"]]["quant_traffic"] = stored_traffic(
+                "quantize", f"flux-dit-step-1024/{c['name']}")
     for row in table.values():
         row["ms_per_step"] = round(row["per_step"] * (row["gemm_us"] + row["quant_us"]) / 1e3, 3)
     return {"ms": ms, "tflops": w.flops_per_step / ms / 1e9, "calls": len(calls),
             "linears": sum(len(c["segments"]) for c in calls),
             "weight_bytes": sum(g["qw"].numel() for c in calls for g in c["segments"]),
-            "flops": w.flops_per_step, "floor_ms": dit_floor_ms(w), "focus": focus,
+            "flops": w.flops_per_step, "floor_ms": dit_floor_ms(w, fmt), "focus": focus,
             "focus_gemm_us": focus_us, "focus_calls": len(focus_marks), "breakdown": table}
 
 
@@ -686,6 +720,8 @@ def main():
     ap.add_argument("--no-qkv", action="store_true")
     ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--no-mx", action="store_true")
+    ap.add_argument("--no-dit-mxfp4", action="store_true",
+                    help="skip the step's MXFP4 variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cpu-configs", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -773,6 +809,33 @@ def main():
                 "the loop on the stream the kernels run on")),
             "quantizer": leg["quantizer"],
         })
+    if not args.no_dit_mxfp4 and w.name == "flux-dit-step-1024":
+        torch.cuda.empty_cache()
+        log("DiT step, MXFP4 variant: the same weights and activations in block-scaled E2M1")
+        d4 = bench_dit_step(args.steps, args.warmup, fmt="mxfp4")
+        ftf4 = focus.flops / d4["focus_gemm_us"] / 1e6
+        log(f"DiT step linears, MXFP4: {d4['ms']:.3f} ms ({d4['tflops']:.0f} TFLOP/s; floor "
+            f"{d4['floor_ms']:.2f} ms); {d4['focus']} GEMM {d4['focus_gemm_us']:.1f} us "
+            f"({ftf4:.0f} TFLOP/s); {d['ms'] / d4['ms']:.2f}x the FP8 step")
+        for name, row in d4["breakdown"].items():
+            log(f"  {name:16s} x{row['per_step']} {row['segments']}: GEMM {row['gemm_us']:7.1f} us "
+                f"({row['gemm_tflops']:6.0f} TFLOP/s)  quantize {row['quant_us']:6.1f} us "
+                f"({row['quant_gbps']:5.0f} GB/s)  -> {row['ms_per_step']:.2f} ms/step")
+        res["dit_step_mxfp4"] = {
+            "ms": round(d4["ms"], 4), "tflops": round(d4["tflops"], 1),
+            "speedup_vs_fp8_step": round(d["ms"] / d4["ms"], 3),
+            "roofline_floor_ms": round(d4["floor_ms"], 3),
+            "frac": round(d4["floor_ms"] / d4["ms"], 4),
+            "weight_bytes_codes": d4["weight_bytes"],
+            "focus": {"linear": d4["focus"], "avg_launch_us": round(d4["focus_gemm_us"], 2),
+                      "achieved": round(ftf4, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(ftf4 / PEAK_FP4_TFLOPS, 4)},
+            "timing": ("as the FP8 step: one HIP event pair around one focus call per timed "
+                       "step, event pairs around every call of 2 further steps"),
+            "breakdown": d4["breakdown"],
+        }
+        del d4
+        torch.cuda.empty_cache()
     if not args.no_text_stream and w.name == "flux-dit-step-1024":
         ts = bench_text_stream(ls)
         for part, r in ts.items():
