@@ -167,6 +167,63 @@ def test_exact_inputs_are_bit_exact(M, K, N, epi, ws):
     assert np.array_equal(dev_to_bf16_bits(out), _bits_of(ref))
 
 
+# Shapes of more than 128 tiles (too many for narrow halves) whose last round runs whole (no
+# workspace): every tile is a whole 256 x 256 tile, including ragged last tile rows and columns.
+WHOLE_TILES = [(2500, 1024, 3520), (2560, 512, 3584), (4608, 3072, 3072)]
+
+
+@pytest.mark.parametrize("epi", EPIS)
+def test_whole_tiles_ragged(epi):
+    """2500 x 1024 -> 3520: 10 x 14 tiles, the last tile row 196 rows and the last tile column
+    192 columns wide; every output against the oracle."""
+    M, K, N = WHOLE_TILES[0]
+    shape = LinearShape(f"whole_{M}x{K}x{N}", M, K, N, epi, K // 100, 30.0)
+    _end_to_end(shape, seed=4000 + len(epi), ws=None)
+
+
+@pytest.mark.parametrize("epi", ["bias", "gated_residual"])
+@pytest.mark.parametrize("M,K,N", [WHOLE_TILES[1], (2500, 512, 3520)])
+def test_whole_tiles_exact_inputs_are_bit_exact(M, K, N, epi):
+    """The exact-input construction of test_exact_inputs_are_bit_exact on whole-tile shapes."""
+    rng = np.random.default_rng(M + K + N + 7)
+    q = _narrow_codes(rng, (M, K))
+    qw = _narrow_codes(rng, (N, K))
+    sa = np.ldexp(1.0, rng.integers(-5, -2, M)).astype(np.float32)
+    sw = np.ldexp(1.0, rng.integers(-5, -2, N)).astype(np.float32)
+    bias = f32_to_bf16_bits((rng.integers(-64, 64, N) * 2.0 ** -6).astype(np.float32))
+    gate = res = None
+    if epi == "gated_residual":
+        gate = f32_to_bf16_bits(np.ldexp(1.0, rng.integers(-1, 2, N)).astype(np.float32))
+        res = f32_to_bf16_bits((rng.integers(-64, 64, (M, N)) * 2.0 ** -4).astype(np.float32))
+    announce(f"whole-tile exact linear {M}x{K}x{N} {epi}")
+    out = _run_linear(q, sa, qw, sw, bias, epi, gate, res, ws=None)
+    ref = linear_ref(q, sa, qw, sw, bf16_bits_to_f32(bias), epi,
+                     None if gate is None else bf16_bits_to_f32(gate),
+                     None if res is None else bf16_bits_to_f32(res))
+    assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)
+    assert np.array_equal(dev_to_bf16_bits(out), _bits_of(ref))
+
+
+def test_whole_tiles_gated_in_place_and_deterministic():
+    """4608 x 3072 -> 3072 (one round of 216 tiles): in place equals out of place, the residual
+    of the out-of-place call is untouched, and a second call gives the same bits."""
+    M, K, N = WHOLE_TILES[2]
+    shape = LinearShape("whole_inplace", M, K, N, "gated_residual", K // 100, 30.0)
+    inp = make_linear_inputs(shape, 78)
+    announce("whole-tile gated in place vs out of place")
+    q, sa = dq.dq_quantize_fp8(bf16_to_dev(inp.x))
+    qw, sw = dq.dq_quantize_weight_fp8(bf16_to_dev(inp.w))
+    b, g = bf16_to_dev(inp.bias), bf16_to_dev(inp.gate)
+    r1 = bf16_to_dev(inp.residual)
+    r2 = bf16_to_dev(inp.residual)
+    o1 = dq.dq_linear_fp8(q, sa, qw, sw, b, "gated_residual", g, r1, workspace=None)
+    o3 = dq.dq_linear_fp8(q, sa, qw, sw, b, "gated_residual", g, r1, workspace=None)
+    o2 = dq.dq_linear_fp8(q, sa, qw, sw, b, "gated_residual", g, r2, out=r2, workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, r2) and torch.equal(o1, o3)
+    assert torch.equal(r1, bf16_to_dev(inp.residual))
+
+
 def test_permutation_weights_are_bit_exact():
     """W = 448 P: sw = 1, qw = 0x7E at pi(n): out[:, n] = bf16(448 dec(q[:, pi(n)]) sa + b[n])."""
     rng = np.random.default_rng(3)
