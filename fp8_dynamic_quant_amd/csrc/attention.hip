@@ -21,7 +21,8 @@
 //   * K codes by global -> LDS copies (16 bytes per lane), 16-byte chunk c of key row r stored
 //     at slot c ^ ((r >> 1) & 7) so that 16 rows read at one offset hit 16 different slots;
 //   * V codes through registers, decoded once per workgroup to bf16 (exact: every E4M3 value is
-//     a bf16 value), stored [channel][key] with the same swizzle;
+//     a bf16 value), stored [channel][key] with the same swizzle, the keys of each 16-key group
+//     in the order the logits leave them (0-3, 8-11, 4-7, 12-15);
 //   * the blocks' key and value scales.
 // Per block and wave:
 //   1. logits: 2 x 2 FP8 matrix ops (32 keys x 32 queries x 64 channels each, keys as the
@@ -29,13 +30,17 @@
 //   2. online softmax in base 2: t = s sk_j (sq_i log2(e) / sqrt(128)); the row max takes the
 //      lane and its partner l ^ 32; the running max m (and with it the output and the sum,
 //      rescaled by 2^(m - m')) moves only when a block's max exceeds it by more than 8, so the
-//      rescale is rare after the first blocks; p = 2^(t - m) <= 2^8; keys past S are masked;
+//      rescale is rare after the first blocks; p = 2^(t - m) <= 2^8; keys past S are masked.
+//      The weights are first formed against m as it stands: when every lane's sum of them stays
+//      within 2^8 the max would not have moved and is not taken (the common case); otherwise
+//      the logits are formed again and the block goes the way just described;
 //   3. P V: p sv_j rounded to bf16 becomes the second operand of 16 bf16 matrix ops (32
-//      channels x 32 queries x 16 keys) after one half swap between partner lanes (the
-//      logits' layout holds keys 0-3 and 8-11 of a 16-key chunk in the lower lane, 4-7 and 12-15
-//      in the upper one; the operand wants 0-7 and 8-15);
-// so the output accumulates transposed, [channel][query], 64 registers per lane. One workgroup
-// barrier per block. At the end o / sum goes to bf16 and leaves as 16-byte stores.
+//      channels x 32 queries x 16 keys) as the lanes hold it (the logits' layout holds keys 0-3
+//      and 8-11 of a 16-key group in the lower lane of a query, 4-7 and 12-15 in the upper one,
+//      and the values are stored in that order);
+// so the output accumulates transposed, [channel][query], 64 registers per lane, and each lane
+// keeps the sum of its own keys' weights (the lane pair's two sums are added at the end). One
+// workgroup barrier per block. At the end o / sum goes to bf16 and leaves as 16-byte stores.
 #include "dq_internal.h"
 #include "e4m3_codec.h"
 
@@ -153,7 +158,7 @@ struct AttnArgs {
 // Split schedule. The workspace opens with one arrival counter per workgroup boundary, then two
 // partial results per boundary for the tile cut there (side 0: its first key blocks, side 1: its
 // last ones). A partial holds, per wave and lane, the 64 unnormalized output sums as 16-byte
-// groups (lane minor), then (m, sum) of the lane's query.
+// groups (lane minor), then (m, sum) of the lane (the sum of its own keys' weights).
 constexpr int kMaxGroups = 256;
 constexpr uint32_t kFlagBytes = 4096;  // kMaxGroups counters, padded
 constexpr uint32_t kPartBytes = kThreads * (64 + 2) * 4;
@@ -174,7 +179,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 template <int N>
 __device__ __forceinline__ float row_bcast(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                               0x150 + N, 0xF, 0xF, false));
+                                                               0x150 + N, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float row_bcast(float v, int n) {  // n a constant after unrolling
   switch (n) {
@@ -210,23 +215,17 @@ __device__ __forceinline__ void swap_halves(float& a, float& b) {
   b = __uint_as_float(y);
 }
 
-// Global addresses of one key block of one head.
+// One key block of one head: the row index h S + key0 of its first key, and key0 (the
+// addresses follow from these, so a block takes three scalar registers, not nine).
 struct Blk {
-  const uint8_t* k;   // codes of its first key
-  const uint8_t* v;   // value codes of channel 0 at its first key (channel c is c S bytes on)
-  const float* sk;    // scale of its first key
-  const float* sv;
-  int key0;           // index of its first key
+  size_t tok;
+  int key0;
 };
 
 __device__ __forceinline__ Blk block_at(const AttnArgs& a, int h, int kb) {
-  const size_t hs = (size_t)h * (size_t)a.S, k0 = (size_t)kb * kKB;
-  return Blk{a.k8 + (hs + k0) * kD, a.vt8 + hs * kD + k0, a.sk + hs + k0, a.sv + hs + k0,
-             kb * kKB};
+  return Blk{(size_t)h * (size_t)a.S + (size_t)kb * kKB, kb * kKB};
 }
-__device__ __forceinline__ Blk next_block(Blk b) {
-  return Blk{b.k + kKB * kD, b.v + kKB, b.sk + kKB, b.sv + kKB, b.key0 + kKB};
-}
+__device__ __forceinline__ Blk next_block(Blk b) { return Blk{b.tok + kKB, b.key0 + kKB}; }
 
 // A block of key or value codes is 8 KiB: the first kMoveThreads threads move it, 16 bytes each.
 constexpr int kMoveThreads = kKB * kD / 16;
@@ -234,12 +233,14 @@ constexpr int kMoveThreads = kKB * kD / 16;
 // A key block (64 rows of 128 bytes) into an LDS stage, one 16-byte copy per thread of waves
 // 0-7: wave w fills slots [64 w, 64 w + 64); slot n is row n >> 3, position n & 7, which holds
 // chunk (n & 7) ^ key(row). Rows past S read row S - 1 (their logits are masked).
-__device__ __forceinline__ void copy_keys(const Blk& b, int S, uint8_t* stage, int w, int l) {
+__device__ __forceinline__ void copy_keys(const AttnArgs& a, const Blk& b, uint8_t* stage, int w,
+                                          int l) {
   if (w >= kMoveThreads / 64) return;
+  const int S = a.S;
   const int n = w * 64 + l;
   const int r = n >> 3, p = n & 7;
   const int row = b.key0 + r < S ? r : S - 1 - b.key0;
-  const uint8_t* src = b.k + row * kD + swz(r, p) * 16;
+  const uint8_t* src = a.k8 + b.tok * kD + row * kD + swz(r, p) * 16;
   __builtin_amdgcn_global_load_lds(
       src, (__attribute__((address_space(3))) void*)(stage + w * 64 * 16), 16, 0, 0);
 }
@@ -248,16 +249,27 @@ __device__ __forceinline__ void copy_keys(const Blk& b, int S, uint8_t* stage, i
 // is that row offset, (tid >> 2) S + 16 (tid & 3). S is a multiple of 16, so the 16 keys are
 // either inside the sequence or past it (zeros).
 // Threads past kMoveThreads load nothing.
-__device__ __forceinline__ uint4 load_values(const Blk& b, int S, int tid, size_t vrow) {
-  return tid < kMoveThreads && b.key0 + 16 * (tid & 3) < S
-             ? *reinterpret_cast<const uint4*>(b.v + vrow)
-             : make_uint4(0u, 0u, 0u, 0u);
+// Buffer loads with a 32-bit lane offset off a block-uniform base: a 64-bit address per lane
+// would be formed once outside the loop and spilled.
+__device__ __forceinline__ uint4 load_values(const AttnArgs& a, const Blk& b, int tid, uint32_t vrow) {
+  const uint8_t* v = a.vt8 + (b.tok - (size_t)b.key0) * kD + b.key0;  // channel 0, first key
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(v), 0, 0x7FFFFFFF, 0x00020000);
+  if (tid < kMoveThreads && b.key0 + 16 * (tid & 3) < a.S)
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, vrow, 0, 0));
+  return make_uint4(0u, 0u, 0u, 0u);
 }
 
 // The block's key scale (threads 0-63) or value scale (threads 64-127) of key tid & 63, 0 past S.
-__device__ __forceinline__ float load_scale(const Blk& b, int S, int tid) {
+__device__ __forceinline__ float load_scale(const AttnArgs& a, const Blk& b, int tid) {
   const int j = tid & (kKB - 1);
-  return tid < 2 * kKB && b.key0 + j < S ? (tid < kKB ? b.sk : b.sv)[j] : 0.0f;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave 0: key scales, 1: values
+  const float* base = (w == 0 ? a.sk : a.sv) + b.tok;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7FFFFFFF, 0x00020000);
+  if (tid < 2 * kKB && b.key0 + j < a.S)
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4u * j, 0, 0));
+  return 0.0f;
 }
 
 // 8 codes (two dwords) -> 8 bf16: gfx950's scaled conversion, two codes per instruction, at
@@ -270,16 +282,18 @@ __device__ __forceinline__ uint4 decode8(uint32_t d0, uint32_t d1) {
   return make_uint4(decode2<false>(d0), decode2<true>(d0), decode2<false>(d1), decode2<true>(d1));
 }
 
-// The decoded values into an LDS stage, [channel][key] bf16, 128-byte rows, swizzled.
+// The decoded values into an LDS stage, [channel][key] bf16, 128-byte rows, swizzled. Within
+// each 16-key group the keys are stored in the order the logits leave them in a lane pair: keys
+// 0-3 and 8-11 (held by the lower lane of a query) in the first 16 bytes, 4-7 and 12-15 in the
+// second, so the weights enter the P V matrix op without an exchange between lanes.
 __device__ __forceinline__ void store_values(uint8_t* stage, int tid, const uint4 vr) {
   if (tid >= kMoveThreads) return;
   const int ch = tid >> 2, q = tid & 3;
-  const uint32_t d[4] = {vr.x, vr.y, vr.z, vr.w};
+  const uint32_t d[4] = {vr.x, vr.y, vr.z, vr.w};  // keys 16 q + 4 i + [0, 4) in d[i]
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int chunk = 2 * q + j;  // 8 keys = 16 bytes
-    *reinterpret_cast<uint4*>(stage + ch * 128 + swz(ch, chunk) * 16) =
-        decode8(d[2 * j], d[2 * j + 1]);
+    *reinterpret_cast<uint4*>(stage + ch * 128 + swz(ch, chunk) * 16) = decode8(d[j], d[j + 2]);
   }
 }
 
@@ -369,7 +383,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8(AttnArgs a) {
   // One key block of head h in stage st; the block (hn, kbn) goes into the other stage when
   // `more`. kTail marks the last block when S is not a multiple of 64 (the only one whose keys
   // past S must take no weight), a separate instance so that full blocks carry no masking.
-  const size_t vrow = (size_t)((tid >> 2) & (kD - 1)) * (size_t)S + 16 * (tid & 3);
+  // (32 bits: S < 2^24, so 127 S + 48 < 2^31. Formed again in each step from a copy of tid
+  // that the compiler cannot see through: else it is kept, spilled and reloaded.)
+  auto value_row = [&]() -> uint32_t {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    return (uint32_t)((t >> 2) & (kD - 1)) * (uint32_t)S + 16u * (t & 3);
+  };
   auto step = [&](const int kb, const int st, const bool more, const Blk& bn, auto tail_tag) {
     constexpr bool tail = decltype(tail_tag)::value;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's key copies of block kb
@@ -377,128 +397,182 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8(AttnArgs a) {
     uint4 vr = make_uint4(0u, 0u, 0u, 0u);
     float scn = 0.0f;
     if (more) {
-      vr = load_values(bn, S, tid, vrow);
-      scn = load_scale(bn, S, tid);
+      vr = load_values(a, bn, tid, value_row());
+      scn = load_scale(a, bn, tid);
     }
     // 1. logits, [key][query]. The next block's key copies into the other stage are issued only
     //    after this block's key fragments are read: the compiler cannot tell the two stages of
     //    sK apart and would otherwise wait for the copies before the first read.
-    v8i kf[2][2];
+    auto read_keys = [&](v8i (&kf)[2][2]) {
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int r = 32 * kh + (l & 31);
+      for (int kh = 0; kh < 2; ++kh) {
+        const int r = 32 * kh + (l & 31);
 #pragma unroll
-      for (int dh = 0; dh < 2; ++dh) {
-        const int c0 = 4 * dh + 2 * hi;
-        const uint4 lo = *reinterpret_cast<const uint4*>(sK[st] + r * kD + swz(r, c0) * 16);
-        const uint4 up = *reinterpret_cast<const uint4*>(sK[st] + r * kD + swz(r, c0 + 1) * 16);
-        kf[kh][dh] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                           (int)up.x, (int)up.y, (int)up.z, (int)up.w};
+        for (int dh = 0; dh < 2; ++dh) {
+          const int c0 = 4 * dh + 2 * hi;
+          const uint4 lo = *reinterpret_cast<const uint4*>(sK[st] + r * kD + swz(r, c0) * 16);
+          const uint4 up =
+              *reinterpret_cast<const uint4*>(sK[st] + r * kD + swz(r, c0 + 1) * 16);
+          kf[kh][dh] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                             (int)up.x, (int)up.y, (int)up.z, (int)up.w};
+        }
       }
-    }
-    if (more) copy_keys(bn, S, sK[st ^ 1], w, l);
-    v16f s[2];
+    };
+    auto logits = [&](const v8i (&kf)[2][2], v16f (&s)[2]) {
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      s[kh] = (v16f){};
+      for (int kh = 0; kh < 2; ++kh) {
+        s[kh] = (v16f){};
 #pragma unroll
-      for (int dh = 0; dh < 2; ++dh)
-        s[kh] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[kh][dh], qf[dh], s[kh], 0, 0,
-                                                                0, 0, 0, 0);
-    }
-    // 2. softmax in base 2: u = s sk, t = u sqc (sqc >= 0, so max t = sqc max u); the running
-    //    max m moves only when a block's max exceeds it by more than 8 (weights stay <= 2^8,
-    //    harmless in fp32 and bf16), and the rescale runs only when some lane of the wave moved
-    //    The block's scales come in one 16-byte read per lane: lane 16 r + n holds the key
-    //    (n < 8) or value (n >= 8) scales of keys 32 kh + 8 g + 4 (r >> 1) + [0, 4), with
-    //    kh = (n >> 2) & 1 and g = n & 3, i.e. the four keys that lanes of half r >> 1 hold in
-    //    register group (kh, g); a row broadcast from lane n of the row hands them to every lane.
-    const float4 sc4 = *reinterpret_cast<const float4*>(
-        &sSC[st][(l >> 3) & 1][32 * ((l >> 2) & 1) + 8 * (l & 3) + 4 * hi]);
-    const float sc[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
-    v16f (&u)[2] = s;  // u = s sk, in place
-    float mxu = -__builtin_inff();
+        for (int dh = 0; dh < 2; ++dh)
+          s[kh] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[kh][dh], qf[dh], s[kh], 0,
+                                                                  0, 0, 0, 0, 0);
+      }
+    };
+    // 2. softmax in base 2: u = s sk, t = u sqc (sqc >= 0, so max t = sqc max u). The block's
+    //    scales come in one 16-byte read per lane: lane 16 r + n holds the key (n < 8) or value
+    //    (n >= 8) scales of keys 32 kh + 8 g + 4 (r >> 1) + [0, 4), with kh = (n >> 2) & 1 and
+    //    g = n & 3, i.e. the four keys that lanes of half r >> 1 hold in register group (kh, g);
+    //    a row broadcast from lane n of the row hands them to every lane.
+    auto read_scales = [&](float (&sc)[4]) {
+      const float4 sc4 = *reinterpret_cast<const float4*>(
+          &sSC[st][(l >> 3) & 1][32 * ((l >> 2) & 1) + 8 * (l & 3) + 4 * hi]);
+      sc[0] = sc4.x, sc[1] = sc4.y, sc[2] = sc4.z, sc[3] = sc4.w;
+    };
+    auto scale_keys = [&](v16f (&u)[2], const float (&sc)[4]) {  // u = s sk, in place
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
+      for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq)
+        for (int gq = 0; gq < 4; ++gq)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) u[kh][4 * gq + j] *= row_bcast(sc[j], 4 * kh + gq);
-    if constexpr (tail) {
+          for (int j = 0; j < 4; ++j) u[kh][4 * gq + j] *= row_bcast(sc[j], 4 * kh + gq);
+    };
+    // p = 2^(u sqc - mn) (0 for keys past S), times the value scale, into bf16 pairs [kh][gq][j
+    // pair]; returns the sum of this lane's p (the partner lane l ^ 32 holds the query's other
+    // keys; the two partial sums are added when the tile ends).
+    auto weights = [&](const v16f (&u)[2], const float (&sc)[4], float mn,
+                       uint32_t (&pk)[2][4][2]) -> float {
+      float ps = 0.0f;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          float p[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            p[j] = __builtin_amdgcn_exp2f(fmaf(u[kh][4 * gq + j], sqc, -mn));
+            if constexpr (tail)
+              if (kb * kKB + 32 * kh + 8 * gq + 4 * hi + j >= S) p[j] = 0.0f;
+            ps += p[j];
+          }
+          const int n = 8 + 4 * kh + gq;
+          pk[kh][gq][0] = pack_bf16(p[0] * row_bcast(sc[0], n), p[1] * row_bcast(sc[1], n));
+          pk[kh][gq][1] = pack_bf16(p[2] * row_bcast(sc[2], n), p[3] * row_bcast(sc[3], n));
+        }
+      return ps;
+    };
+    // The running max m moves only when a block's max exceeds it by more than 8 (weights stay
+    // <= 2^8, harmless in fp32 and bf16); the output is rescaled only when some lane of the
+    // wave moved, which is rare after the first blocks. The weights are first formed against m
+    // as it stands: when every lane's sum stays within 2^8 (so does each weight) the max would
+    // not have moved and is not needed. Otherwise (the first block of a tile, a new max) the
+    // block max is taken and the weights are formed once more, by the same code.
+    auto new_max = [&](const v16f (&u)[2]) -> float {
+      float mxu = -__builtin_inff();
+      asm volatile("" : "+v"(mxu));  // (keeps the max on the path that needs it)
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int key = kb * kKB + 32 * kh + 8 * (v >> 2) + 4 * hi + (v & 3);
-          if (key < S) mxu = fmaxf(mxu, u[kh][v]);
+          if constexpr (tail) {
+            const int key = kb * kKB + 32 * kh + 8 * (v >> 2) + 4 * hi + (v & 3);
+            if (key < S) mxu = fmaxf(mxu, u[kh][v]);
+          } else {
+            mxu = fmaxf(mxu, u[kh][v]);
+          }
         }
-    } else {
+      float a0 = mxu, b0 = mxu;
+      swap_halves(a0, b0);
+      const float mx = fmaxf(a0, b0) * sqc;
+      return mx > m + 8.0f ? mx : m;
+    };
+    // One pass of the block's logits and weights; a second pass (rare: see above) forms the
+    // logits again from the keys still in this stage, takes the max and then the weights.
+    uint32_t pk[2][4][2];
+    float mn = m, ps;
+    bool again = false;
+#pragma nounroll
+    for (;;) {
+      v16f s[2];
+      // The key fragments and the scales are read before the next block's key copies are
+      // issued: the compiler does not tell the LDS arrays apart from the copies' target and
+      // would make any later LDS read wait for every outstanding load (those copies, and the
+      // next block's values and scales, issued at the top of the step).
+      float sc[4];
+      {
+        v8i kf[2][2];
+        read_keys(kf);
+        read_scales(sc);
+        if (more && !again) copy_keys(a, bn, sK[st ^ 1], w, l);
+        logits(kf, s);
+      }
+      scale_keys(s, sc);
+      if (again) mn = new_max(s);
+      ps = weights(s, sc, mn, pk);
+      // (the packed weights are pinned here: else the compiler moves their products out of the
+      // loop, away from the scales' row broadcasts that they would fold in, and keeps the 32
+      // fp32 weights alive instead of 16 packed pairs)
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mxu = fmaxf(mxu, u[kh][v]);
+        for (int gq = 0; gq < 4; ++gq) asm volatile("" : "+v"(pk[kh][gq][0]), "+v"(pk[kh][gq][1]));
+      if (again || __builtin_amdgcn_ballot_w64(!(ps <= 256.0f)) == 0) break;
+      again = true;
+      asm volatile("" ::: "memory");  // (the second pass reads the keys and scales again)
     }
-    {
-      float a0 = mxu, b0 = mxu;
-      swap_halves(a0, b0);
-      mxu = fmaxf(a0, b0);
-    }
-    const float mx = mxu * sqc;
-    const bool move = mx > m + 8.0f;
-    const float mn = move ? mx : m;
-    float ps = 0.0f;
-    uint32_t pk[2][4][2];  // bf16 pairs of p sv: [kh][gq][j pair]
+    if (again) {
+      // rescale by 2^(m - m') (2^0 = 1 where the max holds)
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      lsum = lsum * alpha + ps;
+      if (__builtin_amdgcn_ballot_w64(mn != m) != 0) {
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        float p[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(fmaf(u[kh][4 * gq + j], sqc, -mn));
-          if constexpr (tail)
-            if (kb * kKB + 32 * kh + 8 * gq + 4 * hi + j >= S) p[j] = 0.0f;
-          ps += p[j];
-        }
-        const int n = 8 + 4 * kh + gq;
-        pk[kh][gq][0] = pack_bf16(p[0] * row_bcast(sc[0], n), p[1] * row_bcast(sc[1], n));
-        pk[kh][gq][1] = pack_bf16(p[2] * row_bcast(sc[2], n), p[3] * row_bcast(sc[3], n));
+        for (int i = 0; i < 4; ++i) o[i] *= alpha;
       }
-    {
-      float a0 = ps, b0 = ps;
-      swap_halves(a0, b0);
-      ps = a0 + b0;
+      m = mn;
+    } else {
+      lsum += ps;
     }
-    // P V operands: weights of keys [16 kc, +16) after the half swap (done here, ahead of the
-    // branch below, so that the products above stay next to their scale broadcasts)
+    // 3. P V: the weights of keys [16 kc, +16) as the lanes hold them (the values are stored in
+    //    that key order)
     bf8v pb[4];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const int kh = kc >> 1, c2 = kc & 1;
-      uint32_t x0 = pk[kh][2 * c2][0], x1 = pk[kh][2 * c2][1];
-      uint32_t y0 = pk[kh][2 * c2 + 1][0], y1 = pk[kh][2 * c2 + 1][1];
-      swap_halves(x0, y0);
-      swap_halves(x1, y1);
-      pb[kc] = __builtin_bit_cast(bf8v, make_uint4(x0, x1, y0, y1));
+      pb[kc] = __builtin_bit_cast(bf8v, make_uint4(pk[kh][2 * c2][0], pk[kh][2 * c2][1],
+                                                   pk[kh][2 * c2 + 1][0], pk[kh][2 * c2 + 1][1]));
     }
-    // rescale by 2^(m - m') when the max moved (2^0 = 1 otherwise); the output only when some
-    // lane of the wave moved, which is rare after the first blocks
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    lsum = lsum * alpha + ps;
-    if (__builtin_amdgcn_ballot_w64(move) != 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] *= alpha;
-    }
-    m = mn;
-    // 3. P V
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
+    // The value fragments of one 16-key group (four reads) are in flight while the matrix ops
+    // of the previous group run: left to itself the compiler reads one fragment at a time,
+    // each matrix op waiting for its read.
+    auto read_values = [&](int kc, bf8v (&vf)[4]) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const int r = 32 * db + (l & 31);
-        const bf8v vf = *reinterpret_cast<const bf8v*>(sV[st] + r * 128 + swz(r, 2 * kc + hi) * 16);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kc], o[db], 0, 0, 0);
+        vf[db] = *reinterpret_cast<const bf8v*>(sV[st] + r * 128 + swz(r, 2 * kc + hi) * 16);
       }
+    };
+    bf8v vf[2][4];
+    read_values(0, vf[0]);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      if (kc < 3) read_values(kc + 1, vf[(kc + 1) & 1]);
+      if (kc == 0)  // DS reads: this group's and the next one's, then the next one's only
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      else if (kc < 3)
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kc & 1][db], pb[kc], o[db], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // matrix ops
     }
     if (more) {
       store_values(sV[st ^ 1], tid, vr);
@@ -579,7 +653,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8(AttnArgs a) {
 
   // o / sum, [channel][query] -> out[query][h][channel]
   auto write_out = [&](int h) {
-    const float inv = 1.0f / lsum;
+    float s0 = lsum, s1 = lsum;  // the query's sum: this lane's keys and its partner's
+    swap_halves(s0, s1);
+    const float inv = 1.0f / (s0 + s1);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -605,9 +681,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8(AttnArgs a) {
   // the run's first block into stage 0
   Blk bc = block_at(a, t / a.qtiles, k0);
   {
-    copy_keys(bc, S, sK[0], w, l);
-    store_values(sV[0], tid, load_values(bc, S, tid, vrow));
-    const float sc = load_scale(bc, S, tid);
+    copy_keys(a, bc, sK[0], w, l);
+    store_values(sV[0], tid, load_values(a, bc, tid, value_row()));
+    const float sc = load_scale(a, bc, tid);
     if (tid < 2 * kKB) sSC[0][tid >> 6][tid & (kKB - 1)] = sc;
   }
   int st = 0;
