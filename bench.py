@@ -195,8 +195,9 @@ def bench_qkv(steps, warmup, n_sets, M=4096, K=3072, heads=24, seed=3200):
     """The attention input projection of the image stream at 1024^2 (4096 tokens, 3072 -> 3 x 24
     heads x 128) with the fused query/key RMS norm + rotary epilogue, against the same GEMM with
     the plain bias epilogue and, for context, that GEMM followed by the torch ops the fusion
-    replaces. Back-to-back calls, one event pair around each loop; returns microseconds per
-    call."""
+    replaces; then the variant whose queries and keys leave as FP8 codes for the attention
+    kernel, against the bf16 variant followed by the two per-row quantizations it replaces.
+    Back-to-back calls, one event pair around each loop; returns microseconds per call."""
     import torch
     import torch.nn.functional as F
     import fp8_dynamic_quant_amd as dq
@@ -217,6 +218,11 @@ def bench_qkv(steps, warmup, n_sets, M=4096, K=3072, heads=24, seed=3200):
         sets.append({"q": q, "sa": sa, "qw": qw, "sw": sw, "b": to_dev_bf16(torch, inp.bias, dev),
                      "o": tuple(torch.empty((heads, M, 128), dtype=torch.bfloat16, device=dev)
                                 for _ in range(3)),
+                     "o8": (torch.empty((heads, M, 128), dtype=torch.uint8, device=dev),
+                            torch.empty((heads, M), dtype=torch.float32, device=dev),
+                            torch.empty((heads, M, 128), dtype=torch.uint8, device=dev),
+                            torch.empty((heads, M), dtype=torch.float32, device=dev),
+                            torch.empty((heads, M, 128), dtype=torch.bfloat16, device=dev)),
                      "plain": torch.empty((M, N), dtype=torch.bfloat16, device=dev)})
     torch.cuda.synchronize()
     c2 = tcos[:, None, :]
@@ -228,6 +234,18 @@ def bench_qkv(steps, warmup, n_sets, M=4096, K=3072, heads=24, seed=3200):
 
     def plain(st):
         dq.dq_linear_fp8(st["q"], st["sa"], st["qw"], st["sw"], st["b"], "bias", out=st["plain"])
+
+    def fused8(st):
+        dq.dq_linear_qkv_fp8_attn(st["q"], st["sa"], st["qw"], st["sw"], heads, st["b"], nqk, tcos,
+                                  tsin, out=st["o8"])
+
+    def fused_then_quantize(st):
+        fused(st)
+        o8 = st["o8"]
+        dq.dq_quantize_fp8(st["o"][0].view(heads * M, 128), q=o8[0].view(heads * M, 128),
+                           scale=o8[1].view(heads * M))
+        dq.dq_quantize_fp8(st["o"][1].view(heads * M, 128), q=o8[2].view(heads * M, 128),
+                           scale=o8[3].view(heads * M))
 
     def unfused(st):
         plain(st)
@@ -245,7 +263,8 @@ def bench_qkv(steps, warmup, n_sets, M=4096, K=3072, heads=24, seed=3200):
         return loop_us(fn, sets, n, warmup)
 
     return {"fused_us": timed(fused, steps), "plain_us": timed(plain, steps),
-            "unfused_us": timed(unfused, max(steps // 4, 5)), "flops": 2 * M * N * K,
+            "unfused_us": timed(unfused, max(steps // 4, 5)), "fp8_qk_us": timed(fused8, steps),
+            "bf16_then_quantize_us": timed(fused_then_quantize, steps), "flops": 2 * M * N * K,
             "shape": [M, K, N], "heads": heads}
 
 
@@ -882,7 +901,9 @@ def main():
         qk = bench_qkv(ls, 20, min(args.sets, 4))
         tf = qk["flops"] / qk["fused_us"] / 1e6
         log(f"QKV + norm + rotary {qk['shape']}: {qk['fused_us']:.1f} us ({tf:.0f} TFLOP/s); "
-            f"bias epilogue {qk['plain_us']:.1f} us; unfused {qk['unfused_us']:.1f} us")
+            f"bias epilogue {qk['plain_us']:.1f} us; unfused {qk['unfused_us']:.1f} us; "
+            f"queries and keys as FP8 codes {qk['fp8_qk_us']:.1f} us (bf16 outputs then "
+            f"quantized: {qk['bf16_then_quantize_us']:.1f} us)")
         res["qkv_linear"] = {
             "kernel": "gemm_fp8_pp<qkv>",
             "timing": ("back-to-back calls over rotating inputs (1 or 2 launches per call), one "
@@ -895,6 +916,8 @@ def main():
             "algorithmic_flop_per_launch": qk["flops"],
             "bias_epilogue_us": round(qk["plain_us"], 2),
             "unfused_torch_us": round(qk["unfused_us"], 2),
+            "fp8_query_key_us": round(qk["fp8_qk_us"], 2),
+            "bf16_then_quantize_us": round(qk["bf16_then_quantize_us"], 2),
         }
     if not args.no_attention:
         at = bench_attention(ls, 20, 3)

@@ -73,6 +73,10 @@ def lib() -> ctypes.CDLL:
         L.dq_linear_qkv_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, vp,
                                         ctypes.c_float, vp, vp, vp, vp, ctypes.c_uint64, vp]
         L.dq_linear_qkv_fp8.restype = i32
+        L.dq_linear_qkv_fp8_attn.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, vp,
+                                             ctypes.c_float, vp, vp, vp, vp, vp, vp,
+                                             ctypes.c_uint64, vp]
+        L.dq_linear_qkv_fp8_attn.restype = i32
         L.dq_quantize_v_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
         L.dq_quantize_v_fp8.restype = i32
         L.dq_attention_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp,
@@ -395,6 +399,53 @@ def dq_linear_qkv_fp8(q, scale, qw, w_scale, heads, bias, norm_qk, rope_cos, rop
     return tuple(out)
 
 
+def dq_linear_qkv_fp8_attn(q, scale, qw, w_scale, heads, bias, norm_qk, rope_cos, rope_sin,
+                           eps=1e-6, out=None, stream=None, workspace="auto"):
+    """dq_linear_qkv_fp8 with the queries and keys as FP8 codes and per-(head, token) scales, the
+    operands of dq_attention_fp8; the values stay bf16 (for dq_quantize_v_fp8).
+
+    Arguments as dq_linear_qkv_fp8. Returns (q8 uint8 [heads, M, 128], q_scale f32 [heads, M],
+    k8, k_scale, out_v bf16 [heads, M, 128]); `out` may supply the five."""
+    where = "dq_linear_qkv_fp8_attn"
+    if not isinstance(q, torch.Tensor) or q.dim() != 2 or not isinstance(qw, torch.Tensor) \
+            or qw.dim() != 2:
+        raise ValueError(f"{where}: q and qw must be 2-D tensors")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError(f"{where}: tensors must be on a GPU")
+    M, K = q.shape
+    heads = int(heads)
+    N = 3 * heads * HEAD_DIM
+    _need(q, "q", torch.uint8, (M, K), dev)
+    _need(scale, "scale", torch.float32, (M,), dev)
+    _need(qw, "qw", torch.uint8, (N, K), dev)
+    _need(w_scale, "w_scale", torch.float32, (N,), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, (N,), dev)
+    _need(norm_qk, "norm_qk", torch.bfloat16, (2, HEAD_DIM), dev)
+    _need(rope_cos, "rope_cos", torch.float32, (M, HEAD_DIM // 2), dev)
+    _need(rope_sin, "rope_sin", torch.float32, (M, HEAD_DIM // 2), dev)
+    if out is None:
+        out = (torch.empty((heads, M, HEAD_DIM), dtype=torch.uint8, device=dev),
+               torch.empty((heads, M), dtype=torch.float32, device=dev),
+               torch.empty((heads, M, HEAD_DIM), dtype=torch.uint8, device=dev),
+               torch.empty((heads, M), dtype=torch.float32, device=dev),
+               torch.empty((heads, M, HEAD_DIM), dtype=torch.bfloat16, device=dev))
+    specs = ((torch.uint8, (heads, M, HEAD_DIM)), (torch.float32, (heads, M)),
+             (torch.uint8, (heads, M, HEAD_DIM)), (torch.float32, (heads, M)),
+             (torch.bfloat16, (heads, M, HEAD_DIM)))
+    for t, name, (dt, shp) in zip(out, ("q8", "q_scale", "k8", "k_scale", "out_v"), specs):
+        _need(t, name, dt, shp, dev)
+    with torch.cuda.device(dev):
+        st = stream if stream is not None else torch.cuda.current_stream(dev)
+        workspace, ws_bytes = _resolve_workspace(workspace, dev, st, M, K, N)
+        _check(lib().dq_linear_qkv_fp8_attn(
+            _ptr(q), _ptr(scale), M, K, _ptr(qw), _ptr(w_scale), heads, _ptr(bias), _ptr(norm_qk),
+            _ptr(rope_cos), _ptr(rope_sin), float(eps), *(_ptr(t) for t in out),
+            _ptr(workspace), ws_bytes, ctypes.c_void_p(st.cuda_stream)), where)
+    return tuple(out)
+
+
 def dq_quantize_v_fp8(v, vt=None, v_scale=None, stream=None):
     """Per-(head, token) FP8 quantization of values bf16 [H, S, 128], codes written transposed:
     returns (vt uint8 [H, 128, S], v_scale float32 [H, S]). S must be a multiple of 16."""
@@ -615,7 +666,8 @@ def dq_linear_mxfp4_segmented(qa, sa, seg_rows, qws, sws, biases, epilogue="bias
 
 __all__ = ["dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8", "dq_linear_fp8_noalloc",
            "dq_linear_fp8_segmented", "dq_linear_fp8_segmented_workspace_size",
-           "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8", "HEAD_DIM",
+           "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8", "dq_linear_qkv_fp8_attn",
+           "HEAD_DIM",
            "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
            "quantize_qkv_heads_fp8", "dq_quantize_mx_fp8", "dq_linear_mx_fp8", "MX_BLOCK",
            "dq_quantize_mxfp4", "dq_linear_mxfp4", "dq_linear_mxfp4_segmented",

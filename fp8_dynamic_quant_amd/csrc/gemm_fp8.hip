@@ -54,6 +54,7 @@
 // "Solucion de WaveSpeed para Acelerar la Generacion de Imagenes FLUX.1-dev", section
 // "Cuantizacion Dinamica FP8".
 #include "dq_internal.h"
+#include "e4m3_codec.h"
 
 #include <atomic>
 #include <mutex>
@@ -78,7 +79,8 @@ constexpr int kMaxSeg = (int)kMaxSegments;      // row segments with their own w
 
 enum { EPI_BIAS = 0, EPI_GELU_TANH = 1, EPI_GATED_RESIDUAL = 2, EPI_QKV = 3,
        EPI_MX_BIAS = 4, EPI_MX_GELU_TANH = 5, EPI_MX_GATED = 6,
-       EPI_MX4_BIAS = 7, EPI_MX4_GELU_TANH = 8, EPI_MX4_GATED = 9 };
+       EPI_MX4_BIAS = 7, EPI_MX4_GELU_TANH = 8, EPI_MX4_GATED = 9,
+       EPI_QKV_Q8 = 10 };  // the QKV epilogue with queries and keys leaving as E4M3 codes
 
 // Block-scaled (MX) operands: E4M3 codes with one E8M0 scale byte per 32 values along K. Each
 // K step then also stages the 4 scale bytes (one dword) of every A and B row of the tile, after
@@ -89,14 +91,17 @@ enum { EPI_BIAS = 0, EPI_GELU_TANH = 1, EPI_GATED_RESIDUAL = 2, EPI_QKV = 3,
 // per row is 256 values along K and its 8 scale bytes are two dwords per row: lanes 0-31 of the
 // copy move the first dword of 32 rows, lanes 32-63 the second, filling the whole slot.
 constexpr int kScaleBytes = 4096;
-__host__ __device__ constexpr bool is_mx(int epi) { return epi >= EPI_MX_BIAS; }
+__host__ __device__ constexpr bool is_mx(int epi) {
+  return epi >= EPI_MX_BIAS && epi <= EPI_MX4_GATED;
+}
+__host__ __device__ constexpr bool is_qkv(int epi) { return epi == EPI_QKV || epi == EPI_QKV_Q8; }
 // 0: per-row scales; 1: MX with E4M3 elements; 2: MX with E2M1 elements
 __host__ __device__ constexpr int mx_kind(int epi) {
-  return epi >= EPI_MX4_BIAS ? 2 : epi >= EPI_MX_BIAS ? 1 : 0;
+  return epi >= EPI_MX4_BIAS && epi <= EPI_MX4_GATED ? 2 : is_mx(epi) ? 1 : 0;
 }
 // The output step after dequantization: EPI_BIAS, EPI_GELU_TANH, EPI_GATED_RESIDUAL (or EPI_QKV)
 __host__ __device__ constexpr int act_of(int epi) {
-  return epi < EPI_MX_BIAS ? epi : (epi - EPI_MX_BIAS) % 3;
+  return is_qkv(epi) ? EPI_QKV : epi < EPI_MX_BIAS ? epi : (epi - EPI_MX_BIAS) % 3;
 }
 __host__ __device__ constexpr int stage_bytes(int epi) {
   return kStageBytes + (is_mx(epi) ? kScaleBytes : 0);
@@ -111,9 +116,11 @@ struct QkvArgs {
   const uint16_t* norm_qk;   // [2][128] query then key RMS-norm weights
   const float* rope_cos;     // [M, 64]
   const float* rope_sin;     // [M, 64]
-  uint16_t* out_q;           // [heads, M, 128] each
+  uint16_t* out_q;           // [heads, M, 128] each (EPI_QKV_Q8: query and key codes, bytes)
   uint16_t* out_k;
   uint16_t* out_v;
+  float* scale_q;            // EPI_QKV_Q8 only: [heads, M], the scale of each code row
+  float* scale_k;
   float eps;
   int heads;
 };
@@ -164,6 +171,8 @@ __device__ __forceinline__ QkvArgs qkv_args() {
   a.out_q = kp->qkv.out_q;
   a.out_k = kp->qkv.out_k;
   a.out_v = kp->qkv.out_v;
+  a.scale_q = kp->qkv.scale_q;
+  a.scale_k = kp->qkv.scale_k;
   a.eps = kp->qkv.eps;
   a.heads = kp->qkv.heads;
   return a;
@@ -502,7 +511,7 @@ __device__ __forceinline__ void copy_params(const Params& p, const TileDesc& d, 
     copy_to_lds(buffer_rsrc(bias + n0, bias ? cols * 2u : 0u), lo, lp);
   } else if (act_of(EPI) == EPI_GATED_RESIDUAL) {
     copy_to_lds(buffer_rsrc(sg->gate[s] + n0, cols * 2u), lo, lp);
-  } else if (EPI == EPI_QKV) {
+  } else if (is_qkv(EPI)) {
     copy_to_lds(buffer_rsrc(qkv_args().norm_qk, 512u), lo, lp);
   }
 }
@@ -744,10 +753,10 @@ __device__ __forceinline__ void rope_load(__amdgpu_buffer_rsrc_t rc, __amdgpu_bu
   }
 }
 
-template <int NB>
+template <int NB, bool kQ8>
 __device__ __forceinline__ void epilogue_qkv(v16f (&acc)[NB][4], const Params& p, int m0,
                                              int n0, int wm, int wn, int lane, const uint8_t* pb,
-                                             float* scratch) {
+                                             float* scratch, uint32_t* qscr) {
   const float* s_sa = reinterpret_cast<const float*>(pb);
   const float* s_sw = reinterpret_cast<const float*>(pb + 1024);
   const uint16_t* s_b = reinterpret_cast<const uint16_t*>(pb + 2048);
@@ -831,6 +840,7 @@ __device__ __forceinline__ void epilogue_qkv(v16f (&acc)[NB][4], const Params& p
       }
       rr = 1.0f / __builtin_sqrtf(fmaf(t, 1.0f / 128.0f, qa.eps));
     }
+    uint32_t amx = 0;  // kQ8: packed maxima of |bf16| over this lane's query or key outputs
 #pragma unroll
     for (int bn = 0; bn < NB; ++bn) {
       const int nu = bm * NB + bn + 1;  // next unit
@@ -868,7 +878,14 @@ __device__ __forceinline__ void epilogue_qkv(v16f (&acc)[NB][4], const Params& p
         o.y = pack_bf16(y[2], y[3]);
         o.z = pack_bf16(y[4], y[5]);
         o.w = pack_bf16(y[6], y[7]);
-        if (m < p.M && region < 3) {
+        if (kQ8 && normed) {
+          // the bf16 results wait in the accumulator registers for the head row's scale
+          acc[bn][bm][gp * 8 + 0] = __uint_as_float(o.x);
+          acc[bn][bm][gp * 8 + 1] = __uint_as_float(o.y);
+          acc[bn][bm][gp * 8 + 2] = __uint_as_float(o.z);
+          acc[bn][bm][gp * 8 + 3] = __uint_as_float(o.w);
+          amx = codec::absmax4(amx, o);
+        } else if (m < p.M && region < 3) {
           uint16_t* out = region == 0 ? qa.out_q : region == 1 ? qa.out_k : qa.out_v;
           *reinterpret_cast<uint4*>(out + ((size_t)head * (size_t)p.M + (size_t)m) * 128 + d) = o;
         }
@@ -879,6 +896,72 @@ __device__ __forceinline__ void epilogue_qkv(v16f (&acc)[NB][4], const Params& p
           cc[gp] = cn[gp];
           ss4[gp] = sn4[gp];
         }
+      }
+    }
+    if (kQ8 && normed) {
+      // the row's maximum over this wave's columns (lanes l and l + 32 hold its two halves)
+      const uint32_t m16 = (amx & 0xFFFFu) > (amx >> 16) ? (amx & 0xFFFFu) : (amx >> 16);
+      // (through the float form of the half swap, which moves the bits unchanged)
+      float a0 = __uint_as_float(m16), a1 = a0;
+      swap_halves(a0, a1);
+      const uint32_t o16 = __float_as_uint(a0) > __float_as_uint(a1) ? __float_as_uint(a0)
+                                                                     : __float_as_uint(a1);
+      if (hi == 0) qscr[wn * 256 + ml] = o16;
+    }
+  }
+  if constexpr (kQ8) {
+    // Queries and keys to E4M3 with one scale per head row, exactly as dq_quantize_fp8 encodes
+    // those bf16 rows: the row's |max| over the head's waves, scale = amax / 448, then the
+    // quantizer's encoder on each group of 8 values.
+    phase_barrier();  // every wave's row maxima are in LDS (every wave reaches it)
+    if (normed) {
+      uint8_t* codes = reinterpret_cast<uint8_t*>(region == 0 ? qa.out_q : qa.out_k);
+      float* scales = region == 0 ? qa.scale_q : qa.scale_k;
+      const int w0 = NB == 2 ? (wn & ~1) : (wn & ~3);
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm) {
+        const int ml = wm * 128 + bm * 32 + (lane & 31);
+        const int m = m0 + ml;
+        uint32_t mx = 0;
+#pragma unroll
+        for (int i = 0; i < 4 / NB; ++i) {
+          const uint32_t o = qscr[(w0 + i) * 256 + ml];
+          mx = mx > o ? mx : o;
+        }
+        const float amax = __uint_as_float(mx << 16);
+        const float sc = amax / codec::kE4M3Max;
+        float ss = sc, y = 0.0f;
+        const int kind = mx == 0 ? 0 : sc < codec::kFltMinNormal ? 1
+                                     : amax < codec::kTinyAmax ? 2 : 3;
+        if (kind == 2) {
+          ss = sc * 0x1p64f;
+          y = 1.0f / ss;
+        } else if (kind == 3) {
+          y = 1.0f / sc;
+        }
+        const bool live = m < p.M;
+        const size_t row = (size_t)head * (size_t)p.M + (size_t)(live ? m : 0);
+        if (live && hi == 0 && wn == w0) scales[row] = sc;
+#pragma unroll
+        for (int bn = 0; bn < NB; ++bn)
+#pragma unroll
+          for (int gp = 0; gp < 2; ++gp) {
+            const uint4 v = make_uint4(__float_as_uint(acc[bn][bm][gp * 8 + 0]),
+                                       __float_as_uint(acc[bn][bm][gp * 8 + 1]),
+                                       __float_as_uint(acc[bn][bm][gp * 8 + 2]),
+                                       __float_as_uint(acc[bn][bm][gp * 8 + 3]));
+            uint2 c;
+            if (kind == 0)
+              c = codec::signs8(v);
+            else if (kind == 1)
+              c = codec::encode8<1, false>(v, sc, 0.0f);
+            else if (kind == 2)
+              c = codec::encode8<0, true>(v, ss, y);
+            else
+              c = codec::encode8<0, false>(v, sc, y);
+            const int d = dw + bn * 32 + (gp * 2 + hi) * 8;
+            if (live) *reinterpret_cast<uint2*>(codes + row * 128 + d) = c;
+          }
       }
     }
   }
@@ -987,9 +1070,13 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
   constexpr int MX = mx_kind(EPI);
   constexpr int kStage = stage_bytes(EPI);
   constexpr int kOps = batch_ops(EPI);
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStage + kParamBufs * kParamBytes];
+  // (EPI_QKV_Q8: 4 KiB more, for the rows' absolute maxima exchanged between the waves of a head)
+  constexpr int kQ8Bytes = EPI == EPI_QKV_Q8 ? 4096 : 0;
+  __shared__ __attribute__((aligned(1024)))
+  uint8_t lds[2 * kStage + kParamBufs * kParamBytes + kQ8Bytes];
   __shared__ int s_last;
   uint8_t* pbuf = lds + 2 * kStage;
+  uint32_t* qscr = reinterpret_cast<uint32_t*>(pbuf + kParamBufs * kParamBytes);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1108,21 +1195,21 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
     float* scratch = reinterpret_cast<float*>(pbuf + ((part + 2) % kParamBufs) * kParamBytes);
     if constexpr (NB == 2) {
       const bool cut = cutp >= 0;
-      const bool align = cut || EPI == EPI_QKV;
+      const bool align = cut || is_qkv(EPI);
       bool write = true;
       if (align && g == 0) phase_barrier();  // group 1's last MFMAs of this item are done
       if (cut) write = finish_split(acc, p, t, cutp, wave, lane, &s_last);
       if (write) {
-        if constexpr (EPI == EPI_QKV)
-          epilogue_qkv<2>(acc, p, m0, n0, wm, wn, lane, pb, scratch);
+        if constexpr (is_qkv(EPI))
+          epilogue_qkv<2, EPI == EPI_QKV_Q8>(acc, p, m0, n0, wm, wn, lane, pb, scratch, qscr);
         else
           epilogue<EPI, 2>(acc, p, m0, n0, gi.mend, wm, wn, lane, pb);
       }
       if (align && g == 1) phase_barrier();  // back to one phase behind
     } else {
-      if constexpr (EPI == EPI_QKV) {
+      if constexpr (is_qkv(EPI)) {
         if (g == 0) phase_barrier();
-        epilogue_qkv<1>(acc, p, m0, n0, wm, wn, lane, pb, scratch);
+        epilogue_qkv<1, EPI == EPI_QKV_Q8>(acc, p, m0, n0, wm, wn, lane, pb, scratch, qscr);
         if (g == 1) phase_barrier();
       } else {
         epilogue<EPI, 1>(acc, p, m0, n0, gi.mend, wm, wn, lane, pb);
@@ -1268,6 +1355,7 @@ static hipError_t schedule_and_launch(Params& p, int64_t M, int64_t K, int64_t N
     case EPI_BIAS: return launch_epi<EPI_BIAS>(p, g, ng, stream);
     case EPI_GELU_TANH: return launch_epi<EPI_GELU_TANH>(p, g, ng, stream);
     case EPI_QKV: return launch_epi<EPI_QKV>(p, g, ng, stream);
+    case EPI_QKV_Q8: return launch_epi<EPI_QKV_Q8>(p, g, ng, stream);
     case EPI_MX_BIAS: return launch_epi<EPI_MX_BIAS>(p, g, ng, stream);
     case EPI_MX_GELU_TANH: return launch_epi<EPI_MX_GELU_TANH>(p, g, ng, stream);
     case EPI_MX4_BIAS: return launch_epi<EPI_MX4_BIAS>(p, g, ng, stream);
@@ -1465,6 +1553,35 @@ hipError_t launch_linear_qkv(const uint8_t* q, const float* scale, int64_t M, in
   p.qkv.eps = eps;
   p.qkv.heads = (int)heads;
   return schedule_and_launch(p, M, K, 3 * heads * 128, EPI_QKV, workspace, workspace_bytes,
+                             stream);
+}
+
+hipError_t launch_linear_qkv_q8(const uint8_t* q, const float* scale, int64_t M, int64_t K,
+                                const uint8_t* qw, const float* w_scale, int64_t heads,
+                                const uint16_t* bias, const uint16_t* norm_qk,
+                                const float* rope_cos, const float* rope_sin, float eps,
+                                uint8_t* q8, float* q_scale, uint8_t* k8, float* k_scale,
+                                uint16_t* out_v, void* workspace, uint64_t workspace_bytes,
+                                hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  Params p{};
+  set_segments(p, 1, &M);
+  p.A = q;
+  p.sa = scale;
+  p.seg.B[0] = qw;
+  p.seg.sw[0] = w_scale;
+  p.seg.bias[0] = bias;
+  p.qkv.norm_qk = norm_qk;
+  p.qkv.rope_cos = rope_cos;
+  p.qkv.rope_sin = rope_sin;
+  p.qkv.out_q = reinterpret_cast<uint16_t*>(q8);
+  p.qkv.out_k = reinterpret_cast<uint16_t*>(k8);
+  p.qkv.out_v = out_v;
+  p.qkv.scale_q = q_scale;
+  p.qkv.scale_k = k_scale;
+  p.qkv.eps = eps;
+  p.qkv.heads = (int)heads;
+  return schedule_and_launch(p, M, K, 3 * heads * 128, EPI_QKV_Q8, workspace, workspace_bytes,
                              stream);
 }
 

@@ -35,6 +35,8 @@ def lib():
                                                      vp, vp, vp]
     L.dq_linear_qkv_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, vp, ctypes.c_float,
                                     vp, vp, vp, vp, ctypes.c_uint64, vp]
+    L.dq_linear_qkv_fp8_attn.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, vp,
+                                         ctypes.c_float, vp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
     L.dq_quantize_v_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
     L.dq_attention_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, ctypes.c_uint64,
                                    i64, vp]
@@ -61,7 +63,7 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
-              "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8",
+              "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8", "dq_linear_qkv_fp8_attn",
               "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
               "dq_quantize_mx_fp8", "dq_linear_mx_fp8", "dq_quantize_mxfp4", "dq_linear_mxfp4",
               "dq_linear_mxfp4_segmented",
@@ -76,7 +78,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dq_abi_version() == 10
+    assert lib.dq_abi_version() == 11
     for st in range(9):
         s = lib.dq_status_string(st)
         assert s and len(s) > 1
@@ -239,6 +241,48 @@ def test_linear_qkv_workspace_checks(lib):
     assert qkv(lib, ws=Wk, ws_bytes=need, oq=Wk + 4096) == ALIAS
     assert qkv(lib, ws=Wk, ws_bytes=need, cos=Wk + (1 << 20)) == ALIAS
     assert qkv(lib, ws=Wk, ws_bytes=need, q=None) == NULL
+    assert lib.dq_last_hip_error() == 0
+
+
+Q8, SQ8, K8, SK8 = (0x10000000 * i for i in range(16, 20))   # fake, far from the others
+
+
+def qkv8(lib, M=64, K=256, heads=1, q=Aq, sa=As, qw=Wq, sw=Ws, bias=Bi, nqk=NQ, cos=CS, sin=SN,
+         eps=1e-6, q8=Q8, sq=SQ8, k8=K8, sk=SK8, ov=OV, ws=None, ws_bytes=0):
+    return lib.dq_linear_qkv_fp8_attn(q, sa, M, K, qw, sw, heads, bias, nqk, cos, sin, eps, q8, sq,
+                                      k8, sk, ov, ws, ws_bytes, None)
+
+
+def test_linear_qkv_attn_argument_checks(lib):
+    assert qkv8(lib, M=0) == OK
+    assert qkv8(lib, M=0, q=None, q8=None) == OK              # empty: pointers are not checked
+    assert qkv8(lib, heads=0) == SHAPE
+    assert qkv8(lib, heads=1 << 30) == SHAPE
+    assert qkv8(lib, K=192) == SHAPE
+    assert qkv8(lib, M=-1) == SHAPE
+    assert qkv8(lib, eps=0.0) == VALUE
+    assert qkv8(lib, eps=float("nan")) == VALUE
+    for name in ("q", "sa", "qw", "sw", "nqk", "cos", "sin", "q8", "sq", "k8", "sk", "ov"):
+        assert qkv8(lib, **{name: None}) == NULL, name
+    base = dict(q=Aq, sa=As, qw=Wq, sw=Ws, bias=Bi, nqk=NQ, cos=CS, sin=SN, q8=Q8, sq=SQ8, k8=K8,
+                sk=SK8, ov=OV)
+    for name, val in base.items():
+        assert qkv8(lib, **{name: val + 8}) == ALIGN, name
+    # codes [heads, M, 128] = 8 KiB here, scales [heads, M] = 256 bytes, values 16 KiB
+    assert qkv8(lib, q8=Aq) == ALIAS                          # query codes over the input codes
+    assert qkv8(lib, sk=CS + 64) == ALIAS                     # key scales over the cosines
+    assert qkv8(lib, k8=Q8 + 8192 - 16) == ALIAS              # two code outputs overlap
+    assert qkv8(lib, sq=Q8 + 4096) == ALIAS                   # scales inside the query codes
+    assert qkv8(lib, ov=K8 - 16384 + 16) == ALIAS             # values run into the key codes
+    assert qkv8(lib, k8=Q8 + 8192, sq=Q8 + 16384, sk=Q8 + 16640, ov=Q8 + 16896,
+                q=None) == NULL                               # adjacent outputs are fine
+
+
+def test_linear_qkv_attn_workspace_checks(lib):
+    need = 4096 + 4 * 256 * 256 * 4
+    assert qkv8(lib, ws=Wk + 16, ws_bytes=need) == WORKSPACE
+    assert qkv8(lib, ws=Wk, ws_bytes=need, sq=Wk + 4096) == ALIAS
+    assert qkv8(lib, ws=Wk, ws_bytes=need, q=None) == NULL
     assert lib.dq_last_hip_error() == 0
 
 
@@ -558,11 +602,11 @@ def test_python_binding_names_match_the_c_entry_points():
     for name in ("dq_quantize_fp8", "dq_quantize_weight_fp8", "dq_linear_fp8",
                  "dq_linear_fp8_noalloc", "dq_linear_fp8_segmented",
                  "dq_linear_fp8_segmented_workspace_size", "dq_layernorm_modulate_quantize_fp8", "dq_linear_qkv_fp8",
-                 "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
+                 "dq_linear_qkv_fp8_attn", "dq_quantize_v_fp8", "dq_attention_fp8", "dq_attention_fp8_workspace_size",
                  "dq_quantize_mx_fp8", "dq_linear_mx_fp8", "dq_quantize_mxfp4", "dq_linear_mxfp4",
                  "dq_linear_mxfp4_segmented", "dq_linear_fp8_workspace_size"):
         assert callable(getattr(dq, name))
-    assert dq.lib().dq_abi_version() == 10
+    assert dq.lib().dq_abi_version() == 11
     assert dq.dq_linear_fp8_workspace_size(512, 12288, 3072) == 4096 + 96 * 262144
 
 
