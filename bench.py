@@ -195,8 +195,8 @@ def bench_qkv(steps, warmup, n_sets, M=4096, K=3072, heads=24, seed=3200):
     """The attention input projection of the image stream at 1024^2 (4096 tokens, 3072 -> 3 x 24
     heads x 128) with the fused query/key RMS norm + rotary epilogue, against the same GEMM with
     the plain bias epilogue and, for context, that GEMM followed by the torch ops the fusion
-    replaces; then the variant whose queries and keys leave as FP8 codes for the attention
-    kernel, against the bf16 variant followed by the two per-row quantizations it replaces.
+    replaces; then the variant whose outputs leave as FP8 codes for the attention kernel, against
+    the bf16 variant followed by the three quantizations it replaces.
     Back-to-back calls, one event pair around each loop; returns microseconds per call."""
     import torch
     import torch.nn.functional as F
@@ -222,7 +222,8 @@ def bench_qkv(steps, warmup, n_sets, M=4096, K=3072, heads=24, seed=3200):
                             torch.empty((heads, M), dtype=torch.float32, device=dev),
                             torch.empty((heads, M, 128), dtype=torch.uint8, device=dev),
                             torch.empty((heads, M), dtype=torch.float32, device=dev),
-                            torch.empty((heads, M, 128), dtype=torch.bfloat16, device=dev)),
+                            torch.empty((heads, 128, M), dtype=torch.uint8, device=dev),
+                            torch.empty((heads, M), dtype=torch.float32, device=dev)),
                      "plain": torch.empty((M, N), dtype=torch.bfloat16, device=dev)})
     torch.cuda.synchronize()
     c2 = tcos[:, None, :]
@@ -246,6 +247,7 @@ def bench_qkv(steps, warmup, n_sets, M=4096, K=3072, heads=24, seed=3200):
                            scale=o8[1].view(heads * M))
         dq.dq_quantize_fp8(st["o"][1].view(heads * M, 128), q=o8[2].view(heads * M, 128),
                            scale=o8[3].view(heads * M))
+        dq.dq_quantize_v_fp8(st["o"][2], vt=o8[4], v_scale=o8[5])
 
     def unfused(st):
         plain(st)
@@ -902,8 +904,8 @@ def main():
         tf = qk["flops"] / qk["fused_us"] / 1e6
         log(f"QKV + norm + rotary {qk['shape']}: {qk['fused_us']:.1f} us ({tf:.0f} TFLOP/s); "
             f"bias epilogue {qk['plain_us']:.1f} us; unfused {qk['unfused_us']:.1f} us; "
-            f"queries and keys as FP8 codes {qk['fp8_qk_us']:.1f} us (bf16 outputs then "
-            f"quantized: {qk['bf16_then_quantize_us']:.1f} us)")
+            f"outputs as FP8 codes {qk['fp8_qk_us']:.1f} us (bf16 outputs then quantized: "
+            f"{qk['bf16_then_quantize_us']:.1f} us)")
         res["qkv_linear"] = {
             "kernel": "gemm_fp8_pp<qkv>",
             "timing": ("back-to-back calls over rotating inputs (1 or 2 launches per call), one "
@@ -916,7 +918,7 @@ def main():
             "algorithmic_flop_per_launch": qk["flops"],
             "bias_epilogue_us": round(qk["plain_us"], 2),
             "unfused_torch_us": round(qk["unfused_us"], 2),
-            "fp8_query_key_us": round(qk["fp8_qk_us"], 2),
+            "fp8_outputs_us": round(qk["fp8_qk_us"], 2),
             "bf16_then_quantize_us": round(qk["bf16_then_quantize_us"], 2),
         }
     if not args.no_attention:

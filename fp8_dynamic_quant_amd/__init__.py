@@ -74,7 +74,7 @@ def lib() -> ctypes.CDLL:
                                         ctypes.c_float, vp, vp, vp, vp, ctypes.c_uint64, vp]
         L.dq_linear_qkv_fp8.restype = i32
         L.dq_linear_qkv_fp8_attn.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, vp,
-                                             ctypes.c_float, vp, vp, vp, vp, vp, vp,
+                                             ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
                                              ctypes.c_uint64, vp]
         L.dq_linear_qkv_fp8_attn.restype = i32
         L.dq_quantize_v_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
@@ -401,11 +401,12 @@ def dq_linear_qkv_fp8(q, scale, qw, w_scale, heads, bias, norm_qk, rope_cos, rop
 
 def dq_linear_qkv_fp8_attn(q, scale, qw, w_scale, heads, bias, norm_qk, rope_cos, rope_sin,
                            eps=1e-6, out=None, stream=None, workspace="auto"):
-    """dq_linear_qkv_fp8 with the queries and keys as FP8 codes and per-(head, token) scales, the
-    operands of dq_attention_fp8; the values stay bf16 (for dq_quantize_v_fp8).
+    """dq_linear_qkv_fp8 with its outputs as FP8 codes and per-(head, token) scales, the operands
+    of dq_attention_fp8 (M a multiple of 16).
 
     Arguments as dq_linear_qkv_fp8. Returns (q8 uint8 [heads, M, 128], q_scale f32 [heads, M],
-    k8, k_scale, out_v bf16 [heads, M, 128]); `out` may supply the five."""
+    k8, k_scale, vt8 uint8 [heads, 128, M] (values transposed), v_scale f32 [heads, M]); `out`
+    may supply the six."""
     where = "dq_linear_qkv_fp8_attn"
     if not isinstance(q, torch.Tensor) or q.dim() != 2 or not isinstance(qw, torch.Tensor) \
             or qw.dim() != 2:
@@ -430,11 +431,13 @@ def dq_linear_qkv_fp8_attn(q, scale, qw, w_scale, heads, bias, norm_qk, rope_cos
                torch.empty((heads, M), dtype=torch.float32, device=dev),
                torch.empty((heads, M, HEAD_DIM), dtype=torch.uint8, device=dev),
                torch.empty((heads, M), dtype=torch.float32, device=dev),
-               torch.empty((heads, M, HEAD_DIM), dtype=torch.bfloat16, device=dev))
+               torch.empty((heads, HEAD_DIM, M), dtype=torch.uint8, device=dev),
+               torch.empty((heads, M), dtype=torch.float32, device=dev))
     specs = ((torch.uint8, (heads, M, HEAD_DIM)), (torch.float32, (heads, M)),
              (torch.uint8, (heads, M, HEAD_DIM)), (torch.float32, (heads, M)),
-             (torch.bfloat16, (heads, M, HEAD_DIM)))
-    for t, name, (dt, shp) in zip(out, ("q8", "q_scale", "k8", "k_scale", "out_v"), specs):
+             (torch.uint8, (heads, HEAD_DIM, M)), (torch.float32, (heads, M)))
+    for t, name, (dt, shp) in zip(out, ("q8", "q_scale", "k8", "k_scale", "vt8", "v_scale"),
+                                  specs):
         _need(t, name, dt, shp, dev)
     with torch.cuda.device(dev):
         st = stream if stream is not None else torch.cuda.current_stream(dev)

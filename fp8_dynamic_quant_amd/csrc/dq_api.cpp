@@ -316,21 +316,23 @@ int dq_linear_qkv_fp8(const void* q, const float* scale, int64_t M, int64_t K, c
 int dq_linear_qkv_fp8_attn(const void* q, const float* scale, int64_t M, int64_t K, const void* qw,
                            const float* w_scale, int64_t heads, const void* bias,
                            const void* norm_qk, const float* rope_cos, const float* rope_sin,
-                           float eps, void* q8, float* q_scale, void* k8, float* k_scale,
-                           void* out_v, void* workspace, uint64_t workspace_bytes, void* stream) {
+                           float eps, void* q8, float* q_scale, void* k8, float* k_scale, void* vt8,
+                           float* v_scale, void* workspace, uint64_t workspace_bytes,
+                           void* stream) {
   if (heads < 1 || heads > kMaxDim / (3 * dq::kHeadDim)) return DQ_ERR_SHAPE;
   const int64_t N = 3 * heads * dq::kHeadDim;
   const int shape = check_linear_shape(M, K, N);
   if (shape != DQ_OK) return shape;
+  if (M % 16 != 0) return DQ_ERR_SHAPE;  // the transposed value rows: 16-byte chunks of tokens
   if (!std::isfinite(eps) || !(eps > 0.0f)) return DQ_ERR_VALUE;
   if (M == 0) return DQ_OK;
   if (!q || !scale || !qw || !w_scale || !norm_qk || !rope_cos || !rope_sin || !q8 || !q_scale ||
-      !k8 || !k_scale || !out_v)
+      !k8 || !k_scale || !vt8 || !v_scale)
     return DQ_ERR_NULL;
   if (!aligned16(q) || !aligned16(scale) || !aligned16(qw) || !aligned16(w_scale) ||
       (bias && !aligned16(bias)) || !aligned16(norm_qk) || !aligned16(rope_cos) ||
       !aligned16(rope_sin) || !aligned16(q8) || !aligned16(q_scale) || !aligned16(k8) ||
-      !aligned16(k_scale) || !aligned16(out_v))
+      !aligned16(k_scale) || !aligned16(vt8) || !aligned16(v_scale))
     return DQ_ERR_ALIGN;
   const uint64_t m = static_cast<uint64_t>(M), k = static_cast<uint64_t>(K),
                  n = static_cast<uint64_t>(N);
@@ -339,27 +341,27 @@ int dq_linear_qkv_fp8_attn(const void* q, const float* scale, int64_t M, int64_t
   const void* ins[8] = {q, scale, qw, w_scale, bias, norm_qk, rope_cos, rope_sin};
   const uint64_t in_bytes[8] = {m * k, 4 * m, n * k, 4 * n, bias ? 2 * n : 0,
                                 4 * static_cast<uint64_t>(dq::kHeadDim), rope_bytes, rope_bytes};
-  void* outs[5] = {q8, q_scale, k8, k_scale, out_v};
-  const uint64_t out_bytes[5] = {rows * dq::kHeadDim, 4 * rows, rows * dq::kHeadDim, 4 * rows,
-                                 2 * rows * dq::kHeadDim};
-  for (int o = 0; o < 5; ++o) {
+  void* outs[6] = {q8, q_scale, k8, k_scale, vt8, v_scale};
+  const uint64_t cb = rows * dq::kHeadDim;
+  const uint64_t out_bytes[6] = {cb, 4 * rows, cb, 4 * rows, cb, 4 * rows};
+  for (int o = 0; o < 6; ++o) {
     for (int i = 0; i < 8; ++i)
       if (overlap(outs[o], out_bytes[o], ins[i], in_bytes[i])) return DQ_ERR_ALIAS;
-    for (int o2 = o + 1; o2 < 5; ++o2)
+    for (int o2 = o + 1; o2 < 6; ++o2)
       if (overlap(outs[o], out_bytes[o], outs[o2], out_bytes[o2])) return DQ_ERR_ALIAS;
   }
   if (workspace) {
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DQ_ERR_WORKSPACE;
     for (int i = 0; i < 8; ++i)
       if (overlap(workspace, workspace_bytes, ins[i], in_bytes[i])) return DQ_ERR_ALIAS;
-    for (int o = 0; o < 5; ++o)
+    for (int o = 0; o < 6; ++o)
       if (overlap(workspace, workspace_bytes, outs[o], out_bytes[o])) return DQ_ERR_ALIAS;
   }
   return hip_status(dq::launch_linear_qkv_q8(
       static_cast<const uint8_t*>(q), scale, M, K, static_cast<const uint8_t*>(qw), w_scale,
       heads, static_cast<const uint16_t*>(bias), static_cast<const uint16_t*>(norm_qk), rope_cos,
       rope_sin, eps, static_cast<uint8_t*>(q8), q_scale, static_cast<uint8_t*>(k8), k_scale,
-      static_cast<uint16_t*>(out_v), workspace, workspace ? workspace_bytes : 0,
+      static_cast<uint8_t*>(vt8), v_scale, workspace, workspace ? workspace_bytes : 0,
       static_cast<hipStream_t>(stream)));
 }
 

@@ -93,15 +93,15 @@ hipError_t launch_linear_qkv(const uint8_t* q, const float* scale, int64_t M, in
                              const float* rope_sin, float eps, uint16_t* out_q, uint16_t* out_k,
                              uint16_t* out_v, void* workspace, uint64_t workspace_bytes,
                              hipStream_t stream);
-// launch_linear_qkv with the queries and keys as E4M3 codes [heads, M, 128] and one scale per
-// head row [heads, M] (the values stay bf16).
+// launch_linear_qkv with every output as E4M3 codes and one scale per head row [heads, M]:
+// queries and keys [heads, M, 128], values transposed [heads, 128, M] (M % 16 == 0).
 hipError_t launch_linear_qkv_q8(const uint8_t* q, const float* scale, int64_t M, int64_t K,
                                 const uint8_t* qw, const float* w_scale, int64_t heads,
                                 const uint16_t* bias, const uint16_t* norm_qk,
                                 const float* rope_cos, const float* rope_sin, float eps,
                                 uint8_t* q8, float* q_scale, uint8_t* k8, float* k_scale,
-                                uint16_t* out_v, void* workspace, uint64_t workspace_bytes,
-                                hipStream_t stream);
+                                uint8_t* vt8, float* v_scale, void* workspace,
+                                uint64_t workspace_bytes, hipStream_t stream);
 
 // FP8 attention (attention.hip). S % 16 == 0 and 1 <= S, H.
 //   launch_quantize_v: v bf16 [H, S, kHeadDim] -> codes transposed [H, kHeadDim, S], scales [H, S]

@@ -116,11 +116,12 @@ struct QkvArgs {
   const uint16_t* norm_qk;   // [2][128] query then key RMS-norm weights
   const float* rope_cos;     // [M, 64]
   const float* rope_sin;     // [M, 64]
-  uint16_t* out_q;           // [heads, M, 128] each (EPI_QKV_Q8: query and key codes, bytes)
-  uint16_t* out_k;
+  uint16_t* out_q;           // [heads, M, 128] each; EPI_QKV_Q8: codes (bytes), the values'
+  uint16_t* out_k;           // transposed, [heads, 128, M]
   uint16_t* out_v;
-  float* scale_q;            // EPI_QKV_Q8 only: [heads, M], the scale of each code row
+  float* scale_q;            // EPI_QKV_Q8 only: [heads, M], the scale of each head row
   float* scale_k;
+  float* scale_v;
   float eps;
   int heads;
 };
@@ -173,6 +174,7 @@ __device__ __forceinline__ QkvArgs qkv_args() {
   a.out_v = kp->qkv.out_v;
   a.scale_q = kp->qkv.scale_q;
   a.scale_k = kp->qkv.scale_k;
+  a.scale_v = kp->qkv.scale_v;
   a.eps = kp->qkv.eps;
   a.heads = kp->qkv.heads;
   return a;
@@ -878,7 +880,7 @@ __device__ __forceinline__ void epilogue_qkv(v16f (&acc)[NB][4], const Params& p
         o.y = pack_bf16(y[2], y[3]);
         o.z = pack_bf16(y[4], y[5]);
         o.w = pack_bf16(y[6], y[7]);
-        if (kQ8 && normed) {
+        if (kQ8 && region < 3) {
           // the bf16 results wait in the accumulator registers for the head row's scale
           acc[bn][bm][gp * 8 + 0] = __uint_as_float(o.x);
           acc[bn][bm][gp * 8 + 1] = __uint_as_float(o.y);
@@ -898,7 +900,7 @@ __device__ __forceinline__ void epilogue_qkv(v16f (&acc)[NB][4], const Params& p
         }
       }
     }
-    if (kQ8 && normed) {
+    if (kQ8 && region < 3) {
       // the row's maximum over this wave's columns (lanes l and l + 32 hold its two halves)
       const uint32_t m16 = (amx & 0xFFFFu) > (amx >> 16) ? (amx & 0xFFFFu) : (amx >> 16);
       // (through the float form of the half swap, which moves the bits unchanged)
@@ -910,13 +912,16 @@ __device__ __forceinline__ void epilogue_qkv(v16f (&acc)[NB][4], const Params& p
     }
   }
   if constexpr (kQ8) {
-    // Queries and keys to E4M3 with one scale per head row, exactly as dq_quantize_fp8 encodes
-    // those bf16 rows: the row's |max| over the head's waves, scale = amax / 448, then the
-    // quantizer's encoder on each group of 8 values.
+    // Queries, keys and values to E4M3 with one scale per head row, exactly as dq_quantize_fp8
+    // (and, for the values, dq_quantize_v_fp8) encode those bf16 rows: the row's |max| over the
+    // head's waves, scale = amax / 448, then the quantizer's encoder on each group of 8 values.
     phase_barrier();  // every wave's row maxima are in LDS (every wave reaches it)
-    if (normed) {
-      uint8_t* codes = reinterpret_cast<uint8_t*>(region == 0 ? qa.out_q : qa.out_k);
-      float* scales = region == 0 ? qa.scale_q : qa.scale_k;
+    if (region < 3) {
+      uint8_t* codes = reinterpret_cast<uint8_t*>(region == 0 ? qa.out_q
+                                                  : region == 1 ? qa.out_k : qa.out_v);
+      float* scales = region == 0 ? qa.scale_q : region == 1 ? qa.scale_k : qa.scale_v;
+      // values: this wave's 1 KiB of LDS for turning 32 rows x 32 channels of codes around
+      uint8_t* vtile = reinterpret_cast<uint8_t*>(qscr + 1024) + (wm * 4 + wn) * 1024;
       const int w0 = NB == 2 ? (wn & ~1) : (wn & ~3);
 #pragma unroll
       for (int bm = 0; bm < 4; ++bm) {
@@ -943,25 +948,52 @@ __device__ __forceinline__ void epilogue_qkv(v16f (&acc)[NB][4], const Params& p
         const size_t row = (size_t)head * (size_t)p.M + (size_t)(live ? m : 0);
         if (live && hi == 0 && wn == w0) scales[row] = sc;
 #pragma unroll
-        for (int bn = 0; bn < NB; ++bn)
+        for (int bn = 0; bn < NB; ++bn) {
+          uint2 c[2];
 #pragma unroll
           for (int gp = 0; gp < 2; ++gp) {
             const uint4 v = make_uint4(__float_as_uint(acc[bn][bm][gp * 8 + 0]),
                                        __float_as_uint(acc[bn][bm][gp * 8 + 1]),
                                        __float_as_uint(acc[bn][bm][gp * 8 + 2]),
                                        __float_as_uint(acc[bn][bm][gp * 8 + 3]));
-            uint2 c;
             if (kind == 0)
-              c = codec::signs8(v);
+              c[gp] = codec::signs8(v);
             else if (kind == 1)
-              c = codec::encode8<1, false>(v, sc, 0.0f);
+              c[gp] = codec::encode8<1, false>(v, sc, 0.0f);
             else if (kind == 2)
-              c = codec::encode8<0, true>(v, ss, y);
+              c[gp] = codec::encode8<0, true>(v, ss, y);
             else
-              c = codec::encode8<0, false>(v, sc, y);
-            const int d = dw + bn * 32 + (gp * 2 + hi) * 8;
-            if (live) *reinterpret_cast<uint2*>(codes + row * 128 + d) = c;
+              c[gp] = codec::encode8<0, false>(v, sc, y);
           }
+          if (region < 2) {  // queries and keys: [head row][channel]
+#pragma unroll
+            for (int gp = 0; gp < 2; ++gp) {
+              const int d = dw + bn * 32 + (gp * 2 + hi) * 8;
+              if (live) *reinterpret_cast<uint2*>(codes + row * 128 + d) = c[gp];
+            }
+          } else {
+            // values: [head][channel][token]. The 32 rows x 32 channels of codes go into the
+            // wave's LDS tile as [channel][row] bytes, and come back as 16 rows of one channel
+            // per lane, a 16-byte store (M is a multiple of 16, so a chunk is all in or out)
+#pragma unroll
+            for (int gp = 0; gp < 2; ++gp)
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                const int cl = (gp * 2 + hi) * 8 + i;
+                const uint32_t w = i < 4 ? c[gp].x : c[gp].y;
+                vtile[cl * 32 + (lane & 31)] = (uint8_t)(w >> (8 * (i & 3)));
+              }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's tile is written
+            const int cl = lane >> 1, half = lane & 1;
+            const uint4 t = *reinterpret_cast<const uint4*>(vtile + cl * 32 + half * 16);
+            const int mt = m0 + wm * 128 + bm * 32 + half * 16;  // first row of the chunk
+            if (mt < p.M)
+              *reinterpret_cast<uint4*>(
+                  codes + ((size_t)head * 128 + (size_t)(dw + bn * 32 + cl)) * (size_t)p.M +
+                  (size_t)mt) = t;
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // (the tile is read before it is written again)
+          }
+        }
       }
     }
   }
@@ -1070,8 +1102,9 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
   constexpr int MX = mx_kind(EPI);
   constexpr int kStage = stage_bytes(EPI);
   constexpr int kOps = batch_ops(EPI);
-  // (EPI_QKV_Q8: 4 KiB more, for the rows' absolute maxima exchanged between the waves of a head)
-  constexpr int kQ8Bytes = EPI == EPI_QKV_Q8 ? 4096 : 0;
+  // (EPI_QKV_Q8: 4 KiB more for the rows' absolute maxima exchanged between the waves of a head,
+  // and 1 KiB per wave for turning value codes around)
+  constexpr int kQ8Bytes = EPI == EPI_QKV_Q8 ? 4096 + 8 * 1024 : 0;
   __shared__ __attribute__((aligned(1024)))
   uint8_t lds[2 * kStage + kParamBufs * kParamBytes + kQ8Bytes];
   __shared__ int s_last;
@@ -1561,8 +1594,8 @@ hipError_t launch_linear_qkv_q8(const uint8_t* q, const float* scale, int64_t M,
                                 const uint16_t* bias, const uint16_t* norm_qk,
                                 const float* rope_cos, const float* rope_sin, float eps,
                                 uint8_t* q8, float* q_scale, uint8_t* k8, float* k_scale,
-                                uint16_t* out_v, void* workspace, uint64_t workspace_bytes,
-                                hipStream_t stream) {
+                                uint8_t* vt8, float* v_scale, void* workspace,
+                                uint64_t workspace_bytes, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   Params p{};
   set_segments(p, 1, &M);
@@ -1576,9 +1609,10 @@ hipError_t launch_linear_qkv_q8(const uint8_t* q, const float* scale, int64_t M,
   p.qkv.rope_sin = rope_sin;
   p.qkv.out_q = reinterpret_cast<uint16_t*>(q8);
   p.qkv.out_k = reinterpret_cast<uint16_t*>(k8);
-  p.qkv.out_v = out_v;
+  p.qkv.out_v = reinterpret_cast<uint16_t*>(vt8);
   p.qkv.scale_q = q_scale;
   p.qkv.scale_k = k_scale;
+  p.qkv.scale_v = v_scale;
   p.qkv.eps = eps;
   p.qkv.heads = (int)heads;
   return schedule_and_launch(p, M, K, 3 * heads * 128, EPI_QKV_Q8, workspace, workspace_bytes,

@@ -234,29 +234,31 @@ int dq_linear_qkv_fp8(const void* q, const float* scale, int64_t M, int64_t K, c
                       void* stream);
 
 /*
- * dq_linear_qkv_fp8_attn -- dq_linear_qkv_fp8 with the queries and keys leaving as the FP8
- * operands of dq_attention_fp8: E4M3 codes with one scale per head row, written by the GEMM's
- * epilogue in place of their bf16 form. The fused query/key/value epilogue (page "Accelerarea
- * generarii de imagini cu FLUX 3 Image Klein pe GPU-urile Blackwell NVIDIA", its paragraph on the
- * PrimsTS GEMMs) meets the pages' FP8 attention (page "Optimizacion de la inferencia de FLUX 3
- * Image Klein en GPUs NVIDIA Blackwell", section "Como funciona": query, key and value held in
- * FP8); the reading taken is that the handoff equals the unfused path exactly:
+ * dq_linear_qkv_fp8_attn -- dq_linear_qkv_fp8 with every output leaving as the FP8 operands of
+ * dq_attention_fp8: E4M3 codes with one scale per head row, written by the GEMM's epilogue in
+ * place of the bf16 outputs. The fused query/key/value epilogue (page "Accelerarea generarii de
+ * imagini cu FLUX 3 Image Klein pe GPU-urile Blackwell NVIDIA", its paragraph on the PrimsTS
+ * GEMMs) meets the pages' FP8 attention (page "Optimizacion de la inferencia de FLUX 3 Image
+ * Klein en GPUs NVIDIA Blackwell", section "Como funciona": query, key and value held in FP8);
+ * the reading taken is that the handoff equals the unfused path exactly:
  *
  *   q8, q_scale = dq_quantize_fp8 of the bf16 queries dq_linear_qkv_fp8 gives, as
  *                 [heads * M] rows of 128 (codes [heads][M][128], scales [heads][M]);
  *   k8, k_scale   the same for the keys;
- *   out_v         bf16 [heads][M][128], as dq_linear_qkv_fp8's out_v
+ *   vt8, v_scale  dq_quantize_v_fp8 of its bf16 values (codes transposed [heads][128][M],
+ *                 scales [heads][M])
  *
- * so every code, scale and value is bit-identical to dq_linear_qkv_fp8 followed by
- * dq_quantize_fp8 on its query and key outputs. Other arguments, requirements and errors as
- * dq_linear_qkv_fp8; all five outputs 16-byte aligned and overlapping no input, no other output
- * and no workspace.
+ * so every code and scale is bit-identical to dq_linear_qkv_fp8 followed by those quantizers.
+ * Other arguments, requirements and errors as dq_linear_qkv_fp8, and M % 16 == 0 (else
+ * DQ_ERR_SHAPE; dq_attention_fp8 asks the same of S); all six outputs 16-byte aligned and
+ * overlapping no input, no other output and no workspace.
  */
 int dq_linear_qkv_fp8_attn(const void* q, const float* scale, int64_t M, int64_t K, const void* qw,
                            const float* w_scale, int64_t heads, const void* bias,
                            const void* norm_qk, const float* rope_cos, const float* rope_sin,
-                           float eps, void* q8, float* q_scale, void* k8, float* k_scale,
-                           void* out_v, void* workspace, uint64_t workspace_bytes, void* stream);
+                           float eps, void* q8, float* q_scale, void* k8, float* k_scale, void* vt8,
+                           float* v_scale, void* workspace, uint64_t workspace_bytes,
+                           void* stream);
 
 /*
  * dq_quantize_v_fp8 -- per-(head, token) FP8 quantization of attention values, codes written

@@ -36,7 +36,8 @@ def lib():
     L.dq_linear_qkv_fp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, vp, ctypes.c_float,
                                     vp, vp, vp, vp, ctypes.c_uint64, vp]
     L.dq_linear_qkv_fp8_attn.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, vp,
-                                         ctypes.c_float, vp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
+                                         ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
+                                         ctypes.c_uint64, vp]
     L.dq_quantize_v_fp8.argtypes = [vp, i64, i64, vp, vp, vp]
     L.dq_attention_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, ctypes.c_uint64,
                                    i64, vp]
@@ -244,13 +245,13 @@ def test_linear_qkv_workspace_checks(lib):
     assert lib.dq_last_hip_error() == 0
 
 
-Q8, SQ8, K8, SK8 = (0x10000000 * i for i in range(16, 20))   # fake, far from the others
+Q8, SQ8, K8, SK8, SV8 = (0x10000000 * i for i in range(16, 21))   # fake, far from the others
 
 
 def qkv8(lib, M=64, K=256, heads=1, q=Aq, sa=As, qw=Wq, sw=Ws, bias=Bi, nqk=NQ, cos=CS, sin=SN,
-         eps=1e-6, q8=Q8, sq=SQ8, k8=K8, sk=SK8, ov=OV, ws=None, ws_bytes=0):
+         eps=1e-6, q8=Q8, sq=SQ8, k8=K8, sk=SK8, ov=OV, sv=SV8, ws=None, ws_bytes=0):
     return lib.dq_linear_qkv_fp8_attn(q, sa, M, K, qw, sw, heads, bias, nqk, cos, sin, eps, q8, sq,
-                                      k8, sk, ov, ws, ws_bytes, None)
+                                      k8, sk, ov, sv, ws, ws_bytes, None)
 
 
 def test_linear_qkv_attn_argument_checks(lib):
@@ -260,22 +261,24 @@ def test_linear_qkv_attn_argument_checks(lib):
     assert qkv8(lib, heads=1 << 30) == SHAPE
     assert qkv8(lib, K=192) == SHAPE
     assert qkv8(lib, M=-1) == SHAPE
+    assert qkv8(lib, M=72) == SHAPE                           # M % 16 (the transposed values)
     assert qkv8(lib, eps=0.0) == VALUE
     assert qkv8(lib, eps=float("nan")) == VALUE
-    for name in ("q", "sa", "qw", "sw", "nqk", "cos", "sin", "q8", "sq", "k8", "sk", "ov"):
+    for name in ("q", "sa", "qw", "sw", "nqk", "cos", "sin", "q8", "sq", "k8", "sk", "ov", "sv"):
         assert qkv8(lib, **{name: None}) == NULL, name
     base = dict(q=Aq, sa=As, qw=Wq, sw=Ws, bias=Bi, nqk=NQ, cos=CS, sin=SN, q8=Q8, sq=SQ8, k8=K8,
-                sk=SK8, ov=OV)
+                sk=SK8, ov=OV, sv=SV8)
     for name, val in base.items():
         assert qkv8(lib, **{name: val + 8}) == ALIGN, name
-    # codes [heads, M, 128] = 8 KiB here, scales [heads, M] = 256 bytes, values 16 KiB
+    # codes [heads, M, 128] = 8 KiB here (the values' too), scales [heads, M] = 256 bytes
     assert qkv8(lib, q8=Aq) == ALIAS                          # query codes over the input codes
     assert qkv8(lib, sk=CS + 64) == ALIAS                     # key scales over the cosines
     assert qkv8(lib, k8=Q8 + 8192 - 16) == ALIAS              # two code outputs overlap
     assert qkv8(lib, sq=Q8 + 4096) == ALIAS                   # scales inside the query codes
-    assert qkv8(lib, ov=K8 - 16384 + 16) == ALIAS             # values run into the key codes
+    assert qkv8(lib, ov=K8 - 8192 + 16) == ALIAS              # value codes run into the key codes
+    assert qkv8(lib, sv=SK8 + 128) == ALIAS                   # two scale outputs overlap
     assert qkv8(lib, k8=Q8 + 8192, sq=Q8 + 16384, sk=Q8 + 16640, ov=Q8 + 16896,
-                q=None) == NULL                               # adjacent outputs are fine
+                sv=Q8 + 25088, q=None) == NULL                # adjacent outputs are fine
 
 
 def test_linear_qkv_attn_workspace_checks(lib):
