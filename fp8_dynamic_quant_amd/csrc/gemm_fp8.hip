@@ -80,7 +80,8 @@ constexpr int kMaxSeg = (int)kMaxSegments;      // row segments with their own w
 enum { EPI_BIAS = 0, EPI_GELU_TANH = 1, EPI_GATED_RESIDUAL = 2, EPI_QKV = 3,
        EPI_MX_BIAS = 4, EPI_MX_GELU_TANH = 5, EPI_MX_GATED = 6,
        EPI_MX4_BIAS = 7, EPI_MX4_GELU_TANH = 8, EPI_MX4_GATED = 9,
-       EPI_QKV_Q8 = 10 };  // the QKV epilogue with queries and keys leaving as E4M3 codes
+       EPI_QKV_Q8 = 10,    // the QKV epilogue with its outputs leaving as E4M3 codes
+       EPI_MXG_BIAS = 11, EPI_MXG_GELU_TANH = 12 };  // MX FP8 with grouped scale copies
 
 // Block-scaled (MX) operands: E4M3 codes with one E8M0 scale byte per 32 values along K. Each
 // K step then also stages the 4 scale bytes (one dword) of every A and B row of the tile, after
@@ -90,24 +91,46 @@ enum { EPI_BIAS = 0, EPI_GELU_TANH = 1, EPI_GATED_RESIDUAL = 2, EPI_QKV = 3,
 // With FP4 (E2M1) elements (EPI_MX4_*) the operands are two codes per byte, so a step of 128 bytes
 // per row is 256 values along K and its 8 scale bytes are two dwords per row: lanes 0-31 of the
 // copy move the first dword of 32 rows, lanes 32-63 the second, filling the whole slot.
+//
+// Grouped scale copies (EPI_MXG_*, E4M3 elements, K steps per tile a multiple of 4): the 4 scale
+// bytes of a row for 4 consecutive K steps are 16 contiguous bytes of the [M, K / 32] scale
+// matrix, so every fourth step one 16-byte copy per lane moves the next 4 steps' scales of 64 rows,
+// two copies per wave of group 0 (its A rows 64 q + [0, 64), and the 64 B rows of its batches 2
+// and 3) instead of one 4-byte copy per batch and step. They go into one of two 8 KiB group
+// buffers (A rows [0, 4 KiB) at 16 bytes a row, then wave q's B copy at 4 KiB + 1 KiB q), the
+// group's index parity choosing the buffer; with every item a multiple of 4 steps long, group j
+// holds steps [4 j, 4 j + 4) of the workgroup's sequence and rides on group 0's batch 1 of step
+// 4 j (issued in step 4 j - 1, waited for at its end), three steps after the last reader of the
+// buffer's previous group. (Issuing it a step earlier measured no faster.)
 constexpr int kScaleBytes = 4096;
+constexpr int kGroupBytes = 16384;
+__host__ __device__ constexpr bool is_mxg(int epi) {
+  return epi == EPI_MXG_BIAS || epi == EPI_MXG_GELU_TANH;
+}
 __host__ __device__ constexpr bool is_mx(int epi) {
-  return epi >= EPI_MX_BIAS && epi <= EPI_MX4_GATED;
+  return (epi >= EPI_MX_BIAS && epi <= EPI_MX4_GATED) || is_mxg(epi);
 }
 __host__ __device__ constexpr bool is_qkv(int epi) { return epi == EPI_QKV || epi == EPI_QKV_Q8; }
-// 0: per-row scales; 1: MX with E4M3 elements; 2: MX with E2M1 elements
+// 0: per-row scales; 1: MX with E4M3 elements; 2: MX with E2M1 elements; 3: MX with E4M3
+// elements and grouped scale copies
 __host__ __device__ constexpr int mx_kind(int epi) {
-  return epi >= EPI_MX4_BIAS && epi <= EPI_MX4_GATED ? 2 : is_mx(epi) ? 1 : 0;
+  return epi >= EPI_MX4_BIAS && epi <= EPI_MX4_GATED ? 2 : is_mxg(epi) ? 3 : is_mx(epi) ? 1 : 0;
 }
 // The output step after dequantization: EPI_BIAS, EPI_GELU_TANH, EPI_GATED_RESIDUAL (or EPI_QKV)
 __host__ __device__ constexpr int act_of(int epi) {
-  return is_qkv(epi) ? EPI_QKV : epi < EPI_MX_BIAS ? epi : (epi - EPI_MX_BIAS) % 3;
+  return is_qkv(epi) ? EPI_QKV : epi < EPI_MX_BIAS ? epi
+       : is_mxg(epi) ? epi - EPI_MXG_BIAS : (epi - EPI_MX_BIAS) % 3;
+}
+// Scales staged with each step's codes (MX kinds 1 and 2)
+__host__ __device__ constexpr bool step_scales(int epi) {
+  return mx_kind(epi) == 1 || mx_kind(epi) == 2;
 }
 __host__ __device__ constexpr int stage_bytes(int epi) {
-  return kStageBytes + (is_mx(epi) ? kScaleBytes : 0);
+  return kStageBytes + (step_scales(epi) ? kScaleBytes : 0);
 }
-// Copy instructions per batch: four of codes, plus one of scales in MX mode.
-__host__ __device__ constexpr int batch_ops(int epi) { return is_mx(epi) ? 5 : 4; }
+// Copy instructions per batch: four of codes, plus one of scales with per-step scale copies. (The
+// grouped copies are the last instructions of batch 1, which no wait leaves in flight.)
+__host__ __device__ constexpr int batch_ops(int epi) { return step_scales(epi) ? 5 : 4; }
 
 // Arguments of the QKV epilogue only. They are read where they are used (the epilogue and the
 // parameter copy), through qkv_args(), so that they do not sit in scalar registers through the
@@ -411,11 +434,17 @@ struct Batch {
   uint32_t off0, lds01, lds23;
   v4i rsS;               // MX only: the batch's 32 rows' scale dwords of step k (lanes 0-31)
   uint32_t soff, slds;
+  // grouped scale copies (MX kind 3, a batch given a group buffer for a step that starts a group):
+  // the offsets of this lane's 16 bytes for the A and the B copy, and their LDS places
+  bool grp;
+  v4i rsGA, rsGB;
+  uint32_t goA, goB, gldsA, gldsB;
 };
 
 template <int NB, int MX>
 __device__ __forceinline__ Batch batch_of(const TileDesc& d, uint32_t K, int k, uint8_t* st,
-                                          uint32_t vlane, int q, int which, bool live) {
+                                          uint32_t vlane, int q, int which, bool live,
+                                          uint8_t* gbuf = nullptr) {
   Batch b;
   const uint32_t base = lds_addr(st);
   int grow, lrow;
@@ -461,12 +490,50 @@ __device__ __forceinline__ Batch batch_of(const TileDesc& d, uint32_t K, int k, 
     b.slds = base + (uint32_t)kStageBytes + (which < 2 ? 0u : 2048u) +
              (uint32_t)(n16 ? grow >> 4 : grow >> 5) * 256u;
   }
+  if (MX == 3) {
+    b.grp = live && gbuf != nullptr && (k & 3) == 0;
+    b.rsGA = d.rsSA;
+    b.rsGB = d.rsSB;
+    if (b.grp) {
+      // lane L: A tile row 64 q + L; B tile row (q >> 1) 128 + (L >> 5) 64 + (q & 1) 32 + (L & 31)
+      // in a full tile (batch 3's rows, then batch 2's), in a narrow half lanes L < 32 take
+      // (q >> 1) 64 + ((L >> 4) & 1) 32 + (q & 1) 16 + (L & 15) and the others read past the
+      // range (zeros into bytes no reader reads)
+      const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      const uint32_t kb = K / 32u, qq = (uint32_t)q;
+      const uint32_t ra = 64u * qq + lane;
+      uint32_t rb;
+      bool okb = true;
+      if (NB == 2) {
+        rb = (qq >> 1) * 128u + (lane >> 5) * 64u + (qq & 1u) * 32u + (lane & 31u);
+      } else {
+        rb = (qq >> 1) * 64u + ((lane >> 4) & 1u) * 32u + (qq & 1u) * 16u + (lane & 15u);
+        okb = lane < 32u;
+      }
+      b.goA = ra * kb + (uint32_t)k * 4u;
+      b.goB = okb ? rb * kb + (uint32_t)k * 4u : 0x80000000u;
+      b.gldsA = lds_addr(gbuf) + qq * 1024u;
+      b.gldsB = b.gldsA + 4096u;
+    }
+  }
   return b;
 }
 
 // The scale dwords of a batch (MX): lanes 0-31 one row each (no branch: see batch_of).
 __device__ __forceinline__ void copy_scales(const Batch& b) {
   copy_to_lds_b32(b.rsS, b.soff, __builtin_amdgcn_readfirstlane(b.slds));
+}
+
+// Grouped scale copies of a group-0 wave: its A rows' and its B rows' next 4 steps (see above).
+__device__ __forceinline__ v4i uniform_rsrc(v4i r) {
+  return (v4i){__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
+               __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3])};
+}
+__device__ __forceinline__ void copy_group_a(const Batch& b) {
+  copy_to_lds(uniform_rsrc(b.rsGA), b.goA, __builtin_amdgcn_readfirstlane(b.gldsA));
+}
+__device__ __forceinline__ void copy_group_b(const Batch& b) {
+  copy_to_lds(uniform_rsrc(b.rsGB), b.goB, __builtin_amdgcn_readfirstlane(b.gldsB));
 }
 
 __device__ __forceinline__ void copy_block(const Batch& b, uint32_t K, uint32_t dodd, int j) {
@@ -477,11 +544,16 @@ __device__ __forceinline__ void copy_block(const Batch& b, uint32_t K, uint32_t 
 
 template <int NB, int MX>
 __device__ __forceinline__ void copy_batch(const TileDesc& d, uint32_t K, int k, uint8_t* st,
-                                           uint32_t vlane, uint32_t dodd, int q, int which) {
-  const Batch b = batch_of<NB, MX>(d, K, k, st, vlane, q, which, true);
+                                           uint32_t vlane, uint32_t dodd, int q, int which,
+                                           uint8_t* gbuf = nullptr) {
+  const Batch b = batch_of<NB, MX>(d, K, k, st, vlane, q, which, true, gbuf);
 #pragma unroll
   for (int j = 0; j < 4; ++j) copy_block(b, K, dodd, j);
-  if (MX) copy_scales(b);
+  if (MX == 1 || MX == 2) copy_scales(b);
+  if (MX == 3 && b.grp) {
+    copy_group_a(b);
+    copy_group_b(b);
+  }
 }
 
 // The tile's epilogue parameters into param buffer pb, one copy per group-0 wave (q).
@@ -540,9 +612,10 @@ struct Frags {
 // the operands of two instructions (64 values each: registers 0-3 of lanes l and l + 32 the
 // first, registers 4-7 the second), and each K half reads the rows' dword of its 4 blocks, of
 // which the two instructions select bytes 0 and 2.
+// With grouped scale copies gb is the step's group buffer plus 4 (step mod 4).
 template <int NB, int MX>
 __device__ __forceinline__ void read_frags(const uint8_t* st, Frags& f, int h, int wm, int wn,
-                                           int lane) {
+                                           int lane, const uint8_t* gb = nullptr) {
   const int r = lane & 31;
   const int c0 = MX ? h * 4 + (lane >> 5) : h * 4 + (lane >> 5) * 2;
   const int dc = MX ? 2 : 1;
@@ -564,7 +637,28 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, Frags& f, int h, i
     f.b[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
-  if (MX && (MX == 2 || h == 0)) {  // 256-byte slots (A rows from 0, B rows from 2048)
+  if (MX == 3 && h == 0) {
+    // A tile row ra at 16 ra; B tile row rb in the copy of wave
+    // 2 (rb >> 7) + ((rb >> 5) & 1), lane ((rb >> 6) & 1) 32 + (rb & 31) (full tile), or of wave
+    // 2 (rb >> 6) + ((rb >> 4) & 1), lane ((rb >> 5) & 1) 16 + (rb & 15) (narrow half)
+    const int sh = 8 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f.sa[i] = *reinterpret_cast<const uint32_t*>(gb + (wm * 128 + i * 32 + r) * 16) >> sh;
+    if (NB == 2) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int rb = b0 + i * 32 + r;
+        const int wq = 2 * (rb >> 7) + ((rb >> 5) & 1), l = ((rb >> 6) & 1) * 32 + (rb & 31);
+        f.sb[i] = *reinterpret_cast<const uint32_t*>(gb + 4096 + wq * 1024 + l * 16) >> sh;
+      }
+    } else {
+      const int rb = 32 * wn + r;
+      const int wq = 2 * (rb >> 6) + ((rb >> 4) & 1), l = ((rb >> 5) & 1) * 16 + (rb & 15);
+      f.sb[0] = *reinterpret_cast<const uint32_t*>(gb + 4096 + wq * 1024 + l * 16) >> sh;
+    }
+  }
+  if ((MX == 1 || MX == 2) && (MX == 2 || h == 0)) {  // 256-byte slots (A rows from 0, B from 2048)
     const uint32_t* sc = reinterpret_cast<const uint32_t*>(st + kStageBytes);
     const int sh = 8 * (lane >> 5);
     const int hd = MX == 2 ? 32 * h : 0;  // FP4: the K half's dword sits 32 dwords further
@@ -584,7 +678,7 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, Frags& f, int h, i
 // takes fragment registers 4P .. 4P + 3 and scale byte 2P. The first pass issues the batch's
 // copies: one after each of its first four MFMAs (a copy instruction waits for the vector memory
 // unit to take it, which here overlaps the matrix unit's work instead of holding up the next
-// phase), and the scale copy after the fifth.
+// phase), and the scale copy after the fifth (grouped scale copies: after the sixth and seventh).
 template <int NB, int MX, int H, int P>
 __device__ __forceinline__ void mma_pass(const Frags& f, v16f (&acc)[NB][4], const Batch& b,
                                          uint32_t K, uint32_t dodd) {
@@ -607,7 +701,9 @@ __device__ __forceinline__ void mma_pass(const Frags& f, v16f (&acc)[NB][4], con
             f.b[bn], f.a[bm], acc[bn][bm], 0, 0, 0, 0, 0, 0);
       }
       if (P == 0 && bn == 0) copy_block(b, K, dodd, bm);
-      if (MX && P == 0 && bn == NB - 1 && bm == 0) copy_scales(b);
+      if ((MX == 1 || MX == 2) && P == 0 && bn == NB - 1 && bm == 0) copy_scales(b);
+      if (MX == 3 && b.grp && bn == NB - 1 && bm == 1) copy_group_a(b);
+      if (MX == 3 && b.grp && bn == NB - 1 && bm == 2) copy_group_b(b);
       __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -1105,11 +1201,14 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
   // (EPI_QKV_Q8: 4 KiB more for the rows' absolute maxima exchanged between the waves of a head,
   // and 1 KiB per wave for turning value codes around)
   constexpr int kQ8Bytes = EPI == EPI_QKV_Q8 ? 4096 + 8 * 1024 : 0;
+  // (grouped scale copies: the two group buffers)
+  constexpr int kGrpBytes = MX == 3 ? kGroupBytes : 0;
   __shared__ __attribute__((aligned(1024)))
-  uint8_t lds[2 * kStage + kParamBufs * kParamBytes + kQ8Bytes];
+  uint8_t lds[2 * kStage + kParamBufs * kParamBytes + kQ8Bytes + kGrpBytes];
   __shared__ int s_last;
   uint8_t* pbuf = lds + 2 * kStage;
   uint32_t* qscr = reinterpret_cast<uint32_t*>(pbuf + kParamBufs * kParamBytes);
+  uint8_t* gbase = pbuf + kParamBufs * kParamBytes + kQ8Bytes;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1153,7 +1252,7 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
     const TileDesc d0 = tile_desc<NB, MX>(p, c0.t, c0.half);
     if (g == 0) {
       copy_batch<NB, MX>(d0, uK, c0.k, lds, vlane, dodd, q, 0);
-      copy_batch<NB, MX>(d0, uK, c0.k, lds, vlane, dodd, q, 1);
+      copy_batch<NB, MX>(d0, uK, c0.k, lds, vlane, dodd, q, 1, gbase);
       copy_params<EPI>(p, d0, pbuf, q, lane);
     } else {
       copy_batch<NB, MX>(d0, uK, c0.k, lds, vlane, dodd, q, 2);
@@ -1193,10 +1292,16 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
       const bool has1 = S + 1 < nsteps, has2 = S + 2 < nsteps;
       const bool starts = has1 && (j + 1 == len);  // step S + 1 begins the next item
       // reads of K half 0 (G0: phase A, G1: phase B)
-      read_frags<NB, MX>(st, f, 0, wm, wn, lane);
+      read_frags<NB, MX>(st, f, 0, wm, wn, lane, gbase + ((S >> 2) & 1) * 8192 + (S & 3) * 4);
       phase_barrier();
       // MFMAs of K half 0 with batch g + 1 of step S + 1 (G0: phase B, G1: phase C)
-      mma8_copy<NB, MX, 0>(f, acc, batch_of<NB, MX>(d1, uK, c1.k, st1, vlane, q, g + 1, has1), uK, dodd);
+      // (grouped scale copies: G0's batch 1 also carries the scales of the group step S + 1 starts)
+      mma8_copy<NB, MX, 0>(f, acc,
+                           batch_of<NB, MX>(d1, uK, c1.k, st1, vlane, q, g + 1, has1,
+                                            MX == 3 && g == 0
+                                                ? gbase + (((S + 1) >> 2) & 1) * 8192
+                                                : nullptr),
+                           uK, dodd);
       phase_barrier();
       // reads of K half 1 (G0: phase C, G1: phase D); G0 starts the next item's parameters,
       // G1 waits for its batch 0 of step S + 1
@@ -1391,6 +1496,8 @@ static hipError_t schedule_and_launch(Params& p, int64_t M, int64_t K, int64_t N
     case EPI_QKV_Q8: return launch_epi<EPI_QKV_Q8>(p, g, ng, stream);
     case EPI_MX_BIAS: return launch_epi<EPI_MX_BIAS>(p, g, ng, stream);
     case EPI_MX_GELU_TANH: return launch_epi<EPI_MX_GELU_TANH>(p, g, ng, stream);
+    case EPI_MXG_BIAS: return launch_epi<EPI_MXG_BIAS>(p, g, ng, stream);
+    case EPI_MXG_GELU_TANH: return launch_epi<EPI_MXG_GELU_TANH>(p, g, ng, stream);
     case EPI_MX4_BIAS: return launch_epi<EPI_MX4_BIAS>(p, g, ng, stream);
     case EPI_MX4_GELU_TANH: return launch_epi<EPI_MX4_GELU_TANH>(p, g, ng, stream);
     case EPI_MX4_GATED: return launch_epi<EPI_MX4_GATED>(p, g, ng, stream);
@@ -1472,7 +1579,11 @@ hipError_t launch_linear_mx(const uint8_t* qa, const uint8_t* sa, int64_t M, int
   p.seg.B[0] = qw;
   p.seg.sw[0] = reinterpret_cast<const float*>(sw);
   p.seg.bias[0] = bias;
-  return schedule_and_launch(p, M, K, N, epilogue == 1 ? EPI_MX_GELU_TANH : EPI_MX_BIAS, nullptr,
+  // grouped scale copies when every item's K steps come in whole groups of 4
+  const bool grouped = (K / kBK) % 4 == 0;
+  const int epi = grouped ? (epilogue == 1 ? EPI_MXG_GELU_TANH : EPI_MXG_BIAS)
+                          : (epilogue == 1 ? EPI_MX_GELU_TANH : EPI_MX_BIAS);
+  return schedule_and_launch(p, M, K, N, epi, nullptr,
                              0, stream);
 }
 

@@ -102,9 +102,12 @@ def _end_to_end(M, K, N, epi, seed, bias=True, rows=None):
 
 
 @pytest.mark.parametrize("M,K,N", [(64, 128, 64), (1, 256, 192), (255, 384, 320), (257, 1024, 256),
-                                   (300, 640, 512), (513, 128, 64)])
+                                   (300, 640, 512), (513, 128, 64), (300, 2048, 576),
+                                   (40, 512, 128)])
 @pytest.mark.parametrize("epi", ["bias", "gelu_tanh"])
 def test_tiles_and_ragged_tails(M, K, N, epi):
+    """K steps of 128 a multiple of 4 (K = 512, 1024, 2048) take the grouped scale copies, the
+    others the per-step ones."""
     _end_to_end(M, K, N, epi, seed=1)
 
 
@@ -119,19 +122,23 @@ def test_mlp_up_full_size_sampled_rows():
     _end_to_end(4608, 3072, 12288, "gelu_tanh", seed=3, rows=rows)
 
 
-def test_more_tiles_than_compute_units_ragged():
+@pytest.mark.parametrize("K", [256, 512])
+def test_more_tiles_than_compute_units_ragged(K):
     """4608 x 3648 (18 x 15 tiles, the last tile column 64 wide): more tiles than compute units,
-    so workgroups of the second round take the tiles of the last tile rows."""
+    so the 14 tiles left after the first round run as narrow halves (per-step scale copies at
+    K = 256, grouped at K = 512)."""
     rows = np.unique(np.concatenate([[0, 4095, 4096, 4607],
                                      np.random.default_rng(6).choice(4608, 44, replace=False)]))
-    _end_to_end(4608, 256, 3648, "bias", seed=4, rows=rows)
+    _end_to_end(4608, K, 3648, "bias", seed=4, rows=rows)
 
 
-def test_longest_k():
-    """M = 3, K = 16776960 (the longest the layer accepts: 131070 steps of 128), N = 64: random
-    codes and scale bytes 127 +- 6, against the oracle summed over K chunks of 131072."""
+@pytest.mark.parametrize("steps", [131070, 131068])
+def test_longest_k(steps):
+    """M = 3, K = 16776960 (the longest the layer accepts: 131070 steps of 128; per-step scale
+    copies) and 131068 steps (grouped scale copies), N = 64: random codes and scale bytes
+    127 +- 6, against the oracle summed over K chunks of 131072."""
     rng = np.random.default_rng(32)
-    M, K, N = 3, 131070 * 128, 64
+    M, K, N = 3, steps * 128, 64
     q = rng.integers(0, 256, size=(M, K), dtype=np.uint8)
     qw = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
     q[(q & 0x7F) == 0x7F] = 0x01
