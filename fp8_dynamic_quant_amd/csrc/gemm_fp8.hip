@@ -81,7 +81,8 @@ enum { EPI_BIAS = 0, EPI_GELU_TANH = 1, EPI_GATED_RESIDUAL = 2, EPI_QKV = 3,
        EPI_MX_BIAS = 4, EPI_MX_GELU_TANH = 5, EPI_MX_GATED = 6,
        EPI_MX4_BIAS = 7, EPI_MX4_GELU_TANH = 8, EPI_MX4_GATED = 9,
        EPI_QKV_Q8 = 10,    // the QKV epilogue with its outputs leaving as E4M3 codes
-       EPI_MXG_BIAS = 11, EPI_MXG_GELU_TANH = 12 };  // MX FP8 with grouped scale copies
+       EPI_MXG_BIAS = 11, EPI_MXG_GELU_TANH = 12,    // MX FP8 with grouped scale copies
+       EPI_MX4G_BIAS = 13, EPI_MX4G_GELU_TANH = 14, EPI_MX4G_GATED = 15 };  // and MX FP4
 
 // Block-scaled (MX) operands: E4M3 codes with one E8M0 scale byte per 32 values along K. Each
 // K step then also stages the 4 scale bytes (one dword) of every A and B row of the tile, after
@@ -101,25 +102,36 @@ enum { EPI_BIAS = 0, EPI_GELU_TANH = 1, EPI_GATED_RESIDUAL = 2, EPI_QKV = 3,
 // group's index parity choosing the buffer; with every item a multiple of 4 steps long, group j
 // holds steps [4 j, 4 j + 4) of the workgroup's sequence and rides on group 0's batch 1 of step
 // 4 j (issued in step 4 j - 1, waited for at its end), three steps after the last reader of the
-// buffer's previous group. (Issuing it a step earlier measured no faster.)
+// buffer's previous group. (Issuing it a step earlier measured no faster.) With E2M1 elements
+// (EPI_MX4G_*, K steps a multiple of 2) a row's 16 bytes are the 8 scale bytes of 2 steps, so a
+// group is 2 steps and the buffer's previous group was last read one step before the copy.
 constexpr int kScaleBytes = 4096;
 constexpr int kGroupBytes = 16384;
 __host__ __device__ constexpr bool is_mxg(int epi) {
   return epi == EPI_MXG_BIAS || epi == EPI_MXG_GELU_TANH;
 }
+__host__ __device__ constexpr bool is_mx4g(int epi) {
+  return epi >= EPI_MX4G_BIAS && epi <= EPI_MX4G_GATED;
+}
 __host__ __device__ constexpr bool is_mx(int epi) {
-  return (epi >= EPI_MX_BIAS && epi <= EPI_MX4_GATED) || is_mxg(epi);
+  return (epi >= EPI_MX_BIAS && epi <= EPI_MX4_GATED) || is_mxg(epi) || is_mx4g(epi);
 }
 __host__ __device__ constexpr bool is_qkv(int epi) { return epi == EPI_QKV || epi == EPI_QKV_Q8; }
-// 0: per-row scales; 1: MX with E4M3 elements; 2: MX with E2M1 elements; 3: MX with E4M3
-// elements and grouped scale copies
+// 0: per-row scales; 1: MX with E4M3 elements; 2: MX with E2M1 elements; 3 and 4: MX with E4M3
+// and with E2M1 elements and grouped scale copies
 __host__ __device__ constexpr int mx_kind(int epi) {
-  return epi >= EPI_MX4_BIAS && epi <= EPI_MX4_GATED ? 2 : is_mxg(epi) ? 3 : is_mx(epi) ? 1 : 0;
+  return epi >= EPI_MX4_BIAS && epi <= EPI_MX4_GATED ? 2 : is_mxg(epi) ? 3 : is_mx4g(epi) ? 4
+       : is_mx(epi) ? 1 : 0;
 }
+__host__ __device__ constexpr bool mx_fp4(int mx) { return mx == 2 || mx == 4; }
+__host__ __device__ constexpr bool mx_grouped(int mx) { return mx == 3 || mx == 4; }
+// K steps per scale group (grouped kinds)
+__host__ __device__ constexpr int group_steps(int mx) { return mx == 4 ? 2 : 4; }
 // The output step after dequantization: EPI_BIAS, EPI_GELU_TANH, EPI_GATED_RESIDUAL (or EPI_QKV)
 __host__ __device__ constexpr int act_of(int epi) {
   return is_qkv(epi) ? EPI_QKV : epi < EPI_MX_BIAS ? epi
-       : is_mxg(epi) ? epi - EPI_MXG_BIAS : (epi - EPI_MX_BIAS) % 3;
+       : is_mxg(epi) ? epi - EPI_MXG_BIAS : is_mx4g(epi) ? epi - EPI_MX4G_BIAS
+       : (epi - EPI_MX_BIAS) % 3;
 }
 // Scales staged with each step's codes (MX kinds 1 and 2)
 __host__ __device__ constexpr bool step_scales(int epi) {
@@ -399,7 +411,7 @@ __device__ __forceinline__ TileDesc tile_desc(const Params& p, int t, int half) 
   if (MX) {
     // scale bytes per row: K / 32 values; p.K counts bytes, two values each with FP4. A
     // segment's weight scale bytes sit where its per-channel scales would.
-    const uint32_t kb = (uint32_t)p.K / (MX == 2 ? 16u : 32u);
+    const uint32_t kb = (uint32_t)p.K / (mx_fp4(MX) ? 16u : 32u);
     const uint8_t* sw = reinterpret_cast<const uint8_t*>(seg_args()->sw[d.g.s]);
     d.rsSA = buffer_rsrc(p.mxa + (size_t)m0 * kb, rowsA * kb);
     d.rsSB = buffer_rsrc(sw + (size_t)(rb > 0 ? n0 : 0) * kb, rowsB * kb);
@@ -490,8 +502,8 @@ __device__ __forceinline__ Batch batch_of(const TileDesc& d, uint32_t K, int k, 
     b.slds = base + (uint32_t)kStageBytes + (which < 2 ? 0u : 2048u) +
              (uint32_t)(n16 ? grow >> 4 : grow >> 5) * 256u;
   }
-  if (MX == 3) {
-    b.grp = live && gbuf != nullptr && (k & 3) == 0;
+  if (mx_grouped(MX)) {
+    b.grp = live && gbuf != nullptr && k % group_steps(MX) == 0;
     b.rsGA = d.rsSA;
     b.rsGB = d.rsSB;
     if (b.grp) {
@@ -500,7 +512,8 @@ __device__ __forceinline__ Batch batch_of(const TileDesc& d, uint32_t K, int k, 
       // (q >> 1) 64 + ((L >> 4) & 1) 32 + (q & 1) 16 + (L & 15) and the others read past the
       // range (zeros into bytes no reader reads)
       const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-      const uint32_t kb = K / 32u, qq = (uint32_t)q;
+      // scale bytes per row and per step: 4 (E4M3; p.K counts values), 8 (E2M1; p.K counts bytes)
+      const uint32_t kb = K / (MX == 4 ? 16u : 32u), kstep = MX == 4 ? 8u : 4u, qq = (uint32_t)q;
       const uint32_t ra = 64u * qq + lane;
       uint32_t rb;
       bool okb = true;
@@ -510,8 +523,8 @@ __device__ __forceinline__ Batch batch_of(const TileDesc& d, uint32_t K, int k, 
         rb = (qq >> 1) * 64u + ((lane >> 4) & 1u) * 32u + (qq & 1u) * 16u + (lane & 15u);
         okb = lane < 32u;
       }
-      b.goA = ra * kb + (uint32_t)k * 4u;
-      b.goB = okb ? rb * kb + (uint32_t)k * 4u : 0x80000000u;
+      b.goA = ra * kb + (uint32_t)k * kstep;
+      b.goB = okb ? rb * kb + (uint32_t)k * kstep : 0x80000000u;
       b.gldsA = lds_addr(gbuf) + qq * 1024u;
       b.gldsB = b.gldsA + 4096u;
     }
@@ -550,7 +563,7 @@ __device__ __forceinline__ void copy_batch(const TileDesc& d, uint32_t K, int k,
 #pragma unroll
   for (int j = 0; j < 4; ++j) copy_block(b, K, dodd, j);
   if (MX == 1 || MX == 2) copy_scales(b);
-  if (MX == 3 && b.grp) {
+  if (mx_grouped(MX) && b.grp) {
     copy_group_a(b);
     copy_group_b(b);
   }
@@ -612,7 +625,9 @@ struct Frags {
 // the operands of two instructions (64 values each: registers 0-3 of lanes l and l + 32 the
 // first, registers 4-7 the second), and each K half reads the rows' dword of its 4 blocks, of
 // which the two instructions select bytes 0 and 2.
-// With grouped scale copies gb is the step's group buffer plus 4 (step mod 4).
+// With grouped scale copies gb is the step's group buffer plus the step's place in its rows'
+// 16 bytes: 4 (step mod 4) with E4M3 elements, 8 (step mod 2) with E2M1 (whose K halves read the
+// two dwords there).
 template <int NB, int MX>
 __device__ __forceinline__ void read_frags(const uint8_t* st, Frags& f, int h, int wm, int wn,
                                            int lane, const uint8_t* gb = nullptr) {
@@ -637,11 +652,12 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, Frags& f, int h, i
     f.b[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
-  if (MX == 3 && h == 0) {
+  if (mx_grouped(MX) && (MX == 4 || h == 0)) {
     // A tile row ra at 16 ra; B tile row rb in the copy of wave
     // 2 (rb >> 7) + ((rb >> 5) & 1), lane ((rb >> 6) & 1) 32 + (rb & 31) (full tile), or of wave
     // 2 (rb >> 6) + ((rb >> 4) & 1), lane ((rb >> 5) & 1) 16 + (rb & 15) (narrow half)
     const int sh = 8 * (lane >> 5);
+    if (MX == 4) gb += 4 * h;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       f.sa[i] = *reinterpret_cast<const uint32_t*>(gb + (wm * 128 + i * 32 + r) * 16) >> sh;
@@ -686,7 +702,7 @@ __device__ __forceinline__ void mma_pass(const Frags& f, v16f (&acc)[NB][4], con
   for (int bn = 0; bn < NB; ++bn)
 #pragma unroll
     for (int bm = 0; bm < 4; ++bm) {
-      if (MX == 2) {
+      if (mx_fp4(MX)) {
         const v8i bv = P == 0 ? f.b[bn]
                               : __builtin_shufflevector(f.b[bn], f.b[bn], 4, 5, 6, 7, 0, 1, 2, 3);
         const v8i av = P == 0 ? f.a[bm]
@@ -702,8 +718,8 @@ __device__ __forceinline__ void mma_pass(const Frags& f, v16f (&acc)[NB][4], con
       }
       if (P == 0 && bn == 0) copy_block(b, K, dodd, bm);
       if ((MX == 1 || MX == 2) && P == 0 && bn == NB - 1 && bm == 0) copy_scales(b);
-      if (MX == 3 && b.grp && bn == NB - 1 && bm == 1) copy_group_a(b);
-      if (MX == 3 && b.grp && bn == NB - 1 && bm == 2) copy_group_b(b);
+      if (mx_grouped(MX) && P == 0 && b.grp && bn == NB - 1 && bm == 1) copy_group_a(b);
+      if (mx_grouped(MX) && P == 0 && b.grp && bn == NB - 1 && bm == 2) copy_group_b(b);
       __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -715,7 +731,7 @@ template <int NB, int MX, int H>
 __device__ __forceinline__ void mma8_copy(const Frags& f, v16f (&acc)[NB][4], const Batch& b,
                                           uint32_t K, uint32_t dodd) {
   mma_pass<NB, MX, H, 0>(f, acc, b, K, dodd);
-  if constexpr (MX == 2) mma_pass<NB, MX, H, 1>(f, acc, b, K, dodd);
+  if constexpr (mx_fp4(MX)) mma_pass<NB, MX, H, 1>(f, acc, b, K, dodd);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1202,7 +1218,8 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
   // and 1 KiB per wave for turning value codes around)
   constexpr int kQ8Bytes = EPI == EPI_QKV_Q8 ? 4096 + 8 * 1024 : 0;
   // (grouped scale copies: the two group buffers)
-  constexpr int kGrpBytes = MX == 3 ? kGroupBytes : 0;
+  constexpr int kGrpBytes = mx_grouped(MX) ? kGroupBytes : 0;
+  constexpr int GS = group_steps(MX);
   __shared__ __attribute__((aligned(1024)))
   uint8_t lds[2 * kStage + kParamBufs * kParamBytes + kQ8Bytes + kGrpBytes];
   __shared__ int s_last;
@@ -1292,20 +1309,21 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_pp(Params p) {
       const bool has1 = S + 1 < nsteps, has2 = S + 2 < nsteps;
       const bool starts = has1 && (j + 1 == len);  // step S + 1 begins the next item
       // reads of K half 0 (G0: phase A, G1: phase B)
-      read_frags<NB, MX>(st, f, 0, wm, wn, lane, gbase + ((S >> 2) & 1) * 8192 + (S & 3) * 4);
+      const uint8_t* gb = gbase + ((S / GS) & 1) * 8192 + (S % GS) * (16 / GS);
+      read_frags<NB, MX>(st, f, 0, wm, wn, lane, gb);
       phase_barrier();
       // MFMAs of K half 0 with batch g + 1 of step S + 1 (G0: phase B, G1: phase C)
       // (grouped scale copies: G0's batch 1 also carries the scales of the group step S + 1 starts)
       mma8_copy<NB, MX, 0>(f, acc,
                            batch_of<NB, MX>(d1, uK, c1.k, st1, vlane, q, g + 1, has1,
-                                            MX == 3 && g == 0
-                                                ? gbase + (((S + 1) >> 2) & 1) * 8192
+                                            mx_grouped(MX) && g == 0
+                                                ? gbase + (((S + 1) / GS) & 1) * 8192
                                                 : nullptr),
                            uK, dodd);
       phase_barrier();
       // reads of K half 1 (G0: phase C, G1: phase D); G0 starts the next item's parameters,
       // G1 waits for its batch 0 of step S + 1
-      read_frags<NB, MX>(st, f, 1, wm, wn, lane);
+      read_frags<NB, MX>(st, f, 1, wm, wn, lane, gb);
       if (g == 0) {
         if (starts)
           copy_params<EPI>(p, d1, pbuf + ((part + 1) % kParamBufs) * kParamBytes, q, lane);
@@ -1501,6 +1519,9 @@ static hipError_t schedule_and_launch(Params& p, int64_t M, int64_t K, int64_t N
     case EPI_MX4_BIAS: return launch_epi<EPI_MX4_BIAS>(p, g, ng, stream);
     case EPI_MX4_GELU_TANH: return launch_epi<EPI_MX4_GELU_TANH>(p, g, ng, stream);
     case EPI_MX4_GATED: return launch_epi<EPI_MX4_GATED>(p, g, ng, stream);
+    case EPI_MX4G_BIAS: return launch_epi<EPI_MX4G_BIAS>(p, g, ng, stream);
+    case EPI_MX4G_GELU_TANH: return launch_epi<EPI_MX4G_GELU_TANH>(p, g, ng, stream);
+    case EPI_MX4G_GATED: return launch_epi<EPI_MX4G_GATED>(p, g, ng, stream);
     default: return launch_epi<EPI_GATED_RESIDUAL>(p, g, ng, stream);
   }
 }
@@ -1609,8 +1630,12 @@ hipError_t launch_linear_mxfp4_segmented(const uint8_t* qa, const uint8_t* sa, i
     p.seg.bias[i] = bias[i];
     p.seg.gate[i] = gate[i];
   }
-  const int epi = epilogue == 1 ? EPI_MX4_GELU_TANH
-                  : epilogue == 2 ? EPI_MX4_GATED : EPI_MX4_BIAS;
+  // grouped scale copies when every item's K steps (256 values each) come in pairs
+  const bool grouped = (K / 2 / kBK) % 2 == 0;
+  const int epi = grouped ? (epilogue == 1 ? EPI_MX4G_GELU_TANH
+                             : epilogue == 2 ? EPI_MX4G_GATED : EPI_MX4G_BIAS)
+                          : (epilogue == 1 ? EPI_MX4_GELU_TANH
+                             : epilogue == 2 ? EPI_MX4_GATED : EPI_MX4_BIAS);
   return schedule_and_launch(p, M, K / 2, N, epi, nullptr, 0, stream);
 }
 

@@ -131,18 +131,22 @@ def test_mlp_up_full_size_sampled_rows():
     _end_to_end(4608, 3072, 12288, "gelu_tanh", seed=3, rows=rows)
 
 
-def test_more_tiles_than_compute_units_ragged():
-    """4608 x 256 -> 3648 (18 x 15 tiles, the last tile column 64 wide)."""
+@pytest.mark.parametrize("K", [256, 512])
+def test_more_tiles_than_compute_units_ragged(K):
+    """4608 x K -> 3648 (18 x 15 tiles, the last tile column 64 wide; the 14 tiles left after the
+    first round run as narrow halves): per-step scale copies at K = 256, grouped at K = 512."""
     rows = np.unique(np.concatenate([[0, 4095, 4096, 4607],
                                      np.random.default_rng(6).choice(4608, 44, replace=False)]))
-    _end_to_end(4608, 256, 3648, "bias", seed=4, rows=rows)
+    _end_to_end(4608, K, 3648, "bias", seed=4, rows=rows)
 
 
-def test_longest_k():
-    """M = 3, K = 16776960 (the longest the layer accepts: 65535 steps of 256 values), N = 64:
-    random codes and scale bytes 127 +- 6, against the oracle summed over K chunks of 131072."""
+@pytest.mark.parametrize("steps", [65535, 65534])
+def test_longest_k(steps):
+    """M = 3, K = 16776960 (the longest the layer accepts: 65535 steps of 256 values; per-step
+    scale copies) and 65534 steps (grouped scale copies), N = 64: random codes and scale bytes
+    127 +- 6, against the oracle summed over K chunks of 131072."""
     rng = np.random.default_rng(33)
-    M, K, N = 3, 65535 * 256, 64
+    M, K, N = 3, steps * 256, 64
     q = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
     qw = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
     s = (127 + rng.integers(-6, 7, (M, K // 32))).astype(np.uint8)
